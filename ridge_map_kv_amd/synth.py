@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and builds input structures (row masks, block
+tables, synthetic linear "model" data).  It contains none of the method's arithmetic:
+no map prediction, normalisation, projection, rotation, moment accumulation or solve.
+
+Recipes (the shapes and value distributions of the workloads):
+  * x_S ~ N(0, 1), drawn in float32 and rounded to bfloat16 where the library takes it.
+  * norm weights w = 1 + 0.1 N(0, 1); key/value projections W_K, W_V ~ N(0, 1/d).
+  * Synthetic layer inputs for calibration follow a near-identity linear model:
+    x_l = W_true,l x_S + c_l + s * e, with W_true,l = I + U_l diag(0.5) V_l^T (rank 64,
+    U, V ~ N(0, 1/d)), c_l ~ N(0, 1) and e either N(0, 1) or Student-t with 3 degrees
+    of freedom (the heavy-tailed case).
+  * Where a workload is too large for a CPU-side fit, a fill input map is drawn as
+    A = I + U diag(0.5) V^T, b ~ N(0, 1): the same near-identity family.  The fill
+    computes the same function of whatever map bytes it is given.
+  * Exact prefix rows: a seeded uniform draw without replacement ("count"), none, or
+    seeded contiguous blocks with lengths U[16, 80] covering half of the budget plus
+    uniformly drawn singletons for the other half ("blocks").
+  * Block tables: a seeded permutation of the physical pages.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+TRUE_MAP_RANK = 64
+TRUE_MAP_GAIN = 0.5
+
+
+def rng(seed: int, *tags: int) -> np.random.Generator:
+    """Independent stream for (seed, tags...), via SeedSequence spawn keys."""
+    return np.random.default_rng(np.random.SeedSequence(entropy=int(seed),
+                                                        spawn_key=tuple(int(t) for t in tags)))
+
+
+# Stream tags, so every tensor has its own stream.
+TAG_XS, TAG_EXACT, TAG_TABLE, TAG_NORM, TAG_WK, TAG_WV, TAG_MAPU, TAG_MAPV, TAG_MAPB, \
+    TAG_CAL_X, TAG_CAL_NOISE, TAG_CAL_C = range(1, 13)
+
+
+def exact_rows(cfg) -> np.ndarray:
+    """Seeded exact prefix rows of a fill workload (ascending int64)."""
+    P = cfg.prefix
+    g = rng(cfg.seed, TAG_EXACT)
+    if cfg.exact == "none" or cfg.exact_count == 0:
+        return np.zeros(0, dtype=np.int64)
+    if cfg.exact == "count":
+        return np.sort(g.choice(P, size=cfg.exact_count, replace=False)).astype(np.int64)
+    if cfg.exact == "blocks":
+        return blocks_and_singletons(P, cfg.exact_count, g)
+    raise ValueError(cfg.exact)
+
+
+def blocks_and_singletons(P: int, count: int, g: np.random.Generator,
+                          lo: int = 16, hi: int = 80) -> np.ndarray:
+    taken = np.zeros(P, dtype=bool)
+    block_budget = count // 2
+    placed = 0
+    while placed < block_budget:
+        length = int(g.integers(lo, hi + 1))
+        length = min(length, block_budget - placed)
+        start = int(g.integers(0, P - length + 1))
+        if taken[start:start + length].any():
+            continue
+        taken[start:start + length] = True
+        placed += length
+    free = np.flatnonzero(~taken)
+    singles = g.choice(free, size=count - placed, replace=False)
+    taken[singles] = True
+    out = np.flatnonzero(taken).astype(np.int64)
+    assert out.size == count
+    return out
+
+
+def exact_mask(cfg) -> np.ndarray:
+    """uint8 mask over the prefix: 1 where the row is exact."""
+    m = np.zeros(cfg.prefix, dtype=np.uint8)
+    m[exact_rows(cfg)] = 1
+    return m
+
+
+def n_pages(N: int, page_size: int) -> int:
+    return (N + page_size - 1) // page_size
+
+
+def block_table(N: int, page_size: int, seed: int, spare: int = 3) -> tuple[np.ndarray, int]:
+    """Permuted block table for one prompt.  Returns (table int32, number of physical
+    pages); the pool has a few spare pages that no row maps to."""
+    n_log = n_pages(N, page_size)
+    num = n_log + spare
+    perm = rng(seed, TAG_TABLE).permutation(num)[:n_log]
+    return perm.astype(np.int32), num
+
+
+def x_split(cfg_or_shape, seed: int | None = None) -> np.ndarray:
+    """x_S ~ N(0, 1) float32 [N, d]."""
+    if seed is None:
+        N, d, seed = cfg_or_shape.N, cfg_or_shape.d, cfg_or_shape.seed
+    else:
+        N, d = cfg_or_shape
+    return rng(seed, TAG_XS).standard_normal((N, d), dtype=np.float32)
+
+
+def layer_weights(d: int, kv: int, seed: int, layer: int):
+    """(norm_w, W_K, W_V) float32 for one layer: 1 + 0.1 N(0,1), N(0, 1/d), N(0, 1/d)."""
+    s = 1.0 / np.sqrt(d)
+    w = 1.0 + 0.1 * rng(seed, TAG_NORM, layer).standard_normal(d, dtype=np.float32)
+    WK = s * rng(seed, TAG_WK, layer).standard_normal((kv, d), dtype=np.float32)
+    WV = s * rng(seed, TAG_WV, layer).standard_normal((kv, d), dtype=np.float32)
+    return w.astype(np.float32), WK.astype(np.float32), WV.astype(np.float32)
+
+
+def true_map_factors(d: int, seed: int, layer: int, rank: int = TRUE_MAP_RANK):
+    """U, V ~ N(0, 1/d) [d, rank] of W_true = I + U diag(0.5) V^T."""
+    s = 1.0 / np.sqrt(d)
+    U = s * rng(seed, TAG_MAPU, layer).standard_normal((d, rank), dtype=np.float32)
+    V = s * rng(seed, TAG_MAPV, layer).standard_normal((d, rank), dtype=np.float32)
+    return U.astype(np.float32), V.astype(np.float32)
+
+
+def near_identity_map(d: int, seed: int, layer: int):
+    """A = I + U diag(0.5) V^T (float32 [d, d]) and b ~ N(0, 1) (float32 [d])."""
+    U, V = true_map_factors(d, seed, layer)
+    A = np.eye(d, dtype=np.float32) + TRUE_MAP_GAIN * (U @ V.T)
+    b = rng(seed, TAG_MAPB, layer).standard_normal(d, dtype=np.float32)
+    return A.astype(np.float32), b.astype(np.float32)
+
+
+def calib_data(d: int, n_layers: int, rows: int, seed: int, *, noise_scale: float = 0.1,
+               noise_dof: float | None = None, x_shift: float = 0.0):
+    """Synthetic calibration rows: x_S [rows, d] and x_l [n_layers, rows, d] (float32),
+    x_l = W_true,l x_S + c_l + noise_scale * e; e is N(0,1), or Student-t(noise_dof)."""
+    xS = rng(seed, TAG_CAL_X).standard_normal((rows, d), dtype=np.float32) + np.float32(x_shift)
+    xl = np.empty((n_layers, rows, d), dtype=np.float32)
+    for l in range(n_layers):
+        U, V = true_map_factors(d, seed, l)
+        c = rng(seed, TAG_CAL_C, l).standard_normal(d, dtype=np.float32)
+        gn = rng(seed, TAG_CAL_NOISE, l)
+        e = (gn.standard_t(noise_dof, size=(rows, d)) if noise_dof
+             else gn.standard_normal((rows, d)))
+        xl[l] = xS + TRUE_MAP_GAIN * ((xS @ V) @ U.T) + c[None, :] + noise_scale * e
+    return xS, xl
+
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1 (int8)."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    H = np.ones((1, 1), dtype=np.int8)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def sparse_dyadic_matrix(d_out: int, d_in: int, seed: int, per_row: int = 2) -> np.ndarray:
+    """d_out x d_in matrix with at most `per_row` nonzeros per row, each in
+    {+-1, +-1/2}: every product and sum with +-1 data is exact in bf16/fp32."""
+    g = rng(seed, 99)
+    W = np.zeros((d_out, d_in), dtype=np.float32)
+    vals = np.array([1.0, -1.0, 0.5, -0.5], dtype=np.float32)
+    for o in range(d_out):
+        cols = g.choice(d_in, size=per_row, replace=False)
+        W[o, cols] = g.choice(vals, size=per_row)
+    return W
