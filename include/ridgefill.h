@@ -1,0 +1,178 @@
+/*
+ * ridgefill.h -- C ABI of the RidgeFill upper-layer KV fill, its one-pass calibration
+ * and its closed-form ridge solve, for AMD Instinct MI355X (gfx950).
+ *
+ * Method source: the English RidgeFill review (jaehun.me, "paper-2611-09709v1", English
+ * edition).  Each entry point names the section it implements.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked "device" point to GPU memory the caller allocated; pointers
+ *    marked "host" point to CPU memory.  The library allocates no device memory,
+ *    keeps no device state between calls and creates no streams.  Every buffer it
+ *    needs beyond inputs and outputs is a caller-owned workspace whose size a
+ *    *_workspace_bytes / *_state_bytes query returns.
+ *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round-to-nearest-
+ *    even where the library produces them).  All matrices are row-major.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is enqueued
+ *    on it and the call returns without waiting, except where stated.
+ *  - Errors found on the host (null pointers, shapes, sizes, workspace too small,
+ *    invalid parameters) return a non-zero rf_status before anything is enqueued;
+ *    ridgefill_last_error() then gives a description.  A failed launch returns
+ *    RF_E_HIP.  Errors that only the device can see (an index out of range, a
+ *    non-increasing index list, a non-positive pivot) set bits in the status word
+ *    at the start of the workspace; ridgefill_read_status() returns them.  Rows whose
+ *    index is invalid are skipped: the library never writes outside the rows it was
+ *    given and never aborts.
+ *  - Calls that share a workspace or state buffer must not run concurrently.
+ */
+#ifndef RIDGEFILL_H
+#define RIDGEFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rf_status {
+  RF_OK = 0,
+  RF_E_INVALID = 1,      /* null pointer or invalid scalar parameter            */
+  RF_E_SHAPE = 2,        /* unsupported or inconsistent sizes                   */
+  RF_E_WORKSPACE = 3,    /* workspace / state buffer too small or mismatched    */
+  RF_E_HIP = 4,          /* a HIP runtime call or kernel launch failed          */
+  RF_E_NOT_SPD = 5,      /* device: X^T X + alpha I was not positive definite   */
+  RF_E_ROWS = 6,         /* device: an index was out of range or not increasing */
+  RF_E_UNSUPPORTED = 7   /* the requested variant is not built                  */
+} rf_status;
+
+/* Model shape shared by all layers of one fill call. */
+typedef struct rf_shape {
+  int32_t d;            /* hidden size; the map is d x d. Multiple of 256.          */
+  int32_t n_kv_heads;   /* KV heads; n_kv_heads * head_dim must be a multiple of 128 */
+  int32_t head_dim;     /* 64 or 128                                                 */
+  float rms_eps;        /* RMSNorm epsilon (inside the square root), >= 0            */
+  double rope_theta;    /* RoPE base, > 1                                            */
+} rf_shape;
+
+/* One upper layer l >= S.  Every pointer is a device pointer owned by the caller.   */
+typedef struct rf_layer {
+  const uint16_t* A;       /* bf16 [d][d]: x_hat = A x_S + b (A[out][in])             */
+  const float* b;          /* fp32 [d]                                                 */
+  const uint16_t* norm_w;  /* bf16 [d]: the layer's RMSNorm weight                     */
+  const uint16_t* W_K;     /* bf16 [n_kv_heads*head_dim][d]: key projection, no bias   */
+  const uint16_t* W_V;     /* bf16 [n_kv_heads*head_dim][d]: value projection, no bias */
+  uint16_t* k_pages;       /* bf16 [num_pages][page_size][n_kv_heads][head_dim]        */
+  uint16_t* v_pages;       /* bf16 [num_pages][page_size][n_kv_heads][head_dim]        */
+} rf_layer;
+
+/* Paged KV layout of one prompt, shared by every layer's k_pages / v_pages. */
+typedef struct rf_paged_kv {
+  const int32_t* block_table;   /* device int32 [n_logical]: logical page -> physical */
+  int64_t n_logical;            /* entries in block_table (>= ceil(N / page_size))    */
+  int32_t page_size;            /* rows per page, >= 1                                */
+  int32_t num_pages;            /* physical pages in each k_pages / v_pages pool      */
+} rf_paged_kv;
+
+/* ------------------------------------------------------------------------------
+ * Row partition.  Section "Method: ..." -> "Two numbers set the skip range": the last
+ * T rows are the tail; the other N - T rows are the prefix, and a prefix row is either
+ * exact or filled.  Host-only, integer, no GPU.
+ *
+ *   exact_mask  host uint8 [N - T]: nonzero marks an exact row (may be NULL = none)
+ *   filled_idx  host int32 [N - T] out: the filled rows in ascending order
+ *   n_filled    host out: their count (N - T - number of exact rows)
+ * Returns RF_E_SHAPE unless 0 <= T <= N and N - T fits in int32.
+ * ------------------------------------------------------------------------------ */
+rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
+                              int32_t* filled_idx, int64_t* n_filled);
+
+/* ------------------------------------------------------------------------------
+ * Fill.  Section "Ridge map: predict the input, and the original projection runs
+ * unchanged" (prediction equation, "own normalization and projections", Fig. 2):
+ * for every filled row t and every given upper layer l,
+ *     x_hat = A_l x_S[t] + b_l
+ *     h     = x_hat / sqrt(mean(x_hat^2) + eps) * norm_w_l
+ *     k     = RoPE_t(W_K,l h)   (pairs (j, j + head_dim/2), angle t * theta^(-2j/head_dim))
+ *     v     = W_V,l h
+ * and k, v are written to row t of layer l's paged cache (page block_table[t /
+ * page_size], slot t % page_size).  Nothing else in the caches is touched; with
+ * n_filled = 0 or n_layers = 0 only the status word is cleared (if ws is given).  Layers are independent; a caller that streams
+ * maps may call once per layer.
+ *
+ *   x_S         device bf16 [N][x_stride]: split-layer states of all prompt rows
+ *   filled_idx  device int32 [n_filled]: filled rows, strictly increasing, each
+ *               < N - T (the tail never receives a filled entry).  Violations set
+ *               RF_E_ROWS in the device status; out-of-range rows are skipped.
+ *   layers      host array [n_layers] of device-pointer descriptors
+ *   ws          device workspace of ws_bytes >= ridgefill_fill_workspace_bytes(shape,
+ *               n_filled, 1); a larger workspace (up to the value for n_layers) lets
+ *               more layers share one launch.  Its first 256 bytes hold the status.
+ * Computation: bf16 inputs, fp32 accumulation, x_hat and the RMS in fp32, one bf16
+ * rounding of x_hat * norm_w, one bf16 rounding of the stored k and v.
+ * ------------------------------------------------------------------------------ */
+size_t ridgefill_fill_workspace_bytes(const rf_shape* shape, int64_t n_filled,
+                                      int32_t n_layers);
+rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                         int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                         const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Calibration.  Same section, paragraph on alpha and the one-pass statistics: one pass
+ * accumulates X^T X, Y_l^T X and the two means; a new lambda needs only a new solve.
+ * The state belongs to one split (one x_S source) and is caller-owned device memory:
+ *   [0, 256)   header: int64 row count n, int32 d, int32 n_layers, magic
+ *   then       fp64 sum_t x_S          [d]
+ *              fp64 sum_t x_l          [n_layers][d]
+ *              fp32 sum_t x_S x_S^T    [d][d]   (lower triangle valid; i >= j)
+ *              fp32 sum_t x_l x_S^T    [n_layers][d][d]  (row = output feature of x_l)
+ * Saving the state is a device-to-host copy of ridgefill_calib_state_bytes() bytes.
+ *
+ * ridgefill_calib_reset clears the state for (d, n_layers); later calls on the state
+ * must pass the same d and n_layers (they size every access to it).
+ * ridgefill_calibrate adds n_rows rows: x_S device bf16 [n_rows][d]; x_l host array
+ * [n_layers] of device bf16 [n_rows][d] pointers.  Sums in fp32 per call and fp64
+ * across calls for the means; moments accumulated in fp32.  d: multiple of 256.
+ * ------------------------------------------------------------------------------ */
+size_t ridgefill_calib_state_bytes(int32_t d, int32_t n_layers);
+rf_status ridgefill_calib_reset(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                                void* stream);
+rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                              const uint16_t* x_S, const uint16_t* const* x_l, int64_t n_rows,
+                              void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Solve.  Same section, closed-form equation and the scale-free penalty: with
+ * mu = sums / n,  C = sum x_S x_S^T - n mu_S mu_S^T,  C_l = sum x_l x_S^T - n mu_l mu_S^T,
+ * alpha = lambda * tr(C) / d,
+ *     A_l = C_l (C + alpha I)^-1,     b_l = mu_l - A_l mu_S.
+ * (C + alpha I) is factored by a device Cholesky in fp64 and inverted in fp64; the
+ * product with C_l is an fp32 matrix-core GEMM.
+ *
+ *   A_out       device fp32 [n_layers][d][d] (may be NULL if A_bf16_out is given)
+ *   b_out       device fp32 [n_layers][d]
+ *   A_bf16_out  device bf16 [n_layers][d][d] or NULL: the map as the fill takes it
+ *   ws          device workspace >= ridgefill_solve_workspace_bytes(d, n_layers);
+ *               its first 256 bytes hold the status (RF_E_NOT_SPD on a bad pivot).
+ * lambda must be >= 0 and finite.  Repeated solves reuse the state unchanged.
+ * ------------------------------------------------------------------------------ */
+size_t ridgefill_solve_workspace_bytes(int32_t d, int32_t n_layers);
+rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                          double lambda, float* A_out, float* b_out, uint16_t* A_bf16_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Waits for `stream`, then returns the device status word of a fill or solve workspace
+ * (RF_OK, RF_E_ROWS, RF_E_NOT_SPD).  Each fill or solve call clears that word on the
+ * stream before its own kernels run, so the word reflects the last call only. */
+rf_status ridgefill_read_status(void* ws, void* stream);
+
+const char* ridgefill_status_string(rf_status s);
+/* Description of the last non-OK status returned on this thread ("" if none). */
+const char* ridgefill_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RIDGEFILL_H */

@@ -1,0 +1,200 @@
+"""Thin ctypes binding of libridgefill.so (C ABI in include/ridgefill.h).
+
+Argument marshalling only: every step of the fill, calibration and solve runs in the
+HIP library.  torch tensors supply device memory and the current stream.  There is no
+fallback: if the library is missing, `lib()` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libridgefill.so")
+
+RF_OK, RF_E_INVALID, RF_E_SHAPE, RF_E_WORKSPACE, RF_E_HIP, RF_E_NOT_SPD, RF_E_ROWS, \
+    RF_E_UNSUPPORTED = range(8)
+
+EXPORTED = [
+    "ridgefill_partition",
+    "ridgefill_fill_workspace_bytes",
+    "ridgefill_fill",
+    "ridgefill_calib_state_bytes",
+    "ridgefill_calib_reset",
+    "ridgefill_calibrate",
+    "ridgefill_solve_workspace_bytes",
+    "ridgefill_solve",
+    "ridgefill_read_status",
+    "ridgefill_status_string",
+    "ridgefill_last_error",
+]
+
+
+class RidgeFillError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ridgefill status {status}: {msg}")
+        self.status = status
+
+
+class rf_shape(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("rms_eps", C.c_float), ("rope_theta", C.c_double)]
+
+
+class rf_layer(C.Structure):
+    _fields_ = [("A", C.c_void_p), ("b", C.c_void_p), ("norm_w", C.c_void_p),
+                ("W_K", C.c_void_p), ("W_V", C.c_void_p), ("k_pages", C.c_void_p),
+                ("v_pages", C.c_void_p)]
+
+
+class rf_paged_kv(C.Structure):
+    _fields_ = [("block_table", C.c_void_p), ("n_logical", C.c_int64),
+                ("page_size", C.c_int32), ("num_pages", C.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m ridge_map_kv_amd.build` (there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    st = C.c_int
+    sig = {
+        "ridgefill_partition": (st, [i64, i64, vp, vp, C.POINTER(i64)]),
+        "ridgefill_fill_workspace_bytes": (sz, [C.POINTER(rf_shape), i64, i32]),
+        "ridgefill_fill": (st, [C.POINTER(rf_shape), vp, i64, i64, i64, vp, i64,
+                                C.POINTER(rf_layer), i32, C.POINTER(rf_paged_kv), vp, sz, vp]),
+        "ridgefill_calib_state_bytes": (sz, [i32, i32]),
+        "ridgefill_calib_reset": (st, [vp, sz, i32, i32, vp]),
+        "ridgefill_calibrate": (st, [vp, sz, i32, i32, vp, C.POINTER(vp), i64, vp]),
+        "ridgefill_solve_workspace_bytes": (sz, [i32, i32]),
+        "ridgefill_solve": (st, [vp, sz, i32, i32, C.c_double, vp, vp, vp, vp, sz, vp]),
+        "ridgefill_read_status": (st, [vp, vp]),
+        "ridgefill_status_string": (C.c_char_p, [st]),
+        "ridgefill_last_error": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != RF_OK:
+        msg = lib().ridgefill_last_error().decode() or lib().ridgefill_status_string(status).decode()
+        raise RidgeFillError(status, msg)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_shape(d: int, n_kv_heads: int, head_dim: int, rms_eps: float = 1e-5,
+               rope_theta: float = 500000.0) -> rf_shape:
+    return rf_shape(d, n_kv_heads, head_dim, rms_eps, rope_theta)
+
+
+# ------------------------------------------------------------------------------ partition
+
+def ridgefill_partition(N: int, T: int, exact_mask: np.ndarray | None) -> np.ndarray:
+    """Host row partition; returns the filled rows (int32, ascending)."""
+    P = max(int(N) - int(T), 0)
+    out = np.zeros(max(P, 1), dtype=np.int32)
+    n = C.c_int64(0)
+    m = None
+    if exact_mask is not None:
+        exact_mask = np.ascontiguousarray(exact_mask, dtype=np.uint8)
+        if exact_mask.size < P:
+            raise ValueError("exact_mask shorter than the prefix")
+        m = exact_mask.ctypes.data
+    _check(lib().ridgefill_partition(int(N), int(T), m, out.ctypes.data, C.byref(n)))
+    return out[: n.value].copy()
+
+
+# ------------------------------------------------------------------------------ fill
+
+def ridgefill_fill_workspace_bytes(shape: rf_shape, n_filled: int, n_layers: int) -> int:
+    return int(lib().ridgefill_fill_workspace_bytes(C.byref(shape), int(n_filled), int(n_layers)))
+
+
+def ridgefill_fill(shape: rf_shape, x_S, N: int, T: int, filled_idx, n_filled: int,
+                   layers: list[dict], block_table, page_size: int, num_pages: int,
+                   ws, x_stride: int | None = None, stream=None) -> None:
+    """layers: dicts with torch tensors A (bf16 [d][d]), b (fp32 [d]), norm_w (bf16 [d]),
+    W_K, W_V (bf16 [kv][d]), k_pages, v_pages (bf16 [num_pages][page_size][n_kv][hd])."""
+    arr = (rf_layer * max(len(layers), 1))()
+    for i, l in enumerate(layers):
+        arr[i] = rf_layer(_ptr(l["A"]), _ptr(l["b"]), _ptr(l["norm_w"]), _ptr(l["W_K"]),
+                          _ptr(l["W_V"]), _ptr(l["k_pages"]), _ptr(l["v_pages"]))
+    kv = rf_paged_kv(_ptr(block_table), int(block_table.numel()), int(page_size), int(num_pages))
+    stride = int(x_stride if x_stride is not None else x_S.stride(0))
+    _check(lib().ridgefill_fill(C.byref(shape), _ptr(x_S), int(N), int(T), stride,
+                                _ptr(filled_idx), int(n_filled), arr, len(layers), C.byref(kv),
+                                _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------ calibration
+
+def ridgefill_calib_state_bytes(d: int, n_layers: int) -> int:
+    return int(lib().ridgefill_calib_state_bytes(int(d), int(n_layers)))
+
+
+def _nbytes(t) -> int:
+    return int(t.numel() * t.element_size())
+
+
+def ridgefill_calib_reset(state, d: int, n_layers: int, stream=None) -> None:
+    _check(lib().ridgefill_calib_reset(_ptr(state), _nbytes(state), int(d), int(n_layers),
+                                       _stream(stream)))
+
+
+def ridgefill_calibrate(state, d: int, n_layers: int, x_S, x_l: list, n_rows: int | None = None,
+                        stream=None) -> None:
+    ptrs = (C.c_void_p * max(len(x_l), 1))(*[_ptr(t) for t in x_l])
+    n = int(n_rows if n_rows is not None else x_S.shape[0])
+    _check(lib().ridgefill_calibrate(_ptr(state), _nbytes(state), int(d), int(n_layers),
+                                     _ptr(x_S), ptrs, n, _stream(stream)))
+
+
+def ridgefill_solve_workspace_bytes(d: int, n_layers: int) -> int:
+    return int(lib().ridgefill_solve_workspace_bytes(int(d), int(n_layers)))
+
+
+def ridgefill_solve(state, d: int, n_layers: int, lam: float, A_out, b_out, A_bf16_out, ws,
+                    stream=None) -> None:
+    _check(lib().ridgefill_solve(_ptr(state), _nbytes(state), int(d), int(n_layers), float(lam),
+                                 _ptr(A_out), _ptr(b_out), _ptr(A_bf16_out), _ptr(ws),
+                                 _nbytes(ws), _stream(stream)))
+
+
+def ridgefill_read_status(ws, stream=None) -> int:
+    """Device status of the last fill/solve on this workspace (waits for the stream)."""
+    s = lib().ridgefill_read_status(_ptr(ws), _stream(stream))
+    if s not in (RF_OK, RF_E_ROWS, RF_E_NOT_SPD):
+        _check(s)
+    return int(s)
+
+
+def ridgefill_status_string(s: int) -> str:
+    return lib().ridgefill_status_string(int(s)).decode()

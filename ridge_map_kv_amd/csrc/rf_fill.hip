@@ -1,0 +1,426 @@
+// RidgeFill upper-layer KV fill on gfx950.
+//
+// Source of the computation: English RidgeFill review (jaehun.me), section "Ridge map:
+// predict the input, and the original projection runs unchanged" -- the prediction
+// equation x_hat = A x_S + b, and the predicted input passing through the layer's own
+// normalisation and key/value projections (Fig. 2).  Exact rows and the tail are not
+// given to these kernels ("Two numbers set the skip range").
+//
+// Two bf16 matrix-core GEMMs per upper layer, both "NT" (both operands contiguous along
+// the reduction axis):
+//   map   [token][feature]  x_hat = x_S[filled] * A^T + b   (M=features of A, N=tokens)
+//         epilogue: + b, per-row sum of squares over each 128-feature chunk (fp32,
+//         written to a small partials buffer), bf16(x_hat * norm_w) to the workspace.
+//   kv    [token][2*kv]     (x_hat*w) * [W_K; W_V]^T
+//         epilogue: * 1/sqrt(mean(x_hat^2)+eps) from the partials, RoPE on the key
+//         half in registers, bf16 store into the paged cache.
+// The weight rows sit on the MFMA M axis and the token rows on N, so in the 32x32 MFMA
+// result each lane holds one token and runs of four consecutive features: the row
+// reduction needs one cross-lane add, RoPE's pair (j, j + hd/2) sits in the same lane
+// and register of two MFMA blocks, and stores are 8-byte vectors.
+#include "rf_common.h"
+#include "rf_internal.h"
+
+namespace rf {
+
+namespace {
+
+constexpr int BK = 64;                          // reduction slice per LDS stage
+constexpr int kThreads = 256;                   // 4 waves: 2 (features) x 2 (tokens)
+constexpr int kOperandStage = kTile * BK * 2;   // 32 KB: 256 rows x 64 bf16
+constexpr int kStageBytes = 2 * kOperandStage;  // F and T operands
+constexpr int kLdsBytes = 2 * kStageBytes;      // double buffered: 128 KB
+constexpr int kTokGroup = 4;                    // token tiles walked together
+
+struct FillKArgs {
+  FillLayerPtrs L[kMaxGroup];
+  const uint16_t* xS;
+  int64_t x_stride;
+  const int32_t* idx;
+  int64_t P;
+  int n_filled;
+  int d, kv, hd;
+  float eps;
+  int mpad, nchunk;             // nchunk = d / 128 sum-of-squares partials per row
+  unsigned char* layer_ws;      // per layer: hbuf [mpad][d] bf16, then ssq [mpad][nchunk]
+  size_t per_layer, per_layer_h;
+  const float* rcos;
+  const float* rsin;
+  const int32_t* bt;
+  int64_t n_logical;
+  int ps, num_pages;
+  int ntt, nft;                 // token tiles, feature tiles of this launch
+};
+
+// Tile order: layer, then groups of kTokGroup token tiles, then feature tile, then the
+// token tile inside the group; combined with xcd_remap each XCD sweeps a few token tiles
+// against all feature tiles of one layer.
+__device__ __forceinline__ void decode_tile(int tile, int ntt, int nft, int& g, int& tt, int& ft) {
+  const int per_layer = ntt * nft;
+  g = tile / per_layer;
+  const int r = tile - g * per_layer;
+  const int tg = r / (kTokGroup * nft);
+  const int within = r - tg * kTokGroup * nft;
+  const int rows_left = ntt - tg * kTokGroup;
+  const int gsz = rows_left < kTokGroup ? rows_left : kTokGroup;
+  ft = within / gsz;
+  tt = tg * kTokGroup + (within - ft * gsz);
+}
+
+__device__ __forceinline__ void load_rows(u32x4 (&v)[8], const uint16_t* const (&rows)[8],
+                                          int k0) {
+#pragma unroll
+  for (int p = 0; p < 8; ++p) v[p] = *reinterpret_cast<const u32x4*>(rows[p] + k0);
+}
+
+__device__ __forceinline__ void store_rows(unsigned char* buf, const u32x4 (&v)[8], int rr, int c) {
+#pragma unroll
+  for (int p = 0; p < 8; ++p) *reinterpret_cast<u32x4*>(buf + lds_off128(rr + 32 * p, c)) = v[p];
+}
+
+// One BK slice of the 256x256 tile: each wave multiplies its 128 features x 128 tokens.
+__device__ __forceinline__ void mma_slice(f32x16 (&acc)[4][4], const unsigned char* Fs,
+                                          const unsigned char* Ts, int wf, int wt, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int c = kk * 2 + (lane >> 5);
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      a[m] = *reinterpret_cast<const bf16x8*>(Fs + lds_off128(wf * 128 + m * 32 + (lane & 31), c));
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      b[n] = *reinterpret_cast<const bf16x8*>(Ts + lds_off128(wt * 128 + n * 32 + (lane & 31), c));
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
+  }
+}
+
+// acc[m][n] += F[256 x K] * T[256 x K]^T; fr/tr: this thread's 8 row pointers of each
+// operand, already offset by its 16-byte chunk.
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const uint16_t* const (&fr)[8],
+                                              const uint16_t* const (&tr)[8], int K,
+                                              unsigned char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wf = wave >> 1, wt = wave & 1, rr = tid >> 3, c = tid & 7;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+
+  u32x4 vf[8], vt[8];
+  load_rows(vf, fr, 0);
+  load_rows(vt, tr, 0);
+  store_rows(smem, vf, rr, c);
+  store_rows(smem + kOperandStage, vt, rr, c);
+  __syncthreads();
+  const int nk = K / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const unsigned char* cur = smem + (kt & 1) * kStageBytes;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      load_rows(vf, fr, (kt + 1) * BK);
+      load_rows(vt, tr, (kt + 1) * BK);
+    }
+    mma_slice(acc, cur, cur + kOperandStage, wf, wt, lane);
+    if (more) {
+      unsigned char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
+      store_rows(nxt, vf, rr, c);
+      store_rows(nxt + kOperandStage, vt, rr, c);
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ float lo16(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
+__device__ __forceinline__ float hi16(uint32_t x) { return bf16_to_f32(x >> 16); }
+
+__global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  int g, tt, ft;
+  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  const FillLayerPtrs Lp = a.L[g];
+  const int t0 = tt * kTile, f0 = ft * kTile;
+  const int tid = threadIdx.x, rr = tid >> 3, c = tid & 7;
+
+  const uint16_t* fr[8];
+  const uint16_t* tr[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    fr[p] = Lp.A + (size_t)(f0 + rr + 32 * p) * a.d + c * 8;
+    const int tok = t0 + rr + 32 * p;
+    int row = 0;
+    if (tok < a.n_filled) {
+      const int t = a.idx[tok];
+      if (t >= 0 && t < a.P) row = t;
+    }
+    tr[p] = a.xS + (size_t)row * a.x_stride + c * 8;
+  }
+
+  f32x16 acc[4][4];
+  gemm_mainloop(acc, fr, tr, a.d, smem);
+
+  const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+  uint16_t* hb = reinterpret_cast<uint16_t*>(a.layer_ws + g * a.per_layer);
+  float* ssq = reinterpret_cast<float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = f0 + wf * 128 + m * 32 + q * 8 + h * 4;
+      const f32x4 bias = *reinterpret_cast<const f32x4*>(Lp.b + f);
+      const u32x2 wb = *reinterpret_cast<const u32x2*>(Lp.w + f);
+      const float w0 = lo16(wb.x), w1 = hi16(wb.x), w2 = lo16(wb.y), w3 = hi16(wb.y);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
+        const float v0 = acc[m][n][q * 4 + 0] + bias.x;
+        const float v1 = acc[m][n][q * 4 + 1] + bias.y;
+        const float v2 = acc[m][n][q * 4 + 2] + bias.z;
+        const float v3 = acc[m][n][q * 4 + 3] + bias.w;
+        ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+        u32x2 o;
+        o.x = pack_bf16x2(v0 * w0, v1 * w1);
+        o.y = pack_bf16x2(v2 * w2, v3 * w3);
+        *reinterpret_cast<u32x2*>(hb + (size_t)tok * a.d + f) = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) ss[n] += __shfl_xor(ss[n], 32);
+  if (h == 0) {
+    const int chunk = (f0 + wf * 128) >> 7;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
+      ssq[(size_t)tok * a.nchunk + chunk] = ss[n];
+    }
+  }
+}
+
+// RoPE on one pair of 32-feature MFMA blocks (mlo holds pair index j, mhi holds j + hd/2).
+template <int MLO, int MHI, int JOFF>
+__device__ __forceinline__ void rope_pair(f32x16 (&acc)[4][4], int n, const float* cs,
+                                          const float* sn, int h) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = JOFF + q * 8 + h * 4;
+    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + j);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = acc[MLO][n][q * 4 + e], hi = acc[MHI][n][q * 4 + e];
+      acc[MLO][n][q * 4 + e] = lo * cv[e] - hi * sv[e];
+      acc[MHI][n][q * 4 + e] = hi * cv[e] + lo * sv[e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  int g, tt, ft;
+  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  const FillLayerPtrs Lp = a.L[g];
+  const int t0 = tt * kTile, f0 = ft * kTile;
+  const int tid = threadIdx.x, rr = tid >> 3, c = tid & 7;
+  const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.layer_ws + g * a.per_layer);
+  const float* ssq = reinterpret_cast<const float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
+
+  const uint16_t* fr[8];
+  const uint16_t* tr[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int f = f0 + rr + 32 * p;
+    fr[p] = (f < a.kv ? Lp.WK + (size_t)f * a.d : Lp.WV + (size_t)(f - a.kv) * a.d) + c * 8;
+    tr[p] = hb + (size_t)(t0 + rr + 32 * p) * a.d + c * 8;
+  }
+
+  f32x16 acc[4][4];
+  gemm_mainloop(acc, fr, tr, a.d, smem);
+
+  // 1/sqrt(mean(x_hat^2) + eps) of the tile's 256 tokens, from the map kernel's partials.
+  float* rs = reinterpret_cast<float*>(smem);
+  {
+    const float* p = ssq + (size_t)(t0 + tid) * a.nchunk;
+    float s = 0.f;
+    for (int i = 0; i < a.nchunk; ++i) s += p[i];
+    rs[tid] = 1.0f / sqrtf(s / (float)a.d + a.eps);
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+  const int fw = f0 + wf * 128;                  // first feature of this wave in [K | V]
+  const bool isK = fw < a.kv;                    // kv % 128 == 0: a wave is all K or all V
+  const int fo = isK ? fw : fw - a.kv;
+  uint16_t* base = isK ? Lp.kp : Lp.vp;
+  const int half = a.hd >> 1;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int tl = wt * 128 + n * 32 + (lane & 31);
+    const int tok = t0 + tl;
+    bool ok = tok < a.n_filled;
+    int64_t dst = 0;
+    if (ok) {
+      const int t = a.idx[tok];
+      ok = t >= 0 && t < a.P;
+      if (ok) {
+        const int64_t lp = t / a.ps;
+        ok = lp < a.n_logical;
+        if (ok) {
+          const int pg = a.bt[lp];
+          ok = pg >= 0 && pg < a.num_pages;
+          dst = ((int64_t)pg * a.ps + (t - lp * a.ps)) * a.kv + fo;
+        }
+      }
+    }
+    const float r = rs[tl];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[m][n][e] *= r;
+    if (isK) {
+      const int tc = tok < a.n_filled ? tok : a.n_filled - 1;
+      const float* cs = a.rcos + (size_t)tc * half;
+      const float* sn = a.rsin + (size_t)tc * half;
+      if (a.hd == 128) {
+        rope_pair<0, 2, 0>(acc, n, cs, sn, h);
+        rope_pair<1, 3, 32>(acc, n, cs, sn, h);
+      } else {
+        rope_pair<0, 1, 0>(acc, n, cs, sn, h);
+        rope_pair<2, 3, 0>(acc, n, cs, sn, h);
+      }
+    }
+    if (ok) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u32x2 o;
+          o.x = pack_bf16x2(acc[m][n][q * 4 + 0], acc[m][n][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[m][n][q * 4 + 2], acc[m][n][q * 4 + 3]);
+          *reinterpret_cast<u32x2*>(base + dst + m * 32 + q * 8 + h * 4) = o;
+        }
+    }
+  }
+}
+
+// cos/sin of angle t * theta^(-2j/hd) for every filled row, computed in fp64.
+__global__ void rope_table_kernel(const int32_t* idx, int n_filled, int64_t P, int hd,
+                                  double theta, float* rcos, float* rsin) {
+  const int half = hd >> 1;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_filled * half) return;
+  const int tok = (int)(i / half), j = (int)(i - (int64_t)tok * half);
+  int t = idx[tok];
+  if (t < 0 || t >= P) t = 0;
+  const double inv = pow(theta, -2.0 * (double)j / (double)hd);
+  double s, cth;
+  sincos((double)t * inv, &s, &cth);
+  rcos[i] = (float)cth;
+  rsin[i] = (float)s;
+}
+
+// Flags filled-row indices that are out of the prefix, not strictly increasing, or whose
+// page is missing from the block table.
+__global__ void validate_rows_kernel(const int32_t* idx, int n_filled, int64_t P,
+                                     const int32_t* bt, int64_t n_logical, int ps,
+                                     int num_pages, unsigned* status) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_filled) return;
+  const int t = idx[i];
+  bool bad = t < 0 || t >= P;
+  if (!bad && i > 0 && idx[i - 1] >= t) bad = true;
+  if (!bad) {
+    const int64_t lp = t / ps;
+    if (lp >= n_logical) {
+      bad = true;
+    } else {
+      const int pg = bt[lp];
+      bad = pg < 0 || pg >= num_pages;
+    }
+  }
+  if (bad) atomicOr(status, kStatusRowsBit);
+}
+
+}  // namespace
+
+__global__ void clear_status_kernel(unsigned* status) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
+}
+
+hipError_t launch_clear_status(unsigned* status, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, stream, status);
+  return hipGetLastError();
+}
+
+FillWsLayout fill_ws_layout(int d, int hd, int64_t n_filled) {
+  FillWsLayout L;
+  const int64_t mpad = (n_filled + kTile - 1) / kTile * kTile;
+  const size_t table = align256((size_t)n_filled * (hd / 2) * sizeof(float));
+  L.rope_cos = kStatusBytes;
+  L.rope_sin = L.rope_cos + table;
+  L.fixed = L.rope_sin + table;
+  L.per_layer_h = align256((size_t)mpad * d * 2);
+  L.per_layer_ssq = align256((size_t)mpad * (d / 128) * sizeof(float));
+  L.per_layer = L.per_layer_h + L.per_layer_ssq;
+  L.hbuf = L.fixed;
+  L.ssq_off = L.fixed + L.per_layer_h;
+  return L;
+}
+
+hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_layers,
+                       hipStream_t stream) {
+  hipError_t e = launch_clear_status(p.status, stream);
+  if (e != hipSuccess) return e;
+  const int nb = (p.n_filled + 255) / 256;
+  hipLaunchKernelGGL(validate_rows_kernel, dim3(nb), dim3(256), 0, stream, p.idx, p.n_filled,
+                     (int64_t)p.P, p.block_table, p.n_logical, p.page_size, p.num_pages,
+                     p.status);
+  const int64_t nt = (int64_t)p.n_filled * (p.hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream,
+                     p.idx, p.n_filled, (int64_t)p.P, p.hd, p.theta, p.rope_cos, p.rope_sin);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  FillKArgs a = {};
+  a.xS = p.xS;
+  a.x_stride = p.x_stride;
+  a.idx = p.idx;
+  a.P = p.P;
+  a.n_filled = p.n_filled;
+  a.d = p.d;
+  a.kv = p.kv;
+  a.hd = p.hd;
+  a.eps = p.eps;
+  a.mpad = p.mpad;
+  a.nchunk = p.d / 128;
+  a.layer_ws = reinterpret_cast<unsigned char*>(p.hbuf);
+  const FillWsLayout L = fill_ws_layout(p.d, p.hd, p.n_filled);
+  a.per_layer = L.per_layer;
+  a.per_layer_h = L.per_layer_h;
+  a.rcos = p.rope_cos;
+  a.rsin = p.rope_sin;
+  a.bt = p.block_table;
+  a.n_logical = p.n_logical;
+  a.ps = p.page_size;
+  a.num_pages = p.num_pages;
+  a.ntt = p.mpad / kTile;
+
+  for (int l0 = 0; l0 < n_layers; l0 += p.group) {
+    const int G = (n_layers - l0) < p.group ? (n_layers - l0) : p.group;
+    for (int g = 0; g < G; ++g) a.L[g] = layers[l0 + g];
+    a.nft = p.d / kTile;
+    hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    a.nft = 2 * p.kv / kTile;
+    hipLaunchKernelGGL(fill_kv_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rf

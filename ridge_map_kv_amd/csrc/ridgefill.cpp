@@ -1,0 +1,273 @@
+// C ABI of the RidgeFill library: argument checks, workspace carve-up, the host row
+// partition and status reporting.  Device work is in rf_fill.hip, rf_calib.hip and
+// rf_solve.hip.
+#include "ridgefill.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "rf_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rf_status fail(rf_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rf_status fail(rf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+rf_status ok() {
+  g_last_error.clear();
+  return RF_OK;
+}
+
+rf_status hip_fail(hipError_t e, const char* what) {
+  return fail(RF_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+rf_status check_shape(const rf_shape* s) {
+  if (!s) return fail(RF_E_INVALID, "shape is NULL");
+  if (s->d < rf::kTile || s->d % rf::kTile)
+    return fail(RF_E_SHAPE, "d = %d must be a positive multiple of %d", s->d, rf::kTile);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RF_E_SHAPE, "head_dim = %d must be 64 or 128", s->head_dim);
+  if (s->n_kv_heads < 1) return fail(RF_E_SHAPE, "n_kv_heads = %d must be >= 1", s->n_kv_heads);
+  const int64_t kv = (int64_t)s->n_kv_heads * s->head_dim;
+  if (kv % 128) return fail(RF_E_SHAPE, "n_kv_heads * head_dim = %lld must be a multiple of 128",
+                            (long long)kv);
+  if (kv > (1 << 20)) return fail(RF_E_SHAPE, "n_kv_heads * head_dim too large");
+  if (!(s->rms_eps >= 0.f) || !std::isfinite(s->rms_eps))
+    return fail(RF_E_INVALID, "rms_eps must be finite and >= 0");
+  if (!(s->rope_theta > 1.0) || !std::isfinite(s->rope_theta))
+    return fail(RF_E_INVALID, "rope_theta must be finite and > 1");
+  return RF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ridgefill_status_string(rf_status s) {
+  switch (s) {
+    case RF_OK: return "ok";
+    case RF_E_INVALID: return "invalid argument";
+    case RF_E_SHAPE: return "unsupported or inconsistent shape";
+    case RF_E_WORKSPACE: return "workspace or state buffer too small or mismatched";
+    case RF_E_HIP: return "HIP runtime error";
+    case RF_E_NOT_SPD: return "X^T X + alpha I is not positive definite";
+    case RF_E_ROWS: return "filled-row index out of range or not strictly increasing";
+    case RF_E_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* ridgefill_last_error(void) { return g_last_error.c_str(); }
+
+rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
+                              int32_t* filled_idx, int64_t* n_filled) {
+  if (N < 0 || T < 0 || T > N) return fail(RF_E_SHAPE, "need 0 <= T <= N (N=%lld, T=%lld)",
+                                          (long long)N, (long long)T);
+  const int64_t P = N - T;
+  if (P > INT32_MAX) return fail(RF_E_SHAPE, "prefix of %lld rows exceeds int32", (long long)P);
+  if (!n_filled) return fail(RF_E_INVALID, "n_filled is NULL");
+  if (P > 0 && !filled_idx) return fail(RF_E_INVALID, "filled_idx is NULL");
+  int64_t k = 0;
+  for (int64_t t = 0; t < P; ++t)
+    if (!exact_mask || exact_mask[t] == 0) filled_idx[k++] = (int32_t)t;
+  *n_filled = k;
+  return ok();
+}
+
+size_t ridgefill_fill_workspace_bytes(const rf_shape* shape, int64_t n_filled, int32_t n_layers) {
+  if (check_shape(shape) != RF_OK || n_filled < 0 || n_layers < 1) return 0;
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, shape->head_dim, n_filled);
+  const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
+  return L.fixed + (size_t)g * L.per_layer;
+}
+
+rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                         int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                         const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
+                         void* ws, size_t ws_bytes, void* stream) {
+  rf_status s = check_shape(shape);
+  if (s != RF_OK) return s;
+  if (N < 0 || T < 0 || T > N) return fail(RF_E_SHAPE, "need 0 <= T <= N");
+  const int64_t P = N - T;
+  if (n_filled < 0 || n_filled > P)
+    return fail(RF_E_SHAPE, "n_filled = %lld must be in [0, N - T = %lld]", (long long)n_filled,
+                (long long)P);
+  if (n_filled > INT32_MAX - rf::kTile) return fail(RF_E_SHAPE, "n_filled too large");
+  if (n_layers < 0) return fail(RF_E_INVALID, "n_layers < 0");
+  if (n_filled == 0 || n_layers == 0) {
+    if (ws) {
+      if (!aligned(ws, 256) || ws_bytes < rf::kStatusBytes)
+        return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned and >= 256 bytes");
+      hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws),
+                                             static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "status clear");
+    }
+    return ok();
+  }
+  if (!x_S || !filled_idx || !layers || !kv || !ws)
+    return fail(RF_E_INVALID, "null pointer among x_S, filled_idx, layers, kv, ws");
+  if (x_stride < shape->d) return fail(RF_E_SHAPE, "x_stride < d");
+  if (x_stride % 8 || !aligned(x_S, 16))
+    return fail(RF_E_SHAPE, "x_S must be 16-byte aligned with x_stride a multiple of 8");
+  if (!kv->block_table || kv->page_size < 1 || kv->num_pages < 1 || kv->n_logical < 1)
+    return fail(RF_E_INVALID, "paged layout: block_table, page_size, num_pages, n_logical");
+  if (kv->n_logical < (P + kv->page_size - 1) / kv->page_size)
+    return fail(RF_E_SHAPE, "block table has %lld pages, the prefix needs %lld",
+                (long long)kv->n_logical, (long long)((P + kv->page_size - 1) / kv->page_size));
+  if (!aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned");
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    if (!l.A || !l.b || !l.norm_w || !l.W_K || !l.W_V || !l.k_pages || !l.v_pages)
+      return fail(RF_E_INVALID, "layer %d has a null pointer", i);
+    if (!aligned(l.A, 16) || !aligned(l.b, 16) || !aligned(l.norm_w, 8) || !aligned(l.W_K, 16) ||
+        !aligned(l.W_V, 16) || !aligned(l.k_pages, 8) || !aligned(l.v_pages, 8))
+      return fail(RF_E_SHAPE, "layer %d: A, b, W_K, W_V need 16-byte, norm_w and the pages "
+                  "8-byte alignment", i);
+  }
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, shape->head_dim, n_filled);
+  if (ws_bytes < L.fixed + L.per_layer)
+    return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed for one layer", ws_bytes,
+                L.fixed + L.per_layer);
+  size_t group = (ws_bytes - L.fixed) / L.per_layer;
+  if (group > (size_t)rf::kMaxGroup) group = rf::kMaxGroup;
+
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  rf::FillPlan p = {};
+  p.d = shape->d;
+  p.n_kv = shape->n_kv_heads;
+  p.hd = shape->head_dim;
+  p.kv = shape->n_kv_heads * shape->head_dim;
+  p.eps = shape->rms_eps;
+  p.theta = shape->rope_theta;
+  p.xS = x_S;
+  p.x_stride = x_stride;
+  p.N = N;
+  p.P = P;
+  p.idx = filled_idx;
+  p.n_filled = (int)n_filled;
+  p.mpad = (int)((n_filled + rf::kTile - 1) / rf::kTile * rf::kTile);
+  p.block_table = kv->block_table;
+  p.n_logical = kv->n_logical;
+  p.page_size = kv->page_size;
+  p.num_pages = kv->num_pages;
+  p.status = reinterpret_cast<unsigned*>(w);
+  p.rope_cos = reinterpret_cast<float*>(w + L.rope_cos);
+  p.rope_sin = reinterpret_cast<float*>(w + L.rope_sin);
+  p.hbuf = reinterpret_cast<uint16_t*>(w + L.hbuf);
+  p.ssq = reinterpret_cast<float*>(w + L.ssq_off);
+  p.group = (int)group;
+
+  std::vector<rf::FillLayerPtrs> lp((size_t)n_layers);
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.k_pages, l.v_pages};
+  }
+  hipError_t e = rf::launch_fill(p, lp.data(), n_layers, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  return ok();
+}
+
+size_t ridgefill_calib_state_bytes(int32_t d, int32_t n_layers) {
+  if (d < rf::kTile || d % rf::kTile || n_layers < 1) return 0;
+  return rf::calib_layout(d, n_layers).total;
+}
+
+static rf_status check_state(const void* state, size_t bytes, int d, int n_layers) {
+  if (!state) return fail(RF_E_INVALID, "state is NULL");
+  if (!aligned(state, 256)) return fail(RF_E_WORKSPACE, "state must be 256-byte aligned");
+  if (d < rf::kTile || d % rf::kTile)
+    return fail(RF_E_SHAPE, "d = %d must be a positive multiple of %d", d, rf::kTile);
+  if (n_layers < 1 || n_layers > 4096) return fail(RF_E_SHAPE, "n_layers = %d", n_layers);
+  if (bytes < rf::calib_layout(d, n_layers).total)
+    return fail(RF_E_WORKSPACE, "state %zu bytes < %zu needed", bytes,
+                rf::calib_layout(d, n_layers).total);
+  return RF_OK;
+}
+
+rf_status ridgefill_calib_reset(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                                void* stream) {
+  rf_status s = check_state(state, state_bytes, d, n_layers);
+  if (s != RF_OK) return s;
+  hipError_t e = rf::launch_calib_reset(state, d, n_layers, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "calibration reset");
+  return ok();
+}
+
+rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                              const uint16_t* x_S, const uint16_t* const* x_l, int64_t n_rows,
+                              void* stream) {
+  rf_status s = check_state(state, state_bytes, d, n_layers);
+  if (s != RF_OK) return s;
+  if (n_rows < 0 || n_rows > INT32_MAX) return fail(RF_E_SHAPE, "n_rows out of range");
+  if (n_rows == 0) return ok();
+  if (!x_S || !x_l) return fail(RF_E_INVALID, "x_S or x_l is NULL");
+  if (!aligned(x_S, 16)) return fail(RF_E_SHAPE, "x_S must be 16-byte aligned");
+  for (int l = 0; l < n_layers; ++l)
+    if (!x_l[l] || !aligned(x_l[l], 16))
+      return fail(RF_E_INVALID, "x_l[%d] is NULL or not 16-byte aligned", l);
+  hipError_t e = rf::launch_calibrate(state, d, n_layers, x_S, x_l, n_rows,
+                                      static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(RF_E_UNSUPPORTED, "calibration kernels not built");
+  if (e != hipSuccess) return hip_fail(e, "calibration launch");
+  return ok();
+}
+
+size_t ridgefill_solve_workspace_bytes(int32_t d, int32_t n_layers) {
+  if (d < rf::kTile || d % rf::kTile || n_layers < 1) return 0;
+  return rf::solve_layout(d, n_layers).total;
+}
+
+rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                          double lambda, float* A_out, float* b_out, uint16_t* A_bf16_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  rf_status s = check_state(state, state_bytes, d, n_layers);
+  if (s != RF_OK) return s;
+  if (!(lambda >= 0.0) || !std::isfinite(lambda))
+    return fail(RF_E_INVALID, "lambda must be finite and >= 0");
+  if (!b_out || (!A_out && !A_bf16_out))
+    return fail(RF_E_INVALID, "b_out and at least one of A_out, A_bf16_out are required");
+  if ((A_out && !aligned(A_out, 16)) || !aligned(b_out, 16) || (A_bf16_out && !aligned(A_bf16_out, 16)))
+    return fail(RF_E_SHAPE, "outputs must be 16-byte aligned");
+  if (!ws || !aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < rf::solve_layout(d, n_layers).total)
+    return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes,
+                rf::solve_layout(d, n_layers).total);
+  hipError_t e = rf::launch_solve(state, d, n_layers, lambda, A_out, b_out, A_bf16_out, ws,
+                                  static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(RF_E_UNSUPPORTED, "solve kernels not built");
+  if (e != hipSuccess) return hip_fail(e, "solve launch");
+  return ok();
+}
+
+rf_status ridgefill_read_status(void* ws, void* stream) {
+  if (!ws) return fail(RF_E_INVALID, "workspace is NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  unsigned word = 0;
+  e = hipMemcpy(&word, ws, sizeof word, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "status read");
+  if (word & rf::kStatusRowsBit) return fail(RF_E_ROWS, "device flagged filled-row indices");
+  if (word & rf::kStatusNotSpdBit) return fail(RF_E_NOT_SPD, "device flagged a non-positive pivot");
+  return ok();
+}
+
+}  // extern "C"
