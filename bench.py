@@ -1,0 +1,216 @@
+"""Benchmark of the RidgeFill fill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-calib]
+
+One step is one ridgefill_fill call over every upper layer of the Llama-3.1-8B-shaped
+workload (d = 4096, layers 12..31, 8 KV heads x 128, N = 32768, T = 4096, 10% of the
+prefix exact: 25,805 filled rows), with every input already in HBM.  The partition of
+the rows is done once beforehand (it is the routing input).  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_fill_inputs(cfg, dev, maps=None):
+    import torch
+    from ridge_map_kv_amd import binding as B
+    from ridge_map_kv_amd import synth
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    d, kv = cfg.d, cfg.kv
+    xS = torch.randn((cfg.N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    filled = B.ridgefill_partition(cfg.N, cfg.T, synth.exact_mask(cfg))
+    idx = torch.from_numpy(filled).to(dev)
+    table_np, num_pages = synth.block_table(cfg.N, cfg.page_size, cfg.seed)
+    table = torch.from_numpy(table_np).to(dev)
+    layers = []
+    s = 1.0 / np.sqrt(d)
+    for l in range(cfg.n_upper):
+        if maps is not None:
+            A, b = maps[l]
+        else:
+            U = torch.randn((d, 64), generator=g, device=dev) * s
+            V = torch.randn((d, 64), generator=g, device=dev) * s
+            A = (torch.eye(d, device=dev) + 0.5 * (U @ V.T)).to(torch.bfloat16)
+            b = torch.randn(d, generator=g, device=dev)
+        w = (1.0 + 0.1 * torch.randn(d, generator=g, device=dev)).to(torch.bfloat16)
+        WK = (torch.randn((kv, d), generator=g, device=dev) * s).to(torch.bfloat16)
+        WV = (torch.randn((kv, d), generator=g, device=dev) * s).to(torch.bfloat16)
+        pages = (num_pages, cfg.page_size, cfg.n_kv, cfg.head_dim)
+        layers.append(dict(A=A.contiguous(), b=b.float().contiguous(), norm_w=w, W_K=WK, W_V=WV,
+                           k_pages=torch.zeros(pages, dtype=torch.bfloat16, device=dev),
+                           v_pages=torch.zeros(pages, dtype=torch.bfloat16, device=dev)))
+    shape = B.make_shape(d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
+    ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, len(filled), cfg.n_upper),
+                     dtype=torch.uint8, device=dev)
+    return dict(xS=xS, filled=filled, idx=idx, table=table, table_np=table_np,
+                num_pages=num_pages, layers=layers, shape=shape, ws=ws)
+
+
+def fill_step(cfg, inp):
+    from ridge_map_kv_amd import binding as B
+    B.ridgefill_fill(inp["shape"], inp["xS"], cfg.N, cfg.T, inp["idx"], len(inp["filled"]),
+                     inp["layers"], inp["table"], cfg.page_size, inp["num_pages"], inp["ws"])
+
+
+def cpu_baseline_fill(cfg, inp, budget_s: float = 15.0):
+    """The oracle, as it stands, on a bounded sample of filled rows over every upper layer."""
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    def np64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    filled = inp["filled"]
+    rng = np.random.default_rng(cfg.seed)
+    layers = inp["layers"]
+
+    def layer_np(l):
+        L = layers[l]
+        return (np64(L["A"]), L["b"].cpu().numpy().astype(np.float64), np64(L["norm_w"]),
+                np64(L["W_K"]), np64(L["W_V"]))
+
+    # size the sample from a short probe on the first layer (the first call warms up BLAS)
+    probe = np.sort(rng.choice(filled, size=256, replace=False))
+    xs = np64(inp["xS"][torch.from_numpy(probe.astype(np.int64)).to(inp["xS"].device)])
+    A, b, w, WK, WV = layer_np(0)
+    for _ in range(2):
+        t0 = time.perf_counter()
+        oracle.fill_rows(xs, probe, A, b, w, WK, WV, eps=cfg.rms_eps, theta=cfg.rope_theta,
+                         n_kv=cfg.n_kv, hd=cfg.head_dim)
+        per_row_layer = (time.perf_counter() - t0) / len(probe)
+    n_rows = int(np.clip(budget_s / (per_row_layer * cfg.n_upper), 64, len(filled)))
+    rows = np.sort(rng.choice(filled, size=n_rows, replace=False))
+    xs = np64(inp["xS"][torch.from_numpy(rows.astype(np.int64)).to(inp["xS"].device)])
+    spent = 0.0
+    for l in range(cfg.n_upper):
+        A, b, w, WK, WV = layer_np(l)
+        t0 = time.perf_counter()
+        oracle.fill_rows(xs, rows, A, b, w, WK, WV, eps=cfg.rms_eps, theta=cfg.rope_theta,
+                         n_kv=cfg.n_kv, hd=cfg.head_dim)
+        spent += time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                  or [1])
+    return {"value": n_rows / spent, "unit": "filled rows/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_rows} seeded filled rows x {cfg.n_upper} upper layers of the same "
+                      f"workload (NumPy float64), {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fill shards by layer with one broadcast of "
+              "the filled split-layer states, and no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ridge_map_kv_amd import binding as B
+    from ridge_map_kv_amd import configs
+
+    B.lib()
+    dev = torch.device("cuda:0")
+    cfg = configs.LLAMA8B
+    log(f"bench: building {cfg.name} fill inputs")
+    inp = make_fill_inputs(cfg, dev)
+    nf = len(inp["filled"])
+    assert nf == cfg.n_filled
+
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        fill_step(cfg, inp)
+    torch.cuda.synchronize()
+    st = B.ridgefill_read_status(inp["ws"])
+    if st != B.RF_OK:
+        raise SystemExit(f"fill reported device status {st}")
+
+    B.ridgefill_profile_reset()
+    B.ridgefill_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fill_step(cfg, inp)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.ridgefill_profile_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    map_n, map_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_MAP)
+    kv_n, kv_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_KV)
+    log(f"bench: {ms_step:.3f} ms/step; map {map_n} launches {map_ms / map_n:.3f} ms; "
+        f"kv {kv_n} launches {kv_ms / kv_n:.3f} ms")
+
+    flops_total = cfg.fill_flops()
+    launches_per_step = map_n // args.steps
+    map_flops_launch = 2.0 * cfg.d * cfg.d * nf * cfg.n_upper / launches_per_step
+    kv_flops_launch = 2.0 * 2 * cfg.kv * cfg.d * nf * cfg.n_upper / launches_per_step
+    map_avg = map_ms / map_n
+    kv_avg = kv_ms / kv_n
+    achieved = map_flops_launch / (map_avg * 1e-3) / 1e12
+    rows_per_s = nf / (ms_step * 1e-3)
+
+    out = {
+        "metric": "filled prefix rows/sec over all upper layers (8B shape) + % bf16 MFMA peak",
+        "value": rows_per_s,
+        "unit": "filled rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_bf16_mfma_peak": 100.0 * flops_total / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "config": {"workload": "llama3.1-8b-shaped fill", "d": cfg.d, "upper_layers": cfg.n_upper,
+                   "split": cfg.S, "layers": cfg.L, "n_kv_heads": cfg.n_kv,
+                   "head_dim": cfg.head_dim, "N": cfg.N, "T": cfg.T, "filled_rows": nf,
+                   "exact_rows": cfg.exact_count, "page_size": cfg.page_size,
+                   "maps": "synthetic near-identity bf16 maps",
+                   "fill_tflop_per_step": flops_total / 1e12},
+        "roofline": {"bound": "mfma", "kernel": "fill_map_kernel",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "launch_ms": map_avg, "flop_per_launch": map_flops_launch},
+        "kernels": {
+            "fill_map_kernel": {"avg_ms": map_avg, "launches": map_n,
+                                "tflops": achieved},
+            "fill_kv_kernel": {"avg_ms": kv_avg, "launches": kv_n,
+                               "tflops": kv_flops_launch / (kv_avg * 1e-3) / 1e12},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_fill(cfg, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,6 +168,26 @@ rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int3
  * stream before its own kernels run, so the word reflects the last call only. */
 rf_status ridgefill_read_status(void* ws, void* stream);
 
+/* ------------------------------------------------------------------------------
+ * Kernel timing for measurement.  While enabled, every compute-kernel launch of the
+ * library is bracketed by a pair of HIP events recorded on the caller's stream (no
+ * synchronisation is added).  ridgefill_profile_read waits for the recorded events and
+ * returns, for one kernel, the launches seen since the last reset and their summed
+ * duration in milliseconds.  Host-side only; thread safe.
+ * ------------------------------------------------------------------------------ */
+typedef enum rf_kernel_id {
+  RF_KERNEL_FILL_MAP = 0,      /* map GEMM: x_hat = A x_S + b, RMS partials, x_hat * w   */
+  RF_KERNEL_FILL_KV = 1,       /* K/V GEMM: RMS scale, RoPE, paged store                 */
+  RF_KERNEL_CALIB_GRAM = 2,    /* calibration: sum x_S x_S^T (lower triangle)           */
+  RF_KERNEL_CALIB_CROSS = 3,   /* calibration: sum x_l x_S^T for every layer             */
+  RF_KERNEL_CALIB_SUMS = 4,    /* calibration: column sums                                */
+  RF_KERNEL_SOLVE_MAP = 5,     /* solve: A_l = C_l (C + alpha I)^-1 product              */
+  RF_KERNEL_COUNT = 6
+} rf_kernel_id;
+rf_status ridgefill_profile_enable(int32_t enable);
+rf_status ridgefill_profile_read(int32_t kernel, int64_t* launches, double* total_ms);
+rf_status ridgefill_profile_reset(void);
+
 const char* ridgefill_status_string(rf_status s);
 /* Description of the last non-OK status returned on this thread ("" if none). */
 const char* ridgefill_last_error(void);

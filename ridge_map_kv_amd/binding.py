@@ -28,6 +28,9 @@ EXPORTED = [
     "ridgefill_solve_workspace_bytes",
     "ridgefill_solve",
     "ridgefill_read_status",
+    "ridgefill_profile_enable",
+    "ridgefill_profile_read",
+    "ridgefill_profile_reset",
     "ridgefill_status_string",
     "ridgefill_last_error",
 ]
@@ -80,6 +83,9 @@ def lib() -> C.CDLL:
         "ridgefill_solve_workspace_bytes": (sz, [i32, i32]),
         "ridgefill_solve": (st, [vp, sz, i32, i32, C.c_double, vp, vp, vp, vp, sz, vp]),
         "ridgefill_read_status": (st, [vp, vp]),
+        "ridgefill_profile_enable": (st, [i32]),
+        "ridgefill_profile_read": (st, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
+        "ridgefill_profile_reset": (st, []),
         "ridgefill_status_string": (C.c_char_p, [st]),
         "ridgefill_last_error": (C.c_char_p, []),
     }
@@ -194,6 +200,26 @@ def ridgefill_read_status(ws, stream=None) -> int:
     if s not in (RF_OK, RF_E_ROWS, RF_E_NOT_SPD):
         _check(s)
     return int(s)
+
+
+RF_KERNEL_FILL_MAP, RF_KERNEL_FILL_KV, RF_KERNEL_CALIB_GRAM, RF_KERNEL_CALIB_CROSS, \
+    RF_KERNEL_CALIB_SUMS, RF_KERNEL_SOLVE_MAP = range(6)
+
+
+def ridgefill_profile_enable(enable: bool) -> None:
+    _check(lib().ridgefill_profile_enable(1 if enable else 0))
+
+
+def ridgefill_profile_read(kernel: int) -> tuple[int, float]:
+    """(launches, summed milliseconds) of one kernel since the last reset."""
+    n = C.c_int64(0)
+    ms = C.c_double(0.0)
+    _check(lib().ridgefill_profile_read(int(kernel), C.byref(n), C.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+def ridgefill_profile_reset() -> None:
+    _check(lib().ridgefill_profile_reset())
 
 
 def ridgefill_status_string(s: int) -> str:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libridgefill.so")
 
-SOURCES = ["rf_fill.hip", "rf_calib.hip", "rf_solve.hip", "ridgefill.cpp"]
+SOURCES = ["rf_fill.hip", "rf_calib.hip", "rf_solve.hip", "ridgefill.cpp", "rf_profile.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -47,7 +47,7 @@ def build(extra: list[str] | None = None, verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]

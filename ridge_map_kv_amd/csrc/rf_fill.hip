@@ -20,6 +20,8 @@
 // and register of two MFMA blocks, and stores are 8-byte vectors.
 #include "rf_common.h"
 #include "rf_internal.h"
+#include "rf_profile.h"
+#include "ridgefill.h"
 
 namespace rf {
 
@@ -411,13 +413,23 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
   a.num_pages = p.num_pages;
   a.ntt = p.mpad / kTile;
 
-  for (int l0 = 0; l0 < n_layers; l0 += p.group) {
-    const int G = (n_layers - l0) < p.group ? (n_layers - l0) : p.group;
+  // Balanced groups of at most p.group layers, so one call makes as few, equal
+  // launches as the workspace allows.
+  const int ngroups = (n_layers + p.group - 1) / p.group;
+  const int gsize = (n_layers + ngroups - 1) / ngroups;
+  for (int l0 = 0; l0 < n_layers; l0 += gsize) {
+    const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
     for (int g = 0; g < G; ++g) a.L[g] = layers[l0 + g];
     a.nft = p.d / kTile;
-    hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    {
+      ProfileScope ps(RF_KERNEL_FILL_MAP, stream);
+      hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    }
     a.nft = 2 * p.kv / kTile;
-    hipLaunchKernelGGL(fill_kv_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    {
+      ProfileScope ps(RF_KERNEL_FILL_KV, stream);
+      hipLaunchKernelGGL(fill_kv_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -7,7 +7,7 @@
 
 namespace rf {
 
-constexpr int kMaxGroup = 16;   // layers sharing one fill launch
+constexpr int kMaxGroup = 32;   // layers sharing one fill launch
 constexpr int kTile = 256;      // fill/calibration tile edge (rows and features)
 constexpr size_t kStatusBytes = 256;
 // Device status bits kept in the first word of a fill or solve workspace.

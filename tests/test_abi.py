@@ -73,8 +73,9 @@ def test_size_queries():
     one = B.ridgefill_fill_workspace_bytes(s, 25805, 1)
     twenty = B.ridgefill_fill_workspace_bytes(s, 25805, 20)
     per = twenty - one
-    assert one > 0 and per > 0 and per % 15 == 0          # capped at 16 layers per launch
-    assert per // 15 >= 25856 * 4096 * 2                    # at least the bf16 staging rows
+    assert one > 0 and per > 0 and per % 19 == 0          # one staging slab per layer
+    assert per // 19 >= 25856 * 4096 * 2                    # at least the bf16 staging rows
+    assert B.ridgefill_fill_workspace_bytes(s, 25805, 64) == one + 31 * (per // 19)
     assert B.ridgefill_fill_workspace_bytes(B.make_shape(100, 8, 128), 10, 1) == 0
     st = B.ridgefill_calib_state_bytes(4096, 20)
     assert st >= 4 * 4096 * 4096 * 21
