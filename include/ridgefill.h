@@ -134,7 +134,8 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
  * must pass the same d and n_layers (they size every access to it).
  * ridgefill_calibrate adds n_rows rows: x_S device bf16 [n_rows][d]; x_l host array
  * [n_layers] of device bf16 [n_rows][d] pointers.  Sums in fp32 per call and fp64
- * across calls for the means; moments accumulated in fp32.  d: multiple of 256.
+ * across calls for the means; moments accumulated in fp32.  d: multiple of 256;
+ * n_layers: 1 .. 64.
  * ------------------------------------------------------------------------------ */
 size_t ridgefill_calib_state_bytes(int32_t d, int32_t n_layers);
 rf_status ridgefill_calib_reset(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
@@ -178,11 +179,10 @@ rf_status ridgefill_read_status(void* ws, void* stream);
 typedef enum rf_kernel_id {
   RF_KERNEL_FILL_MAP = 0,      /* map GEMM: x_hat = A x_S + b, RMS partials, x_hat * w   */
   RF_KERNEL_FILL_KV = 1,       /* K/V GEMM: RMS scale, RoPE, paged store                 */
-  RF_KERNEL_CALIB_GRAM = 2,    /* calibration: sum x_S x_S^T (lower triangle)           */
-  RF_KERNEL_CALIB_CROSS = 3,   /* calibration: sum x_l x_S^T for every layer             */
-  RF_KERNEL_CALIB_SUMS = 4,    /* calibration: column sums                                */
-  RF_KERNEL_SOLVE_MAP = 5,     /* solve: A_l = C_l (C + alpha I)^-1 product              */
-  RF_KERNEL_COUNT = 6
+  RF_KERNEL_CALIB_MOMENTS = 2, /* calibration: sum x_S x_S^T (lower) and every x_l x_S^T */
+  RF_KERNEL_CALIB_SUMS = 3,    /* calibration: column sums and row count                 */
+  RF_KERNEL_SOLVE_MAP = 4,     /* solve: A_l = C_l (C + alpha I)^-1 product              */
+  RF_KERNEL_COUNT = 5
 } rf_kernel_id;
 rf_status ridgefill_profile_enable(int32_t enable);
 rf_status ridgefill_profile_read(int32_t kernel, int64_t* launches, double* total_ms);

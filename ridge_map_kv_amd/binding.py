@@ -202,8 +202,8 @@ def ridgefill_read_status(ws, stream=None) -> int:
     return int(s)
 
 
-RF_KERNEL_FILL_MAP, RF_KERNEL_FILL_KV, RF_KERNEL_CALIB_GRAM, RF_KERNEL_CALIB_CROSS, \
-    RF_KERNEL_CALIB_SUMS, RF_KERNEL_SOLVE_MAP = range(6)
+RF_KERNEL_FILL_MAP, RF_KERNEL_FILL_KV, RF_KERNEL_CALIB_MOMENTS, RF_KERNEL_CALIB_SUMS, \
+    RF_KERNEL_SOLVE_MAP = range(5)
 
 
 def ridgefill_profile_enable(enable: bool) -> None:

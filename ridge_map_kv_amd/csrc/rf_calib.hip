@@ -1,6 +1,23 @@
-// One-pass calibration statistics (placeholder until the kernels land).
+// One-pass calibration statistics on gfx950.
+//
+// Source: English RidgeFill review (jaehun.me), section "Ridge map: predict the input,
+// and the original projection runs unchanged" -- calibration accumulates X^T X, X^T Y_l
+// and the two means in one pass of the original model, so a new lambda needs only a new
+// solve.  Raw sums and raw second moments are kept; the solve centres them.
+//
+// Per call (n rows of x_S and of every x_l, bf16, row-major [n][d]):
+//   sums   fp64 s_S += sum_t x_S[t], s_l += sum_t x_l[t]; header n += rows
+//   moments one launch over the lower-triangle tiles of G += x_S^T x_S and all tiles of
+//           every YX_l += x_l^T x_S (row = output feature of x_l, column = feature of x_S).
+// The moments kernel reduces over rows: each thread loads an 8-row x 8-feature block
+// (eight 16-byte loads), transposes it in registers and writes eight feature-major
+// 16-byte chunks, so the LDS tiles have the same [feature][row] layout the fill's
+// [row][reduction] tiles have, and the same MFMA slice code runs on them.
 #include "rf_common.h"
+#include "rf_gemm_tile.h"
 #include "rf_internal.h"
+#include "rf_profile.h"
+#include "ridgefill.h"
 
 namespace rf {
 
@@ -15,10 +32,234 @@ CalibLayout calib_layout(int d, int n_layers) {
   return L;
 }
 
-hipError_t launch_calib_reset(void*, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_calibrate(void*, int, int, const uint16_t*, const uint16_t* const*, int64_t,
-                            hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int kMaxCalibLayers = 64;
+
+struct CalibArgs {
+  const uint16_t* xS;
+  const uint16_t* xl[kMaxCalibLayers];
+  int n_rows, d, n_layers, nt;   // nt = d / 256
+  int ngram;                     // lower-triangle tiles of G
+  float* G;
+  float* YX;
+};
+
+__global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d, int n_layers) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  u32x4* p = reinterpret_cast<u32x4*>(state + 256);
+  const size_t n16 = (bytes - 256) / 16;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (size_t i = tid; i < n16; i += stride) p[i] = z;
+  if (tid == 0) {
+    *reinterpret_cast<int64_t*>(state) = 0;
+    reinterpret_cast<int32_t*>(state)[2] = d;
+    reinterpret_cast<int32_t*>(state)[3] = n_layers;
+    reinterpret_cast<uint32_t*>(state)[4] = kCalibMagic;
+  }
+}
+
+// Column sums: block (column block cb of 256, matrix m: 0 = x_S, 1 + l = x_l).  Thread
+// (slice s = tid / 32, group q = tid % 32) sums rows s, s + 8, ... of columns 8q..8q+7 in
+// fp32; the 8 slices are then added in order in fp64 and folded into the state.
+struct SumArgs {
+  const uint16_t* x[kMaxCalibLayers + 1];
+  int n_rows, d;
+  double* sums;          // [1 + n_layers][d] (sum_S then sum_l, contiguous)
+  int64_t* count;
+};
+
+__global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
+  __shared__ float part[8][256];
+  const int cb = blockIdx.x, m = blockIdx.y;
+  const int tid = threadIdx.x, s = tid >> 5, q = tid & 31;
+  const uint16_t* base = a.x[m] + cb * 256 + q * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int t = s; t < a.n_rows; t += 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (size_t)t * a.d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_to_f32(v[e] & 0xffffu);
+      acc[2 * e + 1] += bf16_to_f32(v[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[s][q * 8 + e] = acc[e];
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) tot += (double)part[k][tid];
+  double* dst = a.sums + (size_t)m * a.d + cb * 256 + tid;
+  *dst += tot;
+  if (cb == 0 && m == 0 && tid == 0) *a.count += a.n_rows;
+}
+
+// Loads rows t0 + 8*rg .. +7, features f0 + 8*fg .. +7 of a row-major [n][d] bf16 matrix
+// (rows past n read as zero).
+__device__ __forceinline__ void load_block(u32x4 (&v)[8], const uint16_t* x, int d, int n_rows,
+                                           int t0, int rg, int f0, int fg) {
+  const uint16_t* p = x + (size_t)(t0 + rg * 8) * d + f0 + fg * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (t0 + rg * 8 + e < n_rows) {
+      v[e] = *reinterpret_cast<const u32x4*>(p + (size_t)e * d);
+    } else {
+      v[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Transposes the 8x8 bf16 block and writes feature row 8*fg + q, chunk rg.
+__device__ __forceinline__ void store_block_t(unsigned char* buf, const u32x4 (&v)[8], int rg,
+                                              int fg) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    u32x4 o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a = v[2 * m][q >> 1], b = v[2 * m + 1][q >> 1];
+      o[m] = (q & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    *reinterpret_cast<u32x4*>(buf + lds_off128(fg * 8 + q, rg)) = o;
+  }
+}
+
+// Lower-triangle tile k of G -> (ti <= tj): tj = largest j with j (j + 1) / 2 <= k.
+__device__ __forceinline__ void gram_tile(int k, int& ti, int& tj) {
+  int j = (int)((sqrtf(8.0f * k + 1.0f) - 1.0f) * 0.5f);
+  while ((j + 1) * (j + 2) / 2 <= k) ++j;
+  while (j * (j + 1) / 2 > k) --j;
+  tj = j;
+  ti = k - j * (j + 1) / 2;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const uint16_t* X = a.xS;      // F operand: features of x_S (output columns)
+  const uint16_t* Y;             // T operand: features of x_S (Gram) or x_l (output rows)
+  float* out;
+  int fi, tj;
+  if (tile < a.ngram) {
+    gram_tile(tile, fi, tj);     // rows tj >= columns fi
+    Y = a.xS;
+    out = a.G;
+  } else {
+    const int k = tile - a.ngram;
+    const int per = a.nt * a.nt;
+    const int l = k / per;
+    const int r = k - l * per;
+    // groups of kTokGroup output-row tiles against every column tile
+    const int tg = r / (kTokGroup * a.nt);
+    const int within = r - tg * kTokGroup * a.nt;
+    const int left = a.nt - tg * kTokGroup;
+    const int gsz = left < kTokGroup ? left : kTokGroup;
+    fi = within / gsz;
+    tj = tg * kTokGroup + (within - fi * gsz);
+    Y = a.xl[l];
+    out = a.YX + (size_t)l * a.d * a.d;
+  }
+  const int f0 = fi * kTile, o0 = tj * kTile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wf = wave >> 1, wt = wave & 1, rg = tid >> 5, fg = tid & 31;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+
+  u32x4 vx[8], vy[8];
+  load_block(vx, X, a.d, a.n_rows, 0, rg, f0, fg);
+  load_block(vy, Y, a.d, a.n_rows, 0, rg, o0, fg);
+  store_block_t(smem, vx, rg, fg);
+  store_block_t(smem + kOperandStage, vy, rg, fg);
+  __syncthreads();
+  const int nk = (a.n_rows + BK - 1) / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const unsigned char* cur = smem + (kt & 1) * kStageBytes;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      load_block(vx, X, a.d, a.n_rows, (kt + 1) * BK, rg, f0, fg);
+      load_block(vy, Y, a.d, a.n_rows, (kt + 1) * BK, rg, o0, fg);
+    }
+    mma_slice(acc, cur, cur + kOperandStage, wf, wt, lane);
+    if (more) {
+      unsigned char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
+      store_block_t(nxt, vx, rg, fg);
+      store_block_t(nxt + kOperandStage, vy, rg, fg);
+    }
+    __syncthreads();
+  }
+
+  const int h = lane >> 5;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int o = o0 + wt * 128 + n * 32 + (lane & 31);
+    float* row = out + (size_t)o * a.d;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = f0 + wf * 128 + m * 32 + q * 8 + h * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
+        v[0] += acc[m][n][q * 4 + 0];
+        v[1] += acc[m][n][q * 4 + 1];
+        v[2] += acc[m][n][q * 4 + 2];
+        v[3] += acc[m][n][q * 4 + 3];
+        *reinterpret_cast<f32x4*>(row + i) = v;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_calib_reset(void* state, int d, int n_layers, hipStream_t stream) {
+  const CalibLayout L = calib_layout(d, n_layers);
+  hipLaunchKernelGGL(calib_reset_kernel, dim3(2048), dim3(256), 0, stream,
+                     static_cast<unsigned char*>(state), L.total, d, n_layers);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(void* state, int d, int n_layers, const uint16_t* xS,
+                            const uint16_t* const* xl, int64_t n_rows, hipStream_t stream) {
+  if (n_layers > kMaxCalibLayers) return hipErrorInvalidValue;
+  const CalibLayout L = calib_layout(d, n_layers);
+  unsigned char* st = static_cast<unsigned char*>(state);
+
+  SumArgs s = {};
+  s.x[0] = xS;
+  for (int l = 0; l < n_layers; ++l) s.x[1 + l] = xl[l];
+  s.n_rows = (int)n_rows;
+  s.d = d;
+  s.sums = reinterpret_cast<double*>(st + L.sum_S);
+  s.count = reinterpret_cast<int64_t*>(st);
+  // sum_l follows sum_S contiguously only when d * 8 is a multiple of 256 (d % 32 == 0).
+  {
+    ProfileScope ps(RF_KERNEL_CALIB_SUMS, stream);
+    hipLaunchKernelGGL(calib_sums_kernel, dim3(d / 256, 1 + n_layers), dim3(256), 0, stream, s);
+  }
+
+  CalibArgs a = {};
+  a.xS = xS;
+  for (int l = 0; l < n_layers; ++l) a.xl[l] = xl[l];
+  a.n_rows = (int)n_rows;
+  a.d = d;
+  a.n_layers = n_layers;
+  a.nt = d / kTile;
+  a.ngram = a.nt * (a.nt + 1) / 2;
+  a.G = reinterpret_cast<float*>(st + L.G);
+  a.YX = reinterpret_cast<float*>(st + L.YX);
+  const int tiles = a.ngram + n_layers * a.nt * a.nt;
+  {
+    ProfileScope ps(RF_KERNEL_CALIB_MOMENTS, stream);
+    hipLaunchKernelGGL(calib_moments_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace rf

@@ -19,6 +19,7 @@
 // reduction needs one cross-lane add, RoPE's pair (j, j + hd/2) sits in the same lane
 // and register of two MFMA blocks, and stores are 8-byte vectors.
 #include "rf_common.h"
+#include "rf_gemm_tile.h"
 #include "rf_internal.h"
 #include "rf_profile.h"
 #include "ridgefill.h"
@@ -26,13 +27,6 @@
 namespace rf {
 
 namespace {
-
-constexpr int BK = 64;                          // reduction slice per LDS stage
-constexpr int kThreads = 256;                   // 4 waves: 2 (features) x 2 (tokens)
-constexpr int kOperandStage = kTile * BK * 2;   // 32 KB: 256 rows x 64 bf16
-constexpr int kStageBytes = 2 * kOperandStage;  // F and T operands
-constexpr int kLdsBytes = 2 * kStageBytes;      // double buffered: 128 KB
-constexpr int kTokGroup = 4;                    // token tiles walked together
 
 struct FillKArgs {
   FillLayerPtrs L[kMaxGroup];
@@ -78,27 +72,6 @@ __device__ __forceinline__ void load_rows(u32x4 (&v)[8], const uint16_t* const (
 __device__ __forceinline__ void store_rows(unsigned char* buf, const u32x4 (&v)[8], int rr, int c) {
 #pragma unroll
   for (int p = 0; p < 8; ++p) *reinterpret_cast<u32x4*>(buf + lds_off128(rr + 32 * p, c)) = v[p];
-}
-
-// One BK slice of the 256x256 tile: each wave multiplies its 128 features x 128 tokens.
-__device__ __forceinline__ void mma_slice(f32x16 (&acc)[4][4], const unsigned char* Fs,
-                                          const unsigned char* Ts, int wf, int wt, int lane) {
-#pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    const int c = kk * 2 + (lane >> 5);
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      a[m] = *reinterpret_cast<const bf16x8*>(Fs + lds_off128(wf * 128 + m * 32 + (lane & 31), c));
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-      b[n] = *reinterpret_cast<const bf16x8*>(Ts + lds_off128(wt * 128 + n * 32 + (lane & 31), c));
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
-  }
 }
 
 // acc[m][n] += F[256 x K] * T[256 x K]^T; fr/tr: this thread's 8 row pointers of each

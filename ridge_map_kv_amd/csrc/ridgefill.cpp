@@ -196,7 +196,7 @@ static rf_status check_state(const void* state, size_t bytes, int d, int n_layer
   if (!aligned(state, 256)) return fail(RF_E_WORKSPACE, "state must be 256-byte aligned");
   if (d < rf::kTile || d % rf::kTile)
     return fail(RF_E_SHAPE, "d = %d must be a positive multiple of %d", d, rf::kTile);
-  if (n_layers < 1 || n_layers > 4096) return fail(RF_E_SHAPE, "n_layers = %d", n_layers);
+  if (n_layers < 1 || n_layers > 64) return fail(RF_E_SHAPE, "n_layers = %d must be in 1..64", n_layers);
   if (bytes < rf::calib_layout(d, n_layers).total)
     return fail(RF_E_WORKSPACE, "state %zu bytes < %zu needed", bytes,
                 rf::calib_layout(d, n_layers).total);
