@@ -1,18 +1,513 @@
-// Ridge solve (placeholder until the kernels land).
+// Closed-form ridge solve on gfx950, from the one-pass calibration state.
+//
+// Source: English RidgeFill review (jaehun.me), section "Ridge map: predict the input,
+// and the original projection runs unchanged" -- after subtracting the means,
+// A_l = Y_l^T X (X^T X + alpha I)^-1, b_l = mu_l - A_l mu_S, alpha = lambda tr(X^T X)/d_in.
+//
+// Per call (one lambda):
+//   means    mu = sums / n                                              fp64
+//   centre   C = G - n mu_S mu_S^T (G mirrored from its lower triangle);
+//            alpha = lambda tr(C) / d; C += alpha I                      fp64
+//   Cholesky blocked, 64-wide panels: diagonal block factor + its inverse, panel
+//            L_ik = A_ik L_kk^-T, trailing update A_ij -= L_ik L_jk^T    fp64
+//   inverse  W = L^-1 by blocked forward substitution on the identity;
+//            M = (C + alpha I)^-1 = W^T W                               fp64 (+ fp32 copy)
+//   maps     A_l = YX_l M - n mu_l v^T with v = M mu_S, one fp32 matrix-core GEMM over all
+//            layers (M symmetric, so both operands are read along rows)
+//   offsets  b_l = mu_l - A_l mu_S = mu_l - YX_l v + n mu_l (v . mu_S)      fp64 accumulate
+// Every launch is on the caller's stream; nothing is synchronised.
 #include "rf_common.h"
 #include "rf_internal.h"
+#include "rf_profile.h"
+#include "ridgefill.h"
 
 namespace rf {
 
+namespace {
+constexpr int NB = 64;        // Cholesky / substitution block
+constexpr int LDT = NB + 1;   // padded LDS row (fp64)
+}  // namespace
+
 SolveLayout solve_layout(int d, int n_layers) {
-  SolveLayout L = {};
-  L.total = 256 + (size_t)d * d * 8 * 4 + (size_t)(n_layers + 2) * d * 8;
+  SolveLayout L;
+  const size_t dd = (size_t)d * d;
+  L.scalars = 0;
+  L.mu = 256;
+  L.v = L.mu + align256((size_t)(1 + n_layers) * d * 8);
+  L.linv = L.v + align256((size_t)d * 8);
+  L.C = L.linv + align256((size_t)(d / NB) * NB * NB * 8);
+  L.W = L.C + align256(dd * 8);
+  L.M64 = L.W + align256(dd * 8);
+  L.M32 = L.M64 + align256(dd * 8);
+  L.total = L.M32 + align256(dd * 4);
   return L;
 }
 
-hipError_t launch_solve(const void*, int, int, double, float*, float*, uint16_t*, void*,
-                        hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+// scalars block: [0] status word (unsigned), then doubles at byte offsets below
+constexpr int kAlphaOff = 8, kNOff = 16, kVMuOff = 24;
+
+__device__ __forceinline__ double* scal(unsigned char* s, int off) {
+  return reinterpret_cast<double*>(s + off);
+}
+
+__global__ void means_kernel(const unsigned char* state, int d, int n_layers, size_t sum_off,
+                             double* mu, unsigned char* scalars) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const double n = (double)*reinterpret_cast<const int64_t*>(state);
+  const double* sums = reinterpret_cast<const double*>(state + sum_off);
+  if (i < (1 + n_layers) * d) mu[i] = n > 0 ? sums[i] / n : 0.0;
+  if (i == 0) *scal(scalars, kNOff) = n;
+}
+
+// C[r][c] = G[max][min] - n mu_r mu_c (full symmetric, fp64).
+__global__ void centre_kernel(const float* G, const double* mu, const unsigned char* scalars,
+                              int d, double* C) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)d * d) return;
+  const int r = (int)(idx / d), c = (int)(idx - (size_t)r * d);
+  const double n = *reinterpret_cast<const double*>(scalars + kNOff);
+  const float g = r >= c ? G[(size_t)r * d + c] : G[(size_t)c * d + r];
+  C[idx] = (double)g - n * mu[r] * mu[c];
+}
+
+// alpha = lambda tr(C) / d in a fixed order; then C += alpha I.
+__global__ __launch_bounds__(1024) void alpha_kernel(double* C, int d, double lambda,
+                                                     unsigned char* scalars) {
+  __shared__ double part[1024];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  for (int i = t; i < d; i += 1024) s += C[(size_t)i * d + i];
+  part[t] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) part[t] += part[t + w];
+    __syncthreads();
+  }
+  const double alpha = lambda * part[0] / d;
+  for (int i = t; i < d; i += 1024) C[(size_t)i * d + i] += alpha;
+  if (t == 0) *scal(scalars, kAlphaOff) = alpha;
+}
+
+// ---------------------------------------------------------------- 64x64 fp64 tiles
+
+// LDS tile [64][65]; load rows r of src (leading dimension ld), or its transpose.
+__device__ __forceinline__ void load64(double* t, const double* src, size_t ld, bool trans) {
+  for (int e = threadIdx.x; e < NB * NB; e += blockDim.x) {
+    const int r = e >> 6, c = e & 63;
+    if (trans)
+      t[c * LDT + r] = src[(size_t)r * ld + c];
+    else
+      t[r * LDT + c] = src[(size_t)r * ld + c];
+  }
+}
+
+// acc (4x4 per thread, rows 4*(tid>>4).., cols 4*(tid&15)..) += A * B^T from LDS tiles.
+__device__ __forceinline__ void mac64(double (&acc)[4][4], const double* A, const double* Bt) {
+  const int r0 = (threadIdx.x >> 4) * 4, c0 = (threadIdx.x & 15) * 4;
+  for (int q = 0; q < NB; ++q) {
+    double a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = A[(r0 + i) * LDT + q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = Bt[(c0 + j) * LDT + q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+  }
+}
+
+__device__ __forceinline__ void zero44(double (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+}
+
+// dst[r][c] = s * acc + (add ? dst : 0)
+__device__ __forceinline__ void store44(double* dst, size_t ld, const double (&acc)[4][4],
+                                        double s, bool add) {
+  const int r0 = (threadIdx.x >> 4) * 4, c0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      double* p = dst + (size_t)(r0 + i) * ld + c0 + j;
+      *p = s * acc[i][j] + (add ? *p : 0.0);
+    }
+}
+
+// Factor diagonal block k in place (lower) and store its inverse in linv[k].
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k, double* linv,
+                                                        unsigned* status) {
+  __shared__ double a[NB * LDT];
+  __shared__ double x[NB * LDT];
+  double* blk = C + (size_t)k * NB * d + (size_t)k * NB;
+  load64(a, blk, d, false);
+  __syncthreads();
+  const int t = threadIdx.x;
+  for (int j = 0; j < NB; ++j) {
+    if (t == 0) {
+      double p = a[j * LDT + j];
+      if (!(p > 0.0) || !isfinite(p)) {
+        atomicOr(status, kStatusNotSpdBit);
+        p = 1.0;
+      }
+      a[j * LDT + j] = sqrt(p);
+    }
+    __syncthreads();
+    const double piv = a[j * LDT + j];
+    for (int i = j + 1 + t; i < NB; i += blockDim.x) a[i * LDT + j] /= piv;
+    __syncthreads();
+    // trailing update of the lower part: a[i][c] -= a[i][j] a[c][j], j < c <= i
+    const int m = NB - j - 1;
+    for (int e = t; e < m * m; e += blockDim.x) {
+      const int i = j + 1 + e / m, c = j + 1 + e % m;
+      if (c <= i) a[i * LDT + c] -= a[i * LDT + j] * a[c * LDT + j];
+    }
+    __syncthreads();
+  }
+  // inverse of the lower factor, one column per thread: x = L^-1
+  if (t < NB) {
+    const int c = t;
+    for (int r = 0; r < NB; ++r) {
+      double s = (r == c) ? 1.0 : 0.0;
+      for (int q = c; q < r; ++q) s -= a[r * LDT + q] * x[q * LDT + c];
+      x[r * LDT + c] = r < c ? 0.0 : s / a[r * LDT + r];
+    }
+  }
+  __syncthreads();
+  double* li = linv + (size_t)k * NB * NB;
+  for (int e = t; e < NB * NB; e += blockDim.x) {
+    const int r = e >> 6, c = e & 63;
+    blk[(size_t)r * d + c] = c <= r ? a[r * LDT + c] : 0.0;
+    li[e] = x[r * LDT + c];
+  }
+}
+
+// Block row i = k + 1 + blockIdx.x:  L_ik = A_ik * Linv_kk^T.
+__global__ __launch_bounds__(256) void chol_panel_kernel(double* C, int d, int k,
+                                                         const double* linv) {
+  __shared__ double a[NB * LDT];
+  __shared__ double li[NB * LDT];
+  const int i = k + 1 + blockIdx.x;
+  double* blk = C + (size_t)i * NB * d + (size_t)k * NB;
+  load64(a, blk, d, false);
+  load64(li, linv + (size_t)k * NB * NB, NB, false);
+  __syncthreads();
+  double acc[4][4];
+  zero44(acc);
+  mac64(acc, a, li);
+  __syncthreads();
+  store44(blk, d, acc, 1.0, false);
+}
+
+// Trailing blocks (i, j), k < j <= i:  A_ij -= L_ik L_jk^T.
+__global__ __launch_bounds__(256) void chol_update_kernel(double* C, int d, int k) {
+  __shared__ double a[NB * LDT];
+  __shared__ double b[NB * LDT];
+  const int e = blockIdx.x;
+  int jj = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+  while ((jj + 1) * (jj + 2) / 2 <= e) ++jj;
+  while (jj * (jj + 1) / 2 > e) --jj;
+  const int ii_rel = jj, jj_rel = e - jj * (jj + 1) / 2;   // jj_rel <= ii_rel
+  const int i = k + 1 + ii_rel, j = k + 1 + jj_rel;
+  load64(a, C + (size_t)i * NB * d + (size_t)k * NB, d, false);
+  load64(b, C + (size_t)j * NB * d + (size_t)k * NB, d, false);
+  __syncthreads();
+  double acc[4][4];
+  zero44(acc);
+  mac64(acc, a, b);
+  store44(C + (size_t)i * NB * d + (size_t)j * NB, d, acc, -1.0, true);
+}
+
+__global__ void identity_kernel(double* W, int d) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)d * d) return;
+  const size_t r = idx / d, c = idx - r * d;
+  W[idx] = r == c ? 1.0 : 0.0;
+}
+
+// Forward substitution, block row i, column block cb = blockIdx.x <= i:
+// W_i,cb = Linv_ii * B_i,cb (in place).
+__global__ __launch_bounds__(256) void fsub_rows_kernel(double* W, int d, int i,
+                                                        const double* linv) {
+  __shared__ double li[NB * LDT];
+  __shared__ double bt[NB * LDT];
+  const int cb = blockIdx.x;
+  double* blk = W + (size_t)i * NB * d + (size_t)cb * NB;
+  load64(li, linv + (size_t)i * NB * NB, NB, false);
+  load64(bt, blk, d, true);
+  __syncthreads();
+  double acc[4][4];
+  zero44(acc);
+  mac64(acc, li, bt);
+  __syncthreads();
+  store44(blk, d, acc, 1.0, false);
+}
+
+// B_m,cb -= L_mi W_i,cb for m > i, cb <= i;  blockIdx.x = (m - i - 1) * (i + 1) + cb.
+__global__ __launch_bounds__(256) void fsub_update_kernel(double* W, const double* C, int d, int i) {
+  __shared__ double l[NB * LDT];
+  __shared__ double wt[NB * LDT];
+  const int m = i + 1 + blockIdx.x / (i + 1), cb = blockIdx.x % (i + 1);
+  load64(l, C + (size_t)m * NB * d + (size_t)i * NB, d, false);
+  load64(wt, W + (size_t)i * NB * d + (size_t)cb * NB, d, true);
+  __syncthreads();
+  double acc[4][4];
+  zero44(acc);
+  mac64(acc, l, wt);
+  store44(W + (size_t)m * NB * d + (size_t)cb * NB, d, acc, -1.0, true);
+}
+
+// M = W^T W for lower tiles (ab >= bb), mirrored: M[a][b] = sum_k W[k][a] W[k][b], k >= ab.
+__global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double* M64, float* M32) {
+  __shared__ double wa[NB * LDT];
+  __shared__ double wb[NB * LDT];
+  const int e = blockIdx.x;
+  int ab = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+  while ((ab + 1) * (ab + 2) / 2 <= e) ++ab;
+  while (ab * (ab + 1) / 2 > e) --ab;
+  const int bb = e - ab * (ab + 1) / 2;
+  const int nbk = d / NB;
+  double acc[4][4];
+  zero44(acc);
+  for (int kb = ab; kb < nbk; ++kb) {
+    load64(wa, W + (size_t)kb * NB * d + (size_t)ab * NB, d, true);
+    load64(wb, W + (size_t)kb * NB * d + (size_t)bb * NB, d, true);
+    __syncthreads();
+    mac64(acc, wa, wb);
+    __syncthreads();
+  }
+  const int r0 = (threadIdx.x >> 4) * 4, c0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t a = (size_t)ab * NB + r0 + i, b = (size_t)bb * NB + c0 + j;
+      M64[a * d + b] = acc[i][j];
+      M64[b * d + a] = acc[i][j];
+      M32[a * d + b] = (float)acc[i][j];
+      M32[b * d + a] = (float)acc[i][j];
+    }
+}
+
+// v = M mu_S (one wave per row, fixed-order reduction); then v . mu_S.
+__global__ __launch_bounds__(256) void mv_kernel(const double* M64, const double* mu, int d,
+                                                 double* v) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= d) return;
+  double s = 0.0;
+  for (int k = lane; k < d; k += 64) s += M64[(size_t)row * d + k] * mu[k];
+  for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
+  if (lane == 0) v[row] = s;
+}
+
+__global__ __launch_bounds__(1024) void dot_kernel(const double* v, const double* mu, int d,
+                                                   unsigned char* scalars) {
+  __shared__ double part[1024];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  for (int i = t; i < d; i += 1024) s += v[i] * mu[i];
+  part[t] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) part[t] += part[t + w];
+    __syncthreads();
+  }
+  if (t == 0) *scal(scalars, kVMuOff) = part[0];
+}
+
+// b_l[o] = mu_l[o] - sum_k YX_l[o][k] v[k] + n mu_l[o] (v . mu_S); one wave per (l, o).
+__global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double* mu,
+                                                   const double* v, const unsigned char* scalars,
+                                                   int d, int n_layers, float* b_out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= n_layers * d) return;
+  const int l = row / d, o = row - l * d;
+  const float* y = YX + (size_t)row * d;
+  double s = 0.0;
+  for (int k = lane; k < d; k += 64) s += (double)y[k] * v[k];
+  for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
+  if (lane == 0) {
+    const double n = *reinterpret_cast<const double*>(scalars + kNOff);
+    const double vmu = *reinterpret_cast<const double*>(scalars + kVMuOff);
+    const double m = mu[(size_t)(1 + l) * d + o];
+    b_out[row] = (float)(m - s + n * m * vmu);
+  }
+}
+
+// ---------------------------------------------------------------- fp32 MFMA map GEMM
+// out[l][o][i] = sum_k YX_l[o][k] M[i][k] - n mu_l[o] v[i];  128x128 tiles, 4 waves (2x2),
+// v_mfma_f32_32x32x2f32.  LDS rows are 32 floats (128 bytes) of one reduction slice.
+constexpr int SB = 128;          // tile edge
+constexpr int SBK = 32;          // floats per reduction slice
+constexpr int kSStage = SB * SBK * 4;   // 16 KB per operand
+
+struct MapArgs {
+  const float* YX;
+  const float* M32;
+  const double* mu;
+  const double* v;
+  const unsigned char* scalars;
+  float* A_out;
+  uint16_t* A_bf16;
+  int d, n_layers, nt;
+};
+
+__global__ __launch_bounds__(256, 2) void solve_map_kernel(MapArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kSStage];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = a.nt * a.nt;
+  const int l = tile / per;
+  const int r = tile - l * per;
+  const int to = r / a.nt, ti = r - to * a.nt;          // output row tile (o), column tile (i)
+  const int o0 = to * SB, i0 = ti * SB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wf = wave >> 1, wt = wave & 1, rr = tid >> 3, c = tid & 7;
+  const float* F = a.M32 + (size_t)i0 * a.d;                         // rows i
+  const float* Tm = a.YX + ((size_t)l * a.d + o0) * a.d;             // rows o
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.f;
+
+  f32x4 vf[4], vt[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      vf[p] = *reinterpret_cast<const f32x4*>(F + (size_t)(rr + 32 * p) * a.d + k0 + c * 4);
+      vt[p] = *reinterpret_cast<const f32x4*>(Tm + (size_t)(rr + 32 * p) * a.d + k0 + c * 4);
+    }
+  };
+  auto store = [&](unsigned char* buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      *reinterpret_cast<f32x4*>(buf + lds_off128(rr + 32 * p, c)) = vf[p];
+      *reinterpret_cast<f32x4*>(buf + kSStage + lds_off128(rr + 32 * p, c)) = vt[p];
+    }
+  };
+  load(0);
+  store(smem);
+  __syncthreads();
+  const int nk = a.d / SBK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const unsigned char* cur = smem + (kt & 1) * 2 * kSStage;
+    const bool more = kt + 1 < nk;
+    if (more) load((kt + 1) * SBK);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int ch = cc * 2 + (lane >> 5);
+      f32x4 fa[2], tb[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        fa[m] = *reinterpret_cast<const f32x4*>(cur + lds_off128(wf * 64 + m * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        tb[n] = *reinterpret_cast<const f32x4*>(cur + kSStage +
+                                                lds_off128(wt * 64 + n * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[m][s], tb[n][s], acc[m][n], 0, 0, 0);
+    }
+    if (more) store(smem + ((kt + 1) & 1) * 2 * kSStage);
+    __syncthreads();
+  }
+
+  const double n = *reinterpret_cast<const double*>(a.scalars + kNOff);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn) {
+    const int o = o0 + wt * 64 + nn * 32 + (lane & 31);
+    const double nm = n * a.mu[(size_t)(1 + l) * a.d + o];
+    const size_t rowoff = ((size_t)l * a.d + o) * a.d;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + wf * 64 + m * 32 + q * 8 + h * 4;
+        f32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          out[e] = (float)((double)acc[m][nn][q * 4 + e] - nm * a.v[i + e]);
+        if (a.A_out) *reinterpret_cast<f32x4*>(a.A_out + rowoff + i) = out;
+        if (a.A_bf16) {
+          u32x2 bb;
+          bb.x = pack_bf16x2(out[0], out[1]);
+          bb.y = pack_bf16x2(out[2], out[3]);
+          *reinterpret_cast<u32x2*>(a.A_bf16 + rowoff + i) = bb;
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, float* A_out,
+                        float* b_out, uint16_t* A_bf16, void* ws, hipStream_t stream) {
+  const CalibLayout CL = calib_layout(d, n_layers);
+  const SolveLayout L = solve_layout(d, n_layers);
+  const unsigned char* st = static_cast<const unsigned char*>(state);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  unsigned* status = reinterpret_cast<unsigned*>(w);
+  double* mu = reinterpret_cast<double*>(w + L.mu);
+  double* v = reinterpret_cast<double*>(w + L.v);
+  double* linv = reinterpret_cast<double*>(w + L.linv);
+  double* C = reinterpret_cast<double*>(w + L.C);
+  double* W = reinterpret_cast<double*>(w + L.W);
+  double* M64 = reinterpret_cast<double*>(w + L.M64);
+  float* M32 = reinterpret_cast<float*>(w + L.M32);
+  const float* G = reinterpret_cast<const float*>(st + CL.G);
+  const float* YX = reinterpret_cast<const float*>(st + CL.YX);
+  const size_t dd = (size_t)d * d;
+  const unsigned gdd = (unsigned)((dd + 255) / 256);
+  const int nbk = d / NB;
+
+  hipError_t e = launch_clear_status(status, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(means_kernel, dim3(((1 + n_layers) * d + 255) / 256), dim3(256), 0, stream,
+                     st, d, n_layers, CL.sum_S, mu, w);
+  hipLaunchKernelGGL(centre_kernel, dim3(gdd), dim3(256), 0, stream, G, mu, w, d, C);
+  hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
+  for (int k = 0; k < nbk; ++k) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, C, d, k, linv, status);
+    const int below = nbk - k - 1;
+    if (below > 0) {
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(below), dim3(256), 0, stream, C, d, k, linv);
+      hipLaunchKernelGGL(chol_update_kernel, dim3(below * (below + 1) / 2), dim3(256), 0, stream,
+                         C, d, k);
+    }
+  }
+  hipLaunchKernelGGL(identity_kernel, dim3(gdd), dim3(256), 0, stream, W, d);
+  for (int i = 0; i < nbk; ++i) {
+    hipLaunchKernelGGL(fsub_rows_kernel, dim3(i + 1), dim3(256), 0, stream, W, d, i, linv);
+    const int below = nbk - i - 1;
+    if (below > 0)
+      hipLaunchKernelGGL(fsub_update_kernel, dim3(below * (i + 1)), dim3(256), 0, stream, W, C, d, i);
+  }
+  hipLaunchKernelGGL(wtw_kernel, dim3(nbk * (nbk + 1) / 2), dim3(256), 0, stream, W, d, M64, M32);
+  hipLaunchKernelGGL(mv_kernel, dim3((d + 3) / 4), dim3(256), 0, stream, M64, mu, d, v);
+  hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, stream, v, mu, d, w);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  MapArgs a = {YX, M32, mu, v, w, A_out, A_bf16, d, n_layers, d / SB};
+  {
+    ProfileScope ps(RF_KERNEL_SOLVE_MAP, stream);
+    hipLaunchKernelGGL(solve_map_kernel, dim3(n_layers * a.nt * a.nt), dim3(256), 0, stream, a);
+  }
+  hipLaunchKernelGGL(bias_kernel, dim3((n_layers * d + 3) / 4), dim3(256), 0, stream, YX, mu, v,
+                     w, d, n_layers, b_out);
+  return hipGetLastError();
 }
 
 }  // namespace rf
