@@ -5,7 +5,10 @@
 One step is one ridgefill_fill call over every upper layer of the Llama-3.1-8B-shaped
 workload (d = 4096, layers 12..31, 8 KV heads x 128, N = 32768, T = 4096, 10% of the
 prefix exact: 25,805 filled rows), with every input already in HBM.  The partition of
-the rows is done once beforehand (it is the routing input).  Prints one JSON line.
+the rows is done once beforehand (it is the routing input).  Before the fill, the
+8B-shaped calibration (131,072 synthetic rows of x_S and 20 layer inputs, streamed in
+16,384-row chunks) is timed, then one solve per lambda in {1e-4 .. 1}; the lambda = 0.03
+maps are the ones the fill uses.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -118,12 +121,139 @@ def cpu_baseline_fill(cfg, inp, budget_s: float = 15.0):
                       f"workload (NumPy float64), {spent:.1f} s"}
 
 
+def make_calib_chunks(ccfg, dev):
+    """Synthetic calibration rows on the GPU, chunk by chunk: x_l = W_true,l x_S + c_l +
+    s * t3 with W_true,l = I + U_l diag(0.5) V_l^T (rank 64) and Student-t(3) noise."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(ccfg.seed)
+    d, L = ccfg.d, ccfg.n_layers
+    s = 1.0 / np.sqrt(d)
+    U = [torch.randn((d, 64), generator=g, device=dev) * s for _ in range(L)]
+    V = [torch.randn((d, 64), generator=g, device=dev) * s for _ in range(L)]
+    c = [torch.randn(d, generator=g, device=dev) for _ in range(L)]
+    chunks = []
+    for r0 in range(0, ccfg.rows, ccfg.chunk):
+        n = min(ccfg.chunk, ccfg.rows - r0)
+        xs = torch.randn((n, d), generator=g, device=dev)
+        xl = []
+        for l in range(L):
+            z = torch.randn((n, d), generator=g, device=dev)
+            chi = sum(torch.randn((n, d), generator=g, device=dev) ** 2 for _ in range(3))
+            t3 = z / torch.sqrt(chi / 3.0)
+            y = xs + 0.5 * ((xs @ V[l]) @ U[l].T) + c[l] + ccfg.noise_scale * t3
+            xl.append(y.to(torch.bfloat16))
+            del z, chi, t3, y
+        chunks.append((xs.to(torch.bfloat16), xl))
+    return chunks
+
+
+def run_calibration(ccfg, dev, passes: int = 2):
+    """Times ridgefill_calibrate over all chunks (after one untimed pass), then one solve
+    per lambda; returns the timing dict and the lambda = 0.03 maps for the fill."""
+    import torch
+    from ridge_map_kv_amd import binding as B
+
+    d, L = ccfg.d, ccfg.n_layers
+    log(f"bench: generating {ccfg.rows} calibration rows x {L + 1} matrices")
+    chunks = make_calib_chunks(ccfg, dev)
+    state = torch.empty(B.ridgefill_calib_state_bytes(d, L), dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        B.ridgefill_calib_reset(state, d, L)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for xs, xl in chunks:
+            B.ridgefill_calibrate(state, d, L, xs, xl)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    one_pass()
+    B.ridgefill_profile_reset()
+    B.ridgefill_profile_enable(True)
+    times = [one_pass() for _ in range(passes)]
+    B.ridgefill_profile_enable(False)
+    mom_n, mom_ms = B.ridgefill_profile_read(B.RF_KERNEL_CALIB_MOMENTS)
+    sum_n, sum_ms = B.ridgefill_profile_read(B.RF_KERNEL_CALIB_SUMS)
+    t_cal = min(times)
+    flops = ccfg.accumulate_flops()
+    mom_flops_launch = flops / len(chunks)
+    calib = {
+        "rows": ccfg.rows, "chunk_rows": ccfg.chunk, "upper_layers": L, "d": d,
+        "seconds": t_cal, "rows_per_s": ccfg.rows / t_cal,
+        "tflop": flops / 1e12, "pct_bf16_mfma_peak": 100.0 * flops / t_cal / (PEAK_BF16_TFLOPS * 1e12),
+        "moments_kernel": {"avg_ms": mom_ms / mom_n, "launches": mom_n,
+                           "tflops": mom_flops_launch / (mom_ms / mom_n * 1e-3) / 1e12},
+        "sums_kernel": {"avg_ms": sum_ms / sum_n, "launches": sum_n},
+        "noise": "0.1 * Student-t(3)",
+    }
+
+    A = torch.empty((L, d, d), dtype=torch.float32, device=dev)
+    Ab = torch.empty((L, d, d), dtype=torch.bfloat16, device=dev)
+    b = torch.empty((L, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.ridgefill_solve_workspace_bytes(d, L), dtype=torch.uint8, device=dev)
+    B.ridgefill_solve(state, d, L, 0.03, A, b, Ab, ws)      # warm-up
+    torch.cuda.synchronize()
+    B.ridgefill_profile_reset()
+    B.ridgefill_profile_enable(True)
+    per_lambda = []
+    maps = None
+    for lam in ccfg.lambdas:
+        t0 = time.perf_counter()
+        B.ridgefill_solve(state, d, L, lam, A, b, Ab, ws)
+        st = B.ridgefill_read_status(ws)
+        per_lambda.append((time.perf_counter() - t0) * 1e3)
+        if st != B.RF_OK:
+            raise SystemExit(f"solve at lambda={lam} reported device status {st}")
+        if lam == 0.03:
+            maps = [(Ab[l].clone(), b[l].clone()) for l in range(L)]
+    B.ridgefill_profile_enable(False)
+    map_n, map_ms = B.ridgefill_profile_read(B.RF_KERNEL_SOLVE_MAP)
+    map_flops = 2.0 * L * d * d * d
+    solve = {"lambdas": list(ccfg.lambdas), "ms_per_lambda": per_lambda,
+             "map_gemm": {"avg_ms": map_ms / map_n, "launches": map_n,
+                          "tflops": map_flops / (map_ms / map_n * 1e-3) / 1e12,
+                          "pct_fp32_mfma_peak": 100.0 * map_flops / (map_ms / map_n * 1e-3)
+                          / (PEAK_FP32_TFLOPS * 1e12)},
+             "context": "the pages quote 26 min on one RTX 5090 for calibrating and solving "
+                        "three splits of a 27B model, model passes included"}
+    del chunks
+    torch.cuda.empty_cache()
+    return calib, solve, maps, state
+
+
+def cpu_baseline_calib(ccfg, budget_s: float = 10.0):
+    """The oracle's one-pass accumulation on a bounded row sample (same shapes)."""
+    import oracle
+    from ridge_map_kv_amd import synth
+
+    d, L = ccfg.d, ccfg.n_layers
+    rows = 64
+    xS, xl = synth.calib_data(d, L, rows, seed=ccfg.seed, noise_dof=ccfg.noise_dof)
+    st = oracle.calib_new(d, L)
+    t0 = time.perf_counter()
+    oracle.calib_accumulate(st, xS.astype(np.float64), [y.astype(np.float64) for y in xl])
+    per_row = (time.perf_counter() - t0) / rows
+    rows = int(np.clip(budget_s / per_row, 64, 4096))
+    xS, xl = synth.calib_data(d, L, rows, seed=ccfg.seed, noise_dof=ccfg.noise_dof)
+    st = oracle.calib_new(d, L)
+    t0 = time.perf_counter()
+    oracle.calib_accumulate(st, xS.astype(np.float64), [y.astype(np.float64) for y in xl])
+    spent = time.perf_counter() - t0
+    return {"value": rows / spent, "unit": "calibration rows/s", "kind": "oracle",
+            "sample": f"{rows} synthetic rows x {L + 1} matrices, d = {d} (NumPy float64), "
+                      f"{spent:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip calibration/solve and fill with synthetic near-identity maps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -138,8 +268,13 @@ def main():
     B.lib()
     dev = torch.device("cuda:0")
     cfg = configs.LLAMA8B
+    calib = solve = maps = None
+    if not args.no_calib:
+        calib, solve, maps, _ = run_calibration(configs.CALIB8B, dev)
+        log(f"bench: calibration {calib['seconds'] * 1e3:.1f} ms "
+            f"({calib['rows_per_s'] / 1e6:.2f} M rows/s); solve ms {solve['ms_per_lambda']}")
     log(f"bench: building {cfg.name} fill inputs")
-    inp = make_fill_inputs(cfg, dev)
+    inp = make_fill_inputs(cfg, dev, maps=maps)
     nf = len(inp["filled"])
     assert nf == cfg.n_filled
 
@@ -193,7 +328,8 @@ def main():
                    "split": cfg.S, "layers": cfg.L, "n_kv_heads": cfg.n_kv,
                    "head_dim": cfg.head_dim, "N": cfg.N, "T": cfg.T, "filled_rows": nf,
                    "exact_rows": cfg.exact_count, "page_size": cfg.page_size,
-                   "maps": "synthetic near-identity bf16 maps",
+                   "maps": ("synthetic near-identity bf16 maps" if maps is None else
+                            "bf16 maps from this run's calibration + solve at lambda = 0.03"),
                    "fill_tflop_per_step": flops_total / 1e12},
         "roofline": {"bound": "mfma", "kernel": "fill_map_kernel",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -206,9 +342,14 @@ def main():
                                "tflops": kv_flops_launch / (kv_avg * 1e-3) / 1e12},
         },
     }
+    if calib is not None:
+        out["calibration"] = calib
+        out["solve"] = solve
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline_fill(cfg, inp)
+        if calib is not None:
+            out["calibration"]["cpu_baseline"] = cpu_baseline_calib(configs.CALIB8B)
     print(json.dumps(out), flush=True)
 
 
