@@ -254,6 +254,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip calibration/solve and fill with synthetic near-identity maps")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy, to scale HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -351,6 +353,12 @@ def main():
         if calib is not None:
             out["calibration"]["cpu_baseline"] = cpu_baseline_calib(configs.CALIB8B)
     print(json.dumps(out), flush=True)
+    if args.traffic_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

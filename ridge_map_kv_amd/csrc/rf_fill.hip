@@ -63,82 +63,51 @@ __device__ __forceinline__ void decode_tile(int tile, int ntt, int nft, int& g, 
   tt = tg * kTokGroup + (within - ft * gsz);
 }
 
-__device__ __forceinline__ void load_rows(u32x4 (&v)[8], const uint16_t* const (&rows)[8],
-                                          int k0) {
-#pragma unroll
-  for (int p = 0; p < 8; ++p) v[p] = *reinterpret_cast<const u32x4*>(rows[p] + k0);
+
+// Output staging: after the main loop the 128 KB of LDS hold one 256 (rows) x 256
+// (features) bf16 tile, 512 bytes per row, 16-byte chunk c of row r stored at chunk
+// c ^ (r & 31).  Lanes write their runs of four features (8 bytes); the tile then leaves as
+// 16-byte vectors, 32 lanes per 512-byte row segment.
+__device__ __forceinline__ int stage_off(int r, int f) {
+  return r * 512 + ((((f >> 3) ^ (r & 31)) << 4) | ((f & 7) << 1));
 }
 
-__device__ __forceinline__ void store_rows(unsigned char* buf, const u32x4 (&v)[8], int rr, int c) {
-#pragma unroll
-  for (int p = 0; p < 8; ++p) *reinterpret_cast<u32x4*>(buf + lds_off128(rr + 32 * p, c)) = v[p];
-}
-
-// acc[m][n] += F[256 x K] * T[256 x K]^T; fr/tr: this thread's 8 row pointers of each
-// operand, already offset by its 16-byte chunk.
-__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const uint16_t* const (&fr)[8],
-                                              const uint16_t* const (&tr)[8], int K,
-                                              unsigned char* smem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wf = wave >> 1, wt = wave & 1, rr = tid >> 3, c = tid & 7;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
-
-  u32x4 vf[8], vt[8];
-  load_rows(vf, fr, 0);
-  load_rows(vt, tr, 0);
-  store_rows(smem, vf, rr, c);
-  store_rows(smem + kOperandStage, vt, rr, c);
-  __syncthreads();
-  const int nk = K / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const unsigned char* cur = smem + (kt & 1) * kStageBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_rows(vf, fr, (kt + 1) * BK);
-      load_rows(vt, tr, (kt + 1) * BK);
-    }
-    mma_slice(acc, cur, cur + kOperandStage, wf, wt, lane);
-    if (more) {
-      unsigned char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-      store_rows(nxt, vf, rr, c);
-      store_rows(nxt + kOperandStage, vt, rr, c);
-    }
-    __syncthreads();
-  }
+__device__ __forceinline__ void stage_put4(unsigned char* smem, int r, int f, float v0, float v1,
+                                           float v2, float v3) {
+  u32x2 o;
+  o.x = pack_bf16x2(v0, v1);
+  o.y = pack_bf16x2(v2, v3);
+  *reinterpret_cast<u32x2*>(smem + stage_off(r, f)) = o;
 }
 
 __device__ __forceinline__ float lo16(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
 __device__ __forceinline__ float hi16(uint32_t x) { return bf16_to_f32(x >> 16); }
 
 __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds2];
   int g, tt, ft;
   decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
   const FillLayerPtrs Lp = a.L[g];
   const int t0 = tt * kTile, f0 = ft * kTile;
-  const int tid = threadIdx.x, rr = tid >> 3, c = tid & 7;
+  const int tid = threadIdx.x;
 
-  const uint16_t* fr[8];
-  const uint16_t* tr[8];
+  DmaRows rs;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    fr[p] = Lp.A + (size_t)(f0 + rr + 32 * p) * a.d + c * 8;
-    const int tok = t0 + rr + 32 * p;
+  for (int p = 0; p < 4; ++p) {
+    const int r = dma_row(p, tid >> 6, tid & 63);
+    const int ce = dma_chunk_elems(r, tid & 63);
+    rs.f[p] = Lp.A + (size_t)(f0 + r) * a.d + ce;
+    const int tok = t0 + r;
     int row = 0;
     if (tok < a.n_filled) {
       const int t = a.idx[tok];
       if (t >= 0 && t < a.P) row = t;
     }
-    tr[p] = a.xS + (size_t)row * a.x_stride + c * 8;
+    rs.t[p] = a.xS + (size_t)row * a.x_stride + ce;
   }
 
   f32x16 acc[4][4];
-  gemm_mainloop(acc, fr, tr, a.d, smem);
+  gemm_pipeline(acc, rs, a.d, smem);
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
   uint16_t* hb = reinterpret_cast<uint16_t*>(a.layer_ws + g * a.per_layer);
@@ -148,22 +117,19 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
   for (int m = 0; m < 4; ++m) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int f = f0 + wf * 128 + m * 32 + q * 8 + h * 4;
-      const f32x4 bias = *reinterpret_cast<const f32x4*>(Lp.b + f);
-      const u32x2 wb = *reinterpret_cast<const u32x2*>(Lp.w + f);
+      const int fl = wf * 128 + m * 32 + q * 8 + h * 4;      // feature within the tile
+      const f32x4 bias = *reinterpret_cast<const f32x4*>(Lp.b + f0 + fl);
+      const u32x2 wb = *reinterpret_cast<const u32x2*>(Lp.w + f0 + fl);
       const float w0 = lo16(wb.x), w1 = hi16(wb.x), w2 = lo16(wb.y), w3 = hi16(wb.y);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
+        const int tl = wt * 128 + n * 32 + (lane & 31);
         const float v0 = acc[m][n][q * 4 + 0] + bias.x;
         const float v1 = acc[m][n][q * 4 + 1] + bias.y;
         const float v2 = acc[m][n][q * 4 + 2] + bias.z;
         const float v3 = acc[m][n][q * 4 + 3] + bias.w;
         ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
-        u32x2 o;
-        o.x = pack_bf16x2(v0 * w0, v1 * w1);
-        o.y = pack_bf16x2(v2 * w2, v3 * w3);
-        *reinterpret_cast<u32x2*>(hb + (size_t)tok * a.d + f) = o;
+        stage_put4(smem, tl, fl, v0 * w0, v1 * w1, v2 * w2, v3 * w3);
       }
     }
   }
@@ -176,6 +142,15 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
       const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
       ssq[(size_t)tok * a.nchunk + chunk] = ss[n];
     }
+  }
+  __syncthreads();
+  // rows t0 .. t0 + 255 of the staging buffer (rows past n_filled are padding, in bounds)
+  const int c = tid & 31;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const int r = (tid >> 5) + 8 * i;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
+    *reinterpret_cast<u32x4*>(hb + (size_t)(t0 + r) * a.d + f0 + c * 8) = v;
   }
 }
 
@@ -198,63 +173,61 @@ __device__ __forceinline__ void rope_pair(f32x16 (&acc)[4][4], int n, const floa
 }
 
 __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds2];
   int g, tt, ft;
   decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
   const FillLayerPtrs Lp = a.L[g];
   const int t0 = tt * kTile, f0 = ft * kTile;
-  const int tid = threadIdx.x, rr = tid >> 3, c = tid & 7;
+  const int tid = threadIdx.x;
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.layer_ws + g * a.per_layer);
   const float* ssq = reinterpret_cast<const float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
 
-  const uint16_t* fr[8];
-  const uint16_t* tr[8];
+  DmaRows rs;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int f = f0 + rr + 32 * p;
-    fr[p] = (f < a.kv ? Lp.WK + (size_t)f * a.d : Lp.WV + (size_t)(f - a.kv) * a.d) + c * 8;
-    tr[p] = hb + (size_t)(t0 + rr + 32 * p) * a.d + c * 8;
+  for (int p = 0; p < 4; ++p) {
+    const int r = dma_row(p, tid >> 6, tid & 63);
+    const int ce = dma_chunk_elems(r, tid & 63);
+    const int f = f0 + r;
+    rs.f[p] = (f < a.kv ? Lp.WK + (size_t)f * a.d : Lp.WV + (size_t)(f - a.kv) * a.d) + ce;
+    rs.t[p] = hb + (size_t)(t0 + r) * a.d + ce;
   }
 
   f32x16 acc[4][4];
-  gemm_mainloop(acc, fr, tr, a.d, smem);
+  gemm_pipeline(acc, rs, a.d, smem);
 
-  // 1/sqrt(mean(x_hat^2) + eps) of the tile's 256 tokens, from the map kernel's partials.
-  float* rs = reinterpret_cast<float*>(smem);
+  // Per row of the tile: 1/sqrt(mean(x_hat^2) + eps) from the map kernel's partials, and
+  // the element offset of its slot in the page pools (-1: skip the row).
+  __shared__ float rstd[kTile];
+  __shared__ long long rowoff[kTile];
   {
-    const float* p = ssq + (size_t)(t0 + tid) * a.nchunk;
+    const int tok = t0 + tid;
+    const float* p = ssq + (size_t)tok * a.nchunk;
     float s = 0.f;
     for (int i = 0; i < a.nchunk; ++i) s += p[i];
-    rs[tid] = 1.0f / sqrtf(s / (float)a.d + a.eps);
+    rstd[tid] = 1.0f / sqrtf(s / (float)a.d + a.eps);
+    long long off = -1;
+    if (tok < a.n_filled) {
+      const int t = a.idx[tok];
+      if (t >= 0 && t < a.P) {
+        const int64_t lp = t / a.ps;
+        if (lp < a.n_logical) {
+          const int pg = a.bt[lp];
+          if (pg >= 0 && pg < a.num_pages) off = ((int64_t)pg * a.ps + (t - lp * a.ps)) * a.kv;
+        }
+      }
+    }
+    rowoff[tid] = off;
   }
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
-  const int fw = f0 + wf * 128;                  // first feature of this wave in [K | V]
-  const bool isK = fw < a.kv;                    // kv % 128 == 0: a wave is all K or all V
-  const int fo = isK ? fw : fw - a.kv;
-  uint16_t* base = isK ? Lp.kp : Lp.vp;
+  const bool isK = (f0 + wf * 128) < a.kv;       // kv % 128 == 0: a wave is all K or all V
   const int half = a.hd >> 1;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int tl = wt * 128 + n * 32 + (lane & 31);
     const int tok = t0 + tl;
-    bool ok = tok < a.n_filled;
-    int64_t dst = 0;
-    if (ok) {
-      const int t = a.idx[tok];
-      ok = t >= 0 && t < a.P;
-      if (ok) {
-        const int64_t lp = t / a.ps;
-        ok = lp < a.n_logical;
-        if (ok) {
-          const int pg = a.bt[lp];
-          ok = pg >= 0 && pg < a.num_pages;
-          dst = ((int64_t)pg * a.ps + (t - lp * a.ps)) * a.kv + fo;
-        }
-      }
-    }
-    const float r = rs[tl];
+    const float r = rstd[tl];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -271,16 +244,27 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
         rope_pair<2, 3, 0>(acc, n, cs, sn, h);
       }
     }
-    if (ok) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u32x2 o;
-          o.x = pack_bf16x2(acc[m][n][q * 4 + 0], acc[m][n][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[m][n][q * 4 + 2], acc[m][n][q * 4 + 3]);
-          *reinterpret_cast<u32x2*>(base + dst + m * 32 + q * 8 + h * 4) = o;
-        }
+      for (int q = 0; q < 4; ++q)
+        stage_put4(smem, tl, wf * 128 + m * 32 + q * 8 + h * 4, acc[m][n][q * 4 + 0],
+                   acc[m][n][q * 4 + 1], acc[m][n][q * 4 + 2], acc[m][n][q * 4 + 3]);
+  }
+  __syncthreads();
+  // 16-byte chunk c of every valid row goes to its page slot; chunks 0..15 and 16..31 are
+  // the tile's two 128-feature halves, each all K or all V.
+  const int c = tid & 31;
+  const int fh = f0 + (c >> 4) * 128;
+  uint16_t* base = fh < a.kv ? Lp.kp : Lp.vp;
+  const int fo = (fh < a.kv ? fh : fh - a.kv) + (c & 15) * 8;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const int r = (tid >> 5) + 8 * i;
+    const long long off = rowoff[r];
+    if (off >= 0) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
+      *reinterpret_cast<u32x4*>(base + off + fo) = v;
     }
   }
 }
