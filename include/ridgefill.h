@@ -101,7 +101,9 @@ rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
  * n_filled = 0 or n_layers = 0 only the status word is cleared (if ws is given).  Layers are independent; a caller that streams
  * maps may call once per layer.
  *
- *   x_S         device bf16 [N][x_stride]: split-layer states of all prompt rows
+ *   x_S         device bf16 [N][x_stride]: split-layer states of all prompt rows; the
+ *               prefix rows must span at most 4 GiB ((N - T) x x_stride x 2 bytes), and
+ *               x_stride is a multiple of 8
  *   filled_idx  device int32 [n_filled]: filled rows, strictly increasing, each
  *               < N - T (the tail never receives a filled entry).  Violations set
  *               RF_E_ROWS in the device status; out-of-range rows are skipped.

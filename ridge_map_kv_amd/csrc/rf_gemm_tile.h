@@ -44,95 +44,88 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[4][4], const unsigned ch
 // ---------------------------------------------------------------------------------
 // Direct-to-LDS pipeline (used by the fill GEMMs).
 //
-// A stage holds a 32-element (64-byte) reduction slice of both 256-row operands: 32 KB.
-// Four stages rotate through 128 KB of LDS; the slice kt + 4 is loaded (global_load_lds,
-// one 1 KB block of 16 rows per wave instruction) as soon as every wave has read slice kt,
-// so loads run three slices ahead of the MFMAs.  Within a slice, the fragments of the second
-// 16-wide half are read while the first half's MFMAs run, and the next slice's first-half
-// fragments are read (after the barrier) while the second half's MFMAs run.
+// A stage holds a 64-element (128-byte) reduction slice of both 256-row operands: 64 KB;
+// two stages fill 128 KB of LDS.  Each wave instruction global_load_lds_dwordx4 moves one
+// 1 KB block (8 rows x 128 bytes) straight from memory into LDS.  Slice kt + 2 is loaded
+// while slice kt + 1 is multiplied (one slice of ~2048 MFMA cycles ahead suffices), with a
+// single barrier per slice.  Every load and every fragment read is issued between two
+// MFMAs: a wave issues in order, and these instructions then go out in the shadow of an
+// MFMA that is executing, instead of holding up the next one.
 //
 // The LDS loads are issued from inline assembly: the compiler does not track them, so the
-// waits for them are explicit (vmcnt counts 8 loads per stage per thread), and it does not
-// place a full vmcnt(0) before every LDS read as it does for loads it cannot tell apart
-// from the data being read.
-constexpr int kBK2 = 32;                      // bf16 per reduction slice
-constexpr int kRow2 = kBK2 * 2;               // 64-byte LDS rows
-constexpr int kOp2 = kTile * kRow2;           // 16 KB per operand per stage
-constexpr int kStage2 = 2 * kOp2;             // 32 KB per stage
-constexpr int kNStage = 4;
-constexpr int kLds2 = kNStage * kStage2;      // 128 KB
-
-// Chunk swizzle for 64-byte rows (4 chunks): rows of one parity within an aligned group
-// of 8, and rows of one residue mod 4 within an aligned group of 16, get distinct chunk
-// positions, so fragment reads are free of bank conflicts for 32 and 64 banks alike.
-__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int lds_off64(int r, int c) { return r * kRow2 + ((c ^ swz64(r)) << 4); }
+// waits for them are explicit, and it does not place a full vmcnt(0) in front of every
+// LDS read as it does for LDS loads it cannot tell apart from the data being read.
+constexpr int kPipeBK = 64;                   // bf16 per reduction slice
+constexpr int kPipeOp = kTile * 128;          // 32 KB per operand per stage
+constexpr int kPipeStage = 2 * kPipeOp;       // 64 KB per stage
+constexpr int kPipeLds = 2 * kPipeStage;      // 128 KB
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// One 16-byte global -> LDS load per lane; lane l lands at lds + 16 l.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// One 16-byte load per lane from sbase + voff (sbase wave-uniform); lane l lands at
+// lds + 16 l.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 
-__device__ __forceinline__ void wait_vm_stages(int later) {
-  if (later >= 2)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (later == 1)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// This thread's global row pointers: rows 64 p + 16 wave + (lane >> 2), p = 0..3, of each
-// operand, already offset to the 16-byte chunk the lane fetches (its LDS position
-// lane & 3 holds logical chunk (lane & 3) ^ swz64(row)).
-struct DmaRows {
-  const uint16_t* f[4];
-  const uint16_t* t[4];
+// Block j = 4 p + wave (p = 0..7) of an operand stage: LDS rows 8 j .. 8 j + 7.  Lane l
+// lands on row 8 j + (l >> 3) at chunk position l & 7, which holds logical chunk
+// (l & 7) ^ swz(row).  base[p]: wave-uniform byte pointer, off[p]: this lane's byte offset
+// from it (row and chunk), both for reduction index 0.
+struct DmaOperand {
+  const unsigned char* base[8];
+  uint32_t off[8];
 };
 
-__device__ __forceinline__ int dma_row(int p, int wave, int lane) { return 64 * p + 16 * wave + (lane >> 2); }
-__device__ __forceinline__ int dma_chunk_elems(int row, int lane) { return (((lane & 3) ^ swz64(row)) * 8); }
+__device__ __forceinline__ int dma_block_row(int p, int wave) { return 8 * (4 * p + wave); }
+__device__ __forceinline__ int dma_lane_row(int lane) { return lane >> 3; }
+__device__ __forceinline__ int dma_chunk_elems(int row, int lane) { return ((lane & 7) ^ swz(row)) * 8; }
 
-__device__ __forceinline__ void issue_stage(const DmaRows& rs, int k0, uint32_t stage, int wave) {
+__device__ __forceinline__ void dma_block(const DmaOperand& o, int p, int kbytes, uint32_t lds_op,
+                                          int wave) {
+  dma16(o.base[p] + kbytes, o.off[p], lds_op + (4 * p + wave) * 1024);
+}
+
+// Fragment i (0..3: F rows, 4..7: T rows) of 16-wide step s of a stage.
+__device__ __forceinline__ void read_frag(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
+                                          int i, int s, int wf, int wt, int lane) {
+  const int c = s * 2 + (lane >> 5);
+  if (i < 4)
+    a[i] = *reinterpret_cast<const bf16x8*>(st + lds_off128(wf * 128 + i * 32 + (lane & 31), c));
+  else
+    b[i - 4] = *reinterpret_cast<const bf16x8*>(st + kPipeOp +
+                                                lds_off128(wt * 128 + (i - 4) * 32 + (lane & 31), c));
+}
+
+__device__ __forceinline__ void mfma_i(f32x16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4],
+                                       int i) {
+  acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i >> 2], b[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+}
+
+// 16 MFMAs on (a, b); after each of the first 8, one fragment of step s of stage st is
+// read into (na, nb).
+__device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                            const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
+                                            const unsigned char* st, int s, int wf, int wt, int lane) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int j = p * 4 + wave;               // 1 KB block = rows 16 j .. 16 j + 15
-    dma16(rs.f[p] + k0, stage + j * 1024);
-    dma16(rs.t[p] + k0, stage + kOp2 + j * 1024);
+  for (int i = 0; i < 16; ++i) {
+    mfma_i(acc, a, b, i);
+    if (i < 8) read_frag(na, nb, st, i, s, wf, wt, lane);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__device__ __forceinline__ void read_frags(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
-                                           int half, int wf, int wt, int lane) {
-  const int c = half * 2 + (lane >> 5);
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    a[m] = *reinterpret_cast<const bf16x8*>(st + lds_off64(wf * 128 + m * 32 + (lane & 31), c));
-#pragma unroll
-  for (int n = 0; n < 4; ++n)
-    b[n] = *reinterpret_cast<const bf16x8*>(st + kOp2 + lds_off64(wt * 128 + n * 32 + (lane & 31), c));
-}
-
-__device__ __forceinline__ void mma16(f32x16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-      acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
-}
-
-// acc = F[256 x K] * T[256 x K]^T with the pipeline above; K a multiple of 32.  Leaves LDS
-// free for the epilogue (ends with a barrier).
-__device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaRows& rs, int K,
-                                              unsigned char* smem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// acc = F[256 x K] * T[256 x K]^T, K a multiple of 64.  Ends with a barrier, leaving the
+// 128 KB of LDS to the epilogue.
+__device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOperand& F,
+                                              const DmaOperand& T, int K, unsigned char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
@@ -141,36 +134,56 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaRows
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
-  const int nk = K / kBK2;
+  const int nk = K / kPipeBK;
   const uint32_t base = lds_addr(smem);
-  const int pro = nk < kNStage ? nk : kNStage;
-  for (int s = 0; s < pro; ++s) issue_stage(rs, s * kBK2, base + s * kStage2, wave);
-  wait_vm_stages(pro - 1);
-  __syncthreads();
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  read_frags(a0, b0, smem, 0, wf, wt, lane);
-  // all slices but the last: the last one has no successor to wait for or prefetch, and is
-  // peeled so the loop body has a single path (no conservative waits at a merge point)
-  // sched_barrier(0) keeps each batch of fragment reads ahead of the 16 MFMAs that hide it
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    const unsigned char* cur = smem + (kt % kNStage) * kStage2;
-    read_frags(a1, b1, cur, 1, wf, wt, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(acc, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    const int issued = (nk < kt + kNStage) ? nk : kt + kNStage;
-    wait_vm_stages(issued - (kt + 2));
-    __syncthreads();                         // slice kt + 1 landed; slice kt fully read
-    if (kt + kNStage < nk)
-      issue_stage(rs, (kt + kNStage) * kBK2, base + (kt % kNStage) * kStage2, wave);
-    read_frags(a0, b0, smem + ((kt + 1) % kNStage) * kStage2, 0, wf, wt, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(acc, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < 2 && s < nk; ++s) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      dma_block(F, p, s * kPipeBK * 2, base + s * kPipeStage, wave);
+      dma_block(T, p, s * kPipeBK * 2, base + s * kPipeStage + kPipeOp, wave);
+    }
   }
-  read_frags(a1, b1, smem + ((nk - 1) % kNStage) * kStage2, 1, wf, wt, lane);
-  mma16(acc, a0, b0);
-  mma16(acc, a1, b1);
+  if (nk > 1)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // slice 0 landed (slice 1: 16 loads)
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_frag(a0, b0, smem, i, 0, wf, wt, lane);
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const unsigned char* cur = smem + (kt & 1) * kPipeStage;
+    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
+    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
+    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slice kt + 1, the only one in flight
+    __syncthreads();                                       // ... landed for every wave; slice kt read
+    const bool more = kt + 2 < nk;
+    const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
+    const uint32_t dst = base + (kt & 1) * kPipeStage;
+    const int kb = (kt + 2) * kPipeBK * 2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mfma_i(acc, a1, b1, i);
+      if (more) {
+        if (i & 1)
+          dma_block(T, i >> 1, kb, dst + kPipeOp, wave);
+        else
+          dma_block(F, i >> 1, kb, dst, wave);
+      }
+      if (i >= 8) read_frag(a0, b0, nxt, i - 8, 0, wf, wt, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  {
+    const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
+    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
+    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
+    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
+  }
   __syncthreads();
 }
 

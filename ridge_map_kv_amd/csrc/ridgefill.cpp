@@ -128,6 +128,8 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
   if (x_stride < shape->d) return fail(RF_E_SHAPE, "x_stride < d");
   if (x_stride % 8 || !aligned(x_S, 16))
     return fail(RF_E_SHAPE, "x_S must be 16-byte aligned with x_stride a multiple of 8");
+  if ((uint64_t)(P - 1) * (uint64_t)x_stride * 2u + (uint64_t)shape->d * 2u > 0xffffffffull)
+    return fail(RF_E_SHAPE, "the prefix rows of x_S span more than 4 GiB (rows x x_stride x 2 bytes)");
   if (!kv->block_table || kv->page_size < 1 || kv->num_pages < 1 || kv->n_logical < 1)
     return fail(RF_E_INVALID, "paged layout: block_table, page_size, num_pages, n_logical");
   if (kv->n_logical < (P + kv->page_size - 1) / kv->page_size)
