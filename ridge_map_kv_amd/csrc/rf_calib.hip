@@ -39,7 +39,8 @@ constexpr int kMaxCalibLayers = 64;
 struct CalibArgs {
   const uint16_t* xS;
   const uint16_t* xl[kMaxCalibLayers];
-  int n_rows, d, n_layers, nt;   // nt = d / 256
+  int row0;                      // first row this launch covers
+  int n_rows, d, n_layers, nt;   // rows covered (from row0); nt = d / 256
   int ngram;                     // lower-triangle tiles of G
   float* G;
   float* YX;
@@ -135,33 +136,74 @@ __device__ __forceinline__ void gram_tile(int k, int& ti, int& tj) {
   ti = k - j * (j + 1) / 2;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const uint16_t* X = a.xS;      // F operand: features of x_S (output columns)
-  const uint16_t* Y;             // T operand: features of x_S (Gram) or x_l (output rows)
+// Tile k of one launch: lower-triangle tiles of G first, then every layer's cross tiles in
+// groups of kTokGroup output-row tiles against all column tiles.  X = x_S (output
+// columns), Y = x_S or x_l (output rows).
+struct CalibTile {
+  const uint16_t* X;
+  const uint16_t* Y;
   float* out;
+  int f0, o0;
+};
+
+__device__ __forceinline__ CalibTile calib_tile(const CalibArgs& a, int tile) {
+  CalibTile t;
   int fi, tj;
+  t.X = a.xS;
   if (tile < a.ngram) {
     gram_tile(tile, fi, tj);     // rows tj >= columns fi
-    Y = a.xS;
-    out = a.G;
+    t.Y = a.xS;
+    t.out = a.G;
   } else {
     const int k = tile - a.ngram;
     const int per = a.nt * a.nt;
     const int l = k / per;
     const int r = k - l * per;
-    // groups of kTokGroup output-row tiles against every column tile
     const int tg = r / (kTokGroup * a.nt);
     const int within = r - tg * kTokGroup * a.nt;
     const int left = a.nt - tg * kTokGroup;
     const int gsz = left < kTokGroup ? left : kTokGroup;
     fi = within / gsz;
     tj = tg * kTokGroup + (within - fi * gsz);
-    Y = a.xl[l];
-    out = a.YX + (size_t)l * a.d * a.d;
+    t.Y = a.xl[l];
+    t.out = a.YX + (size_t)l * a.d * a.d;
   }
-  const int f0 = fi * kTile, o0 = tj * kTile;
+  t.f0 = fi * kTile;
+  t.o0 = tj * kTile;
+  return t;
+}
+
+// out[o][i .. i+3] += the lane's four consecutive M-entries (M = x_S feature i, N = o).
+__device__ __forceinline__ void calib_store(const f32x16 (&acc)[4][4], const CalibTile& t, int d) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int o = t.o0 + wt * 128 + n * 32 + (lane & 31);
+    float* row = t.out + (size_t)o * d;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = t.f0 + wf * 128 + m * 32 + q * 8 + h * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
+        v[0] += acc[m][n][q * 4 + 0];
+        v[1] += acc[m][n][q * 4 + 1];
+        v[2] += acc[m][n][q * 4 + 2];
+        v[3] += acc[m][n][q * 4 + 3];
+        *reinterpret_cast<f32x4*>(row + i) = v;
+      }
+  }
+}
+
+// Rows row0 .. row0 + n_rows - 1 (any count; rows past the end read as zero), register-
+// staged with the transpose done in registers.  Used for the ragged row tail.
+__global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  const CalibTile t = calib_tile(a, xcd_remap(blockIdx.x, gridDim.x));
+  const uint16_t* X = t.X + (size_t)a.row0 * a.d;
+  const uint16_t* Y = t.Y + (size_t)a.row0 * a.d;
+  const int f0 = t.f0, o0 = t.o0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wf = wave >> 1, wt = wave & 1, rg = tid >> 5, fg = tid & 31;
 
@@ -195,25 +237,152 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a)
     }
     __syncthreads();
   }
+  calib_store(acc, t, a.d);
+}
 
-  const int h = lane >> 5;
+// ---------------------------------------------------------------- full 64-row slices
+// The fill's pipeline (two 64 KB stages, loads straight into LDS one slice ahead, loads
+// and fragment reads between MFMAs), with LDS holding each operand's 64 rows x 256
+// features untransposed: 512 bytes per row, 16-byte chunk c of row r at chunk
+// c ^ ((r & 3) << 1).  The fragments come out transposed through ds_read_b64_tr_b16:
+// within each 16-lane group, lane i receives element i % 4 of the 8-byte pieces named by
+// lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  With lane p of the group naming reduction row
+// (p >> 2) and feature 4 (p & 3), lane i receives feature i at four consecutive rows; two
+// such reads give the eight consecutive reduction indices of a v_mfma_f32_32x32x16_bf16
+// operand.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int tr_off(int r, int col) {
+  return r * 512 + ((((col >> 3) ^ ((r & 3) << 1)) << 4) | ((col & 7) << 1));
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* op, int s, int col0, int lane) {
+  const int g = (lane >> 4) & 3, p = lane & 15;
+  const int col = col0 + (g & 1) * 16 + 4 * (p & 3);
+  const int r = 16 * s + 8 * (g >> 1) + (p >> 2);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)(op + tr_off(r, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)(op + tr_off(r + 4, col)));
+  struct Pair { s16x4 a, b; } pr = {lo, hi};
+  return __builtin_bit_cast(bf16x8, pr);
+}
+
+__device__ __forceinline__ void read_frag_tr(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
+                                             int i, int s, int wf, int wt, int lane) {
+  if (i < 4)
+    a[i] = tr_frag(st, s, wf * 128 + i * 32, lane);
+  else
+    b[i - 4] = tr_frag(st + kPipeOp, s, wt * 128 + (i - 4) * 32, lane);
+}
+
+__device__ __forceinline__ void mfma16_read_tr(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                               const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
+                                               const unsigned char* st, int s, int wf, int wt, int lane) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int o = o0 + wt * 128 + n * 32 + (lane & 31);
-    float* row = out + (size_t)o * a.d;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = f0 + wf * 128 + m * 32 + q * 8 + h * 4;
-        f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
-        v[0] += acc[m][n][q * 4 + 0];
-        v[1] += acc[m][n][q * 4 + 1];
-        v[2] += acc[m][n][q * 4 + 2];
-        v[3] += acc[m][n][q * 4 + 3];
-        *reinterpret_cast<f32x4*>(row + i) = v;
-      }
+  for (int i = 0; i < 16; ++i) {
+    mfma_i(acc, a, b, i);
+    if (i < 8) read_frag_tr(na, nb, st, i, s, wf, wt, lane);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// DMA block j = 4 p + wave (p = 0..7) of an operand stage: rows 2 j, 2 j + 1 (1 KB).  Lane
+// l lands on row 2 j + (l >> 5), chunk position l & 31, which holds logical chunk
+// (l & 31) ^ ((row & 3) << 1).
+__device__ __forceinline__ void calib_operand(DmaOperand& o, const uint16_t* x, int d, int col0,
+                                              int wave, int lane) {
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r0 = 2 * (4 * p + wave), r = r0 + (lane >> 5);
+    const int c = (lane & 31) ^ ((r & 3) << 1);
+    o.base[p] = reinterpret_cast<const unsigned char*>(x + (size_t)r0 * d + col0);
+    o.off[p] = (uint32_t)((((lane >> 5) * d) + c * 8) * 2);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
+  const CalibTile t = calib_tile(a, xcd_remap(blockIdx.x, gridDim.x));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wave >> 1, wt = wave & 1;
+  DmaOperand F, T;
+  calib_operand(F, t.X + (size_t)a.row0 * a.d, a.d, t.f0, wave, lane);
+  calib_operand(T, t.Y + (size_t)a.row0 * a.d, a.d, t.o0, wave, lane);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+
+  const int nk = a.n_rows / kPipeBK;                 // a multiple of 64 rows
+  const int64_t slice = (int64_t)kPipeBK * a.d * 2;  // bytes between consecutive slices
+  const uint32_t base = lds_addr(smem);
+  for (int s = 0; s < 2 && s < nk; ++s) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      dma_block(F, p, (int)0, base + s * kPipeStage, wave);
+      dma_block(T, p, (int)0, base + s * kPipeStage + kPipeOp, wave);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      F.base[p] += slice;
+      T.base[p] += slice;
+    }
+  }
+  if (nk > 1)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_frag_tr(a0, b0, smem, i, 0, wf, wt, lane);
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const unsigned char* cur = smem + (kt & 1) * kPipeStage;
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
+    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const bool more = kt + 2 < nk;
+    const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
+    const uint32_t dst = base + (kt & 1) * kPipeStage;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mfma_i(acc, a1, b1, i);
+      if (more) {
+        if (i & 1)
+          dma_block(T, i >> 1, 0, dst + kPipeOp, wave);
+        else
+          dma_block(F, i >> 1, 0, dst, wave);
+      }
+      if (i >= 8) read_frag_tr(a0, b0, nxt, i - 8, 0, wf, wt, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        F.base[p] += slice;
+        T.base[p] += slice;
+      }
+    }
+  }
+  {
+    const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
+    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
+  }
+  calib_store(acc, t, a.d);
 }
 
 }  // namespace
@@ -247,7 +416,6 @@ hipError_t launch_calibrate(void* state, int d, int n_layers, const uint16_t* xS
   CalibArgs a = {};
   a.xS = xS;
   for (int l = 0; l < n_layers; ++l) a.xl[l] = xl[l];
-  a.n_rows = (int)n_rows;
   a.d = d;
   a.n_layers = n_layers;
   a.nt = d / kTile;
@@ -255,8 +423,16 @@ hipError_t launch_calibrate(void* state, int d, int n_layers, const uint16_t* xS
   a.G = reinterpret_cast<float*>(st + L.G);
   a.YX = reinterpret_cast<float*>(st + L.YX);
   const int tiles = a.ngram + n_layers * a.nt * a.nt;
-  {
+  const int bulk = (int)(n_rows / kPipeBK) * kPipeBK;
+  if (bulk > 0) {
+    a.row0 = 0;
+    a.n_rows = bulk;
     ProfileScope ps(RF_KERNEL_CALIB_MOMENTS, stream);
+    hipLaunchKernelGGL(calib_moments_dma_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+  }
+  if (n_rows > bulk) {
+    a.row0 = bulk;
+    a.n_rows = (int)(n_rows - bulk);
     hipLaunchKernelGGL(calib_moments_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
