@@ -38,36 +38,14 @@ def make_fill_inputs(cfg, dev, maps=None):
     from ridge_map_kv_amd import binding as B
     from ridge_map_kv_amd import synth
 
-    g = torch.Generator(device=dev)
-    g.manual_seed(cfg.seed)
-    d, kv = cfg.d, cfg.kv
-    xS = torch.randn((cfg.N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    filled = B.ridgefill_partition(cfg.N, cfg.T, synth.exact_mask(cfg))
-    idx = torch.from_numpy(filled).to(dev)
-    table_np, num_pages = synth.block_table(cfg.N, cfg.page_size, cfg.seed)
-    table = torch.from_numpy(table_np).to(dev)
-    layers = []
-    s = 1.0 / np.sqrt(d)
-    for l in range(cfg.n_upper):
-        if maps is not None:
-            A, b = maps[l]
-        else:
-            U = torch.randn((d, 64), generator=g, device=dev) * s
-            V = torch.randn((d, 64), generator=g, device=dev) * s
-            A = (torch.eye(d, device=dev) + 0.5 * (U @ V.T)).to(torch.bfloat16)
-            b = torch.randn(d, generator=g, device=dev)
-        w = (1.0 + 0.1 * torch.randn(d, generator=g, device=dev)).to(torch.bfloat16)
-        WK = (torch.randn((kv, d), generator=g, device=dev) * s).to(torch.bfloat16)
-        WV = (torch.randn((kv, d), generator=g, device=dev) * s).to(torch.bfloat16)
-        pages = (num_pages, cfg.page_size, cfg.n_kv, cfg.head_dim)
-        layers.append(dict(A=A.contiguous(), b=b.float().contiguous(), norm_w=w, W_K=WK, W_V=WV,
-                           k_pages=torch.zeros(pages, dtype=torch.bfloat16, device=dev),
-                           v_pages=torch.zeros(pages, dtype=torch.bfloat16, device=dev)))
-    shape = B.make_shape(d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
-    ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, len(filled), cfg.n_upper),
-                     dtype=torch.uint8, device=dev)
-    return dict(xS=xS, filled=filled, idx=idx, table=table, table_np=table_np,
-                num_pages=num_pages, layers=layers, shape=shape, ws=ws)
+    inp = synth.device_fill_inputs(cfg, dev, maps=maps)
+    filled = B.ridgefill_partition(cfg.N, cfg.T, inp["exact_mask"])
+    inp["filled"] = filled
+    inp["idx"] = torch.from_numpy(filled).to(dev)
+    inp["shape"] = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
+    inp["ws"] = torch.empty(B.ridgefill_fill_workspace_bytes(inp["shape"], len(filled), cfg.n_upper),
+                            dtype=torch.uint8, device=dev)
+    return inp
 
 
 def fill_step(cfg, inp):
@@ -121,34 +99,6 @@ def cpu_baseline_fill(cfg, inp, budget_s: float = 15.0):
                       f"workload (NumPy float64), {spent:.1f} s"}
 
 
-def make_calib_chunks(ccfg, dev):
-    """Synthetic calibration rows on the GPU, chunk by chunk: x_l = W_true,l x_S + c_l +
-    s * t3 with W_true,l = I + U_l diag(0.5) V_l^T (rank 64) and Student-t(3) noise."""
-    import torch
-
-    g = torch.Generator(device=dev)
-    g.manual_seed(ccfg.seed)
-    d, L = ccfg.d, ccfg.n_layers
-    s = 1.0 / np.sqrt(d)
-    U = [torch.randn((d, 64), generator=g, device=dev) * s for _ in range(L)]
-    V = [torch.randn((d, 64), generator=g, device=dev) * s for _ in range(L)]
-    c = [torch.randn(d, generator=g, device=dev) for _ in range(L)]
-    chunks = []
-    for r0 in range(0, ccfg.rows, ccfg.chunk):
-        n = min(ccfg.chunk, ccfg.rows - r0)
-        xs = torch.randn((n, d), generator=g, device=dev)
-        xl = []
-        for l in range(L):
-            z = torch.randn((n, d), generator=g, device=dev)
-            chi = sum(torch.randn((n, d), generator=g, device=dev) ** 2 for _ in range(3))
-            t3 = z / torch.sqrt(chi / 3.0)
-            y = xs + 0.5 * ((xs @ V[l]) @ U[l].T) + c[l] + ccfg.noise_scale * t3
-            xl.append(y.to(torch.bfloat16))
-            del z, chi, t3, y
-        chunks.append((xs.to(torch.bfloat16), xl))
-    return chunks
-
-
 def run_calibration(ccfg, dev, passes: int = 2):
     """Times ridgefill_calibrate over all chunks (after one untimed pass), then one solve
     per lambda; returns the timing dict and the lambda = 0.03 maps for the fill."""
@@ -157,7 +107,8 @@ def run_calibration(ccfg, dev, passes: int = 2):
 
     d, L = ccfg.d, ccfg.n_layers
     log(f"bench: generating {ccfg.rows} calibration rows x {L + 1} matrices")
-    chunks = make_calib_chunks(ccfg, dev)
+    from ridge_map_kv_amd import synth
+    chunks = synth.device_calib_chunks(ccfg, dev)
     state = torch.empty(B.ridgefill_calib_state_bytes(d, L), dtype=torch.uint8, device=dev)
 
     def one_pass():

@@ -163,3 +163,90 @@ def sparse_dyadic_matrix(d_out: int, d_in: int, seed: int, per_row: int = 2) -> 
         cols = g.choice(d_in, size=per_row, replace=False)
         W[o, cols] = g.choice(vals, size=per_row)
     return W
+
+
+# --------------------------------------------------------------------------- on the GPU
+# Large workloads are drawn on the device with torch's seeded generator (same recipes).
+
+def device_fill_inputs(cfg, dev, maps=None, sentinel: bool = False):
+    """Seeded fill inputs on `dev` for a FillConfig: x_S bf16 [N, d]; per upper layer A
+    (bf16, near-identity unless `maps` gives (A bf16, b fp32) pairs), b fp32, norm_w, W_K,
+    W_V (bf16) and K/V page pools (zeros, or 0xFFFF everywhere when `sentinel`); the block
+    table; the exact-row mask."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    d, kv = cfg.d, cfg.kv
+    xS = torch.randn((cfg.N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    table_np, num_pages = block_table(cfg.N, cfg.page_size, cfg.seed)
+    s = 1.0 / np.sqrt(d)
+    layers = []
+    for l in range(cfg.n_upper):
+        if maps is not None:
+            A, b = maps[l]
+        else:
+            U = torch.randn((d, TRUE_MAP_RANK), generator=g, device=dev) * s
+            V = torch.randn((d, TRUE_MAP_RANK), generator=g, device=dev) * s
+            A = (torch.eye(d, device=dev) + TRUE_MAP_GAIN * (U @ V.T)).to(torch.bfloat16)
+            b = torch.randn(d, generator=g, device=dev)
+            del U, V
+        w = (1.0 + 0.1 * torch.randn(d, generator=g, device=dev)).to(torch.bfloat16)
+        WK = (torch.randn((kv, d), generator=g, device=dev) * s).to(torch.bfloat16)
+        WV = (torch.randn((kv, d), generator=g, device=dev) * s).to(torch.bfloat16)
+        shape = (num_pages, cfg.page_size, cfg.n_kv, cfg.head_dim)
+        pools = []
+        for _ in range(2):
+            t = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+            if sentinel:
+                t.view(torch.int16).fill_(-1)
+            pools.append(t)
+        layers.append(dict(A=A.contiguous(), b=b.float().contiguous(), norm_w=w, W_K=WK, W_V=WV,
+                           k_pages=pools[0], v_pages=pools[1]))
+    return dict(xS=xS, table=torch.from_numpy(table_np).to(dev), table_np=table_np,
+                num_pages=num_pages, layers=layers, exact_mask=exact_mask(cfg))
+
+
+def device_calib_chunks(ccfg, dev):
+    """Seeded calibration rows on `dev`, chunk by chunk: x_l = W_true,l x_S + c_l + s * e with
+    W_true,l = I + U_l diag(0.5) V_l^T (rank 64) and e Student-t(dof) built from normals
+    (z / sqrt(chi^2_dof / dof)).  Returns [(x_S bf16 [n, d], [x_l bf16 [n, d]] * L)]."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(ccfg.seed)
+    d, L = ccfg.d, ccfg.n_layers
+    s = 1.0 / np.sqrt(d)
+    dof = int(ccfg.noise_dof)
+    U = [torch.randn((d, TRUE_MAP_RANK), generator=g, device=dev) * s for _ in range(L)]
+    V = [torch.randn((d, TRUE_MAP_RANK), generator=g, device=dev) * s for _ in range(L)]
+    c = [torch.randn(d, generator=g, device=dev) for _ in range(L)]
+    chunks = []
+    for r0 in range(0, ccfg.rows, ccfg.chunk):
+        n = min(ccfg.chunk, ccfg.rows - r0)
+        xs = torch.randn((n, d), generator=g, device=dev)
+        xl = []
+        for l in range(L):
+            z = torch.randn((n, d), generator=g, device=dev)
+            chi = sum(torch.randn((n, d), generator=g, device=dev) ** 2 for _ in range(dof))
+            e = z / torch.sqrt(chi / dof)
+            y = xs + TRUE_MAP_GAIN * ((xs @ V[l]) @ U[l].T) + c[l] + ccfg.noise_scale * e
+            xl.append(y.to(torch.bfloat16))
+            del z, chi, e, y
+        chunks.append((xs.to(torch.bfloat16), xl))
+    return chunks
+
+
+def device_hadamard_columns(rows: int, cols: int, dev, first_col: int = 1):
+    """Columns first_col .. first_col + cols - 1 of the Sylvester Hadamard matrix of order
+    2^k >= rows (entry (r, c) = (-1)^popcount(r & c)), rows 0 .. rows-1, float32 on `dev`."""
+    import torch
+
+    r = torch.arange(rows, device=dev, dtype=torch.int64)[:, None]
+    c = torch.arange(first_col, first_col + cols, device=dev, dtype=torch.int64)[None, :]
+    v = r & c
+    par = torch.zeros_like(v)
+    while bool((v != 0).any()):
+        par ^= v & 1
+        v = v >> 1
+    return (1 - 2 * par).to(torch.float32)
