@@ -33,6 +33,39 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+# Sources that define the fill kernels; a recorded HBM-traffic measurement is reported only
+# while their hash still matches the one recorded with it.
+FILL_KERNEL_SOURCES = ["ridge_map_kv_amd/csrc/rf_fill.hip", "ridge_map_kv_amd/csrc/rf_gemm_tile.h",
+                       "ridge_map_kv_amd/csrc/rf_common.h", "ridge_map_kv_amd/csrc/rf_internal.h"]
+
+
+def fill_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in FILL_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the counter summary under profiles/, or None
+    if there is none for the current kernel sources."""
+    import glob
+    import re
+    want = fill_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                m = re.match(r"\s*traffic-record:\s*(\{.*\})\s*$", line)
+                if not m:
+                    continue
+                rec = json.loads(m.group(1))
+                if rec.get("kernel") == kernel and rec.get("source_sha256") == want:
+                    return rec
+    return None
+
+
 def make_fill_inputs(cfg, dev, maps=None):
     import torch
     from ridge_map_kv_amd import binding as B
@@ -295,6 +328,12 @@ def main():
                                "tflops": kv_flops_launch / (kv_avg * 1e-3) / 1e12},
         },
     }
+    rec = recorded_traffic("fill_map_kernel")
+    if rec is not None:
+        out["roofline"]["traffic"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        out["roofline"]["traffic_detail"] = {
+            "fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
+            "algorithmic_bytes": rec.get("algorithmic_bytes"), "source": rec.get("summary")}
     if calib is not None:
         out["calibration"] = calib
         out["solve"] = solve
