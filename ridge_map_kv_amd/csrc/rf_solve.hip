@@ -139,15 +139,23 @@ __device__ __forceinline__ void store44(double* dst, size_t ld, const double (&a
     }
 }
 
-// Factor diagonal block k in place (lower) and store its inverse in linv[k].
+// Factor diagonal block k in place (lower) and store its inverse in linv[k].  256 threads:
+// in the right-looking factorisation, thread t owns row t / 4 and the 16 columns
+// 16 (t % 4) .. + 15 of the trailing update; the inverse X = L^-1 is formed the same way
+// (row j of X scaled by 1 / L_jj, then subtracted from the rows below with weight L_ij).
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k, double* linv,
                                                         unsigned* status) {
   __shared__ double a[NB * LDT];
   __shared__ double x[NB * LDT];
   double* blk = C + (size_t)k * NB * d + (size_t)k * NB;
-  load64(a, blk, d, false);
-  __syncthreads();
   const int t = threadIdx.x;
+  const int row = t >> 2, c0 = (t & 3) * 16;
+  for (int e = t; e < NB * NB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    a[r * LDT + c] = blk[(size_t)r * d + c];
+    x[r * LDT + c] = r == c ? 1.0 : 0.0;
+  }
+  __syncthreads();
   for (int j = 0; j < NB; ++j) {
     if (t == 0) {
       double p = a[j * LDT + j];
@@ -159,31 +167,34 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k,
     }
     __syncthreads();
     const double piv = a[j * LDT + j];
-    for (int i = j + 1 + t; i < NB; i += blockDim.x) a[i * LDT + j] /= piv;
+    if (t > j && t < NB) a[t * LDT + j] /= piv;
     __syncthreads();
-    // trailing update of the lower part: a[i][c] -= a[i][j] a[c][j], j < c <= i
-    const int m = NB - j - 1;
-    for (int e = t; e < m * m; e += blockDim.x) {
-      const int i = j + 1 + e / m, c = j + 1 + e % m;
-      if (c <= i) a[i * LDT + c] -= a[i * LDT + j] * a[c * LDT + j];
+    if (row > j) {
+      const double lij = a[row * LDT + j];
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        const int c = c0 + cc;
+        if (c > j && c <= row) a[row * LDT + c] -= lij * a[c * LDT + j];
+      }
     }
     __syncthreads();
   }
-  // inverse of the lower factor, one column per thread: x = L^-1
-  if (t < NB) {
-    const int c = t;
-    for (int r = 0; r < NB; ++r) {
-      double s = (r == c) ? 1.0 : 0.0;
-      for (int q = c; q < r; ++q) s -= a[r * LDT + q] * x[q * LDT + c];
-      x[r * LDT + c] = r < c ? 0.0 : s / a[r * LDT + r];
+  for (int j = 0; j < NB; ++j) {
+    const double inv = 1.0 / a[j * LDT + j];
+    if (t < NB) x[j * LDT + t] *= inv;
+    __syncthreads();
+    if (row > j) {
+      const double lij = a[row * LDT + j];
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) x[row * LDT + c0 + cc] -= lij * x[j * LDT + c0 + cc];
     }
+    __syncthreads();
   }
-  __syncthreads();
   double* li = linv + (size_t)k * NB * NB;
-  for (int e = t; e < NB * NB; e += blockDim.x) {
+  for (int e = t; e < NB * NB; e += 256) {
     const int r = e >> 6, c = e & 63;
     blk[(size_t)r * d + c] = c <= r ? a[r * LDT + c] : 0.0;
-    li[e] = x[r * LDT + c];
+    li[e] = c <= r ? x[r * LDT + c] : 0.0;
   }
 }
 
