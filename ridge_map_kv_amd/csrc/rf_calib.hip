@@ -277,12 +277,17 @@ __device__ __forceinline__ void read_frag_tr(bf16x8 (&a)[4], bf16x8 (&b)[4], con
     b[i - 4] = tr_frag(st + kPipeOp, s, wt * 128 + (i - 4) * 32, lane);
 }
 
+// As mfma16_read, with transposed fragment reads; with `dma`, load issues 8 .. 15 of the
+// slice the operand pointers hold go out after the even-numbered MFMAs, into stage dst.
 __device__ __forceinline__ void mfma16_read_tr(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
                                                const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
-                                               const unsigned char* st, int s, int wf, int wt, int lane) {
+                                               const unsigned char* st, int s, int wf, int wt, int lane,
+                                               bool dma, const DmaOperand& F, const DmaOperand& T,
+                                               uint32_t dst, int wave) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     mfma_i(acc, a, b, i);
+    if (dma && !(i & 1)) dma_issue(F, T, 8 + (i >> 1), 0, dst, wave);
     if (i < 8) read_frag_tr(na, nb, st, i, s, wf, wt, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -344,11 +349,23 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
   bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) read_frag_tr(a0, b0, smem, i, 0, wf, wt, lane);
+  // Loads split as in the fill pipeline: blocks 0..3 of each operand right after the
+  // barrier that frees a stage, blocks 4..7 during the next slice's first step.  Each block
+  // pointer moves on by one slice once its load has gone out.
   for (int kt = 0; kt < nk - 1; ++kt) {
     const unsigned char* cur = smem + (kt & 1) * kPipeStage;
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
-    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+    const bool pend = kt >= 1;                           // second half of slice kt + 1
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, pend, F, T,
+                   base + ((kt + 1) & 1) * kPipeStage, wave);
+    if (pend) {
+#pragma unroll
+      for (int p = 4; p < 8; ++p) {
+        F.base[p] += slice;
+        T.base[p] += slice;
+      }
+    }
+    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const bool more = kt + 2 < nk;
@@ -357,18 +374,13 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mfma_i(acc, a1, b1, i);
-      if (more) {
-        if (i & 1)
-          dma_block(T, i >> 1, 0, dst + kPipeOp, wave);
-        else
-          dma_block(F, i >> 1, 0, dst, wave);
-      }
+      if (more && !(i & 1)) dma_issue(F, T, i >> 1, 0, dst, wave);
       if (i >= 8) read_frag_tr(a0, b0, nxt, i - 8, 0, wf, wt, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < 4; ++p) {
         F.base[p] += slice;
         T.base[p] += slice;
       }
@@ -376,9 +388,9 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
   }
   {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
-    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, wave);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }

@@ -12,8 +12,9 @@
 //         epilogue: + b, per-row sum of squares over each 128-feature chunk (fp32,
 //         written to a small partials buffer), bf16(x_hat * norm_w) to the workspace.
 //   kv    [token][2*kv]     (x_hat*w) * [W_K; W_V]^T
-//         epilogue: * 1/sqrt(mean(x_hat^2)+eps) from the partials, RoPE on the key
-//         half in registers, bf16 store into the paged cache.
+//         epilogue: * 1/sqrt(mean(x_hat^2)+eps) (reduced from the partials by a small
+//         kernel between the two), RoPE on the key half in registers, bf16 store into
+//         the paged cache.
 // The weight rows sit on the MFMA M axis and the token rows on N, so in the 32x32 MFMA
 // result each lane holds one token and runs of four consecutive features: the row
 // reduction needs one cross-lane add, RoPE's pair (j, j + hd/2) sits in the same lane
@@ -38,13 +39,11 @@ struct FillKArgs {
   int d, kv, hd;
   float eps;
   int mpad, nchunk;             // nchunk = d / 128 sum-of-squares partials per row
-  unsigned char* layer_ws;      // per layer: hbuf [mpad][d] bf16, then ssq [mpad][nchunk]
-  size_t per_layer, per_layer_h;
+  unsigned char* layer_ws;      // per layer: hbuf [mpad][d] bf16, ssq [mpad][nchunk], rstd [mpad]
+  size_t per_layer, per_layer_h, per_layer_ssq;
   const float* rcos;
   const float* rsin;
-  const int32_t* bt;
-  int64_t n_logical;
-  int ps, num_pages;
+  const int64_t* row_slot;
   int ntt, nft;                 // token tiles, feature tiles of this launch
 };
 
@@ -112,9 +111,19 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
     }
   }
 
+  // bias and norm weight of feature f0 + tid, fetched under the main loop and parked in LDS
+  // for the epilogue
+  __shared__ __attribute__((aligned(16))) float sbias[kTile];
+  __shared__ __attribute__((aligned(16))) float swt[kTile];
+  const float my_b = Lp.b[f0 + tid];
+  const uint16_t my_w = Lp.w[f0 + tid];
+
   f32x16 acc[4][4];
   gemm_pipeline(acc, Fo, To, a.d, smem);
 
+  sbias[tid] = my_b;
+  swt[tid] = bf16_to_f32(my_w);
+  __syncthreads();
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
   uint16_t* hb = reinterpret_cast<uint16_t*>(a.layer_ws + g * a.per_layer);
   float* ssq = reinterpret_cast<float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
@@ -124,9 +133,9 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int fl = wf * 128 + m * 32 + q * 8 + h * 4;      // feature within the tile
-      const f32x4 bias = *reinterpret_cast<const f32x4*>(Lp.b + f0 + fl);
-      const u32x2 wb = *reinterpret_cast<const u32x2*>(Lp.w + f0 + fl);
-      const float w0 = lo16(wb.x), w1 = hi16(wb.x), w2 = lo16(wb.y), w3 = hi16(wb.y);
+      const f32x4 bias = *reinterpret_cast<const f32x4*>(sbias + fl);
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(swt + fl);
+      const float w0 = wv.x, w1 = wv.y, w2 = wv.z, w3 = wv.w;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int tl = wt * 128 + n * 32 + (lane & 31);
@@ -161,14 +170,17 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 }
 
 // RoPE on one pair of 32-feature MFMA blocks (mlo holds pair index j, mhi holds j + hd/2).
+// cs, sn: this lane's entry for j = 4 h in the blocked tables (row-block of 32 rows, then
+// groups of 4 consecutive j), so pair index j sits (j / 4) * 128 floats further on, and the
+// 32 lanes of a half-wave read one contiguous 512-byte run.
 template <int MLO, int MHI, int JOFF>
 __device__ __forceinline__ void rope_pair(f32x16 (&acc)[4][4], int n, const float* cs,
-                                          const float* sn, int h) {
+                                          const float* sn) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int j = JOFF + q * 8 + h * 4;
-    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + j);
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + j);
+    const int jb = (JOFF / 4 + q * 2) * 128;
+    const f32x4 cv = *reinterpret_cast<const f32x4*>(cs + jb);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + jb);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float lo = acc[MLO][n][q * 4 + e], hi = acc[MHI][n][q * 4 + e];
@@ -186,7 +198,8 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
   const int t0 = tt * kTile, f0 = ft * kTile;
   const int tid = threadIdx.x;
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.layer_ws + g * a.per_layer);
-  const float* ssq = reinterpret_cast<const float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
+  const float* rs_tab = reinterpret_cast<const float*>(a.layer_ws + g * a.per_layer +
+                                                       a.per_layer_h + a.per_layer_ssq);
 
   DmaOperand Fo, To;
   {
@@ -204,32 +217,18 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
     }
   }
 
+  // Per row of the tile: 1/sqrt(mean(x_hat^2) + eps), and the element offset of its slot in
+  // the page pools (-1: skip the row); fetched under the main loop, parked in LDS after it.
+  __shared__ float rstd[kTile];
+  __shared__ long long rowoff[kTile];
+  const float my_r = rs_tab[t0 + tid];
+  const long long my_off = a.row_slot[t0 + tid];
+
   f32x16 acc[4][4];
   gemm_pipeline(acc, Fo, To, a.d, smem);
 
-  // Per row of the tile: 1/sqrt(mean(x_hat^2) + eps) from the map kernel's partials, and
-  // the element offset of its slot in the page pools (-1: skip the row).
-  __shared__ float rstd[kTile];
-  __shared__ long long rowoff[kTile];
-  {
-    const int tok = t0 + tid;
-    const float* p = ssq + (size_t)tok * a.nchunk;
-    float s = 0.f;
-    for (int i = 0; i < a.nchunk; ++i) s += p[i];
-    rstd[tid] = 1.0f / sqrtf(s / (float)a.d + a.eps);
-    long long off = -1;
-    if (tok < a.n_filled) {
-      const int t = a.idx[tok];
-      if (t >= 0 && t < a.P) {
-        const int64_t lp = t / a.ps;
-        if (lp < a.n_logical) {
-          const int pg = a.bt[lp];
-          if (pg >= 0 && pg < a.num_pages) off = ((int64_t)pg * a.ps + (t - lp * a.ps)) * a.kv;
-        }
-      }
-    }
-    rowoff[tid] = off;
-  }
+  rstd[tid] = my_r;
+  rowoff[tid] = my_off;
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
@@ -239,21 +238,21 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
   for (int n = 0; n < 4; ++n) {
     const int tl = wt * 128 + n * 32 + (lane & 31);
     const int tok = t0 + tl;
-    const float r = rstd[tl];
+    const float r = rstd[tl];   // rows past n_filled: finite padding, never stored
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[m][n][e] *= r;
     if (isK) {
-      const int tc = tok < a.n_filled ? tok : a.n_filled - 1;
-      const float* cs = a.rcos + (size_t)tc * half;
-      const float* sn = a.rsin + (size_t)tc * half;
+      const size_t e0 = ((size_t)(tok >> 5) * (half >> 2) + h) * 128 + (tok & 31) * 4;
+      const float* cs = a.rcos + e0;
+      const float* sn = a.rsin + e0;
       if (a.hd == 128) {
-        rope_pair<0, 2, 0>(acc, n, cs, sn, h);
-        rope_pair<1, 3, 32>(acc, n, cs, sn, h);
+        rope_pair<0, 2, 0>(acc, n, cs, sn);
+        rope_pair<1, 3, 32>(acc, n, cs, sn);
       } else {
-        rope_pair<0, 1, 0>(acc, n, cs, sn, h);
-        rope_pair<2, 3, 0>(acc, n, cs, sn, h);
+        rope_pair<0, 1, 0>(acc, n, cs, sn);
+        rope_pair<2, 3, 0>(acc, n, cs, sn);
       }
     }
 #pragma unroll
@@ -281,14 +280,19 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
   }
 }
 
-// cos/sin of angle t * theta^(-2j/hd) for every filled row, computed in fp64.
-__global__ void rope_table_kernel(const int32_t* idx, int n_filled, int64_t P, int hd,
+// cos/sin of angle t * theta^(-2j/hd) for every row of the padded filled list (padding
+// rows use t = 0), computed in fp64 and stored in the blocked layout the kv epilogue reads:
+// element ((row / 32) * (hd / 8) + j / 4) * 128 + (row % 32) * 4 + j % 4.
+__global__ void rope_table_kernel(const int32_t* idx, int n_filled, int mpad, int64_t P, int hd,
                                   double theta, float* rcos, float* rsin) {
-  const int half = hd >> 1;
+  const int half = hd >> 1, jg = half >> 2;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)n_filled * half) return;
-  const int tok = (int)(i / half), j = (int)(i - (int64_t)tok * half);
-  int t = idx[tok];
+  if (i >= (int64_t)mpad * half) return;
+  const int e = (int)(i & 3), rl = (int)((i >> 2) & 31);
+  const int64_t blk = i >> 7;
+  const int rb = (int)(blk / jg), j = (int)(blk - (int64_t)rb * jg) * 4 + e;
+  const int row = rb * 32 + rl;
+  int t = row < n_filled ? idx[row] : 0;
   if (t < 0 || t >= P) t = 0;
   const double inv = pow(theta, -2.0 * (double)j / (double)hd);
   double s, cth;
@@ -297,26 +301,50 @@ __global__ void rope_table_kernel(const int32_t* idx, int n_filled, int64_t P, i
   rsin[i] = (float)s;
 }
 
-// Flags filled-row indices that are out of the prefix, not strictly increasing, or whose
-// page is missing from the block table.
-__global__ void validate_rows_kernel(const int32_t* idx, int n_filled, int64_t P,
-                                     const int32_t* bt, int64_t n_logical, int ps,
-                                     int num_pages, unsigned* status) {
+// Over the padded filled list: flags indices that are out of the prefix, not strictly
+// increasing, or whose page is missing from the block table, and stores each row's
+// element offset in the page pools (-1 for flagged and padding rows, which the kv
+// epilogue skips).
+__global__ void row_slot_kernel(const int32_t* idx, int n_filled, int mpad, int64_t P,
+                                const int32_t* bt, int64_t n_logical, int ps, int num_pages,
+                                int kv, int64_t* slot, unsigned* status) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_filled) return;
-  const int t = idx[i];
-  bool bad = t < 0 || t >= P;
-  if (!bad && i > 0 && idx[i - 1] >= t) bad = true;
-  if (!bad) {
-    const int64_t lp = t / ps;
-    if (lp >= n_logical) {
-      bad = true;
-    } else {
-      const int pg = bt[lp];
-      bad = pg < 0 || pg >= num_pages;
+  if (i >= mpad) return;
+  int64_t off = -1;
+  if (i < n_filled) {
+    const int t = idx[i];
+    bool bad = t < 0 || t >= P;
+    if (!bad && i > 0 && idx[i - 1] >= t) bad = true;
+    if (!bad) {
+      const int64_t lp = t / ps;
+      if (lp >= n_logical) {
+        bad = true;
+      } else {
+        const int pg = bt[lp];
+        bad = pg < 0 || pg >= num_pages;
+        if (!bad) off = ((int64_t)pg * ps + (t - lp * ps)) * kv;
+      }
     }
+    if (bad) atomicOr(status, kStatusRowsBit);
   }
-  if (bad) atomicOr(status, kStatusRowsBit);
+  slot[i] = off;
+}
+
+// 1/sqrt(mean(x_hat^2) + eps) per padded row and layer of a launch group, from the map
+// kernel's per-128-feature partial sums (added in a fixed order).
+__global__ void rstd_kernel(unsigned char* layer_ws, size_t per_layer, size_t per_layer_h,
+                            size_t per_layer_ssq, int mpad, int nchunk, int d, float eps) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= mpad) return;
+  unsigned char* lw = layer_ws + (size_t)blockIdx.y * per_layer;
+  const float* p = reinterpret_cast<const float*>(lw + per_layer_h) + (size_t)row * nchunk;
+  float s = 0.f;
+  for (int c = 0; c < nchunk; c += 2) {      // nchunk = d / 128 is even (d % 256 == 0)
+    const float2 v = *reinterpret_cast<const float2*>(p + c);
+    s += v.x;
+    s += v.y;
+  }
+  reinterpret_cast<float*>(lw + per_layer_h + per_layer_ssq)[row] = 1.0f / sqrtf(s / (float)d + eps);
 }
 
 }  // namespace
@@ -333,15 +361,16 @@ hipError_t launch_clear_status(unsigned* status, hipStream_t stream) {
 FillWsLayout fill_ws_layout(int d, int hd, int64_t n_filled) {
   FillWsLayout L;
   const int64_t mpad = (n_filled + kTile - 1) / kTile * kTile;
-  const size_t table = align256((size_t)n_filled * (hd / 2) * sizeof(float));
+  const size_t table = align256((size_t)mpad * (hd / 2) * sizeof(float));
   L.rope_cos = kStatusBytes;
   L.rope_sin = L.rope_cos + table;
-  L.fixed = L.rope_sin + table;
+  L.row_slot = L.rope_sin + table;
+  L.fixed = L.row_slot + align256((size_t)mpad * sizeof(int64_t));
   L.per_layer_h = align256((size_t)mpad * d * 2);
   L.per_layer_ssq = align256((size_t)mpad * (d / 128) * sizeof(float));
-  L.per_layer = L.per_layer_h + L.per_layer_ssq;
+  L.per_layer_rstd = align256((size_t)mpad * sizeof(float));
+  L.per_layer = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
   L.hbuf = L.fixed;
-  L.ssq_off = L.fixed + L.per_layer_h;
   return L;
 }
 
@@ -349,13 +378,13 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
                        hipStream_t stream) {
   hipError_t e = launch_clear_status(p.status, stream);
   if (e != hipSuccess) return e;
-  const int nb = (p.n_filled + 255) / 256;
-  hipLaunchKernelGGL(validate_rows_kernel, dim3(nb), dim3(256), 0, stream, p.idx, p.n_filled,
-                     (int64_t)p.P, p.block_table, p.n_logical, p.page_size, p.num_pages,
-                     p.status);
-  const int64_t nt = (int64_t)p.n_filled * (p.hd / 2);
+  hipLaunchKernelGGL(row_slot_kernel, dim3(p.mpad / 256), dim3(256), 0, stream, p.idx, p.n_filled,
+                     p.mpad, (int64_t)p.P, p.block_table, p.n_logical, p.page_size, p.num_pages,
+                     p.kv, p.row_slot, p.status);
+  const int64_t nt = (int64_t)p.mpad * (p.hd / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream,
-                     p.idx, p.n_filled, (int64_t)p.P, p.hd, p.theta, p.rope_cos, p.rope_sin);
+                     p.idx, p.n_filled, p.mpad, (int64_t)p.P, p.hd, p.theta, p.rope_cos,
+                     p.rope_sin);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   FillKArgs a = {};
@@ -374,12 +403,10 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
   const FillWsLayout L = fill_ws_layout(p.d, p.hd, p.n_filled);
   a.per_layer = L.per_layer;
   a.per_layer_h = L.per_layer_h;
+  a.per_layer_ssq = L.per_layer_ssq;
   a.rcos = p.rope_cos;
   a.rsin = p.rope_sin;
-  a.bt = p.block_table;
-  a.n_logical = p.n_logical;
-  a.ps = p.page_size;
-  a.num_pages = p.num_pages;
+  a.row_slot = p.row_slot;
   a.ntt = p.mpad / kTile;
 
   // Balanced groups of at most p.group layers, so one call makes as few, equal
@@ -394,6 +421,8 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
       ProfileScope ps(RF_KERNEL_FILL_MAP, stream);
       hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
     }
+    hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
+                       a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
     a.nft = 2 * p.kv / kTile;
     {
       ProfileScope ps(RF_KERNEL_FILL_KV, stream);

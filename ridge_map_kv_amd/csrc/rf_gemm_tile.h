@@ -107,14 +107,27 @@ __device__ __forceinline__ void mfma_i(f32x16 (&acc)[4][4], const bf16x8 (&a)[4]
   acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i >> 2], b[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
 }
 
+// Load issue j (0..15) of a slice: even j -> F block j / 2, odd j -> T block j / 2.
+__device__ __forceinline__ void dma_issue(const DmaOperand& F, const DmaOperand& T, int j, int kb,
+                                          uint32_t dst, int wave) {
+  if (j & 1)
+    dma_block(T, j >> 1, kb, dst + kPipeOp, wave);
+  else
+    dma_block(F, j >> 1, kb, dst, wave);
+}
+
 // 16 MFMAs on (a, b); after each of the first 8, one fragment of step s of stage st is
-// read into (na, nb).
+// read into (na, nb).  With `dma`, load issues j0 .. j0 + 7 of the slice at byte offset kb
+// go out after the even-numbered MFMAs, into the stage at LDS address dst.
 __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
                                             const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
-                                            const unsigned char* st, int s, int wf, int wt, int lane) {
+                                            const unsigned char* st, int s, int wf, int wt, int lane,
+                                            bool dma, const DmaOperand& F, const DmaOperand& T,
+                                            int kb, uint32_t dst, int j0, int wave) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     mfma_i(acc, a, b, i);
+    if (dma && !(i & 1)) dma_issue(F, T, j0 + (i >> 1), kb, dst, wave);
     if (i < 8) read_frag(na, nb, st, i, s, wf, wt, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -122,6 +135,11 @@ __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&
 
 // acc = F[256 x K] * T[256 x K]^T, K a multiple of 64.  Ends with a barrier, leaving the
 // 128 KB of LDS to the epilogue.
+//
+// Two 64 KB stages.  The 16 load issues per wave that refill a stage are split: the first 8
+// follow the barrier that frees the stage (one after every other MFMA of the last 16-wide
+// step), the other 8 go out during the first step of the next slice, so the CU's address
+// unit never has all 64 of a slice queued inside one 16-MFMA window.
 __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOperand& F,
                                               const DmaOperand& T, int K, unsigned char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -154,9 +172,13 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
   for (int i = 0; i < 8; ++i) read_frag(a0, b0, smem, i, 0, wf, wt, lane);
   for (int kt = 0; kt < nk - 1; ++kt) {
     const unsigned char* cur = smem + (kt & 1) * kPipeStage;
-    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
-    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
-    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+    // second half of slice kt + 1 (slices 0 and 1 came whole with the prologue)
+    const bool pend = kt >= 1;
+    const int kbp = (kt + 1) * kPipeBK * 2;
+    const uint32_t dstp = base + ((kt + 1) & 1) * kPipeStage;
+    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, pend, F, T, kbp, dstp, 8, wave);
+    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slice kt + 1, the only one in flight
     __syncthreads();                                       // ... landed for every wave; slice kt read
     const bool more = kt + 2 < nk;
@@ -166,21 +188,16 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mfma_i(acc, a1, b1, i);
-      if (more) {
-        if (i & 1)
-          dma_block(T, i >> 1, kb, dst + kPipeOp, wave);
-        else
-          dma_block(F, i >> 1, kb, dst, wave);
-      }
+      if (more && !(i & 1)) dma_issue(F, T, i >> 1, kb, dst, wave);
       if (i >= 8) read_frag(a0, b0, nxt, i - 8, 0, wf, wt, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
-    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane);
-    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane);
-    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane);
+    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }

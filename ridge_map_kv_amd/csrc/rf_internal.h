@@ -41,16 +41,17 @@ struct FillPlan {
   int page_size, num_pages;
   // workspace carve-up
   unsigned* status;
-  float* rope_cos;              // [n_filled][hd/2]
-  float* rope_sin;
-  uint16_t* hbuf;               // [group][mpad][d]
-  float* ssq;                   // [group][mpad][d/128]
+  float* rope_cos;              // [mpad / 32][hd / 8][32][4]: (row, j) at
+  float* rope_sin;              //   ((row / 32) * hd / 8 + j / 4) * 128 + (row % 32) * 4 + j % 4
+  int64_t* row_slot;            // [mpad] element offset of the row in a page pool, or -1
+  uint16_t* hbuf;               // per layer: [mpad][d] bf16, [mpad][d/128] fp32, [mpad] fp32
   int group;                    // layers per launch
 };
 
 // Workspace layout of a fill call (bytes from the start of ws).
 struct FillWsLayout {
-  size_t rope_cos, rope_sin, hbuf, ssq_off, per_layer_h, per_layer_ssq, fixed, per_layer;
+  size_t rope_cos, rope_sin, row_slot, hbuf, per_layer_h, per_layer_ssq, per_layer_rstd, fixed,
+      per_layer;
 };
 FillWsLayout fill_ws_layout(int d, int hd, int64_t n_filled);
 

@@ -174,8 +174,8 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
   p.status = reinterpret_cast<unsigned*>(w);
   p.rope_cos = reinterpret_cast<float*>(w + L.rope_cos);
   p.rope_sin = reinterpret_cast<float*>(w + L.rope_sin);
+  p.row_slot = reinterpret_cast<int64_t*>(w + L.row_slot);
   p.hbuf = reinterpret_cast<uint16_t*>(w + L.hbuf);
-  p.ssq = reinterpret_cast<float*>(w + L.ssq_off);
   p.group = (int)group;
 
   std::vector<rf::FillLayerPtrs> lp((size_t)n_layers);
