@@ -39,7 +39,7 @@ struct FillKArgs {
   int d, kv, hd;
   float eps;
   int mpad, nchunk;             // nchunk = d / 128 sum-of-squares partials per row
-  unsigned char* layer_ws;      // per layer: hbuf [mpad][d] bf16, ssq [mpad][nchunk], rstd [mpad]
+  unsigned char* layer_ws;      // per layer: hbuf [mpad][d] bf16, ssq [nchunk][mpad], rstd [mpad]
   size_t per_layer, per_layer_h, per_layer_ssq;
   const float* rcos;
   const float* rsin;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
-      ssq[(size_t)tok * a.nchunk + chunk] = ss[n];
+      ssq[(size_t)chunk * a.mpad + tok] = ss[n];        // chunk-major: coalesced
     }
   }
   __syncthreads();
@@ -337,13 +337,9 @@ __global__ void rstd_kernel(unsigned char* layer_ws, size_t per_layer, size_t pe
   const int row = blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= mpad) return;
   unsigned char* lw = layer_ws + (size_t)blockIdx.y * per_layer;
-  const float* p = reinterpret_cast<const float*>(lw + per_layer_h) + (size_t)row * nchunk;
+  const float* p = reinterpret_cast<const float*>(lw + per_layer_h) + row;
   float s = 0.f;
-  for (int c = 0; c < nchunk; c += 2) {      // nchunk = d / 128 is even (d % 256 == 0)
-    const float2 v = *reinterpret_cast<const float2*>(p + c);
-    s += v.x;
-    s += v.y;
-  }
+  for (int c = 0; c < nchunk; ++c) s += p[(size_t)c * mpad];
   reinterpret_cast<float*>(lw + per_layer_h + per_layer_ssq)[row] = 1.0f / sqrtf(s / (float)d + eps);
 }
 

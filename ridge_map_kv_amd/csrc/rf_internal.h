@@ -44,7 +44,7 @@ struct FillPlan {
   float* rope_cos;              // [mpad / 32][hd / 8][32][4]: (row, j) at
   float* rope_sin;              //   ((row / 32) * hd / 8 + j / 4) * 128 + (row % 32) * 4 + j % 4
   int64_t* row_slot;            // [mpad] element offset of the row in a page pool, or -1
-  uint16_t* hbuf;               // per layer: [mpad][d] bf16, [mpad][d/128] fp32, [mpad] fp32
+  uint16_t* hbuf;               // per layer: [mpad][d] bf16, [d/128][mpad] fp32, [mpad] fp32
   int group;                    // layers per launch
 };
 
