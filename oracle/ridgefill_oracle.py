@@ -19,6 +19,12 @@ by its section:
   [own]    same section, "own normalization and projections" and Fig. 2
   [arms]   "Tables from the paper", Table 3 (exact / no fill / identity / RidgeFill)
   [notation] "Tables from the paper", Table 2
+  [size]   same section as [map], the paragraph on map size (int8 maps, rectangular maps
+           of input width 10,240 and output width 2,560, resident or streamed maps)
+  [rescale] "Hybrid layers and two corrections", the value-rescale paragraph
+  [qknorm] same paragraph (Qwen models normalise keys) and "Experiments", the error
+           attribution paragraph on key normalization
+  [select] "Which rows to compute exactly", attention selection
 
 Readings of points the page leaves open (each is listed with its reason in the design
 notes of the repository):
@@ -34,6 +40,17 @@ notes of the repository):
     them at solve time; the trace in alpha is that of the centred X^T X; d_in = d.
   * The statistic kept per layer is Y_l^T X (d_out x d_in), the factor that appears in
     the closed form.
+  * Key normalization (Qwen-style layers) is an RMSNorm over each key head's hd entries
+    with its own weight [hd], after the key projection and before RoPE; it uses the
+    same eps as the layer norm.
+  * Value rescale: "magnitude" is the Euclidean norm of one KV head's value vector; the
+    exact and predicted values both go through the layer's RMSNorm and W_V; the scale
+    of head h is the plain mean over the c rows of |v_exact| / |v_pred|, and it
+    multiplies head h of every filled row's value.
+  * int8 maps: symmetric, one scale per output row (max |A| / 127, round half to
+    even, clip to [-127, 127]); the map used is q * scale.
+  * Selection from scores: the k prefix rows with the largest score, ties to the lower
+    index; the attention-selected arm uses k = round(0.1 * P).
 
 Parity status: every function below is pinned by the CPU tests in tests/test_oracle_*.py
 (closed forms, library routines that solve the same problem another way, invariants,
@@ -53,6 +70,11 @@ __all__ = [
     "rope_keys",
     "project_kv",
     "fill_rows",
+    "key_norm",
+    "value_scale",
+    "quantize_map_int8",
+    "dequantize_map_int8",
+    "select_exact",
     "paged_location",
     "fill_paged_cache",
     "CalibStats",
@@ -178,18 +200,83 @@ def project_kv(h: np.ndarray, W_K: np.ndarray, W_V: np.ndarray, n_kv: int, hd: i
     return K.reshape(rows, n_kv, hd), V.reshape(rows, n_kv, hd)
 
 
-def fill_rows(x_S_rows, positions, A, b, norm_w, W_K, W_V, *, eps, theta, n_kv, hd):
-    """Cache entries of one upper layer for the given filled rows (Fig. 2 flow):
-    predicted input -> the layer's RMSNorm -> K and V projections -> RoPE on K.
+def key_norm(K: np.ndarray, k_norm_w: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head key normalization ([qknorm]): each key head's hd entries divided by their
+    root mean square (eps inside the root), then scaled by the head weight k_norm_w [hd].
+    K has shape [rows, heads, hd]."""
+    return rms_norm(K, k_norm_w, eps)
 
-    x_S_rows: [rows, d] split-layer states of the filled rows; positions: their prompt
-    indices.  Returns (K, V), each [rows, n_kv, hd] in float64.
+
+def fill_rows(x_S_rows, positions, A, b, norm_w, W_K, W_V, *, eps, theta, n_kv, hd,
+              k_norm_w=None, v_scale=None):
+    """Cache entries of one upper layer for the given filled rows (Fig. 2 flow):
+    predicted input -> the layer's RMSNorm -> K and V projections -> (key norm) -> RoPE
+    on K; V times the per-head value-rescale factors when given ([rescale]).
+
+    x_S_rows: [rows, d_in] split-layer states of the filled rows; positions: their prompt
+    indices; A is d_out x d_in.  Returns (K, V), each [rows, n_kv, hd] in float64.
     """
     x_hat = predict_input(x_S_rows, A, b)
     h = rms_norm(x_hat, norm_w, eps)
     K, V = project_kv(h, W_K, W_V, n_kv, hd)
+    if k_norm_w is not None:
+        K = key_norm(K, k_norm_w, eps)
     K = rope_keys(K, positions, theta)
+    if v_scale is not None:
+        V = V * np.asarray(v_scale, dtype=np.float64)[None, :, None]
     return K, V
+
+
+# --------------------------------------------------------------------------- [rescale]
+
+def value_scale(x_S_tail, x_l_exact_tail, A, b, norm_w, W_V, *, eps, n_kv, hd):
+    """Per-KV-head value-rescale factors of one upper layer ([rescale]).
+
+    The first c tail rows go through the layer's value projection twice: with their
+    exact layer input x_l (x_l_exact_tail, [c, d_out]) and with the map's prediction
+    from their split-layer state (x_S_tail, [c, d_in]).  For head h the factor is the
+    mean over the c rows of |v_exact[h]| / |v_pred[h]|.  Returns [n_kv] float64.
+    """
+    W_V = np.asarray(W_V, dtype=np.float64)
+    v_ex = (rms_norm(x_l_exact_tail, norm_w, eps) @ W_V.T).reshape(-1, n_kv, hd)
+    x_hat = predict_input(x_S_tail, A, b)
+    v_pr = (rms_norm(x_hat, norm_w, eps) @ W_V.T).reshape(-1, n_kv, hd)
+    ratio = np.linalg.norm(v_ex, axis=-1) / np.linalg.norm(v_pr, axis=-1)
+    return ratio.mean(axis=0)
+
+
+# --------------------------------------------------------------------------- [size]
+
+def quantize_map_int8(A: np.ndarray, dtype=np.float64):
+    """Symmetric int8 map with one scale per output row: scale = max_k |A[o, k]| / 127,
+    q = round-half-even(A / scale) clipped to [-127, 127] (an all-zero row gets scale 0
+    and q = 0).  The arithmetic runs in `dtype` (float32 to take the same rounding
+    decisions as a float32 quantizer).  Returns (q int8 [d_out, d_in], scale [d_out])."""
+    A = np.asarray(A).astype(dtype)
+    amax = np.max(np.abs(A), axis=1)
+    scale = (amax / dtype(127.0)).astype(dtype)
+    safe = np.where(scale > 0, scale, dtype(1.0)).astype(dtype)
+    q = np.clip(np.rint((A / safe[:, None]).astype(dtype)), -127, 127)
+    q[scale == 0] = 0
+    return q.astype(np.int8), scale
+
+
+def dequantize_map_int8(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """The map an int8 map stands for: q[o, k] * scale[o], in float64."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+# --------------------------------------------------------------------------- [select]
+
+def select_exact(scores, k: int) -> np.ndarray:
+    """The k prefix rows with the largest score, ties broken toward the lower row index
+    ([select]); returned in ascending row order.  scores: one value per prefix row."""
+    sc = np.asarray(scores, dtype=np.float64)
+    P = sc.shape[0]
+    if not 0 <= k <= P:
+        raise ValueError("need 0 <= k <= P")
+    order = sorted(range(P), key=lambda i: (-sc[i], i))
+    return np.sort(np.asarray(order[:k], dtype=np.int64))
 
 
 def paged_location(t, block_table, page_size: int):
