@@ -49,22 +49,42 @@ typedef enum rf_status {
 
 /* Model shape shared by all layers of one fill call. */
 typedef struct rf_shape {
-  int32_t d;            /* hidden size; the map is d x d. Multiple of 256.          */
+  int32_t d;            /* hidden size of the upper layers (the map's output width);
+                           multiple of 256                                             */
   int32_t n_kv_heads;   /* KV heads; n_kv_heads * head_dim must be a multiple of 128 */
   int32_t head_dim;     /* 64 or 128                                                 */
-  float rms_eps;        /* RMSNorm epsilon (inside the square root), >= 0            */
+  float rms_eps;        /* RMSNorm epsilon (inside the square root), >= 0; also the
+                           epsilon of the per-head key norm when one is given        */
   double rope_theta;    /* RoPE base, > 1                                            */
+  int32_t d_in;         /* width of x_S, the map's input (section "Ridge map ...", map
+                           size paragraph: a gated-residual model reads a 10,240-wide
+                           state into 2,560-wide layers).  0 means d.  Multiple of 64. */
+  int32_t reserved;     /* must be 0                                                  */
 } rf_shape;
 
 /* One upper layer l >= S.  Every pointer is a device pointer owned by the caller.   */
 typedef struct rf_layer {
-  const uint16_t* A;       /* bf16 [d][d]: x_hat = A x_S + b (A[out][in])             */
+  const uint16_t* A;       /* bf16 [d][d_in]: x_hat = A x_S + b (A[out][in]); NULL when
+                              the map is given in int8 (A_q)                            */
   const float* b;          /* fp32 [d]                                                 */
   const uint16_t* norm_w;  /* bf16 [d]: the layer's RMSNorm weight                     */
   const uint16_t* W_K;     /* bf16 [n_kv_heads*head_dim][d]: key projection, no bias   */
   const uint16_t* W_V;     /* bf16 [n_kv_heads*head_dim][d]: value projection, no bias */
   uint16_t* k_pages;       /* bf16 [num_pages][page_size][n_kv_heads][head_dim]        */
   uint16_t* v_pages;       /* bf16 [num_pages][page_size][n_kv_heads][head_dim]        */
+  /* Optional parts (NULL = absent). */
+  const uint16_t* k_norm_w; /* bf16 [head_dim]: per-head key RMSNorm (Qwen-style layers;
+                               section "Hybrid layers and two corrections": Qwen models
+                               normalise keys), applied to each key head after W_K and
+                               before RoPE                                               */
+  const float* v_scale;     /* fp32 [n_kv_heads]: value-rescale factors (same section,
+                               value rescale); head h of every filled value is
+                               multiplied by v_scale[h].  ridgefill_value_scale computes
+                               them.                                                    */
+  const int8_t* A_q;        /* int8 [d][d_in] with A_scale: the map is A_q[o][i] *
+                               A_scale[o] (section "Ridge map ...", map size paragraph:
+                               int8 maps).  Exactly one of A and A_q is set.             */
+  const float* A_scale;     /* fp32 [d]: per-output-row scale of A_q                    */
 } rf_layer;
 
 /* Paged KV layout of one prompt, shared by every layer's k_pages / v_pages. */
@@ -92,18 +112,19 @@ rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
  * Fill.  Section "Ridge map: predict the input, and the original projection runs
  * unchanged" (prediction equation, "own normalization and projections", Fig. 2):
  * for every filled row t and every given upper layer l,
- *     x_hat = A_l x_S[t] + b_l
+ *     x_hat = A_l x_S[t] + b_l          (A_l = A_q,l * A_scale,l for an int8 map)
  *     h     = x_hat / sqrt(mean(x_hat^2) + eps) * norm_w_l
- *     k     = RoPE_t(W_K,l h)   (pairs (j, j + head_dim/2), angle t * theta^(-2j/head_dim))
- *     v     = W_V,l h
+ *     k     = W_K,l h,  then per head k / sqrt(mean(k^2) + eps) * k_norm_w_l if given
+ *     k     = RoPE_t(k)   (pairs (j, j + head_dim/2), angle t * theta^(-2j/head_dim))
+ *     v     = W_V,l h,  times v_scale_l[head] if given
  * and k, v are written to row t of layer l's paged cache (page block_table[t /
  * page_size], slot t % page_size).  Nothing else in the caches is touched; with
  * n_filled = 0 or n_layers = 0 only the status word is cleared (if ws is given).  Layers are independent; a caller that streams
  * maps may call once per layer.
  *
- *   x_S         device bf16 [N][x_stride]: split-layer states of all prompt rows; the
- *               prefix rows must span at most 4 GiB ((N - T) x x_stride x 2 bytes), and
- *               x_stride is a multiple of 8
+ *   x_S         device bf16 [N][x_stride]: split-layer states of all prompt rows
+ *               (x_stride >= d_in); the prefix rows must span at most 4 GiB
+ *               ((N - T) x x_stride x 2 bytes), and x_stride is a multiple of 8
  *   filled_idx  device int32 [n_filled]: filled rows, strictly increasing, each
  *               < N - T (the tail never receives a filled entry).  Violations set
  *               RF_E_ROWS in the device status; out-of-range rows are skipped.
@@ -112,7 +133,11 @@ rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
  *               n_filled, 1); a larger workspace (up to the value for n_layers) lets
  *               more layers share one launch.  Its first 256 bytes hold the status.
  * Computation: bf16 inputs, fp32 accumulation, x_hat and the RMS in fp32, one bf16
- * rounding of x_hat * norm_w, one bf16 rounding of the stored k and v.
+ * rounding of x_hat * norm_w, one bf16 rounding of the stored k and v.  An int8 map is
+ * expanded exactly (integer codes as bf16) into a staging area of the workspace and its
+ * row scale is applied to the fp32 product, so it adds no rounding of its own.  All
+ * layers of one call must agree on which optional parts they use (int8 or bf16 map,
+ * key norm); v_scale may be set per layer.
  * ------------------------------------------------------------------------------ */
 size_t ridgefill_fill_workspace_bytes(const rf_shape* shape, int64_t n_filled,
                                       int32_t n_layers);
@@ -120,6 +145,60 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
                          int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
                          const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Map variants for the workspace query: RF_MAPS_INT8 when the layers carry A_q/A_scale
+ * (the workspace then holds a bf16 expansion of each layer's codes), RF_MAPS_STREAMED for
+ * ridgefill_fill_streamed (two landing slots per layer).  Returns 0 on invalid input.
+ * ridgefill_fill_workspace_bytes(...) is ridgefill_fill_workspace_bytes_ex(..., 0). */
+#define RF_MAPS_INT8 1
+#define RF_MAPS_STREAMED 2
+size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled,
+                                         int32_t n_layers, int32_t map_flags);
+
+/* ------------------------------------------------------------------------------
+ * Fill with host-resident maps.  Section "Ridge map ...", map size paragraph: maps can
+ * stay in GPU memory or be streamed from host memory one layer at a time.  Same
+ * computation and arguments as ridgefill_fill, except that every layer's A (or A_q) is
+ * a HOST pointer, ideally page-locked (hipHostMalloc) so that the copies run
+ * asynchronously.  Layers are processed in groups sized by the workspace
+ * (ridgefill_fill_workspace_bytes_ex with RF_MAPS_STREAMED, plus RF_MAPS_INT8 for int8
+ * maps); group g's maps are copied on `copy_stream` into landing slot g % 2 while group
+ * g - 1 computes on `stream`.  copy_stream must be a different stream; both must stay
+ * valid until the work completes.  The results are bit-identical to ridgefill_fill's.
+ * ------------------------------------------------------------------------------ */
+rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                                  int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                                  const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
+                                  void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/* ------------------------------------------------------------------------------
+ * Value-rescale factors.  Section "Hybrid layers and two corrections", value rescale:
+ * the first c tail rows pass through each upper layer's value projection twice, once
+ * with their exact layer input and once with the map's prediction; per KV head the
+ * ratio of the exact value's norm to the predicted value's norm, averaged over the c
+ * rows, is the factor that multiplies the filled values.  For layer l and head h:
+ *     v_e(t) = W_V,l RMSNorm_l(x_l,exact[t]),  v_p(t) = W_V,l RMSNorm_l(A_l x_S[t] + b_l)
+ *     v_scale_out[l][h] = (1/c) sum_t |v_e(t)_h| / |v_p(t)_h|
+ * Pass v_scale_out + l * n_kv_heads as layer l's v_scale to ridgefill_fill.
+ *
+ *   x_S_tail     device bf16 [c][x_stride]: split-layer states of the first c tail rows
+ *   x_l_tail     host array [n_layers] of device bf16 [c][d] (contiguous): each layer's
+ *                exact input for the same rows
+ *   layers       A or A_q/A_scale, b, norm_w, W_K, W_V of each layer (W_K is read only
+ *                to share the fill's tiling; K and the pages are not written)
+ *   v_scale_out  device fp32 [n_layers][n_kv_heads]
+ *   ws           >= ridgefill_value_scale_workspace_bytes(shape, c, 1, map_flags); a
+ *                larger one lets more layers share a launch
+ * Norms are taken in fp32 on the fp32 projections (before any bf16 rounding of v); the
+ * inputs to W_V are rounded to bf16 once, as in the fill.  The mean is added in row order
+ * in fp64.  A predicted norm of 0 gives an infinite factor.
+ * ------------------------------------------------------------------------------ */
+size_t ridgefill_value_scale_workspace_bytes(const rf_shape* shape, int64_t c, int32_t n_layers,
+                                             int32_t map_flags);
+rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail, int64_t x_stride,
+                                const uint16_t* const* x_l_tail, int64_t c, const rf_layer* layers,
+                                int32_t n_layers, float* v_scale_out, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* ------------------------------------------------------------------------------
  * Calibration.  Same section, paragraph on alpha and the one-pass statistics: one pass

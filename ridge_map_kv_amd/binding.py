@@ -21,7 +21,11 @@ RF_OK, RF_E_INVALID, RF_E_SHAPE, RF_E_WORKSPACE, RF_E_HIP, RF_E_NOT_SPD, RF_E_RO
 EXPORTED = [
     "ridgefill_partition",
     "ridgefill_fill_workspace_bytes",
+    "ridgefill_fill_workspace_bytes_ex",
     "ridgefill_fill",
+    "ridgefill_fill_streamed",
+    "ridgefill_value_scale_workspace_bytes",
+    "ridgefill_value_scale",
     "ridgefill_calib_state_bytes",
     "ridgefill_calib_reset",
     "ridgefill_calibrate",
@@ -42,15 +46,21 @@ class RidgeFillError(RuntimeError):
         self.status = status
 
 
+RF_MAPS_INT8 = 1
+RF_MAPS_STREAMED = 2
+
+
 class rf_shape(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("rms_eps", C.c_float), ("rope_theta", C.c_double)]
+                ("rms_eps", C.c_float), ("rope_theta", C.c_double), ("d_in", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class rf_layer(C.Structure):
     _fields_ = [("A", C.c_void_p), ("b", C.c_void_p), ("norm_w", C.c_void_p),
                 ("W_K", C.c_void_p), ("W_V", C.c_void_p), ("k_pages", C.c_void_p),
-                ("v_pages", C.c_void_p)]
+                ("v_pages", C.c_void_p), ("k_norm_w", C.c_void_p), ("v_scale", C.c_void_p),
+                ("A_q", C.c_void_p), ("A_scale", C.c_void_p)]
 
 
 class rf_paged_kv(C.Structure):
@@ -75,8 +85,15 @@ def lib() -> C.CDLL:
     sig = {
         "ridgefill_partition": (st, [i64, i64, vp, vp, C.POINTER(i64)]),
         "ridgefill_fill_workspace_bytes": (sz, [C.POINTER(rf_shape), i64, i32]),
+        "ridgefill_fill_workspace_bytes_ex": (sz, [C.POINTER(rf_shape), i64, i32, i32]),
         "ridgefill_fill": (st, [C.POINTER(rf_shape), vp, i64, i64, i64, vp, i64,
                                 C.POINTER(rf_layer), i32, C.POINTER(rf_paged_kv), vp, sz, vp]),
+        "ridgefill_fill_streamed": (st, [C.POINTER(rf_shape), vp, i64, i64, i64, vp, i64,
+                                         C.POINTER(rf_layer), i32, C.POINTER(rf_paged_kv), vp,
+                                         sz, vp, vp]),
+        "ridgefill_value_scale_workspace_bytes": (sz, [C.POINTER(rf_shape), i64, i32, i32]),
+        "ridgefill_value_scale": (st, [C.POINTER(rf_shape), vp, i64, C.POINTER(vp), i64,
+                                       C.POINTER(rf_layer), i32, vp, vp, sz, vp]),
         "ridgefill_calib_state_bytes": (sz, [i32, i32]),
         "ridgefill_calib_reset": (st, [vp, sz, i32, i32, vp]),
         "ridgefill_calibrate": (st, [vp, sz, i32, i32, vp, C.POINTER(vp), i64, vp]),
@@ -117,8 +134,8 @@ def _stream(stream) -> int | None:
 
 
 def make_shape(d: int, n_kv_heads: int, head_dim: int, rms_eps: float = 1e-5,
-               rope_theta: float = 500000.0) -> rf_shape:
-    return rf_shape(d, n_kv_heads, head_dim, rms_eps, rope_theta)
+               rope_theta: float = 500000.0, d_in: int = 0) -> rf_shape:
+    return rf_shape(d, n_kv_heads, head_dim, rms_eps, rope_theta, d_in, 0)
 
 
 # ------------------------------------------------------------------------------ partition
@@ -140,24 +157,59 @@ def ridgefill_partition(N: int, T: int, exact_mask: np.ndarray | None) -> np.nda
 
 # ------------------------------------------------------------------------------ fill
 
-def ridgefill_fill_workspace_bytes(shape: rf_shape, n_filled: int, n_layers: int) -> int:
-    return int(lib().ridgefill_fill_workspace_bytes(C.byref(shape), int(n_filled), int(n_layers)))
+def ridgefill_fill_workspace_bytes(shape: rf_shape, n_filled: int, n_layers: int,
+                                   map_flags: int = 0) -> int:
+    return int(lib().ridgefill_fill_workspace_bytes_ex(C.byref(shape), int(n_filled),
+                                                       int(n_layers), int(map_flags)))
+
+
+def _layers(layers: list[dict]):
+    """rf_layer array from dicts of torch tensors: A (bf16 [d][d_in]) or A_q (int8) with
+    A_scale (fp32 [d]); b (fp32 [d]); norm_w (bf16 [d]); W_K, W_V (bf16 [kv][d]); k_pages,
+    v_pages (bf16 [num_pages][page_size][n_kv][hd]); optional k_norm_w (bf16 [hd]) and
+    v_scale (fp32 [n_kv])."""
+    arr = (rf_layer * max(len(layers), 1))()
+    for i, l in enumerate(layers):
+        g = l.get
+        arr[i] = rf_layer(_ptr(g("A")), _ptr(g("b")), _ptr(g("norm_w")), _ptr(g("W_K")),
+                          _ptr(g("W_V")), _ptr(g("k_pages")), _ptr(g("v_pages")),
+                          _ptr(g("k_norm_w")), _ptr(g("v_scale")), _ptr(g("A_q")),
+                          _ptr(g("A_scale")))
+    return arr
 
 
 def ridgefill_fill(shape: rf_shape, x_S, N: int, T: int, filled_idx, n_filled: int,
                    layers: list[dict], block_table, page_size: int, num_pages: int,
-                   ws, x_stride: int | None = None, stream=None) -> None:
-    """layers: dicts with torch tensors A (bf16 [d][d]), b (fp32 [d]), norm_w (bf16 [d]),
-    W_K, W_V (bf16 [kv][d]), k_pages, v_pages (bf16 [num_pages][page_size][n_kv][hd])."""
-    arr = (rf_layer * max(len(layers), 1))()
-    for i, l in enumerate(layers):
-        arr[i] = rf_layer(_ptr(l["A"]), _ptr(l["b"]), _ptr(l["norm_w"]), _ptr(l["W_K"]),
-                          _ptr(l["W_V"]), _ptr(l["k_pages"]), _ptr(l["v_pages"]))
+                   ws, x_stride: int | None = None, stream=None, copy_stream=None) -> None:
+    """The fill; with copy_stream given, the streamed variant (maps in host tensors)."""
+    arr = _layers(layers)
     kv = rf_paged_kv(_ptr(block_table), int(block_table.numel()), int(page_size), int(num_pages))
     stride = int(x_stride if x_stride is not None else x_S.stride(0))
-    _check(lib().ridgefill_fill(C.byref(shape), _ptr(x_S), int(N), int(T), stride,
-                                _ptr(filled_idx), int(n_filled), arr, len(layers), C.byref(kv),
-                                _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
+    args = (C.byref(shape), _ptr(x_S), int(N), int(T), stride, _ptr(filled_idx), int(n_filled),
+            arr, len(layers), C.byref(kv), _ptr(ws), int(ws.numel() * ws.element_size()),
+            _stream(stream))
+    if copy_stream is None:
+        _check(lib().ridgefill_fill(*args))
+    else:
+        _check(lib().ridgefill_fill_streamed(*args, _stream(copy_stream)))
+
+
+def ridgefill_value_scale_workspace_bytes(shape: rf_shape, c: int, n_layers: int,
+                                          map_flags: int = 0) -> int:
+    return int(lib().ridgefill_value_scale_workspace_bytes(C.byref(shape), int(c), int(n_layers),
+                                                           int(map_flags)))
+
+
+def ridgefill_value_scale(shape: rf_shape, x_S_tail, x_l_tail: list, layers: list[dict], out,
+                          ws, x_stride: int | None = None, stream=None) -> None:
+    """Value-rescale factors of every layer into out (fp32 [n_layers][n_kv])."""
+    arr = _layers(layers)
+    ptrs = (C.c_void_p * max(len(x_l_tail), 1))(*[_ptr(t) for t in x_l_tail])
+    stride = int(x_stride if x_stride is not None else x_S_tail.stride(0))
+    _check(lib().ridgefill_value_scale(C.byref(shape), _ptr(x_S_tail), stride, ptrs,
+                                       int(x_S_tail.shape[0]), arr, len(layers), _ptr(out),
+                                       _ptr(ws), int(ws.numel() * ws.element_size()),
+                                       _stream(stream)))
 
 
 # ------------------------------------------------------------------------------ calibration

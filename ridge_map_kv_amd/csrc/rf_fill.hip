@@ -34,9 +34,9 @@ struct FillKArgs {
   const uint16_t* xS;
   int64_t x_stride;
   const int32_t* idx;
-  int64_t P;
+  int64_t P;                    // rows with index >= P are not read (tail / out of range)
   int n_filled;
-  int d, kv, hd;
+  int d, d_in, kv, hd, n_kv;
   float eps;
   int mpad, nchunk;             // nchunk = d / 128 sum-of-squares partials per row
   unsigned char* layer_ws;      // per layer: hbuf [mpad][d] bf16, ssq [nchunk][mpad], rstd [mpad]
@@ -44,7 +44,10 @@ struct FillKArgs {
   const float* rcos;
   const float* rsin;
   const int64_t* row_slot;
+  float* vnorm;                 // norms mode: |v| per row and head, [group][mpad][n_kv]
   int ntt, nft;                 // token tiles, feature tiles of this launch
+  int f_base;                   // first feature tile (norms mode: the V half)
+  int has_scale, has_knorm;     // int8 map row scales; per-head key norm
 };
 
 // Tile order: layer, then groups of kFeatGroup feature tiles (weight rows) swept against
@@ -98,8 +101,8 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
       const int ce = dma_chunk_elems(r, lane);
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d);
-      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d + ce) * 2);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in);
+      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
       const int tok = t0 + r;
       int row = 0;
       if (tok < a.n_filled) {
@@ -111,18 +114,21 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
     }
   }
 
-  // bias and norm weight of feature f0 + tid, fetched under the main loop and parked in LDS
-  // for the epilogue
+  // bias, norm weight (and int8 row scale) of feature f0 + tid, fetched under the main loop
+  // and parked in LDS for the epilogue
   __shared__ __attribute__((aligned(16))) float sbias[kTile];
   __shared__ __attribute__((aligned(16))) float swt[kTile];
+  __shared__ __attribute__((aligned(16))) float ssc[kTile];
   const float my_b = Lp.b[f0 + tid];
   const uint16_t my_w = Lp.w[f0 + tid];
+  const float my_s = a.has_scale ? Lp.As[f0 + tid] : 1.0f;
 
   f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, a.d, smem);
+  gemm_pipeline(acc, Fo, To, a.d_in, smem);
 
   sbias[tid] = my_b;
   swt[tid] = bf16_to_f32(my_w);
+  ssc[tid] = my_s;
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
   uint16_t* hb = reinterpret_cast<uint16_t*>(a.layer_ws + g * a.per_layer);
@@ -136,13 +142,15 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
       const f32x4 bias = *reinterpret_cast<const f32x4*>(sbias + fl);
       const f32x4 wv = *reinterpret_cast<const f32x4*>(swt + fl);
       const float w0 = wv.x, w1 = wv.y, w2 = wv.z, w3 = wv.w;
+      f32x4 sc = {1.f, 1.f, 1.f, 1.f};
+      if (a.has_scale) sc = *reinterpret_cast<const f32x4*>(ssc + fl);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int tl = wt * 128 + n * 32 + (lane & 31);
-        const float v0 = acc[m][n][q * 4 + 0] + bias.x;
-        const float v1 = acc[m][n][q * 4 + 1] + bias.y;
-        const float v2 = acc[m][n][q * 4 + 2] + bias.z;
-        const float v3 = acc[m][n][q * 4 + 3] + bias.w;
+        const float v0 = acc[m][n][q * 4 + 0] * sc.x + bias.x;
+        const float v1 = acc[m][n][q * 4 + 1] * sc.y + bias.y;
+        const float v2 = acc[m][n][q * 4 + 2] * sc.z + bias.z;
+        const float v3 = acc[m][n][q * 4 + 3] * sc.w + bias.w;
         ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
         stage_put4(smem, tl, fl, v0 * w0, v1 * w1, v2 * w2, v3 * w3);
       }
@@ -190,10 +198,32 @@ __device__ __forceinline__ void rope_pair(f32x16 (&acc)[4][4], int n, const floa
   }
 }
 
+// Per-head sums of squares of token block n of the wave's 128 features: head 0 of the wave
+// owns MFMA blocks m with m * 32 / hd == 0, head 1 (hd = 64 only) the others.  Each lane
+// holds half of a head's entries for its token; the lane 32 apart holds the rest.
+__device__ __forceinline__ void head_sumsq(const f32x16 (&acc)[4][4], int n, int hd, float& s0,
+                                           float& s1) {
+  s0 = 0.f;
+  s1 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t += acc[m][n][e] * acc[m][n][e];
+    if (m * 32 < hd) s0 += t; else s1 += t;
+  }
+  s0 += __shfl_xor(s0, 32);
+  s1 += __shfl_xor(s1, 32);
+}
+
+// MODE 0: fill (K and V tiles; RoPE, optional key norm and value rescale, paged stores).
+// MODE 1: value norms (V tiles only): |v| of every (row, head) into a.vnorm.
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   int g, tt, ft;
   decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  ft += a.f_base;
   const FillLayerPtrs Lp = a.L[g];
   const int t0 = tt * kTile, f0 = ft * kTile;
   const int tid = threadIdx.x;
@@ -218,22 +248,53 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
   }
 
   // Per row of the tile: 1/sqrt(mean(x_hat^2) + eps), and the element offset of its slot in
-  // the page pools (-1: skip the row); fetched under the main loop, parked in LDS after it.
+  // the page pools (-1: skip the row); per feature of a key head the key-norm weight, per
+  // value head its rescale factor.  Fetched under the main loop, parked in LDS after it.
   __shared__ float rstd[kTile];
   __shared__ long long rowoff[kTile];
+  __shared__ __attribute__((aligned(16))) float skn[128];
+  __shared__ float svs[kTile];
   const float my_r = rs_tab[t0 + tid];
-  const long long my_off = a.row_slot[t0 + tid];
+  long long my_off = -1;
+  float my_kn = 1.f, my_vs = 1.f;
+  if (MODE == 0) {
+    my_off = a.row_slot[t0 + tid];
+    if (a.has_knorm && tid < a.hd) my_kn = bf16_to_f32(Lp.kn[tid]);
+    if (Lp.vs && tid < a.n_kv) my_vs = Lp.vs[tid];
+  }
 
   f32x16 acc[4][4];
   gemm_pipeline(acc, Fo, To, a.d, smem);
 
   rstd[tid] = my_r;
   rowoff[tid] = my_off;
+  if (tid < 128) skn[tid] = my_kn;
+  svs[tid] = my_vs;
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
-  const bool isK = (f0 + wf * 128) < a.kv;       // kv % 128 == 0: a wave is all K or all V
+  const int fw = f0 + wf * 128;                  // the wave's first feature
+  const bool isK = fw < a.kv;                    // kv % 128 == 0: a wave is all K or all V
   const int half = a.hd >> 1;
+  if (MODE == 1) {
+    if (isK) return;                             // a tile may straddle K and V (kv % 256 != 0)
+    // heads (fw - kv) / hd and, for hd = 64, the next one
+    const int h0 = (fw - a.kv) / a.hd;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int tl = wt * 128 + n * 32 + (lane & 31);
+      const int tok = t0 + tl;
+      const float r = rstd[tl];
+      float s0, s1;
+      head_sumsq(acc, n, a.hd, s0, s1);
+      if (h == 0 && tok < a.n_filled) {
+        float* out = a.vnorm + ((size_t)g * a.mpad + tok) * a.n_kv;
+        out[h0] = r * sqrtf(s0);
+        if (a.hd == 64) out[h0 + 1] = r * sqrtf(s1);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int tl = wt * 128 + n * 32 + (lane & 31);
@@ -244,6 +305,22 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[m][n][e] *= r;
     if (isK) {
+      if (a.has_knorm) {
+        float s0, s1;
+        head_sumsq(acc, n, a.hd, s0, s1);
+        const float k0 = 1.0f / sqrtf(s0 / (float)a.hd + a.eps);
+        const float k1 = 1.0f / sqrtf(s1 / (float)a.hd + a.eps);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float km = (m * 32 < a.hd) ? k0 : k1;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 wk = *reinterpret_cast<const f32x4*>(skn + ((m * 32 + q * 8 + h * 4) & (a.hd - 1)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m][n][q * 4 + e] *= km * wk[e];
+          }
+        }
+      }
       const size_t e0 = ((size_t)(tok >> 5) * (half >> 2) + h) * 128 + (tok & 31) * 4;
       const float* cs = a.rcos + e0;
       const float* sn = a.rsin + e0;
@@ -253,6 +330,17 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
       } else {
         rope_pair<0, 1, 0>(acc, n, cs, sn);
         rope_pair<2, 3, 0>(acc, n, cs, sn);
+      }
+    } else if (Lp.vs) {
+      // value rescale: one factor per head
+      const int hv = (fw - a.kv) / a.hd;
+      const float v0 = svs[hv];
+      const float v1 = a.hd == 64 ? svs[hv + 1] : v0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float vm = (m * 32 < a.hd) ? v0 : v1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[m][n][e] *= vm;
       }
     }
 #pragma unroll
@@ -343,6 +431,90 @@ __global__ void rstd_kernel(unsigned char* layer_ws, size_t per_layer, size_t pe
   reinterpret_cast<float*>(lw + per_layer_h + per_layer_ssq)[row] = 1.0f / sqrtf(s / (float)d + eps);
 }
 
+// int8 map codes as bf16 numbers: |q| <= 127 has at most 8 significant bits, so the bf16
+// value equals the integer exactly (the row scale is applied to the fp32 product).
+__global__ void expand_int8_kernel(const int8_t* q, uint16_t* out, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 16;
+  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; i < n; i += stride) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q + i);   // n and i are multiples of 16
+    u32x4 o[2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = v[w];
+      const float f0 = (float)(int8_t)(x & 0xff), f1 = (float)(int8_t)((x >> 8) & 0xff);
+      const float f2 = (float)(int8_t)((x >> 16) & 0xff), f3 = (float)(int8_t)(x >> 24);
+      o[w >> 1][(w & 1) * 2 + 0] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+      o[w >> 1][(w & 1) * 2 + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+    }
+    *reinterpret_cast<u32x4*>(out + i) = o[0];
+    *reinterpret_cast<u32x4*>(out + i + 8) = o[1];
+  }
+}
+
+__global__ void iota_kernel(int32_t* idx, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) idx[i] = i;
+}
+
+// Exact tail inputs of the value rescale, one block per (row, layer): bf16(x * w) and
+// 1/sqrt(mean(x^2) + eps), written where the map kernel and rstd_kernel put the predicted
+// ones, so the value-norm pass reads both the same way.  Padding rows get zeros.
+struct ExactArgs {
+  const uint16_t* x[kMaxGroup];
+  const uint16_t* w[kMaxGroup];
+  int c, d;
+  float eps;
+  unsigned char* layer_ws;
+  size_t per_layer, per_layer_h, per_layer_ssq;
+};
+
+__global__ void exact_rows_kernel(ExactArgs a) {
+  const int row = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+  unsigned char* lw = a.layer_ws + (size_t)l * a.per_layer;
+  uint16_t* hb = reinterpret_cast<uint16_t*>(lw) + (size_t)row * a.d;
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int c8 = tid; c8 < a.d / 8; c8 += 256) {
+    u32x4 o = {0u, 0u, 0u, 0u};
+    if (row < a.c) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x[l] + (size_t)row * a.d + c8 * 8);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(a.w[l] + c8 * 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = bf16_to_f32(xv[k] & 0xffffu), x1 = bf16_to_f32(xv[k] >> 16);
+        s += x0 * x0;
+        s += x1 * x1;
+        o[k] = pack_bf16x2(x0 * bf16_to_f32(wv[k] & 0xffffu), x1 * bf16_to_f32(wv[k] >> 16));
+      }
+    }
+    *reinterpret_cast<u32x4*>(hb + c8 * 8) = o;
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {          // fixed-order tree: deterministic
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    float* rs = reinterpret_cast<float*>(lw + a.per_layer_h + a.per_layer_ssq);
+    rs[row] = row < a.c ? 1.0f / sqrtf(red[0] / (float)a.d + a.eps) : 0.f;
+  }
+}
+
+// v_scale[l][h] = mean over the c rows of |v_exact| / |v_pred|, added in row order.
+__global__ void vscale_kernel(const float* vn_pred, const float* vn_exact, int c, int cpad,
+                              int n_kv, int G, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= G * n_kv) return;
+  const int l = i / n_kv, hh = i - l * n_kv;
+  double s = 0.0;
+  for (int t = 0; t < c; ++t) {
+    const size_t k = ((size_t)l * cpad + t) * n_kv + hh;
+    s += (double)vn_exact[k] / (double)vn_pred[k];
+  }
+  out[i] = (float)(s / c);
+}
+
 }  // namespace
 
 __global__ void clear_status_kernel(unsigned* status) {
@@ -354,8 +526,8 @@ hipError_t launch_clear_status(unsigned* status, hipStream_t stream) {
   return hipGetLastError();
 }
 
-FillWsLayout fill_ws_layout(int d, int hd, int64_t n_filled) {
-  FillWsLayout L;
+FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned flags) {
+  FillWsLayout L = {};
   const int64_t mpad = (n_filled + kTile - 1) / kTile * kTile;
   const size_t table = align256((size_t)mpad * (hd / 2) * sizeof(float));
   L.rope_cos = kStatusBytes;
@@ -365,13 +537,47 @@ FillWsLayout fill_ws_layout(int d, int hd, int64_t n_filled) {
   L.per_layer_h = align256((size_t)mpad * d * 2);
   L.per_layer_ssq = align256((size_t)mpad * (d / 128) * sizeof(float));
   L.per_layer_rstd = align256((size_t)mpad * sizeof(float));
-  L.per_layer = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
+  const size_t map_elems = (size_t)d * d_in;
+  L.expand = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
+  L.land = L.expand + ((flags & kWsInt8) ? align256(map_elems * 2) : 0);
+  L.land_slot = (flags & kWsStreamed) ? align256(map_elems * ((flags & kWsInt8) ? 1 : 2)) : 0;
+  L.per_layer = L.land + 2 * L.land_slot;
   L.hbuf = L.fixed;
   return L;
 }
 
-hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_layers,
-                       hipStream_t stream) {
+namespace {
+
+FillKArgs fill_args(const FillPlan& p, unsigned char* layer_ws) {
+  FillKArgs a = {};
+  a.xS = p.xS;
+  a.x_stride = p.x_stride;
+  a.idx = p.idx;
+  a.P = p.P;
+  a.n_filled = p.n_filled;
+  a.d = p.d;
+  a.d_in = p.d_in;
+  a.kv = p.kv;
+  a.hd = p.hd;
+  a.n_kv = p.n_kv;
+  a.eps = p.eps;
+  a.mpad = p.mpad;
+  a.nchunk = p.d / 128;
+  a.layer_ws = layer_ws;
+  a.per_layer = p.L.per_layer;
+  a.per_layer_h = p.L.per_layer_h;
+  a.per_layer_ssq = p.L.per_layer_ssq;
+  a.rcos = p.rope_cos;
+  a.rsin = p.rope_sin;
+  a.row_slot = p.row_slot;
+  a.ntt = p.mpad / kTile;
+  a.has_scale = (p.flags & kWsInt8) ? 1 : 0;
+  a.has_knorm = p.has_knorm;
+  return a;
+}
+
+// Status clear, row validation and page slots, RoPE tables: once per call.
+hipError_t launch_fill_prep(const FillPlan& p, hipStream_t stream) {
   hipError_t e = launch_clear_status(p.status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_slot_kernel, dim3(p.mpad / 256), dim3(256), 0, stream, p.idx, p.n_filled,
@@ -381,49 +587,163 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream,
                      p.idx, p.n_filled, p.mpad, (int64_t)p.P, p.hd, p.theta, p.rope_cos,
                      p.rope_sin);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
 
-  FillKArgs a = {};
-  a.xS = p.xS;
-  a.x_stride = p.x_stride;
-  a.idx = p.idx;
-  a.P = p.P;
-  a.n_filled = p.n_filled;
-  a.d = p.d;
-  a.kv = p.kv;
-  a.hd = p.hd;
-  a.eps = p.eps;
-  a.mpad = p.mpad;
-  a.nchunk = p.d / 128;
-  a.layer_ws = reinterpret_cast<unsigned char*>(p.hbuf);
-  const FillWsLayout L = fill_ws_layout(p.d, p.hd, p.n_filled);
-  a.per_layer = L.per_layer;
-  a.per_layer_h = L.per_layer_h;
-  a.per_layer_ssq = L.per_layer_ssq;
-  a.rcos = p.rope_cos;
-  a.rsin = p.rope_sin;
-  a.row_slot = p.row_slot;
-  a.ntt = p.mpad / kTile;
+// int8 codes of the group's maps -> exact bf16 in each layer block's expansion area.
+void expand_group(const FillPlan& p, FillKArgs& a, int G, const int8_t* const* codes,
+                  hipStream_t stream) {
+  const size_t n = (size_t)p.d * p.d_in;
+  for (int g = 0; g < G; ++g) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.layer_ws + g * a.per_layer + p.L.expand);
+    hipLaunchKernelGGL(expand_int8_kernel, dim3(1024), dim3(256), 0, stream, codes[g], dst, n);
+    a.L[g].A = dst;
+  }
+}
 
-  // Balanced groups of at most p.group layers, so one call makes as few, equal
-  // launches as the workspace allows.
-  const int ngroups = (n_layers + p.group - 1) / p.group;
-  const int gsize = (n_layers + ngroups - 1) / ngroups;
+// Map GEMM, 1/RMS, K/V GEMM for the G layers in a.L (their maps already on the device).
+hipError_t launch_fill_group(const FillPlan& p, FillKArgs& a, int G, hipStream_t stream) {
+  a.nft = p.d / kTile;
+  a.f_base = 0;
+  {
+    ProfileScope ps(RF_KERNEL_FILL_MAP, stream);
+    hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+  }
+  hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
+                     a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
+  a.nft = 2 * p.kv / kTile;
+  {
+    ProfileScope ps(RF_KERNEL_FILL_KV, stream);
+    hipLaunchKernelGGL(fill_kv_kernel<0>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// Balanced groups of at most `group` layers: as few, equal launches as the workspace allows.
+int group_size(int n_layers, int group) {
+  const int ngroups = (n_layers + group - 1) / group;
+  return (n_layers + ngroups - 1) / ngroups;
+}
+
+struct StreamEvents {
+  hipEvent_t ready[2] = {nullptr, nullptr};
+  hipEvent_t done[2] = {nullptr, nullptr};
+};
+
+}  // namespace
+
+hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_layers,
+                       hipStream_t stream) {
+  hipError_t e = launch_fill_prep(p, stream);
+  if (e != hipSuccess) return e;
+  unsigned char* lws = reinterpret_cast<unsigned char*>(p.hbuf);
+  const int gsize = group_size(n_layers, p.group);
   for (int l0 = 0; l0 < n_layers; l0 += gsize) {
     const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
-    for (int g = 0; g < G; ++g) a.L[g] = layers[l0 + g];
-    a.nft = p.d / kTile;
-    {
-      ProfileScope ps(RF_KERNEL_FILL_MAP, stream);
-      hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    FillKArgs a = fill_args(p, lws);
+    const int8_t* codes[kMaxGroup];
+    for (int g = 0; g < G; ++g) {
+      a.L[g] = layers[l0 + g];
+      codes[g] = layers[l0 + g].Aq;
     }
+    if (p.flags & kWsInt8) expand_group(p, a, G, codes, stream);
+    if ((e = launch_fill_group(p, a, G, stream)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Maps in (pinned) host memory: group g's maps are copied on copy_stream into landing slot
+// g % 2 of its layer blocks while group g - 1 computes on `stream`; the copy into a slot
+// waits until the group that used it two steps before has finished.
+hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, int n_layers,
+                                hipStream_t stream, hipStream_t copy_stream) {
+  static thread_local StreamEvents ev;
+  for (int i = 0; i < 2; ++i) {
+    hipError_t e;
+    if (!ev.ready[i] && (e = hipEventCreateWithFlags(&ev.ready[i], hipEventDisableTiming)) != hipSuccess) return e;
+    if (!ev.done[i] && (e = hipEventCreateWithFlags(&ev.done[i], hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  hipError_t e = launch_fill_prep(p, stream);
+  if (e != hipSuccess) return e;
+  unsigned char* lws = reinterpret_cast<unsigned char*>(p.hbuf);
+  const bool int8 = (p.flags & kWsInt8) != 0;
+  const size_t map_bytes = (size_t)p.d * p.d_in * (int8 ? 1 : 2);
+  const int gsize = group_size(n_layers, p.group);
+  int gi = 0;
+  for (int l0 = 0; l0 < n_layers; l0 += gsize, ++gi) {
+    const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
+    const int slot = gi & 1;
+    if (gi >= 2 && (e = hipStreamWaitEvent(copy_stream, ev.done[slot], 0)) != hipSuccess) return e;
+    FillKArgs a = fill_args(p, lws);
+    const int8_t* codes[kMaxGroup];
+    for (int g = 0; g < G; ++g) {
+      a.L[g] = layers[l0 + g];
+      unsigned char* land = lws + g * p.L.per_layer + p.L.land + slot * p.L.land_slot;
+      const void* src = int8 ? static_cast<const void*>(layers[l0 + g].Aq)
+                             : static_cast<const void*>(layers[l0 + g].A);
+      if ((e = hipMemcpyAsync(land, src, map_bytes, hipMemcpyHostToDevice, copy_stream)) != hipSuccess)
+        return e;
+      if (int8) codes[g] = reinterpret_cast<const int8_t*>(land);
+      else a.L[g].A = reinterpret_cast<const uint16_t*>(land);
+    }
+    if ((e = hipEventRecord(ev.ready[slot], copy_stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, ev.ready[slot], 0)) != hipSuccess) return e;
+    if (int8) expand_group(p, a, G, codes, stream);
+    if ((e = launch_fill_group(p, a, G, stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev.done[slot], stream)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Value-rescale factors: the c tail rows (indices 0 .. c-1 of x_S_tail) through the map,
+// RMSNorm and W_V, and the exact tail inputs through RMSNorm and W_V; per (row, head) the
+// two value norms; per head the mean of their ratio.
+hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
+                              const uint16_t* const* x_exact, int n_layers, float* out,
+                              const VsLayout& V, hipStream_t stream) {
+  hipError_t e = launch_clear_status(p.status, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(iota_kernel, dim3(p.mpad / 256), dim3(256), 0, stream,
+                     const_cast<int32_t*>(p.idx), p.mpad);
+  unsigned char* pred = reinterpret_cast<unsigned char*>(p.hbuf);
+  const int gsize = group_size(n_layers, p.group);
+  for (int l0 = 0; l0 < n_layers; l0 += gsize) {
+    const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
+    FillKArgs a = fill_args(p, pred);
+    const int8_t* codes[kMaxGroup];
+    for (int g = 0; g < G; ++g) {
+      a.L[g] = layers[l0 + g];
+      codes[g] = layers[l0 + g].Aq;
+    }
+    if (p.flags & kWsInt8) expand_group(p, a, G, codes, stream);
+    a.nft = p.d / kTile;
+    a.f_base = 0;
+    hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
                        a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
-    a.nft = 2 * p.kv / kTile;
-    {
-      ProfileScope ps(RF_KERNEL_FILL_KV, stream);
-      hipLaunchKernelGGL(fill_kv_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    ExactArgs x = {};
+    for (int g = 0; g < G; ++g) {
+      x.x[g] = x_exact[l0 + g];
+      x.w[g] = layers[l0 + g].w;
     }
+    x.c = p.n_filled;
+    x.d = p.d;
+    x.eps = p.eps;
+    x.layer_ws = V.exact;
+    x.per_layer = p.L.per_layer;
+    x.per_layer_h = p.L.per_layer_h;
+    x.per_layer_ssq = p.L.per_layer_ssq;
+    hipLaunchKernelGGL(exact_rows_kernel, dim3(p.mpad, G), dim3(256), 0, stream, x);
+    // value norms of the predicted and of the exact rows: the tiles that hold V features
+    a.f_base = p.kv / kTile;
+    a.nft = 2 * p.kv / kTile - a.f_base;
+    a.vnorm = V.vn_pred;
+    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    a.layer_ws = V.exact;
+    a.vnorm = V.vn_exact;
+    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(vscale_kernel, dim3((G * p.n_kv + 255) / 256), dim3(256), 0, stream,
+                       V.vn_pred, V.vn_exact, p.n_filled, p.mpad, p.n_kv, G, out + (size_t)l0 * p.n_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -17,17 +17,35 @@ constexpr unsigned kStatusNotSpdBit = 2u;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct FillLayerPtrs {
-  const uint16_t* A;
+  const uint16_t* A;            // bf16 map (for an int8 map: its expansion in the workspace)
   const float* b;
   const uint16_t* w;
   const uint16_t* WK;
   const uint16_t* WV;
   uint16_t* kp;
   uint16_t* vp;
+  const uint16_t* kn;           // per-head key-norm weight [hd] or null
+  const float* vs;              // value-rescale factors [n_kv] or null
+  const int8_t* Aq;             // int8 map codes or null
+  const float* As;              // int8 map row scales
 };
 
+// Workspace variants of a fill call.
+constexpr unsigned kWsInt8 = 1u;       // int8 maps: a bf16 expansion area per layer
+constexpr unsigned kWsStreamed = 2u;   // host maps: two landing slots per layer
+
+// Workspace layout of a fill call (bytes from the start of ws; per-layer offsets from the
+// start of that layer's block).
+struct FillWsLayout {
+  size_t rope_cos, rope_sin, row_slot, hbuf, fixed;
+  size_t per_layer_h, per_layer_ssq, per_layer_rstd, expand, land, land_slot, per_layer;
+};
+FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned flags);
+
 struct FillPlan {
-  int d, n_kv, hd, kv;
+  int d, d_in, n_kv, hd, kv;
+  unsigned flags;               // kWsInt8 | kWsStreamed
+  int has_knorm;
   float eps;
   double theta;
   const uint16_t* xS;
@@ -46,17 +64,26 @@ struct FillPlan {
   int64_t* row_slot;            // [mpad] element offset of the row in a page pool, or -1
   uint16_t* hbuf;               // per layer: [mpad][d] bf16, [d/128][mpad] fp32, [mpad] fp32
   int group;                    // layers per launch
+  FillWsLayout L;
 };
-
-// Workspace layout of a fill call (bytes from the start of ws).
-struct FillWsLayout {
-  size_t rope_cos, rope_sin, row_slot, hbuf, per_layer_h, per_layer_ssq, per_layer_rstd, fixed,
-      per_layer;
-};
-FillWsLayout fill_ws_layout(int d, int hd, int64_t n_filled);
 
 hipError_t launch_fill(const FillPlan& plan, const FillLayerPtrs* layers, int n_layers,
                        hipStream_t stream);
+hipError_t launch_fill_streamed(const FillPlan& plan, const FillLayerPtrs* layers, int n_layers,
+                                hipStream_t stream, hipStream_t copy_stream);
+
+// Value-rescale pass: the plan describes c tail rows as its "filled" rows (idx points at
+// an int32 [mpad] scratch list the pass fills with 0 .. mpad-1); predicted rows use the
+// plan's per-layer blocks, exact rows the blocks at `exact`.
+struct VsLayout {
+  size_t idx, vn_pred_off, vn_exact_off, pred, total_fixed;
+  unsigned char* exact;
+  float* vn_pred;
+  float* vn_exact;
+};
+hipError_t launch_value_scale(const FillPlan& plan, const FillLayerPtrs* layers,
+                              const uint16_t* const* x_exact, int n_layers, float* out,
+                              const VsLayout& V, hipStream_t stream);
 
 // Calibration -------------------------------------------------------------------
 struct CalibLayout {

@@ -51,10 +51,137 @@ rf_status check_shape(const rf_shape* s) {
   if (kv % 128) return fail(RF_E_SHAPE, "n_kv_heads * head_dim = %lld must be a multiple of 128",
                             (long long)kv);
   if (kv > (1 << 20)) return fail(RF_E_SHAPE, "n_kv_heads * head_dim too large");
+  if (s->n_kv_heads > 256) return fail(RF_E_SHAPE, "n_kv_heads = %d must be <= 256", s->n_kv_heads);
+  if (s->reserved != 0) return fail(RF_E_INVALID, "shape.reserved must be 0");
+  if (s->d_in != 0 && (s->d_in < 64 || s->d_in % 64))
+    return fail(RF_E_SHAPE, "d_in = %d must be 0 (= d) or a positive multiple of 64", s->d_in);
   if (!(s->rms_eps >= 0.f) || !std::isfinite(s->rms_eps))
     return fail(RF_E_INVALID, "rms_eps must be finite and >= 0");
   if (!(s->rope_theta > 1.0) || !std::isfinite(s->rope_theta))
     return fail(RF_E_INVALID, "rope_theta must be finite and > 1");
+  return RF_OK;
+}
+
+int d_in_of(const rf_shape* s) { return s->d_in ? s->d_in : s->d; }
+
+unsigned map_flags_of(int32_t f) {
+  return ((f & RF_MAPS_INT8) ? rf::kWsInt8 : 0u) | ((f & RF_MAPS_STREAMED) ? rf::kWsStreamed : 0u);
+}
+
+// Checks shared by the resident and the streamed fill; fills the plan and the layer
+// pointers.  `streamed`: the maps (A or A_q) are host pointers.
+rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                       int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                       const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv, void* ws,
+                       size_t ws_bytes, bool streamed, rf::FillPlan& p,
+                       std::vector<rf::FillLayerPtrs>& lp) {
+  const int64_t P = N - T;
+  if (!x_S || !filled_idx || !layers || !kv || !ws)
+    return fail(RF_E_INVALID, "null pointer among x_S, filled_idx, layers, kv, ws");
+  const int d_in = d_in_of(shape);
+  if (x_stride < d_in) return fail(RF_E_SHAPE, "x_stride < d_in");
+  if (x_stride % 8 || !aligned(x_S, 16))
+    return fail(RF_E_SHAPE, "x_S must be 16-byte aligned with x_stride a multiple of 8");
+  if ((uint64_t)(P - 1) * (uint64_t)x_stride * 2u + (uint64_t)d_in * 2u > 0xffffffffull)
+    return fail(RF_E_SHAPE, "the prefix rows of x_S span more than 4 GiB (rows x x_stride x 2 bytes)");
+  if (!kv->block_table || kv->page_size < 1 || kv->num_pages < 1 || kv->n_logical < 1)
+    return fail(RF_E_INVALID, "paged layout: block_table, page_size, num_pages, n_logical");
+  if (kv->n_logical < (P + kv->page_size - 1) / kv->page_size)
+    return fail(RF_E_SHAPE, "block table has %lld pages, the prefix needs %lld",
+                (long long)kv->n_logical, (long long)((P + kv->page_size - 1) / kv->page_size));
+  if (!aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const bool int8 = layers[0].A_q != nullptr;
+  const bool knorm = layers[0].k_norm_w != nullptr;
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    if (!l.b || !l.norm_w || !l.W_K || !l.W_V || !l.k_pages || !l.v_pages)
+      return fail(RF_E_INVALID, "layer %d has a null pointer", i);
+    if ((l.A != nullptr) == (l.A_q != nullptr))
+      return fail(RF_E_INVALID, "layer %d: exactly one of A and A_q must be set", i);
+    if ((l.A_q != nullptr) != int8)
+      return fail(RF_E_INVALID, "layer %d: all layers of a call must use bf16 maps or all int8", i);
+    if (int8 && !l.A_scale) return fail(RF_E_INVALID, "layer %d: A_q without A_scale", i);
+    if ((l.k_norm_w != nullptr) != knorm)
+      return fail(RF_E_INVALID, "layer %d: all layers of a call must have a key norm or none", i);
+    if ((l.A && !aligned(l.A, 16)) || (l.A_q && !aligned(l.A_q, 16)) || !aligned(l.b, 16) ||
+        !aligned(l.norm_w, 8) || !aligned(l.W_K, 16) || !aligned(l.W_V, 16) ||
+        !aligned(l.k_pages, 8) || !aligned(l.v_pages, 8) ||
+        (l.A_scale && !aligned(l.A_scale, 4)) || (l.v_scale && !aligned(l.v_scale, 4)) ||
+        (l.k_norm_w && !aligned(l.k_norm_w, 2)))
+      return fail(RF_E_SHAPE, "layer %d: A, A_q, b, W_K, W_V need 16-byte, norm_w and the pages "
+                  "8-byte alignment", i);
+  }
+  const unsigned flags = (int8 ? rf::kWsInt8 : 0u) | (streamed ? rf::kWsStreamed : 0u);
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim, n_filled, flags);
+  if (ws_bytes < L.fixed + L.per_layer)
+    return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed for one layer", ws_bytes,
+                L.fixed + L.per_layer);
+  size_t group = (ws_bytes - L.fixed) / L.per_layer;
+  if (group > (size_t)rf::kMaxGroup) group = rf::kMaxGroup;
+
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  p = rf::FillPlan{};
+  p.d = shape->d;
+  p.d_in = d_in;
+  p.n_kv = shape->n_kv_heads;
+  p.hd = shape->head_dim;
+  p.kv = shape->n_kv_heads * shape->head_dim;
+  p.flags = flags;
+  p.has_knorm = knorm ? 1 : 0;
+  p.eps = shape->rms_eps;
+  p.theta = shape->rope_theta;
+  p.xS = x_S;
+  p.x_stride = x_stride;
+  p.N = N;
+  p.P = P;
+  p.idx = filled_idx;
+  p.n_filled = (int)n_filled;
+  p.mpad = (int)((n_filled + rf::kTile - 1) / rf::kTile * rf::kTile);
+  p.block_table = kv->block_table;
+  p.n_logical = kv->n_logical;
+  p.page_size = kv->page_size;
+  p.num_pages = kv->num_pages;
+  p.status = reinterpret_cast<unsigned*>(w);
+  p.rope_cos = reinterpret_cast<float*>(w + L.rope_cos);
+  p.rope_sin = reinterpret_cast<float*>(w + L.rope_sin);
+  p.row_slot = reinterpret_cast<int64_t*>(w + L.row_slot);
+  p.hbuf = reinterpret_cast<uint16_t*>(w + L.hbuf);
+  p.group = (int)group;
+  p.L = L;
+
+  lp.resize((size_t)n_layers);
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.k_pages, l.v_pages,
+             l.k_norm_w, l.v_scale, l.A_q, l.A_scale};
+  }
+  return RF_OK;
+}
+
+// Common front of ridgefill_fill and ridgefill_fill_streamed: scalar checks and the empty
+// call.  Returns RF_OK with *done set when nothing more is to be done.
+rf_status fill_front(const rf_shape* shape, int64_t N, int64_t T, int64_t n_filled,
+                     int32_t n_layers, void* ws, size_t ws_bytes, void* stream, bool* done) {
+  *done = false;
+  rf_status s = check_shape(shape);
+  if (s != RF_OK) return s;
+  if (N < 0 || T < 0 || T > N) return fail(RF_E_SHAPE, "need 0 <= T <= N");
+  const int64_t P = N - T;
+  if (n_filled < 0 || n_filled > P)
+    return fail(RF_E_SHAPE, "n_filled = %lld must be in [0, N - T = %lld]", (long long)n_filled,
+                (long long)P);
+  if (n_filled > INT32_MAX - rf::kTile) return fail(RF_E_SHAPE, "n_filled too large");
+  if (n_layers < 0) return fail(RF_E_INVALID, "n_layers < 0");
+  if (n_filled == 0 || n_layers == 0) {
+    if (ws) {
+      if (!aligned(ws, 256) || ws_bytes < rf::kStatusBytes)
+        return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned and >= 256 bytes");
+      hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws),
+                                             static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "status clear");
+    }
+    *done = true;
+  }
   return RF_OK;
 }
 
@@ -93,98 +220,163 @@ rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
   return ok();
 }
 
-size_t ridgefill_fill_workspace_bytes(const rf_shape* shape, int64_t n_filled, int32_t n_layers) {
-  if (check_shape(shape) != RF_OK || n_filled < 0 || n_layers < 1) return 0;
-  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, shape->head_dim, n_filled);
+size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled,
+                                         int32_t n_layers, int32_t map_flags) {
+  if (check_shape(shape) != RF_OK || n_filled < 0 || n_layers < 1 ||
+      (map_flags & ~(RF_MAPS_INT8 | RF_MAPS_STREAMED)))
+    return 0;
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim,
+                                                n_filled, map_flags_of(map_flags));
   const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
   return L.fixed + (size_t)g * L.per_layer;
+}
+
+size_t ridgefill_fill_workspace_bytes(const rf_shape* shape, int64_t n_filled, int32_t n_layers) {
+  return ridgefill_fill_workspace_bytes_ex(shape, n_filled, n_layers, 0);
 }
 
 rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
                          int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
                          const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
                          void* ws, size_t ws_bytes, void* stream) {
+  bool done;
+  rf_status s = fill_front(shape, N, T, n_filled, n_layers, ws, ws_bytes, stream, &done);
+  if (s != RF_OK || done) return s == RF_OK ? ok() : s;
+  rf::FillPlan p;
+  std::vector<rf::FillLayerPtrs> lp;
+  s = prepare_fill(shape, x_S, N, T, x_stride, filled_idx, n_filled, layers, n_layers, kv, ws,
+                   ws_bytes, false, p, lp);
+  if (s != RF_OK) return s;
+  hipError_t e = rf::launch_fill(p, lp.data(), n_layers, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  return ok();
+}
+
+rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                                  int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                                  const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
+                                  void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
+  bool done;
+  rf_status s = fill_front(shape, N, T, n_filled, n_layers, ws, ws_bytes, stream, &done);
+  if (s != RF_OK || done) return s == RF_OK ? ok() : s;
+  if (copy_stream == stream)
+    return fail(RF_E_INVALID, "copy_stream must differ from stream for the copies to overlap");
+  rf::FillPlan p;
+  std::vector<rf::FillLayerPtrs> lp;
+  s = prepare_fill(shape, x_S, N, T, x_stride, filled_idx, n_filled, layers, n_layers, kv, ws,
+                   ws_bytes, true, p, lp);
+  if (s != RF_OK) return s;
+  hipError_t e = rf::launch_fill_streamed(p, lp.data(), n_layers, static_cast<hipStream_t>(stream),
+                                          static_cast<hipStream_t>(copy_stream));
+  if (e != hipSuccess) return hip_fail(e, "streamed fill launch");
+  return ok();
+}
+
+// Value-rescale workspace: status, row list, two norm arrays, then per layer of a group a
+// predicted block and an exact block (each laid out like a fill layer block).
+static rf::VsLayout vs_layout(const rf::FillWsLayout& L, int64_t c, int n_kv, int group) {
+  rf::VsLayout V = {};
+  const int64_t cpad = (c + rf::kTile - 1) / rf::kTile * rf::kTile;
+  V.idx = rf::kStatusBytes;
+  V.vn_pred_off = V.idx + rf::align256((size_t)cpad * 4);
+  const size_t vn = rf::align256((size_t)group * cpad * n_kv * 4);
+  V.vn_exact_off = V.vn_pred_off + vn;
+  V.pred = V.vn_exact_off + vn;
+  V.exact = nullptr;
+  V.total_fixed = V.pred;
+  (void)L;
+  return V;
+}
+
+size_t ridgefill_value_scale_workspace_bytes(const rf_shape* shape, int64_t c, int32_t n_layers,
+                                             int32_t map_flags) {
+  if (check_shape(shape) != RF_OK || c < 1 || n_layers < 1 || (map_flags & ~RF_MAPS_INT8))
+    return 0;
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim, c,
+                                                map_flags_of(map_flags));
+  const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
+  const rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, g);
+  return V.total_fixed + (size_t)2 * g * L.per_layer;
+}
+
+rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail, int64_t x_stride,
+                                const uint16_t* const* x_l_tail, int64_t c, const rf_layer* layers,
+                                int32_t n_layers, float* v_scale_out, void* ws, size_t ws_bytes,
+                                void* stream) {
   rf_status s = check_shape(shape);
   if (s != RF_OK) return s;
-  if (N < 0 || T < 0 || T > N) return fail(RF_E_SHAPE, "need 0 <= T <= N");
-  const int64_t P = N - T;
-  if (n_filled < 0 || n_filled > P)
-    return fail(RF_E_SHAPE, "n_filled = %lld must be in [0, N - T = %lld]", (long long)n_filled,
-                (long long)P);
-  if (n_filled > INT32_MAX - rf::kTile) return fail(RF_E_SHAPE, "n_filled too large");
-  if (n_layers < 0) return fail(RF_E_INVALID, "n_layers < 0");
-  if (n_filled == 0 || n_layers == 0) {
-    if (ws) {
-      if (!aligned(ws, 256) || ws_bytes < rf::kStatusBytes)
-        return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned and >= 256 bytes");
-      hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws),
-                                             static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return hip_fail(e, "status clear");
-    }
-    return ok();
-  }
-  if (!x_S || !filled_idx || !layers || !kv || !ws)
-    return fail(RF_E_INVALID, "null pointer among x_S, filled_idx, layers, kv, ws");
-  if (x_stride < shape->d) return fail(RF_E_SHAPE, "x_stride < d");
-  if (x_stride % 8 || !aligned(x_S, 16))
-    return fail(RF_E_SHAPE, "x_S must be 16-byte aligned with x_stride a multiple of 8");
-  if ((uint64_t)(P - 1) * (uint64_t)x_stride * 2u + (uint64_t)shape->d * 2u > 0xffffffffull)
-    return fail(RF_E_SHAPE, "the prefix rows of x_S span more than 4 GiB (rows x x_stride x 2 bytes)");
-  if (!kv->block_table || kv->page_size < 1 || kv->num_pages < 1 || kv->n_logical < 1)
-    return fail(RF_E_INVALID, "paged layout: block_table, page_size, num_pages, n_logical");
-  if (kv->n_logical < (P + kv->page_size - 1) / kv->page_size)
-    return fail(RF_E_SHAPE, "block table has %lld pages, the prefix needs %lld",
-                (long long)kv->n_logical, (long long)((P + kv->page_size - 1) / kv->page_size));
-  if (!aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (c < 1 || c > (1 << 20)) return fail(RF_E_SHAPE, "c = %lld must be in [1, 2^20]", (long long)c);
+  if (n_layers < 1) return fail(RF_E_INVALID, "n_layers must be >= 1");
+  if (!x_S_tail || !x_l_tail || !layers || !v_scale_out || !ws)
+    return fail(RF_E_INVALID, "null pointer among x_S_tail, x_l_tail, layers, v_scale_out, ws");
+  const int d_in = d_in_of(shape);
+  if (x_stride < d_in || x_stride % 8 || !aligned(x_S_tail, 16))
+    return fail(RF_E_SHAPE, "x_S_tail must be 16-byte aligned, x_stride >= d_in and a multiple of 8");
+  if ((uint64_t)(c - 1) * (uint64_t)x_stride * 2u + (uint64_t)d_in * 2u > 0xffffffffull)
+    return fail(RF_E_SHAPE, "the tail rows of x_S span more than 4 GiB");
+  if (!aligned(ws, 256) || !aligned(v_scale_out, 4))
+    return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned, v_scale_out 4-byte aligned");
+  const bool int8 = layers[0].A_q != nullptr;
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
-    if (!l.A || !l.b || !l.norm_w || !l.W_K || !l.W_V || !l.k_pages || !l.v_pages)
-      return fail(RF_E_INVALID, "layer %d has a null pointer", i);
-    if (!aligned(l.A, 16) || !aligned(l.b, 16) || !aligned(l.norm_w, 8) || !aligned(l.W_K, 16) ||
-        !aligned(l.W_V, 16) || !aligned(l.k_pages, 8) || !aligned(l.v_pages, 8))
-      return fail(RF_E_SHAPE, "layer %d: A, b, W_K, W_V need 16-byte, norm_w and the pages "
-                  "8-byte alignment", i);
+    if (!l.b || !l.norm_w || !l.W_K || !l.W_V || !x_l_tail[i])
+      return fail(RF_E_INVALID, "layer %d: b, norm_w, W_K, W_V and its exact tail rows are "
+                  "required", i);
+    if ((l.A != nullptr) == (l.A_q != nullptr) || (l.A_q != nullptr) != int8 ||
+        (int8 && !l.A_scale))
+      return fail(RF_E_INVALID, "layer %d: exactly one of A and A_q (with A_scale), the same kind "
+                  "for all layers", i);
+    if ((l.A && !aligned(l.A, 16)) || (l.A_q && !aligned(l.A_q, 16)) || !aligned(l.b, 16) ||
+        !aligned(l.norm_w, 16) || !aligned(l.W_K, 16) || !aligned(l.W_V, 16) ||
+        !aligned(x_l_tail[i], 16))
+      return fail(RF_E_SHAPE, "layer %d: A, A_q, b, norm_w, W_V and the exact rows need 16-byte "
+                  "alignment", i);
   }
-  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, shape->head_dim, n_filled);
-  if (ws_bytes < L.fixed + L.per_layer)
-    return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed for one layer", ws_bytes,
-                L.fixed + L.per_layer);
-  size_t group = (ws_bytes - L.fixed) / L.per_layer;
-  if (group > (size_t)rf::kMaxGroup) group = rf::kMaxGroup;
-
+  const unsigned flags = int8 ? rf::kWsInt8 : 0u;
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim, c, flags);
+  const int gmax = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
+  // the largest group the workspace holds: fixed part for that group + 2 blocks per layer
+  int group = 0;
+  for (int g = gmax; g >= 1; --g) {
+    const rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, g);
+    if (ws_bytes >= V.total_fixed + (size_t)2 * g * L.per_layer) { group = g; break; }
+  }
+  if (group == 0)
+    return fail(RF_E_WORKSPACE, "workspace %zu bytes too small for one layer", ws_bytes);
+  rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, group);
   unsigned char* w = static_cast<unsigned char*>(ws);
+  V.exact = w + V.pred + (size_t)group * L.per_layer;
+  V.vn_pred = reinterpret_cast<float*>(w + V.vn_pred_off);
+  V.vn_exact = reinterpret_cast<float*>(w + V.vn_exact_off);
+
   rf::FillPlan p = {};
   p.d = shape->d;
+  p.d_in = d_in;
   p.n_kv = shape->n_kv_heads;
   p.hd = shape->head_dim;
   p.kv = shape->n_kv_heads * shape->head_dim;
+  p.flags = flags;
   p.eps = shape->rms_eps;
   p.theta = shape->rope_theta;
-  p.xS = x_S;
+  p.xS = x_S_tail;
   p.x_stride = x_stride;
-  p.N = N;
-  p.P = P;
-  p.idx = filled_idx;
-  p.n_filled = (int)n_filled;
-  p.mpad = (int)((n_filled + rf::kTile - 1) / rf::kTile * rf::kTile);
-  p.block_table = kv->block_table;
-  p.n_logical = kv->n_logical;
-  p.page_size = kv->page_size;
-  p.num_pages = kv->num_pages;
+  p.N = c;
+  p.P = c;
+  p.idx = reinterpret_cast<const int32_t*>(w + V.idx);
+  p.n_filled = (int)c;
+  p.mpad = (int)((c + rf::kTile - 1) / rf::kTile * rf::kTile);
   p.status = reinterpret_cast<unsigned*>(w);
-  p.rope_cos = reinterpret_cast<float*>(w + L.rope_cos);
-  p.rope_sin = reinterpret_cast<float*>(w + L.rope_sin);
-  p.row_slot = reinterpret_cast<int64_t*>(w + L.row_slot);
-  p.hbuf = reinterpret_cast<uint16_t*>(w + L.hbuf);
-  p.group = (int)group;
-
+  p.hbuf = reinterpret_cast<uint16_t*>(w + V.pred);
+  p.group = group;
+  p.L = L;
   std::vector<rf::FillLayerPtrs> lp((size_t)n_layers);
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
-    lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.k_pages, l.v_pages};
+    lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, nullptr, nullptr, nullptr, nullptr, l.A_q, l.A_scale};
   }
-  hipError_t e = rf::launch_fill(p, lp.data(), n_layers, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  hipError_t e = rf::launch_value_scale(p, lp.data(), x_l_tail, n_layers, v_scale_out, V,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "value-scale launch");
   return ok();
 }
 

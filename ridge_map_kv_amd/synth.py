@@ -18,6 +18,14 @@ Recipes (the shapes and value distributions of the workloads):
     seeded contiguous blocks with lengths U[16, 80] covering half of the budget plus
     uniformly drawn singletons for the other half ("blocks").
   * Block tables: a seeded permutation of the physical pages.
+  * Rectangular maps (a gated-residual model reads a d_in-wide state into d-wide layers):
+    A = [I | 0] + U V^T / 2 with U ~ N(0, 1/d) [d, 64], V ~ N(0, 1/d_in) [d_in, 64]
+    (the identity block on the first d inputs), b ~ N(0, 1).
+  * Key-norm weights 1 + 0.1 N(0, 1) [head_dim]; value-rescale factors U[0.5, 1.5].
+  * Exact tail inputs for the value rescale: the near-identity model's x_l on the tail
+    rows (x_l = W_true x_S + c + 0.1 e, e ~ N(0, 1)).
+  * Attention-like row scores: Exp(1) draws, rounded to multiples of 1/64 so that ties
+    occur.
 """
 
 from __future__ import annotations
@@ -36,7 +44,7 @@ def rng(seed: int, *tags: int) -> np.random.Generator:
 
 # Stream tags, so every tensor has its own stream.
 TAG_XS, TAG_EXACT, TAG_TABLE, TAG_NORM, TAG_WK, TAG_WV, TAG_MAPU, TAG_MAPV, TAG_MAPB, \
-    TAG_CAL_X, TAG_CAL_NOISE, TAG_CAL_C = range(1, 13)
+    TAG_CAL_X, TAG_CAL_NOISE, TAG_CAL_C, TAG_KNORM, TAG_VSCALE, TAG_SCORES = range(1, 16)
 
 
 def exact_rows(cfg) -> np.ndarray:
@@ -250,3 +258,38 @@ def device_hadamard_columns(rows: int, cols: int, dev, first_col: int = 1):
         par ^= v & 1
         v = v >> 1
     return (1 - 2 * par).to(torch.float32)
+
+
+def rect_map(d_out: int, d_in: int, seed: int, layer: int):
+    """A = [I | 0] + U V^T / 2 (float32 [d_out, d_in]) and b ~ N(0, 1) (float32 [d_out])."""
+    U = rng(seed, TAG_MAPU, layer).standard_normal((d_out, TRUE_MAP_RANK), dtype=np.float32)
+    V = rng(seed, TAG_MAPV, layer).standard_normal((d_in, TRUE_MAP_RANK), dtype=np.float32)
+    A = (U / np.sqrt(d_out)) @ (V / np.sqrt(d_in)).T * np.float32(TRUE_MAP_GAIN)
+    A[:, :min(d_out, d_in)] += np.eye(d_out, min(d_out, d_in), dtype=np.float32)
+    b = rng(seed, TAG_MAPB, layer).standard_normal(d_out, dtype=np.float32)
+    return A.astype(np.float32), b.astype(np.float32)
+
+
+def key_norm_weight(hd: int, seed: int, layer: int) -> np.ndarray:
+    """1 + 0.1 N(0, 1), float32 [hd]."""
+    return (1.0 + 0.1 * rng(seed, TAG_KNORM, layer).standard_normal(hd)).astype(np.float32)
+
+
+def value_factors(n_kv: int, seed: int, layer: int) -> np.ndarray:
+    """U[0.5, 1.5], float32 [n_kv]."""
+    return rng(seed, TAG_VSCALE, layer).uniform(0.5, 1.5, n_kv).astype(np.float32)
+
+
+def exact_tail_inputs(xS_tail: np.ndarray, d: int, seed: int, layer: int) -> np.ndarray:
+    """x_l of the near-identity model on the given split-layer rows (float32 [c, d])."""
+    U, V = true_map_factors(d, seed, layer)
+    c = rng(seed, TAG_CAL_C, layer).standard_normal(d, dtype=np.float32)
+    e = rng(seed, TAG_CAL_NOISE, layer).standard_normal(xS_tail.shape, dtype=np.float32)
+    return (xS_tail + TRUE_MAP_GAIN * ((xS_tail @ V) @ U.T) + c[None, :] + 0.1 * e).astype(np.float32)
+
+
+def row_scores(P: int, seed: int) -> np.ndarray:
+    """Exp(1) draws rounded to multiples of 1/64 (ties occur), float32 [P]."""
+    s = rng(seed, TAG_SCORES).exponential(1.0, P)
+    return (np.round(s * 64.0) / 64.0).astype(np.float32)
+

@@ -39,27 +39,54 @@ class Case:
     theta: float = 500000.0
     map_kind: str = "near_identity"      # or "identity", or "given"
     maps: list | None = None             # [(A float32 [d,d], b float32 [d])] for "given"
+    d_in: int = 0                        # width of x_S (0: d); != d gives a rectangular map
+    knorm: bool = False                  # per-head key norm
+    vscale: bool = False                 # value-rescale factors
+    int8: bool = False                   # int8 maps (codes + row scales)
 
     @property
     def kv(self):
         return self.n_kv * self.hd
 
+    @property
+    def width(self):
+        return self.d_in or self.d
+
+    @property
+    def map_flags(self):
+        return B.RF_MAPS_INT8 if self.int8 else 0
+
 
 def build_inputs(case: Case, dev="cuda"):
     d, kv = case.d, case.kv
-    xS = synth.x_split((case.N, d), seed=case.seed)
+    xS = synth.x_split((case.N, case.width), seed=case.seed)
     table, num_pages = synth.block_table(case.N, case.page_size, case.seed)
     layers = []
     for l in range(case.n_layers):
         w, WK, WV = synth.layer_weights(d, kv, case.seed, l)
         if case.map_kind == "identity":
-            A, b = np.eye(d, dtype=np.float32), np.zeros(d, dtype=np.float32)
+            A, b = np.eye(d, case.width, dtype=np.float32), np.zeros(d, dtype=np.float32)
         elif case.map_kind == "given":
             A, b = case.maps[l]
+        elif case.width != d:
+            A, b = synth.rect_map(d, case.width, case.seed, l)
         else:
             A, b = synth.near_identity_map(d, case.seed, l)
-        layers.append(dict(A=to_bf16(A, dev), b=torch.from_numpy(np.asarray(b, np.float32)).to(dev),
-                           norm_w=to_bf16(w, dev), W_K=to_bf16(WK, dev), W_V=to_bf16(WV, dev)))
+        lay = dict(b=torch.from_numpy(np.asarray(b, np.float32)).to(dev), norm_w=to_bf16(w, dev),
+                   W_K=to_bf16(WK, dev), W_V=to_bf16(WV, dev))
+        if case.int8:
+            # codes from the oracle's float32 quantizer; the reference uses q * scale exactly
+            q, sc = oracle.quantize_map_int8(A.astype(np.float32), np.float32)
+            lay["A_q"] = torch.from_numpy(q).to(dev)
+            lay["A_scale"] = torch.from_numpy(sc.astype(np.float32)).to(dev)
+            lay["A_ref"] = oracle.dequantize_map_int8(q, sc)
+        else:
+            lay["A"] = to_bf16(A, dev)
+        if case.knorm:
+            lay["k_norm_w"] = to_bf16(synth.key_norm_weight(case.hd, case.seed, l), dev)
+        if case.vscale:
+            lay["v_scale"] = torch.from_numpy(synth.value_factors(case.n_kv, case.seed, l)).to(dev)
+        layers.append(lay)
     for lay in layers:
         shape = (num_pages, case.page_size, case.n_kv, case.hd)
         lay["k_pages"] = _sentinel(shape, dev)
@@ -74,16 +101,42 @@ def _sentinel(shape, dev):
     return t
 
 
-def run_fill(case: Case, inp, filled: np.ndarray, ws_layers: int | None = None, stream=None):
+def make_shape(case: Case):
+    return B.make_shape(case.d, case.n_kv, case.hd, case.eps, case.theta,
+                        d_in=case.d_in if case.width != case.d else 0)
+
+
+def host_maps(layers: list[dict]) -> list[dict]:
+    """The same layers with their maps (A or A_q) copied to page-locked host tensors."""
+    out = []
+    for lay in layers:
+        h = dict(lay)
+        key = "A_q" if "A_q" in lay else "A"
+        pinned = torch.empty(lay[key].shape, dtype=lay[key].dtype, pin_memory=True)
+        pinned.copy_(lay[key].cpu())
+        h[key] = pinned
+        out.append(h)
+    return out
+
+
+def run_fill(case: Case, inp, filled: np.ndarray, ws_layers: int | None = None, stream=None,
+             streamed: bool = False):
     dev = inp["xS"].device
-    shape = B.make_shape(case.d, case.n_kv, case.hd, case.eps, case.theta)
+    shape = make_shape(case)
     nf = int(filled.size)
     idx = torch.from_numpy(np.asarray(filled, dtype=np.int32)).to(dev)
+    flags = case.map_flags | (B.RF_MAPS_STREAMED if streamed else 0)
     nbytes = B.ridgefill_fill_workspace_bytes(shape, max(nf, 1),
-                                              ws_layers if ws_layers else case.n_layers)
+                                              ws_layers if ws_layers else case.n_layers, flags)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, inp["layers"], inp["table"],
-                     case.page_size, inp["num_pages"], ws, stream=stream)
+    if streamed:
+        layers = host_maps(inp["layers"])
+        copy = torch.cuda.Stream()
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, layers, inp["table"],
+                         case.page_size, inp["num_pages"], ws, stream=stream, copy_stream=copy)
+    else:
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, inp["layers"], inp["table"],
+                         case.page_size, inp["num_pages"], ws, stream=stream)
     status = B.ridgefill_read_status(ws, stream)
     return status
 
@@ -93,9 +146,13 @@ def oracle_layer(case: Case, inp, l: int, filled: np.ndarray, rows: np.ndarray |
     lay = inp["layers"][l]
     sel = filled if rows is None else rows
     xs = bf16_np(inp["xS"][torch.from_numpy(np.asarray(sel, np.int64)).to(inp["xS"].device)])
-    return oracle.fill_rows(xs, sel, bf16_np(lay["A"]), lay["b"].cpu().numpy().astype(np.float64),
+    A = lay["A_ref"] if "A_ref" in lay else bf16_np(lay["A"])
+    kn = bf16_np(lay["k_norm_w"]) if "k_norm_w" in lay else None
+    vs = lay["v_scale"].cpu().numpy().astype(np.float64) if "v_scale" in lay else None
+    return oracle.fill_rows(xs, sel, A, lay["b"].cpu().numpy().astype(np.float64),
                             bf16_np(lay["norm_w"]), bf16_np(lay["W_K"]), bf16_np(lay["W_V"]),
-                            eps=case.eps, theta=case.theta, n_kv=case.n_kv, hd=case.hd)
+                            eps=case.eps, theta=case.theta, n_kv=case.n_kv, hd=case.hd,
+                            k_norm_w=kn, v_scale=vs)
 
 
 def gpu_rows(case: Case, inp, l: int, rows: np.ndarray):
