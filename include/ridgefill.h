@@ -109,6 +109,27 @@ rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
                               int32_t* filled_idx, int64_t* n_filled);
 
 /* ------------------------------------------------------------------------------
+ * Exact-row selection from scores, on the device.  Section "Which rows to compute
+ * exactly", attention selection: the prefix rows that receive the most attention are
+ * computed exactly (10% of them in the reference study's "+rows" arm).  Given one score
+ * per prefix row, the k rows with the largest score, ties broken toward the lower row
+ * index, are the exact rows; the other P - k rows, in ascending order, are written to
+ * filled_idx, ready for ridgefill_fill with n_filled = P - k.
+ *
+ *   scores      device fp32 [P]; -0.0 and +0.0 tie; a NaN score ranks lowest and sets
+ *               RF_E_INVALID in the device status (ridgefill_read_status(ws))
+ *   k           0 <= k <= P
+ *   exact_mask  device uint8 [P] out (1 = exact), or NULL
+ *   filled_idx  device int32 [P - k] out
+ *   ws          device workspace >= ridgefill_select_workspace_bytes(P); its first 256
+ *               bytes hold the status
+ * Integer and order decisions only: the result is exact and deterministic.
+ * ------------------------------------------------------------------------------ */
+size_t ridgefill_select_workspace_bytes(int64_t P);
+rf_status ridgefill_select_rows(const float* scores, int64_t P, int64_t k, uint8_t* exact_mask,
+                                int32_t* filled_idx, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Fill.  Section "Ridge map: predict the input, and the original projection runs
  * unchanged" (prediction equation, "own normalization and projections", Fig. 2):
  * for every filled row t and every given upper layer l,
@@ -245,9 +266,10 @@ rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int3
                           double lambda, float* A_out, float* b_out, uint16_t* A_bf16_out,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* Waits for `stream`, then returns the device status word of a fill or solve workspace
- * (RF_OK, RF_E_ROWS, RF_E_NOT_SPD).  Each fill or solve call clears that word on the
- * stream before its own kernels run, so the word reflects the last call only. */
+/* Waits for `stream`, then returns the device status word of a fill, solve or selection
+ * workspace: RF_OK, RF_E_ROWS, RF_E_NOT_SPD, or RF_E_INVALID for a NaN score.  Each call
+ * clears that word on the stream before its own kernels run, so the word reflects the
+ * last call only. */
 rf_status ridgefill_read_status(void* ws, void* stream);
 
 /* ------------------------------------------------------------------------------

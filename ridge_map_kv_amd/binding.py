@@ -26,6 +26,8 @@ EXPORTED = [
     "ridgefill_fill_streamed",
     "ridgefill_value_scale_workspace_bytes",
     "ridgefill_value_scale",
+    "ridgefill_select_workspace_bytes",
+    "ridgefill_select_rows",
     "ridgefill_calib_state_bytes",
     "ridgefill_calib_reset",
     "ridgefill_calibrate",
@@ -94,6 +96,8 @@ def lib() -> C.CDLL:
         "ridgefill_value_scale_workspace_bytes": (sz, [C.POINTER(rf_shape), i64, i32, i32]),
         "ridgefill_value_scale": (st, [C.POINTER(rf_shape), vp, i64, C.POINTER(vp), i64,
                                        C.POINTER(rf_layer), i32, vp, vp, sz, vp]),
+        "ridgefill_select_workspace_bytes": (sz, [i64]),
+        "ridgefill_select_rows": (st, [vp, i64, i64, vp, vp, vp, sz, vp]),
         "ridgefill_calib_state_bytes": (sz, [i32, i32]),
         "ridgefill_calib_reset": (st, [vp, sz, i32, i32, vp]),
         "ridgefill_calibrate": (st, [vp, sz, i32, i32, vp, C.POINTER(vp), i64, vp]),
@@ -153,6 +157,19 @@ def ridgefill_partition(N: int, T: int, exact_mask: np.ndarray | None) -> np.nda
         m = exact_mask.ctypes.data
     _check(lib().ridgefill_partition(int(N), int(T), m, out.ctypes.data, C.byref(n)))
     return out[: n.value].copy()
+
+
+# ------------------------------------------------------------------------------ selection
+
+def ridgefill_select_workspace_bytes(P: int) -> int:
+    return int(lib().ridgefill_select_workspace_bytes(int(P)))
+
+
+def ridgefill_select_rows(scores, k: int, filled_idx, ws, exact_mask=None, stream=None) -> None:
+    """Top-k rows by score (ties to the lower index) -> exact_mask (optional, uint8 [P])
+    and the remaining rows in ascending order -> filled_idx (int32 [P - k])."""
+    _check(lib().ridgefill_select_rows(_ptr(scores), int(scores.numel()), int(k), _ptr(exact_mask),
+                                       _ptr(filled_idx), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------ fill
@@ -247,9 +264,12 @@ def ridgefill_solve(state, d: int, n_layers: int, lam: float, A_out, b_out, A_bf
 
 
 def ridgefill_read_status(ws, stream=None) -> int:
-    """Device status of the last fill/solve on this workspace (waits for the stream)."""
+    """Device status of the last fill/solve/selection on this workspace (waits for the
+    stream): RF_OK, RF_E_ROWS, RF_E_NOT_SPD or RF_E_INVALID (a NaN selection score)."""
+    if ws is None:
+        raise ValueError("ws is None")
     s = lib().ridgefill_read_status(_ptr(ws), _stream(stream))
-    if s not in (RF_OK, RF_E_ROWS, RF_E_NOT_SPD):
+    if s not in (RF_OK, RF_E_ROWS, RF_E_NOT_SPD, RF_E_INVALID):
         _check(s)
     return int(s)
 

@@ -13,6 +13,7 @@ constexpr size_t kStatusBytes = 256;
 // Device status bits kept in the first word of a fill or solve workspace.
 constexpr unsigned kStatusRowsBit = 1u;
 constexpr unsigned kStatusNotSpdBit = 2u;
+constexpr unsigned kStatusScoreBit = 4u;     // a selection score was NaN
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -105,5 +106,13 @@ hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, f
                         float* b_out, uint16_t* A_bf16, void* ws, hipStream_t stream);
 
 hipError_t launch_clear_status(unsigned* status, hipStream_t stream);
+
+// Exact-row selection ------------------------------------------------------------
+struct SelLayout {
+  size_t state, hist, blocks, total;
+};
+SelLayout select_layout(int64_t P);
+hipError_t launch_select(const float* scores, int64_t P, int64_t k, uint8_t* exact,
+                         int32_t* filled, void* ws, hipStream_t stream);
 
 }  // namespace rf

@@ -461,6 +461,35 @@ rf_status ridgefill_read_status(void* ws, void* stream) {
   if (e != hipSuccess) return hip_fail(e, "status read");
   if (word & rf::kStatusRowsBit) return fail(RF_E_ROWS, "device flagged filled-row indices");
   if (word & rf::kStatusNotSpdBit) return fail(RF_E_NOT_SPD, "device flagged a non-positive pivot");
+  if (word & rf::kStatusScoreBit) return fail(RF_E_INVALID, "device flagged a NaN selection score");
+  return ok();
+}
+
+size_t ridgefill_select_workspace_bytes(int64_t P) {
+  if (P < 0 || P > INT32_MAX) return 0;
+  return rf::select_layout(P).total;
+}
+
+rf_status ridgefill_select_rows(const float* scores, int64_t P, int64_t k, uint8_t* exact_mask,
+                                int32_t* filled_idx, void* ws, size_t ws_bytes, void* stream) {
+  if (P < 0 || P > INT32_MAX) return fail(RF_E_SHAPE, "P = %lld must be in [0, 2^31)", (long long)P);
+  if (k < 0 || k > P) return fail(RF_E_SHAPE, "k = %lld must be in [0, P = %lld]", (long long)k,
+                                  (long long)P);
+  if (!ws) return fail(RF_E_INVALID, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < rf::select_layout(P).total)
+    return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, rf::select_layout(P).total);
+  if (P == 0) {
+    hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "status clear");
+  }
+  if (!scores || (P > k && !filled_idx))
+    return fail(RF_E_INVALID, "scores and (unless k = P) filled_idx are required");
+  if (!aligned(scores, 4) || !aligned(filled_idx, 4))
+    return fail(RF_E_SHAPE, "scores and filled_idx need 4-byte alignment");
+  hipError_t e = rf::launch_select(scores, P, k, exact_mask, filled_idx, ws,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selection launch");
   return ok();
 }
 
