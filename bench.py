@@ -132,6 +132,140 @@ def cpu_baseline_fill(cfg, inp, budget_s: float = 15.0):
                       f"workload (NumPy float64), {spent:.1f} s"}
 
 
+def _time_ms(fn, reps: int, warmup: int = 1) -> float:
+    """Average milliseconds of fn() over reps calls, from events on the current stream (the
+    library enqueues everything on it; streamed copies join it through events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, ws_layers=None, reps=3,
+                 keep=False):
+    """One fill workload with its map/projection options; returns its timing line (and the
+    inputs when keep)."""
+    import torch
+    from ridge_map_kv_amd import binding as B
+    from ridge_map_kv_amd import synth
+
+    inp = synth.device_fill_inputs(cfg, dev)
+    filled = B.ridgefill_partition(cfg.N, cfg.T, inp["exact_mask"])
+    idx = torch.from_numpy(filled).to(dev)
+    nf = len(filled)
+    shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta,
+                         d_in=cfg.d_in)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 77)
+    for lay in inp["layers"]:
+        if int8:
+            q = torch.empty(lay["A"].shape, dtype=torch.int8, device=dev)
+            sc = torch.empty(cfg.d, dtype=torch.float32, device=dev)
+            B.ridgefill_quantize_map(lay["A"].float(), q, sc)
+            lay["A_q"], lay["A_scale"] = q, sc
+            del lay["A"]
+        if knorm:
+            lay["k_norm_w"] = (1 + 0.1 * torch.randn(cfg.head_dim, generator=g, device=dev)).to(
+                torch.bfloat16)
+    layers = inp["layers"]
+    copy = None
+    if streamed:
+        copy = torch.cuda.Stream()
+        host = []
+        for lay in layers:
+            h = dict(lay)
+            key = "A_q" if int8 else "A"
+            pinned = torch.empty(lay[key].shape, dtype=lay[key].dtype, pin_memory=True)
+            pinned.copy_(lay[key].cpu())
+            h[key] = pinned
+            del lay[key]
+            host.append(h)
+        layers = host
+        torch.cuda.empty_cache()
+    flags = (B.RF_MAPS_INT8 if int8 else 0) | (B.RF_MAPS_STREAMED if streamed else 0)
+    wsb = B.ridgefill_fill_workspace_bytes(shape, nf, ws_layers or cfg.n_upper, flags)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        B.ridgefill_fill(shape, inp["xS"], cfg.N, cfg.T, idx, nf, layers, inp["table"],
+                         cfg.page_size, inp["num_pages"], ws, copy_stream=copy)
+
+    ms = _time_ms(step, reps)
+    if B.ridgefill_read_status(ws) != B.RF_OK:
+        raise SystemExit(f"variant fill reported device status for {cfg.name}")
+    flops = cfg.fill_flops()
+    line = {"workload": cfg.name, "d": cfg.d, "d_in": cfg.width, "upper_layers": cfg.n_upper,
+            "N": cfg.N, "T": cfg.T, "filled_rows": nf,
+            "maps": ("int8" if int8 else "bf16") + (" streamed from pinned host memory" if streamed
+                                                     else " resident"),
+            "key_norm": knorm, "ms_per_step": ms, "filled_rows_per_s": nf / (ms * 1e-3),
+            "tflop_per_step": flops / 1e12,
+            "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+            "workspace_gib": wsb / 2**30}
+    if keep:
+        return line, (inp, shape)
+    del inp, layers, ws
+    torch.cuda.empty_cache()
+    return line
+
+
+def run_variants(dev):
+    """The fill's variants at full size: the 27B-shaped workload with bf16, int8 and int8
+    host-streamed maps; the Qwen3-8B-shaped workload with and without the per-head key
+    norm; a split state twice as wide as the layers; value-rescale factors over c = 512
+    tail rows of every 27B upper layer; selection of the exact rows of the 8B prefix."""
+    import torch
+    from ridge_map_kv_amd import binding as B
+    from ridge_map_kv_amd import configs
+
+    res = {}
+    log("bench: variants: 27B-shaped fill (bf16 resident, int8 resident, int8 streamed)")
+    line, (inp, shape) = fill_variant(configs.QWEN27B, dev, keep=True)
+    res["27b_bf16_resident"] = line
+    # value-rescale factors on the same layers: c = 512 tail rows, exact inputs drawn as
+    # the near-identity model's noisy layer inputs would be (random here: timing only)
+    cfg = configs.QWEN27B
+    c = 512
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    xt = torch.randn((c, cfg.d), generator=g, device=dev).to(torch.bfloat16)
+    xl = [torch.randn((c, cfg.d), generator=g, device=dev).to(torch.bfloat16)
+          for _ in range(cfg.n_upper)]
+    out = torch.empty((cfg.n_upper, cfg.n_kv), device=dev)
+    vws = torch.empty(B.ridgefill_value_scale_workspace_bytes(shape, c, cfg.n_upper),
+                      dtype=torch.uint8, device=dev)
+    vms = _time_ms(lambda: B.ridgefill_value_scale(shape, xt, xl, inp["layers"], out, vws), 3)
+    vflop = 2.0 * c * cfg.n_upper * (cfg.d * cfg.d + 2 * cfg.kv * cfg.d)
+    res["27b_value_scale"] = {"c": c, "upper_layers": cfg.n_upper, "ms": vms,
+                              "tflop": vflop / 1e12,
+                              "pct_bf16_mfma_peak": 100.0 * vflop / (vms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+    del inp, xl, vws
+    torch.cuda.empty_cache()
+    res["27b_int8_resident"] = fill_variant(configs.QWEN27B, dev, int8=True)
+    res["27b_int8_streamed_4_layer_groups"] = fill_variant(configs.QWEN27B, dev, int8=True,
+                                                           streamed=True, ws_layers=4)
+    log("bench: variants: Qwen3-8B-shaped fill with and without key norm; wide split state")
+    res["qwen3_8b"] = fill_variant(configs.QWEN3_8B, dev)
+    res["qwen3_8b_key_norm"] = fill_variant(configs.QWEN3_8B, dev, knorm=True)
+    res["8b_wide_split"] = fill_variant(configs.WIDE8B, dev)
+    log("bench: variants: exact-row selection")
+    P, k = configs.LLAMA8B.prefix, configs.LLAMA8B.exact_count
+    sc = torch.empty(P, device=dev).exponential_(generator=g)
+    filled = torch.empty(P - k, dtype=torch.int32, device=dev)
+    sws = torch.empty(B.ridgefill_select_workspace_bytes(P), dtype=torch.uint8, device=dev)
+    sms = _time_ms(lambda: B.ridgefill_select_rows(sc, k, filled, sws), 10)
+    res["select_8b_prefix"] = {"P": P, "k": k, "ms": sms}
+    return res
+
+
 def run_calibration(ccfg, dev, passes: int = 2):
     """Times ridgefill_calibrate over all chunks (after one untimed pass), then one solve
     per lambda; returns the timing dict and the lambda = 0.03 maps for the fill."""
@@ -238,6 +372,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip calibration/solve and fill with synthetic near-identity maps")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the 27B / key-norm / wide-split / value-scale / selection lines")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run a plain 1 GiB device copy, to scale HBM byte counters")
     args = ap.parse_args()
@@ -342,6 +478,10 @@ def main():
         out["cpu_baseline"] = cpu_baseline_fill(cfg, inp)
         if calib is not None:
             out["calibration"]["cpu_baseline"] = cpu_baseline_calib(configs.CALIB8B)
+    if not args.no_variants:
+        del inp
+        torch.cuda.empty_cache()
+        out["variants"] = run_variants(dev)
     print(json.dumps(out), flush=True)
     if args.traffic_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB

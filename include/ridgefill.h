@@ -9,9 +9,10 @@
  * ---------------------------------------
  *  - Pointers marked "device" point to GPU memory the caller allocated; pointers
  *    marked "host" point to CPU memory.  The library allocates no device memory,
- *    keeps no device state between calls and creates no streams.  Every buffer it
- *    needs beyond inputs and outputs is a caller-owned workspace whose size a
- *    *_workspace_bytes / *_state_bytes query returns.
+ *    keeps no device state between calls and creates no streams (the streamed fill
+ *    creates two pairs of HIP events per host thread on first use and reuses them).
+ *    Every buffer it needs beyond inputs and outputs is a caller-owned workspace whose
+ *    size a *_workspace_bytes / *_state_bytes query returns.
  *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round-to-nearest-
  *    even where the library produces them).  All matrices are row-major.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is enqueued
@@ -57,8 +58,8 @@ typedef struct rf_shape {
                            epsilon of the per-head key norm when one is given        */
   double rope_theta;    /* RoPE base, > 1                                            */
   int32_t d_in;         /* width of x_S, the map's input (section "Ridge map ...", map
-                           size paragraph: a gated-residual model reads a 10,240-wide
-                           state into 2,560-wide layers).  0 means d.  Multiple of 64. */
+                           size paragraph: a map's input width may differ from its
+                           output width).  0 means d.  Multiple of 64.                */
   int32_t reserved;     /* must be 0                                                  */
 } rf_shape;
 
@@ -140,8 +141,8 @@ rf_status ridgefill_select_rows(const float* scores, int64_t P, int64_t k, uint8
  *     v     = W_V,l h,  times v_scale_l[head] if given
  * and k, v are written to row t of layer l's paged cache (page block_table[t /
  * page_size], slot t % page_size).  Nothing else in the caches is touched; with
- * n_filled = 0 or n_layers = 0 only the status word is cleared (if ws is given).  Layers are independent; a caller that streams
- * maps may call once per layer.
+ * n_filled = 0 or n_layers = 0 only the status word is cleared (if ws is given).  Layers
+ * are independent, so a caller may also split them over several calls.
  *
  *   x_S         device bf16 [N][x_stride]: split-layer states of all prompt rows
  *               (x_stride >= d_in); the prefix rows must span at most 4 GiB
@@ -191,6 +192,18 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
                                   int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
                                   const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
                                   void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/* ------------------------------------------------------------------------------
+ * int8 maps.  Section "Ridge map ...", map size paragraph: maps held in int8 (1.2 GiB
+ * for 48 upper layers at hidden size 5120).  Symmetric, one scale per output row:
+ *     A_scale[o] = max_i |A[o][i]| / 127,  A_q[o][i] = round-half-even(A[o][i] / A_scale[o])
+ * clipped to [-127, 127]; a zero row gets scale 0 and zero codes.  All decisions in fp32
+ * with correctly rounded division.  The fill then uses A_q * A_scale as the map.
+ *   A        device fp32 [rows][cols] (e.g. one layer of ridgefill_solve's A_out)
+ *   A_q      device int8 [rows][cols] out;  A_scale  device fp32 [rows] out
+ * ------------------------------------------------------------------------------ */
+rf_status ridgefill_quantize_map(const float* A, int64_t rows, int64_t cols, int8_t* A_q,
+                                 float* A_scale, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Value-rescale factors.  Section "Hybrid layers and two corrections", value rescale:

@@ -19,8 +19,8 @@ by its section:
   [own]    same section, "own normalization and projections" and Fig. 2
   [arms]   "Tables from the paper", Table 3 (exact / no fill / identity / RidgeFill)
   [notation] "Tables from the paper", Table 2
-  [size]   same section as [map], the paragraph on map size (int8 maps, rectangular maps
-           of input width 10,240 and output width 2,560, resident or streamed maps)
+  [size]   same section as [map], the paragraph on map size (int8 maps, maps whose input
+           width differs from their output width, resident or streamed maps)
   [rescale] "Hybrid layers and two corrections", the value-rescale paragraph
   [qknorm] same paragraph (Qwen models normalise keys) and "Experiments", the error
            attribution paragraph on key normalization

@@ -26,6 +26,7 @@ EXPORTED = [
     "ridgefill_fill_streamed",
     "ridgefill_value_scale_workspace_bytes",
     "ridgefill_value_scale",
+    "ridgefill_quantize_map",
     "ridgefill_select_workspace_bytes",
     "ridgefill_select_rows",
     "ridgefill_calib_state_bytes",
@@ -96,6 +97,7 @@ def lib() -> C.CDLL:
         "ridgefill_value_scale_workspace_bytes": (sz, [C.POINTER(rf_shape), i64, i32, i32]),
         "ridgefill_value_scale": (st, [C.POINTER(rf_shape), vp, i64, C.POINTER(vp), i64,
                                        C.POINTER(rf_layer), i32, vp, vp, sz, vp]),
+        "ridgefill_quantize_map": (st, [vp, i64, i64, vp, vp, vp]),
         "ridgefill_select_workspace_bytes": (sz, [i64]),
         "ridgefill_select_rows": (st, [vp, i64, i64, vp, vp, vp, sz, vp]),
         "ridgefill_calib_state_bytes": (sz, [i32, i32]),
@@ -157,6 +159,14 @@ def ridgefill_partition(N: int, T: int, exact_mask: np.ndarray | None) -> np.nda
         m = exact_mask.ctypes.data
     _check(lib().ridgefill_partition(int(N), int(T), m, out.ctypes.data, C.byref(n)))
     return out[: n.value].copy()
+
+
+# ------------------------------------------------------------------------------ int8 maps
+
+def ridgefill_quantize_map(A, A_q, A_scale, stream=None) -> None:
+    """fp32 [rows][cols] map -> int8 codes A_q (same shape) and fp32 row scales A_scale."""
+    _check(lib().ridgefill_quantize_map(_ptr(A), int(A.shape[0]), int(A.shape[1]), _ptr(A_q),
+                                        _ptr(A_scale), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------ selection

@@ -33,6 +33,11 @@ class FillConfig:
     calib_rows: int       # rows of synthetic calibration data a map fit may use
     rope_theta: float = 500000.0
     rms_eps: float = 1e-5
+    d_in: int = 0         # width of x_S (0: d)
+
+    @property
+    def width(self) -> int:
+        return self.d_in or self.d
 
     @property
     def n_upper(self) -> int:
@@ -53,7 +58,7 @@ class FillConfig:
     def fill_flops(self) -> float:
         """Algorithmic multiply-add work of the fill: per filled row and upper layer,
         the d x d map plus the two kv x d projections, 2 flops per multiply-add."""
-        per = 2.0 * (self.d * self.d + 2 * self.kv * self.d)
+        per = 2.0 * (self.d * self.width + 2 * self.kv * self.d)
         return per * self.n_filled * self.n_upper
 
 
@@ -90,6 +95,12 @@ QWEN3_8B = FillConfig("qwen3-8b", d=4096, L=36, S=13, n_kv=8, head_dim=128,
 QWEN27B = FillConfig("27b-long", d=5120, L=64, S=16, n_kv=8, head_dim=128,
                      N=65536, T=4096, exact="blocks", exact_count=3072, lam=0.03,
                      page_size=16, seed=1004, calib_rows=8192)
+
+# Generic rectangular-map workload: the 8B prompt and layers with a split-layer state twice
+# as wide as the layers (d_in = 2 d).
+WIDE8B = FillConfig("8b-shape-wide-split", d=4096, L=32, S=12, n_kv=8, head_dim=128,
+                    N=32768, T=4096, exact="count", exact_count=2867, lam=0.03,
+                    page_size=16, seed=1006, calib_rows=8192, d_in=8192)
 
 CALIB8B = CalibConfig("calib-8b", d=4096, n_layers=20, rows=131072, chunk=16384)
 

@@ -114,5 +114,7 @@ struct SelLayout {
 SelLayout select_layout(int64_t P);
 hipError_t launch_select(const float* scores, int64_t P, int64_t k, uint8_t* exact,
                          int32_t* filled, void* ws, hipStream_t stream);
+hipError_t launch_quantize(const float* A, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                           hipStream_t stream);
 
 }  // namespace rf

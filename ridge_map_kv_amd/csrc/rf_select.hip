@@ -203,3 +203,44 @@ hipError_t launch_select(const float* scores, int64_t P, int64_t k, uint8_t* exa
 }
 
 }  // namespace rf
+
+// ------------------------------------------------------------------------------
+// int8 map quantization.  Section "Ridge map ...", map size paragraph (maps held in int8):
+// symmetric, one scale per output row, scale = max |A[o, :]| / 127 and
+// q = round-half-even(A / scale) clipped to [-127, 127] (a zero row: scale 0, q = 0).  All
+// rounding decisions in fp32 with correctly rounded division.
+namespace rf {
+namespace {
+
+__global__ void quantize_rows_kernel(const float* A, int64_t cols, int8_t* q, float* scale) {
+  const int64_t row = blockIdx.x;
+  const float* a = A + row * cols;
+  __shared__ float red[256];
+  float m = 0.f;
+  for (int64_t c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(a[c]));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float s = red[0] / 127.0f;
+  if (threadIdx.x == 0) scale[row] = s;
+  int8_t* out = q + row * cols;
+  for (int64_t c = threadIdx.x; c < cols; c += 256) {
+    float v = 0.f;
+    if (s > 0.f) v = fminf(fmaxf(rintf(a[c] / s), -127.f), 127.f);
+    out[c] = (int8_t)(int)v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* A, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)rows), dim3(256), 0, stream, A, cols, q,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace rf

@@ -465,6 +465,17 @@ rf_status ridgefill_read_status(void* ws, void* stream) {
   return ok();
 }
 
+rf_status ridgefill_quantize_map(const float* A, int64_t rows, int64_t cols, int8_t* A_q,
+                                 float* A_scale, void* stream) {
+  if (rows < 1 || rows > INT32_MAX || cols < 1)
+    return fail(RF_E_SHAPE, "rows = %lld, cols = %lld", (long long)rows, (long long)cols);
+  if (!A || !A_q || !A_scale) return fail(RF_E_INVALID, "null pointer among A, A_q, A_scale");
+  if (!aligned(A, 4) || !aligned(A_scale, 4)) return fail(RF_E_SHAPE, "A and A_scale need 4-byte alignment");
+  hipError_t e = rf::launch_quantize(A, rows, cols, A_q, A_scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return ok();
+}
+
 size_t ridgefill_select_workspace_bytes(int64_t P) {
   if (P < 0 || P > INT32_MAX) return 0;
   return rf::select_layout(P).total;

@@ -18,7 +18,7 @@ Recipes (the shapes and value distributions of the workloads):
     seeded contiguous blocks with lengths U[16, 80] covering half of the budget plus
     uniformly drawn singletons for the other half ("blocks").
   * Block tables: a seeded permutation of the physical pages.
-  * Rectangular maps (a gated-residual model reads a d_in-wide state into d-wide layers):
+  * Rectangular maps (input width d_in != output width d):
     A = [I | 0] + U V^T / 2 with U ~ N(0, 1/d) [d, 64], V ~ N(0, 1/d_in) [d_in, 64]
     (the identity block on the first d inputs), b ~ N(0, 1).
   * Key-norm weights 1 + 0.1 N(0, 1) [head_dim]; value-rescale factors U[0.5, 1.5].
@@ -177,8 +177,9 @@ def sparse_dyadic_matrix(d_out: int, d_in: int, seed: int, per_row: int = 2) -> 
 # Large workloads are drawn on the device with torch's seeded generator (same recipes).
 
 def device_fill_inputs(cfg, dev, maps=None, sentinel: bool = False):
-    """Seeded fill inputs on `dev` for a FillConfig: x_S bf16 [N, d]; per upper layer A
-    (bf16, near-identity unless `maps` gives (A bf16, b fp32) pairs), b fp32, norm_w, W_K,
+    """Seeded fill inputs on `dev` for a FillConfig: x_S bf16 [N, d_in]; per upper layer A
+    (bf16 [d, d_in], near-identity, [I | 0] plus the low-rank term when d_in > d, unless
+    `maps` gives (A bf16, b fp32) pairs), b fp32, norm_w, W_K,
     W_V (bf16) and K/V page pools (zeros, or 0xFFFF everywhere when `sentinel`); the block
     table; the exact-row mask."""
     import torch
@@ -186,7 +187,8 @@ def device_fill_inputs(cfg, dev, maps=None, sentinel: bool = False):
     g = torch.Generator(device=dev)
     g.manual_seed(cfg.seed)
     d, kv = cfg.d, cfg.kv
-    xS = torch.randn((cfg.N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    width = getattr(cfg, "width", d)
+    xS = torch.randn((cfg.N, width), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     table_np, num_pages = block_table(cfg.N, cfg.page_size, cfg.seed)
     s = 1.0 / np.sqrt(d)
     layers = []
@@ -195,8 +197,8 @@ def device_fill_inputs(cfg, dev, maps=None, sentinel: bool = False):
             A, b = maps[l]
         else:
             U = torch.randn((d, TRUE_MAP_RANK), generator=g, device=dev) * s
-            V = torch.randn((d, TRUE_MAP_RANK), generator=g, device=dev) * s
-            A = (torch.eye(d, device=dev) + TRUE_MAP_GAIN * (U @ V.T)).to(torch.bfloat16)
+            V = torch.randn((width, TRUE_MAP_RANK), generator=g, device=dev) / np.sqrt(width)
+            A = (torch.eye(d, width, device=dev) + TRUE_MAP_GAIN * (U @ V.T)).to(torch.bfloat16)
             b = torch.randn(d, generator=g, device=dev)
             del U, V
         w = (1.0 + 0.1 * torch.randn(d, generator=g, device=dev)).to(torch.bfloat16)

@@ -55,7 +55,7 @@ VARIANTS = [
     (768, 2, 4, 64, 333, 33, 17, 8, 32, dict(knorm=True)),
     (512, 2, 2, 128, 700, 100, 60, 16, 33, dict(vscale=True)),
     (768, 2, 4, 64, 333, 33, 17, 8, 34, dict(vscale=True, knorm=True)),
-    (256, 2, 2, 64, 600, 80, 40, 16, 35, dict(d_in=1024)),            # 4 streams -> 1
+    (256, 2, 2, 64, 600, 80, 40, 16, 35, dict(d_in=1024)),
     (512, 2, 8, 128, 300, 0, 0, 16, 36, dict(d_in=320)),              # d_in not a tile multiple
     (512, 3, 2, 128, 700, 100, 60, 16, 37, dict(int8=True)),
     (256, 2, 2, 128, 520, 8, 5, 16, 38, dict(int8=True, d_in=1024, knorm=True, vscale=True)),
@@ -226,3 +226,19 @@ def test_variant_argument_errors():
         B.ridgefill_fill(bad, inp["xS"], case.N, case.T, idx, f.size, inp["layers"], inp["table"],
                          16, inp["num_pages"], ws)
     assert e.value.status == B.RF_E_SHAPE
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(256, 4096, 61), (37, 1000, 62), (5120, 5120, 63)])
+def test_quantize_map_bit_exact(rows, cols, seed):
+    # integer codes decided in fp32 on both sides: bit-exact codes and scales
+    g = np.random.default_rng(seed)
+    A = (g.standard_normal((rows, cols)) * np.exp(0.5 * g.standard_normal((rows, 1)))).astype(np.float32)
+    A[rows // 2] = 0.0
+    A[0, :8] = [0.5, -0.5, 1.5, -2.5, 127.0, 0.0, -0.0, 3.0]     # half-way cases for row 0
+    q, sc = oracle.quantize_map_int8(A, np.float32)
+    At = torch.from_numpy(A).cuda()
+    qg = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    sg = torch.empty(rows, dtype=torch.float32, device="cuda")
+    B.ridgefill_quantize_map(At, qg, sg)
+    assert np.array_equal(qg.cpu().numpy(), q)
+    assert np.array_equal(sg.cpu().numpy().view(np.uint32), sc.astype(np.float32).view(np.uint32))
