@@ -139,62 +139,76 @@ __device__ __forceinline__ void store44(double* dst, size_t ld, const double (&a
     }
 }
 
-// Factor diagonal block k in place (lower) and store its inverse in linv[k].  256 threads:
-// in the right-looking factorisation, thread t owns row t / 4 and the 16 columns
-// 16 (t % 4) .. + 15 of the trailing update; the inverse X = L^-1 is formed the same way
-// (row j of X scaled by 1 / L_jj, then subtracted from the rows below with weight L_ij).
+// Factor diagonal block k in place (lower) and store its inverse in linv[k].  256 threads;
+// thread t owns row t / 4 and the 16 columns 16 (t % 4) .. + 15.
+//
+// Column j is eliminated with its pivot d_j left unscaled: every row below subtracts
+// (a_ij / d_j) times column j from its columns j+1 .. i, which leaves a_ij = L_ij sqrt(d_j).
+// The inverse is built in the same sweep on Y = diag(L) L^-1: row i of Y (i > j) subtracts
+// (a_ij / d_j) times row j of Y, since L_ij / L_jj = a_ij / d_j.  Both updates read only
+// column j and row j, which the previous step finished, so one barrier per column suffices.
+// At the end L_ij = a_ij / sqrt(d_j), L_jj = sqrt(d_j) and (L^-1)_i = Y_i / sqrt(d_i).
+// A non-positive or non-finite pivot sets the NOT_SPD bit and is taken as 1.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k, double* linv,
                                                         unsigned* status) {
   __shared__ double a[NB * LDT];
-  __shared__ double x[NB * LDT];
+  __shared__ double y[NB * LDT];
+  __shared__ double rs[NB];
   double* blk = C + (size_t)k * NB * d + (size_t)k * NB;
   const int t = threadIdx.x;
   const int row = t >> 2, c0 = (t & 3) * 16;
   for (int e = t; e < NB * NB; e += 256) {
     const int r = e >> 6, c = e & 63;
     a[r * LDT + c] = blk[(size_t)r * d + c];
-    x[r * LDT + c] = r == c ? 1.0 : 0.0;
+    y[r * LDT + c] = r == c ? 1.0 : 0.0;
   }
   __syncthreads();
   for (int j = 0; j < NB; ++j) {
-    if (t == 0) {
-      double p = a[j * LDT + j];
-      if (!(p > 0.0) || !isfinite(p)) {
-        atomicOr(status, kStatusNotSpdBit);
-        p = 1.0;
-      }
-      a[j * LDT + j] = sqrt(p);
-    }
-    __syncthreads();
-    const double piv = a[j * LDT + j];
-    if (t > j && t < NB) a[t * LDT + j] /= piv;
-    __syncthreads();
+    double p = a[j * LDT + j];
+    const bool bad = !(p > 0.0) || !isfinite(p);
+    if (bad) p = 1.0;
+    if (t == 0 && bad) atomicOr(status, kStatusNotSpdBit);
     if (row > j) {
-      const double lij = a[row * LDT + j];
+      // all operands first (one LDS round trip), then the update, then the stores; the
+      // pivot column itself (c = j) is never stored in this step
+      double ar[16], ac[16], yr[16], yj[16];
+      const double aij = a[row * LDT + j];
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        ar[cc] = a[row * LDT + c0 + cc];
+        ac[cc] = a[(c0 + cc) * LDT + j];
+        yr[cc] = y[row * LDT + c0 + cc];
+        yj[cc] = y[j * LDT + c0 + cc];
+      }
+      const double m = aij / p;
 #pragma unroll
       for (int cc = 0; cc < 16; ++cc) {
         const int c = c0 + cc;
-        if (c > j && c <= row) a[row * LDT + c] -= lij * a[c * LDT + j];
+        if (c > j && c <= row) ar[cc] -= m * ac[cc];
+        yr[cc] -= m * yj[cc];
+      }
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        if (c0 + cc > j) a[row * LDT + c0 + cc] = ar[cc];
+        y[row * LDT + c0 + cc] = yr[cc];
       }
     }
     __syncthreads();
   }
-  for (int j = 0; j < NB; ++j) {
-    const double inv = 1.0 / a[j * LDT + j];
-    if (t < NB) x[j * LDT + t] *= inv;
-    __syncthreads();
-    if (row > j) {
-      const double lij = a[row * LDT + j];
-#pragma unroll
-      for (int cc = 0; cc < 16; ++cc) x[row * LDT + c0 + cc] -= lij * x[j * LDT + c0 + cc];
-    }
-    __syncthreads();
+  if (t < NB) {
+    double p = a[t * LDT + t];
+    if (!(p > 0.0) || !isfinite(p)) p = 1.0;
+    rs[t] = 1.0 / sqrt(p);
   }
+  __syncthreads();
   double* li = linv + (size_t)k * NB * NB;
   for (int e = t; e < NB * NB; e += 256) {
     const int r = e >> 6, c = e & 63;
-    blk[(size_t)r * d + c] = c <= r ? a[r * LDT + c] : 0.0;
-    li[e] = c <= r ? x[r * LDT + c] : 0.0;
+    double lv = 0.0;
+    if (c < r) lv = a[r * LDT + c] * rs[c];
+    else if (c == r) lv = 1.0 / rs[r];
+    blk[(size_t)r * d + c] = lv;
+    li[e] = c <= r ? y[r * LDT + c] * rs[r] : 0.0;
   }
 }
 
