@@ -98,8 +98,10 @@ hipError_t launch_calibrate(void* state, int d, int n_layers, const uint16_t* xS
                             const uint16_t* const* xl, int64_t n_rows, hipStream_t stream);
 
 // Solve ---------------------------------------------------------------------------
+constexpr int kSolveGroup = 4;   // layers per split-map GEMM launch of the solve
 struct SolveLayout {
-  size_t scalars, mu, C, W, M64, M32, linv, v, total;
+  size_t scalars, mu, C, W, M64, Mx, Cx, linv, v, total;
+  int group;
 };
 SolveLayout solve_layout(int d, int n_layers);
 hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, float* A_out,

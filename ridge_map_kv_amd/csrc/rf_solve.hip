@@ -11,12 +11,19 @@
 //   Cholesky blocked, 64-wide panels: diagonal block factor + its inverse, panel
 //            L_ik = A_ik L_kk^-T, trailing update A_ij -= L_ik L_jk^T    fp64
 //   inverse  W = L^-1 by blocked forward substitution on the identity;
-//            M = (C + alpha I)^-1 = W^T W                               fp64 (+ fp32 copy)
-//   maps     A_l = YX_l M - n mu_l v^T with v = M mu_S, one fp32 matrix-core GEMM over all
-//            layers (M symmetric, so both operands are read along rows)
+//            M = (C + alpha I)^-1 = W^T W                               fp64
+//   maps     A_l = C_l M with C_l = YX_l - n mu_l mu_S^T centred in fp64.  Each fp64
+//            operand x is split into bf16 parts x_hi = bf16(x), x_lo = bf16(x - x_hi),
+//            which hold it to about 2^-17; then
+//              A_l ~ C_hi M_hi + C_hi M_lo + C_lo M_hi
+//            is one bf16 matrix-core GEMM with the reduction axis tripled:
+//            [C_hi | C_hi | C_lo] (d x 3d) times [M_hi | M_lo | M_hi]^T (M symmetric),
+//            fp32 accumulation, on the fill's 256 x 256 tile pipeline.  Layers go in
+//            groups sized by the workspace.
 //   offsets  b_l = mu_l - A_l mu_S = mu_l - YX_l v + n mu_l (v . mu_S)      fp64 accumulate
 // Every launch is on the caller's stream; nothing is synchronised.
 #include "rf_common.h"
+#include "rf_gemm_tile.h"
 #include "rf_internal.h"
 #include "rf_profile.h"
 #include "ridgefill.h"
@@ -38,8 +45,10 @@ SolveLayout solve_layout(int d, int n_layers) {
   L.C = L.linv + align256((size_t)(d / NB) * NB * NB * 8);
   L.W = L.C + align256(dd * 8);
   L.M64 = L.W + align256(dd * 8);
-  L.M32 = L.M64 + align256(dd * 8);
-  L.total = L.M32 + align256(dd * 4);
+  L.Mx = L.M64 + align256(dd * 8);
+  L.group = n_layers < kSolveGroup ? n_layers : kSolveGroup;
+  L.Cx = L.Mx + align256(dd * 6);
+  L.total = L.Cx + align256((size_t)L.group * dd * 6);
   return L;
 }
 
@@ -288,7 +297,15 @@ __global__ __launch_bounds__(256) void fsub_update_kernel(double* W, const doubl
 }
 
 // M = W^T W for lower tiles (ab >= bb), mirrored: M[a][b] = sum_k W[k][a] W[k][b], k >= ab.
-__global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double* M64, float* M32) {
+// bf16 parts of an fp64 value: hi = bf16(x), lo = bf16(x - hi); |x - hi - lo| <= ~2^-17 |x|.
+__device__ __forceinline__ void split_bf16(double x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16((float)x);
+  lo = f32_to_bf16((float)(x - (double)bf16_to_f32(hi)));
+}
+
+// M = W^T W for one lower tile pair, written to both triangles in fp64 and as the GEMM
+// operand Mx [d][3d] = [M_hi | M_lo | M_hi] (bf16).
+__global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double* M64, uint16_t* Mx) {
   __shared__ double wa[NB * LDT];
   __shared__ double wb[NB * LDT];
   const int e = blockIdx.x;
@@ -314,8 +331,15 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double
       const size_t a = (size_t)ab * NB + r0 + i, b = (size_t)bb * NB + c0 + j;
       M64[a * d + b] = acc[i][j];
       M64[b * d + a] = acc[i][j];
-      M32[a * d + b] = (float)acc[i][j];
-      M32[b * d + a] = (float)acc[i][j];
+      uint16_t hi, lo;
+      split_bf16(acc[i][j], hi, lo);
+      const size_t d3 = (size_t)3 * d;
+      Mx[a * d3 + b] = hi;
+      Mx[a * d3 + d + b] = lo;
+      Mx[a * d3 + 2 * d + b] = hi;
+      Mx[b * d3 + a] = hi;
+      Mx[b * d3 + d + a] = lo;
+      Mx[b * d3 + 2 * d + a] = hi;
     }
 }
 
@@ -364,116 +388,95 @@ __global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double
   }
 }
 
-// ---------------------------------------------------------------- fp32 MFMA map GEMM
-// out[l][o][i] = sum_k YX_l[o][k] M[i][k] - n mu_l[o] v[i];  128x128 tiles, 4 waves (2x2),
-// v_mfma_f32_32x32x2f32.  LDS rows are 32 floats (128 bytes) of one reduction slice.
-constexpr int SB = 128;          // tile edge
-constexpr int SBK = 32;          // floats per reduction slice
-constexpr int kSStage = SB * SBK * 4;   // 16 KB per operand
+// ---------------------------------------------------------------- split bf16 map GEMM
+// Cx[g][o] = [C_hi | C_hi | C_lo] of row o of C_l = YX_l - n mu_l mu_S^T (l = l0 + g), the
+// centring in fp64.  Four consecutive k per thread.
+__global__ void split_c_kernel(const float* YX, const double* mu, const unsigned char* scalars,
+                               int d, int l0, int G, uint16_t* Cx) {
+  const double n = *reinterpret_cast<const double*>(scalars + kNOff);
+  const size_t quads = (size_t)G * d * d / 4;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads;
+       q += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = q * 4;
+    const int g = (int)(e / ((size_t)d * d));
+    const size_t r = e - (size_t)g * d * d;
+    const int o = (int)(r / d), k = (int)(r - (size_t)o * d);
+    const int l = l0 + g;
+    const f32x4 y = *reinterpret_cast<const f32x4*>(YX + ((size_t)l * d + o) * d + k);
+    const double nm = n * mu[(size_t)(1 + l) * d + o];
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split_bf16((double)y[j] - nm * mu[k + j], hi[j], lo[j]);
+    uint16_t* row = Cx + ((size_t)g * d + o) * (3 * (size_t)d);
+    u32x2 h2, l2;
+    h2.x = hi[0] | (uint32_t)hi[1] << 16;
+    h2.y = hi[2] | (uint32_t)hi[3] << 16;
+    l2.x = lo[0] | (uint32_t)lo[1] << 16;
+    l2.y = lo[2] | (uint32_t)lo[3] << 16;
+    *reinterpret_cast<u32x2*>(row + k) = h2;
+    *reinterpret_cast<u32x2*>(row + d + k) = h2;
+    *reinterpret_cast<u32x2*>(row + 2 * d + k) = l2;
+  }
+}
 
-struct MapArgs {
-  const float* YX;
-  const float* M32;
-  const double* mu;
-  const double* v;
-  const unsigned char* scalars;
-  float* A_out;
-  uint16_t* A_bf16;
-  int d, n_layers, nt;
+struct SolveGemmArgs {
+  const uint16_t* Cx;       // [G][d][3d]
+  const uint16_t* Mx;       // [d][3d]
+  float* A_out;             // [n_layers][d][d] or null
+  uint16_t* A_bf16;         // [n_layers][d][d] or null
+  int d, l0, nt;
 };
 
-__global__ __launch_bounds__(256, 2) void solve_map_kernel(MapArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kSStage];
+// A_l[o][i] for one 256 x 256 tile: F = rows o of Cx, T = rows i of Mx, K = 3d.  In the
+// MFMA result each lane holds one i and runs of four o, so for each o a half-wave writes
+// 32 consecutive i.
+__global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per = a.nt * a.nt;
-  const int l = tile / per;
-  const int r = tile - l * per;
-  const int to = r / a.nt, ti = r - to * a.nt;          // output row tile (o), column tile (i)
-  const int o0 = to * SB, i0 = ti * SB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wf = wave >> 1, wt = wave & 1, rr = tid >> 3, c = tid & 7;
-  const float* F = a.M32 + (size_t)i0 * a.d;                         // rows i
-  const float* Tm = a.YX + ((size_t)l * a.d + o0) * a.d;             // rows o
-
-  f32x16 acc[2][2];
+  const int g = tile / per;
+  const int r = tile - g * per;
+  // groups of 4 o-tiles against all i-tiles (o-tiles share the Cx rows across i)
+  const int fg = r / (4 * a.nt), within = r - fg * 4 * a.nt;
+  const int left = a.nt - fg * 4, gsz = left < 4 ? left : 4;
+  const int it = within / gsz, ot = fg * 4 + (within - it * gsz);
+  const int o0 = ot * kTile, i0 = it * kTile;
+  const size_t d3 = (size_t)3 * a.d;
+  const int tid = threadIdx.x;
+  DmaOperand Fo, To;
+  {
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.f;
-
-  f32x4 vf[4], vt[4];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      vf[p] = *reinterpret_cast<const f32x4*>(F + (size_t)(rr + 32 * p) * a.d + k0 + c * 4);
-      vt[p] = *reinterpret_cast<const f32x4*>(Tm + (size_t)(rr + 32 * p) * a.d + k0 + c * 4);
+    for (int p = 0; p < 8; ++p) {
+      const int r0 = dma_block_row(p, wave), rr = r0 + dma_lane_row(lane);
+      const int ce = dma_chunk_elems(rr, lane);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(a.Cx + ((size_t)g * a.d + o0 + r0) * d3);
+      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * d3 + ce) * 2);
+      To.base[p] = reinterpret_cast<const unsigned char*>(a.Mx + (size_t)(i0 + r0) * d3);
+      To.off[p] = Fo.off[p];
     }
-  };
-  auto store = [&](unsigned char* buf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<f32x4*>(buf + lds_off128(rr + 32 * p, c)) = vf[p];
-      *reinterpret_cast<f32x4*>(buf + kSStage + lds_off128(rr + 32 * p, c)) = vt[p];
-    }
-  };
-  load(0);
-  store(smem);
-  __syncthreads();
-  const int nk = a.d / SBK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const unsigned char* cur = smem + (kt & 1) * 2 * kSStage;
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * SBK);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int ch = cc * 2 + (lane >> 5);
-      f32x4 fa[2], tb[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        fa[m] = *reinterpret_cast<const f32x4*>(cur + lds_off128(wf * 64 + m * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        tb[n] = *reinterpret_cast<const f32x4*>(cur + kSStage +
-                                                lds_off128(wt * 64 + n * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int n = 0; n < 2; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[m][s], tb[n][s], acc[m][n], 0, 0, 0);
-    }
-    if (more) store(smem + ((kt + 1) & 1) * 2 * kSStage);
-    __syncthreads();
   }
+  f32x16 acc[4][4];
+  gemm_pipeline(acc, Fo, To, 3 * a.d, smem);
 
-  const double n = *reinterpret_cast<const double*>(a.scalars + kNOff);
-  const int h = lane >> 5;
+  const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+  const int l = a.l0 + g;
 #pragma unroll
-  for (int nn = 0; nn < 2; ++nn) {
-    const int o = o0 + wt * 64 + nn * 32 + (lane & 31);
-    const double nm = n * a.mu[(size_t)(1 + l) * a.d + o];
-    const size_t rowoff = ((size_t)l * a.d + o) * a.d;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int n = 0; n < 4; ++n) {
+      const int i = i0 + wt * 128 + n * 32 + (lane & 31);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = i0 + wf * 64 + m * 32 + q * 8 + h * 4;
-        f32x4 out;
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          out[e] = (float)((double)acc[m][nn][q * 4 + e] - nm * a.v[i + e]);
-        if (a.A_out) *reinterpret_cast<f32x4*>(a.A_out + rowoff + i) = out;
-        if (a.A_bf16) {
-          u32x2 bb;
-          bb.x = pack_bf16x2(out[0], out[1]);
-          bb.y = pack_bf16x2(out[2], out[3]);
-          *reinterpret_cast<u32x2*>(a.A_bf16 + rowoff + i) = bb;
+        for (int e = 0; e < 4; ++e) {
+          const int o = o0 + wf * 128 + m * 32 + q * 8 + h * 4 + e;
+          const size_t idx = ((size_t)l * a.d + o) * a.d + i;
+          const float v = acc[m][n][q * 4 + e];
+          if (a.A_out) a.A_out[idx] = v;
+          if (a.A_bf16) a.A_bf16[idx] = f32_to_bf16(v);
         }
-      }
-  }
+    }
 }
 
 }  // namespace
@@ -491,7 +494,8 @@ hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, f
   double* C = reinterpret_cast<double*>(w + L.C);
   double* W = reinterpret_cast<double*>(w + L.W);
   double* M64 = reinterpret_cast<double*>(w + L.M64);
-  float* M32 = reinterpret_cast<float*>(w + L.M32);
+  uint16_t* Mx = reinterpret_cast<uint16_t*>(w + L.Mx);
+  uint16_t* Cx = reinterpret_cast<uint16_t*>(w + L.Cx);
   const float* G = reinterpret_cast<const float*>(st + CL.G);
   const float* YX = reinterpret_cast<const float*>(st + CL.YX);
   const size_t dd = (size_t)d * d;
@@ -520,15 +524,17 @@ hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, f
     if (below > 0)
       hipLaunchKernelGGL(fsub_update_kernel, dim3(below * (i + 1)), dim3(256), 0, stream, W, C, d, i);
   }
-  hipLaunchKernelGGL(wtw_kernel, dim3(nbk * (nbk + 1) / 2), dim3(256), 0, stream, W, d, M64, M32);
+  hipLaunchKernelGGL(wtw_kernel, dim3(nbk * (nbk + 1) / 2), dim3(256), 0, stream, W, d, M64, Mx);
   hipLaunchKernelGGL(mv_kernel, dim3((d + 3) / 4), dim3(256), 0, stream, M64, mu, d, v);
   hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, stream, v, mu, d, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  MapArgs a = {YX, M32, mu, v, w, A_out, A_bf16, d, n_layers, d / SB};
-  {
+  for (int l0 = 0; l0 < n_layers; l0 += L.group) {
+    const int G = (n_layers - l0) < L.group ? (n_layers - l0) : L.group;
+    hipLaunchKernelGGL(split_c_kernel, dim3(2048), dim3(256), 0, stream, YX, mu, w, d, l0, G, Cx);
+    SolveGemmArgs a = {Cx, Mx, A_out, A_bf16, d, l0, d / kTile};
     ProfileScope ps(RF_KERNEL_SOLVE_MAP, stream);
-    hipLaunchKernelGGL(solve_map_kernel, dim3(n_layers * a.nt * a.nt), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(solve_gemm_kernel, dim3(G * a.nt * a.nt), dim3(kThreads), 0, stream, a);
   }
   hipLaunchKernelGGL(bias_kernel, dim3((n_layers * d + 3) / 4), dim3(256), 0, stream, YX, mu, v,
                      w, d, n_layers, b_out);
