@@ -264,8 +264,10 @@ rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_
  * mu = sums / n,  C = sum x_S x_S^T - n mu_S mu_S^T,  C_l = sum x_l x_S^T - n mu_l mu_S^T,
  * alpha = lambda * tr(C) / d,
  *     A_l = C_l (C + alpha I)^-1,     b_l = mu_l - A_l mu_S.
- * (C + alpha I) is factored by a device Cholesky in fp64 and inverted in fp64; the
- * product with C_l is an fp32 matrix-core GEMM.
+ * (C + alpha I) is factored by a device Cholesky in fp64 and inverted in fp64.  The
+ * product C_l M (M = (C + alpha I)^-1) is a bf16 matrix-core GEMM on operands split into
+ * bf16 high and low parts (three products, fp32 accumulation), about 2^-17 relative per
+ * operand; b_l is accumulated in fp64.
  *
  *   A_out       device fp32 [n_layers][d][d] (may be NULL if A_bf16_out is given)
  *   b_out       device fp32 [n_layers][d]
