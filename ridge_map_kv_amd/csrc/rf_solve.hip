@@ -149,75 +149,80 @@ __device__ __forceinline__ void store44(double* dst, size_t ld, const double (&a
 }
 
 // Factor diagonal block k in place (lower) and store its inverse in linv[k].  256 threads;
-// thread t owns row t / 4 and the 16 columns 16 (t % 4) .. + 15.
+// thread t owns row t / 4 and the 16 columns 16 (t % 4) .. + 15, and keeps its segment of
+// the block and of Y in registers for the whole sweep.
 //
 // Column j is eliminated with its pivot d_j left unscaled: every row below subtracts
 // (a_ij / d_j) times column j from its columns j+1 .. i, which leaves a_ij = L_ij sqrt(d_j).
 // The inverse is built in the same sweep on Y = diag(L) L^-1: row i of Y (i > j) subtracts
-// (a_ij / d_j) times row j of Y, since L_ij / L_jj = a_ij / d_j.  Both updates read only
-// column j and row j, which the previous step finished, so one barrier per column suffices.
-// At the end L_ij = a_ij / sqrt(d_j), L_jj = sqrt(d_j) and (L^-1)_i = Y_i / sqrt(d_i).
-// A non-positive or non-finite pivot sets the NOT_SPD bit and is taken as 1.
+// (a_ij / d_j) times row j of Y, since L_ij / L_jj = a_ij / d_j.  Step j reads only column
+// j of the block and row j of Y, which are final after step j - 1; their owners publish
+// them to LDS (double-buffered) at the end of step j - 1, so one barrier per column
+// suffices and no other LDS traffic is needed.  At the end L_ij = a_ij / sqrt(d_j),
+// L_jj = sqrt(d_j) and (L^-1)_i = Y_i / sqrt(d_i).  A non-positive or non-finite pivot sets
+// the NOT_SPD bit and is taken as 1.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k, double* linv,
                                                         unsigned* status) {
-  __shared__ double a[NB * LDT];
-  __shared__ double y[NB * LDT];
-  __shared__ double rs[NB];
+  __shared__ double col[2][NB];       // column j of the block (double-buffered by j parity)
+  __shared__ double yrow[2][NB];      // row j of Y
+  __shared__ double piv[NB];          // pivots d_j (after the NOT_SPD replacement)
   double* blk = C + (size_t)k * NB * d + (size_t)k * NB;
   const int t = threadIdx.x;
   const int row = t >> 2, c0 = (t & 3) * 16;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    a[r * LDT + c] = blk[(size_t)r * d + c];
-    y[r * LDT + c] = r == c ? 1.0 : 0.0;
+  double ar[16], yr[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    ar[cc] = blk[(size_t)row * d + c0 + cc];
+    yr[cc] = row == c0 + cc ? 1.0 : 0.0;
+  }
+  // publish column 0 and row 0 of Y
+  if (c0 == 0) col[0][row] = ar[0];
+  if (row == 0) {
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) yrow[0][c0 + cc] = yr[cc];
   }
   __syncthreads();
   for (int j = 0; j < NB; ++j) {
-    double p = a[j * LDT + j];
+    const int b = j & 1;
+    double p = col[b][j];
     const bool bad = !(p > 0.0) || !isfinite(p);
     if (bad) p = 1.0;
-    if (t == 0 && bad) atomicOr(status, kStatusNotSpdBit);
+    if (t == 0) {
+      piv[j] = p;
+      if (bad) atomicOr(status, kStatusNotSpdBit);
+    }
     if (row > j) {
-      // all operands first (one LDS round trip), then the update, then the stores; the
-      // pivot column itself (c = j) is never stored in this step
-      double ar[16], ac[16], yr[16], yj[16];
-      const double aij = a[row * LDT + j];
-#pragma unroll
-      for (int cc = 0; cc < 16; ++cc) {
-        ar[cc] = a[row * LDT + c0 + cc];
-        ac[cc] = a[(c0 + cc) * LDT + j];
-        yr[cc] = y[row * LDT + c0 + cc];
-        yj[cc] = y[j * LDT + c0 + cc];
-      }
-      const double m = aij / p;
+      const double m = col[b][row] / p;
 #pragma unroll
       for (int cc = 0; cc < 16; ++cc) {
         const int c = c0 + cc;
-        if (c > j && c <= row) ar[cc] -= m * ac[cc];
-        yr[cc] -= m * yj[cc];
+        if (c > j && c <= row) ar[cc] -= m * col[b][c];
+        yr[cc] -= m * yrow[b][c];
       }
+    }
+    // column j + 1 and row j + 1 of Y are now final: publish them for the next step
+    if (j + 1 < NB) {
 #pragma unroll
-      for (int cc = 0; cc < 16; ++cc) {
-        if (c0 + cc > j) a[row * LDT + c0 + cc] = ar[cc];
-        y[row * LDT + c0 + cc] = yr[cc];
+      for (int cc = 0; cc < 16; ++cc)
+        if (c0 + cc == j + 1) col[b ^ 1][row] = ar[cc];
+      if (row == j + 1) {
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) yrow[b ^ 1][c0 + cc] = yr[cc];
       }
     }
     __syncthreads();
   }
-  if (t < NB) {
-    double p = a[t * LDT + t];
-    if (!(p > 0.0) || !isfinite(p)) p = 1.0;
-    rs[t] = 1.0 / sqrt(p);
-  }
-  __syncthreads();
+  // 1 / sqrt(d_j): own columns and own row
   double* li = linv + (size_t)k * NB * NB;
-  for (int e = t; e < NB * NB; e += 256) {
-    const int r = e >> 6, c = e & 63;
+  const double rrow = 1.0 / sqrt(piv[row]);
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const int c = c0 + cc;
     double lv = 0.0;
-    if (c < r) lv = a[r * LDT + c] * rs[c];
-    else if (c == r) lv = 1.0 / rs[r];
-    blk[(size_t)r * d + c] = lv;
-    li[e] = c <= r ? y[r * LDT + c] * rs[r] : 0.0;
+    if (c < row) lv = ar[cc] / sqrt(piv[c]);
+    else if (c == row) lv = sqrt(piv[row]);
+    blk[(size_t)row * d + c] = lv;
+    li[row * NB + c] = c <= row ? yr[cc] * rrow : 0.0;
   }
 }
 
