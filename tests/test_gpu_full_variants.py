@@ -1,0 +1,168 @@
+"""Parity of the fill's variants at the workloads' full sizes, in the launch configurations
+the benchmark times: the 27B-shaped fill with int8 maps streamed from pinned host memory in
+4-layer groups, the Qwen3-8B-shaped fill with key norm, the 8B-shaped fill with a split
+state twice as wide as the layers, and the value-rescale factors over c = 512 tail rows of
+the 27B shape.
+
+Fills: routing bit-exact on every byte of every layer's pools (sentinel-filled), K and V
+against the oracle on 512 sampled rows of every layer (first and last filled row, rows
+next to exact rows, page edges, the rest seeded), relative Frobenius error <= 5e-3.
+Value-rescale factors: relative error <= 2e-3 on four layers.  The int8 codes come from the
+oracle's float32 quantizer; the oracle uses q * scale exactly."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ridge_map_kv_amd import binding as B
+from ridge_map_kv_amd import configs, synth
+
+from test_gpu_full import _np64, _rel, _sample_rows
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+def _routing(cfg, inp, filled):
+    dev = inp["xS"].device
+    pg, sl = oracle.paged_location(filled, inp["table_np"], cfg.page_size)
+    expect = torch.zeros((inp["num_pages"], cfg.page_size), dtype=torch.bool, device=dev)
+    expect[torch.from_numpy(pg).to(dev), torch.from_numpy(sl).to(dev)] = True
+    for l, lay in enumerate(inp["layers"]):
+        for key in ("k_pages", "v_pages"):
+            sent = lay[key].view(torch.int16) == -1
+            assert torch.equal((~sent).flatten(2).all(-1), expect), f"layer {l} {key}: row not fully written"
+            assert torch.equal(sent.flatten(2).all(-1), ~expect), f"layer {l} {key}: write outside filled rows"
+            del sent
+    return pg, sl
+
+
+def _values(cfg, inp, filled, exact, pg, sl, A_of=None, kn_of=None):
+    dev = inp["xS"].device
+    rows = _sample_rows(filled, exact, cfg.page_size)
+    xs = _np64(inp["xS"][torch.from_numpy(rows).to(dev)])
+    sel = np.searchsorted(filled, rows)
+    rpg = torch.from_numpy(pg[sel]).to(dev)
+    rsl = torch.from_numpy(sl[sel]).to(dev)
+    worst = 0.0
+    for l, lay in enumerate(inp["layers"]):
+        A = A_of(l) if A_of else _np64(lay["A"])
+        Ko, Vo = oracle.fill_rows(xs, rows, A, lay["b"].cpu().numpy().astype(np.float64),
+                                  _np64(lay["norm_w"]), _np64(lay["W_K"]), _np64(lay["W_V"]),
+                                  eps=cfg.rms_eps, theta=cfg.rope_theta, n_kv=cfg.n_kv,
+                                  hd=cfg.head_dim, k_norm_w=kn_of(l) if kn_of else None)
+        ek = _rel(_np64(lay["k_pages"][rpg, rsl]), Ko)
+        ev = _rel(_np64(lay["v_pages"][rpg, rsl]), Vo)
+        worst = max(worst, ek, ev)
+        assert ek <= TOL and ev <= TOL, f"layer {l}: K {ek:.3e} V {ev:.3e}"
+    return rows.size, worst
+
+
+def _run(cfg, inp, flags=0, ws_layers=None, copy=None, layers=None):
+    dev = inp["xS"].device
+    filled = B.ridgefill_partition(cfg.N, cfg.T, inp["exact_mask"])
+    shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta, d_in=cfg.d_in)
+    idx = torch.from_numpy(filled).to(dev)
+    ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, filled.size, ws_layers or cfg.n_upper,
+                                                      flags), dtype=torch.uint8, device=dev)
+    B.ridgefill_fill(shape, inp["xS"], cfg.N, cfg.T, idx, filled.size, layers or inp["layers"],
+                     inp["table"], cfg.page_size, inp["num_pages"], ws, copy_stream=copy)
+    assert B.ridgefill_read_status(ws) == B.RF_OK
+    del ws
+    return filled
+
+
+def test_27b_int8_maps_streamed_full_size():
+    cfg = configs.QWEN27B
+    dev = torch.device("cuda")
+    print("\n27B int8 streamed: inputs and oracle quantization", flush=True)
+    inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
+    codes, host = [], []
+    for l, lay in enumerate(inp["layers"]):
+        q, sc = oracle.quantize_map_int8(lay["A"].float().cpu().numpy(), np.float32)
+        codes.append((q, sc))
+        h = dict(lay)
+        del h["A"]
+        pinned = torch.empty(q.shape, dtype=torch.int8, pin_memory=True)
+        pinned.copy_(torch.from_numpy(q))
+        h["A_q"] = pinned
+        h["A_scale"] = torch.from_numpy(sc.astype(np.float32)).to(dev)
+        host.append(h)
+        del lay["A"]
+        if l % 12 == 11:
+            print(f"  quantized {l + 1} maps", flush=True)
+    torch.cuda.empty_cache()
+    print("27B int8 streamed: fill", flush=True)
+    filled = _run(cfg, inp, B.RF_MAPS_INT8 | B.RF_MAPS_STREAMED, ws_layers=4,
+                  copy=torch.cuda.Stream(), layers=host)
+    _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
+    print("27B int8 streamed: routing", flush=True)
+    pg, sl = _routing(cfg, inp, filled)
+    print("27B int8 streamed: values", flush=True)
+    n, worst = _values(cfg, inp, filled, exact, pg, sl,
+                       A_of=lambda l: oracle.dequantize_map_int8(*codes[l]))
+    print(f"27B int8 streamed: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
+
+
+def test_qwen3_8b_key_norm_full_size():
+    cfg = configs.QWEN3_8B
+    dev = torch.device("cuda")
+    print("\nQwen3-8B key norm: inputs", flush=True)
+    inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
+    kn = [synth.key_norm_weight(cfg.head_dim, cfg.seed, l) for l in range(cfg.n_upper)]
+    for l, lay in enumerate(inp["layers"]):
+        lay["k_norm_w"] = torch.from_numpy(kn[l]).to(dev).to(torch.bfloat16)
+    filled = _run(cfg, inp)
+    _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
+    pg, sl = _routing(cfg, inp, filled)
+    n, worst = _values(cfg, inp, filled, exact, pg, sl,
+                       kn_of=lambda l: _np64(inp["layers"][l]["k_norm_w"]))
+    print(f"Qwen3-8B key norm: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
+
+
+def test_wide_split_state_full_size():
+    cfg = configs.WIDE8B
+    dev = torch.device("cuda")
+    print("\nwide split state: inputs", flush=True)
+    inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
+    filled = _run(cfg, inp)
+    _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
+    pg, sl = _routing(cfg, inp, filled)
+    n, worst = _values(cfg, inp, filled, exact, pg, sl)
+    print(f"wide split state: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
+
+
+def test_value_scale_27b_shape():
+    cfg = configs.QWEN27B
+    dev = torch.device("cuda")
+    c = 512
+    print("\nvalue scale 27B shape: inputs", flush=True)
+    inp = synth.device_fill_inputs(cfg, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7070)
+    xt = torch.randn((c, cfg.d), generator=g, device=dev).to(torch.bfloat16)
+    # exact inputs near the prediction: A x + b plus noise of a tenth of its scale
+    exact = []
+    for lay in inp["layers"]:
+        pred = xt.float() @ lay["A"].float().T + lay["b"]
+        exact.append((pred + 0.1 * pred.std() * torch.randn(pred.shape, generator=g, device=dev))
+                     .to(torch.bfloat16).contiguous())
+        del pred
+    shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
+    ws = torch.empty(B.ridgefill_value_scale_workspace_bytes(shape, c, cfg.n_upper),
+                     dtype=torch.uint8, device=dev)
+    out = torch.full((cfg.n_upper, cfg.n_kv), float("nan"), device=dev)
+    B.ridgefill_value_scale(shape, xt, exact, inp["layers"], out, ws)
+    assert B.ridgefill_read_status(ws) == B.RF_OK
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    print("value scale 27B shape: oracle on 4 layers", flush=True)
+    for l in (0, 17, 30, cfg.n_upper - 1):
+        lay = inp["layers"][l]
+        want = oracle.value_scale(_np64(xt), _np64(exact[l]), _np64(lay["A"]),
+                                  lay["b"].cpu().numpy().astype(np.float64), _np64(lay["norm_w"]),
+                                  _np64(lay["W_V"]), eps=cfg.rms_eps, n_kv=cfg.n_kv,
+                                  hd=cfg.head_dim)
+        np.testing.assert_allclose(got[l], want, rtol=2e-3)
+        print(f"  layer {l}: max rel {np.max(np.abs(got[l] / want - 1)):.2e}", flush=True)
