@@ -315,23 +315,26 @@ class CalibStats:
     of x_S and of every x_l, the raw second moment sum_t x_S x_S^T and, per upper layer,
     the raw cross moment sum_t x_l x_S^T (= Y_l^T X before centring, d_out x d_in)."""
 
-    def __init__(self, d: int, n_layers: int):
-        self.d = int(d)
+    def __init__(self, d: int, n_layers: int, d_out: int | None = None):
+        self.d = int(d)                          # d_in: width of x_S
+        self.d_out = int(d_out) if d_out else self.d
         self.n_layers = int(n_layers)
         self.n = 0
-        self.s_S = np.zeros(d, dtype=np.float64)
-        self.s_l = np.zeros((n_layers, d), dtype=np.float64)
-        self.G = np.zeros((d, d), dtype=np.float64)
-        self.YX = np.zeros((n_layers, d, d), dtype=np.float64)
+        self.s_S = np.zeros(self.d, dtype=np.float64)
+        self.s_l = np.zeros((n_layers, self.d_out), dtype=np.float64)
+        self.G = np.zeros((self.d, self.d), dtype=np.float64)
+        self.YX = np.zeros((n_layers, self.d_out, self.d), dtype=np.float64)
 
 
-def calib_new(d: int, n_layers: int) -> CalibStats:
-    return CalibStats(d, n_layers)
+def calib_new(d: int, n_layers: int, d_out: int | None = None) -> CalibStats:
+    """Empty statistics for x_S of width d (= d_in) and layer inputs of width d_out
+    (default d; [size]: a map's input width may differ from its output width)."""
+    return CalibStats(d, n_layers, d_out)
 
 
 def calib_accumulate(st: CalibStats, x_S_chunk, x_l_chunks) -> CalibStats:
-    """Add one chunk of calibration rows: x_S_chunk [n_c, d] and one [n_c, d] array per
-    upper layer.  Only sums and moments are kept, so a new lambda needs no re-read."""
+    """Add one chunk of calibration rows: x_S_chunk [n_c, d_in] and one [n_c, d_out] array
+    per upper layer.  Only sums and moments are kept, so a new lambda needs no re-read."""
     X = np.asarray(x_S_chunk, dtype=np.float64)
     if len(x_l_chunks) != st.n_layers:
         raise ValueError("one chunk per upper layer is required")
@@ -340,8 +343,8 @@ def calib_accumulate(st: CalibStats, x_S_chunk, x_l_chunks) -> CalibStats:
     st.G += X.T @ X
     for l, Y in enumerate(x_l_chunks):
         Y = np.asarray(Y, dtype=np.float64)
-        if Y.shape != X.shape:
-            raise ValueError("x_l chunk shape differs from x_S chunk shape")
+        if Y.shape != (X.shape[0], st.d_out):
+            raise ValueError("x_l chunk must be [rows of x_S, d_out]")
         st.s_l[l] += Y.sum(axis=0)
         st.YX[l] += Y.T @ X
     return st
@@ -371,7 +374,7 @@ def solve(st: CalibStats, lam: float):
 
     (X^T X + alpha I) is factored by Cholesky; A_l^T is found from
     (X^T X + alpha I) A_l^T = (Y_l^T X)^T by two triangular solves.
-    Returns (A [n_layers, d, d], b [n_layers, d]) in float64.
+    Returns (A [n_layers, d_out, d_in], b [n_layers, d_out]) in float64.
     """
     import scipy.linalg as sla
 

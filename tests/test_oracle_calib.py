@@ -11,17 +11,18 @@ from ridge_map_kv_amd import synth
 
 
 def _stats(xS, xl, chunks=1):
-    st = oracle.calib_new(xS.shape[1], xl.shape[0])
+    st = oracle.calib_new(xS.shape[1], len(xl), np.asarray(xl[0]).shape[1])
     for part in np.array_split(np.arange(xS.shape[0]), chunks):
         oracle.calib_accumulate(st, xS[part], [y[part] for y in xl])
     return st
 
 
-def _hadamard_design(n=2048, d=64, shift=0.0, seed=5):
+def _hadamard_design(n=2048, d=64, shift=0.0, seed=5, d_out=None):
+    d_out = d_out or d
     H = synth.sylvester_hadamard(n).astype(np.float64)
     X = H[:, 1:d + 1]                       # columns 1..d: +-1, zero column means
-    W = synth.sparse_dyadic_matrix(d, d, seed).astype(np.float64)
-    c = np.random.default_rng(seed).integers(-8, 9, size=d) / 4.0
+    W = synth.sparse_dyadic_matrix(d_out, d, seed).astype(np.float64)
+    c = np.random.default_rng(seed).integers(-8, 9, size=d_out) / 4.0
     m = np.random.default_rng(seed + 1).integers(-4, 5, size=d) / 2.0 * (shift != 0)
     xS = X + m
     Y = xS @ W.T + c
@@ -30,11 +31,13 @@ def _hadamard_design(n=2048, d=64, shift=0.0, seed=5):
 
 @pytest.mark.parametrize("lam", [1e-4, 0.03, 1.0])
 @pytest.mark.parametrize("shift", [0.0, 1.0])
-def test_hadamard_closed_form(lam, shift):
+@pytest.mark.parametrize("d_out", [64, 40, 96])
+def test_hadamard_closed_form(lam, shift, d_out):
     # centred X^T X = n I, so alpha = lam n and A = W n (n + lam n)^-1 = W / (1 + lam);
-    # b = mu_l - A mu_S = (W m + c) - W m / (1 + lam) = c + lam / (1 + lam) W m
+    # b = mu_l - A mu_S = (W m + c) - W m / (1 + lam) = c + lam / (1 + lam) W m.
+    # d_out != 64: a rectangular map (output width differs from the split state's width)
     n, d = 2048, 64
-    xS, Y, W, c, m = _hadamard_design(n, d, shift)
+    xS, Y, W, c, m = _hadamard_design(n, d, shift, d_out=d_out)
     st = _stats(xS, Y[None], chunks=3)
     mu_S, mu_l, XtX, YtX = oracle.centred_moments(st)
     np.testing.assert_allclose(XtX, n * np.eye(d), atol=1e-9)
@@ -44,25 +47,28 @@ def test_hadamard_closed_form(lam, shift):
     np.testing.assert_allclose(b[0], c + lam / (1 + lam) * (W @ m), atol=1e-10)
 
 
-def _gauss_problem(n=3000, d=24, noise=0.3, seed=7, shift=0.5):
+def _gauss_problem(n=3000, d=24, noise=0.3, seed=7, shift=0.5, d_out=None):
+    d_out = d_out or d
     g = np.random.default_rng(seed)
     xS = g.standard_normal((n, d)) @ (np.eye(d) + 0.3 * g.standard_normal((d, d))) + shift
-    W = g.standard_normal((d, d)) / np.sqrt(d)
-    c = g.standard_normal(d)
-    Y = xS @ W.T + c + noise * g.standard_normal((n, d))
+    W = g.standard_normal((d_out, d)) / np.sqrt(d)
+    c = g.standard_normal(d_out)
+    Y = xS @ W.T + c + noise * g.standard_normal((n, d_out))
     return xS, Y, W, c
 
 
 @pytest.mark.parametrize("lam", [1e-3, 0.03, 0.5])
-def test_matches_lstsq_of_objective(lam):
+@pytest.mark.parametrize("d_out", [24, 9, 40])
+def test_matches_lstsq_of_objective(lam, d_out):
     # Solve the page's objective another way: least squares on [x_S, 1] with sqrt(alpha) I
-    # rows that penalise A but not b.  alpha from the centred trace = n * sum of variances.
-    xS, Y, _, _ = _gauss_problem()
+    # rows that penalise A but not b.  alpha from the centred trace = n * sum of variances
+    # over the d_in input features (d_out != d_in: a rectangular map).
+    xS, Y, _, _ = _gauss_problem(d_out=d_out)
     n, d = xS.shape
     alpha = lam * n * np.var(xS, axis=0).sum() / d
     aug = np.vstack([np.hstack([xS, np.ones((n, 1))]),
                      np.hstack([np.sqrt(alpha) * np.eye(d), np.zeros((d, 1))])])
-    rhs = np.vstack([Y, np.zeros((d, d))])
+    rhs = np.vstack([Y, np.zeros((d, d_out))])
     sol, *_ = np.linalg.lstsq(aug, rhs, rcond=None)
     A_ref, b_ref = sol[:d].T, sol[d]
     A, b = oracle.solve(_stats(xS, Y[None]), lam)
