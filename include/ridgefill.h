@@ -259,6 +259,21 @@ rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_
                               const uint16_t* x_S, const uint16_t* const* x_l, int64_t n_rows,
                               void* stream);
 
+/* The same for maps whose input width differs from their output width (section "Ridge
+ * map ...", map-size paragraph): x_S rows are d_in wide, x_l rows d_out wide (both
+ * multiples of 256).  The state then holds
+ *   [0, 256)   header: int64 n, int32 d_out, int32 n_layers, magic, int32 d_in
+ *   then       fp64 sum_t x_S [d_in], fp64 sum_t x_l [n_layers][d_out],
+ *              fp32 sum_t x_S x_S^T [d_in][d_in] (lower triangle valid),
+ *              fp32 sum_t x_l x_S^T [n_layers][d_out][d_in].
+ * The plain calls are these with d_in = d_out = d. */
+size_t ridgefill_calib_state_bytes_ex(int32_t d_in, int32_t d_out, int32_t n_layers);
+rf_status ridgefill_calib_reset_ex(void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
+                                   int32_t n_layers, void* stream);
+rf_status ridgefill_calibrate_ex(void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
+                                 int32_t n_layers, const uint16_t* x_S, const uint16_t* const* x_l,
+                                 int64_t n_rows, void* stream);
+
 /* ------------------------------------------------------------------------------
  * Solve.  Same section, closed-form equation and the scale-free penalty: with
  * mu = sums / n,  C = sum x_S x_S^T - n mu_S mu_S^T,  C_l = sum x_l x_S^T - n mu_l mu_S^T,
@@ -280,6 +295,14 @@ size_t ridgefill_solve_workspace_bytes(int32_t d, int32_t n_layers);
 rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int32_t n_layers,
                           double lambda, float* A_out, float* b_out, uint16_t* A_bf16_out,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* The solve for a state made by the _ex calls: alpha = lambda tr(C) / d_in, the Cholesky
+ * on the d_in x d_in side, A_out fp32 [n_layers][d_out][d_in], b_out fp32
+ * [n_layers][d_out], A_bf16_out bf16 [n_layers][d_out][d_in]. */
+size_t ridgefill_solve_workspace_bytes_ex(int32_t d_in, int32_t d_out, int32_t n_layers);
+rf_status ridgefill_solve_ex(const void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
+                             int32_t n_layers, double lambda, float* A_out, float* b_out,
+                             uint16_t* A_bf16_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Waits for `stream`, then returns the device status word of a fill, solve or selection
  * workspace: RF_OK, RF_E_ROWS, RF_E_NOT_SPD, or RF_E_INVALID for a NaN score.  Each call

@@ -32,8 +32,13 @@ EXPORTED = [
     "ridgefill_calib_state_bytes",
     "ridgefill_calib_reset",
     "ridgefill_calibrate",
+    "ridgefill_calib_state_bytes_ex",
+    "ridgefill_calib_reset_ex",
+    "ridgefill_calibrate_ex",
     "ridgefill_solve_workspace_bytes",
     "ridgefill_solve",
+    "ridgefill_solve_workspace_bytes_ex",
+    "ridgefill_solve_ex",
     "ridgefill_read_status",
     "ridgefill_profile_enable",
     "ridgefill_profile_read",
@@ -105,6 +110,11 @@ def lib() -> C.CDLL:
         "ridgefill_calibrate": (st, [vp, sz, i32, i32, vp, C.POINTER(vp), i64, vp]),
         "ridgefill_solve_workspace_bytes": (sz, [i32, i32]),
         "ridgefill_solve": (st, [vp, sz, i32, i32, C.c_double, vp, vp, vp, vp, sz, vp]),
+        "ridgefill_calib_state_bytes_ex": (sz, [i32, i32, i32]),
+        "ridgefill_calib_reset_ex": (st, [vp, sz, i32, i32, i32, vp]),
+        "ridgefill_calibrate_ex": (st, [vp, sz, i32, i32, i32, vp, C.POINTER(vp), i64, vp]),
+        "ridgefill_solve_workspace_bytes_ex": (sz, [i32, i32, i32]),
+        "ridgefill_solve_ex": (st, [vp, sz, i32, i32, i32, C.c_double, vp, vp, vp, vp, sz, vp]),
         "ridgefill_read_status": (st, [vp, vp]),
         "ridgefill_profile_enable": (st, [i32]),
         "ridgefill_profile_read": (st, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
@@ -241,36 +251,39 @@ def ridgefill_value_scale(shape: rf_shape, x_S_tail, x_l_tail: list, layers: lis
 
 # ------------------------------------------------------------------------------ calibration
 
-def ridgefill_calib_state_bytes(d: int, n_layers: int) -> int:
-    return int(lib().ridgefill_calib_state_bytes(int(d), int(n_layers)))
+def ridgefill_calib_state_bytes(d: int, n_layers: int, d_out: int | None = None) -> int:
+    """State size for x_S of width d (= d_in) and layer inputs of width d_out (default d)."""
+    return int(lib().ridgefill_calib_state_bytes_ex(int(d), int(d_out or d), int(n_layers)))
 
 
 def _nbytes(t) -> int:
     return int(t.numel() * t.element_size())
 
 
-def ridgefill_calib_reset(state, d: int, n_layers: int, stream=None) -> None:
-    _check(lib().ridgefill_calib_reset(_ptr(state), _nbytes(state), int(d), int(n_layers),
-                                       _stream(stream)))
+def ridgefill_calib_reset(state, d: int, n_layers: int, stream=None,
+                          d_out: int | None = None) -> None:
+    _check(lib().ridgefill_calib_reset_ex(_ptr(state), _nbytes(state), int(d), int(d_out or d),
+                                          int(n_layers), _stream(stream)))
 
 
 def ridgefill_calibrate(state, d: int, n_layers: int, x_S, x_l: list, n_rows: int | None = None,
-                        stream=None) -> None:
+                        stream=None, d_out: int | None = None) -> None:
     ptrs = (C.c_void_p * max(len(x_l), 1))(*[_ptr(t) for t in x_l])
     n = int(n_rows if n_rows is not None else x_S.shape[0])
-    _check(lib().ridgefill_calibrate(_ptr(state), _nbytes(state), int(d), int(n_layers),
-                                     _ptr(x_S), ptrs, n, _stream(stream)))
+    _check(lib().ridgefill_calibrate_ex(_ptr(state), _nbytes(state), int(d), int(d_out or d),
+                                        int(n_layers), _ptr(x_S), ptrs, n, _stream(stream)))
 
 
-def ridgefill_solve_workspace_bytes(d: int, n_layers: int) -> int:
-    return int(lib().ridgefill_solve_workspace_bytes(int(d), int(n_layers)))
+def ridgefill_solve_workspace_bytes(d: int, n_layers: int, d_out: int | None = None) -> int:
+    return int(lib().ridgefill_solve_workspace_bytes_ex(int(d), int(d_out or d), int(n_layers)))
 
 
 def ridgefill_solve(state, d: int, n_layers: int, lam: float, A_out, b_out, A_bf16_out, ws,
-                    stream=None) -> None:
-    _check(lib().ridgefill_solve(_ptr(state), _nbytes(state), int(d), int(n_layers), float(lam),
-                                 _ptr(A_out), _ptr(b_out), _ptr(A_bf16_out), _ptr(ws),
-                                 _nbytes(ws), _stream(stream)))
+                    stream=None, d_out: int | None = None) -> None:
+    """A_out fp32 [n_layers][d_out][d], b_out [n_layers][d_out] (d_out defaults to d)."""
+    _check(lib().ridgefill_solve_ex(_ptr(state), _nbytes(state), int(d), int(d_out or d),
+                                    int(n_layers), float(lam), _ptr(A_out), _ptr(b_out),
+                                    _ptr(A_bf16_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def ridgefill_read_status(ws, stream=None) -> int:

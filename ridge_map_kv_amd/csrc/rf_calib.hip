@@ -5,7 +5,7 @@
 // and the two means in one pass of the original model, so a new lambda needs only a new
 // solve.  Raw sums and raw second moments are kept; the solve centres them.
 //
-// Per call (n rows of x_S and of every x_l, bf16, row-major [n][d]):
+// Per call (n rows of x_S, bf16 [n][d_in], and of every x_l, bf16 [n][d_out]):
 //   sums   fp64 s_S += sum_t x_S[t], s_l += sum_t x_l[t]; header n += rows
 //   moments one launch over the lower-triangle tiles of G += x_S^T x_S and all tiles of
 //           every YX_l += x_l^T x_S (row = output feature of x_l, column = feature of x_S).
@@ -21,14 +21,14 @@
 
 namespace rf {
 
-CalibLayout calib_layout(int d, int n_layers) {
+CalibLayout calib_layout(int d_in, int d_out, int n_layers) {
   CalibLayout L;
   L.header = 0;
   L.sum_S = 256;
-  L.sum_l = L.sum_S + align256((size_t)d * 8);
-  L.G = L.sum_l + align256((size_t)n_layers * d * 8);
-  L.YX = L.G + align256((size_t)d * d * 4);
-  L.total = L.YX + (size_t)n_layers * d * d * 4;
+  L.sum_l = L.sum_S + align256((size_t)d_in * 8);
+  L.G = L.sum_l + align256((size_t)n_layers * d_out * 8);
+  L.YX = L.G + align256((size_t)d_in * d_in * 4);
+  L.total = L.YX + (size_t)n_layers * d_out * d_in * 4;
   return L;
 }
 
@@ -40,13 +40,15 @@ struct CalibArgs {
   const uint16_t* xS;
   const uint16_t* xl[kMaxCalibLayers];
   int row0;                      // first row this launch covers
-  int n_rows, d, n_layers, nt;   // rows covered (from row0); nt = d / 256
+  int n_rows, d_in, d_out, n_layers;   // rows covered (from row0)
+  int nt_in, nt_out;             // 256-wide tiles of d_in and of d_out
   int ngram;                     // lower-triangle tiles of G
   float* G;
   float* YX;
 };
 
-__global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d, int n_layers) {
+__global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d_in, int d_out,
+                                   int n_layers) {
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   u32x4* p = reinterpret_cast<u32x4*>(state + 256);
@@ -55,9 +57,10 @@ __global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d, in
   for (size_t i = tid; i < n16; i += stride) p[i] = z;
   if (tid == 0) {
     *reinterpret_cast<int64_t*>(state) = 0;
-    reinterpret_cast<int32_t*>(state)[2] = d;
+    reinterpret_cast<int32_t*>(state)[2] = d_out;
     reinterpret_cast<int32_t*>(state)[3] = n_layers;
     reinterpret_cast<uint32_t*>(state)[4] = kCalibMagic;
+    reinterpret_cast<int32_t*>(state)[5] = d_in;
   }
 }
 
@@ -66,20 +69,22 @@ __global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d, in
 // fp32; the 8 slices are then added in order in fp64 and folded into the state.
 struct SumArgs {
   const uint16_t* x[kMaxCalibLayers + 1];
-  int n_rows, d;
-  double* sums;          // [1 + n_layers][d] (sum_S then sum_l, contiguous)
+  int n_rows, d_in, d_out;
+  double* sums;          // sum_S [d_in], then sum_l [n_layers][d_out], contiguous
   int64_t* count;
 };
 
 __global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
   __shared__ float part[8][256];
   const int cb = blockIdx.x, m = blockIdx.y;
+  const int width = m == 0 ? a.d_in : a.d_out;
+  if (cb * 256 >= width) return;                 // the grid covers the wider of the two
   const int tid = threadIdx.x, s = tid >> 5, q = tid & 31;
   const uint16_t* base = a.x[m] + cb * 256 + q * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int t = s; t < a.n_rows; t += 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (size_t)t * a.d);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (size_t)t * width);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] += bf16_to_f32(v[e] & 0xffffu);
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
   double tot = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) tot += (double)part[k][tid];
-  double* dst = a.sums + (size_t)m * a.d + cb * 256 + tid;
+  double* dst = a.sums + (m == 0 ? 0 : (size_t)a.d_in + (size_t)(m - 1) * a.d_out) + cb * 256 + tid;
   *dst += tot;
   if (cb == 0 && m == 0 && tid == 0) *a.count += a.n_rows;
 }
@@ -144,6 +149,7 @@ struct CalibTile {
   const uint16_t* Y;
   float* out;
   int f0, o0;
+  int dy;                        // row stride of Y (d_in for G, d_out for a layer)
 };
 
 __device__ __forceinline__ CalibTile calib_tile(const CalibArgs& a, int tile) {
@@ -154,19 +160,21 @@ __device__ __forceinline__ CalibTile calib_tile(const CalibArgs& a, int tile) {
     gram_tile(tile, fi, tj);     // rows tj >= columns fi
     t.Y = a.xS;
     t.out = a.G;
+    t.dy = a.d_in;
   } else {
     const int k = tile - a.ngram;
-    const int per = a.nt * a.nt;
+    const int per = a.nt_out * a.nt_in;
     const int l = k / per;
     const int r = k - l * per;
-    const int tg = r / (kTokGroup * a.nt);
-    const int within = r - tg * kTokGroup * a.nt;
-    const int left = a.nt - tg * kTokGroup;
+    const int tg = r / (kTokGroup * a.nt_in);
+    const int within = r - tg * kTokGroup * a.nt_in;
+    const int left = a.nt_out - tg * kTokGroup;
     const int gsz = left < kTokGroup ? left : kTokGroup;
     fi = within / gsz;
     tj = tg * kTokGroup + (within - fi * gsz);
     t.Y = a.xl[l];
-    t.out = a.YX + (size_t)l * a.d * a.d;
+    t.out = a.YX + (size_t)l * a.d_out * a.d_in;
+    t.dy = a.d_out;
   }
   t.f0 = fi * kTile;
   t.o0 = tj * kTile;
@@ -201,8 +209,8 @@ __device__ __forceinline__ void calib_store(const f32x16 (&acc)[4][4], const Cal
 __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   const CalibTile t = calib_tile(a, xcd_remap(blockIdx.x, gridDim.x));
-  const uint16_t* X = t.X + (size_t)a.row0 * a.d;
-  const uint16_t* Y = t.Y + (size_t)a.row0 * a.d;
+  const uint16_t* X = t.X + (size_t)a.row0 * a.d_in;
+  const uint16_t* Y = t.Y + (size_t)a.row0 * t.dy;
   const int f0 = t.f0, o0 = t.o0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wf = wave >> 1, wt = wave & 1, rg = tid >> 5, fg = tid & 31;
@@ -216,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a)
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
   u32x4 vx[8], vy[8];
-  load_block(vx, X, a.d, a.n_rows, 0, rg, f0, fg);
-  load_block(vy, Y, a.d, a.n_rows, 0, rg, o0, fg);
+  load_block(vx, X, a.d_in, a.n_rows, 0, rg, f0, fg);
+  load_block(vy, Y, t.dy, a.n_rows, 0, rg, o0, fg);
   store_block_t(smem, vx, rg, fg);
   store_block_t(smem + kOperandStage, vy, rg, fg);
   __syncthreads();
@@ -226,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a)
     const unsigned char* cur = smem + (kt & 1) * kStageBytes;
     const bool more = kt + 1 < nk;
     if (more) {
-      load_block(vx, X, a.d, a.n_rows, (kt + 1) * BK, rg, f0, fg);
-      load_block(vy, Y, a.d, a.n_rows, (kt + 1) * BK, rg, o0, fg);
+      load_block(vx, X, a.d_in, a.n_rows, (kt + 1) * BK, rg, f0, fg);
+      load_block(vy, Y, t.dy, a.n_rows, (kt + 1) * BK, rg, o0, fg);
     }
     mma_slice(acc, cur, cur + kOperandStage, wf, wt, lane);
     if (more) {
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a)
     }
     __syncthreads();
   }
-  calib_store(acc, t, a.d);
+  calib_store(acc, t, a.d_in);
 }
 
 // ---------------------------------------------------------------- full 64-row slices
@@ -314,8 +322,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1;
   DmaOperand F, T;
-  calib_operand(F, t.X + (size_t)a.row0 * a.d, a.d, t.f0, wave, lane);
-  calib_operand(T, t.Y + (size_t)a.row0 * a.d, a.d, t.o0, wave, lane);
+  calib_operand(F, t.X + (size_t)a.row0 * a.d_in, a.d_in, t.f0, wave, lane);
+  calib_operand(T, t.Y + (size_t)a.row0 * t.dy, t.dy, t.o0, wave, lane);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -326,7 +334,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
   const int nk = a.n_rows / kPipeBK;                 // a multiple of 64 rows
-  const int64_t slice = (int64_t)kPipeBK * a.d * 2;  // bytes between consecutive slices
+  const int64_t fslice = (int64_t)kPipeBK * a.d_in * 2;   // bytes between consecutive slices
+  const int64_t tslice = (int64_t)kPipeBK * t.dy * 2;
   const uint32_t base = lds_addr(smem);
   for (int s = 0; s < 2 && s < nk; ++s) {
 #pragma unroll
@@ -336,8 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
     }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      F.base[p] += slice;
-      T.base[p] += slice;
+      F.base[p] += fslice;
+      T.base[p] += tslice;
     }
   }
   if (nk > 1)
@@ -360,8 +369,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
     if (pend) {
 #pragma unroll
       for (int p = 4; p < 8; ++p) {
-        F.base[p] += slice;
-        T.base[p] += slice;
+        F.base[p] += fslice;
+        T.base[p] += tslice;
       }
     }
     mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, wave);
@@ -381,8 +390,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
     if (more) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        F.base[p] += slice;
-        T.base[p] += slice;
+        F.base[p] += fslice;
+        T.base[p] += tslice;
       }
     }
   }
@@ -394,47 +403,51 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }
-  calib_store(acc, t, a.d);
+  calib_store(acc, t, a.d_in);
 }
 
 }  // namespace
 
-hipError_t launch_calib_reset(void* state, int d, int n_layers, hipStream_t stream) {
-  const CalibLayout L = calib_layout(d, n_layers);
+hipError_t launch_calib_reset(void* state, int d_in, int d_out, int n_layers, hipStream_t stream) {
+  const CalibLayout L = calib_layout(d_in, d_out, n_layers);
   hipLaunchKernelGGL(calib_reset_kernel, dim3(2048), dim3(256), 0, stream,
-                     static_cast<unsigned char*>(state), L.total, d, n_layers);
+                     static_cast<unsigned char*>(state), L.total, d_in, d_out, n_layers);
   return hipGetLastError();
 }
 
-hipError_t launch_calibrate(void* state, int d, int n_layers, const uint16_t* xS,
+hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, const uint16_t* xS,
                             const uint16_t* const* xl, int64_t n_rows, hipStream_t stream) {
   if (n_layers > kMaxCalibLayers) return hipErrorInvalidValue;
-  const CalibLayout L = calib_layout(d, n_layers);
+  const CalibLayout L = calib_layout(d_in, d_out, n_layers);
   unsigned char* st = static_cast<unsigned char*>(state);
 
   SumArgs s = {};
   s.x[0] = xS;
   for (int l = 0; l < n_layers; ++l) s.x[1 + l] = xl[l];
   s.n_rows = (int)n_rows;
-  s.d = d;
+  s.d_in = d_in;
+  s.d_out = d_out;
   s.sums = reinterpret_cast<double*>(st + L.sum_S);
   s.count = reinterpret_cast<int64_t*>(st);
-  // sum_l follows sum_S contiguously only when d * 8 is a multiple of 256 (d % 32 == 0).
+  // sum_l follows sum_S contiguously: d_in * 8 is a multiple of 256 (d_in % 256 == 0).
   {
     ProfileScope ps(RF_KERNEL_CALIB_SUMS, stream);
-    hipLaunchKernelGGL(calib_sums_kernel, dim3(d / 256, 1 + n_layers), dim3(256), 0, stream, s);
+    const int widest = d_in > d_out ? d_in : d_out;
+    hipLaunchKernelGGL(calib_sums_kernel, dim3(widest / 256, 1 + n_layers), dim3(256), 0, stream, s);
   }
 
   CalibArgs a = {};
   a.xS = xS;
   for (int l = 0; l < n_layers; ++l) a.xl[l] = xl[l];
-  a.d = d;
+  a.d_in = d_in;
+  a.d_out = d_out;
   a.n_layers = n_layers;
-  a.nt = d / kTile;
-  a.ngram = a.nt * (a.nt + 1) / 2;
+  a.nt_in = d_in / kTile;
+  a.nt_out = d_out / kTile;
+  a.ngram = a.nt_in * (a.nt_in + 1) / 2;
   a.G = reinterpret_cast<float*>(st + L.G);
   a.YX = reinterpret_cast<float*>(st + L.YX);
-  const int tiles = a.ngram + n_layers * a.nt * a.nt;
+  const int tiles = a.ngram + n_layers * a.nt_out * a.nt_in;
   const int bulk = (int)(n_rows / kPipeBK) * kPipeBK;
   if (bulk > 0) {
     a.row0 = 0;

@@ -90,11 +90,11 @@ hipError_t launch_value_scale(const FillPlan& plan, const FillLayerPtrs* layers,
 struct CalibLayout {
   size_t header, sum_S, sum_l, G, YX, total;
 };
-CalibLayout calib_layout(int d, int n_layers);
+CalibLayout calib_layout(int d_in, int d_out, int n_layers);
 constexpr uint32_t kCalibMagic = 0x52464331u;   // "RFC1"
 
-hipError_t launch_calib_reset(void* state, int d, int n_layers, hipStream_t stream);
-hipError_t launch_calibrate(void* state, int d, int n_layers, const uint16_t* xS,
+hipError_t launch_calib_reset(void* state, int d_in, int d_out, int n_layers, hipStream_t stream);
+hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, const uint16_t* xS,
                             const uint16_t* const* xl, int64_t n_rows, hipStream_t stream);
 
 // Solve ---------------------------------------------------------------------------
@@ -103,9 +103,10 @@ struct SolveLayout {
   size_t scalars, mu, C, W, M64, Mx, Cx, linv, v, total;
   int group;
 };
-SolveLayout solve_layout(int d, int n_layers);
-hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, float* A_out,
-                        float* b_out, uint16_t* A_bf16, void* ws, hipStream_t stream);
+SolveLayout solve_layout(int d_in, int d_out, int n_layers);
+hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, double lambda,
+                        float* A_out, float* b_out, uint16_t* A_bf16, void* ws,
+                        hipStream_t stream);
 
 hipError_t launch_clear_status(unsigned* status, hipStream_t stream);
 

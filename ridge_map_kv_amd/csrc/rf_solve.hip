@@ -35,20 +35,20 @@ constexpr int NB = 64;        // Cholesky / substitution block
 constexpr int LDT = NB + 1;   // padded LDS row (fp64)
 }  // namespace
 
-SolveLayout solve_layout(int d, int n_layers) {
+SolveLayout solve_layout(int d_in, int d_out, int n_layers) {
   SolveLayout L;
-  const size_t dd = (size_t)d * d;
+  const size_t dd = (size_t)d_in * d_in;
   L.scalars = 0;
   L.mu = 256;
-  L.v = L.mu + align256((size_t)(1 + n_layers) * d * 8);
-  L.linv = L.v + align256((size_t)d * 8);
-  L.C = L.linv + align256((size_t)(d / NB) * NB * NB * 8);
+  L.v = L.mu + align256(((size_t)d_in + (size_t)n_layers * d_out) * 8);
+  L.linv = L.v + align256((size_t)d_in * 8);
+  L.C = L.linv + align256((size_t)(d_in / NB) * NB * NB * 8);
   L.W = L.C + align256(dd * 8);
   L.M64 = L.W + align256(dd * 8);
   L.Mx = L.M64 + align256(dd * 8);
   L.group = n_layers < kSolveGroup ? n_layers : kSolveGroup;
   L.Cx = L.Mx + align256(dd * 6);
-  L.total = L.Cx + align256((size_t)L.group * dd * 6);
+  L.total = L.Cx + align256((size_t)L.group * d_out * d_in * 6);
   return L;
 }
 
@@ -61,12 +61,13 @@ __device__ __forceinline__ double* scal(unsigned char* s, int off) {
   return reinterpret_cast<double*>(s + off);
 }
 
-__global__ void means_kernel(const unsigned char* state, int d, int n_layers, size_t sum_off,
-                             double* mu, unsigned char* scalars) {
+// mu = sums / n for mu_S [d_in] and every mu_l [d_out] (count = d_in + n_layers d_out).
+__global__ void means_kernel(const unsigned char* state, int count, size_t sum_off, double* mu,
+                             unsigned char* scalars) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const double n = (double)*reinterpret_cast<const int64_t*>(state);
   const double* sums = reinterpret_cast<const double*>(state + sum_off);
-  if (i < (1 + n_layers) * d) mu[i] = n > 0 ? sums[i] / n : 0.0;
+  if (i < count) mu[i] = n > 0 ? sums[i] / n : 0.0;
   if (i == 0) *scal(scalars, kNOff) = n;
 }
 
@@ -377,42 +378,43 @@ __global__ __launch_bounds__(1024) void dot_kernel(const double* v, const double
 // b_l[o] = mu_l[o] - sum_k YX_l[o][k] v[k] + n mu_l[o] (v . mu_S); one wave per (l, o).
 __global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double* mu,
                                                    const double* v, const unsigned char* scalars,
-                                                   int d, int n_layers, float* b_out) {
+                                                   int d_in, int d_out, int n_layers, float* b_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= n_layers * d) return;
-  const int l = row / d, o = row - l * d;
-  const float* y = YX + (size_t)row * d;
+  if (row >= n_layers * d_out) return;
+  const float* y = YX + (size_t)row * d_in;
   double s = 0.0;
-  for (int k = lane; k < d; k += 64) s += (double)y[k] * v[k];
+  for (int k = lane; k < d_in; k += 64) s += (double)y[k] * v[k];
   for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
   if (lane == 0) {
     const double n = *reinterpret_cast<const double*>(scalars + kNOff);
     const double vmu = *reinterpret_cast<const double*>(scalars + kVMuOff);
-    const double m = mu[(size_t)(1 + l) * d + o];
+    const double m = mu[(size_t)d_in + row];
     b_out[row] = (float)(m - s + n * m * vmu);
   }
 }
 
 // ---------------------------------------------------------------- split bf16 map GEMM
-// Cx[g][o] = [C_hi | C_hi | C_lo] of row o of C_l = YX_l - n mu_l mu_S^T (l = l0 + g), the
-// centring in fp64.  Four consecutive k per thread.
+// Cx[g][o] = [C_hi | C_hi | C_lo] of row o of C_l = YX_l - n mu_l mu_S^T (l = l0 + g;
+// o < d_out, columns k < d_in), the centring in fp64.  Four consecutive k per thread.
 __global__ void split_c_kernel(const float* YX, const double* mu, const unsigned char* scalars,
-                               int d, int l0, int G, uint16_t* Cx) {
+                               int d_in, int d_out, int l0, int G, uint16_t* Cx) {
   const double n = *reinterpret_cast<const double*>(scalars + kNOff);
-  const size_t quads = (size_t)G * d * d / 4;
+  const size_t per = (size_t)d_out * d_in;
+  const size_t quads = (size_t)G * per / 4;
   for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads;
        q += (size_t)gridDim.x * blockDim.x) {
     const size_t e = q * 4;
-    const int g = (int)(e / ((size_t)d * d));
-    const size_t r = e - (size_t)g * d * d;
-    const int o = (int)(r / d), k = (int)(r - (size_t)o * d);
+    const int g = (int)(e / per);
+    const size_t r = e - (size_t)g * per;
+    const int o = (int)(r / d_in), k = (int)(r - (size_t)o * d_in);
     const int l = l0 + g;
-    const f32x4 y = *reinterpret_cast<const f32x4*>(YX + ((size_t)l * d + o) * d + k);
-    const double nm = n * mu[(size_t)(1 + l) * d + o];
+    const f32x4 y = *reinterpret_cast<const f32x4*>(YX + ((size_t)l * d_out + o) * d_in + k);
+    const double nm = n * mu[(size_t)d_in + (size_t)l * d_out + o];
     uint16_t hi[4], lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) split_bf16((double)y[j] - nm * mu[k + j], hi[j], lo[j]);
-    uint16_t* row = Cx + ((size_t)g * d + o) * (3 * (size_t)d);
+    const size_t d = (size_t)d_in;
+    uint16_t* row = Cx + ((size_t)g * d_out + o) * (3 * d);
     u32x2 h2, l2;
     h2.x = hi[0] | (uint32_t)hi[1] << 16;
     h2.y = hi[2] | (uint32_t)hi[3] << 16;
@@ -425,28 +427,28 @@ __global__ void split_c_kernel(const float* YX, const double* mu, const unsigned
 }
 
 struct SolveGemmArgs {
-  const uint16_t* Cx;       // [G][d][3d]
-  const uint16_t* Mx;       // [d][3d]
-  float* A_out;             // [n_layers][d][d] or null
-  uint16_t* A_bf16;         // [n_layers][d][d] or null
-  int d, l0, nt;
+  const uint16_t* Cx;       // [G][d_out][3 d_in]
+  const uint16_t* Mx;       // [d_in][3 d_in]
+  float* A_out;             // [n_layers][d_out][d_in] or null
+  uint16_t* A_bf16;         // [n_layers][d_out][d_in] or null
+  int d_in, d_out, l0, nt_in, nt_out;
 };
 
-// A_l[o][i] for one 256 x 256 tile: F = rows o of Cx, T = rows i of Mx, K = 3d.  In the
+// A_l[o][i] for one 256 x 256 tile: F = rows o of Cx, T = rows i of Mx, K = 3 d_in.  In the
 // MFMA result each lane holds one i and runs of four o, so for each o a half-wave writes
 // 32 consecutive i.
 __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = a.nt * a.nt;
+  const int per = a.nt_out * a.nt_in;
   const int g = tile / per;
   const int r = tile - g * per;
   // groups of 4 o-tiles against all i-tiles (o-tiles share the Cx rows across i)
-  const int fg = r / (4 * a.nt), within = r - fg * 4 * a.nt;
-  const int left = a.nt - fg * 4, gsz = left < 4 ? left : 4;
+  const int fg = r / (4 * a.nt_in), within = r - fg * 4 * a.nt_in;
+  const int left = a.nt_out - fg * 4, gsz = left < 4 ? left : 4;
   const int it = within / gsz, ot = fg * 4 + (within - it * gsz);
   const int o0 = ot * kTile, i0 = it * kTile;
-  const size_t d3 = (size_t)3 * a.d;
+  const size_t d3 = (size_t)3 * a.d_in;
   const int tid = threadIdx.x;
   DmaOperand Fo, To;
   {
@@ -455,14 +457,14 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), rr = r0 + dma_lane_row(lane);
       const int ce = dma_chunk_elems(rr, lane);
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(a.Cx + ((size_t)g * a.d + o0 + r0) * d3);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(a.Cx + ((size_t)g * a.d_out + o0 + r0) * d3);
       Fo.off[p] = (uint32_t)((dma_lane_row(lane) * d3 + ce) * 2);
       To.base[p] = reinterpret_cast<const unsigned char*>(a.Mx + (size_t)(i0 + r0) * d3);
       To.off[p] = Fo.off[p];
     }
   }
   f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, 3 * a.d, smem);
+  gemm_pipeline(acc, Fo, To, 3 * a.d_in, smem);
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
   const int l = a.l0 + g;
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int o = o0 + wf * 128 + m * 32 + q * 8 + h * 4 + e;
-          const size_t idx = ((size_t)l * a.d + o) * a.d + i;
+          const size_t idx = ((size_t)l * a.d_out + o) * a.d_in + i;
           const float v = acc[m][n][q * 4 + e];
           if (a.A_out) a.A_out[idx] = v;
           if (a.A_bf16) a.A_bf16[idx] = f32_to_bf16(v);
@@ -486,10 +488,12 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
 
 }  // namespace
 
-hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, float* A_out,
-                        float* b_out, uint16_t* A_bf16, void* ws, hipStream_t stream) {
-  const CalibLayout CL = calib_layout(d, n_layers);
-  const SolveLayout L = solve_layout(d, n_layers);
+hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, double lambda,
+                        float* A_out, float* b_out, uint16_t* A_bf16, void* ws,
+                        hipStream_t stream) {
+  const CalibLayout CL = calib_layout(d_in, d_out, n_layers);
+  const SolveLayout L = solve_layout(d_in, d_out, n_layers);
+  const int d = d_in;            // the Cholesky, inverse and M live on the d_in x d_in side
   const unsigned char* st = static_cast<const unsigned char*>(state);
   unsigned char* w = static_cast<unsigned char*>(ws);
   unsigned* status = reinterpret_cast<unsigned*>(w);
@@ -509,8 +513,9 @@ hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, f
 
   hipError_t e = launch_clear_status(status, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(means_kernel, dim3(((1 + n_layers) * d + 255) / 256), dim3(256), 0, stream,
-                     st, d, n_layers, CL.sum_S, mu, w);
+  const int nmu = d_in + n_layers * d_out;
+  hipLaunchKernelGGL(means_kernel, dim3((nmu + 255) / 256), dim3(256), 0, stream, st, nmu,
+                     CL.sum_S, mu, w);
   hipLaunchKernelGGL(centre_kernel, dim3(gdd), dim3(256), 0, stream, G, mu, w, d, C);
   hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
   for (int k = 0; k < nbk; ++k) {
@@ -536,13 +541,15 @@ hipError_t launch_solve(const void* state, int d, int n_layers, double lambda, f
 
   for (int l0 = 0; l0 < n_layers; l0 += L.group) {
     const int G = (n_layers - l0) < L.group ? (n_layers - l0) : L.group;
-    hipLaunchKernelGGL(split_c_kernel, dim3(2048), dim3(256), 0, stream, YX, mu, w, d, l0, G, Cx);
-    SolveGemmArgs a = {Cx, Mx, A_out, A_bf16, d, l0, d / kTile};
+    hipLaunchKernelGGL(split_c_kernel, dim3(2048), dim3(256), 0, stream, YX, mu, w, d_in, d_out,
+                       l0, G, Cx);
+    SolveGemmArgs a = {Cx, Mx, A_out, A_bf16, d_in, d_out, l0, d_in / kTile, d_out / kTile};
     ProfileScope ps(RF_KERNEL_SOLVE_MAP, stream);
-    hipLaunchKernelGGL(solve_gemm_kernel, dim3(G * a.nt * a.nt), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(solve_gemm_kernel, dim3(G * a.nt_out * a.nt_in), dim3(kThreads), 0, stream,
+                       a);
   }
-  hipLaunchKernelGGL(bias_kernel, dim3((n_layers * d + 3) / 4), dim3(256), 0, stream, YX, mu, v,
-                     w, d, n_layers, b_out);
+  hipLaunchKernelGGL(bias_kernel, dim3((n_layers * d_out + 3) / 4), dim3(256), 0, stream, YX, mu,
+                     v, w, d_in, d_out, n_layers, b_out);
   return hipGetLastError();
 }
 

@@ -380,36 +380,51 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
   return ok();
 }
 
-size_t ridgefill_calib_state_bytes(int32_t d, int32_t n_layers) {
-  if (d < rf::kTile || d % rf::kTile || n_layers < 1) return 0;
-  return rf::calib_layout(d, n_layers).total;
+static bool dims_ok(int d_in, int d_out) {
+  return d_in >= rf::kTile && d_in % rf::kTile == 0 && d_out >= rf::kTile && d_out % rf::kTile == 0;
 }
 
-static rf_status check_state(const void* state, size_t bytes, int d, int n_layers) {
+size_t ridgefill_calib_state_bytes_ex(int32_t d_in, int32_t d_out, int32_t n_layers) {
+  if (!dims_ok(d_in, d_out) || n_layers < 1) return 0;
+  return rf::calib_layout(d_in, d_out, n_layers).total;
+}
+
+size_t ridgefill_calib_state_bytes(int32_t d, int32_t n_layers) {
+  return ridgefill_calib_state_bytes_ex(d, d, n_layers);
+}
+
+static rf_status check_state(const void* state, size_t bytes, int d_in, int d_out, int n_layers) {
   if (!state) return fail(RF_E_INVALID, "state is NULL");
   if (!aligned(state, 256)) return fail(RF_E_WORKSPACE, "state must be 256-byte aligned");
-  if (d < rf::kTile || d % rf::kTile)
-    return fail(RF_E_SHAPE, "d = %d must be a positive multiple of %d", d, rf::kTile);
+  if (!dims_ok(d_in, d_out))
+    return fail(RF_E_SHAPE, "d_in = %d and d_out = %d must be positive multiples of %d", d_in,
+                d_out, rf::kTile);
   if (n_layers < 1 || n_layers > 64) return fail(RF_E_SHAPE, "n_layers = %d must be in 1..64", n_layers);
-  if (bytes < rf::calib_layout(d, n_layers).total)
+  if (bytes < rf::calib_layout(d_in, d_out, n_layers).total)
     return fail(RF_E_WORKSPACE, "state %zu bytes < %zu needed", bytes,
-                rf::calib_layout(d, n_layers).total);
+                rf::calib_layout(d_in, d_out, n_layers).total);
   return RF_OK;
 }
 
-rf_status ridgefill_calib_reset(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
-                                void* stream) {
-  rf_status s = check_state(state, state_bytes, d, n_layers);
+rf_status ridgefill_calib_reset_ex(void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
+                                   int32_t n_layers, void* stream) {
+  rf_status s = check_state(state, state_bytes, d_in, d_out, n_layers);
   if (s != RF_OK) return s;
-  hipError_t e = rf::launch_calib_reset(state, d, n_layers, static_cast<hipStream_t>(stream));
+  hipError_t e = rf::launch_calib_reset(state, d_in, d_out, n_layers,
+                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "calibration reset");
   return ok();
 }
 
-rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
-                              const uint16_t* x_S, const uint16_t* const* x_l, int64_t n_rows,
-                              void* stream) {
-  rf_status s = check_state(state, state_bytes, d, n_layers);
+rf_status ridgefill_calib_reset(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                                void* stream) {
+  return ridgefill_calib_reset_ex(state, state_bytes, d, d, n_layers, stream);
+}
+
+rf_status ridgefill_calibrate_ex(void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
+                                 int32_t n_layers, const uint16_t* x_S, const uint16_t* const* x_l,
+                                 int64_t n_rows, void* stream) {
+  rf_status s = check_state(state, state_bytes, d_in, d_out, n_layers);
   if (s != RF_OK) return s;
   if (n_rows < 0 || n_rows > INT32_MAX) return fail(RF_E_SHAPE, "n_rows out of range");
   if (n_rows == 0) return ok();
@@ -418,22 +433,32 @@ rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_
   for (int l = 0; l < n_layers; ++l)
     if (!x_l[l] || !aligned(x_l[l], 16))
       return fail(RF_E_INVALID, "x_l[%d] is NULL or not 16-byte aligned", l);
-  hipError_t e = rf::launch_calibrate(state, d, n_layers, x_S, x_l, n_rows,
+  hipError_t e = rf::launch_calibrate(state, d_in, d_out, n_layers, x_S, x_l, n_rows,
                                       static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return fail(RF_E_UNSUPPORTED, "calibration kernels not built");
   if (e != hipSuccess) return hip_fail(e, "calibration launch");
   return ok();
 }
 
-size_t ridgefill_solve_workspace_bytes(int32_t d, int32_t n_layers) {
-  if (d < rf::kTile || d % rf::kTile || n_layers < 1) return 0;
-  return rf::solve_layout(d, n_layers).total;
+rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                              const uint16_t* x_S, const uint16_t* const* x_l, int64_t n_rows,
+                              void* stream) {
+  return ridgefill_calibrate_ex(state, state_bytes, d, d, n_layers, x_S, x_l, n_rows, stream);
 }
 
-rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int32_t n_layers,
-                          double lambda, float* A_out, float* b_out, uint16_t* A_bf16_out,
-                          void* ws, size_t ws_bytes, void* stream) {
-  rf_status s = check_state(state, state_bytes, d, n_layers);
+size_t ridgefill_solve_workspace_bytes_ex(int32_t d_in, int32_t d_out, int32_t n_layers) {
+  if (!dims_ok(d_in, d_out) || n_layers < 1) return 0;
+  return rf::solve_layout(d_in, d_out, n_layers).total;
+}
+
+size_t ridgefill_solve_workspace_bytes(int32_t d, int32_t n_layers) {
+  return ridgefill_solve_workspace_bytes_ex(d, d, n_layers);
+}
+
+rf_status ridgefill_solve_ex(const void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
+                             int32_t n_layers, double lambda, float* A_out, float* b_out,
+                             uint16_t* A_bf16_out, void* ws, size_t ws_bytes, void* stream) {
+  rf_status s = check_state(state, state_bytes, d_in, d_out, n_layers);
   if (s != RF_OK) return s;
   if (!(lambda >= 0.0) || !std::isfinite(lambda))
     return fail(RF_E_INVALID, "lambda must be finite and >= 0");
@@ -442,14 +467,21 @@ rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int3
   if ((A_out && !aligned(A_out, 16)) || !aligned(b_out, 16) || (A_bf16_out && !aligned(A_bf16_out, 16)))
     return fail(RF_E_SHAPE, "outputs must be 16-byte aligned");
   if (!ws || !aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace NULL or not 256-byte aligned");
-  if (ws_bytes < rf::solve_layout(d, n_layers).total)
+  if (ws_bytes < rf::solve_layout(d_in, d_out, n_layers).total)
     return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes,
-                rf::solve_layout(d, n_layers).total);
-  hipError_t e = rf::launch_solve(state, d, n_layers, lambda, A_out, b_out, A_bf16_out, ws,
-                                  static_cast<hipStream_t>(stream));
+                rf::solve_layout(d_in, d_out, n_layers).total);
+  hipError_t e = rf::launch_solve(state, d_in, d_out, n_layers, lambda, A_out, b_out, A_bf16_out,
+                                  ws, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return fail(RF_E_UNSUPPORTED, "solve kernels not built");
   if (e != hipSuccess) return hip_fail(e, "solve launch");
   return ok();
+}
+
+rf_status ridgefill_solve(const void* state, size_t state_bytes, int32_t d, int32_t n_layers,
+                          double lambda, float* A_out, float* b_out, uint16_t* A_bf16_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  return ridgefill_solve_ex(state, state_bytes, d, d, n_layers, lambda, A_out, b_out, A_bf16_out,
+                            ws, ws_bytes, stream);
 }
 
 rf_status ridgefill_read_status(void* ws, void* stream) {
