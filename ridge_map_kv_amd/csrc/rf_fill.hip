@@ -501,18 +501,25 @@ __global__ void exact_rows_kernel(ExactArgs a) {
   }
 }
 
-// v_scale[l][h] = mean over the c rows of |v_exact| / |v_pred|, added in row order.
-__global__ void vscale_kernel(const float* vn_pred, const float* vn_exact, int c, int cpad,
-                              int n_kv, int G, float* out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= G * n_kv) return;
-  const int l = i / n_kv, hh = i - l * n_kv;
+// v_scale[l][h] = mean over the c rows of |v_exact| / |v_pred|: one block per (l, h); thread
+// t adds rows t, t + 256, ... in fp64, then a fixed-order tree adds the 256 partials
+// (deterministic).
+__global__ __launch_bounds__(256) void vscale_kernel(const float* vn_pred, const float* vn_exact,
+                                                     int c, int cpad, int n_kv, float* out) {
+  __shared__ double part[256];
+  const int i = blockIdx.x, l = i / n_kv, hh = i - l * n_kv, t = threadIdx.x;
   double s = 0.0;
-  for (int t = 0; t < c; ++t) {
-    const size_t k = ((size_t)l * cpad + t) * n_kv + hh;
+  for (int r = t; r < c; r += 256) {
+    const size_t k = ((size_t)l * cpad + r) * n_kv + hh;
     s += (double)vn_exact[k] / (double)vn_pred[k];
   }
-  out[i] = (float)(s / c);
+  part[t] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) part[t] += part[t + w];
+    __syncthreads();
+  }
+  if (t == 0) out[i] = (float)(part[0] / c);
 }
 
 }  // namespace
@@ -742,8 +749,8 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
     a.layer_ws = V.exact;
     a.vnorm = V.vn_exact;
     hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(vscale_kernel, dim3((G * p.n_kv + 255) / 256), dim3(256), 0, stream,
-                       V.vn_pred, V.vn_exact, p.n_filled, p.mpad, p.n_kv, G, out + (size_t)l0 * p.n_kv);
+    hipLaunchKernelGGL(vscale_kernel, dim3(G * p.n_kv), dim3(256), 0, stream, V.vn_pred,
+                       V.vn_exact, p.n_filled, p.mpad, p.n_kv, out + (size_t)l0 * p.n_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
