@@ -25,6 +25,11 @@ by its section:
   [qknorm] same paragraph (Qwen models normalise keys) and "Experiments", the error
            attribution paragraph on key normalization
   [select] "Which rows to compute exactly", attention selection
+  [fold]   [map] and [own] taken together: the folded form of one layer (the norm weight
+           and the K/V projections multiplied into the map, the prediction's sum of
+           squares as a triangular quadratic form).  This is an exact rearrangement of
+           the same arithmetic, not a step the page describes; fill_rows_folded must
+           agree with fill_rows to float64 rounding.
 
 Readings of points the page leaves open (each is listed with its reason in the design
 notes of the repository):
@@ -75,6 +80,8 @@ __all__ = [
     "quantize_map_int8",
     "dequantize_map_int8",
     "select_exact",
+    "fold_map",
+    "fill_rows_folded",
     "paged_location",
     "fill_paged_cache",
     "CalibStats",
@@ -264,6 +271,64 @@ def quantize_map_int8(A: np.ndarray, dtype=np.float64):
 def dequantize_map_int8(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """The map an int8 map stands for: q[o, k] * scale[o], in float64."""
     return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+# --------------------------------------------------------------------------- [fold]
+
+def fold_map(A, b, norm_w, W_K, W_V):
+    """Folded form of one upper layer ([fold]).  In the plain flow x_hat = A x + b,
+    h = x_hat / sqrt(mean(x_hat^2) + eps) * w, k = W_K h, v = W_V h ([map], [own]), the
+    weight w and the projections are linear and the only non-linear quantity is the
+    scalar |x_hat|^2.  With
+
+        P     = [W_K; W_V] diag(w) A                         [2 kv, d_in]
+        c     = [W_K; W_V] (w * b)                           [2 kv]
+        R     = the upper-triangular factor of A^T A with a positive diagonal
+                (R^T R = A^T A: the transpose of its Cholesky factor)
+        r     = R^-T A^T b                                   [d_in]
+        kappa = |b|^2 - |r|^2
+
+    every x has [W_K; W_V] diag(w) x_hat = P x + c, and |x_hat|^2 = |R x + r|^2 + kappa,
+    because |R x + r|^2 = x^T A^T A x + 2 b^T A x + |r|^2.  kappa is the squared distance
+    from b to the column space of A (zero when A is square and invertible).  A^T A must
+    be positive definite (A of full column rank: d_in <= d_out); otherwise numpy's
+    Cholesky raises LinAlgError.  Returns (P, c, R, r, kappa) in float64.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    w = np.asarray(norm_w, dtype=np.float64)
+    W = np.concatenate([np.asarray(W_K, dtype=np.float64), np.asarray(W_V, dtype=np.float64)])
+    Ww = W * w[None, :]
+    P = Ww @ A
+    c = Ww @ b
+    L = np.linalg.cholesky(A.T @ A)          # lower, A^T A = L L^T
+    R = L.T
+    r = np.linalg.solve(L, A.T @ b)          # R^T r = A^T b, R^T = L
+    kappa = float(b @ b - r @ r)
+    return P, c, R, r, kappa
+
+
+def fill_rows_folded(x_S_rows, positions, P, c, R, r, kappa, d, *, eps, theta, n_kv, hd,
+                     k_norm_w=None, v_scale=None):
+    """The cache entries of fill_rows computed from the folded form of fold_map ([fold]):
+    mean(x_hat^2) = (|R x + r|^2 + kappa) / d with d the map's output width, then
+    [k; v] = (P x + c) / sqrt(mean(x_hat^2) + eps), followed by the same key norm, RoPE
+    and value rescale as fill_rows.  Returns (K, V), each [rows, n_kv, hd] in float64."""
+    x = np.asarray(x_S_rows, dtype=np.float64)
+    u = x @ np.asarray(R, dtype=np.float64).T + np.asarray(r, dtype=np.float64)[None, :]
+    ms = (np.sum(u * u, axis=1) + float(kappa)) / float(d)
+    kvp = (x @ np.asarray(P, dtype=np.float64).T + np.asarray(c, dtype=np.float64)[None, :])
+    kvp = kvp / np.sqrt(ms + float(eps))[:, None]
+    kv = n_kv * hd
+    rows = x.shape[0]
+    K = kvp[:, :kv].reshape(rows, n_kv, hd)
+    V = kvp[:, kv:].reshape(rows, n_kv, hd)
+    if k_norm_w is not None:
+        K = key_norm(K, k_norm_w, eps)
+    K = rope_keys(K, positions, theta)
+    if v_scale is not None:
+        V = V * np.asarray(v_scale, dtype=np.float64)[None, :, None]
+    return K, V
 
 
 # --------------------------------------------------------------------------- [select]
