@@ -86,6 +86,10 @@ typedef struct rf_layer {
                                A_scale[o] (section "Ridge map ...", map size paragraph:
                                int8 maps).  Exactly one of A and A_q is set.             */
   const float* A_scale;     /* fp32 [d]: per-output-row scale of A_q                    */
+  const void* folded;       /* device buffer of ridgefill_fold_bytes(shape) bytes made by
+                               ridgefill_fold_maps, 256-byte aligned: the layer's folded
+                               form.  When set, the fill reads it instead of A, A_q,
+                               A_scale, b, norm_w, W_K and W_V (which may then be NULL).  */
 } rf_layer;
 
 /* Paged KV layout of one prompt, shared by every layer's k_pages / v_pages. */
@@ -170,10 +174,13 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
 
 /* Map variants for the workspace query: RF_MAPS_INT8 when the layers carry A_q/A_scale
  * (the workspace then holds a bf16 expansion of each layer's codes), RF_MAPS_STREAMED for
- * ridgefill_fill_streamed (two landing slots per layer).  Returns 0 on invalid input.
+ * ridgefill_fill_streamed (two landing slots per layer), RF_MAPS_FOLDED when the layers
+ * carry folded forms (no predicted-input buffer: a few MB per layer).  Returns 0 on
+ * invalid input.
  * ridgefill_fill_workspace_bytes(...) is ridgefill_fill_workspace_bytes_ex(..., 0). */
 #define RF_MAPS_INT8 1
 #define RF_MAPS_STREAMED 2
+#define RF_MAPS_FOLDED 4
 size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled,
                                          int32_t n_layers, int32_t map_flags);
 
@@ -192,6 +199,44 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
                                   int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
                                   const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
                                   void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/* ------------------------------------------------------------------------------
+ * Folded layers.  Section "Ridge map: predict the input, and the original projection runs
+ * unchanged": after x_hat = A x_S + b the layer's RMSNorm weight w and its projections
+ * W_K, W_V are linear, so they can be multiplied into the map once per layer; the only
+ * non-linear quantity left is |x_hat|^2, which equals |R x_S + r|^2 + kappa with R the
+ * upper-triangular factor of A^T A (R^T R = A^T A, positive diagonal),
+ * r = R^-T A^T b and kappa = |b|^2 - |r|^2.  The fill of a folded layer then computes
+ *     k, v = (P x_S + c) / sqrt((|R x_S + r|^2 + kappa) / d + eps)
+ * with P = [W_K; W_V] diag(w) A and c = [W_K; W_V] (w * b), followed by the same key norm,
+ * RoPE, value rescale and paged store as the plain fill.  Same result up to rounding;
+ * R x_S needs half the multiply-adds of A x_S, and x_hat is never stored.
+ *
+ * Folded buffer of one layer (offsets from its start, each 256-byte aligned):
+ *     P bf16 [2 kv][d_in] (K rows, then V rows), R bf16 [d_in][d_in] (zeros below the
+ *     diagonal), c fp32 [2 kv], r fp32 [d_in], kappa fp32;  kv = n_kv_heads * head_dim.
+ * ridgefill_fold_bytes returns its size, 0 when the shape cannot be folded: A^T A must be
+ * positive definite, so d_in <= d, and d_in must be a multiple of 256.
+ *
+ * ridgefill_fold_maps computes every given layer's folded buffer from its plain fields
+ * (A bf16, b, norm_w, W_K, W_V; int8 maps are not accepted):
+ *   folded     host array [n_layers] of device pointers, each >= ridgefill_fold_bytes
+ *              bytes and 256-byte aligned
+ *   ws         device workspace >= ridgefill_fold_workspace_bytes(shape); its first 256
+ *              bytes hold the status: RF_E_NOT_SPD when some layer's A^T A had a
+ *              non-positive pivot (A not of full column rank; that layer's buffer is
+ *              then not usable)
+ * Arithmetic: P = bf16-split(W diag(w)) times A on the matrix cores (products exact,
+ * fp32 accumulation, one bf16 rounding of P); A^T A with exact products and fp32
+ * accumulation; Cholesky, r and kappa in fp64; R rounded to bf16 once; c in fp64
+ * rounded to fp32.  Layers are folded one after another through the workspace.
+ * Folded layers work with ridgefill_fill (not the streamed fill); all layers of a fill
+ * call must be folded or none.  ridgefill_value_scale always uses the plain fields.
+ * ------------------------------------------------------------------------------ */
+size_t ridgefill_fold_bytes(const rf_shape* shape);
+size_t ridgefill_fold_workspace_bytes(const rf_shape* shape);
+rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int32_t n_layers,
+                              void* const* folded, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
  * int8 maps.  Section "Ridge map ...", map size paragraph: maps held in int8 (1.2 GiB
@@ -323,7 +368,8 @@ typedef enum rf_kernel_id {
   RF_KERNEL_CALIB_MOMENTS = 2, /* calibration: sum x_S x_S^T (lower) and every x_l x_S^T */
   RF_KERNEL_CALIB_SUMS = 3,    /* calibration: column sums and row count                 */
   RF_KERNEL_SOLVE_MAP = 4,     /* solve: A_l = C_l (C + alpha I)^-1 product              */
-  RF_KERNEL_COUNT = 5
+  RF_KERNEL_FILL_NORM = 5,     /* folded fill: per-row |R x_S + r|^2 partials            */
+  RF_KERNEL_COUNT = 6
 } rf_kernel_id;
 rf_status ridgefill_profile_enable(int32_t enable);
 rf_status ridgefill_profile_read(int32_t kernel, int64_t* launches, double* total_ms);

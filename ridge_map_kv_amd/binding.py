@@ -27,6 +27,9 @@ EXPORTED = [
     "ridgefill_value_scale_workspace_bytes",
     "ridgefill_value_scale",
     "ridgefill_quantize_map",
+    "ridgefill_fold_bytes",
+    "ridgefill_fold_workspace_bytes",
+    "ridgefill_fold_maps",
     "ridgefill_select_workspace_bytes",
     "ridgefill_select_rows",
     "ridgefill_calib_state_bytes",
@@ -56,6 +59,7 @@ class RidgeFillError(RuntimeError):
 
 RF_MAPS_INT8 = 1
 RF_MAPS_STREAMED = 2
+RF_MAPS_FOLDED = 4
 
 
 class rf_shape(C.Structure):
@@ -68,7 +72,7 @@ class rf_layer(C.Structure):
     _fields_ = [("A", C.c_void_p), ("b", C.c_void_p), ("norm_w", C.c_void_p),
                 ("W_K", C.c_void_p), ("W_V", C.c_void_p), ("k_pages", C.c_void_p),
                 ("v_pages", C.c_void_p), ("k_norm_w", C.c_void_p), ("v_scale", C.c_void_p),
-                ("A_q", C.c_void_p), ("A_scale", C.c_void_p)]
+                ("A_q", C.c_void_p), ("A_scale", C.c_void_p), ("folded", C.c_void_p)]
 
 
 class rf_paged_kv(C.Structure):
@@ -103,6 +107,10 @@ def lib() -> C.CDLL:
         "ridgefill_value_scale": (st, [C.POINTER(rf_shape), vp, i64, C.POINTER(vp), i64,
                                        C.POINTER(rf_layer), i32, vp, vp, sz, vp]),
         "ridgefill_quantize_map": (st, [vp, i64, i64, vp, vp, vp]),
+        "ridgefill_fold_bytes": (sz, [C.POINTER(rf_shape)]),
+        "ridgefill_fold_workspace_bytes": (sz, [C.POINTER(rf_shape)]),
+        "ridgefill_fold_maps": (st, [C.POINTER(rf_shape), C.POINTER(rf_layer), i32,
+                                     C.POINTER(vp), vp, sz, vp]),
         "ridgefill_select_workspace_bytes": (sz, [i64]),
         "ridgefill_select_rows": (st, [vp, i64, i64, vp, vp, vp, sz, vp]),
         "ridgefill_calib_state_bytes": (sz, [i32, i32]),
@@ -204,15 +212,33 @@ def _layers(layers: list[dict]):
     """rf_layer array from dicts of torch tensors: A (bf16 [d][d_in]) or A_q (int8) with
     A_scale (fp32 [d]); b (fp32 [d]); norm_w (bf16 [d]); W_K, W_V (bf16 [kv][d]); k_pages,
     v_pages (bf16 [num_pages][page_size][n_kv][hd]); optional k_norm_w (bf16 [hd]) and
-    v_scale (fp32 [n_kv])."""
+    v_scale (fp32 [n_kv]); or, for a folded layer, folded (uint8 device buffer made by
+    ridgefill_fold_maps) with the pages and the optional parts."""
     arr = (rf_layer * max(len(layers), 1))()
     for i, l in enumerate(layers):
         g = l.get
         arr[i] = rf_layer(_ptr(g("A")), _ptr(g("b")), _ptr(g("norm_w")), _ptr(g("W_K")),
                           _ptr(g("W_V")), _ptr(g("k_pages")), _ptr(g("v_pages")),
                           _ptr(g("k_norm_w")), _ptr(g("v_scale")), _ptr(g("A_q")),
-                          _ptr(g("A_scale")))
+                          _ptr(g("A_scale")), _ptr(g("folded")))
     return arr
+
+
+def ridgefill_fold_bytes(shape: rf_shape) -> int:
+    """Bytes of one layer's folded buffer (0: the shape cannot be folded)."""
+    return int(lib().ridgefill_fold_bytes(C.byref(shape)))
+
+
+def ridgefill_fold_workspace_bytes(shape: rf_shape) -> int:
+    return int(lib().ridgefill_fold_workspace_bytes(C.byref(shape)))
+
+
+def ridgefill_fold_maps(shape: rf_shape, layers: list[dict], folded: list, ws, stream=None) -> None:
+    """Folded buffers (uint8 device tensors, one per layer) from the layers' plain fields."""
+    arr = _layers(layers)
+    ptrs = (C.c_void_p * max(len(folded), 1))(*[_ptr(f) for f in folded])
+    _check(lib().ridgefill_fold_maps(C.byref(shape), arr, len(layers), ptrs, _ptr(ws),
+                                     _nbytes(ws), _stream(stream)))
 
 
 def ridgefill_fill(shape: rf_shape, x_S, N: int, T: int, filled_idx, n_filled: int,
@@ -298,7 +324,7 @@ def ridgefill_read_status(ws, stream=None) -> int:
 
 
 RF_KERNEL_FILL_MAP, RF_KERNEL_FILL_KV, RF_KERNEL_CALIB_MOMENTS, RF_KERNEL_CALIB_SUMS, \
-    RF_KERNEL_SOLVE_MAP = range(5)
+    RF_KERNEL_SOLVE_MAP, RF_KERNEL_FILL_NORM = range(6)
 
 
 def ridgefill_profile_enable(enable: bool) -> None:

@@ -19,8 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libridgefill.so")
 
-SOURCES = ["rf_fill.hip", "rf_calib.hip", "rf_solve.hip", "rf_select.hip", "ridgefill.cpp",
-           "rf_profile.cpp"]
+SOURCES = ["rf_fill.hip", "rf_calib.hip", "rf_solve.hip", "rf_select.hip", "rf_fold.hip",
+           "ridgefill.cpp", "rf_profile.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

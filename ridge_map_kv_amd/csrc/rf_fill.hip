@@ -48,7 +48,10 @@ struct FillKArgs {
   int ntt, nft;                 // token tiles, feature tiles of this launch
   int f_base;                   // first feature tile (norms mode: the V half)
   int has_scale, has_knorm;     // int8 map row scales; per-head key norm
+  int folded;                   // folded layers: kv operands P [2 kv][d_in] and gathered x_S
+  int kdim;                     // reduction length of the kv GEMM: d, or d_in when folded
 };
+static_assert(sizeof(FillKArgs) <= 4096, "kernel arguments must fit in 4 KB");
 
 // Tile order: layer, then groups of kFeatGroup feature tiles (weight rows) swept against
 // every token tile.  Combined with xcd_remap, an XCD's 32 concurrent tiles are a block of
@@ -177,6 +180,74 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
   }
 }
 
+// Folded layers: per row, the sum of squares of (R x_S + r) over one 256-feature tile of the
+// upper-triangular factor R (A^T A = R^T R), written as two 128-feature partials.  Row f of
+// R is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only.
+__global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
+  int g, tt, ft;
+  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  const FillLayerPtrs Lp = a.L[g];
+  const int t0 = tt * kTile, f0 = ft * kTile;
+  const int tid = threadIdx.x;
+
+  DmaOperand Fo, To;
+  {
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
+      const int ce = dma_chunk_elems(r, lane);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in + f0);
+      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
+      const int tok = t0 + r;
+      int row = 0;
+      if (tok < a.n_filled) {
+        const int t = a.idx[tok];
+        if (t >= 0 && t < a.P) row = t;
+      }
+      To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + f0);
+      To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
+    }
+  }
+  __shared__ __attribute__((aligned(16))) float sr[kTile];
+  const float my_r = Lp.b[f0 + tid];
+
+  f32x16 acc[4][4];
+  gemm_pipeline(acc, Fo, To, a.d_in - f0, smem);
+
+  sr[tid] = my_r;
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+  float* ssq = reinterpret_cast<float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + wf * 128 + m * 32 + q * 8 + h * 4);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const float v0 = acc[m][n][q * 4 + 0] + rv.x;
+        const float v1 = acc[m][n][q * 4 + 1] + rv.y;
+        const float v2 = acc[m][n][q * 4 + 2] + rv.z;
+        const float v3 = acc[m][n][q * 4 + 3] + rv.w;
+        ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) ss[n] += __shfl_xor(ss[n], 32);
+  if (h == 0) {
+    const int chunk = (f0 + wf * 128) >> 7;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
+      ssq[(size_t)chunk * a.mpad + tok] = ss[n];
+    }
+  }
+}
+
 // RoPE on one pair of 32-feature MFMA blocks (mlo holds pair index j, mhi holds j + hd/2).
 // cs, sn: this lane's entry for j = 4 h in the blocked tables (row-block of 32 rows, then
 // groups of 4 consecutive j), so pair index j sits (j / 4) * 128 floats further on, and the
@@ -240,10 +311,21 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
       const int ce = dma_chunk_elems(r, lane);
       const int f = f0 + r0;                 // 8-row blocks never straddle K and V (kv % 128 == 0)
       Fo.base[p] = reinterpret_cast<const unsigned char*>(
-          f < a.kv ? Lp.WK + (size_t)f * a.d : Lp.WV + (size_t)(f - a.kv) * a.d);
-      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d + ce) * 2);
-      To.base[p] = reinterpret_cast<const unsigned char*>(hb + (size_t)(t0 + r0) * a.d);
-      To.off[p] = Fo.off[p];
+          f < a.kv ? Lp.WK + (size_t)f * a.kdim : Lp.WV + (size_t)(f - a.kv) * a.kdim);
+      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.kdim + ce) * 2);
+      if (a.folded) {                        // rows of x_S gathered through the index list
+        const int tok = t0 + r;
+        int row = 0;
+        if (tok < a.n_filled) {
+          const int t = a.idx[tok];
+          if (t >= 0 && t < a.P) row = t;
+        }
+        To.base[p] = reinterpret_cast<const unsigned char*>(a.xS);
+        To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
+      } else {
+        To.base[p] = reinterpret_cast<const unsigned char*>(hb + (size_t)(t0 + r0) * a.d);
+        To.off[p] = Fo.off[p];
+      }
     }
   }
 
@@ -254,22 +336,25 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
   __shared__ long long rowoff[kTile];
   __shared__ __attribute__((aligned(16))) float skn[128];
   __shared__ float svs[kTile];
+  __shared__ __attribute__((aligned(16))) float sfc[kTile];
   const float my_r = rs_tab[t0 + tid];
   long long my_off = -1;
-  float my_kn = 1.f, my_vs = 1.f;
+  float my_kn = 1.f, my_vs = 1.f, my_c = 0.f;
   if (MODE == 0) {
     my_off = a.row_slot[t0 + tid];
     if (a.has_knorm && tid < a.hd) my_kn = bf16_to_f32(Lp.kn[tid]);
     if (Lp.vs && tid < a.n_kv) my_vs = Lp.vs[tid];
+    if (a.folded) my_c = Lp.fc[f0 + tid];
   }
 
   f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, a.d, smem);
+  gemm_pipeline(acc, Fo, To, a.kdim, smem);
 
   rstd[tid] = my_r;
   rowoff[tid] = my_off;
   if (tid < 128) skn[tid] = my_kn;
   svs[tid] = my_vs;
+  sfc[tid] = my_c;
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
@@ -300,10 +385,21 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
     const int tl = wt * 128 + n * 32 + (lane & 31);
     const int tok = t0 + tl;
     const float r = rstd[tl];   // rows past n_filled: finite padding, never stored
+    if (a.folded) {             // (P x + c) / rms
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[m][n][e] *= r;
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 cv = *reinterpret_cast<const f32x4*>(sfc + wf * 128 + m * 32 + q * 8 + h * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[m][n][q * 4 + e] = (acc[m][n][q * 4 + e] + cv[e]) * r;
+        }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[m][n][e] *= r;
+    }
     if (isK) {
       if (a.has_knorm) {
         float s0, s1;
@@ -431,6 +527,20 @@ __global__ void rstd_kernel(unsigned char* layer_ws, size_t per_layer, size_t pe
   reinterpret_cast<float*>(lw + per_layer_h + per_layer_ssq)[row] = 1.0f / sqrtf(s / (float)d + eps);
 }
 
+// Folded layers: 1/sqrt((sum of the partials + kappa) / d + eps), d the map's output width.
+__global__ void rstd_folded_kernel(FillKArgs a) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= a.mpad) return;
+  const int g = blockIdx.y;
+  unsigned char* lw = a.layer_ws + (size_t)g * a.per_layer;
+  const float* p = reinterpret_cast<const float*>(lw + a.per_layer_h) + row;
+  float s = 0.f;
+  for (int c = 0; c < a.nchunk; ++c) s += p[(size_t)c * a.mpad];
+  s = fmaxf(s + *a.L[g].kap, 0.f);
+  reinterpret_cast<float*>(lw + a.per_layer_h + a.per_layer_ssq)[row] =
+      1.0f / sqrtf(s / (float)a.d + a.eps);
+}
+
 // int8 map codes as bf16 numbers: |q| <= 127 has at most 8 significant bits, so the bf16
 // value equals the integer exactly (the row scale is applied to the fp32 product).
 __global__ void expand_int8_kernel(const int8_t* q, uint16_t* out, size_t n) {
@@ -541,8 +651,9 @@ FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned 
   L.rope_sin = L.rope_cos + table;
   L.row_slot = L.rope_sin + table;
   L.fixed = L.row_slot + align256((size_t)mpad * sizeof(int64_t));
-  L.per_layer_h = align256((size_t)mpad * d * 2);
-  L.per_layer_ssq = align256((size_t)mpad * (d / 128) * sizeof(float));
+  const bool folded = (flags & kWsFolded) != 0;
+  L.per_layer_h = folded ? 0 : align256((size_t)mpad * d * 2);
+  L.per_layer_ssq = align256((size_t)mpad * ((folded ? d_in : d) / 128) * sizeof(float));
   L.per_layer_rstd = align256((size_t)mpad * sizeof(float));
   const size_t map_elems = (size_t)d * d_in;
   L.expand = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
@@ -569,7 +680,9 @@ FillKArgs fill_args(const FillPlan& p, unsigned char* layer_ws) {
   a.n_kv = p.n_kv;
   a.eps = p.eps;
   a.mpad = p.mpad;
-  a.nchunk = p.d / 128;
+  a.folded = (p.flags & kWsFolded) ? 1 : 0;
+  a.nchunk = (a.folded ? p.d_in : p.d) / 128;
+  a.kdim = a.folded ? p.d_in : p.d;
   a.layer_ws = layer_ws;
   a.per_layer = p.L.per_layer;
   a.per_layer_h = p.L.per_layer_h;
@@ -610,8 +723,22 @@ void expand_group(const FillPlan& p, FillKArgs& a, int G, const int8_t* const* c
 
 // Map GEMM, 1/RMS, K/V GEMM for the G layers in a.L (their maps already on the device).
 hipError_t launch_fill_group(const FillPlan& p, FillKArgs& a, int G, hipStream_t stream) {
-  a.nft = p.d / kTile;
   a.f_base = 0;
+  if (a.folded) {
+    a.nft = p.d_in / kTile;
+    {
+      ProfileScope ps(RF_KERNEL_FILL_NORM, stream);
+      hipLaunchKernelGGL(fill_norm_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    }
+    hipLaunchKernelGGL(rstd_folded_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a);
+    a.nft = 2 * p.kv / kTile;
+    {
+      ProfileScope ps(RF_KERNEL_FILL_KV, stream);
+      hipLaunchKernelGGL(fill_kv_kernel<0>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
+  a.nft = p.d / kTile;
   {
     ProfileScope ps(RF_KERNEL_FILL_MAP, stream);
     hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);

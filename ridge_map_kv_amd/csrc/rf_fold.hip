@@ -1,0 +1,287 @@
+// Folded form of an upper layer on gfx950.
+//
+// Source of the arithmetic: English RidgeFill review (jaehun.me), section "Ridge map:
+// predict the input, and the original projection runs unchanged": x_hat = A x_S + b, then
+// the layer's own RMSNorm (weight w) and its K/V projections (Fig. 2).  The weight and
+// the projections are linear, so they multiply into the map; the only non-linear
+// quantity is the scalar |x_hat|^2, and with R the upper-triangular factor of A^T A
+//     |A x + b|^2 = |R x + r|^2 + kappa,  r = R^-T A^T b,  kappa = |b|^2 - |r|^2
+// (expand |R x + r|^2).  R x costs half of A x.  Per layer:
+//   At  = [A^T | A^T]              bf16 [d_in][2d], a transpose (exact)
+//   Wx  = [W_hi | W_lo]            W = [W_K; W_V] diag(w), each product exact in fp32,
+//                                  split hi = bf16(W), lo = bf16(W - hi) (~2^-17 of W)
+//   P   = Wx At^T = W_hi A + W_lo A   bf16 MFMA, fp32 accumulation, one bf16 rounding
+//   H   = A^T A (lower tiles)      bf16 MFMA: exact products, fp32 accumulation, kept fp64
+//   L   = Cholesky(H)              fp64, the solve's blocked kernels;  R = L^T in bf16
+//   g   = A^T b,  c = W b,  |b|^2  fp64 accumulation in a fixed order
+//   r   = L^-1 g                   blocked forward substitution, fp64
+//   kappa = |b|^2 - |r|^2          fp64
+// One layer at a time through the workspace; every launch on the caller's stream.
+#include "rf_common.h"
+#include "rf_gemm_tile.h"
+#include "rf_internal.h"
+#include "ridgefill.h"
+
+namespace rf {
+
+FoldLayout fold_layout(int d_in, int kv) {
+  FoldLayout F;
+  F.P = 0;
+  F.R = align256((size_t)2 * kv * d_in * 2);
+  F.c = F.R + align256((size_t)d_in * d_in * 2);
+  F.r = F.c + align256((size_t)2 * kv * 4);
+  F.kappa = F.r + align256((size_t)d_in * 4);
+  F.total = F.kappa + 256;
+  return F;
+}
+
+FoldWsLayout fold_ws_layout(int d, int d_in, int kv) {
+  FoldWsLayout W;
+  W.At = kStatusBytes;
+  W.Wx = W.At + align256((size_t)d_in * 2 * d * 2);
+  W.H64 = W.Wx + align256((size_t)2 * kv * 2 * d * 2);
+  W.linv = W.H64 + align256((size_t)d_in * d_in * 8);
+  W.g = W.linv + align256((size_t)d_in * 64 * 8);
+  W.r = W.g + align256((size_t)d_in * 8);
+  W.scal = W.r + align256((size_t)d_in * 8);
+  W.total = W.scal + 256;
+  return W;
+}
+
+namespace {
+
+constexpr int FB = 64;   // substitution block (the Cholesky's diagonal block)
+
+// At[i][k] = At[i][d + k] = A[k][i] through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(256) void fold_transpose_kernel(const uint16_t* A, int d, int d_in,
+                                                             uint16_t* At) {
+  __shared__ uint16_t t[64][66];
+  const int i0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    t[r][c] = A[(size_t)(k0 + r) * d_in + i0 + c];
+  }
+  __syncthreads();
+  const size_t ld = (size_t)2 * d;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;   // r: i within the tile, c: k within the tile
+    const uint16_t v = t[c][r];
+    At[(size_t)(i0 + r) * ld + k0 + c] = v;
+    At[(size_t)(i0 + r) * ld + d + k0 + c] = v;
+  }
+}
+
+// Wx[i] = [hi | lo] of row i of [W_K; W_V] diag(w).
+__global__ void fold_wsplit_kernel(const uint16_t* WK, const uint16_t* WV, const uint16_t* w,
+                                   int kv, int d, uint16_t* Wx) {
+  const size_t n = (size_t)2 * kv * d;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int i = (int)(e / d), k = (int)(e - (size_t)i * d);
+    const uint16_t wb = i < kv ? WK[(size_t)i * d + k] : WV[(size_t)(i - kv) * d + k];
+    const float v = bf16_to_f32(wb) * bf16_to_f32(w[k]);          // exact: 8 x 8 bits
+    const uint32_t hi = f32_to_bf16(v);
+    const uint32_t lo = f32_to_bf16(v - bf16_to_f32(hi));         // v - hi exact in fp32
+    Wx[(size_t)i * 2 * d + k] = (uint16_t)hi;
+    Wx[(size_t)i * 2 * d + d + k] = (uint16_t)lo;
+  }
+}
+
+// out[m][n] = sum_k F[m][k] T[n][k] for 256 x 256 tiles (F, T bf16 rows, K a multiple of
+// 64); bf16 (mode 0) or fp64 (mode 1) output.  With `lower`, only tiles n <= m.
+struct NtGemmArgs {
+  const uint16_t* F;
+  const uint16_t* T;
+  void* out;
+  int64_t ldf, ldt, ldo;
+  int K, ntm, ntn, mode, lower;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void fold_gemm_kernel(NtGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
+  const int tile = blockIdx.x;
+  const int mt = tile / a.ntn, nt = tile - mt * a.ntn;
+  if (a.lower && nt > mt) return;                 // whole block, before any barrier
+  const int m0 = mt * kTile, n0 = nt * kTile;
+  const int tid = threadIdx.x;
+  DmaOperand Fo, To;
+  {
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r0 = dma_block_row(p, wave), rr = r0 + dma_lane_row(lane);
+      const int ce = dma_chunk_elems(rr, lane);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(a.F + (size_t)(m0 + r0) * a.ldf);
+      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.ldf + ce) * 2);
+      To.base[p] = reinterpret_cast<const unsigned char*>(a.T + (size_t)(n0 + r0) * a.ldt);
+      To.off[p] = (uint32_t)((dma_lane_row(lane) * a.ldt + ce) * 2);
+    }
+  }
+  f32x16 acc[4][4];
+  gemm_pipeline(acc, Fo, To, a.K, smem);
+  const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const size_t col = (size_t)n0 + wt * 128 + n * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const size_t row = (size_t)m0 + wf * 128 + m * 32 + q * 8 + h * 4 + e;
+          const float v = acc[m][n][q * 4 + e];
+          if (a.mode == 0)
+            reinterpret_cast<uint16_t*>(a.out)[row * a.ldo + col] = (uint16_t)f32_to_bf16(v);
+          else
+            reinterpret_cast<double*>(a.out)[row * a.ldo + col] = (double)v;
+        }
+    }
+}
+
+// One wave per output: rows 0 .. d_in-1 give g[i] = sum_k A[k][i] b[k] (from At), rows
+// d_in .. d_in + 2kv - 1 give c[j] = sum_k W[j][k] w[k] b[k]; lane-strided fp64 partial
+// sums, then a fixed xor tree.
+__global__ __launch_bounds__(256) void fold_gemv_kernel(const uint16_t* At, const uint16_t* WK,
+                                                        const uint16_t* WV, const uint16_t* w,
+                                                        const float* b, int d, int d_in, int kv,
+                                                        double* g, float* c) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= d_in + 2 * kv) return;
+  double s = 0.0;
+  if (row < d_in) {
+    const uint16_t* a = At + (size_t)row * 2 * d;
+    for (int k = lane; k < d; k += 64) s += (double)bf16_to_f32(a[k]) * (double)b[k];
+  } else {
+    const int j = row - d_in;
+    const uint16_t* wr = j < kv ? WK + (size_t)j * d : WV + (size_t)(j - kv) * d;
+    for (int k = lane; k < d; k += 64)
+      s += (double)(bf16_to_f32(wr[k]) * bf16_to_f32(w[k])) * (double)b[k];
+  }
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) {
+    if (row < d_in) g[row] = s;
+    else c[row - d_in] = (float)s;
+  }
+}
+
+// scal[0] = |b|^2 (fixed-order tree).
+__global__ __launch_bounds__(1024) void fold_bb_kernel(const float* b, int d, double* scal) {
+  __shared__ double part[1024];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  for (int i = t; i < d; i += 1024) s += (double)b[i] * (double)b[i];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (t < o) part[t] += part[t + o];
+    __syncthreads();
+  }
+  if (t == 0) scal[0] = part[0];
+}
+
+// Block row i of L r = g:  y = g_i - sum_{k < 64 i} L[64 i + row][k] r[k] (four threads per
+// row, strided, combined in a fixed order), then r_i = Linv_ii y.
+__global__ __launch_bounds__(256) void fold_fsub_kernel(const double* L, int d, int i,
+                                                        const double* linv, const double* g,
+                                                        double* r) {
+  __shared__ double part[FB][4];
+  __shared__ double y[FB];
+  const int t = threadIdx.x, row = t >> 2, q = t & 3;
+  const double* Lr = L + (size_t)(i * FB + row) * d;
+  double s = 0.0;
+  for (int k = q; k < i * FB; k += 4) s += Lr[k] * r[k];
+  part[row][q] = s;
+  __syncthreads();
+  if (t < FB) y[t] = g[i * FB + t] - (((part[t][0] + part[t][1]) + part[t][2]) + part[t][3]);
+  __syncthreads();
+  if (t < FB) {
+    const double* li = linv + (size_t)i * FB * FB + (size_t)t * FB;
+    double v = 0.0;
+    for (int j = 0; j <= t; ++j) v += li[j] * y[j];
+    r[i * FB + t] = v;
+  }
+}
+
+// r to fp32, kappa = |b|^2 - |r|^2 (fixed-order tree).
+__global__ __launch_bounds__(1024) void fold_finish_kernel(const double* r, const double* scal,
+                                                           int d_in, float* r_out,
+                                                           float* kappa_out) {
+  __shared__ double part[1024];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  for (int i = t; i < d_in; i += 1024) {
+    s += r[i] * r[i];
+    r_out[i] = (float)r[i];
+  }
+  part[t] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (t < o) part[t] += part[t + o];
+    __syncthreads();
+  }
+  if (t == 0) *kappa_out = (float)(scal[0] - part[0]);
+}
+
+// R[f][k] = bf16(L[k][f]) for k >= f, 0 below the diagonal, through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(256) void fold_rt_kernel(const double* L, int d_in, uint16_t* R) {
+  __shared__ double t[64][65];
+  const int f0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const bool zero = k0 < f0;                      // the whole tile is below the diagonal
+  if (!zero) {
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63;           // r: k, c: f
+      t[r][c] = L[(size_t)(k0 + r) * d_in + f0 + c];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;             // r: f, c: k
+    const int f = f0 + r, k = k0 + c;
+    R[(size_t)f * d_in + k] = (!zero && k >= f) ? (uint16_t)f32_to_bf16((float)t[c][r]) : 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fold(int d, int d_in, int kv, const uint16_t* A, const float* b,
+                       const uint16_t* w, const uint16_t* WK, const uint16_t* WV, void* out,
+                       void* ws, hipStream_t stream) {
+  const FoldLayout F = fold_layout(d_in, kv);
+  const FoldWsLayout W = fold_ws_layout(d, d_in, kv);
+  unsigned char* o = static_cast<unsigned char*>(out);
+  unsigned char* s = static_cast<unsigned char*>(ws);
+  unsigned* status = reinterpret_cast<unsigned*>(s);
+  uint16_t* At = reinterpret_cast<uint16_t*>(s + W.At);
+  uint16_t* Wx = reinterpret_cast<uint16_t*>(s + W.Wx);
+  double* H = reinterpret_cast<double*>(s + W.H64);
+  double* linv = reinterpret_cast<double*>(s + W.linv);
+  double* g = reinterpret_cast<double*>(s + W.g);
+  double* r = reinterpret_cast<double*>(s + W.r);
+  double* scal = reinterpret_cast<double*>(s + W.scal);
+
+  hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream, A, d,
+                     d_in, At);
+  hipLaunchKernelGGL(fold_wsplit_kernel, dim3(2048), dim3(256), 0, stream, WK, WV, w, kv, d, Wx);
+  NtGemmArgs pa = {Wx, At, o + F.P, 2 * (int64_t)d, 2 * (int64_t)d, d_in, 2 * d,
+                   2 * kv / kTile, d_in / kTile, 0, 0};
+  hipLaunchKernelGGL(fold_gemm_kernel, dim3(pa.ntm * pa.ntn), dim3(kThreads), 0, stream, pa);
+  NtGemmArgs ha = {At, At, H, 2 * (int64_t)d, 2 * (int64_t)d, d_in, d, d_in / kTile,
+                   d_in / kTile, 1, 1};
+  hipLaunchKernelGGL(fold_gemm_kernel, dim3(ha.ntm * ha.ntn), dim3(kThreads), 0, stream, ha);
+  hipLaunchKernelGGL(fold_gemv_kernel, dim3((d_in + 2 * kv + 3) / 4), dim3(256), 0, stream, At,
+                     WK, WV, w, b, d, d_in, kv, g, reinterpret_cast<float*>(o + F.c));
+  hipLaunchKernelGGL(fold_bb_kernel, dim3(1), dim3(1024), 0, stream, b, d, scal);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_cholesky(H, d_in, linv, status, stream)) != hipSuccess) return e;
+  for (int i = 0; i < d_in / FB; ++i)
+    hipLaunchKernelGGL(fold_fsub_kernel, dim3(1), dim3(256), 0, stream, H, d_in, i, linv, g, r);
+  hipLaunchKernelGGL(fold_finish_kernel, dim3(1), dim3(1024), 0, stream, r, scal, d_in,
+                     reinterpret_cast<float*>(o + F.r), reinterpret_cast<float*>(o + F.kappa));
+  hipLaunchKernelGGL(fold_rt_kernel, dim3(d_in / 64, d_in / 64), dim3(256), 0, stream, H, d_in,
+                     reinterpret_cast<uint16_t*>(o + F.R));
+  return hipGetLastError();
+}
+
+}  // namespace rf

@@ -17,6 +17,9 @@ constexpr unsigned kStatusScoreBit = 4u;     // a selection score was NaN
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// One layer of a fill launch.  Plain maps use A, b, w, WK, WV.  A folded layer (kWsFolded)
+// puts its triangular factor R [d_in][d_in] in A, r [d_in] in b, the K and V halves of
+// P in WK and WV (rows of d_in), c [2 kv] in fc and kappa in kap; w is unused.
 struct FillLayerPtrs {
   const uint16_t* A;            // bf16 map (for an int8 map: its expansion in the workspace)
   const float* b;
@@ -29,11 +32,34 @@ struct FillLayerPtrs {
   const float* vs;              // value-rescale factors [n_kv] or null
   const int8_t* Aq;             // int8 map codes or null
   const float* As;              // int8 map row scales
+  const float* fc;              // folded: c
+  const float* kap;             // folded: kappa
 };
 
 // Workspace variants of a fill call.
 constexpr unsigned kWsInt8 = 1u;       // int8 maps: a bf16 expansion area per layer
 constexpr unsigned kWsStreamed = 2u;   // host maps: two landing slots per layer
+constexpr unsigned kWsFolded = 4u;     // folded layers: no predicted-input buffer
+
+// Folded form of one layer in its caller-owned buffer (byte offsets): P bf16 [2 kv][d_in],
+// R bf16 [d_in][d_in] (upper triangle, zeros below), c fp32 [2 kv], r fp32 [d_in],
+// kappa fp32.
+struct FoldLayout {
+  size_t P, R, c, r, kappa, total;
+};
+FoldLayout fold_layout(int d_in, int kv);
+
+// Workspace of the fold (one layer at a time): [A^T | A^T] and [W_hi | W_lo] in bf16,
+// A^T A in fp32 and fp64, the diagonal-block inverses, A^T b and r in fp64, |b|^2.
+struct FoldWsLayout {
+  size_t At, Wx, H32, H64, linv, g, r, scal, total;
+};
+FoldWsLayout fold_ws_layout(int d, int d_in, int kv);
+// Per layer: A bf16 [d][d_in], b fp32 [d], w bf16 [d], W_K / W_V bf16 [kv][d] -> the
+// folded buffer.  A non-positive pivot of A^T A sets kStatusNotSpdBit.
+hipError_t launch_fold(int d, int d_in, int kv, const uint16_t* A, const float* b,
+                       const uint16_t* w, const uint16_t* WK, const uint16_t* WV, void* out,
+                       void* ws, hipStream_t stream);
 
 // Workspace layout of a fill call (bytes from the start of ws; per-layer offsets from the
 // start of that layer's block).
@@ -45,7 +71,7 @@ FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned 
 
 struct FillPlan {
   int d, d_in, n_kv, hd, kv;
-  unsigned flags;               // kWsInt8 | kWsStreamed
+  unsigned flags;               // kWsInt8 | kWsStreamed | kWsFolded
   int has_knorm;
   float eps;
   double theta;
@@ -107,6 +133,11 @@ SolveLayout solve_layout(int d_in, int d_out, int n_layers);
 hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, double lambda,
                         float* A_out, float* b_out, uint16_t* A_bf16, void* ws,
                         hipStream_t stream);
+
+// Blocked fp64 Cholesky of the lower triangle of C [d][d] (d a multiple of 64), in place:
+// C's lower triangle becomes L (C = L L^T) and linv [d/64][64][64] the inverses of L's
+// 64 x 64 diagonal blocks.  A non-positive pivot sets kStatusNotSpdBit in *status.
+hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream);
 
 hipError_t launch_clear_status(unsigned* status, hipStream_t stream);
 

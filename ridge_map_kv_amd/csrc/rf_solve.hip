@@ -488,6 +488,20 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
 
 }  // namespace
 
+hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream) {
+  const int nbk = d / NB;
+  for (int k = 0; k < nbk; ++k) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, C, d, k, linv, status);
+    const int below = nbk - k - 1;
+    if (below > 0) {
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(below), dim3(256), 0, stream, C, d, k, linv);
+      hipLaunchKernelGGL(chol_update_kernel, dim3(below * (below + 1) / 2), dim3(256), 0, stream,
+                         C, d, k);
+    }
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, double lambda,
                         float* A_out, float* b_out, uint16_t* A_bf16, void* ws,
                         hipStream_t stream) {
@@ -518,15 +532,7 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
                      CL.sum_S, mu, w);
   hipLaunchKernelGGL(centre_kernel, dim3(gdd), dim3(256), 0, stream, G, mu, w, d, C);
   hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
-  for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, C, d, k, linv, status);
-    const int below = nbk - k - 1;
-    if (below > 0) {
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(below), dim3(256), 0, stream, C, d, k, linv);
-      hipLaunchKernelGGL(chol_update_kernel, dim3(below * (below + 1) / 2), dim3(256), 0, stream,
-                         C, d, k);
-    }
-  }
+  if ((e = launch_cholesky(C, d, linv, status, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(identity_kernel, dim3(gdd), dim3(256), 0, stream, W, d);
   for (int i = 0; i < nbk; ++i) {
     hipLaunchKernelGGL(fsub_rows_kernel, dim3(i + 1), dim3(256), 0, stream, W, d, i, linv);

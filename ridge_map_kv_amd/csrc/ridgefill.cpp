@@ -65,7 +65,19 @@ rf_status check_shape(const rf_shape* s) {
 int d_in_of(const rf_shape* s) { return s->d_in ? s->d_in : s->d; }
 
 unsigned map_flags_of(int32_t f) {
-  return ((f & RF_MAPS_INT8) ? rf::kWsInt8 : 0u) | ((f & RF_MAPS_STREAMED) ? rf::kWsStreamed : 0u);
+  return ((f & RF_MAPS_INT8) ? rf::kWsInt8 : 0u) | ((f & RF_MAPS_STREAMED) ? rf::kWsStreamed : 0u) |
+         ((f & RF_MAPS_FOLDED) ? rf::kWsFolded : 0u);
+}
+
+// A folded form needs A^T A positive definite (d_in <= d) and whole 256-wide tiles of R.
+rf_status check_foldable(const rf_shape* s) {
+  const int d_in = d_in_of(s);
+  if (d_in > s->d)
+    return fail(RF_E_SHAPE, "d_in = %d > d = %d: A^T A is singular, the map cannot be folded",
+                d_in, s->d);
+  if (d_in % rf::kTile)
+    return fail(RF_E_SHAPE, "folded maps need d_in (%d) to be a multiple of %d", d_in, rf::kTile);
+  return RF_OK;
 }
 
 // Checks shared by the resident and the streamed fill; fills the plan and the layer
@@ -90,10 +102,29 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
     return fail(RF_E_SHAPE, "block table has %lld pages, the prefix needs %lld",
                 (long long)kv->n_logical, (long long)((P + kv->page_size - 1) / kv->page_size));
   if (!aligned(ws, 256)) return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned");
-  const bool int8 = layers[0].A_q != nullptr;
+  const bool folded = layers[0].folded != nullptr;
+  const bool int8 = !folded && layers[0].A_q != nullptr;
   const bool knorm = layers[0].k_norm_w != nullptr;
+  if (folded) {
+    rf_status fs = check_foldable(shape);
+    if (fs != RF_OK) return fs;
+    if (streamed)
+      return fail(RF_E_UNSUPPORTED, "folded layers are not supported by the streamed fill");
+  }
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
+    if ((l.folded != nullptr) != folded)
+      return fail(RF_E_INVALID, "layer %d: all layers of a call must be folded or none", i);
+    if ((l.k_norm_w != nullptr) != knorm)
+      return fail(RF_E_INVALID, "layer %d: all layers of a call must have a key norm or none", i);
+    if (folded) {
+      if (!l.k_pages || !l.v_pages) return fail(RF_E_INVALID, "layer %d has a null page pool", i);
+      if (!aligned(l.folded, 256) || !aligned(l.k_pages, 8) || !aligned(l.v_pages, 8) ||
+          (l.v_scale && !aligned(l.v_scale, 4)) || (l.k_norm_w && !aligned(l.k_norm_w, 2)))
+        return fail(RF_E_SHAPE, "layer %d: the folded buffer needs 256-byte, the pages 8-byte "
+                    "alignment", i);
+      continue;
+    }
     if (!l.b || !l.norm_w || !l.W_K || !l.W_V || !l.k_pages || !l.v_pages)
       return fail(RF_E_INVALID, "layer %d has a null pointer", i);
     if ((l.A != nullptr) == (l.A_q != nullptr))
@@ -101,8 +132,6 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
     if ((l.A_q != nullptr) != int8)
       return fail(RF_E_INVALID, "layer %d: all layers of a call must use bf16 maps or all int8", i);
     if (int8 && !l.A_scale) return fail(RF_E_INVALID, "layer %d: A_q without A_scale", i);
-    if ((l.k_norm_w != nullptr) != knorm)
-      return fail(RF_E_INVALID, "layer %d: all layers of a call must have a key norm or none", i);
     if ((l.A && !aligned(l.A, 16)) || (l.A_q && !aligned(l.A_q, 16)) || !aligned(l.b, 16) ||
         !aligned(l.norm_w, 8) || !aligned(l.W_K, 16) || !aligned(l.W_V, 16) ||
         !aligned(l.k_pages, 8) || !aligned(l.v_pages, 8) ||
@@ -111,7 +140,8 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
       return fail(RF_E_SHAPE, "layer %d: A, A_q, b, W_K, W_V need 16-byte, norm_w and the pages "
                   "8-byte alignment", i);
   }
-  const unsigned flags = (int8 ? rf::kWsInt8 : 0u) | (streamed ? rf::kWsStreamed : 0u);
+  const unsigned flags = (int8 ? rf::kWsInt8 : 0u) | (streamed ? rf::kWsStreamed : 0u) |
+                         (folded ? rf::kWsFolded : 0u);
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim, n_filled, flags);
   if (ws_bytes < L.fixed + L.per_layer)
     return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed for one layer", ws_bytes,
@@ -150,10 +180,20 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
   p.L = L;
 
   lp.resize((size_t)n_layers);
+  const rf::FoldLayout F = rf::fold_layout(d_in, p.kv);
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
-    lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.k_pages, l.v_pages,
-             l.k_norm_w, l.v_scale, l.A_q, l.A_scale};
+    if (folded) {
+      const unsigned char* f = static_cast<const unsigned char*>(l.folded);
+      const uint16_t* P = reinterpret_cast<const uint16_t*>(f + F.P);
+      lp[i] = {reinterpret_cast<const uint16_t*>(f + F.R), reinterpret_cast<const float*>(f + F.r),
+               nullptr, P, P + (size_t)p.kv * d_in, l.k_pages, l.v_pages, l.k_norm_w, l.v_scale,
+               nullptr, nullptr, reinterpret_cast<const float*>(f + F.c),
+               reinterpret_cast<const float*>(f + F.kappa)};
+    } else {
+      lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.k_pages, l.v_pages,
+               l.k_norm_w, l.v_scale, l.A_q, l.A_scale, nullptr, nullptr};
+    }
   }
   return RF_OK;
 }
@@ -223,7 +263,10 @@ rf_status ridgefill_partition(int64_t N, int64_t T, const uint8_t* exact_mask,
 size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled,
                                          int32_t n_layers, int32_t map_flags) {
   if (check_shape(shape) != RF_OK || n_filled < 0 || n_layers < 1 ||
-      (map_flags & ~(RF_MAPS_INT8 | RF_MAPS_STREAMED)))
+      (map_flags & ~(RF_MAPS_INT8 | RF_MAPS_STREAMED | RF_MAPS_FOLDED)))
+    return 0;
+  if ((map_flags & RF_MAPS_FOLDED) &&
+      ((map_flags & (RF_MAPS_INT8 | RF_MAPS_STREAMED)) || check_foldable(shape) != RF_OK))
     return 0;
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim,
                                                 n_filled, map_flags_of(map_flags));
@@ -494,6 +537,49 @@ rf_status ridgefill_read_status(void* ws, void* stream) {
   if (word & rf::kStatusRowsBit) return fail(RF_E_ROWS, "device flagged filled-row indices");
   if (word & rf::kStatusNotSpdBit) return fail(RF_E_NOT_SPD, "device flagged a non-positive pivot");
   if (word & rf::kStatusScoreBit) return fail(RF_E_INVALID, "device flagged a NaN selection score");
+  return ok();
+}
+
+size_t ridgefill_fold_bytes(const rf_shape* shape) {
+  if (check_shape(shape) != RF_OK || check_foldable(shape) != RF_OK) return 0;
+  return rf::fold_layout(d_in_of(shape), shape->n_kv_heads * shape->head_dim).total;
+}
+
+size_t ridgefill_fold_workspace_bytes(const rf_shape* shape) {
+  if (check_shape(shape) != RF_OK || check_foldable(shape) != RF_OK) return 0;
+  return rf::fold_ws_layout(shape->d, d_in_of(shape), shape->n_kv_heads * shape->head_dim).total;
+}
+
+rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int32_t n_layers,
+                              void* const* folded, void* ws, size_t ws_bytes, void* stream) {
+  rf_status s = check_shape(shape);
+  if (s != RF_OK) return s;
+  if ((s = check_foldable(shape)) != RF_OK) return s;
+  if (n_layers < 0) return fail(RF_E_INVALID, "n_layers < 0");
+  if (n_layers > 0 && (!layers || !folded)) return fail(RF_E_INVALID, "layers or folded is NULL");
+  if (!ws) return fail(RF_E_INVALID, "ws is NULL");
+  const int d = shape->d, d_in = d_in_of(shape), kv = shape->n_kv_heads * shape->head_dim;
+  const rf::FoldWsLayout W = rf::fold_ws_layout(d, d_in, kv);
+  if (!aligned(ws, 256) || ws_bytes < W.total)
+    return fail(RF_E_WORKSPACE, "fold workspace must be 256-byte aligned and >= %zu bytes", W.total);
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    if (l.A_q) return fail(RF_E_UNSUPPORTED, "layer %d: int8 maps cannot be folded", i);
+    if (!l.A || !l.b || !l.norm_w || !l.W_K || !l.W_V || !folded[i])
+      return fail(RF_E_INVALID, "layer %d: A, b, norm_w, W_K, W_V and its folded buffer are needed", i);
+    if (!aligned(l.A, 16) || !aligned(l.W_K, 16) || !aligned(l.W_V, 16) || !aligned(l.b, 4) ||
+        !aligned(l.norm_w, 2) || !aligned(folded[i], 256))
+      return fail(RF_E_SHAPE, "layer %d: A, W_K, W_V need 16-byte, the folded buffer 256-byte "
+                  "alignment", i);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws), st);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    e = rf::launch_fold(d, d_in, kv, l.A, l.b, l.norm_w, l.W_K, l.W_V, folded[i], ws, st);
+    if (e != hipSuccess) return hip_fail(e, "fold launch");
+  }
   return ok();
 }
 

@@ -119,17 +119,70 @@ def host_maps(layers: list[dict]) -> list[dict]:
     return out
 
 
+def fold_offsets(case: Case):
+    """Byte offsets of P, R, c, r and kappa in one layer's folded buffer: the sections in
+    that order, each starting on a 256-byte boundary."""
+    a = lambda x: (x + 255) // 256 * 256
+    kv2, din = 2 * case.kv, case.width
+    R = a(kv2 * din * 2)
+    c = R + a(din * din * 2)
+    r = c + a(kv2 * 4)
+    return 0, R, c, r, r + a(din * 4)
+
+
+def fold_layers(case: Case, inp, stream=None):
+    """Folded buffers of every layer (cached in inp["folded"]) and the fold's status."""
+    dev = inp["xS"].device
+    shape = make_shape(case)
+    nb = B.ridgefill_fold_bytes(shape)
+    assert nb > 0
+    ws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    bufs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
+    B.ridgefill_fold_maps(shape, inp["layers"], bufs, ws, stream)
+    status = B.ridgefill_read_status(ws, stream)
+    inp["folded"] = bufs
+    return bufs, status
+
+
+def fold_views(case: Case, buf: torch.Tensor):
+    """(P, R, c, r, kappa) of a folded buffer, as float64 numpy values."""
+    oP, oR, oc, orr, ok = fold_offsets(case)
+    kv2, din = 2 * case.kv, case.width
+    b = buf.cpu()
+    P = b[oP:oP + kv2 * din * 2].view(torch.bfloat16).float().numpy().reshape(kv2, din)
+    R = b[oR:oR + din * din * 2].view(torch.bfloat16).float().numpy().reshape(din, din)
+    c = b[oc:oc + kv2 * 4].view(torch.float32).numpy()
+    r = b[orr:orr + din * 4].view(torch.float32).numpy()
+    kappa = float(b[ok:ok + 4].view(torch.float32).item())
+    return (P.astype(np.float64), R.astype(np.float64), c.astype(np.float64),
+            r.astype(np.float64), kappa)
+
+
+def folded_layer_dicts(inp):
+    keep = ("k_pages", "v_pages", "k_norm_w", "v_scale")
+    return [dict({k: lay[k] for k in keep if k in lay}, folded=buf)
+            for lay, buf in zip(inp["layers"], inp["folded"])]
+
+
 def run_fill(case: Case, inp, filled: np.ndarray, ws_layers: int | None = None, stream=None,
-             streamed: bool = False):
+             streamed: bool = False, folded: bool = False):
     dev = inp["xS"].device
     shape = make_shape(case)
     nf = int(filled.size)
     idx = torch.from_numpy(np.asarray(filled, dtype=np.int32)).to(dev)
     flags = case.map_flags | (B.RF_MAPS_STREAMED if streamed else 0)
+    if folded:
+        flags = B.RF_MAPS_FOLDED
+        if "folded" not in inp:
+            _, st = fold_layers(case, inp, stream)
+            assert st == B.RF_OK, f"fold status {st}"
     nbytes = B.ridgefill_fill_workspace_bytes(shape, max(nf, 1),
                                               ws_layers if ws_layers else case.n_layers, flags)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    if streamed:
+    if folded:
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, folded_layer_dicts(inp),
+                         inp["table"], case.page_size, inp["num_pages"], ws, stream=stream)
+    elif streamed:
         layers = host_maps(inp["layers"])
         copy = torch.cuda.Stream()
         B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, layers, inp["table"],

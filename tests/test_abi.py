@@ -111,3 +111,29 @@ def test_calib_and_solve_reject_bad_arguments():
 def test_status_strings():
     for s in range(8):
         assert B.ridgefill_status_string(s)
+
+
+def test_fold_size_queries_and_errors():
+    L = B.lib()
+    s = B.make_shape(4096, 8, 128)
+    fb = B.ridgefill_fold_bytes(s)
+    # P [2 kv][d_in] and R [d_in][d_in] in bf16, c, r and kappa in fp32
+    assert fb >= (2 * 1024 * 4096 + 4096 * 4096) * 2 + (2 * 1024 + 4096 + 1) * 4
+    assert fb % 256 == 0
+    assert B.ridgefill_fold_workspace_bytes(s) >= 4096 * 4096 * 8
+    # no predicted-input buffer: a folded fill's per-layer workspace is small
+    f1 = B.ridgefill_fill_workspace_bytes(s, 25805, 1, B.RF_MAPS_FOLDED)
+    f20 = B.ridgefill_fill_workspace_bytes(s, 25805, 20, B.RF_MAPS_FOLDED)
+    assert 0 < (f20 - f1) // 19 < 25856 * 4096 // 8
+    # wide maps (d_in > d) and ragged d_in cannot be folded
+    wide = B.make_shape(4096, 8, 128, d_in=8192)
+    assert B.ridgefill_fold_bytes(wide) == 0 and B.ridgefill_fold_workspace_bytes(wide) == 0
+    assert B.ridgefill_fill_workspace_bytes(wide, 100, 1, B.RF_MAPS_FOLDED) == 0
+    assert B.ridgefill_fold_bytes(B.make_shape(4096, 8, 128, d_in=4032)) == 0
+    assert B.ridgefill_fill_workspace_bytes(s, 100, 1, B.RF_MAPS_FOLDED | B.RF_MAPS_INT8) == 0
+    assert B.ridgefill_fill_workspace_bytes(s, 100, 1, B.RF_MAPS_FOLDED | B.RF_MAPS_STREAMED) == 0
+    arr = (B.rf_layer * 1)()
+    assert L.ridgefill_fold_maps(C.byref(wide), arr, 1, None, None, 0, None) == B.RF_E_SHAPE
+    assert L.ridgefill_fold_maps(C.byref(s), arr, 1, None, None, 0, None) == B.RF_E_INVALID
+    assert L.ridgefill_fold_maps(C.byref(s), arr, 0, None, None, 0, None) == B.RF_E_INVALID
+    assert L.ridgefill_last_error()

@@ -1,0 +1,156 @@
+"""GPU parity of folded layers, through the C ABI.
+
+ridgefill_fold_maps against the oracle's fold_map on the same bf16/fp32 values:
+  P (one bf16 rounding of a product held to ~2^-17) and R (bf16 of an fp64 Cholesky
+  factor of an fp32-accumulated A^T A): relative Frobenius error <= 2e-3 (a bf16
+  rounding's own error is about 1.1e-3 rms); R's strict lower triangle exactly zero;
+  c (fp64 accumulation, fp32 result): 1e-6; r (fp64 substitution on the fp32-accumulated
+  Gram): 1e-4; kappa within 1e-4 |b|^2.
+The fill of folded layers against the oracle's plain fill_rows (the method's own flow),
+the same bar as every fill: bit-exact routing on sentinel-filled caches, K and V within
+a relative Frobenius error of 5e-3 per layer."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ridge_map_kv_amd import binding as B
+
+from fillcase import (Case, bf16_np, build_inputs, check_routing, check_values, fold_layers,
+                      fold_views, folded_layer_dicts, make_shape, rel_fro, run_fill, to_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(d, nl, nkv, hd, N, T, ne, ps, seed, **kw):
+    g = np.random.default_rng(seed)
+    exact = np.sort(g.choice(N - T, size=ne, replace=False)) if ne else np.zeros(0, np.int64)
+    return Case(d=d, n_layers=nl, n_kv=nkv, hd=hd, N=N, T=T, exact=exact, page_size=ps,
+                seed=seed, **kw)
+
+
+def _filled(case):
+    f, _, _ = oracle.partition(case.N, case.T, case.exact)
+    return f
+
+
+def _oracle_fold(case, inp, l):
+    lay = inp["layers"][l]
+    return oracle.fold_map(bf16_np(lay["A"]), lay["b"].cpu().numpy().astype(np.float64),
+                           bf16_np(lay["norm_w"]), bf16_np(lay["W_K"]), bf16_np(lay["W_V"]))
+
+
+FOLDS = [
+    # d, layers, n_kv, hd, seed, options
+    (512, 2, 2, 128, 51, {}),
+    (768, 1, 4, 64, 52, dict(d_in=512)),        # tall map: kappa > 0
+    (256, 1, 2, 64, 53, dict(map_kind="identity")),
+]
+
+
+@pytest.mark.parametrize("d,nl,nkv,hd,seed,opts", FOLDS)
+def test_fold_outputs_vs_oracle(d, nl, nkv, hd, seed, opts):
+    case = _case(d, nl, nkv, hd, 300, 20, 0, 16, seed, **opts)
+    inp = build_inputs(case)
+    print(f"\nfold d={d} d_in={case.width} kv={case.kv} {opts}", flush=True)
+    bufs, st = fold_layers(case, inp)
+    assert st == B.RF_OK
+    for l in range(nl):
+        P, R, c, r, kappa = fold_views(case, bufs[l])
+        Po, co, Ro, ro, ko = _oracle_fold(case, inp, l)
+        b = inp["layers"][l]["b"].cpu().numpy().astype(np.float64)
+        eP, eR, ec, er = rel_fro(P, Po), rel_fro(R, Ro), rel_fro(c, co), rel_fro(r, ro)
+        print(f"  layer {l}: P {eP:.2e} R {eR:.2e} c {ec:.2e} r {er:.2e} kappa {kappa:.3e} "
+              f"(oracle {ko:.3e})", flush=True)
+        assert eP <= 2e-3 and eR <= 2e-3 and ec <= 1e-6 and er <= 1e-4
+        assert np.all(np.tril(R, -1) == 0.0)
+        assert abs(kappa - ko) <= 1e-4 * (b @ b)
+        if opts.get("map_kind") == "identity":
+            assert np.array_equal(R, np.eye(case.width))          # Cholesky of I is exact
+            assert kappa == 0.0
+
+
+FILLS = [
+    # d, layers, n_kv, hd, N, T, n_exact, page, seed, options
+    (512, 3, 2, 128, 700, 100, 60, 16, 61, {}),
+    (512, 2, 2, 128, 700, 100, 60, 16, 62, dict(knorm=True, vscale=True)),
+    (768, 2, 4, 64, 333, 33, 17, 8, 63, dict(knorm=True)),
+    (768, 2, 4, 64, 600, 40, 25, 16, 64, dict(d_in=512, vscale=True)),     # tall map
+    (256, 2, 2, 64, 1100, 60, 300, 16, 65, {}),                           # ragged tiles
+    (256, 1, 2, 128, 300, 20, 10, 16, 66, dict(map_kind="identity")),
+]
+
+
+@pytest.mark.parametrize("d,nl,nkv,hd,N,T,ne,ps,seed,opts", FILLS)
+def test_folded_fill_parity(d, nl, nkv, hd, N, T, ne, ps, seed, opts):
+    case = _case(d, nl, nkv, hd, N, T, ne, ps, seed, **opts)
+    inp = build_inputs(case)
+    f = _filled(case)
+    print(f"\nfolded fill d={d} d_in={case.width} hd={hd} rows={f.size} {opts}", flush=True)
+    assert run_fill(case, inp, f, folded=True) == B.RF_OK
+    check_routing(case, inp, f)
+    worst = check_values(case, inp, f)
+    print(f"  worst rel {worst:.2e}", flush=True)
+
+
+def test_folded_and_plain_fills_agree():
+    # the two GPU paths on the same inputs: both are within 5e-3 of the oracle, and
+    # their difference is of the order of one bf16 rounding
+    case = _case(512, 2, 2, 128, 700, 100, 60, 16, 67, knorm=True)
+    f = _filled(case)
+    a = build_inputs(case)
+    b = build_inputs(case)
+    assert run_fill(case, a, f) == B.RF_OK
+    assert run_fill(case, b, f, folded=True) == B.RF_OK
+    for l in range(case.n_layers):
+        for key in ("k_pages", "v_pages"):
+            x = a["layers"][l][key].float()
+            y = b["layers"][l][key].float()
+            written = a["layers"][l][key].view(torch.int16) != -1
+            assert torch.equal(written, b["layers"][l][key].view(torch.int16) != -1)
+            e = float(torch.linalg.norm((x - y)[written]) / torch.linalg.norm(x[written]))
+            print(f"layer {l} {key}: plain vs folded {e:.2e}", flush=True)
+            assert e <= 5e-3
+
+
+def test_fold_flags_rank_deficient_map():
+    # a zero column of A makes A^T A singular: the pivot is exactly 0 and the status says so
+    case = _case(256, 1, 2, 64, 300, 20, 0, 16, 68)
+    inp = build_inputs(case)
+    A = inp["layers"][0]["A"].clone()
+    A[:, 5] = 0
+    inp["layers"][0]["A"] = A
+    _, st = fold_layers(case, inp)
+    assert st == B.RF_E_NOT_SPD
+
+
+def test_folded_argument_errors():
+    case = _case(256, 2, 2, 64, 300, 20, 0, 16, 69)
+    inp = build_inputs(case)
+    fold_layers(case, inp)
+    f = _filled(case)
+    dev = inp["xS"].device
+    shape = make_shape(case)
+    idx = torch.from_numpy(f.astype(np.int32)).to(dev)
+    ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, f.size, 2, B.RF_MAPS_FOLDED),
+                     dtype=torch.uint8, device=dev)
+    lays = folded_layer_dicts(inp)
+    mixed = [lays[0], inp["layers"][1]]
+    with pytest.raises(RuntimeError, match="folded"):
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, mixed, inp["table"],
+                         case.page_size, inp["num_pages"], ws)
+    with pytest.raises(RuntimeError, match="streamed"):
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, lays, inp["table"],
+                         case.page_size, inp["num_pages"], ws, copy_stream=torch.cuda.Stream())
+    small = torch.empty(4096, dtype=torch.uint8, device=dev)
+    with pytest.raises(RuntimeError, match="workspace"):
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, lays, inp["table"],
+                         case.page_size, inp["num_pages"], small)
+    int8 = dict(inp["layers"][0])
+    int8.pop("A")
+    int8["A_q"] = torch.zeros((case.d, case.d), dtype=torch.int8, device=dev)
+    int8["A_scale"] = torch.ones(case.d, dtype=torch.float32, device=dev)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    with pytest.raises(RuntimeError, match="int8"):
+        B.ridgefill_fold_maps(shape, [int8], [inp["folded"][0]], fws)

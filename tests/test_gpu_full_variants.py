@@ -166,3 +166,45 @@ def test_value_scale_27b_shape():
                                   hd=cfg.head_dim)
         np.testing.assert_allclose(got[l], want, rtol=2e-3)
         print(f"  layer {l}: max rel {np.max(np.abs(got[l] / want - 1)):.2e}", flush=True)
+
+
+def test_8b_folded_full_size():
+    # the 8B-shaped fill through folded layers (fold once, then the fill), every layer in
+    # one launch as the benchmark runs it; the fold of two layers checked against the
+    # oracle's fold_map as well
+    cfg = configs.LLAMA8B
+    dev = torch.device("cuda")
+    print("\n8B folded: inputs", flush=True)
+    inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
+    shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
+    fb = B.ridgefill_fold_bytes(shape)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    bufs = [torch.empty(fb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
+    print("8B folded: fold", flush=True)
+    B.ridgefill_fold_maps(shape, inp["layers"], bufs, fws)
+    assert B.ridgefill_read_status(fws) == B.RF_OK
+    del fws
+    kv = cfg.n_kv * cfg.head_dim
+    a = lambda x: (x + 255) // 256 * 256
+    oR = a(2 * kv * cfg.d * 2)
+    oc = oR + a(cfg.d * cfg.d * 2)
+    for l in (0, cfg.n_upper - 1):
+        print(f"8B folded: oracle fold of layer {l}", flush=True)
+        lay = inp["layers"][l]
+        Po, co, Ro, ro, ko = oracle.fold_map(_np64(lay["A"]), lay["b"].cpu().numpy().astype(np.float64),
+                                             _np64(lay["norm_w"]), _np64(lay["W_K"]), _np64(lay["W_V"]))
+        buf = bufs[l].cpu()
+        P = buf[:2 * kv * cfg.d * 2].view(torch.bfloat16).double().numpy().reshape(2 * kv, cfg.d)
+        R = buf[oR:oR + cfg.d * cfg.d * 2].view(torch.bfloat16).double().numpy().reshape(cfg.d, cfg.d)
+        c = buf[oc:oc + 2 * kv * 4].view(torch.float32).double().numpy()
+        eP, eR, ec = _rel(P, Po), _rel(R, Ro), _rel(c, co)
+        print(f"  P {eP:.2e} R {eR:.2e} c {ec:.2e}", flush=True)
+        assert eP <= 2e-3 and eR <= 2e-3 and ec <= 1e-6 and np.all(np.tril(R, -1) == 0.0)
+    folded = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"])
+              for l, lay in enumerate(inp["layers"])]
+    print("8B folded: fill", flush=True)
+    filled = _run(cfg, inp, B.RF_MAPS_FOLDED, layers=folded)
+    _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
+    pg, sl = _routing(cfg, inp, filled)
+    n, worst = _values(cfg, inp, filled, exact, pg, sl)
+    print(f"8B folded: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
