@@ -8,7 +8,10 @@ prefix exact: 25,805 filled rows), with every input already in HBM.  The partiti
 the rows is done once beforehand (it is the routing input).  Before the fill, the
 8B-shaped calibration (131,072 synthetic rows of x_S and 20 layer inputs, streamed in
 16,384-row chunks) is timed, then one solve per lambda in {1e-4 .. 1}; the lambda = 0.03
-maps are the ones the fill uses.  Prints one JSON line.
+maps are the ones the fill uses.  Those layers are folded once (ridgefill_fold_maps, timed
+and reported as a per-model cost) and the timed step is the fill of the folded layers;
+the same step with the plain layers is timed and reported beside it.  Prints one JSON
+line.
 """
 
 from __future__ import annotations
@@ -82,9 +85,55 @@ def make_fill_inputs(cfg, dev, maps=None):
 
 
 def fill_step(cfg, inp):
+    """One fill of every upper layer with the plain layers (A, b, norm_w, W_K, W_V)."""
     from ridge_map_kv_amd import binding as B
     B.ridgefill_fill(inp["shape"], inp["xS"], cfg.N, cfg.T, inp["idx"], len(inp["filled"]),
                      inp["layers"], inp["table"], cfg.page_size, inp["num_pages"], inp["ws"])
+
+
+def fold_inputs(cfg, inp):
+    """Folds every upper layer once (ridgefill_fold_maps: a per-model preparation, like
+    choosing lambda, done before any prompt) and sets up the folded fill; returns the
+    fold's milliseconds."""
+    import torch
+    from ridge_map_kv_amd import binding as B
+    dev = inp["xS"].device
+    shape = inp["shape"]
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    fb = B.ridgefill_fold_bytes(shape)
+    bufs = [torch.empty(fb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    B.ridgefill_fold_maps(shape, inp["layers"], bufs, fws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    st = B.ridgefill_read_status(fws)
+    if st != B.RF_OK:
+        raise SystemExit(f"fold reported device status {st}")
+    del fws
+    inp["folded"] = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"])
+                     for l, lay in enumerate(inp["layers"])]
+    inp["ws_folded"] = torch.empty(
+        B.ridgefill_fill_workspace_bytes(shape, len(inp["filled"]), cfg.n_upper, B.RF_MAPS_FOLDED),
+        dtype=torch.uint8, device=dev)
+    return ms
+
+
+def folded_step(cfg, inp):
+    """One fill of every upper layer with the folded layers."""
+    from ridge_map_kv_amd import binding as B
+    B.ridgefill_fill(inp["shape"], inp["xS"], cfg.N, cfg.T, inp["idx"], len(inp["filled"]),
+                     inp["folded"], inp["table"], cfg.page_size, inp["num_pages"],
+                     inp["ws_folded"])
+
+
+def folded_flops(cfg, n_rows):
+    """Useful work of the folded fill: per row and layer the triangle R x (d_in (d_in + 1)
+    flops) and the K/V product (4 kv d_in flops)."""
+    w = cfg.width
+    norm = float(n_rows) * cfg.n_upper * w * (w + 1)
+    kv = float(n_rows) * cfg.n_upper * 4.0 * cfg.kv * w
+    return norm, kv
 
 
 def cpu_baseline_fill(cfg, inp, budget_s: float = 15.0):
@@ -149,8 +198,8 @@ def _time_ms(fn, reps: int, warmup: int = 1) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, ws_layers=None, reps=3,
-                 keep=False):
+def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=False,
+                 ws_layers=None, reps=3, keep=False):
     """One fill workload with its map/projection options; returns its timing line (and the
     inputs when keep)."""
     import torch
@@ -190,7 +239,27 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, ws_layers
             host.append(h)
         layers = host
         torch.cuda.empty_cache()
-    flags = (B.RF_MAPS_INT8 if int8 else 0) | (B.RF_MAPS_STREAMED if streamed else 0)
+    fold_ms = None
+    if folded:
+        fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        fb = B.ridgefill_fold_bytes(shape)
+        bufs = [torch.empty(fb, dtype=torch.uint8, device=dev) for _ in layers]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        B.ridgefill_fold_maps(shape, layers, bufs, fws)
+        torch.cuda.synchronize()
+        fold_ms = (time.perf_counter() - t0) * 1e3
+        if B.ridgefill_read_status(fws) != B.RF_OK:
+            raise SystemExit(f"fold reported a device status for {cfg.name}")
+        del fws
+        layers = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"],
+                       **({"k_norm_w": lay["k_norm_w"]} if knorm else {}))
+                  for l, lay in enumerate(layers)]
+        for lay in inp["layers"]:
+            del lay["A"], lay["W_K"], lay["W_V"]
+        torch.cuda.empty_cache()
+    flags = ((B.RF_MAPS_INT8 if int8 else 0) | (B.RF_MAPS_STREAMED if streamed else 0) |
+             (B.RF_MAPS_FOLDED if folded else 0))
     wsb = B.ridgefill_fill_workspace_bytes(shape, nf, ws_layers or cfg.n_upper, flags)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
@@ -204,12 +273,17 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, ws_layers
     flops = cfg.fill_flops()
     line = {"workload": cfg.name, "d": cfg.d, "d_in": cfg.width, "upper_layers": cfg.n_upper,
             "N": cfg.N, "T": cfg.T, "filled_rows": nf,
-            "maps": ("int8" if int8 else "bf16") + (" streamed from pinned host memory" if streamed
-                                                     else " resident"),
+            "maps": ("folded (bf16 P and R)" if folded else
+                     ("int8" if int8 else "bf16") + (" streamed from pinned host memory" if streamed
+                                                     else " resident")),
             "key_norm": knorm, "ms_per_step": ms, "filled_rows_per_s": nf / (ms * 1e-3),
             "tflop_per_step": flops / 1e12,
             "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
             "workspace_gib": wsb / 2**30}
+    if folded:
+        nflop, kflop = folded_flops(cfg, nf)
+        line["fold_ms_once"] = fold_ms
+        line["pct_bf16_mfma_peak_executed"] = 100.0 * (nflop + kflop) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     if keep:
         return line, (inp, shape)
     del inp, layers, ws
@@ -218,16 +292,16 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, ws_layers
 
 
 def run_variants(dev):
-    """The fill's variants at full size: the 27B-shaped workload with bf16, int8 and int8
-    host-streamed maps; the Qwen3-8B-shaped workload with and without the per-head key
-    norm; a split state twice as wide as the layers; value-rescale factors over c = 512
+    """The fill's variants at full size: the 27B-shaped workload with bf16, int8, int8
+    host-streamed maps and folded layers; the Qwen3-8B-shaped workload with and without the
+    per-head key norm (and folded with it); a split state twice as wide as the layers; value-rescale factors over c = 512
     tail rows of every 27B upper layer; selection of the exact rows of the 8B prefix."""
     import torch
     from ridge_map_kv_amd import binding as B
     from ridge_map_kv_amd import configs
 
     res = {}
-    log("bench: variants: 27B-shaped fill (bf16 resident, int8 resident, int8 streamed)")
+    log("bench: variants: 27B-shaped fill (bf16 resident, int8 resident, int8 streamed, folded)")
     line, (inp, shape) = fill_variant(configs.QWEN27B, dev, keep=True)
     res["27b_bf16_resident"] = line
     # value-rescale factors on the same layers: c = 512 tail rows, exact inputs drawn as
@@ -252,9 +326,11 @@ def run_variants(dev):
     res["27b_int8_resident"] = fill_variant(configs.QWEN27B, dev, int8=True)
     res["27b_int8_streamed_4_layer_groups"] = fill_variant(configs.QWEN27B, dev, int8=True,
                                                            streamed=True, ws_layers=4)
+    res["27b_folded"] = fill_variant(configs.QWEN27B, dev, folded=True)
     log("bench: variants: Qwen3-8B-shaped fill with and without key norm; wide split state")
     res["qwen3_8b"] = fill_variant(configs.QWEN3_8B, dev)
     res["qwen3_8b_key_norm"] = fill_variant(configs.QWEN3_8B, dev, knorm=True)
+    res["qwen3_8b_key_norm_folded"] = fill_variant(configs.QWEN3_8B, dev, knorm=True, folded=True)
     res["8b_wide_split"] = fill_variant(configs.WIDE8B, dev)
     log("bench: variants: exact-row selection")
     P, k = configs.LLAMA8B.prefix, configs.LLAMA8B.exact_count
@@ -402,11 +478,14 @@ def main():
     nf = len(inp["filled"])
     assert nf == cfg.n_filled
 
+    log("bench: folding the upper layers (once per model)")
+    fold_ms = fold_inputs(cfg, inp)
+
     log("bench: warmup")
     for _ in range(args.warmup):
-        fill_step(cfg, inp)
+        folded_step(cfg, inp)
     torch.cuda.synchronize()
-    st = B.ridgefill_read_status(inp["ws"])
+    st = B.ridgefill_read_status(inp["ws_folded"])
     if st != B.RF_OK:
         raise SystemExit(f"fill reported device status {st}")
 
@@ -415,24 +494,42 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        fill_step(cfg, inp)
+        folded_step(cfg, inp)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     B.ridgefill_profile_enable(False)
     ms_step = (t1 - t0) * 1e3 / args.steps
-    map_n, map_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_MAP)
+    norm_n, norm_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_NORM)
     kv_n, kv_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_KV)
-    log(f"bench: {ms_step:.3f} ms/step; map {map_n} launches {map_ms / map_n:.3f} ms; "
+    log(f"bench: {ms_step:.3f} ms/step; norm {norm_n} launches {norm_ms / norm_n:.3f} ms; "
         f"kv {kv_n} launches {kv_ms / kv_n:.3f} ms")
 
-    flops_total = cfg.fill_flops()
-    launches_per_step = map_n // args.steps
-    map_flops_launch = 2.0 * cfg.d * cfg.d * nf * cfg.n_upper / launches_per_step
-    kv_flops_launch = 2.0 * 2 * cfg.kv * cfg.d * nf * cfg.n_upper / launches_per_step
-    map_avg = map_ms / map_n
+    # the same step with the plain layers (map GEMM, then K/V GEMM on the stored x_hat * w)
+    B.ridgefill_profile_reset()
+    B.ridgefill_profile_enable(True)
+    plain_ms = _time_ms(lambda: fill_step(cfg, inp), max(args.steps // 2, 3), warmup=1)
+    B.ridgefill_profile_enable(False)
+    pmap_n, pmap_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_MAP)
+    pkv_n, pkv_ms = B.ridgefill_profile_read(B.RF_KERNEL_FILL_KV)
+    if B.ridgefill_read_status(inp["ws"]) != B.RF_OK:
+        raise SystemExit("plain fill reported a device status")
+    log(f"bench: plain layers {plain_ms:.3f} ms/step")
+
+    flops_total = cfg.fill_flops()            # the method's algorithmic work (plain flow)
+    norm_flops, kv_flops = folded_flops(cfg, nf)
+    launches = norm_n // args.steps
+    norm_avg = norm_ms / norm_n
     kv_avg = kv_ms / kv_n
-    achieved = map_flops_launch / (map_avg * 1e-3) / 1e12
+    norm_tf = norm_flops / launches / (norm_avg * 1e-3) / 1e12
+    kv_tf = kv_flops / launches / (kv_avg * 1e-3) / 1e12
+    dom = "fill_norm_kernel" if norm_avg >= kv_avg else "fill_kv_kernel"
+    dom_flops = (norm_flops if dom == "fill_norm_kernel" else kv_flops) / launches
+    dom_avg = norm_avg if dom == "fill_norm_kernel" else kv_avg
+    achieved = dom_flops / (dom_avg * 1e-3) / 1e12
     rows_per_s = nf / (ms_step * 1e-3)
+    plain_calls = max(args.steps // 2, 3) + 1                # timed calls plus the warm-up
+    pmap_avg = pmap_ms / pmap_n
+    pmap_tf = 2.0 * cfg.d * cfg.width * nf * cfg.n_upper / (pmap_n / plain_calls) / (pmap_avg * 1e-3) / 1e12
 
     out = {
         "metric": "filled prefix rows/sec over all upper layers (8B shape) + % bf16 MFMA peak",
@@ -448,25 +545,37 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "pct_bf16_mfma_peak": 100.0 * flops_total / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "pct_basis": "the method's algorithmic work, 2 (d^2 + 2 kv d) flop per filled row and "
+                     "upper layer, per second, over the bf16 peak; the folded layers compute "
+                     "the same K/V with the triangle d (d + 1) + 4 kv d flop",
+        "pct_bf16_mfma_peak_executed": 100.0 * (norm_flops + kv_flops) / (ms_step * 1e-3)
+                                       / (PEAK_BF16_TFLOPS * 1e12),
         "config": {"workload": "llama3.1-8b-shaped fill", "d": cfg.d, "upper_layers": cfg.n_upper,
                    "split": cfg.S, "layers": cfg.L, "n_kv_heads": cfg.n_kv,
                    "head_dim": cfg.head_dim, "N": cfg.N, "T": cfg.T, "filled_rows": nf,
                    "exact_rows": cfg.exact_count, "page_size": cfg.page_size,
                    "maps": ("synthetic near-identity bf16 maps" if maps is None else
                             "bf16 maps from this run's calibration + solve at lambda = 0.03"),
-                   "fill_tflop_per_step": flops_total / 1e12},
-        "roofline": {"bound": "mfma", "kernel": "fill_map_kernel",
+                   "layers_form": "folded (ridgefill_fold_maps once per model, then the fill)",
+                   "fill_tflop_per_step": flops_total / 1e12,
+                   "folded_tflop_per_step": (norm_flops + kv_flops) / 1e12},
+        "roofline": {"bound": "mfma", "kernel": dom,
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "launch_ms": map_avg, "flop_per_launch": map_flops_launch},
+                     "launch_ms": dom_avg, "flop_per_launch": dom_flops},
         "kernels": {
-            "fill_map_kernel": {"avg_ms": map_avg, "launches": map_n,
-                                "tflops": achieved},
-            "fill_kv_kernel": {"avg_ms": kv_avg, "launches": kv_n,
-                               "tflops": kv_flops_launch / (kv_avg * 1e-3) / 1e12},
+            "fill_norm_kernel": {"avg_ms": norm_avg, "launches": norm_n, "tflops": norm_tf},
+            "fill_kv_kernel": {"avg_ms": kv_avg, "launches": kv_n, "tflops": kv_tf},
         },
+        "fold": {"ms_once": fold_ms, "upper_layers": cfg.n_upper,
+                 "note": "per model (per lambda), not per prompt: P, c, R, r, kappa of each layer"},
+        "plain_layers": {
+            "ms_per_step": plain_ms, "filled_rows_per_s": nf / (plain_ms * 1e-3),
+            "pct_bf16_mfma_peak": 100.0 * flops_total / (plain_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+            "fill_map_kernel": {"avg_ms": pmap_avg, "launches": pmap_n, "tflops": pmap_tf},
+            "fill_kv_kernel": {"avg_ms": pkv_ms / pkv_n, "launches": pkv_n}},
     }
-    rec = recorded_traffic("fill_map_kernel")
+    rec = recorded_traffic(dom)
     if rec is not None:
         out["roofline"]["traffic"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
         out["roofline"]["traffic_detail"] = {

@@ -180,70 +180,84 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
   }
 }
 
-// Folded layers: per row, the sum of squares of (R x_S + r) over one 256-feature tile of the
-// upper-triangular factor R (A^T A = R^T R), written as two 128-feature partials.  Row f of
-// R is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only.
+// Folded layers: per row, the sum of squares of (R x_S + r) over 256-feature tiles of the
+// upper-triangular factor R (A^T A = R^T R), written as 128-feature partials.  Row f of R
+// is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only.  A
+// workgroup takes the pair of tiles ft and nft - 1 - ft (the longer first): every pair
+// then reduces over d_in + 256 columns, so the workgroups are of equal length and the
+// short tiles share the fixed cost of a tile with long ones.  With nft odd the middle
+// tile is a pair of its own.  a.nft counts pairs.  The reduction runs from the last column
+// down to the tile's first: tiles of different lengths then start together at column
+// d_in - 64, so the workgroups of one token tile read each slice of its x_S rows at about
+// the same time and share it in L2.
 __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
-  int g, tt, ft;
-  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  __shared__ __attribute__((aligned(16))) float sr[kTile];
+  int g, tt, pp;
+  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, pp);
   const FillLayerPtrs Lp = a.L[g];
-  const int t0 = tt * kTile, f0 = ft * kTile;
-  const int tid = threadIdx.x;
+  const int nft = a.d_in / kTile;
+  const int t0 = tt * kTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wave >> 1, wt = wave & 1, h = lane >> 5;
 
-  DmaOperand Fo, To;
-  {
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* ssq = reinterpret_cast<float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
+
+  for (int half = 0; half < 2; ++half) {
+    const int ft = half == 0 ? pp : nft - 1 - pp;
+    if (half == 1 && ft == pp) break;                       // the middle tile of an odd nft
+    const int f0 = ft * kTile;
+    DmaOperand Fo, To;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
       const int ce = dma_chunk_elems(r, lane);
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in + f0);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in +
+                                                           (a.d_in - kPipeBK));
       Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
+      // the same gathered x_S rows for both tiles; only the column offset moves
       const int tok = t0 + r;
       int row = 0;
       if (tok < a.n_filled) {
         const int t = a.idx[tok];
         if (t >= 0 && t < a.P) row = t;
       }
-      To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + f0);
+      To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + (a.d_in - kPipeBK));
       To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
     }
-  }
-  __shared__ __attribute__((aligned(16))) float sr[kTile];
-  const float my_r = Lp.b[f0 + tid];
+    const float my_r = Lp.b[f0 + tid];
 
-  f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, a.d_in - f0, smem);
+    f32x16 acc[4][4];
+    gemm_pipeline<true>(acc, Fo, To, a.d_in - f0, smem);   // ends with a barrier: sr is free
 
-  sr[tid] = my_r;
-  __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
-  float* ssq = reinterpret_cast<float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    sr[tid] = my_r;
+    __syncthreads();
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + wf * 128 + m * 32 + q * 8 + h * 4);
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + wf * 128 + m * 32 + q * 8 + h * 4);
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const float v0 = acc[m][n][q * 4 + 0] + rv.x;
-        const float v1 = acc[m][n][q * 4 + 1] + rv.y;
-        const float v2 = acc[m][n][q * 4 + 2] + rv.z;
-        const float v3 = acc[m][n][q * 4 + 3] + rv.w;
-        ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+        for (int n = 0; n < 4; ++n) {
+          const float v0 = acc[m][n][q * 4 + 0] + rv.x;
+          const float v1 = acc[m][n][q * 4 + 1] + rv.y;
+          const float v2 = acc[m][n][q * 4 + 2] + rv.z;
+          const float v3 = acc[m][n][q * 4 + 3] + rv.w;
+          ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+        }
       }
     }
-  }
 #pragma unroll
-  for (int n = 0; n < 4; ++n) ss[n] += __shfl_xor(ss[n], 32);
-  if (h == 0) {
-    const int chunk = (f0 + wf * 128) >> 7;
+    for (int n = 0; n < 4; ++n) ss[n] += __shfl_xor(ss[n], 32);
+    if (h == 0) {
+      const int chunk = (f0 + wf * 128) >> 7;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
-      ssq[(size_t)chunk * a.mpad + tok] = ss[n];
+      for (int n = 0; n < 4; ++n) {
+        const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
+        ssq[(size_t)chunk * a.mpad + tok] = ss[n];
+      }
     }
   }
 }
@@ -725,7 +739,7 @@ void expand_group(const FillPlan& p, FillKArgs& a, int G, const int8_t* const* c
 hipError_t launch_fill_group(const FillPlan& p, FillKArgs& a, int G, hipStream_t stream) {
   a.f_base = 0;
   if (a.folded) {
-    a.nft = p.d_in / kTile;
+    a.nft = (p.d_in / kTile + 1) / 2;          // pairs of R tiles
     {
       ProfileScope ps(RF_KERNEL_FILL_NORM, stream);
       hipLaunchKernelGGL(fill_norm_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);

@@ -134,14 +134,18 @@ __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&
 }
 
 // acc = F[256 x K] * T[256 x K]^T, K a multiple of 64.  Ends with a barrier, leaving the
-// 128 KB of LDS to the epilogue.
+// 128 KB of LDS to the epilogue.  With REV the slices are taken from the last to the first:
+// the operands' base pointers then point at the last slice (reduction index K - 64), and
+// each further slice lies 128 bytes before the previous one.
 //
 // Two 64 KB stages.  The 16 load issues per wave that refill a stage are split: the first 8
 // follow the barrier that frees the stage (one after every other MFMA of the last 16-wide
 // step), the other 8 go out during the first step of the next slice, so the CU's address
 // unit never has all 64 of a slice queued inside one 16-MFMA window.
+template <bool REV = false>
 __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOperand& F,
                                               const DmaOperand& T, int K, unsigned char* smem) {
+  constexpr int kStep = REV ? -kPipeBK * 2 : kPipeBK * 2;    // bytes from one slice to the next
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1;
@@ -157,8 +161,8 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
   for (int s = 0; s < 2 && s < nk; ++s) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      dma_block(F, p, s * kPipeBK * 2, base + s * kPipeStage, wave);
-      dma_block(T, p, s * kPipeBK * 2, base + s * kPipeStage + kPipeOp, wave);
+      dma_block(F, p, s * kStep, base + s * kPipeStage, wave);
+      dma_block(T, p, s * kStep, base + s * kPipeStage + kPipeOp, wave);
     }
   }
   if (nk > 1)
@@ -174,7 +178,7 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
     const unsigned char* cur = smem + (kt & 1) * kPipeStage;
     // second half of slice kt + 1 (slices 0 and 1 came whole with the prologue)
     const bool pend = kt >= 1;
-    const int kbp = (kt + 1) * kPipeBK * 2;
+    const int kbp = (kt + 1) * kStep;
     const uint32_t dstp = base + ((kt + 1) & 1) * kPipeStage;
     mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, pend, F, T, kbp, dstp, 8, wave);
     mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
@@ -184,7 +188,7 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
     const bool more = kt + 2 < nk;
     const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
     const uint32_t dst = base + (kt & 1) * kPipeStage;
-    const int kb = (kt + 2) * kPipeBK * 2;
+    const int kb = (kt + 2) * kStep;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mfma_i(acc, a1, b1, i);
