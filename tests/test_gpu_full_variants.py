@@ -1,8 +1,9 @@
 """Parity of the fill's variants at the workloads' full sizes, in the launch configurations
 the benchmark times: the 27B-shaped fill with int8 maps streamed from pinned host memory in
 4-layer groups, the Qwen3-8B-shaped fill with key norm, the 8B-shaped fill with a split
-state twice as wide as the layers, and the value-rescale factors over c = 512 tail rows of
-the 27B shape.
+state twice as wide as the layers, the value-rescale factors over c = 512 tail rows of
+the 27B shape, and the folded 8B, 27B and Qwen3-8B (key norm) fills against the plain
+oracle.
 
 Fills: routing bit-exact on every byte of every layer's pools (sentinel-filled), K and V
 against the oracle on 512 sampled rows of every layer (first and last filled row, rows
@@ -208,3 +209,40 @@ def test_8b_folded_full_size():
     pg, sl = _routing(cfg, inp, filled)
     n, worst = _values(cfg, inp, filled, exact, pg, sl)
     print(f"8B folded: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
+
+
+def _folded_full(cfg, knorm=False):
+    dev = torch.device("cuda")
+    print(f"\n{cfg.name} folded: inputs", flush=True)
+    inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
+    if knorm:
+        for l, lay in enumerate(inp["layers"]):
+            lay["k_norm_w"] = torch.from_numpy(synth.key_norm_weight(cfg.head_dim, cfg.seed, l)).to(
+                dev).to(torch.bfloat16)
+    shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    bufs = [torch.empty(B.ridgefill_fold_bytes(shape), dtype=torch.uint8, device=dev)
+            for _ in inp["layers"]]
+    print(f"{cfg.name} folded: fold of {cfg.n_upper} layers", flush=True)
+    B.ridgefill_fold_maps(shape, inp["layers"], bufs, fws)
+    assert B.ridgefill_read_status(fws) == B.RF_OK
+    del fws
+    folded = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"],
+                   **({"k_norm_w": lay["k_norm_w"]} if knorm else {}))
+              for l, lay in enumerate(inp["layers"])]
+    print(f"{cfg.name} folded: fill", flush=True)
+    filled = _run(cfg, inp, B.RF_MAPS_FOLDED, layers=folded)
+    _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
+    pg, sl = _routing(cfg, inp, filled)
+    n, worst = _values(cfg, inp, filled, exact, pg, sl,
+                       kn_of=(lambda l: _np64(inp["layers"][l]["k_norm_w"])) if knorm else None)
+    print(f"{cfg.name} folded: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
+
+
+def test_27b_folded_full_size():
+    # 48 folded layers in two 24-layer launches, as the benchmark runs them
+    _folded_full(configs.QWEN27B)
+
+
+def test_qwen3_8b_key_norm_folded_full_size():
+    _folded_full(configs.QWEN3_8B, knorm=True)
