@@ -14,7 +14,7 @@
 //   H   = A^T A (lower tiles)      bf16 MFMA: exact products, fp32 accumulation, kept fp64
 //   L   = Cholesky(H)              fp64, the solve's blocked kernels;  R = L^T in bf16
 //   g   = A^T b,  c = W b,  |b|^2  fp64 accumulation in a fixed order
-//   r   = L^-1 g                   blocked forward substitution, fp64
+//   r   = L^-1 g                   blocked forward substitution (right-looking), fp64
 //   kappa = |b|^2 - |r|^2          fp64
 // One layer at a time through the workspace; every launch on the caller's stream.
 #include "rf_common.h"
@@ -180,27 +180,36 @@ __global__ __launch_bounds__(1024) void fold_bb_kernel(const float* b, int d, do
   if (t == 0) scal[0] = part[0];
 }
 
-// Block row i of L r = g:  y = g_i - sum_{k < 64 i} L[64 i + row][k] r[k] (four threads per
-// row, strided, combined in a fixed order), then r_i = Linv_ii y.
+// Step i of L r = g, right-looking: g_i is final (the steps before subtracted every earlier
+// block from it), so every workgroup of the launch forms r_i = Linv_ii g_i itself (a 64 x 64
+// triangular product); workgroup 0 stores it, workgroup m >= 1 subtracts L[i+m][i] r_i from
+// g_{i+m} (four threads per row, combined in a fixed order).  No workgroup writes what
+// another of the same launch reads.
 __global__ __launch_bounds__(256) void fold_fsub_kernel(const double* L, int d, int i,
-                                                        const double* linv, const double* g,
+                                                        const double* linv, double* g,
                                                         double* r) {
-  __shared__ double part[FB][4];
-  __shared__ double y[FB];
-  const int t = threadIdx.x, row = t >> 2, q = t & 3;
-  const double* Lr = L + (size_t)(i * FB + row) * d;
-  double s = 0.0;
-  for (int k = q; k < i * FB; k += 4) s += Lr[k] * r[k];
-  part[row][q] = s;
-  __syncthreads();
-  if (t < FB) y[t] = g[i * FB + t] - (((part[t][0] + part[t][1]) + part[t][2]) + part[t][3]);
-  __syncthreads();
+  __shared__ double ri[FB];
+  const int t = threadIdx.x;
   if (t < FB) {
     const double* li = linv + (size_t)i * FB * FB + (size_t)t * FB;
+    const double* gi = g + (size_t)i * FB;
     double v = 0.0;
-    for (int j = 0; j <= t; ++j) v += li[j] * y[j];
-    r[i * FB + t] = v;
+    for (int j = 0; j <= t; ++j) v += li[j] * gi[j];
+    ri[t] = v;
   }
+  __syncthreads();
+  const int m = blockIdx.x;
+  if (m == 0) {
+    if (t < FB) r[(size_t)i * FB + t] = ri[t];
+    return;
+  }
+  const int row = t >> 2, q = t & 3;
+  const double* Lr = L + (size_t)((i + m) * FB + row) * d + (size_t)i * FB;
+  double s = 0.0;
+  for (int j = q; j < FB; j += 4) s += Lr[j] * ri[j];
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  if (q == 0) g[(size_t)(i + m) * FB + row] -= s;
 }
 
 // r to fp32, kappa = |b|^2 - |r|^2 (fixed-order tree).
@@ -275,8 +284,9 @@ hipError_t launch_fold(int d, int d_in, int kv, const uint16_t* A, const float* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_cholesky(H, d_in, linv, status, stream)) != hipSuccess) return e;
-  for (int i = 0; i < d_in / FB; ++i)
-    hipLaunchKernelGGL(fold_fsub_kernel, dim3(1), dim3(256), 0, stream, H, d_in, i, linv, g, r);
+  const int nb = d_in / FB;
+  for (int i = 0; i < nb; ++i)
+    hipLaunchKernelGGL(fold_fsub_kernel, dim3(nb - i), dim3(256), 0, stream, H, d_in, i, linv, g, r);
   hipLaunchKernelGGL(fold_finish_kernel, dim3(1), dim3(1024), 0, stream, r, scal, d_in,
                      reinterpret_cast<float*>(o + F.r), reinterpret_cast<float*>(o + F.kappa));
   hipLaunchKernelGGL(fold_rt_kernel, dim3(d_in / 64, d_in / 64), dim3(256), 0, stream, H, d_in,

@@ -149,9 +149,21 @@ __device__ __forceinline__ void store44(double* dst, size_t ld, const double (&a
     }
 }
 
-// Factor diagonal block k in place (lower) and store its inverse in linv[k].  256 threads;
-// thread t owns row t / 4 and the 16 columns 16 (t % 4) .. + 15, and keeps its segment of
-// the block and of Y in registers for the whole sweep.
+// 1/p from the hardware reciprocal and two Newton steps (each doubles the correct bits):
+// within an ulp or two of the correctly rounded quotient, at a fraction of its cost.
+__device__ __forceinline__ double recip(double p) {
+  double r = __builtin_amdgcn_rcp(p);
+  double e = fma(-p, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-p, r, 1.0);
+  return fma(r, e, r);
+}
+
+// Factor diagonal block k in place (lower) and store its inverse in linv[k].  1024 threads;
+// thread t owns row t / 16 and the 4 columns 4 (t % 16) .. + 3, and keeps its segment of
+// the block and of Y in registers for the whole sweep.  (The 64 column steps are
+// sequential; with 4 columns per thread each step is a few instructions, measured 2.5x
+// faster than 16 columns per thread on 256 threads.)
 //
 // Column j is eliminated with its pivot d_j left unscaled: every row below subtracts
 // (a_ij / d_j) times column j from its columns j+1 .. i, which leaves a_ij = L_ij sqrt(d_j).
@@ -162,17 +174,19 @@ __device__ __forceinline__ void store44(double* dst, size_t ld, const double (&a
 // suffices and no other LDS traffic is needed.  At the end L_ij = a_ij / sqrt(d_j),
 // L_jj = sqrt(d_j) and (L^-1)_i = Y_i / sqrt(d_i).  A non-positive or non-finite pivot sets
 // the NOT_SPD bit and is taken as 1.
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k, double* linv,
-                                                        unsigned* status) {
-  __shared__ double col[2][NB];       // column j of the block (double-buffered by j parity)
-  __shared__ double yrow[2][NB];      // row j of Y
+constexpr int kDiagThreads = 1024, kDiagW = 4;
+__global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int d, int k,
+                                                                 double* linv, unsigned* status) {
+  __shared__ __attribute__((aligned(16))) double col[2][NB];   // column j (by j parity)
+  __shared__ __attribute__((aligned(16))) double yrow[2][NB];  // row j of Y
   __shared__ double piv[NB];          // pivots d_j (after the NOT_SPD replacement)
   double* blk = C + (size_t)k * NB * d + (size_t)k * NB;
   const int t = threadIdx.x;
-  const int row = t >> 2, c0 = (t & 3) * 16;
-  double ar[16], yr[16];
+  constexpr int TPR = NB / kDiagW;
+  const int row = t / TPR, c0 = (t % TPR) * kDiagW;
+  double ar[kDiagW], yr[kDiagW];
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
+  for (int cc = 0; cc < kDiagW; ++cc) {
     ar[cc] = blk[(size_t)row * d + c0 + cc];
     yr[cc] = row == c0 + cc ? 1.0 : 0.0;
   }
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k,
   if (c0 == 0) col[0][row] = ar[0];
   if (row == 0) {
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) yrow[0][c0 + cc] = yr[cc];
+    for (int cc = 0; cc < kDiagW; ++cc) yrow[0][c0 + cc] = yr[cc];
   }
   __syncthreads();
   for (int j = 0; j < NB; ++j) {
@@ -193,22 +207,27 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k,
       if (bad) atomicOr(status, kStatusNotSpdBit);
     }
     if (row > j) {
-      const double m = col[b][row] / p;
+      const double m = col[b][row] * recip(p);
+      const double2* cv = reinterpret_cast<const double2*>(&col[b][c0]);
+      const double2* yv = reinterpret_cast<const double2*>(&yrow[b][c0]);
 #pragma unroll
-      for (int cc = 0; cc < 16; ++cc) {
-        const int c = c0 + cc;
-        if (c > j && c <= row) ar[cc] -= m * col[b][c];
-        yr[cc] -= m * yrow[b][c];
+      for (int q = 0; q < kDiagW / 2; ++q) {
+        const double2 cq = cv[q], yq = yv[q];
+        const int c = c0 + 2 * q;
+        if (c > j && c <= row) ar[2 * q] -= m * cq.x;
+        if (c + 1 > j && c + 1 <= row) ar[2 * q + 1] -= m * cq.y;
+        yr[2 * q] -= m * yq.x;
+        yr[2 * q + 1] -= m * yq.y;
       }
     }
     // column j + 1 and row j + 1 of Y are now final: publish them for the next step
     if (j + 1 < NB) {
 #pragma unroll
-      for (int cc = 0; cc < 16; ++cc)
+      for (int cc = 0; cc < kDiagW; ++cc)
         if (c0 + cc == j + 1) col[b ^ 1][row] = ar[cc];
       if (row == j + 1) {
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc) yrow[b ^ 1][c0 + cc] = yr[cc];
+        for (int cc = 0; cc < kDiagW; ++cc) yrow[b ^ 1][c0 + cc] = yr[cc];
       }
     }
     __syncthreads();
@@ -217,7 +236,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* C, int d, int k,
   double* li = linv + (size_t)k * NB * NB;
   const double rrow = 1.0 / sqrt(piv[row]);
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
+  for (int cc = 0; cc < kDiagW; ++cc) {
     const int c = c0 + cc;
     double lv = 0.0;
     if (c < row) lv = ar[cc] / sqrt(piv[c]);
@@ -491,7 +510,8 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
 hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream) {
   const int nbk = d / NB;
   for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, C, d, k, linv, status);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kDiagThreads), 0, stream, C, d, k, linv,
+                       status);
     const int below = nbk - k - 1;
     if (below > 0) {
       hipLaunchKernelGGL(chol_panel_kernel, dim3(below), dim3(256), 0, stream, C, d, k, linv);

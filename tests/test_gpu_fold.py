@@ -154,3 +154,19 @@ def test_folded_argument_errors():
     fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
     with pytest.raises(RuntimeError, match="int8"):
         B.ridgefill_fold_maps(shape, [int8], [inp["folded"][0]], fws)
+
+
+def test_folded_group_split_is_bit_identical():
+    # one launch per layer (a one-layer workspace) against all layers in one launch: the
+    # per-layer arithmetic is the same, so the caches agree bit for bit
+    case = _case(512, 3, 2, 128, 700, 100, 60, 16, 70, knorm=True, vscale=True)
+    f = _filled(case)
+    a = build_inputs(case)
+    b = build_inputs(case)
+    assert run_fill(case, a, f, folded=True) == B.RF_OK
+    b["folded"] = a["folded"]
+    assert run_fill(case, b, f, folded=True, ws_layers=1) == B.RF_OK
+    for l in range(case.n_layers):
+        for key in ("k_pages", "v_pages"):
+            assert torch.equal(a["layers"][l][key].view(torch.int16),
+                               b["layers"][l][key].view(torch.int16)), f"layer {l} {key}"
