@@ -113,40 +113,59 @@ __device__ __forceinline__ void load64(double* t, const double* src, size_t ld, 
   }
 }
 
-// acc (4x4 per thread, rows 4*(tid>>4).., cols 4*(tid&15)..) += A * B^T from LDS tiles.
-__device__ __forceinline__ void mac64(double (&acc)[4][4], const double* A, const double* Bt) {
-  const int r0 = (threadIdx.x >> 4) * 4, c0 = (threadIdx.x & 15) * 4;
-  for (int q = 0; q < NB; ++q) {
-    double a[4], b[4];
+// 64 x 64 fp64 accumulator on the fp64 matrix cores: wave w of a 256-thread block owns rows
+// 32 (w >> 1) .. and columns 32 (w & 1) .. as 2 x 2 blocks of v_mfma_f64_16x16x4_f64.  That
+// instruction takes A[m][k] from lane 16 k + m, B[k][n] from lane 16 k + n, and leaves
+// D[i + 4 j][n] in register j of lane 16 i + n (measured on gfx950).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+struct Acc64 {
+  f64x4 v[2][2];
+};
+
+__device__ __forceinline__ void zero44(Acc64& acc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = A[(r0 + i) * LDT + q];
+  for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = Bt[(c0 + j) * LDT + q];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    for (int bj = 0; bj < 2; ++bj) acc.v[bi][bj] = f64x4{0.0, 0.0, 0.0, 0.0};
+}
+
+// acc += A * Bt^T for the LDS tiles A, Bt [64][LDT]: acc[r][c] += sum_q A[r][q] Bt[c][q].
+__device__ __forceinline__ void mac64(Acc64& acc, const double* A, const double* Bt) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r0 = (w >> 1) * 32 + (lane & 15), c0 = (w & 1) * 32 + (lane & 15), kq = lane >> 4;
+#pragma unroll 4
+  for (int k = 0; k < NB; k += 4) {
+    const double a0 = A[r0 * LDT + k + kq], a1 = A[(r0 + 16) * LDT + k + kq];
+    const double b0 = Bt[c0 * LDT + k + kq], b1 = Bt[(c0 + 16) * LDT + k + kq];
+    acc.v[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc.v[0][0], 0, 0, 0);
+    acc.v[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc.v[0][1], 0, 0, 0);
+    acc.v[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc.v[1][0], 0, 0, 0);
+    acc.v[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc.v[1][1], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void zero44(double (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+// Element (row, col) of the tile held in register j of block (bi, bj) of this lane.
+__device__ __forceinline__ int acc_row(int bi, int j) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return (w >> 1) * 32 + bi * 16 + (lane >> 4) + 4 * j;
+}
+__device__ __forceinline__ int acc_col(int bj) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return (w & 1) * 32 + bj * 16 + (lane & 15);
 }
 
 // dst[r][c] = s * acc + (add ? dst : 0)
-__device__ __forceinline__ void store44(double* dst, size_t ld, const double (&acc)[4][4],
-                                        double s, bool add) {
-  const int r0 = (threadIdx.x >> 4) * 4, c0 = (threadIdx.x & 15) * 4;
+__device__ __forceinline__ void store44(double* dst, size_t ld, const Acc64& acc, double s,
+                                        bool add) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      double* p = dst + (size_t)(r0 + i) * ld + c0 + j;
-      *p = s * acc[i][j] + (add ? *p : 0.0);
-    }
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        double* p = dst + (size_t)acc_row(bi, j) * ld + acc_col(bj);
+        *p = s * acc.v[bi][bj][j] + (add ? *p : 0.0);
+      }
 }
 
 // 1/p from the hardware reciprocal and two Newton steps (each doubles the correct bits):
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* C, int d, int k
   load64(a, blk, d, false);
   load64(li, linv + (size_t)k * NB * NB, NB, false);
   __syncthreads();
-  double acc[4][4];
+  Acc64 acc;
   zero44(acc);
   mac64(acc, a, li);
   __syncthreads();
@@ -276,7 +295,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* C, int d, int 
   load64(a, C + (size_t)i * NB * d + (size_t)k * NB, d, false);
   load64(b, C + (size_t)j * NB * d + (size_t)k * NB, d, false);
   __syncthreads();
-  double acc[4][4];
+  Acc64 acc;
   zero44(acc);
   mac64(acc, a, b);
   store44(C + (size_t)i * NB * d + (size_t)j * NB, d, acc, -1.0, true);
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(256) void fsub_rows_kernel(double* W, int d, int i,
   load64(li, linv + (size_t)i * NB * NB, NB, false);
   load64(bt, blk, d, true);
   __syncthreads();
-  double acc[4][4];
+  Acc64 acc;
   zero44(acc);
   mac64(acc, li, bt);
   __syncthreads();
@@ -315,7 +334,7 @@ __global__ __launch_bounds__(256) void fsub_update_kernel(double* W, const doubl
   load64(l, C + (size_t)m * NB * d + (size_t)i * NB, d, false);
   load64(wt, W + (size_t)i * NB * d + (size_t)cb * NB, d, true);
   __syncthreads();
-  double acc[4][4];
+  Acc64 acc;
   zero44(acc);
   mac64(acc, l, wt);
   store44(W + (size_t)m * NB * d + (size_t)cb * NB, d, acc, -1.0, true);
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double
   while (ab * (ab + 1) / 2 > e) --ab;
   const int bb = e - ab * (ab + 1) / 2;
   const int nbk = d / NB;
-  double acc[4][4];
+  Acc64 acc;
   zero44(acc);
   for (int kb = ab; kb < nbk; ++kb) {
     load64(wa, W + (size_t)kb * NB * d + (size_t)ab * NB, d, true);
@@ -348,16 +367,18 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double
     mac64(acc, wa, wb);
     __syncthreads();
   }
-  const int r0 = (threadIdx.x >> 4) * 4, c0 = (threadIdx.x & 15) * 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const size_t a = (size_t)ab * NB + r0 + i, b = (size_t)bb * NB + c0 + j;
-      M64[a * d + b] = acc[i][j];
-      M64[b * d + a] = acc[i][j];
+      const size_t a = (size_t)ab * NB + acc_row(bi, j), b = (size_t)bb * NB + acc_col(bj);
+      const double v = acc.v[bi][bj][j];
+      M64[a * d + b] = v;
+      M64[b * d + a] = v;
       uint16_t hi, lo;
-      split_bf16(acc[i][j], hi, lo);
+      split_bf16(v, hi, lo);
       const size_t d3 = (size_t)3 * d;
       Mx[a * d3 + b] = hi;
       Mx[a * d3 + d + b] = lo;
