@@ -99,7 +99,8 @@ def fold_inputs(cfg, inp):
     from ridge_map_kv_amd import binding as B
     dev = inp["xS"].device
     shape = inp["shape"]
-    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, len(inp["layers"])),
+                      dtype=torch.uint8, device=dev)
     fb = B.ridgefill_fold_bytes(shape)
     bufs = [torch.empty(fb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
     torch.cuda.synchronize()
@@ -241,7 +242,8 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=Fa
         torch.cuda.empty_cache()
     fold_ms = None
     if folded:
-        fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        fws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, len(layers)),
+                          dtype=torch.uint8, device=dev)
         fb = B.ridgefill_fold_bytes(shape)
         bufs = [torch.empty(fb, dtype=torch.uint8, device=dev) for _ in layers]
         torch.cuda.synchronize()

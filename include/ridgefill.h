@@ -225,16 +225,22 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
  *   ws         device workspace >= ridgefill_fold_workspace_bytes(shape); its first 256
  *              bytes hold the status: RF_E_NOT_SPD when some layer's A^T A had a
  *              non-positive pivot (A not of full column rank; that layer's buffer is
- *              then not usable)
+ *              then not usable).  A workspace of ridgefill_fold_workspace_bytes_ex(shape, G)
+ *              bytes folds G layers side by side (their Cholesky factorizations share
+ *              one sequence of launches); a smaller one folds as many as it holds, at
+ *              least one (at most 64) at a time.  The results do not depend on G.
  * Arithmetic: P = bf16-split(W diag(w)) times A on the matrix cores (products exact,
  * fp32 accumulation, one bf16 rounding of P); A^T A with exact products and fp32
  * accumulation; Cholesky, r and kappa in fp64; R rounded to bf16 once; c in fp64
- * rounded to fp32.  Layers are folded one after another through the workspace.
+ * rounded to fp32.
  * Folded layers work with ridgefill_fill (not the streamed fill); all layers of a fill
  * call must be folded or none.  ridgefill_value_scale always uses the plain fields.
  * ------------------------------------------------------------------------------ */
 size_t ridgefill_fold_bytes(const rf_shape* shape);
 size_t ridgefill_fold_workspace_bytes(const rf_shape* shape);
+/* Workspace that folds layers_at_once (>= 1) layers side by side; 0 for a shape that
+ * cannot be folded or layers_at_once < 1. */
+size_t ridgefill_fold_workspace_bytes_ex(const rf_shape* shape, int32_t layers_at_once);
 rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int32_t n_layers,
                               void* const* folded, void* ws, size_t ws_bytes, void* stream);
 

@@ -29,6 +29,7 @@ EXPORTED = [
     "ridgefill_quantize_map",
     "ridgefill_fold_bytes",
     "ridgefill_fold_workspace_bytes",
+    "ridgefill_fold_workspace_bytes_ex",
     "ridgefill_fold_maps",
     "ridgefill_select_workspace_bytes",
     "ridgefill_select_rows",
@@ -109,6 +110,7 @@ def lib() -> C.CDLL:
         "ridgefill_quantize_map": (st, [vp, i64, i64, vp, vp, vp]),
         "ridgefill_fold_bytes": (sz, [C.POINTER(rf_shape)]),
         "ridgefill_fold_workspace_bytes": (sz, [C.POINTER(rf_shape)]),
+        "ridgefill_fold_workspace_bytes_ex": (sz, [C.POINTER(rf_shape), i32]),
         "ridgefill_fold_maps": (st, [C.POINTER(rf_shape), C.POINTER(rf_layer), i32,
                                      C.POINTER(vp), vp, sz, vp]),
         "ridgefill_select_workspace_bytes": (sz, [i64]),
@@ -231,6 +233,11 @@ def ridgefill_fold_bytes(shape: rf_shape) -> int:
 
 def ridgefill_fold_workspace_bytes(shape: rf_shape) -> int:
     return int(lib().ridgefill_fold_workspace_bytes(C.byref(shape)))
+
+
+def ridgefill_fold_workspace_bytes_ex(shape: rf_shape, layers_at_once: int) -> int:
+    """Fold workspace for layers_at_once layers folded side by side."""
+    return int(lib().ridgefill_fold_workspace_bytes_ex(C.byref(shape), layers_at_once))
 
 
 def ridgefill_fold_maps(shape: rf_shape, layers: list[dict], folded: list, ws, stream=None) -> None:

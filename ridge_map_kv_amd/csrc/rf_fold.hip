@@ -16,7 +16,9 @@
 //   g   = A^T b,  c = W b,  |b|^2  fp64 accumulation in a fixed order
 //   r   = L^-1 g                   blocked forward substitution (right-looking), fp64
 //   kappa = |b|^2 - |r|^2          fp64
-// One layer at a time through the workspace; every launch on the caller's stream.
+// Layers go in groups as large as the workspace holds: the GEMMs layer by layer, then the
+// group's Cholesky factorizations and substitutions side by side.  Every launch is on the
+// caller's stream.
 #include "rf_common.h"
 #include "rf_gemm_tile.h"
 #include "rf_internal.h"
@@ -35,16 +37,18 @@ FoldLayout fold_layout(int d_in, int kv) {
   return F;
 }
 
-FoldWsLayout fold_ws_layout(int d, int d_in, int kv) {
+FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par) {
   FoldWsLayout W;
   W.At = kStatusBytes;
   W.Wx = W.At + align256((size_t)d_in * 2 * d * 2);
-  W.H64 = W.Wx + align256((size_t)2 * kv * 2 * d * 2);
+  W.blocks = W.Wx + align256((size_t)2 * kv * 2 * d * 2);
+  W.H64 = 0;
   W.linv = W.H64 + align256((size_t)d_in * d_in * 8);
   W.g = W.linv + align256((size_t)d_in * 64 * 8);
   W.r = W.g + align256((size_t)d_in * 8);
   W.scal = W.r + align256((size_t)d_in * 8);
-  W.total = W.scal + 256;
+  W.per_layer = W.scal + 256;
+  W.total = W.blocks + (size_t)n_par * W.per_layer;
   return W;
 }
 
@@ -187,8 +191,13 @@ __global__ __launch_bounds__(1024) void fold_bb_kernel(const float* b, int d, do
 // another of the same launch reads.
 __global__ __launch_bounds__(256) void fold_fsub_kernel(const double* L, int d, int i,
                                                         const double* linv, double* g,
-                                                        double* r) {
+                                                        double* r, size_t sP) {
   __shared__ double ri[FB];
+  const size_t off = blockIdx.y * sP;             // layer blockIdx.y of the group
+  L += off;
+  linv += off;
+  g += off;
+  r += off;
   const int t = threadIdx.x;
   if (t < FB) {
     const double* li = linv + (size_t)i * FB * FB + (size_t)t * FB;
@@ -253,44 +262,56 @@ __global__ __launch_bounds__(256) void fold_rt_kernel(const double* L, int d_in,
 
 }  // namespace
 
-hipError_t launch_fold(int d, int d_in, int kv, const uint16_t* A, const float* b,
-                       const uint16_t* w, const uint16_t* WK, const uint16_t* WV, void* out,
-                       void* ws, hipStream_t stream) {
+hipError_t launch_fold(int d, int d_in, int kv, const FoldLayerIn* layers, int G,
+                       void* const* out, void* ws, const FoldWsLayout& W, hipStream_t stream) {
   const FoldLayout F = fold_layout(d_in, kv);
-  const FoldWsLayout W = fold_ws_layout(d, d_in, kv);
-  unsigned char* o = static_cast<unsigned char*>(out);
   unsigned char* s = static_cast<unsigned char*>(ws);
   unsigned* status = reinterpret_cast<unsigned*>(s);
   uint16_t* At = reinterpret_cast<uint16_t*>(s + W.At);
   uint16_t* Wx = reinterpret_cast<uint16_t*>(s + W.Wx);
-  double* H = reinterpret_cast<double*>(s + W.H64);
-  double* linv = reinterpret_cast<double*>(s + W.linv);
-  double* g = reinterpret_cast<double*>(s + W.g);
-  double* r = reinterpret_cast<double*>(s + W.r);
-  double* scal = reinterpret_cast<double*>(s + W.scal);
-
-  hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream, A, d,
-                     d_in, At);
-  hipLaunchKernelGGL(fold_wsplit_kernel, dim3(2048), dim3(256), 0, stream, WK, WV, w, kv, d, Wx);
-  NtGemmArgs pa = {Wx, At, o + F.P, 2 * (int64_t)d, 2 * (int64_t)d, d_in, 2 * d,
-                   2 * kv / kTile, d_in / kTile, 0, 0};
-  hipLaunchKernelGGL(fold_gemm_kernel, dim3(pa.ntm * pa.ntn), dim3(kThreads), 0, stream, pa);
-  NtGemmArgs ha = {At, At, H, 2 * (int64_t)d, 2 * (int64_t)d, d_in, d, d_in / kTile,
-                   d_in / kTile, 1, 1};
-  hipLaunchKernelGGL(fold_gemm_kernel, dim3(ha.ntm * ha.ntn), dim3(kThreads), 0, stream, ha);
-  hipLaunchKernelGGL(fold_gemv_kernel, dim3((d_in + 2 * kv + 3) / 4), dim3(256), 0, stream, At,
-                     WK, WV, w, b, d, d_in, kv, g, reinterpret_cast<float*>(o + F.c));
-  hipLaunchKernelGGL(fold_bb_kernel, dim3(1), dim3(1024), 0, stream, b, d, scal);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if ((e = launch_cholesky(H, d_in, linv, status, stream)) != hipSuccess) return e;
+  auto blk = [&](int l) { return s + W.blocks + (size_t)l * W.per_layer; };
+  hipError_t e;
+  for (int l = 0; l < G; ++l) {
+    const FoldLayerIn& in = layers[l];
+    unsigned char* o = static_cast<unsigned char*>(out[l]);
+    double* H = reinterpret_cast<double*>(blk(l) + W.H64);
+    hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream, in.A,
+                       d, d_in, At);
+    hipLaunchKernelGGL(fold_wsplit_kernel, dim3(2048), dim3(256), 0, stream, in.WK, in.WV, in.w,
+                       kv, d, Wx);
+    NtGemmArgs pa = {Wx, At, o + F.P, 2 * (int64_t)d, 2 * (int64_t)d, d_in, 2 * d,
+                     2 * kv / kTile, d_in / kTile, 0, 0};
+    hipLaunchKernelGGL(fold_gemm_kernel, dim3(pa.ntm * pa.ntn), dim3(kThreads), 0, stream, pa);
+    NtGemmArgs ha = {At, At, H, 2 * (int64_t)d, 2 * (int64_t)d, d_in, d, d_in / kTile,
+                     d_in / kTile, 1, 1};
+    hipLaunchKernelGGL(fold_gemm_kernel, dim3(ha.ntm * ha.ntn), dim3(kThreads), 0, stream, ha);
+    hipLaunchKernelGGL(fold_gemv_kernel, dim3((d_in + 2 * kv + 3) / 4), dim3(256), 0, stream, At,
+                       in.WK, in.WV, in.w, in.b, d, d_in, kv,
+                       reinterpret_cast<double*>(blk(l) + W.g), reinterpret_cast<float*>(o + F.c));
+    hipLaunchKernelGGL(fold_bb_kernel, dim3(1), dim3(1024), 0, stream, in.b, d,
+                       reinterpret_cast<double*>(blk(l) + W.scal));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // the G factorizations and substitutions side by side (strides in doubles)
+  const size_t sP = W.per_layer / 8;
+  double* H0 = reinterpret_cast<double*>(blk(0) + W.H64);
+  double* linv0 = reinterpret_cast<double*>(blk(0) + W.linv);
+  if ((e = launch_cholesky(H0, d_in, linv0, status, stream, G, sP, sP)) != hipSuccess) return e;
   const int nb = d_in / FB;
   for (int i = 0; i < nb; ++i)
-    hipLaunchKernelGGL(fold_fsub_kernel, dim3(nb - i), dim3(256), 0, stream, H, d_in, i, linv, g, r);
-  hipLaunchKernelGGL(fold_finish_kernel, dim3(1), dim3(1024), 0, stream, r, scal, d_in,
-                     reinterpret_cast<float*>(o + F.r), reinterpret_cast<float*>(o + F.kappa));
-  hipLaunchKernelGGL(fold_rt_kernel, dim3(d_in / 64, d_in / 64), dim3(256), 0, stream, H, d_in,
-                     reinterpret_cast<uint16_t*>(o + F.R));
+    hipLaunchKernelGGL(fold_fsub_kernel, dim3(nb - i, G), dim3(256), 0, stream, H0, d_in, i,
+                       linv0, reinterpret_cast<double*>(blk(0) + W.g),
+                       reinterpret_cast<double*>(blk(0) + W.r), sP);
+  for (int l = 0; l < G; ++l) {
+    unsigned char* o = static_cast<unsigned char*>(out[l]);
+    const double* H = reinterpret_cast<const double*>(blk(l) + W.H64);
+    hipLaunchKernelGGL(fold_finish_kernel, dim3(1), dim3(1024), 0, stream,
+                       reinterpret_cast<const double*>(blk(l) + W.r),
+                       reinterpret_cast<const double*>(blk(l) + W.scal), d_in,
+                       reinterpret_cast<float*>(o + F.r), reinterpret_cast<float*>(o + F.kappa));
+    hipLaunchKernelGGL(fold_rt_kernel, dim3(d_in / 64, d_in / 64), dim3(256), 0, stream, H, d_in,
+                       reinterpret_cast<uint16_t*>(o + F.R));
+  }
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 namespace rf {
 
 constexpr int kMaxGroup = 32;   // layers sharing one fill launch
+constexpr int kMaxFoldGroup = 64;   // layers folded side by side
 constexpr int kTile = 256;      // fill/calibration tile edge (rows and features)
 constexpr size_t kStatusBytes = 256;
 // Device status bits kept in the first word of a fill or solve workspace.
@@ -49,17 +50,30 @@ struct FoldLayout {
 };
 FoldLayout fold_layout(int d_in, int kv);
 
-// Workspace of the fold (one layer at a time): [A^T | A^T] and [W_hi | W_lo] in bf16,
-// A^T A in fp32 and fp64, the diagonal-block inverses, A^T b and r in fp64, |b|^2.
+// Workspace of the fold: the status word, then the parts rebuilt for each layer
+// ([A^T | A^T] and [W_hi | W_lo] in bf16), then one block per layer of a group folded side
+// by side: A^T A in fp64 (the Cholesky works in place), the diagonal-block inverses, A^T b
+// and r in fp64, |b|^2.  Block offsets are from the block's start; `total` covers n_par
+// blocks.
 struct FoldWsLayout {
-  size_t At, Wx, H32, H64, linv, g, r, scal, total;
+  size_t At, Wx, blocks;
+  size_t H64, linv, g, r, scal, per_layer;
+  size_t total;
 };
-FoldWsLayout fold_ws_layout(int d, int d_in, int kv);
-// Per layer: A bf16 [d][d_in], b fp32 [d], w bf16 [d], W_K / W_V bf16 [kv][d] -> the
-// folded buffer.  A non-positive pivot of A^T A sets kStatusNotSpdBit.
-hipError_t launch_fold(int d, int d_in, int kv, const uint16_t* A, const float* b,
-                       const uint16_t* w, const uint16_t* WK, const uint16_t* WV, void* out,
-                       void* ws, hipStream_t stream);
+FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par);
+// One layer's plain fields: A bf16 [d][d_in], b fp32 [d], w bf16 [d], W_K / W_V bf16 [kv][d].
+struct FoldLayerIn {
+  const uint16_t* A;
+  const float* b;
+  const uint16_t* w;
+  const uint16_t* WK;
+  const uint16_t* WV;
+};
+// Folds G layers (G <= the n_par of W) into their buffers out[0 .. G-1]: the GEMMs layer by
+// layer, then one batched Cholesky and substitution for the G layers.  A non-positive pivot
+// of some A^T A sets kStatusNotSpdBit.
+hipError_t launch_fold(int d, int d_in, int kv, const FoldLayerIn* layers, int G,
+                       void* const* out, void* ws, const FoldWsLayout& W, hipStream_t stream);
 
 // Workspace layout of a fill call (bytes from the start of ws; per-layer offsets from the
 // start of that layer's block).
@@ -136,8 +150,11 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
 
 // Blocked fp64 Cholesky of the lower triangle of C [d][d] (d a multiple of 64), in place:
 // C's lower triangle becomes L (C = L L^T) and linv [d/64][64][64] the inverses of L's
-// 64 x 64 diagonal blocks.  A non-positive pivot sets kStatusNotSpdBit in *status.
-hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream);
+// 64 x 64 diagonal blocks.  A non-positive pivot sets kStatusNotSpdBit in *status.  A batch
+// of nbatch such matrices is factored side by side: matrix b at C + b sC with its
+// inverses at linv + b sL (strides in doubles).
+hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream,
+                           int nbatch, size_t sC, size_t sL);
 
 hipError_t launch_clear_status(unsigned* status, hipStream_t stream);
 

@@ -8,8 +8,10 @@
 //   means    mu = sums / n                                              fp64
 //   centre   C = G - n mu_S mu_S^T (G mirrored from its lower triangle);
 //            alpha = lambda tr(C) / d; C += alpha I                      fp64
-//   Cholesky blocked, 64-wide panels: diagonal block factor + its inverse, panel
-//            L_ik = A_ik L_kk^-T, trailing update A_ij -= L_ik L_jk^T    fp64
+//   Cholesky blocked, 64-wide blocks: diagonal block factor + its inverse, block
+//            column L_ik = A_ik L_kk^-T, update of the rest of its 256-wide panel;
+//            after each panel one trailing update A_ij -= L_ik L_jk^T over the
+//            panel's 256 columns (fp64 matrix cores)                    fp64
 //   inverse  W = L^-1 by blocked forward substitution on the identity;
 //            M = (C + alpha I)^-1 = W^T W                               fp64
 //   maps     A_l = C_l M with C_l = YX_l - n mu_l mu_S^T centred in fp64.  Each fp64
@@ -32,6 +34,7 @@ namespace rf {
 
 namespace {
 constexpr int NB = 64;        // Cholesky / substitution block
+constexpr int kCholPanel = 4; // 64-blocks per Cholesky panel: one trailing update per panel
 constexpr int LDT = NB + 1;   // padded LDS row (fp64)
 }  // namespace
 
@@ -195,10 +198,13 @@ __device__ __forceinline__ double recip(double p) {
 // the NOT_SPD bit and is taken as 1.
 constexpr int kDiagThreads = 1024, kDiagW = 4;
 __global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int d, int k,
-                                                                 double* linv, unsigned* status) {
+                                                                 double* linv, unsigned* status,
+                                                                 size_t sC, size_t sL) {
   __shared__ __attribute__((aligned(16))) double col[2][NB];   // column j (by j parity)
   __shared__ __attribute__((aligned(16))) double yrow[2][NB];  // row j of Y
   __shared__ double piv[NB];          // pivots d_j (after the NOT_SPD replacement)
+  C += blockIdx.y * sC;               // matrix blockIdx.y of a batch
+  linv += blockIdx.y * sL;
   double* blk = C + (size_t)k * NB * d + (size_t)k * NB;
   const int t = threadIdx.x;
   constexpr int TPR = NB / kDiagW;
@@ -265,11 +271,14 @@ __global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int 
   }
 }
 
-// Block row i = k + 1 + blockIdx.x:  L_ik = A_ik * Linv_kk^T.
+// Block row i = k + 1 + blockIdx.x:  L_ik = A_ik * Linv_kk^T (matrix blockIdx.y).
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* C, int d, int k,
-                                                         const double* linv) {
+                                                         const double* linv, size_t sC,
+                                                         size_t sL) {
   __shared__ double a[NB * LDT];
   __shared__ double li[NB * LDT];
+  C += blockIdx.y * sC;
+  linv += blockIdx.y * sL;
   const int i = k + 1 + blockIdx.x;
   double* blk = C + (size_t)i * NB * d + (size_t)k * NB;
   load64(a, blk, d, false);
@@ -282,16 +291,20 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* C, int d, int k
   store44(blk, d, acc, 1.0, false);
 }
 
-// Trailing blocks (i, j), k < j <= i:  A_ij -= L_ik L_jk^T.
-__global__ __launch_bounds__(256) void chol_update_kernel(double* C, int d, int k) {
+// Blocks (i, j) of the current panel's remaining columns, k < j < j_end, j <= i < d / 64:
+// A_ij -= L_ik L_jk^T (matrix blockIdx.y).  blockIdx.x counts the blocks column by column.
+__global__ __launch_bounds__(256) void chol_update_kernel(double* C, int d, int k, int j_end,
+                                                          size_t sC) {
   __shared__ double a[NB * LDT];
   __shared__ double b[NB * LDT];
-  const int e = blockIdx.x;
-  int jj = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
-  while ((jj + 1) * (jj + 2) / 2 <= e) ++jj;
-  while (jj * (jj + 1) / 2 > e) --jj;
-  const int ii_rel = jj, jj_rel = e - jj * (jj + 1) / 2;   // jj_rel <= ii_rel
-  const int i = k + 1 + ii_rel, j = k + 1 + jj_rel;
+  C += blockIdx.y * sC;
+  const int nbk = d / NB;
+  int j = k + 1, e = blockIdx.x;
+  while (j < j_end - 1 && e >= nbk - j) {
+    e -= nbk - j;
+    ++j;
+  }
+  const int i = j + e;
   load64(a, C + (size_t)i * NB * d + (size_t)k * NB, d, false);
   load64(b, C + (size_t)j * NB * d + (size_t)k * NB, d, false);
   __syncthreads();
@@ -299,6 +312,97 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* C, int d, int 
   zero44(acc);
   mac64(acc, a, b);
   store44(C + (size_t)i * NB * d + (size_t)j * NB, d, acc, -1.0, true);
+}
+
+// Trailing update after the panel of block columns [k0, k1): for the 64-blocks
+// k1 <= j <= i, A_ij -= sum_{k0 <= k < k1} L_ik L_jk^T (matrix blockIdx.y).  The trailing
+// matrix (rows and columns from 64 k1 on) is cut into 128 x 128 tiles (I, J), J <= I; when
+// its size is an odd number of 64-blocks the last tile row and column are half outside the
+// matrix.  Each wave owns one 64 x 64 block of the tile as 4 x 4 fp64 MFMA blocks (the
+// block above the diagonal of a diagonal tile, and blocks outside the matrix, are neither
+// computed nor stored).  The reduction runs over 16-wide slices through two LDS stages:
+// slice s + 1 is fetched into registers while slice s is multiplied.
+constexpr int kTrT = 128, kTrK = 16, kTrLd = kTrK + 2;   // padded rows stay 16-byte aligned
+__global__ __launch_bounds__(256, 2) void chol_trail_kernel(double* C, int d, int k0, int k1,
+                                                            size_t sC) {
+  __shared__ __attribute__((aligned(16))) double sa[2][kTrT * kTrLd];
+  __shared__ __attribute__((aligned(16))) double sb[2][kTrT * kTrLd];
+  C += blockIdx.y * sC;
+  const int e = blockIdx.x;
+  int I = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+  while ((I + 1) * (I + 2) / 2 <= e) ++I;
+  while (I * (I + 1) / 2 > e) --I;
+  const int J = e - I * (I + 1) / 2;
+  const int r0 = k1 * NB + I * kTrT, c0 = k1 * NB + J * kTrT;
+  const int kc0 = k0 * NB, nks = (k1 - k0) * NB / kTrK;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // loader: row tid / 2 of each operand, 8 doubles from column 8 (tid % 2) of the slice
+  const int lrow = tid >> 1, lcol = (tid & 1) * 8;
+  const bool va = r0 + lrow < d, vb = c0 + lrow < d;
+  const double* ga = C + (size_t)(va ? r0 + lrow : 0) * d + kc0 + lcol;
+  const double* gb = C + (size_t)(vb ? c0 + lrow : 0) * d + kc0 + lcol;
+  double2 ra[4], rb[4];
+  auto fetch = [&](int ks) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = va ? *reinterpret_cast<const double2*>(ga + ks + 2 * q) : double2{0.0, 0.0};
+      rb[q] = vb ? *reinterpret_cast<const double2*>(gb + ks + 2 * q) : double2{0.0, 0.0};
+    }
+  };
+  auto park = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<double2*>(&sa[buf][lrow * kTrLd + lcol + 2 * q]) = ra[q];
+      *reinterpret_cast<double2*>(&sb[buf][lrow * kTrLd + lcol + 2 * q]) = rb[q];
+    }
+  };
+  // this wave's 64 x 64 block of the tile
+  const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
+  const bool active = r0 + wr < d && c0 + wc < d && !(I == J && wc > wr);
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  fetch(0);
+  park(0);
+  __syncthreads();
+  for (int s = 0; s < nks; ++s) {
+    if (s + 1 < nks) fetch((s + 1) * kTrK);
+    if (active) {
+      const double* A = sa[s & 1];
+      const double* B = sb[s & 1];
+      const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+      for (int kk = 0; kk < kTrK; kk += 4) {
+        double a[4], b[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a[q] = A[(wr + 16 * q + m) * kTrLd + kk + kq];
+          b[q] = B[(wc + 16 * q + m) * kTrLd + kk + kq];
+        }
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj)
+            acc[bi][bj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+      }
+    }
+    if (s + 1 < nks) park((s + 1) & 1);   // the other stage: last read before the previous barrier
+    __syncthreads();
+  }
+  if (!active) return;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        double* p = C + (size_t)(r0 + wr + 16 * bi + (lane >> 4) + 4 * j) * d + c0 + wc +
+                    16 * bj + (lane & 15);
+        *p -= acc[bi][bj][j];
+      }
 }
 
 __global__ void identity_kernel(double* W, int d) {
@@ -528,16 +632,28 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
 
 }  // namespace
 
-hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream) {
+hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream,
+                           int nbatch, size_t sC, size_t sL) {
   const int nbk = d / NB;
-  for (int k = 0; k < nbk; ++k) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kDiagThreads), 0, stream, C, d, k, linv,
-                       status);
-    const int below = nbk - k - 1;
-    if (below > 0) {
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(below), dim3(256), 0, stream, C, d, k, linv);
-      hipLaunchKernelGGL(chol_update_kernel, dim3(below * (below + 1) / 2), dim3(256), 0, stream,
-                         C, d, k);
+  for (int k0 = 0; k0 < nbk; k0 += kCholPanel) {
+    const int k1 = k0 + kCholPanel < nbk ? k0 + kCholPanel : nbk;
+    for (int k = k0; k < k1; ++k) {
+      hipLaunchKernelGGL(chol_diag_kernel, dim3(1, nbatch), dim3(kDiagThreads), 0, stream, C, d,
+                         k, linv, status, sC, sL);
+      const int below = nbk - k - 1;
+      if (below > 0)
+        hipLaunchKernelGGL(chol_panel_kernel, dim3(below, nbatch), dim3(256), 0, stream, C, d, k,
+                           linv, sC, sL);
+      int thin = 0;
+      for (int j = k + 1; j < k1; ++j) thin += nbk - j;
+      if (thin > 0)
+        hipLaunchKernelGGL(chol_update_kernel, dim3(thin, nbatch), dim3(256), 0, stream, C, d, k,
+                           k1, sC);
+    }
+    if (k1 < nbk) {
+      const int m = (d - k1 * NB + kTrT - 1) / kTrT;
+      hipLaunchKernelGGL(chol_trail_kernel, dim3(m * (m + 1) / 2, nbatch), dim3(256), 0, stream,
+                         C, d, k0, k1, sC);
     }
   }
   return hipGetLastError();
@@ -573,7 +689,7 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
                      CL.sum_S, mu, w);
   hipLaunchKernelGGL(centre_kernel, dim3(gdd), dim3(256), 0, stream, G, mu, w, d, C);
   hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
-  if ((e = launch_cholesky(C, d, linv, status, stream)) != hipSuccess) return e;
+  if ((e = launch_cholesky(C, d, linv, status, stream, 1, 0, 0)) != hipSuccess) return e;
   hipLaunchKernelGGL(identity_kernel, dim3(gdd), dim3(256), 0, stream, W, d);
   for (int i = 0; i < nbk; ++i) {
     hipLaunchKernelGGL(fsub_rows_kernel, dim3(i + 1), dim3(256), 0, stream, W, d, i, linv);

@@ -545,9 +545,14 @@ size_t ridgefill_fold_bytes(const rf_shape* shape) {
   return rf::fold_layout(d_in_of(shape), shape->n_kv_heads * shape->head_dim).total;
 }
 
+size_t ridgefill_fold_workspace_bytes_ex(const rf_shape* shape, int32_t layers_at_once) {
+  if (check_shape(shape) != RF_OK || check_foldable(shape) != RF_OK || layers_at_once < 1) return 0;
+  return rf::fold_ws_layout(shape->d, d_in_of(shape), shape->n_kv_heads * shape->head_dim,
+                            layers_at_once).total;
+}
+
 size_t ridgefill_fold_workspace_bytes(const rf_shape* shape) {
-  if (check_shape(shape) != RF_OK || check_foldable(shape) != RF_OK) return 0;
-  return rf::fold_ws_layout(shape->d, d_in_of(shape), shape->n_kv_heads * shape->head_dim).total;
+  return ridgefill_fold_workspace_bytes_ex(shape, 1);
 }
 
 rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int32_t n_layers,
@@ -559,9 +564,15 @@ rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int
   if (n_layers > 0 && (!layers || !folded)) return fail(RF_E_INVALID, "layers or folded is NULL");
   if (!ws) return fail(RF_E_INVALID, "ws is NULL");
   const int d = shape->d, d_in = d_in_of(shape), kv = shape->n_kv_heads * shape->head_dim;
-  const rf::FoldWsLayout W = rf::fold_ws_layout(d, d_in, kv);
-  if (!aligned(ws, 256) || ws_bytes < W.total)
-    return fail(RF_E_WORKSPACE, "fold workspace must be 256-byte aligned and >= %zu bytes", W.total);
+  const rf::FoldWsLayout W1 = rf::fold_ws_layout(d, d_in, kv, 1);
+  if (!aligned(ws, 256) || ws_bytes < W1.total)
+    return fail(RF_E_WORKSPACE, "fold workspace must be 256-byte aligned and >= %zu bytes", W1.total);
+  // as many layers side by side as the workspace holds
+  size_t cap = n_layers > 0 ? (size_t)n_layers : 1;
+  if (cap > (size_t)rf::kMaxFoldGroup) cap = rf::kMaxFoldGroup;
+  const size_t fit = 1 + (ws_bytes - W1.total) / W1.per_layer;
+  const int n_par = (int)(fit < cap ? fit : cap);
+  const rf::FoldWsLayout W = rf::fold_ws_layout(d, d_in, kv, n_par);
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
     if (l.A_q) return fail(RF_E_UNSUPPORTED, "layer %d: int8 maps cannot be folded", i);
@@ -575,9 +586,14 @@ rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws), st);
   if (e != hipSuccess) return hip_fail(e, "status clear");
-  for (int i = 0; i < n_layers; ++i) {
-    const rf_layer& l = layers[i];
-    e = rf::launch_fold(d, d_in, kv, l.A, l.b, l.norm_w, l.W_K, l.W_V, folded[i], ws, st);
+  rf::FoldLayerIn in[rf::kMaxFoldGroup];
+  for (int l0 = 0; l0 < n_layers; l0 += n_par) {
+    const int G = n_layers - l0 < n_par ? n_layers - l0 : n_par;
+    for (int g = 0; g < G; ++g) {
+      const rf_layer& l = layers[l0 + g];
+      in[g] = {l.A, l.b, l.norm_w, l.W_K, l.W_V};
+    }
+    e = rf::launch_fold(d, d_in, kv, in, G, folded + l0, ws, W, st);
     if (e != hipSuccess) return hip_fail(e, "fold launch");
   }
   return ok();

@@ -130,13 +130,15 @@ def fold_offsets(case: Case):
     return 0, R, c, r, r + a(din * 4)
 
 
-def fold_layers(case: Case, inp, stream=None):
-    """Folded buffers of every layer (cached in inp["folded"]) and the fold's status."""
+def fold_layers(case: Case, inp, stream=None, layers_at_once=None):
+    """Folded buffers of every layer (cached in inp["folded"]) and the fold's status.  The
+    workspace folds layers_at_once layers side by side (default: all of them)."""
     dev = inp["xS"].device
     shape = make_shape(case)
     nb = B.ridgefill_fold_bytes(shape)
     assert nb > 0
-    ws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    g = layers_at_once or len(inp["layers"])
+    ws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, g), dtype=torch.uint8, device=dev)
     bufs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
     B.ridgefill_fold_maps(shape, inp["layers"], bufs, ws, stream)
     status = B.ridgefill_read_status(ws, stream)

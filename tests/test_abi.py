@@ -120,7 +120,13 @@ def test_fold_size_queries_and_errors():
     # P [2 kv][d_in] and R [d_in][d_in] in bf16, c, r and kappa in fp32
     assert fb >= (2 * 1024 * 4096 + 4096 * 4096) * 2 + (2 * 1024 + 4096 + 1) * 4
     assert fb % 256 == 0
-    assert B.ridgefill_fold_workspace_bytes(s) >= 4096 * 4096 * 8
+    w1 = B.ridgefill_fold_workspace_bytes(s)
+    assert w1 >= 4096 * 4096 * 8
+    # layers folded side by side: one fp64 A^T A block per layer, the rest shared
+    assert B.ridgefill_fold_workspace_bytes_ex(s, 1) == w1
+    w4 = B.ridgefill_fold_workspace_bytes_ex(s, 4)
+    assert (w4 - w1) % 3 == 0 and (w4 - w1) // 3 >= 4096 * 4096 * 8
+    assert B.ridgefill_fold_workspace_bytes_ex(s, 0) == 0
     # no predicted-input buffer: a folded fill's per-layer workspace is small
     f1 = B.ridgefill_fill_workspace_bytes(s, 25805, 1, B.RF_MAPS_FOLDED)
     f20 = B.ridgefill_fill_workspace_bytes(s, 25805, 20, B.RF_MAPS_FOLDED)

@@ -114,6 +114,37 @@ def test_folded_and_plain_fills_agree():
             assert e <= 5e-3
 
 
+def test_fold_group_size_does_not_change_the_buffers():
+    # layers folded one at a time and four side by side (one batched Cholesky): the
+    # per-layer arithmetic is the same, so the folded buffers agree bit for bit
+    case = _case(768, 4, 4, 64, 300, 20, 0, 16, 71, d_in=512)
+    inp = build_inputs(case)
+    one, st1 = fold_layers(case, inp, layers_at_once=1)
+    one = [t.clone() for t in one]
+    four, st4 = fold_layers(case, inp, layers_at_once=4)
+    assert st1 == B.RF_OK and st4 == B.RF_OK
+    three, st3 = fold_layers(case, inp, layers_at_once=3)   # groups of 3 and 1
+    assert st3 == B.RF_OK
+    for l in range(case.n_layers):
+        ref = fold_views(case, one[l])         # the fields; padding between them is unset
+        for other, tag in ((four[l], "4"), (three[l], "3")):
+            got = fold_views(case, other)
+            for name, x, y in zip(("P", "R", "c", "r", "kappa"), ref, got):
+                assert np.array_equal(np.asarray(x), np.asarray(y)), \
+                    f"layer {l} {name}: 1 vs {tag} at once"
+
+
+def test_fold_flags_rank_deficient_map_in_a_group():
+    # one singular layer among three folded side by side: the status says so
+    case = _case(256, 3, 2, 64, 300, 20, 0, 16, 72)
+    inp = build_inputs(case)
+    A = inp["layers"][1]["A"].clone()
+    A[:, 9] = 0
+    inp["layers"][1]["A"] = A
+    _, st = fold_layers(case, inp)
+    assert st == B.RF_E_NOT_SPD
+
+
 def test_fold_flags_rank_deficient_map():
     # a zero column of A makes A^T A singular: the pivot is exactly 0 and the status says so
     case = _case(256, 1, 2, 64, 300, 20, 0, 16, 68)

@@ -179,7 +179,8 @@ def test_8b_folded_full_size():
     inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
     shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
     fb = B.ridgefill_fold_bytes(shape)
-    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, len(inp["layers"])),
+                      dtype=torch.uint8, device=dev)
     bufs = [torch.empty(fb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
     print("8B folded: fold", flush=True)
     B.ridgefill_fold_maps(shape, inp["layers"], bufs, fws)
@@ -220,7 +221,8 @@ def _folded_full(cfg, knorm=False):
             lay["k_norm_w"] = torch.from_numpy(synth.key_norm_weight(cfg.head_dim, cfg.seed, l)).to(
                 dev).to(torch.bfloat16)
     shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
-    fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, len(inp["layers"])),
+                      dtype=torch.uint8, device=dev)
     bufs = [torch.empty(B.ridgefill_fold_bytes(shape), dtype=torch.uint8, device=dev)
             for _ in inp["layers"]]
     print(f"{cfg.name} folded: fold of {cfg.n_upper} layers", flush=True)
