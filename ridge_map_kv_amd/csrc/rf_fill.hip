@@ -50,6 +50,7 @@ struct FillKArgs {
   int has_scale, has_knorm;     // int8 map row scales; per-head key norm
   int folded;                   // folded layers: kv operands P [2 kv][d_in] and gathered x_S
   int kdim;                     // reduction length of the kv GEMM: d, or d_in when folded
+  int n_items;                  // tiles (or tile pairs) of the launch
 };
 static_assert(sizeof(FillKArgs) <= 4096, "kernel arguments must fit in 4 KB");
 
@@ -89,10 +90,10 @@ __device__ __forceinline__ void stage_put4(unsigned char* smem, int r, int f, fl
 __device__ __forceinline__ float lo16(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
 __device__ __forceinline__ float hi16(uint32_t x) { return bf16_to_f32(x >> 16); }
 
-__global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
+__device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   int g, tt, ft;
-  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  decode_tile(tile, a.ntt, a.nft, g, tt, ft);
   const FillLayerPtrs Lp = a.L[g];
   const int t0 = tt * kTile, f0 = ft * kTile;
   const int tid = threadIdx.x;
@@ -180,6 +181,10 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
+  fill_map_tile(a, xcd_remap(blockIdx.x, gridDim.x));
+}
+
 // Folded layers: per row, the sum of squares of (R x_S + r) over 256-feature tiles of the
 // upper-triangular factor R (A^T A = R^T R), written as 128-feature partials.  Row f of R
 // is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only.  A
@@ -190,47 +195,89 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 // down to the tile's first: tiles of different lengths then start together at column
 // d_in - 64, so the workgroups of one token tile read each slice of its x_S rows at about
 // the same time and share it in L2.
+//
+// One tile of the norm kernel: item `item` of the launch, half 0 (tile pp) or half 1 (tile
+// nft - 1 - pp).
+struct NormTile {
+  int g, tt, ft;
+};
+
+__device__ __forceinline__ NormTile norm_tile(const FillKArgs& a, int item, int half) {
+  NormTile t;
+  int pp;
+  decode_tile(xcd_remap(item, a.n_items), a.ntt, a.nft, t.g, t.tt, pp);
+  t.ft = half == 0 ? pp : a.d_in / kTile - 1 - pp;
+  return t;
+}
+
+// DMA operands of a norm tile: rows f0 .. f0 + 255 of R from its last column down, and the
+// tile's gathered x_S rows (the same rows for both tiles of an item).
+__device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile& t,
+                                              DmaOperand& Fo, DmaOperand& To) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int f0 = t.ft * kTile, t0 = t.tt * kTile;
+  const uint16_t* R = a.L[t.g].A;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
+    const int ce = dma_chunk_elems(r, lane);
+    Fo.base[p] = reinterpret_cast<const unsigned char*>(R + (size_t)(f0 + r0) * a.d_in +
+                                                         (a.d_in - kPipeBK));
+    Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
+    const int tok = t0 + r;
+    int row = 0;
+    if (tok < a.n_filled) {
+      const int x = a.idx[tok];
+      if (x >= 0 && x < a.P) row = x;
+    }
+    To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + (a.d_in - kPipeBK));
+    To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
+  }
+}
+
+// The norm kernel is persistent: one workgroup per CU (each holds 128 KB of LDS) takes
+// items blockIdx.x, blockIdx.x + gridDim.x, ..., each one or two tiles.  The loads of a
+// tile's first two slices are issued as soon as the previous tile's main loop has left
+// the LDS, before that tile's epilogue, so the epilogue arithmetic and stores overlap
+// them.  (The map and kv kernels, whose epilogues stage their outputs through that LDS,
+// stay one tile per workgroup.)  gridDim.x is a multiple of 8 or equal to n_items, so
+// item i runs on XCD i % 8 and xcd_remap's tile ranges hold.
 __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   __shared__ __attribute__((aligned(16))) float sr[kTile];
-  int g, tt, pp;
-  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, pp);
-  const FillLayerPtrs Lp = a.L[g];
   const int nft = a.d_in / kTile;
-  const int t0 = tt * kTile;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1, h = lane >> 5;
 
-  float* ssq = reinterpret_cast<float*>(a.layer_ws + g * a.per_layer + a.per_layer_h);
-
-  for (int half = 0; half < 2; ++half) {
-    const int ft = half == 0 ? pp : nft - 1 - pp;
-    if (half == 1 && ft == pp) break;                       // the middle tile of an odd nft
-    const int f0 = ft * kTile;
-    DmaOperand Fo, To;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
-      const int ce = dma_chunk_elems(r, lane);
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in +
-                                                           (a.d_in - kPipeBK));
-      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
-      // the same gathered x_S rows for both tiles; only the column offset moves
-      const int tok = t0 + r;
-      int row = 0;
-      if (tok < a.n_filled) {
-        const int t = a.idx[tok];
-        if (t >= 0 && t < a.P) row = t;
-      }
-      To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + (a.d_in - kPipeBK));
-      To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
-    }
-    const float my_r = Lp.b[f0 + tid];
-
+  int item = blockIdx.x, half = 0;
+  if (item >= a.n_items) return;
+  NormTile cur = norm_tile(a, item, 0);
+  DmaOperand Fo, To;
+  norm_operands(a, cur, Fo, To);
+  gemm_prologue<true>(Fo, To, a.d_in - cur.ft * kTile, smem);
+  for (;;) {
+    const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
+    const float my_r = a.L[cur.g].b[f0 + tid];
     f32x16 acc[4][4];
-    gemm_pipeline<true>(acc, Fo, To, a.d_in - f0, smem);   // ends with a barrier: sr is free
+    gemm_mainloop<true>(acc, Fo, To, a.d_in - f0, smem);   // ends with a barrier: LDS is free
 
+    // the next tile: the other half of this item (unless it is the middle tile of an odd
+    // nft), else the first half of the next item
+    int nitem = item, nhalf = half + 1;
+    if (nhalf == 2 || nft - 1 - cur.ft == cur.ft) {
+      nitem = item + gridDim.x;
+      nhalf = 0;
+    }
+    const bool more = nitem < a.n_items;
+    NormTile nxt = cur;
+    if (more) {
+      nxt = norm_tile(a, nitem, nhalf);
+      norm_operands(a, nxt, Fo, To);
+      gemm_prologue<true>(Fo, To, a.d_in - nxt.ft * kTile, smem);
+    }
+
+    float* ssq = reinterpret_cast<float*>(a.layer_ws + cur.g * a.per_layer + a.per_layer_h);
     sr[tid] = my_r;
     __syncthreads();
     float ss[4] = {0.f, 0.f, 0.f, 0.f};
@@ -256,9 +303,13 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
-        ssq[(size_t)chunk * a.mpad + tok] = ss[n];
+        ssq[(size_t)chunk * a.mpad + tok] = ss[n];        // chunk-major: coalesced
       }
     }
+    if (!more) break;
+    item = nitem;
+    half = nhalf;
+    cur = nxt;
   }
 }
 
@@ -304,10 +355,10 @@ __device__ __forceinline__ void head_sumsq(const f32x16 (&acc)[4][4], int n, int
 // MODE 0: fill (K and V tiles; RoPE, optional key norm and value rescale, paged stores).
 // MODE 1: value norms (V tiles only): |v| of every (row, head) into a.vnorm.
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
+__device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   int g, tt, ft;
-  decode_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntt, a.nft, g, tt, ft);
+  decode_tile(tile, a.ntt, a.nft, g, tt, ft);
   ft += a.f_base;
   const FillLayerPtrs Lp = a.L[g];
   const int t0 = tt * kTile, f0 = ft * kTile;
@@ -476,6 +527,11 @@ __global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
       *reinterpret_cast<u32x4*>(base + off + fo) = v;
     }
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void fill_kv_kernel(FillKArgs a) {
+  fill_kv_tile<MODE>(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // cos/sin of angle t * theta^(-2j/hd) for every row of the padded filled list (padding
@@ -680,6 +736,28 @@ FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned 
 
 namespace {
 
+// Workgroups of a persistent tile launch: one per CU, a multiple of 8 (the XCD count), or
+// the item count when that is smaller.  The CU count is read once per device.
+int persist_grid(int n_items) {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 256;
+    cus[dev] = n >= 8 ? n & ~7 : 8;
+  }
+  return n_items < cus[dev] ? n_items : cus[dev];
+}
+
+// A persistent tile launch of n_items items.
+template <typename Kernel>
+void launch_tiles(Kernel kernel, FillKArgs& a, int n_items, hipStream_t stream) {
+  a.n_items = n_items;
+  if (n_items > 0)
+    hipLaunchKernelGGL(kernel, dim3(persist_grid(n_items)), dim3(kThreads), 0, stream, a);
+}
+
 FillKArgs fill_args(const FillPlan& p, unsigned char* layer_ws) {
   FillKArgs a = {};
   a.xS = p.xS;
@@ -742,7 +820,7 @@ hipError_t launch_fill_group(const FillPlan& p, FillKArgs& a, int G, hipStream_t
     a.nft = (p.d_in / kTile + 1) / 2;          // pairs of R tiles
     {
       ProfileScope ps(RF_KERNEL_FILL_NORM, stream);
-      hipLaunchKernelGGL(fill_norm_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+      launch_tiles(fill_norm_kernel, a, G * a.ntt * a.nft, stream);
     }
     hipLaunchKernelGGL(rstd_folded_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a);
     a.nft = 2 * p.kv / kTile;

@@ -133,17 +133,41 @@ __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&
   }
 }
 
-// acc = F[256 x K] * T[256 x K]^T, K a multiple of 64.  Ends with a barrier, leaving the
-// 128 KB of LDS to the epilogue.  With REV the slices are taken from the last to the first:
-// the operands' base pointers then point at the last slice (reduction index K - 64), and
-// each further slice lies 128 bytes before the previous one.
+// acc = F[256 x K] * T[256 x K]^T, K a multiple of 64, in two parts: gemm_prologue issues
+// the first loads, gemm_mainloop does the rest and ends with a barrier, leaving the 128 KB
+// of LDS to the epilogue.  With REV the slices are taken from the last to the first: the
+// operands' base pointers then point at the last slice (reduction index K - 64), and each
+// further slice lies 128 bytes before the previous one.
 //
 // Two 64 KB stages.  The 16 load issues per wave that refill a stage are split: the first 8
 // follow the barrier that frees the stage (one after every other MFMA of the last 16-wide
 // step), the other 8 go out during the first step of the next slice, so the CU's address
 // unit never has all 64 of a slice queued inside one 16-MFMA window.
+//
+// gemm_prologue: the loads of slices 0 and 1 (32 per wave), into the two stages.  The LDS
+// must be free of readers (after a barrier).
 template <bool REV = false>
-__device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOperand& F,
+__device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOperand& T, int K,
+                                              unsigned char* smem) {
+  constexpr int kStep = REV ? -kPipeBK * 2 : kPipeBK * 2;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nk = K / kPipeBK;
+  const uint32_t base = lds_addr(smem);
+  for (int s = 0; s < 2 && s < nk; ++s) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      dma_block(F, p, s * kStep, base + s * kPipeStage, wave);
+      dma_block(T, p, s * kStep, base + s * kPipeStage + kPipeOp, wave);
+    }
+  }
+}
+
+// The rest of the pipeline, once gemm_prologue's loads are issued.  The wait for slice 0
+// counts on loads completing in order: while any load of slice 0 is pending, all 16 of
+// slice 1 are too, so at most 16 outstanding operations (stores issued after the
+// prologue included) means slice 0 has landed.
+template <bool REV = false>
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOperand& F,
                                               const DmaOperand& T, int K, unsigned char* smem) {
   constexpr int kStep = REV ? -kPipeBK * 2 : kPipeBK * 2;    // bytes from one slice to the next
   const int tid = threadIdx.x, lane = tid & 63;
@@ -158,13 +182,6 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
 
   const int nk = K / kPipeBK;
   const uint32_t base = lds_addr(smem);
-  for (int s = 0; s < 2 && s < nk; ++s) {
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      dma_block(F, p, s * kStep, base + s * kPipeStage, wave);
-      dma_block(T, p, s * kStep, base + s * kPipeStage + kPipeOp, wave);
-    }
-  }
   if (nk > 1)
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // slice 0 landed (slice 1: 16 loads)
   else
@@ -206,6 +223,14 @@ __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOper
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }
   __syncthreads();
+}
+
+// acc = F[256 x K] * T[256 x K]^T: gemm_prologue then gemm_mainloop.
+template <bool REV = false>
+__device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOperand& F,
+                                              const DmaOperand& T, int K, unsigned char* smem) {
+  gemm_prologue<REV>(F, T, K, smem);
+  gemm_mainloop<REV>(acc, F, T, K, smem);
 }
 
 }  // namespace
