@@ -152,9 +152,10 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
 // C's lower triangle becomes L (C = L L^T) and linv [d/64][64][64] the inverses of L's
 // 64 x 64 diagonal blocks.  A non-positive pivot sets kStatusNotSpdBit in *status.  A batch
 // of nbatch such matrices is factored side by side: matrix b at C + b sC with its
-// inverses at linv + b sL (strides in doubles).
+// inverses at linv + b sL (strides in doubles).  With U (nbatch 1 only) the same launches
+// also write U = L^-T [d][d] (upper triangle; U is cleared first).
 hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream,
-                           int nbatch, size_t sC, size_t sL);
+                           int nbatch, size_t sC, size_t sL, double* U = nullptr);
 
 hipError_t launch_clear_status(unsigned* status, hipStream_t stream);
 

@@ -12,8 +12,8 @@
 //            column L_ik = A_ik L_kk^-T, update of the rest of its 256-wide panel;
 //            after each panel one trailing update A_ij -= L_ik L_jk^T over the
 //            panel's 256 columns (fp64 matrix cores)                    fp64
-//   inverse  W = L^-1 by blocked forward substitution on the identity;
-//            M = (C + alpha I)^-1 = W^T W                               fp64
+//   inverse  U = L^-T built in the Cholesky's own launches (U L^T = I, column by
+//            column as L's block columns become final); M = (C + alpha I)^-1 = U U^T  fp64
 //   maps     A_l = C_l M with C_l = YX_l - n mu_l mu_S^T centred in fp64.  Each fp64
 //            operand x is split into bf16 parts x_hi = bf16(x), x_lo = bf16(x - x_hi),
 //            which hold it to about 2^-17; then
@@ -271,16 +271,40 @@ __global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int 
   }
 }
 
-// Block row i = k + 1 + blockIdx.x:  L_ik = A_ik * Linv_kk^T (matrix blockIdx.y).
+// The solve also needs the inverse factor.  It builds U = L^-T (upper triangular, 64-blocks
+// U[a][b], a <= b) inside the Cholesky's own launches, from U L^T = I:
+//   U[b][b] = Linv_bb^T,   U[a][b] = -(sum_{a <= k < b} U[a][k] L[b][k]^T) Linv_bb^T  (a < b).
+// U's storage at [a][b] accumulates the sum's negative as the columns k < b become final
+// (right-looking, like the trailing updates), and column b is finished once L's block
+// column b is: the sums need only L's rows, which the factorization has then produced.
+// U must start at zero.
+
+// Block row i = k + 1 + blockIdx.x (blockIdx.x < below):  L_ik = A_ik * Linv_kk^T (matrix
+// blockIdx.y).  With U, the blocks after those finish U's column k: block row
+// a = blockIdx.x - below (0 .. k) gets U[a][k] = S[a][k] Linv_kk^T, U[k][k] = Linv_kk^T.
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* C, int d, int k,
                                                          const double* linv, size_t sC,
-                                                         size_t sL) {
+                                                         size_t sL, double* U) {
   __shared__ double a[NB * LDT];
   __shared__ double li[NB * LDT];
   C += blockIdx.y * sC;
   linv += blockIdx.y * sL;
-  const int i = k + 1 + blockIdx.x;
-  double* blk = C + (size_t)i * NB * d + (size_t)k * NB;
+  const int below = d / NB - k - 1;
+  double* blk;
+  if ((int)blockIdx.x < below) {
+    blk = C + (size_t)(k + 1 + blockIdx.x) * NB * d + (size_t)k * NB;
+  } else {
+    const int ar = blockIdx.x - below;
+    blk = U + (size_t)ar * NB * d + (size_t)k * NB;
+    if (ar == k) {                                  // the diagonal block: Linv_kk transposed
+      const double* lk = linv + (size_t)k * NB * NB;
+      for (int e = threadIdx.x; e < NB * NB; e += blockDim.x) {
+        const int r = e >> 6, c = e & 63;
+        blk[(size_t)r * d + c] = lk[c * NB + r];
+      }
+      return;
+    }
+  }
   load64(a, blk, d, false);
   load64(li, linv + (size_t)k * NB * NB, NB, false);
   __syncthreads();
@@ -292,55 +316,91 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* C, int d, int k
 }
 
 // Blocks (i, j) of the current panel's remaining columns, k < j < j_end, j <= i < d / 64:
-// A_ij -= L_ik L_jk^T (matrix blockIdx.y).  blockIdx.x counts the blocks column by column.
+// A_ij -= L_ik L_jk^T (matrix blockIdx.y); blockIdx.x < nchol counts them column by column.
+// With U, the blocks after those update U's accumulators in the same columns:
+// U[ar][j] -= U[ar][k] L[j][k]^T for block rows ar <= k.
 __global__ __launch_bounds__(256) void chol_update_kernel(double* C, int d, int k, int j_end,
-                                                          size_t sC) {
+                                                          size_t sC, int nchol, double* U) {
   __shared__ double a[NB * LDT];
   __shared__ double b[NB * LDT];
   C += blockIdx.y * sC;
   const int nbk = d / NB;
-  int j = k + 1, e = blockIdx.x;
-  while (j < j_end - 1 && e >= nbk - j) {
-    e -= nbk - j;
-    ++j;
+  const double *sa, *sb;
+  double* out;
+  if ((int)blockIdx.x < nchol) {
+    int j = k + 1, e = blockIdx.x;
+    while (j < j_end - 1 && e >= nbk - j) {
+      e -= nbk - j;
+      ++j;
+    }
+    const int i = j + e;
+    sa = C + (size_t)i * NB * d + (size_t)k * NB;
+    sb = C + (size_t)j * NB * d + (size_t)k * NB;
+    out = C + (size_t)i * NB * d + (size_t)j * NB;
+  } else {
+    const int e = blockIdx.x - nchol;
+    const int ar = e % (k + 1), j = k + 1 + e / (k + 1);
+    sa = U + (size_t)ar * NB * d + (size_t)k * NB;
+    sb = C + (size_t)j * NB * d + (size_t)k * NB;
+    out = U + (size_t)ar * NB * d + (size_t)j * NB;
   }
-  const int i = j + e;
-  load64(a, C + (size_t)i * NB * d + (size_t)k * NB, d, false);
-  load64(b, C + (size_t)j * NB * d + (size_t)k * NB, d, false);
+  load64(a, sa, d, false);
+  load64(b, sb, d, false);
   __syncthreads();
   Acc64 acc;
   zero44(acc);
   mac64(acc, a, b);
-  store44(C + (size_t)i * NB * d + (size_t)j * NB, d, acc, -1.0, true);
+  store44(out, d, acc, -1.0, true);
 }
 
 // Trailing update after the panel of block columns [k0, k1): for the 64-blocks
 // k1 <= j <= i, A_ij -= sum_{k0 <= k < k1} L_ik L_jk^T (matrix blockIdx.y).  The trailing
 // matrix (rows and columns from 64 k1 on) is cut into 128 x 128 tiles (I, J), J <= I; when
 // its size is an odd number of 64-blocks the last tile row and column are half outside the
-// matrix.  Each wave owns one 64 x 64 block of the tile as 4 x 4 fp64 MFMA blocks (the
-// block above the diagonal of a diagonal tile, and blocks outside the matrix, are neither
-// computed nor stored).  The reduction runs over 16-wide slices through two LDS stages:
-// slice s + 1 is fetched into registers while slice s is multiplied.
+// matrix.  With U, the blocks from ntri on take U's accumulators of the columns after the
+// panel, rows before its end, as 128 x 128 tiles of a rectangle:
+// U[a][b] -= sum_{k0 <= k < k1} U[a][k] L[b][k]^T, a < k1 <= b.
+// Each wave owns one 64 x 64 block of a tile as 4 x 4 fp64 MFMA blocks (the block above
+// the diagonal of a diagonal tile, and blocks outside the region, are neither computed
+// nor stored).  The reduction runs over 16-wide slices through two LDS stages: slice s + 1
+// is fetched into registers while slice s is multiplied.
 constexpr int kTrT = 128, kTrK = 16, kTrLd = kTrK + 2;   // padded rows stay 16-byte aligned
 __global__ __launch_bounds__(256, 2) void chol_trail_kernel(double* C, int d, int k0, int k1,
-                                                            size_t sC) {
+                                                            size_t sC, int ntri, double* U) {
   __shared__ __attribute__((aligned(16))) double sa[2][kTrT * kTrLd];
   __shared__ __attribute__((aligned(16))) double sb[2][kTrT * kTrLd];
   C += blockIdx.y * sC;
   const int e = blockIdx.x;
-  int I = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
-  while ((I + 1) * (I + 2) / 2 <= e) ++I;
-  while (I * (I + 1) / 2 > e) --I;
-  const int J = e - I * (I + 1) / 2;
-  const int r0 = k1 * NB + I * kTrT, c0 = k1 * NB + J * kTrT;
+  const double *A, *B;
+  double* O;
+  int r0, c0, rend;
+  bool diag;
+  if (e < ntri) {
+    int I = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
+    while ((I + 1) * (I + 2) / 2 <= e) ++I;
+    while (I * (I + 1) / 2 > e) --I;
+    const int J = e - I * (I + 1) / 2;
+    A = B = O = C;
+    r0 = k1 * NB + I * kTrT;
+    c0 = k1 * NB + J * kTrT;
+    rend = d;
+    diag = I == J;
+  } else {
+    const int nI = (k1 * NB + kTrT - 1) / kTrT, u = e - ntri;
+    A = O = U;
+    B = C;
+    r0 = (u % nI) * kTrT;
+    c0 = k1 * NB + (u / nI) * kTrT;
+    rend = k1 * NB;
+    diag = false;
+  }
   const int kc0 = k0 * NB, nks = (k1 - k0) * NB / kTrK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // loader: row tid / 2 of each operand, 8 doubles from column 8 (tid % 2) of the slice
   const int lrow = tid >> 1, lcol = (tid & 1) * 8;
-  const bool va = r0 + lrow < d, vb = c0 + lrow < d;
-  const double* ga = C + (size_t)(va ? r0 + lrow : 0) * d + kc0 + lcol;
-  const double* gb = C + (size_t)(vb ? c0 + lrow : 0) * d + kc0 + lcol;
+  const bool va = r0 + lrow < rend, vb = c0 + lrow < d;
+  const double* ga = A + (size_t)(va ? r0 + lrow : 0) * d + kc0 + lcol;
+  const double* gb = B + (size_t)(vb ? c0 + lrow : 0) * d + kc0 + lcol;
   double2 ra[4], rb[4];
   auto fetch = [&](int ks) {
 #pragma unroll
@@ -358,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void chol_trail_kernel(double* C, int d, in
   };
   // this wave's 64 x 64 block of the tile
   const int wr = (w >> 1) * 64, wc = (w & 1) * 64;
-  const bool active = r0 + wr < d && c0 + wc < d && !(I == J && wc > wr);
+  const bool active = r0 + wr < rend && c0 + wc < d && !(diag && wc > wr);
   f64x4 acc[4][4];
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
@@ -371,16 +431,16 @@ __global__ __launch_bounds__(256, 2) void chol_trail_kernel(double* C, int d, in
   for (int s = 0; s < nks; ++s) {
     if (s + 1 < nks) fetch((s + 1) * kTrK);
     if (active) {
-      const double* A = sa[s & 1];
-      const double* B = sb[s & 1];
+      const double* As = sa[s & 1];
+      const double* Bs = sb[s & 1];
       const int m = lane & 15, kq = lane >> 4;
 #pragma unroll
       for (int kk = 0; kk < kTrK; kk += 4) {
         double a[4], b[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          a[q] = A[(wr + 16 * q + m) * kTrLd + kk + kq];
-          b[q] = B[(wc + 16 * q + m) * kTrLd + kk + kq];
+          a[q] = As[(wr + 16 * q + m) * kTrLd + kk + kq];
+          b[q] = Bs[(wc + 16 * q + m) * kTrLd + kk + kq];
         }
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)
@@ -399,61 +459,28 @@ __global__ __launch_bounds__(256, 2) void chol_trail_kernel(double* C, int d, in
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        double* p = C + (size_t)(r0 + wr + 16 * bi + (lane >> 4) + 4 * j) * d + c0 + wc +
+        double* p = O + (size_t)(r0 + wr + 16 * bi + (lane >> 4) + 4 * j) * d + c0 + wc +
                     16 * bj + (lane & 15);
         *p -= acc[bi][bj][j];
       }
 }
 
-__global__ void identity_kernel(double* W, int d) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)d * d) return;
-  const size_t r = idx / d, c = idx - r * d;
-  W[idx] = r == c ? 1.0 : 0.0;
+__global__ void zero_kernel(double* W, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    W[i] = 0.0;
 }
 
-// Forward substitution, block row i, column block cb = blockIdx.x <= i:
-// W_i,cb = Linv_ii * B_i,cb (in place).
-__global__ __launch_bounds__(256) void fsub_rows_kernel(double* W, int d, int i,
-                                                        const double* linv) {
-  __shared__ double li[NB * LDT];
-  __shared__ double bt[NB * LDT];
-  const int cb = blockIdx.x;
-  double* blk = W + (size_t)i * NB * d + (size_t)cb * NB;
-  load64(li, linv + (size_t)i * NB * NB, NB, false);
-  load64(bt, blk, d, true);
-  __syncthreads();
-  Acc64 acc;
-  zero44(acc);
-  mac64(acc, li, bt);
-  __syncthreads();
-  store44(blk, d, acc, 1.0, false);
-}
-
-// B_m,cb -= L_mi W_i,cb for m > i, cb <= i;  blockIdx.x = (m - i - 1) * (i + 1) + cb.
-__global__ __launch_bounds__(256) void fsub_update_kernel(double* W, const double* C, int d, int i) {
-  __shared__ double l[NB * LDT];
-  __shared__ double wt[NB * LDT];
-  const int m = i + 1 + blockIdx.x / (i + 1), cb = blockIdx.x % (i + 1);
-  load64(l, C + (size_t)m * NB * d + (size_t)i * NB, d, false);
-  load64(wt, W + (size_t)i * NB * d + (size_t)cb * NB, d, true);
-  __syncthreads();
-  Acc64 acc;
-  zero44(acc);
-  mac64(acc, l, wt);
-  store44(W + (size_t)m * NB * d + (size_t)cb * NB, d, acc, -1.0, true);
-}
-
-// M = W^T W for lower tiles (ab >= bb), mirrored: M[a][b] = sum_k W[k][a] W[k][b], k >= ab.
+// M = U U^T for lower tiles (ab >= bb), mirrored: M[a][b] = sum_k U[a][k] U[b][k], k >= ab.
 // bf16 parts of an fp64 value: hi = bf16(x), lo = bf16(x - hi); |x - hi - lo| <= ~2^-17 |x|.
 __device__ __forceinline__ void split_bf16(double x, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16((float)x);
   lo = f32_to_bf16((float)(x - (double)bf16_to_f32(hi)));
 }
 
-// M = W^T W for one lower tile pair, written to both triangles in fp64 and as the GEMM
-// operand Mx [d][3d] = [M_hi | M_lo | M_hi] (bf16).
-__global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double* M64, uint16_t* Mx) {
+// M = U U^T (= W^T W with W = L^-1) for one lower tile pair, written to both triangles in
+// fp64 and as the GEMM operand Mx [d][3d] = [M_hi | M_lo | M_hi] (bf16).
+__global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double* M64, uint16_t* Mx) {
   __shared__ double wa[NB * LDT];
   __shared__ double wb[NB * LDT];
   const int e = blockIdx.x;
@@ -465,8 +492,8 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* W, int d, double
   Acc64 acc;
   zero44(acc);
   for (int kb = ab; kb < nbk; ++kb) {
-    load64(wa, W + (size_t)kb * NB * d + (size_t)ab * NB, d, true);
-    load64(wb, W + (size_t)kb * NB * d + (size_t)bb * NB, d, true);
+    load64(wa, U + (size_t)ab * NB * d + (size_t)kb * NB, d, false);
+    load64(wb, U + (size_t)bb * NB * d + (size_t)kb * NB, d, false);
     __syncthreads();
     mac64(acc, wa, wb);
     __syncthreads();
@@ -633,27 +660,35 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
 }  // namespace
 
 hipError_t launch_cholesky(double* C, int d, double* linv, unsigned* status, hipStream_t stream,
-                           int nbatch, size_t sC, size_t sL) {
+                           int nbatch, size_t sC, size_t sL, double* U) {
   const int nbk = d / NB;
+  if (U) {
+    if (nbatch != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, stream, U, (size_t)d * d);
+  }
   for (int k0 = 0; k0 < nbk; k0 += kCholPanel) {
     const int k1 = k0 + kCholPanel < nbk ? k0 + kCholPanel : nbk;
     for (int k = k0; k < k1; ++k) {
       hipLaunchKernelGGL(chol_diag_kernel, dim3(1, nbatch), dim3(kDiagThreads), 0, stream, C, d,
                          k, linv, status, sC, sL);
       const int below = nbk - k - 1;
-      if (below > 0)
-        hipLaunchKernelGGL(chol_panel_kernel, dim3(below, nbatch), dim3(256), 0, stream, C, d, k,
-                           linv, sC, sL);
+      const int npanel = below + (U ? k + 1 : 0);
+      if (npanel > 0)
+        hipLaunchKernelGGL(chol_panel_kernel, dim3(npanel, nbatch), dim3(256), 0, stream, C, d, k,
+                           linv, sC, sL, U);
       int thin = 0;
       for (int j = k + 1; j < k1; ++j) thin += nbk - j;
-      if (thin > 0)
-        hipLaunchKernelGGL(chol_update_kernel, dim3(thin, nbatch), dim3(256), 0, stream, C, d, k,
-                           k1, sC);
+      const int nthin = thin + (U ? (k + 1) * (k1 - 1 - k) : 0);
+      if (nthin > 0)
+        hipLaunchKernelGGL(chol_update_kernel, dim3(nthin, nbatch), dim3(256), 0, stream, C, d, k,
+                           k1, sC, thin, U);
     }
     if (k1 < nbk) {
       const int m = (d - k1 * NB + kTrT - 1) / kTrT;
-      hipLaunchKernelGGL(chol_trail_kernel, dim3(m * (m + 1) / 2, nbatch), dim3(256), 0, stream,
-                         C, d, k0, k1, sC);
+      const int ntri = m * (m + 1) / 2;
+      const int nrect = U ? ((k1 * NB + kTrT - 1) / kTrT) * m : 0;
+      hipLaunchKernelGGL(chol_trail_kernel, dim3(ntri + nrect, nbatch), dim3(256), 0, stream, C,
+                         d, k0, k1, sC, ntri, U);
     }
   }
   return hipGetLastError();
@@ -689,14 +724,8 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
                      CL.sum_S, mu, w);
   hipLaunchKernelGGL(centre_kernel, dim3(gdd), dim3(256), 0, stream, G, mu, w, d, C);
   hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
-  if ((e = launch_cholesky(C, d, linv, status, stream, 1, 0, 0)) != hipSuccess) return e;
-  hipLaunchKernelGGL(identity_kernel, dim3(gdd), dim3(256), 0, stream, W, d);
-  for (int i = 0; i < nbk; ++i) {
-    hipLaunchKernelGGL(fsub_rows_kernel, dim3(i + 1), dim3(256), 0, stream, W, d, i, linv);
-    const int below = nbk - i - 1;
-    if (below > 0)
-      hipLaunchKernelGGL(fsub_update_kernel, dim3(below * (i + 1)), dim3(256), 0, stream, W, C, d, i);
-  }
+  // L and U = L^-T together, then M = U U^T
+  if ((e = launch_cholesky(C, d, linv, status, stream, 1, 0, 0, W)) != hipSuccess) return e;
   hipLaunchKernelGGL(wtw_kernel, dim3(nbk * (nbk + 1) / 2), dim3(256), 0, stream, W, d, M64, Mx);
   hipLaunchKernelGGL(mv_kernel, dim3((d + 3) / 4), dim3(256), 0, stream, M64, mu, d, v);
   hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, stream, v, mu, d, w);
