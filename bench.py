@@ -226,9 +226,8 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=Fa
             lay["k_norm_w"] = (1 + 0.1 * torch.randn(cfg.head_dim, generator=g, device=dev)).to(
                 torch.bfloat16)
     layers = inp["layers"]
-    copy = None
-    if streamed:
-        copy = torch.cuda.Stream()
+    copy = torch.cuda.Stream() if streamed else None
+    if streamed and not folded:
         host = []
         for lay in layers:
             h = dict(lay)
@@ -254,6 +253,13 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=Fa
         if B.ridgefill_read_status(fws) != B.RF_OK:
             raise SystemExit(f"fold reported a device status for {cfg.name}")
         del fws
+        if streamed:                                   # folded buffers to page-locked host memory
+            host = []
+            for b in bufs:
+                h = torch.empty(b.shape, dtype=b.dtype, pin_memory=True)
+                h.copy_(b.cpu())
+                host.append(h)
+            bufs = host
         layers = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"],
                        **({"k_norm_w": lay["k_norm_w"]} if knorm else {}))
                   for l, lay in enumerate(layers)]
@@ -275,7 +281,8 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=Fa
     flops = cfg.fill_flops()
     line = {"workload": cfg.name, "d": cfg.d, "d_in": cfg.width, "upper_layers": cfg.n_upper,
             "N": cfg.N, "T": cfg.T, "filled_rows": nf,
-            "maps": ("folded (bf16 P and R)" if folded else
+            "maps": ("folded (bf16 P and R)" + (" streamed from pinned host memory" if streamed
+                                                else "") if folded else
                      ("int8" if int8 else "bf16") + (" streamed from pinned host memory" if streamed
                                                      else " resident")),
             "key_norm": knorm, "ms_per_step": ms, "filled_rows_per_s": nf / (ms * 1e-3),
@@ -295,7 +302,7 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=Fa
 
 def run_variants(dev):
     """The fill's variants at full size: the 27B-shaped workload with bf16, int8, int8
-    host-streamed maps and folded layers; the Qwen3-8B-shaped workload with and without the
+    host-streamed maps and folded layers (resident and host-streamed); the Qwen3-8B-shaped workload with and without the
     per-head key norm (and folded with it); a split state twice as wide as the layers; value-rescale factors over c = 512
     tail rows of every 27B upper layer; selection of the exact rows of the 8B prefix."""
     import torch
@@ -303,7 +310,8 @@ def run_variants(dev):
     from ridge_map_kv_amd import configs
 
     res = {}
-    log("bench: variants: 27B-shaped fill (bf16 resident, int8 resident, int8 streamed, folded)")
+    log("bench: variants: 27B-shaped fill (bf16 resident, int8 resident, int8 streamed, folded, "
+        "folded streamed)")
     line, (inp, shape) = fill_variant(configs.QWEN27B, dev, keep=True)
     res["27b_bf16_resident"] = line
     # value-rescale factors on the same layers: c = 512 tail rows, exact inputs drawn as
@@ -329,6 +337,8 @@ def run_variants(dev):
     res["27b_int8_streamed_4_layer_groups"] = fill_variant(configs.QWEN27B, dev, int8=True,
                                                            streamed=True, ws_layers=4)
     res["27b_folded"] = fill_variant(configs.QWEN27B, dev, folded=True)
+    res["27b_folded_streamed_4_layer_groups"] = fill_variant(configs.QWEN27B, dev, folded=True,
+                                                             streamed=True, ws_layers=4)
     log("bench: variants: Qwen3-8B-shaped fill with and without key norm; wide split state")
     res["qwen3_8b"] = fill_variant(configs.QWEN3_8B, dev)
     res["qwen3_8b_key_norm"] = fill_variant(configs.QWEN3_8B, dev, knorm=True)

@@ -187,12 +187,13 @@ size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled
 /* ------------------------------------------------------------------------------
  * Fill with host-resident maps.  Section "Ridge map ...", map size paragraph: maps can
  * stay in GPU memory or be streamed from host memory one layer at a time.  Same
- * computation and arguments as ridgefill_fill, except that every layer's A (or A_q) is
- * a HOST pointer, ideally page-locked (hipHostMalloc) so that the copies run
- * asynchronously.  Layers are processed in groups sized by the workspace
- * (ridgefill_fill_workspace_bytes_ex with RF_MAPS_STREAMED, plus RF_MAPS_INT8 for int8
- * maps); group g's maps are copied on `copy_stream` into landing slot g % 2 while group
- * g - 1 computes on `stream`.  copy_stream must be a different stream; both must stay
+ * computation and arguments as ridgefill_fill, except that every layer's A (or A_q), or
+ * for folded layers its whole folded buffer, is a HOST pointer, ideally page-locked
+ * (hipHostMalloc) so that the copies run asynchronously.  Layers are processed in groups
+ * sized by the workspace (ridgefill_fill_workspace_bytes_ex with RF_MAPS_STREAMED, plus
+ * RF_MAPS_INT8 for int8 maps or RF_MAPS_FOLDED for folded layers); group g's maps (or
+ * folded buffers) are copied on `copy_stream` into landing slot g % 2 while group g - 1
+ * computes on `stream`.  copy_stream must be a different stream; both must stay
  * valid until the work completes.  The results are bit-identical to ridgefill_fill's.
  * ------------------------------------------------------------------------------ */
 rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
@@ -233,8 +234,9 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
  * fp32 accumulation, one bf16 rounding of P); A^T A with exact products and fp32
  * accumulation; Cholesky, r and kappa in fp64; R rounded to bf16 once; c in fp64
  * rounded to fp32.
- * Folded layers work with ridgefill_fill (not the streamed fill); all layers of a fill
- * call must be folded or none.  ridgefill_value_scale always uses the plain fields.
+ * Folded layers work with ridgefill_fill and, from host memory, ridgefill_fill_streamed;
+ * all layers of a fill call must be folded or none.  ridgefill_value_scale always uses
+ * the plain fields.
  * ------------------------------------------------------------------------------ */
 size_t ridgefill_fold_bytes(const rf_shape* shape);
 size_t ridgefill_fold_workspace_bytes(const rf_shape* shape);

@@ -713,7 +713,7 @@ hipError_t launch_clear_status(unsigned* status, hipStream_t stream) {
   return hipGetLastError();
 }
 
-FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned flags) {
+FillWsLayout fill_ws_layout(int d, int d_in, int hd, int kv, int64_t n_filled, unsigned flags) {
   FillWsLayout L = {};
   const int64_t mpad = (n_filled + kTile - 1) / kTile * kTile;
   const size_t table = align256((size_t)mpad * (hd / 2) * sizeof(float));
@@ -728,7 +728,10 @@ FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned 
   const size_t map_elems = (size_t)d * d_in;
   L.expand = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
   L.land = L.expand + ((flags & kWsInt8) ? align256(map_elems * 2) : 0);
-  L.land_slot = (flags & kWsStreamed) ? align256(map_elems * ((flags & kWsInt8) ? 1 : 2)) : 0;
+  // a landing slot holds one layer's streamed map, or its whole folded buffer
+  if (flags & kWsStreamed)
+    L.land_slot = folded ? fold_layout(d_in, kv).total
+                         : align256(map_elems * ((flags & kWsInt8) ? 1 : 2));
   L.per_layer = L.land + 2 * L.land_slot;
   L.hbuf = L.fixed;
   return L;
@@ -893,7 +896,9 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
   if (e != hipSuccess) return e;
   unsigned char* lws = reinterpret_cast<unsigned char*>(p.hbuf);
   const bool int8 = (p.flags & kWsInt8) != 0;
-  const size_t map_bytes = (size_t)p.d * p.d_in * (int8 ? 1 : 2);
+  const bool folded = (p.flags & kWsFolded) != 0;
+  const FoldLayout F = fold_layout(p.d_in, p.kv);
+  const size_t map_bytes = folded ? F.total : (size_t)p.d * p.d_in * (int8 ? 1 : 2);
   const int gsize = group_size(n_layers, p.group);
   int gi = 0;
   for (int l0 = 0; l0 < n_layers; l0 += gsize, ++gi) {
@@ -905,12 +910,26 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
     for (int g = 0; g < G; ++g) {
       a.L[g] = layers[l0 + g];
       unsigned char* land = lws + g * p.L.per_layer + p.L.land + slot * p.L.land_slot;
-      const void* src = int8 ? static_cast<const void*>(layers[l0 + g].Aq)
-                             : static_cast<const void*>(layers[l0 + g].A);
+      // a folded layer's A points at R inside its host buffer: the buffer starts F.R before
+      const void* src = int8     ? static_cast<const void*>(layers[l0 + g].Aq)
+                        : folded ? static_cast<const void*>(
+                                       reinterpret_cast<const unsigned char*>(layers[l0 + g].A) - F.R)
+                                 : static_cast<const void*>(layers[l0 + g].A);
       if ((e = hipMemcpyAsync(land, src, map_bytes, hipMemcpyHostToDevice, copy_stream)) != hipSuccess)
         return e;
-      if (int8) codes[g] = reinterpret_cast<const int8_t*>(land);
-      else a.L[g].A = reinterpret_cast<const uint16_t*>(land);
+      if (int8) {
+        codes[g] = reinterpret_cast<const int8_t*>(land);
+      } else if (folded) {
+        const uint16_t* P = reinterpret_cast<const uint16_t*>(land + F.P);
+        a.L[g].A = reinterpret_cast<const uint16_t*>(land + F.R);
+        a.L[g].b = reinterpret_cast<const float*>(land + F.r);
+        a.L[g].WK = P;
+        a.L[g].WV = P + (size_t)p.kv * p.d_in;
+        a.L[g].fc = reinterpret_cast<const float*>(land + F.c);
+        a.L[g].kap = reinterpret_cast<const float*>(land + F.kappa);
+      } else {
+        a.L[g].A = reinterpret_cast<const uint16_t*>(land);
+      }
     }
     if ((e = hipEventRecord(ev.ready[slot], copy_stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, ev.ready[slot], 0)) != hipSuccess) return e;

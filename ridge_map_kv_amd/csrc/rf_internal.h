@@ -81,7 +81,7 @@ struct FillWsLayout {
   size_t rope_cos, rope_sin, row_slot, hbuf, fixed;
   size_t per_layer_h, per_layer_ssq, per_layer_rstd, expand, land, land_slot, per_layer;
 };
-FillWsLayout fill_ws_layout(int d, int d_in, int hd, int64_t n_filled, unsigned flags);
+FillWsLayout fill_ws_layout(int d, int d_in, int hd, int kv, int64_t n_filled, unsigned flags);
 
 struct FillPlan {
   int d, d_in, n_kv, hd, kv;

@@ -81,7 +81,7 @@ rf_status check_foldable(const rf_shape* s) {
 }
 
 // Checks shared by the resident and the streamed fill; fills the plan and the layer
-// pointers.  `streamed`: the maps (A or A_q) are host pointers.
+// pointers.  `streamed`: the maps (A or A_q), or the folded buffers, are host pointers.
 rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
                        int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
                        const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv, void* ws,
@@ -108,8 +108,6 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
   if (folded) {
     rf_status fs = check_foldable(shape);
     if (fs != RF_OK) return fs;
-    if (streamed)
-      return fail(RF_E_UNSUPPORTED, "folded layers are not supported by the streamed fill");
   }
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
@@ -142,7 +140,8 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
   }
   const unsigned flags = (int8 ? rf::kWsInt8 : 0u) | (streamed ? rf::kWsStreamed : 0u) |
                          (folded ? rf::kWsFolded : 0u);
-  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim, n_filled, flags);
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim,
+                                                shape->n_kv_heads * shape->head_dim, n_filled, flags);
   if (ws_bytes < L.fixed + L.per_layer)
     return fail(RF_E_WORKSPACE, "workspace %zu bytes < %zu needed for one layer", ws_bytes,
                 L.fixed + L.per_layer);
@@ -265,11 +264,11 @@ size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled
   if (check_shape(shape) != RF_OK || n_filled < 0 || n_layers < 1 ||
       (map_flags & ~(RF_MAPS_INT8 | RF_MAPS_STREAMED | RF_MAPS_FOLDED)))
     return 0;
-  if ((map_flags & RF_MAPS_FOLDED) &&
-      ((map_flags & (RF_MAPS_INT8 | RF_MAPS_STREAMED)) || check_foldable(shape) != RF_OK))
+  if ((map_flags & RF_MAPS_FOLDED) && ((map_flags & RF_MAPS_INT8) || check_foldable(shape) != RF_OK))
     return 0;
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim,
-                                                n_filled, map_flags_of(map_flags));
+                                                shape->n_kv_heads * shape->head_dim, n_filled,
+                                                map_flags_of(map_flags));
   const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
   return L.fixed + (size_t)g * L.per_layer;
 }
@@ -335,7 +334,8 @@ size_t ridgefill_value_scale_workspace_bytes(const rf_shape* shape, int64_t c, i
                                              int32_t map_flags) {
   if (check_shape(shape) != RF_OK || c < 1 || n_layers < 1 || (map_flags & ~RF_MAPS_INT8))
     return 0;
-  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim, c,
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim,
+                                                shape->n_kv_heads * shape->head_dim, c,
                                                 map_flags_of(map_flags));
   const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
   const rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, g);
@@ -376,7 +376,8 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
                   "alignment", i);
   }
   const unsigned flags = int8 ? rf::kWsInt8 : 0u;
-  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim, c, flags);
+  const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim,
+                                                shape->n_kv_heads * shape->head_dim, c, flags);
   const int gmax = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
   // the largest group the workspace holds: fixed part for that group + 2 blocks per layer
   int group = 0;

@@ -107,11 +107,12 @@ def make_shape(case: Case):
 
 
 def host_maps(layers: list[dict]) -> list[dict]:
-    """The same layers with their maps (A or A_q) copied to page-locked host tensors."""
+    """The same layers with their maps (A or A_q, or the folded buffer) copied to
+    page-locked host tensors."""
     out = []
     for lay in layers:
         h = dict(lay)
-        key = "A_q" if "A_q" in lay else "A"
+        key = "folded" if "folded" in lay else "A_q" if "A_q" in lay else "A"
         pinned = torch.empty(lay[key].shape, dtype=lay[key].dtype, pin_memory=True)
         pinned.copy_(lay[key].cpu())
         h[key] = pinned
@@ -174,14 +175,19 @@ def run_fill(case: Case, inp, filled: np.ndarray, ws_layers: int | None = None, 
     idx = torch.from_numpy(np.asarray(filled, dtype=np.int32)).to(dev)
     flags = case.map_flags | (B.RF_MAPS_STREAMED if streamed else 0)
     if folded:
-        flags = B.RF_MAPS_FOLDED
+        flags = B.RF_MAPS_FOLDED | (B.RF_MAPS_STREAMED if streamed else 0)
         if "folded" not in inp:
             _, st = fold_layers(case, inp, stream)
             assert st == B.RF_OK, f"fold status {st}"
     nbytes = B.ridgefill_fill_workspace_bytes(shape, max(nf, 1),
                                               ws_layers if ws_layers else case.n_layers, flags)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    if folded:
+    if folded and streamed:
+        layers = host_maps(folded_layer_dicts(inp))
+        copy = torch.cuda.Stream()
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, layers, inp["table"],
+                         case.page_size, inp["num_pages"], ws, stream=stream, copy_stream=copy)
+    elif folded:
         B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, nf, folded_layer_dicts(inp),
                          inp["table"], case.page_size, inp["num_pages"], ws, stream=stream)
     elif streamed:

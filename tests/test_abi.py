@@ -137,7 +137,9 @@ def test_fold_size_queries_and_errors():
     assert B.ridgefill_fill_workspace_bytes(wide, 100, 1, B.RF_MAPS_FOLDED) == 0
     assert B.ridgefill_fold_bytes(B.make_shape(4096, 8, 128, d_in=4032)) == 0
     assert B.ridgefill_fill_workspace_bytes(s, 100, 1, B.RF_MAPS_FOLDED | B.RF_MAPS_INT8) == 0
-    assert B.ridgefill_fill_workspace_bytes(s, 100, 1, B.RF_MAPS_FOLDED | B.RF_MAPS_STREAMED) == 0
+    # folded layers streamed from host memory: two landing slots of one folded buffer per layer
+    fs1 = B.ridgefill_fill_workspace_bytes(s, 100, 1, B.RF_MAPS_FOLDED | B.RF_MAPS_STREAMED)
+    assert fs1 >= B.ridgefill_fill_workspace_bytes(s, 100, 1, B.RF_MAPS_FOLDED) + 2 * fb
     arr = (B.rf_layer * 1)()
     assert L.ridgefill_fold_maps(C.byref(wide), arr, 1, None, None, 0, None) == B.RF_E_SHAPE
     assert L.ridgefill_fold_maps(C.byref(s), arr, 1, None, None, 0, None) == B.RF_E_INVALID

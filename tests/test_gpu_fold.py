@@ -171,7 +171,8 @@ def test_folded_argument_errors():
     with pytest.raises(RuntimeError, match="folded"):
         B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, mixed, inp["table"],
                          case.page_size, inp["num_pages"], ws)
-    with pytest.raises(RuntimeError, match="streamed"):
+    # the streamed fill needs landing slots: a workspace sized for the resident fill is short
+    with pytest.raises(RuntimeError, match="workspace"):
         B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, lays, inp["table"],
                          case.page_size, inp["num_pages"], ws, copy_stream=torch.cuda.Stream())
     small = torch.empty(4096, dtype=torch.uint8, device=dev)
@@ -201,3 +202,23 @@ def test_folded_group_split_is_bit_identical():
         for key in ("k_pages", "v_pages"):
             assert torch.equal(a["layers"][l][key].view(torch.int16),
                                b["layers"][l][key].view(torch.int16)), f"layer {l} {key}"
+
+
+def test_streamed_folded_layers_bit_identical():
+    # folded buffers in page-locked host memory, 5 layers through a workspace that holds 2:
+    # groups of 2, 2, 1, so both landing slots are reused; the caches match the resident
+    # folded fill bit for bit
+    case = _case(512, 5, 2, 128, 700, 100, 60, 16, 73, knorm=True, vscale=True)
+    f = _filled(case)
+    a = build_inputs(case)
+    b = build_inputs(case)
+    assert run_fill(case, a, f, folded=True) == B.RF_OK
+    b["folded"] = a["folded"]
+    assert run_fill(case, b, f, folded=True, streamed=True, ws_layers=2) == B.RF_OK
+    torch.cuda.synchronize()
+    for l in range(case.n_layers):
+        for key in ("k_pages", "v_pages"):
+            assert torch.equal(a["layers"][l][key].view(torch.int16),
+                               b["layers"][l][key].view(torch.int16)), f"layer {l} {key}"
+    check_routing(case, b, f)
+
