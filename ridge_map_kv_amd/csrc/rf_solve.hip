@@ -183,25 +183,33 @@ __device__ __forceinline__ double recip(double p) {
 
 // Factor diagonal block k in place (lower) and store its inverse in linv[k].  1024 threads;
 // thread t owns row t / 16 and the 4 columns 4 (t % 16) .. + 3, and keeps its segment of
-// the block and of Y in registers for the whole sweep.  (The 64 column steps are
-// sequential; with 4 columns per thread each step is a few instructions, measured 2.5x
-// faster than 16 columns per thread on 256 threads.)
+// the block and of Y in registers for the whole sweep.  (The column steps are sequential;
+// with 4 columns per thread each is a few instructions, measured 2.5x faster than 16
+// columns per thread on 256 threads.)
 //
 // Column j is eliminated with its pivot d_j left unscaled: every row below subtracts
 // (a_ij / d_j) times column j from its columns j+1 .. i, which leaves a_ij = L_ij sqrt(d_j).
 // The inverse is built in the same sweep on Y = diag(L) L^-1: row i of Y (i > j) subtracts
-// (a_ij / d_j) times row j of Y, since L_ij / L_jj = a_ij / d_j.  Step j reads only column
-// j of the block and row j of Y, which are final after step j - 1; their owners publish
-// them to LDS (double-buffered) at the end of step j - 1, so one barrier per column
-// suffices and no other LDS traffic is needed.  At the end L_ij = a_ij / sqrt(d_j),
-// L_jj = sqrt(d_j) and (L^-1)_i = Y_i / sqrt(d_i).  A non-positive or non-finite pivot sets
-// the NOT_SPD bit and is taken as 1.
+// (a_ij / d_j) times row j of Y, since L_ij / L_jj = a_ij / d_j.
+//
+// Columns go two per barrier.  Step (j, j+1) reads column j and row j of Y as left by the
+// columns before j (final for column j), and column j+1 and row j+1 of Y as left by the
+// columns before j (one elimination short).  Every thread applies that missing
+// elimination itself where it needs column j+1: with g = a_(j+1)j / d_j,
+//   column j+1 at row x:  a_x(j+1) - a_xj g,   pivot d_(j+1) = a_(j+1)(j+1) - a_(j+1)j g,
+//   row j+1 of Y:         Y_(j+1) - g Y_j,
+// then eliminates column j from its entries in columns j+1 .. i and column j+1 from those
+// in columns j+2 .. i.  The owners of columns j+2, j+3 and of rows j+2, j+3 of Y then
+// publish them to LDS (double-buffered by step parity): one barrier per two columns.  At
+// the end L_ij = a_ij / sqrt(d_j), L_jj = sqrt(d_j) and (L^-1)_i = Y_i / sqrt(d_i).  A
+// non-positive or non-finite pivot sets the NOT_SPD bit and is taken as 1.
 constexpr int kDiagThreads = 1024, kDiagW = 4;
 __global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int d, int k,
                                                                  double* linv, unsigned* status,
                                                                  size_t sC, size_t sL) {
-  __shared__ __attribute__((aligned(16))) double col[2][NB];   // column j (by j parity)
-  __shared__ __attribute__((aligned(16))) double yrow[2][NB];  // row j of Y
+  // columns j, j+1 and rows j, j+1 of Y, by step parity
+  __shared__ __attribute__((aligned(16))) double colA[2][NB], colB[2][NB];
+  __shared__ __attribute__((aligned(16))) double yA[2][NB], yB[2][NB];
   __shared__ double piv[NB];          // pivots d_j (after the NOT_SPD replacement)
   C += blockIdx.y * sC;               // matrix blockIdx.y of a batch
   linv += blockIdx.y * sL;
@@ -215,44 +223,64 @@ __global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int 
     ar[cc] = blk[(size_t)row * d + c0 + cc];
     yr[cc] = row == c0 + cc ? 1.0 : 0.0;
   }
-  // publish column 0 and row 0 of Y
-  if (c0 == 0) col[0][row] = ar[0];
-  if (row == 0) {
+  // publish columns 0, 1 and rows 0, 1 of Y
+  if (c0 == 0) {
+    colA[0][row] = ar[0];
+    colB[0][row] = ar[1];
+  }
+  if (row < 2) {
 #pragma unroll
-    for (int cc = 0; cc < kDiagW; ++cc) yrow[0][c0 + cc] = yr[cc];
+    for (int cc = 0; cc < kDiagW; ++cc) (row == 0 ? yA : yB)[0][c0 + cc] = yr[cc];
   }
   __syncthreads();
-  for (int j = 0; j < NB; ++j) {
-    const int b = j & 1;
-    double p = col[b][j];
-    const bool bad = !(p > 0.0) || !isfinite(p);
-    if (bad) p = 1.0;
+  for (int j = 0; j < NB; j += 2) {
+    const int b = (j >> 1) & 1;
+    double p0 = colA[b][j];
+    const bool bad0 = !(p0 > 0.0) || !isfinite(p0);
+    if (bad0) p0 = 1.0;
+    const double r0 = recip(p0);
+    const double a10 = colA[b][j + 1];
+    const double g = a10 * r0;
+    double p1 = colB[b][j + 1] - a10 * g;
+    const bool bad1 = !(p1 > 0.0) || !isfinite(p1);
+    if (bad1) p1 = 1.0;
     if (t == 0) {
-      piv[j] = p;
-      if (bad) atomicOr(status, kStatusNotSpdBit);
+      piv[j] = p0;
+      piv[j + 1] = p1;
+      if (bad0 || bad1) atomicOr(status, kStatusNotSpdBit);
     }
     if (row > j) {
-      const double m = col[b][row] * recip(p);
-      const double2* cv = reinterpret_cast<const double2*>(&col[b][c0]);
-      const double2* yv = reinterpret_cast<const double2*>(&yrow[b][c0]);
+      const double xa = colA[b][row];
+      const double m0 = xa * r0;
+      // column j+1 of this row, after column j's elimination, and its multiplier
+      const double m1 = row > j + 1 ? (colB[b][row] - xa * g) * recip(p1) : 0.0;
+      const double2* av = reinterpret_cast<const double2*>(&colA[b][c0]);
+      const double2* bv = reinterpret_cast<const double2*>(&colB[b][c0]);
+      const double2* ya = reinterpret_cast<const double2*>(&yA[b][c0]);
+      const double2* yb = reinterpret_cast<const double2*>(&yB[b][c0]);
 #pragma unroll
       for (int q = 0; q < kDiagW / 2; ++q) {
-        const double2 cq = cv[q], yq = yv[q];
-        const int c = c0 + 2 * q;
-        if (c > j && c <= row) ar[2 * q] -= m * cq.x;
-        if (c + 1 > j && c + 1 <= row) ar[2 * q + 1] -= m * cq.y;
-        yr[2 * q] -= m * yq.x;
-        yr[2 * q + 1] -= m * yq.y;
+        const double2 aq = av[q], bq = bv[q], yaq = ya[q], ybq = yb[q];
+        const double ca[2] = {aq.x, aq.y}, cb[2] = {bq.x - aq.x * g, bq.y - aq.y * g};
+        const double ua[2] = {yaq.x, yaq.y}, ub[2] = {ybq.x - yaq.x * g, ybq.y - yaq.y * g};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int cc = 2 * q + e, c = c0 + cc;
+          if (c > j && c <= row) ar[cc] -= m0 * ca[e];
+          if (c > j + 1 && c <= row) ar[cc] -= m1 * cb[e];
+          yr[cc] -= m0 * ua[e] + m1 * ub[e];
+        }
       }
     }
-    // column j + 1 and row j + 1 of Y are now final: publish them for the next step
-    if (j + 1 < NB) {
+    // columns j+2, j+3 and rows j+2, j+3 of Y are now as the next step expects them
+    if (j + 2 < NB) {
+      if (c0 == ((j + 2) & ~(kDiagW - 1))) {       // j+2 and j+3 fall in one 4-column group
+        colA[b ^ 1][row] = ar[(j + 2) & (kDiagW - 1)];
+        colB[b ^ 1][row] = ar[(j + 3) & (kDiagW - 1)];
+      }
+      if (row == j + 2 || row == j + 3) {
 #pragma unroll
-      for (int cc = 0; cc < kDiagW; ++cc)
-        if (c0 + cc == j + 1) col[b ^ 1][row] = ar[cc];
-      if (row == j + 1) {
-#pragma unroll
-        for (int cc = 0; cc < kDiagW; ++cc) yrow[b ^ 1][c0 + cc] = yr[cc];
+        for (int cc = 0; cc < kDiagW; ++cc) (row == j + 2 ? yA : yB)[b ^ 1][c0 + cc] = yr[cc];
       }
     }
     __syncthreads();
