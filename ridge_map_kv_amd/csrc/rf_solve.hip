@@ -508,44 +508,90 @@ __device__ __forceinline__ void split_bf16(double x, uint16_t& hi, uint16_t& lo)
 
 // M = U U^T (= W^T W with W = L^-1) for one lower tile pair, written to both triangles in
 // fp64 and as the GEMM operand Mx [d][3d] = [M_hi | M_lo | M_hi] (bf16).
+constexpr int kWk = 32, kWld = kWk + 2;     // reduction slice; padded LDS rows (16-byte aligned)
 __global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double* M64, uint16_t* Mx) {
-  __shared__ double wa[NB * LDT];
-  __shared__ double wb[NB * LDT];
+  __shared__ __attribute__((aligned(16))) double wa[2][NB * kWld];
+  __shared__ __attribute__((aligned(16))) double wb[2][NB * kWld];
   const int e = blockIdx.x;
   int ab = (int)((sqrt(8.0 * e + 1.0) - 1.0) * 0.5);
   while ((ab + 1) * (ab + 2) / 2 <= e) ++ab;
   while (ab * (ab + 1) / 2 > e) --ab;
   const int bb = e - ab * (ab + 1) / 2;
-  const int nbk = d / NB;
+  // k from 64 ab (U is zero before its diagonal) in 32-wide slices through two LDS stages;
+  // slice s + 1 is fetched into registers while slice s is multiplied
+  const int tid = threadIdx.x, lrow = tid >> 2, lcol = (tid & 3) * (kWk / 4);
+  const double* ga = U + (size_t)(ab * NB + lrow) * d + lcol;
+  const double* gb = U + (size_t)(bb * NB + lrow) * d + lcol;
+  const int k0 = ab * NB, nks = (d - k0) / kWk;
+  constexpr int kV = kWk / 8;                 // double2 per thread and operand
+  double2 ra[kV], rb[kV];
+  auto fetch = [&](int k) {
+#pragma unroll
+    for (int q = 0; q < kV; ++q) {
+      ra[q] = *reinterpret_cast<const double2*>(ga + k + 2 * q);
+      rb[q] = *reinterpret_cast<const double2*>(gb + k + 2 * q);
+    }
+  };
+  auto park = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < kV; ++q) {
+      *reinterpret_cast<double2*>(&wa[buf][lrow * kWld + lcol + 2 * q]) = ra[q];
+      *reinterpret_cast<double2*>(&wb[buf][lrow * kWld + lcol + 2 * q]) = rb[q];
+    }
+  };
+  const int lane = tid & 63, w = tid >> 6;
+  const int r0 = (w >> 1) * 32 + (lane & 15), c0 = (w & 1) * 32 + (lane & 15), kq = lane >> 4;
   Acc64 acc;
   zero44(acc);
-  for (int kb = ab; kb < nbk; ++kb) {
-    load64(wa, U + (size_t)ab * NB * d + (size_t)kb * NB, d, false);
-    load64(wb, U + (size_t)bb * NB * d + (size_t)kb * NB, d, false);
-    __syncthreads();
-    mac64(acc, wa, wb);
+  fetch(k0);
+  park(0);
+  __syncthreads();
+  for (int s = 0; s < nks; ++s) {
+    if (s + 1 < nks) fetch(k0 + (s + 1) * kWk);
+    const double* A = wa[s & 1];
+    const double* B = wb[s & 1];
+#pragma unroll
+    for (int k = 0; k < kWk; k += 4) {
+      const double a0 = A[r0 * kWld + k + kq], a1 = A[(r0 + 16) * kWld + k + kq];
+      const double b0 = B[c0 * kWld + k + kq], b1 = B[(c0 + 16) * kWld + k + kq];
+      acc.v[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc.v[0][0], 0, 0, 0);
+      acc.v[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc.v[0][1], 0, 0, 0);
+      acc.v[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc.v[1][0], 0, 0, 0);
+      acc.v[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc.v[1][1], 0, 0, 0);
+    }
+    if (s + 1 < nks) park((s + 1) & 1);   // the other stage: last read before the previous barrier
     __syncthreads();
   }
+  // the tile through LDS, so that it and its mirror image leave as row segments; a
+  // diagonal tile takes its lower triangle for both halves (exactly symmetric)
+  constexpr int kT = NB + 1;
+  static_assert(NB * kT <= 2 * NB * kWld, "tile fits in the first operand's two stages");
+  double* t = &wa[0][0];
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t a = (size_t)ab * NB + acc_row(bi, j), b = (size_t)bb * NB + acc_col(bj);
-      const double v = acc.v[bi][bj][j];
+      for (int j = 0; j < 4; ++j) t[acc_row(bi, j) * kT + acc_col(bj)] = acc.v[bi][bj][j];
+  __syncthreads();
+  const size_t d3 = (size_t)3 * d;
+  for (int e = tid; e < NB * NB; e += blockDim.x) {
+    const int r = e >> 6, c = e & 63;
+    for (int side = 0; side < (ab == bb ? 1 : 2); ++side) {
+      const int rt = side == 0 ? ab : bb, ct = side == 0 ? bb : ab;
+      double v;
+      if (side == 1) v = t[c * kT + r];                       // the mirror image
+      else if (ab == bb && r < c) v = t[c * kT + r];          // a diagonal tile's lower triangle
+      else v = t[r * kT + c];
+      const size_t a = (size_t)rt * NB + r, b = (size_t)ct * NB + c;
       M64[a * d + b] = v;
-      M64[b * d + a] = v;
       uint16_t hi, lo;
       split_bf16(v, hi, lo);
-      const size_t d3 = (size_t)3 * d;
       Mx[a * d3 + b] = hi;
       Mx[a * d3 + d + b] = lo;
       Mx[a * d3 + 2 * d + b] = hi;
-      Mx[b * d3 + a] = hi;
-      Mx[b * d3 + d + a] = lo;
-      Mx[b * d3 + 2 * d + a] = hi;
     }
+  }
 }
 
 // v = M mu_S (one wave per row, fixed-order reduction); then v . mu_S.
