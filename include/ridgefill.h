@@ -86,10 +86,12 @@ typedef struct rf_layer {
                                A_scale[o] (section "Ridge map ...", map size paragraph:
                                int8 maps).  Exactly one of A and A_q is set.             */
   const float* A_scale;     /* fp32 [d]: per-output-row scale of A_q                    */
-  const void* folded;       /* device buffer of ridgefill_fold_bytes(shape) bytes made by
+  const void* folded;       /* buffer of ridgefill_fold_bytes(shape) bytes made by
                                ridgefill_fold_maps, 256-byte aligned: the layer's folded
-                               form.  When set, the fill reads it instead of A, A_q,
-                               A_scale, b, norm_w, W_K and W_V (which may then be NULL).  */
+                               form (device memory; host memory, ideally page-locked, for
+                               ridgefill_fill_streamed).  When set, the fill reads it
+                               instead of A, A_q, A_scale, b, norm_w, W_K and W_V (which
+                               may then be NULL).                                          */
 } rf_layer;
 
 /* Paged KV layout of one prompt, shared by every layer's k_pages / v_pages. */
