@@ -10,7 +10,7 @@
  *  - Pointers marked "device" point to GPU memory the caller allocated; pointers
  *    marked "host" point to CPU memory.  The library allocates no device memory,
  *    keeps no device state between calls and creates no streams (the streamed fill
- *    creates two pairs of HIP events per host thread on first use and reuses them).
+ *    creates five HIP events per host thread and device on first use and reuses them).
  *    Every buffer it needs beyond inputs and outputs is a caller-owned workspace whose
  *    size a *_workspace_bytes / *_state_bytes query returns.
  *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round-to-nearest-
@@ -196,7 +196,9 @@ size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled
  * RF_MAPS_INT8 for int8 maps or RF_MAPS_FOLDED for folded layers); group g's maps (or
  * folded buffers) are copied on `copy_stream` into landing slot g % 2 while group g - 1
  * computes on `stream`.  copy_stream must be a different stream; both must stay
- * valid until the work completes.  The results are bit-identical to ridgefill_fill's.
+ * valid until the work completes.  The first copy of a call waits for the work already
+ * enqueued on `stream`, so back-to-back calls on one workspace are ordered.  The results
+ * are bit-identical to ridgefill_fill's.
  * ------------------------------------------------------------------------------ */
 rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
                                   int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,

@@ -857,7 +857,9 @@ int group_size(int n_layers, int group) {
 struct StreamEvents {
   hipEvent_t ready[2] = {nullptr, nullptr};
   hipEvent_t done[2] = {nullptr, nullptr};
+  hipEvent_t start = nullptr;
 };
+constexpr int kMaxDevices = 64;
 
 }  // namespace
 
@@ -886,14 +888,23 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
 // waits until the group that used it two steps before has finished.
 hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, int n_layers,
                                 hipStream_t stream, hipStream_t copy_stream) {
-  static thread_local StreamEvents ev;
+  // events per host thread and device, created on first use
+  static thread_local StreamEvents evs[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  StreamEvents& ev = evs[dev];
   for (int i = 0; i < 2; ++i) {
-    hipError_t e;
     if (!ev.ready[i] && (e = hipEventCreateWithFlags(&ev.ready[i], hipEventDisableTiming)) != hipSuccess) return e;
     if (!ev.done[i] && (e = hipEventCreateWithFlags(&ev.done[i], hipEventDisableTiming)) != hipSuccess) return e;
   }
-  hipError_t e = launch_fill_prep(p, stream);
-  if (e != hipSuccess) return e;
+  if (!ev.start && (e = hipEventCreateWithFlags(&ev.start, hipEventDisableTiming)) != hipSuccess) return e;
+  // this call's copies start after the work already on `stream`: a previous call's last
+  // groups may still be reading the landing slots
+  if ((e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(copy_stream, ev.start, 0)) != hipSuccess) return e;
+  if ((e = launch_fill_prep(p, stream)) != hipSuccess) return e;
   unsigned char* lws = reinterpret_cast<unsigned char*>(p.hbuf);
   const bool int8 = (p.flags & kWsInt8) != 0;
   const bool folded = (p.flags & kWsFolded) != 0;

@@ -15,8 +15,8 @@ import oracle
 from ridge_map_kv_amd import binding as B
 from ridge_map_kv_amd import synth
 
-from fillcase import (Case, bf16_np, build_inputs, check_routing, check_values, make_shape,
-                      run_fill, to_bf16)
+from fillcase import (Case, bf16_np, build_inputs, check_routing, check_values, host_maps,
+                      make_shape, run_fill, to_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +100,38 @@ def test_streamed_maps_bit_identical(int8):
     for (k, v), l in zip(ref, inp["layers"]):
         assert _same_bits(k, l["k_pages"]) and _same_bits(v, l["v_pages"])
     check_routing(case, inp, f)
+
+
+def test_streamed_calls_back_to_back_on_one_workspace():
+    # two streamed fills enqueued without a sync between them, sharing the workspace and
+    # the streams, each into its own page pools: the second call's copies must not
+    # overwrite landing slots that the first call's last groups still read
+    case = _case(512, 5, 2, 128, 700, 100, 60, 16, 42)
+    inp = build_inputs(case)
+    f = _filled(case)
+    assert run_fill(case, inp, f) == B.RF_OK
+    ref = [(l["k_pages"].clone(), l["v_pages"].clone()) for l in inp["layers"]]
+    shape = make_shape(case)
+    idx = torch.from_numpy(np.asarray(f, dtype=np.int32)).to(inp["xS"].device)
+    ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, f.size, 2, B.RF_MAPS_STREAMED),
+                     dtype=torch.uint8, device=inp["xS"].device)
+    copy = torch.cuda.Stream()
+    calls = []
+    for _ in range(2):
+        layers = host_maps(inp["layers"])
+        for l in layers:
+            l["k_pages"] = torch.full_like(l["k_pages"], -1, dtype=torch.int16).view(torch.bfloat16)
+            l["v_pages"] = torch.full_like(l["v_pages"], -1, dtype=torch.int16).view(torch.bfloat16)
+        calls.append(layers)
+    torch.cuda.synchronize()
+    for layers in calls:
+        B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, layers, inp["table"],
+                         case.page_size, inp["num_pages"], ws, copy_stream=copy)
+    assert B.ridgefill_read_status(ws) == B.RF_OK
+    torch.cuda.synchronize()
+    for layers in calls:
+        for (k, v), l in zip(ref, layers):
+            assert _same_bits(k, l["k_pages"]) and _same_bits(v, l["v_pages"])
 
 
 def test_group_split_bit_identical_with_variants():
