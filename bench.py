@@ -454,6 +454,27 @@ def cpu_baseline_calib(ccfg, budget_s: float = 10.0):
                       f"{spent:.1f} s"}
 
 
+def cpu_baseline_solve(ccfg, lam: float = 0.03):
+    """The oracle's solve for one lambda at the full shape (its cost does not depend on the
+    number of calibration rows: statistics of a short seeded sample are solved)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from ridge_map_kv_amd import synth
+
+    d, L = ccfg.d, ccfg.n_layers
+    xS, xl = synth.calib_data(d, L, 64, seed=ccfg.seed, noise_dof=ccfg.noise_dof)
+    st = oracle.calib_new(d, L)
+    oracle.calib_accumulate(st, xS.astype(np.float64), [y.astype(np.float64) for y in xl])
+    t0 = time.perf_counter()
+    oracle.solve(st, lam)
+    spent = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                  or [1])
+    return {"value": spent * 1e3, "unit": "ms per lambda", "cores": int(threads), "kind": "oracle",
+            "sample": f"one lambda = {lam} at d = {d}, {L} upper layers (SciPy Cholesky and "
+                      f"triangular solves, float64), on the statistics of 64 seeded rows"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -601,6 +622,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline_fill(cfg, inp)
         if calib is not None:
             out["calibration"]["cpu_baseline"] = cpu_baseline_calib(configs.CALIB8B)
+            out["solve"]["cpu_baseline"] = cpu_baseline_solve(configs.CALIB8B)
     if not args.no_variants:
         del inp
         torch.cuda.empty_cache()
