@@ -391,7 +391,8 @@ def run_calibration(ccfg, dev, passes: int = 2):
         "tflop": flops / 1e12, "pct_bf16_mfma_peak": 100.0 * flops / t_cal / (PEAK_BF16_TFLOPS * 1e12),
         "moments_kernel": {"avg_ms": mom_ms / mom_n, "launches": mom_n,
                            "tflops": mom_flops_launch / (mom_ms / mom_n * 1e-3) / 1e12},
-        "sums_kernel": {"avg_ms": sum_ms / sum_n, "launches": sum_n},
+        "sums_kernel": ({"avg_ms": sum_ms / sum_n, "launches": sum_n} if sum_n else
+                        "in the moments launch (its workgroups after the tiles)"),
         "noise": "0.1 * Student-t(3)",
     }
 

@@ -70,13 +70,13 @@ __global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d_in,
 struct SumArgs {
   const uint16_t* x[kMaxCalibLayers + 1];
   int n_rows, d_in, d_out;
+  int ncb;               // column blocks of the wider of d_in and d_out
   double* sums;          // sum_S [d_in], then sum_l [n_layers][d_out], contiguous
   int64_t* count;
 };
 
-__global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
-  __shared__ float part[8][256];
-  const int cb = blockIdx.x, m = blockIdx.y;
+// Column block cb of matrix m; part: 8 KB of LDS.
+__device__ __forceinline__ void sums_block(const SumArgs& a, int cb, int m, float (*part)[256]) {
   const int width = m == 0 ? a.d_in : a.d_out;
   if (cb * 256 >= width) return;                 // the grid covers the wider of the two
   const int tid = threadIdx.x, s = tid >> 5, q = tid & 31;
@@ -100,6 +100,11 @@ __global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
   double* dst = a.sums + (m == 0 ? 0 : (size_t)a.d_in + (size_t)(m - 1) * a.d_out) + cb * 256 + tid;
   *dst += tot;
   if (cb == 0 && m == 0 && tid == 0) *a.count += a.n_rows;
+}
+
+__global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
+  __shared__ float part[8][256];
+  sums_block(a, blockIdx.x, blockIdx.y, part);
 }
 
 // Loads rows t0 + 8*rg .. +7, features f0 + 8*fg .. +7 of a row-major [n][d] bf16 matrix
@@ -315,9 +320,19 @@ __device__ __forceinline__ void calib_operand(DmaOperand& o, const uint16_t* x, 
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArgs a) {
+// The column sums ride in the same launch: workgroups from the tile count on each take one
+// column block.  They are dispatched after every tile, into the launch's last round, where
+// the tiles (5,256 at d = 4096 with 20 layers: 20.5 rounds of 256) leave CUs idle; the
+// sums read the same rows again, from HBM, while the last tiles multiply.
+__global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArgs a, SumArgs s) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
-  const CalibTile t = calib_tile(a, xcd_remap(blockIdx.x, gridDim.x));
+  const int ntiles = a.ngram + a.n_layers * a.nt_out * a.nt_in;
+  if ((int)blockIdx.x >= ntiles) {
+    const int b = blockIdx.x - ntiles;
+    sums_block(s, b % s.ncb, b / s.ncb, reinterpret_cast<float (*)[256]>(smem));
+    return;
+  }
+  const CalibTile t = calib_tile(a, xcd_remap(blockIdx.x, ntiles));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1;
@@ -429,12 +444,9 @@ hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, cons
   s.d_out = d_out;
   s.sums = reinterpret_cast<double*>(st + L.sum_S);
   s.count = reinterpret_cast<int64_t*>(st);
+  s.ncb = (d_in > d_out ? d_in : d_out) / 256;
+  const int nsums = s.ncb * (1 + n_layers);
   // sum_l follows sum_S contiguously: d_in * 8 is a multiple of 256 (d_in % 256 == 0).
-  {
-    ProfileScope ps(RF_KERNEL_CALIB_SUMS, stream);
-    const int widest = d_in > d_out ? d_in : d_out;
-    hipLaunchKernelGGL(calib_sums_kernel, dim3(widest / 256, 1 + n_layers), dim3(256), 0, stream, s);
-  }
 
   CalibArgs a = {};
   a.xS = xS;
@@ -449,11 +461,15 @@ hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, cons
   a.YX = reinterpret_cast<float*>(st + L.YX);
   const int tiles = a.ngram + n_layers * a.nt_out * a.nt_in;
   const int bulk = (int)(n_rows / kPipeBK) * kPipeBK;
-  if (bulk > 0) {
+  if (bulk > 0) {                 // the moments of whole 64-row slices, and the sums
     a.row0 = 0;
     a.n_rows = bulk;
     ProfileScope ps(RF_KERNEL_CALIB_MOMENTS, stream);
-    hipLaunchKernelGGL(calib_moments_dma_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(calib_moments_dma_kernel, dim3(tiles + nsums), dim3(kThreads), 0, stream,
+                       a, s);
+  } else {                        // fewer than 64 rows: the sums alone
+    ProfileScope ps(RF_KERNEL_CALIB_SUMS, stream);
+    hipLaunchKernelGGL(calib_sums_kernel, dim3(s.ncb, 1 + n_layers), dim3(256), 0, stream, s);
   }
   if (n_rows > bulk) {
     a.row0 = bulk;
