@@ -39,9 +39,12 @@ FoldLayout fold_layout(int d_in, int kv) {
 
 FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par) {
   FoldWsLayout W;
+  W.slots = n_par < kFoldGemmSlots ? n_par : kFoldGemmSlots;
   W.At = kStatusBytes;
-  W.Wx = W.At + align256((size_t)d_in * 2 * d * 2);
-  W.blocks = W.Wx + align256((size_t)2 * kv * 2 * d * 2);
+  W.at_bytes = align256((size_t)d_in * 2 * d * 2);
+  W.Wx = W.At + (size_t)W.slots * W.at_bytes;
+  W.wx_bytes = align256((size_t)2 * kv * 2 * d * 2);
+  W.blocks = W.Wx + (size_t)W.slots * W.wx_bytes;
   W.H64 = 0;
   W.linv = W.H64 + align256((size_t)d_in * d_in * 8);
   W.g = W.linv + align256((size_t)d_in * 64 * 8);
@@ -91,21 +94,27 @@ __global__ void fold_wsplit_kernel(const uint16_t* WK, const uint16_t* WV, const
   }
 }
 
-// out[m][n] = sum_k F[m][k] T[n][k] for 256 x 256 tiles (F, T bf16 rows, K a multiple of
-// 64); bf16 (mode 0) or fp64 (mode 1) output.  With `lower`, only tiles n <= m.
+// out_l[m][n] = sum_k F_l[m][k] T_l[n][k] for 256 x 256 tiles of the layers l of one launch
+// (F_l, T_l bf16 rows at a fixed element stride from layer to layer, K a multiple of 64);
+// bf16 (mode 0) or fp64 (mode 1) output.  With `lower`, only tiles n <= m.
 struct NtGemmArgs {
   const uint16_t* F;
   const uint16_t* T;
-  void* out;
+  int64_t sF, sT;                 // elements from one layer's operand to the next
+  void* out[kFoldGemmSlots];
   int64_t ldf, ldt, ldo;
   int K, ntm, ntn, mode, lower;
 };
 
 __global__ __launch_bounds__(kThreads, 1) void fold_gemm_kernel(NtGemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
-  const int tile = blockIdx.x;
+  const int per = a.ntm * a.ntn;
+  const int l = blockIdx.x / per, tile = blockIdx.x - l * per;
   const int mt = tile / a.ntn, nt = tile - mt * a.ntn;
   if (a.lower && nt > mt) return;                 // whole block, before any barrier
+  const uint16_t* Fl = a.F + l * a.sF;
+  const uint16_t* Tl = a.T + l * a.sT;
+  void* out = a.out[l];
   const int m0 = mt * kTile, n0 = nt * kTile;
   const int tid = threadIdx.x;
   DmaOperand Fo, To;
@@ -115,9 +124,9 @@ __global__ __launch_bounds__(kThreads, 1) void fold_gemm_kernel(NtGemmArgs a) {
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), rr = r0 + dma_lane_row(lane);
       const int ce = dma_chunk_elems(rr, lane);
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(a.F + (size_t)(m0 + r0) * a.ldf);
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(Fl + (size_t)(m0 + r0) * a.ldf);
       Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.ldf + ce) * 2);
-      To.base[p] = reinterpret_cast<const unsigned char*>(a.T + (size_t)(n0 + r0) * a.ldt);
+      To.base[p] = reinterpret_cast<const unsigned char*>(Tl + (size_t)(n0 + r0) * a.ldt);
       To.off[p] = (uint32_t)((dma_lane_row(lane) * a.ldt + ce) * 2);
     }
   }
@@ -136,9 +145,9 @@ __global__ __launch_bounds__(kThreads, 1) void fold_gemm_kernel(NtGemmArgs a) {
           const size_t row = (size_t)m0 + wf * 128 + m * 32 + q * 8 + h * 4 + e;
           const float v = acc[m][n][q * 4 + e];
           if (a.mode == 0)
-            reinterpret_cast<uint16_t*>(a.out)[row * a.ldo + col] = (uint16_t)f32_to_bf16(v);
+            reinterpret_cast<uint16_t*>(out)[row * a.ldo + col] = (uint16_t)f32_to_bf16(v);
           else
-            reinterpret_cast<double*>(a.out)[row * a.ldo + col] = (double)v;
+            reinterpret_cast<double*>(out)[row * a.ldo + col] = (double)v;
         }
     }
 }
@@ -267,29 +276,38 @@ hipError_t launch_fold(int d, int d_in, int kv, const FoldLayerIn* layers, int G
   const FoldLayout F = fold_layout(d_in, kv);
   unsigned char* s = static_cast<unsigned char*>(ws);
   unsigned* status = reinterpret_cast<unsigned*>(s);
-  uint16_t* At = reinterpret_cast<uint16_t*>(s + W.At);
-  uint16_t* Wx = reinterpret_cast<uint16_t*>(s + W.Wx);
+  uint16_t* At0 = reinterpret_cast<uint16_t*>(s + W.At);
+  uint16_t* Wx0 = reinterpret_cast<uint16_t*>(s + W.Wx);
   auto blk = [&](int l) { return s + W.blocks + (size_t)l * W.per_layer; };
   hipError_t e;
-  for (int l = 0; l < G; ++l) {
-    const FoldLayerIn& in = layers[l];
-    unsigned char* o = static_cast<unsigned char*>(out[l]);
-    double* H = reinterpret_cast<double*>(blk(l) + W.H64);
-    hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream, in.A,
-                       d, d_in, At);
-    hipLaunchKernelGGL(fold_wsplit_kernel, dim3(2048), dim3(256), 0, stream, in.WK, in.WV, in.w,
-                       kv, d, Wx);
-    NtGemmArgs pa = {Wx, At, o + F.P, 2 * (int64_t)d, 2 * (int64_t)d, d_in, 2 * d,
-                     2 * kv / kTile, d_in / kTile, 0, 0};
-    hipLaunchKernelGGL(fold_gemm_kernel, dim3(pa.ntm * pa.ntn), dim3(kThreads), 0, stream, pa);
-    NtGemmArgs ha = {At, At, H, 2 * (int64_t)d, 2 * (int64_t)d, d_in, d, d_in / kTile,
-                     d_in / kTile, 1, 1};
-    hipLaunchKernelGGL(fold_gemm_kernel, dim3(ha.ntm * ha.ntn), dim3(kThreads), 0, stream, ha);
-    hipLaunchKernelGGL(fold_gemv_kernel, dim3((d_in + 2 * kv + 3) / 4), dim3(256), 0, stream, At,
-                       in.WK, in.WV, in.w, in.b, d, d_in, kv,
-                       reinterpret_cast<double*>(blk(l) + W.g), reinterpret_cast<float*>(o + F.c));
-    hipLaunchKernelGGL(fold_bb_kernel, dim3(1), dim3(1024), 0, stream, in.b, d,
-                       reinterpret_cast<double*>(blk(l) + W.scal));
+  // the GEMMs of up to W.slots layers per launch, each layer with its own operand slot
+  for (int l0 = 0; l0 < G; l0 += W.slots) {
+    const int ns = G - l0 < W.slots ? G - l0 : W.slots;
+    NtGemmArgs pa = {Wx0, At0, (int64_t)(W.wx_bytes / 2), (int64_t)(W.at_bytes / 2), {},
+                     2 * (int64_t)d, 2 * (int64_t)d, d_in, 2 * d, 2 * kv / kTile, d_in / kTile,
+                     0, 0};
+    NtGemmArgs ha = {At0, At0, (int64_t)(W.at_bytes / 2), (int64_t)(W.at_bytes / 2), {},
+                     2 * (int64_t)d, 2 * (int64_t)d, d_in, d, d_in / kTile, d_in / kTile, 1, 1};
+    for (int j = 0; j < ns; ++j) {
+      const int l = l0 + j;
+      const FoldLayerIn& in = layers[l];
+      unsigned char* o = static_cast<unsigned char*>(out[l]);
+      uint16_t* At = reinterpret_cast<uint16_t*>(s + W.At + (size_t)j * W.at_bytes);
+      uint16_t* Wx = reinterpret_cast<uint16_t*>(s + W.Wx + (size_t)j * W.wx_bytes);
+      hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream,
+                         in.A, d, d_in, At);
+      hipLaunchKernelGGL(fold_wsplit_kernel, dim3(2048), dim3(256), 0, stream, in.WK, in.WV, in.w,
+                         kv, d, Wx);
+      hipLaunchKernelGGL(fold_gemv_kernel, dim3((d_in + 2 * kv + 3) / 4), dim3(256), 0, stream,
+                         At, in.WK, in.WV, in.w, in.b, d, d_in, kv,
+                         reinterpret_cast<double*>(blk(l) + W.g), reinterpret_cast<float*>(o + F.c));
+      hipLaunchKernelGGL(fold_bb_kernel, dim3(1), dim3(1024), 0, stream, in.b, d,
+                         reinterpret_cast<double*>(blk(l) + W.scal));
+      pa.out[j] = o + F.P;
+      ha.out[j] = blk(l) + W.H64;
+    }
+    hipLaunchKernelGGL(fold_gemm_kernel, dim3(ns * pa.ntm * pa.ntn), dim3(kThreads), 0, stream, pa);
+    hipLaunchKernelGGL(fold_gemm_kernel, dim3(ns * ha.ntm * ha.ntn), dim3(kThreads), 0, stream, ha);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // the G factorizations and substitutions side by side (strides in doubles)

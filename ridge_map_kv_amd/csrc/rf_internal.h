@@ -50,13 +50,15 @@ struct FoldLayout {
 };
 FoldLayout fold_layout(int d_in, int kv);
 
-// Workspace of the fold: the status word, then the parts rebuilt for each layer
-// ([A^T | A^T] and [W_hi | W_lo] in bf16), then one block per layer of a group folded side
-// by side: A^T A in fp64 (the Cholesky works in place), the diagonal-block inverses, A^T b
-// and r in fp64, |b|^2.  Block offsets are from the block's start; `total` covers n_par
-// blocks.
+// Workspace of the fold: the status word, then up to kFoldGemmSlots operand slots rebuilt
+// for each layer ([A^T | A^T] and [W_hi | W_lo] in bf16), then one block per layer of a
+// group folded side by side: A^T A in fp64 (the Cholesky works in place), the
+// diagonal-block inverses, A^T b and r in fp64, |b|^2.  Block offsets are from the block's
+// start; `total` covers n_par blocks.
+constexpr int kFoldGemmSlots = 4;   // layers whose fold GEMMs share one launch
 struct FoldWsLayout {
-  size_t At, Wx, blocks;
+  int slots;                          // operand slots: [A^T | A^T] and [W_hi | W_lo] each
+  size_t At, at_bytes, Wx, wx_bytes, blocks;
   size_t H64, linv, g, r, scal, per_layer;
   size_t total;
 };

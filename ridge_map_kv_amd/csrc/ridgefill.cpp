@@ -569,10 +569,10 @@ rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int
   if (!aligned(ws, 256) || ws_bytes < W1.total)
     return fail(RF_E_WORKSPACE, "fold workspace must be 256-byte aligned and >= %zu bytes", W1.total);
   // as many layers side by side as the workspace holds
-  size_t cap = n_layers > 0 ? (size_t)n_layers : 1;
-  if (cap > (size_t)rf::kMaxFoldGroup) cap = rf::kMaxFoldGroup;
-  const size_t fit = 1 + (ws_bytes - W1.total) / W1.per_layer;
-  const int n_par = (int)(fit < cap ? fit : cap);
+  int cap = n_layers > 0 ? n_layers : 1;
+  if (cap > rf::kMaxFoldGroup) cap = rf::kMaxFoldGroup;
+  int n_par = 1;
+  while (n_par < cap && rf::fold_ws_layout(d, d_in, kv, n_par + 1).total <= ws_bytes) ++n_par;
   const rf::FoldWsLayout W = rf::fold_ws_layout(d, d_in, kv, n_par);
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
