@@ -146,3 +146,48 @@ def test_device_flags_bad_rows_and_skips_them():
     pg, sl = oracle.paged_location(np.array([17]), inp["table_np"], 4)
     k = inp["layers"][0]["k_pages"].view(torch.int16)
     assert bool((k[int(pg[0]), int(sl[0])] == -1).all())
+
+
+def _random_cases(n, seed):
+    """Seeded random small workloads over the options the ABI allows: model widths, head
+    shapes, prompt and tail lengths (T = 0 and all-exact prefixes included), page sizes,
+    rectangular and int8 maps, key norm, value rescale and folded layers."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(g.choice([256, 512, 768, 1024]))
+        hd = int(g.choice([64, 128]))
+        n_kv = int(g.choice([h for h in (1, 2, 4, 8) if (h * hd) % 128 == 0]))
+        N = int(g.integers(2, 900))
+        T = int(g.integers(0, N)) if g.random() < 0.8 else 0
+        P = N - T
+        ne = int(g.integers(0, P + 1)) if g.random() < 0.3 else int(g.integers(0, max(P // 10, 1)))
+        exact = np.sort(g.choice(P, size=ne, replace=False)) if ne else np.zeros(0, np.int64)
+        kind = g.choice(["plain", "rect", "int8", "folded"])
+        d_in = 0
+        if kind == "rect":
+            d_in = int(g.choice([w for w in (256, 320, 512, 1024, 1280) if w != d]))
+        if kind == "folded" and g.random() < 0.5 and d >= 512:
+            d_in = int(g.choice([w for w in (256, 512, 768) if w < d]))   # a tall folded map
+        out.append(dict(case=Case(d=d, n_layers=int(g.integers(1, 4)), n_kv=n_kv, hd=hd, N=N, T=T,
+                                  exact=exact, page_size=int(g.choice([1, 3, 8, 16, 32])),
+                                  seed=int(g.integers(1 << 20)), d_in=d_in,
+                                  knorm=bool(g.random() < 0.3), vscale=bool(g.random() < 0.3),
+                                  int8=kind == "int8"),
+                        folded=kind == "folded"))
+    return out
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_seeded_random_workloads(k):
+    spec = _random_cases(12, 2024)[k]
+    case, folded = spec["case"], spec["folded"]
+    print(f"\ncase {k}: d={case.d} d_in={case.width} layers={case.n_layers} kv={case.n_kv}x"
+          f"{case.hd} N={case.N} T={case.T} exact={len(case.exact)} page={case.page_size} "
+          f"knorm={case.knorm} vscale={case.vscale} int8={case.int8} folded={folded}", flush=True)
+    inp = build_inputs(case)
+    f = _filled(case)
+    assert run_fill(case, inp, f, folded=folded) == B.RF_OK
+    check_routing(case, inp, f)
+    if len(f):
+        check_values(case, inp, f)
