@@ -131,3 +131,48 @@ def test_rect_fit_drives_the_fill():
     assert run_fill(case, inp, f) == B.RF_OK
     check_routing(case, inp, f)
     check_values(case, inp, f)
+
+
+def _random_fits(n, seed):
+    """Seeded random fits: widths, layer counts, row counts split into uneven chunks (some
+    shorter than one 64-row slice) and lambdas across six decades."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d_in = int(g.choice([256, 512, 768]))
+        d_out = int(g.choice([256, 512, 768]))
+        L = int(g.integers(1, 4))
+        rows = int(g.integers(2 * d_in, 4 * d_in))
+        cuts = np.sort(g.choice(np.arange(1, rows), size=int(g.integers(0, 4)), replace=False))
+        lam = float(g.choice([1e-4, 1e-3, 1e-2, 0.03, 0.1, 1.0]))
+        out.append((d_in, d_out, L, rows, [int(c) for c in cuts], lam, int(g.integers(1 << 20))))
+    return out
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_seeded_random_fits_match_oracle(k):
+    d_in, d_out, L, rows, cuts, lam, seed = _random_fits(6, 77)[k]
+    print(f"\nfit {k}: d_in={d_in} d_out={d_out} layers={L} rows={rows} cuts={cuts} "
+          f"lambda={lam}", flush=True)
+    xS, xl = _data(d_in, d_out, L, rows, seed)
+    xs_g, xl_g = bf16(xS), [bf16(y) for y in xl]
+    edges = [0] + cuts + [rows]
+    state = _calib([xs_g[a:b] for a, b in zip(edges, edges[1:])],
+                   [[y[a:b] for y in xl_g] for a, b in zip(edges, edges[1:])], d_in, d_out, L)
+    n, sS, sl, G, YX = _read_state(state, d_in, d_out, L)
+    st = oracle.calib_new(d_in, L, d_out)
+    oracle.calib_accumulate(st, f64(xs_g), [f64(y) for y in xl_g])
+    assert n == rows
+    low = np.tril(np.ones((d_in, d_in), dtype=bool))
+    assert rel(G[low], st.G[low]) < 1e-5 and rel(YX, st.YX) < 1e-5
+    np.testing.assert_allclose(sS, st.s_S, rtol=1e-6, atol=1e-3)
+    np.testing.assert_allclose(sl, st.s_l, rtol=1e-6, atol=1e-3)
+    A, b, _ = _solve(state, d_in, d_out, L, lam)
+    Ao, bo = oracle.solve(st, lam)
+    A, b = A.cpu().numpy().astype(np.float64), b.cpu().numpy().astype(np.float64)
+    _, _, XtX, YtX = oracle.centred_moments(st)
+    alpha = oracle.ridge_alpha(XtX, lam)
+    for l in range(L):
+        assert rel(A[l], Ao[l]) < TOL and rel(b[l], bo[l]) < TOL, (l, rel(A[l], Ao[l]))
+        R = (XtX + alpha * np.eye(d_in)) @ A[l].T - YtX[l].T
+        assert np.linalg.norm(R) / np.linalg.norm(YtX[l]) < 1e-4
