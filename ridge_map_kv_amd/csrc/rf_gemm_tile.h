@@ -162,6 +162,38 @@ __device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOper
   }
 }
 
+// Slice kt of the main loop (kt + 1 < nk): steps 1 to 3 of slice kt, the barrier that
+// frees its stage, step 0 of slice kt + 1.  PEND: the second half of slice kt + 1's loads
+// goes out in step 1 (kt >= 1; slices 0 and 1 came whole with the prologue).  MORE: slice
+// kt + 2 exists and the first half of its loads goes out in step 0.  With both flags fixed at
+// compile time the steady-state body carries no load conditions, which measurably shortens
+// the issue of the 64 MFMAs of a slice.
+template <bool REV, bool PEND, bool MORE>
+__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4], bf16x8 (&b0)[4],
+                                           bf16x8 (&a1)[4], bf16x8 (&b1)[4], const DmaOperand& F,
+                                           const DmaOperand& T, unsigned char* smem, uint32_t base,
+                                           int kt, int wf, int wt, int lane, int wave) {
+  constexpr int kStep = REV ? -kPipeBK * 2 : kPipeBK * 2;    // bytes from one slice to the next
+  const unsigned char* cur = smem + (kt & 1) * kPipeStage;
+  const int kbp = (kt + 1) * kStep;
+  const uint32_t dstp = base + ((kt + 1) & 1) * kPipeStage;
+  mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, PEND, F, T, kbp, dstp, 8, wave);
+  mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+  mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slice kt + 1, the only one in flight
+  __syncthreads();                                       // ... landed for every wave; slice kt read
+  const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
+  const uint32_t dst = base + (kt & 1) * kPipeStage;
+  const int kb = (kt + 2) * kStep;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    mfma_i(acc, a1, b1, i);
+    if (MORE && !(i & 1)) dma_issue(F, T, i >> 1, kb, dst, wave);
+    if (i >= 8) read_frag(a0, b0, nxt, i - 8, 0, wf, wt, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // The rest of the pipeline, once gemm_prologue's loads are issued.  The wait for slice 0
 // counts on loads completing in order: while any load of slice 0 is pending, all 16 of
 // slice 1 are too, so at most 16 outstanding operations (stores issued after the
@@ -169,7 +201,6 @@ __device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOper
 template <bool REV = false>
 __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOperand& F,
                                               const DmaOperand& T, int K, unsigned char* smem) {
-  constexpr int kStep = REV ? -kPipeBK * 2 : kPipeBK * 2;    // bytes from one slice to the next
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave >> 1, wt = wave & 1;
@@ -191,28 +222,14 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOper
   bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) read_frag(a0, b0, smem, i, 0, wf, wt, lane);
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    const unsigned char* cur = smem + (kt & 1) * kPipeStage;
-    // second half of slice kt + 1 (slices 0 and 1 came whole with the prologue)
-    const bool pend = kt >= 1;
-    const int kbp = (kt + 1) * kStep;
-    const uint32_t dstp = base + ((kt + 1) & 1) * kPipeStage;
-    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, pend, F, T, kbp, dstp, 8, wave);
-    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
-    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slice kt + 1, the only one in flight
-    __syncthreads();                                       // ... landed for every wave; slice kt read
-    const bool more = kt + 2 < nk;
-    const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
-    const uint32_t dst = base + (kt & 1) * kPipeStage;
-    const int kb = (kt + 2) * kStep;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mfma_i(acc, a1, b1, i);
-      if (more && !(i & 1)) dma_issue(F, T, i >> 1, kb, dst, wave);
-      if (i >= 8) read_frag(a0, b0, nxt, i - 8, 0, wf, wt, lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  // slices 0 .. nk - 2: the first has nothing pending, the last starts no further slice
+  if (nk == 2) {
+    gemm_slice<REV, false, false>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, wave);
+  } else if (nk > 2) {
+    gemm_slice<REV, false, true>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, wave);
+    for (int kt = 1; kt < nk - 2; ++kt)
+      gemm_slice<REV, true, true>(acc, a0, b0, a1, b1, F, T, smem, base, kt, wf, wt, lane, wave);
+    gemm_slice<REV, true, false>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 2, wf, wt, lane, wave);
   }
   {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
