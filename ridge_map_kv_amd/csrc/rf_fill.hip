@@ -19,6 +19,8 @@
 // result each lane holds one token and runs of four consecutive features: the row
 // reduction needs one cross-lane add, RoPE's pair (j, j + hd/2) sits in the same lane
 // and register of two MFMA blocks, and stores are 8-byte vectors.
+#include <atomic>
+
 #include "rf_common.h"
 #include "rf_gemm_tile.h"
 #include "rf_internal.h"
@@ -739,18 +741,23 @@ FillWsLayout fill_ws_layout(int d, int d_in, int hd, int kv, int64_t n_filled, u
 
 namespace {
 
+constexpr int kMaxDevices = 64;   // per-device host caches
+
 // Workgroups of a persistent tile launch: one per CU, a multiple of 8 (the XCD count), or
-// the item count when that is smaller.  The CU count is read once per device.
+// the item count when that is smaller.  The CU count is read once per device (threads that
+// race on the first read store the same value).
 int persist_grid(int n_items) {
-  static int cus[64];
+  static std::atomic<int> cus[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 256;
-    cus[dev] = n >= 8 ? n & ~7 : 8;
+    c = n >= 8 ? n & ~7 : 8;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return n_items < cus[dev] ? n_items : cus[dev];
+  return n_items < c ? n_items : c;
 }
 
 // A persistent tile launch of n_items items.
@@ -859,7 +866,6 @@ struct StreamEvents {
   hipEvent_t done[2] = {nullptr, nullptr};
   hipEvent_t start = nullptr;
 };
-constexpr int kMaxDevices = 64;
 
 }  // namespace
 
