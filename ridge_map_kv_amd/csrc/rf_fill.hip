@@ -193,10 +193,15 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 // workgroup takes the pair of tiles ft and nft - 1 - ft (the longer first): every pair
 // then reduces over d_in + 256 columns, so the workgroups are of equal length and the
 // short tiles share the fixed cost of a tile with long ones.  With nft odd the middle
-// tile is a pair of its own.  a.nft counts pairs.  The reduction runs from the last column
-// down to the tile's first: tiles of different lengths then start together at column
-// d_in - 64, so the workgroups of one token tile read each slice of its x_S rows at about
-// the same time and share it in L2.
+// tile is a pair of its own.  a.nft counts pairs.  The first tile of a pair reduces from
+// the last column down to its first, the second from its first column up to the last:
+// the first tiles of all pairs then start together at column d_in - 64, and, every pair
+// being of the same length, the second tiles all end together at column d_in - 1.  So the
+// workgroups of one token tile (with different pairs, side by side on an XCD) read each
+// slice of its x_S rows in the same step, in both halves, and share it in L2.  (Both
+// halves top-down had the second halves of different pairs a few slices apart: 88% of
+// their x_S reads missed L2 in a slice-level model of one XCD, 20 GB of fetch per
+// 20-layer launch against 15 GB with this order.)
 //
 // One tile of the norm kernel: item `item` of the launch, half 0 (tile pp) or half 1 (tile
 // nft - 1 - pp).
@@ -212,19 +217,20 @@ __device__ __forceinline__ NormTile norm_tile(const FillKArgs& a, int item, int 
   return t;
 }
 
-// DMA operands of a norm tile: rows f0 .. f0 + 255 of R from its last column down, and the
-// tile's gathered x_S rows (the same rows for both tiles of an item).
-__device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile& t,
+// DMA operands of a norm tile: rows f0 .. f0 + 255 of R over columns f0 .. d_in - 1, and
+// the tile's gathered x_S rows (the same rows for both tiles of an item).  Half 0 runs from
+// the last column down (the bases point at column d_in - 64), half 1 from column f0 up.
+__device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile& t, int half,
                                               DmaOperand& Fo, DmaOperand& To) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int f0 = t.ft * kTile, t0 = t.tt * kTile;
+  const int col = half == 0 ? a.d_in - kPipeBK : f0;
   const uint16_t* R = a.L[t.g].A;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
     const int ce = dma_chunk_elems(r, lane);
-    Fo.base[p] = reinterpret_cast<const unsigned char*>(R + (size_t)(f0 + r0) * a.d_in +
-                                                         (a.d_in - kPipeBK));
+    Fo.base[p] = reinterpret_cast<const unsigned char*>(R + (size_t)(f0 + r0) * a.d_in + col);
     Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
     const int tok = t0 + r;
     int row = 0;
@@ -232,9 +238,18 @@ __device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile
       const int x = a.idx[tok];
       if (x >= 0 && x < a.P) row = x;
     }
-    To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + (a.d_in - kPipeBK));
+    To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + col);
     To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
   }
+}
+
+// The first loads of a norm tile, in its half's direction.
+__device__ __forceinline__ void norm_prologue(const DmaOperand& Fo, const DmaOperand& To, int K,
+                                              int half, unsigned char* smem) {
+  if (half == 0)
+    gemm_prologue<true>(Fo, To, K, smem);
+  else
+    gemm_prologue<false>(Fo, To, K, smem);
 }
 
 // The norm kernel is persistent: one workgroup per CU (each holds 128 KB of LDS) takes
@@ -256,13 +271,16 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   if (item >= a.n_items) return;
   NormTile cur = norm_tile(a, item, 0);
   DmaOperand Fo, To;
-  norm_operands(a, cur, Fo, To);
-  gemm_prologue<true>(Fo, To, a.d_in - cur.ft * kTile, smem);
+  norm_operands(a, cur, 0, Fo, To);
+  norm_prologue(Fo, To, a.d_in - cur.ft * kTile, 0, smem);
   for (;;) {
     const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
     const float my_r = a.L[cur.g].b[f0 + tid];
     f32x16 acc[4][4];
-    gemm_mainloop<true>(acc, Fo, To, a.d_in - f0, smem);   // ends with a barrier: LDS is free
+    if (half == 0)                                          // each ends with a barrier:
+      gemm_mainloop<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
+    else
+      gemm_mainloop<false>(acc, Fo, To, a.d_in - f0, smem);
 
     // the next tile: the other half of this item (unless it is the middle tile of an odd
     // nft), else the first half of the next item
@@ -275,8 +293,8 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     NormTile nxt = cur;
     if (more) {
       nxt = norm_tile(a, nitem, nhalf);
-      norm_operands(a, nxt, Fo, To);
-      gemm_prologue<true>(Fo, To, a.d_in - nxt.ft * kTile, smem);
+      norm_operands(a, nxt, nhalf, Fo, To);
+      norm_prologue(Fo, To, a.d_in - nxt.ft * kTile, nhalf, smem);
     }
 
     float* ssq = reinterpret_cast<float*>(a.layer_ws + cur.g * a.per_layer + a.per_layer_h);
