@@ -99,6 +99,25 @@ def test_calib_hadamard_bit_exact_and_chunk_invariant():
     np.testing.assert_array_equal(one.G[low], (n * np.eye(d))[low])
 
 
+def test_calib_empty_and_one_row_chunks_bit_exact():
+    # chunks of 0, 1, 1, 255 and 1,791 rows: the empty call changes nothing, one-row and
+    # ragged chunks fill a partial row tile, and on exactly representable data the sums
+    # still equal the oracle's bit for bit
+    n, d, L = 2048, 256, 2
+    X, Y, _, _ = _hadamard(n, d, L, 41)
+    xs_g, yl_g = bf16(X), [bf16(y) for y in Y]
+    cuts = [0, 0, 1, 2, 257, n]
+    g = GpuStats(run_calib([xs_g[a:b] for a, b in zip(cuts, cuts[1:])],
+                           [[y[a:b] for y in yl_g] for a, b in zip(cuts, cuts[1:])], d, L), d, L)
+    st = oracle.calib_new(d, L)
+    oracle.calib_accumulate(st, X, list(Y))
+    low = np.tril(np.ones((d, d), dtype=bool))
+    assert g.n == n
+    assert np.array_equal(g.G[low], st.G[low])
+    assert np.array_equal(g.YX, st.YX)
+    assert np.array_equal(g.s_S, st.s_S) and np.array_equal(g.s_l, st.s_l)
+
+
 def test_reset_clears_state():
     d, L = 256, 1
     state = torch.full((B.ridgefill_calib_state_bytes(d, L),), 7, dtype=torch.uint8, device="cuda")

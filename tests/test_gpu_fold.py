@@ -114,6 +114,18 @@ def test_folded_and_plain_fills_agree():
             assert e <= 5e-3
 
 
+def test_folded_empty_filled_list_leaves_cache_untouched():
+    # T = N: no prefix rows, nothing filled; the folded fill writes no page
+    case = _case(256, 2, 2, 64, 40, 40, 0, 4, 74)
+    inp = build_inputs(case)
+    before = [(l["k_pages"].clone(), l["v_pages"].clone()) for l in inp["layers"]]
+    assert run_fill(case, inp, np.zeros(0, np.int32), folded=True) == B.RF_OK
+    torch.cuda.synchronize()
+    for l, (k, v) in zip(inp["layers"], before):
+        assert torch.equal(l["k_pages"].view(torch.int16), k.view(torch.int16))
+        assert torch.equal(l["v_pages"].view(torch.int16), v.view(torch.int16))
+
+
 def test_fold_group_size_does_not_change_the_buffers():
     # layers folded one at a time and four side by side (one batched Cholesky): the
     # per-layer arithmetic is the same, so the folded buffers agree bit for bit
