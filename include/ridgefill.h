@@ -75,8 +75,8 @@ typedef struct rf_layer {
   uint16_t* v_pages;       /* bf16 [num_pages][page_size][n_kv_heads][head_dim]        */
   /* Optional parts (NULL = absent). */
   const uint16_t* k_norm_w; /* bf16 [head_dim]: per-head key RMSNorm (Qwen-style layers;
-                               section "Hybrid layers and two corrections": Qwen models
-                               normalise keys), applied to each key head after W_K and
+                               section "Hybrid layers and two corrections": the Qwen
+                               models apply a norm to the keys), applied to each key head after W_K and
                                before RoPE                                               */
   const float* v_scale;     /* fp32 [n_kv_heads]: value-rescale factors (same section,
                                value rescale); head h of every filled value is
@@ -104,8 +104,8 @@ typedef struct rf_paged_kv {
 
 /* ------------------------------------------------------------------------------
  * Row partition.  Section "Method: ..." -> "Two numbers set the skip range": the last
- * T rows are the tail; the other N - T rows are the prefix, and a prefix row is either
- * exact or filled.  Host-only, integer, no GPU.
+ * T rows are the tail; the N - T rows before them are the prefix, whose rows are each
+ * computed exactly or filled from the maps.  Host-only, integer, no GPU.
  *
  *   exact_mask  host uint8 [N - T]: nonzero marks an exact row (may be NULL = none)
  *   filled_idx  host int32 [N - T] out: the filled rows in ascending order
@@ -138,7 +138,8 @@ rf_status ridgefill_select_rows(const float* scores, int64_t P, int64_t k, uint8
 
 /* ------------------------------------------------------------------------------
  * Fill.  Section "Ridge map: predict the input, and the original projection runs
- * unchanged" (prediction equation, "own normalization and projections", Fig. 2):
+ * unchanged" (prediction equation; the paragraph on feeding the predicted input to the
+ * layer's norm and K/V projections; Fig. 2):
  * for every filled row t and every given upper layer l,
  *     x_hat = A_l x_S[t] + b_l          (A_l = A_q,l * A_scale,l for an int8 map)
  *     h     = x_hat / sqrt(mean(x_hat^2) + eps) * norm_w_l
@@ -188,7 +189,7 @@ size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled
 
 /* ------------------------------------------------------------------------------
  * Fill with host-resident maps.  Section "Ridge map ...", map size paragraph: maps can
- * stay in GPU memory or be streamed from host memory one layer at a time.  Same
+ * stay in GPU memory or be streamed from host memory layer by layer.  Same
  * computation and arguments as ridgefill_fill, except that every layer's A (or A_q), or
  * for folded layers its whole folded buffer, is a HOST pointer, ideally page-locked
  * (hipHostMalloc) so that the copies run asynchronously.  Layers are processed in groups
@@ -264,10 +265,9 @@ rf_status ridgefill_quantize_map(const float* A, int64_t rows, int64_t cols, int
 
 /* ------------------------------------------------------------------------------
  * Value-rescale factors.  Section "Hybrid layers and two corrections", value rescale:
- * the first c tail rows pass through each upper layer's value projection twice, once
- * with their exact layer input and once with the map's prediction; per KV head the
- * ratio of the exact value's norm to the predicted value's norm, averaged over the c
- * rows, is the factor that multiplies the filled values.  For layer l and head h:
+ * for each upper layer, the values of the first c tail rows are computed from both the
+ * true layer input and the mapped input; per KV head, the mean over those rows of
+ * |exact value| / |predicted value| scales the filled values.  For layer l and head h:
  *     v_e(t) = W_V,l RMSNorm_l(x_l,exact[t]),  v_p(t) = W_V,l RMSNorm_l(A_l x_S[t] + b_l)
  *     v_scale_out[l][h] = (1/c) sum_t |v_e(t)_h| / |v_p(t)_h|
  * Pass v_scale_out + l * n_kv_heads as layer l's v_scale to ridgefill_fill.

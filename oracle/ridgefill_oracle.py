@@ -16,14 +16,15 @@ by its section:
   [obj]    same section, the ridge objective
   [closed] same section, the closed-form solution after subtracting the means
   [alpha]  same section, alpha = lambda * tr(X^T X) / d_in and the one-pass statistics
-  [own]    same section, "own normalization and projections" and Fig. 2
+  [own]    same section, the paragraph on feeding the predicted input to the
+           layer's norm and K/V projections, and Fig. 2
   [arms]   "Tables from the paper", Table 3 (exact / no fill / identity / RidgeFill)
   [notation] "Tables from the paper", Table 2
   [size]   same section as [map], the paragraph on map size (int8 maps, maps whose input
            width differs from their output width, resident or streamed maps)
   [rescale] "Hybrid layers and two corrections", the value-rescale paragraph
-  [qknorm] same paragraph (Qwen models normalise keys) and "Experiments", the error
-           attribution paragraph on key normalization
+  [qknorm] same paragraph (the Qwen models apply a norm to the keys) and "Experiments",
+           the error attribution paragraph on key normalization
   [select] "Which rows to compute exactly", attention selection
   [fold]   [map] and [own] taken together: the folded form of one layer (the norm weight
            and the K/V projections multiplied into the map, the prediction's sum of
@@ -35,7 +36,7 @@ Readings of points the page leaves open (each is listed with its reason in the d
 notes of the repository):
   * x_S is the input to layer S; the upper layers are l = S .. L-1 and each has its own
     map, the one at l = S included.
-  * "that layer's own normalization" is RMSNorm with a multiplicative weight w and an
+  * the layer's normalization, whose type the page does not name, is RMSNorm with a multiplicative weight w and an
     epsilon eps:  y = x / sqrt(mean(x^2) + eps) * w.
   * The key/value projections have no bias; head h owns columns [h*hd, (h+1)*hd).
   * RoPE is applied to the keys only, rotate-half pairing (j, j + hd/2), inverse
@@ -101,7 +102,7 @@ __all__ = [
 def upper_layers(S: int, L: int) -> list[int]:
     """Layers whose cache a filled row receives from its map: l = S, ..., L-1.
 
-    [split]: layers 0..S-1 run normally for every row; the map predicts the input of
+    [split]: every row runs the layers below S as usual; the map predicts the input of
     every upper layer l >= S from x_S (one map per upper layer, [map]).
     """
     if not (0 <= S <= L):
@@ -112,9 +113,9 @@ def upper_layers(S: int, L: int) -> list[int]:
 def partition(N: int, T: int, exact_rows):
     """Split a prompt of N rows into (filled, exact, tail), each an ascending int64 array.
 
-    [split]: the last T rows are the tail and run every layer; the other N - T rows are
-    the prefix; in the upper layers a prefix row is either exact (runs normally) or
-    filled (gets its cache from the map).  Exact rows must lie in the prefix and must
+    [split]: the last T rows are the tail and run every layer; the N - T rows before
+    them form the prefix, and above the split each prefix row is exact (computed as
+    usual) or filled (its cache comes from the map).  Exact rows must lie in the prefix and must
     not repeat.
     """
     N = int(N)
@@ -239,9 +240,9 @@ def fill_rows(x_S_rows, positions, A, b, norm_w, W_K, W_V, *, eps, theta, n_kv, 
 def value_scale(x_S_tail, x_l_exact_tail, A, b, norm_w, W_V, *, eps, n_kv, hd):
     """Per-KV-head value-rescale factors of one upper layer ([rescale]).
 
-    The first c tail rows go through the layer's value projection twice: with their
-    exact layer input x_l (x_l_exact_tail, [c, d_out]) and with the map's prediction
-    from their split-layer state (x_S_tail, [c, d_in]).  For head h the factor is the
+    The values of the first c tail rows are computed twice: from their true layer input
+    x_l (x_l_exact_tail, [c, d_out]) and from the map's prediction out of their
+    split-layer state (x_S_tail, [c, d_in]).  For head h the factor is the
     mean over the c rows of |v_exact[h]| / |v_pred[h]|.  Returns [n_kv] float64.
     """
     W_V = np.asarray(W_V, dtype=np.float64)

@@ -1,9 +1,9 @@
 // One-pass calibration statistics on gfx950.
 //
 // Source: English RidgeFill review (jaehun.me), section "Ridge map: predict the input,
-// and the original projection runs unchanged" -- calibration accumulates X^T X, X^T Y_l
-// and the two means in one pass of the original model, so a new lambda needs only a new
-// solve.  Raw sums and raw second moments are kept; the solve centres them.
+// and the original projection runs unchanged" -- calibration gathers X^T X, X^T Y_l
+// and both means while the unmodified model runs once over the calibration rows; another
+// lambda is then just another solve.  Raw sums and raw second moments are kept; the solve centres them.
 //
 // Per call (n rows of x_S, bf16 [n][d_in], and of every x_l, bf16 [n][d_out]):
 //   sums   fp64 s_S += sum_t x_S[t], s_l += sum_t x_l[t]; header n += rows
