@@ -196,7 +196,9 @@ size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled
  * sized by the workspace (ridgefill_fill_workspace_bytes_ex with RF_MAPS_STREAMED, plus
  * RF_MAPS_INT8 for int8 maps or RF_MAPS_FOLDED for folded layers); group g's maps (or
  * folded buffers) are copied on `copy_stream` into landing slot g % 2 while group g - 1
- * computes on `stream`.  copy_stream must be a different stream; both must stay
+ * computes on `stream`.  Of a folded buffer only what the fill reads is copied: P, c, r,
+ * kappa, and R from each 256-row block's diagonal block rightwards (the zeros below the
+ * diagonal blocks, about half of R, are not).  copy_stream must be a different stream; both must stay
  * valid until the work completes.  The first copy of a call waits for the work already
  * enqueued on `stream`, so back-to-back calls on one workspace are ordered.  The results
  * are bit-identical to ridgefill_fill's.

@@ -879,6 +879,24 @@ int group_size(int n_layers, int group) {
   return (n_layers + ngroups - 1) / ngroups;
 }
 
+// A folded buffer from host memory into a landing slot: P whole; of R only what the norm
+// kernel reads (block row f0 .. f0 + 255 from column f0 on: the zeros left of the diagonal
+// blocks, about half of R, stay behind and the slot's bytes there are never read); then c,
+// r and kappa.  d_in is a multiple of kTile.
+hipError_t copy_folded(unsigned char* land, const unsigned char* src, const FoldLayout& F,
+                       int d_in, hipStream_t s) {
+  hipError_t e = hipMemcpyAsync(land + F.P, src + F.P, F.R - F.P, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  const size_t pitch = (size_t)d_in * 2;
+  for (int f0 = 0; f0 < d_in; f0 += kTile) {
+    const size_t off = F.R + (size_t)f0 * pitch + (size_t)f0 * 2;
+    e = hipMemcpy2DAsync(land + off, pitch, src + off, pitch, (size_t)(d_in - f0) * 2, kTile,
+                         hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipMemcpyAsync(land + F.c, src + F.c, F.total - F.c, hipMemcpyHostToDevice, s);
+}
+
 struct StreamEvents {
   hipEvent_t ready[2] = {nullptr, nullptr};
   hipEvent_t done[2] = {nullptr, nullptr};
@@ -945,13 +963,16 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
     for (int g = 0; g < G; ++g) {
       a.L[g] = layers[l0 + g];
       unsigned char* land = lws + g * p.L.per_layer + p.L.land + slot * p.L.land_slot;
-      // a folded layer's A points at R inside its host buffer: the buffer starts F.R before
-      const void* src = int8     ? static_cast<const void*>(layers[l0 + g].Aq)
-                        : folded ? static_cast<const void*>(
-                                       reinterpret_cast<const unsigned char*>(layers[l0 + g].A) - F.R)
-                                 : static_cast<const void*>(layers[l0 + g].A);
-      if ((e = hipMemcpyAsync(land, src, map_bytes, hipMemcpyHostToDevice, copy_stream)) != hipSuccess)
-        return e;
+      if (folded) {
+        // a folded layer's A points at R inside its host buffer: the buffer starts F.R before
+        const unsigned char* src = reinterpret_cast<const unsigned char*>(layers[l0 + g].A) - F.R;
+        if ((e = copy_folded(land, src, F, p.d_in, copy_stream)) != hipSuccess) return e;
+      } else {
+        const void* src = int8 ? static_cast<const void*>(layers[l0 + g].Aq)
+                               : static_cast<const void*>(layers[l0 + g].A);
+        if ((e = hipMemcpyAsync(land, src, map_bytes, hipMemcpyHostToDevice, copy_stream)) != hipSuccess)
+          return e;
+      }
       if (int8) {
         codes[g] = reinterpret_cast<const int8_t*>(land);
       } else if (folded) {

@@ -168,7 +168,7 @@ def folded_layer_dicts(inp):
 
 
 def run_fill(case: Case, inp, filled: np.ndarray, ws_layers: int | None = None, stream=None,
-             streamed: bool = False, folded: bool = False):
+             streamed: bool = False, folded: bool = False, ws_byte: int | None = None):
     dev = inp["xS"].device
     shape = make_shape(case)
     nf = int(filled.size)
@@ -182,6 +182,8 @@ def run_fill(case: Case, inp, filled: np.ndarray, ws_layers: int | None = None, 
     nbytes = B.ridgefill_fill_workspace_bytes(shape, max(nf, 1),
                                               ws_layers if ws_layers else case.n_layers, flags)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if ws_byte is not None:          # poison: a read of workspace bytes the call never wrote
+        ws.fill_(ws_byte)            # then shows in the results
     if folded and streamed:
         layers = host_maps(folded_layer_dicts(inp))
         copy = torch.cuda.Stream()

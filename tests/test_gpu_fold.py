@@ -219,14 +219,16 @@ def test_folded_group_split_is_bit_identical():
 def test_streamed_folded_layers_bit_identical():
     # folded buffers in page-locked host memory, 5 layers through a workspace that holds 2:
     # groups of 2, 2, 1, so both landing slots are reused; the caches match the resident
-    # folded fill bit for bit
+    # folded fill bit for bit.  Only R's upper block triangle is copied: with the workspace
+    # filled with 0xFF bytes (NaN as bf16 and fp32) beforehand, a read of the rest of a
+    # landing slot would show as NaNs
     case = _case(512, 5, 2, 128, 700, 100, 60, 16, 73, knorm=True, vscale=True)
     f = _filled(case)
     a = build_inputs(case)
     b = build_inputs(case)
-    assert run_fill(case, a, f, folded=True) == B.RF_OK
+    assert run_fill(case, a, f, folded=True, ws_byte=0xFF) == B.RF_OK
     b["folded"] = a["folded"]
-    assert run_fill(case, b, f, folded=True, streamed=True, ws_layers=2) == B.RF_OK
+    assert run_fill(case, b, f, folded=True, streamed=True, ws_layers=2, ws_byte=0xFF) == B.RF_OK
     torch.cuda.synchronize()
     for l in range(case.n_layers):
         for key in ("k_pages", "v_pages"):
