@@ -182,13 +182,24 @@ def cpu_baseline_fill(cfg, inp, budget_s: float = 15.0):
                       f"workload (NumPy float64), {spent:.1f} s"}
 
 
-def _time_ms(fn, reps: int, warmup: int = 1) -> float:
-    """Average milliseconds of fn() over reps calls, from events on the current stream (the
-    library enqueues everything on it; streamed copies join it through events)."""
+def _time_ms(fn, reps: int, warmup: int = 1, median: bool = False) -> float:
+    """Milliseconds of fn() from events on the current stream (the library enqueues
+    everything on it; streamed copies join it through events): the average over reps calls
+    enqueued back to back, or with `median` the median of the calls timed one by one (one
+    slow call, such as a transient on the first copies from new page-locked buffers, then
+    does not move the figure)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if median:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        ev[-1].synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -275,7 +286,7 @@ def fill_variant(cfg, dev, *, int8=False, streamed=False, knorm=False, folded=Fa
         B.ridgefill_fill(shape, inp["xS"], cfg.N, cfg.T, idx, nf, layers, inp["table"],
                          cfg.page_size, inp["num_pages"], ws, copy_stream=copy)
 
-    ms = _time_ms(step, reps)
+    ms = _time_ms(step, reps, warmup=2 if streamed else 1, median=True)
     if B.ridgefill_read_status(ws) != B.RF_OK:
         raise SystemExit(f"variant fill reported device status for {cfg.name}")
     flops = cfg.fill_flops()

@@ -952,10 +952,15 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
   const bool folded = (p.flags & kWsFolded) != 0;
   const FoldLayout F = fold_layout(p.d_in, p.kv);
   const size_t map_bytes = folded ? F.total : (size_t)p.d * p.d_in * (int8 ? 1 : 2);
-  const int gsize = group_size(n_layers, p.group);
+  // Group sizes ramp up 1, 2, 3, ... to the workspace's group size: only the first
+  // layer's copy waits with no compute to hide under, and each later group's copy is
+  // about as long as the previous group's compute or shorter (a group of 4 folded 27B-shape
+  // layers copies in ~7 ms, which a first group of that size would leave exposed).
+  const int gmax = p.group;
   int gi = 0;
-  for (int l0 = 0; l0 < n_layers; l0 += gsize, ++gi) {
-    const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
+  for (int l0 = 0, G = 0; l0 < n_layers; l0 += G, ++gi) {
+    const int want = gi + 1 < gmax ? gi + 1 : gmax;
+    G = (n_layers - l0) < want ? (n_layers - l0) : want;
     const int slot = gi & 1;
     if (gi >= 2 && (e = hipStreamWaitEvent(copy_stream, ev.done[slot], 0)) != hipSuccess) return e;
     FillKArgs a = fill_args(p, lws);
