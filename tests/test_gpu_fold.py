@@ -218,7 +218,7 @@ def test_folded_group_split_is_bit_identical():
 
 def test_streamed_folded_layers_bit_identical():
     # folded buffers in page-locked host memory, 5 layers through a workspace that holds 2:
-    # groups of 2, 2, 1, so both landing slots are reused; the caches match the resident
+    # groups of 1, 2, 2, so both landing slots are reused; the caches match the resident
     # folded fill bit for bit.  Only R's upper block triangle is copied: with the workspace
     # filled with 0xFF bytes (NaN as bf16 and fp32) beforehand, a read of the rest of a
     # landing slot would show as NaNs

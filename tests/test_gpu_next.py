@@ -84,10 +84,12 @@ def test_rectangular_identity_block_copies_x():
 
 
 @pytest.mark.parametrize("int8", [False, True])
-def test_streamed_maps_bit_identical(int8):
-    # 5 layers through a workspace that holds 2: groups of 2, 2, 1, so both landing slots
-    # are reused
-    case = _case(512, 5, 2, 128, 700, 100, 60, 16, 40, int8=int8)
+@pytest.mark.parametrize("nl,ws_layers", [(5, 2), (9, 3)])
+def test_streamed_maps_bit_identical(int8, nl, ws_layers):
+    # group sizes ramp up to what the workspace holds: 5 layers through 2 run as groups of
+    # 1, 2, 2 and 9 through 3 as 1, 2, 3, 3, so landing slots are reused, also by groups of
+    # another size than the one that used them before
+    case = _case(512, nl, 2, 128, 700, 100, 60, 16, 40, int8=int8)
     inp = build_inputs(case)
     f = _filled(case)
     assert run_fill(case, inp, f) == B.RF_OK
@@ -95,7 +97,7 @@ def test_streamed_maps_bit_identical(int8):
     for l in inp["layers"]:
         l["k_pages"].view(torch.int16).fill_(-1)
         l["v_pages"].view(torch.int16).fill_(-1)
-    assert run_fill(case, inp, f, ws_layers=2, streamed=True) == B.RF_OK
+    assert run_fill(case, inp, f, ws_layers=ws_layers, streamed=True) == B.RF_OK
     torch.cuda.synchronize()
     for (k, v), l in zip(ref, inp["layers"]):
         assert _same_bits(k, l["k_pages"]) and _same_bits(v, l["v_pages"])
