@@ -2,8 +2,8 @@
 the benchmark times: the 27B-shaped fill with int8 maps streamed from pinned host memory in
 4-layer groups, the Qwen3-8B-shaped fill with key norm, the 8B-shaped fill with a split
 state twice as wide as the layers, the value-rescale factors over c = 512 tail rows of
-the 27B shape, and the folded 8B, 27B and Qwen3-8B (key norm) fills against the plain
-oracle.
+the 27B shape, and the folded 8B, 27B (resident, and streamed from pinned host memory in
+groups of up to 4 layers) and Qwen3-8B (key norm) fills against the plain oracle.
 
 Fills: routing bit-exact on every byte of every layer's pools (sentinel-filled), K and V
 against the oracle on 512 sampled rows of every layer (first and last filled row, rows
@@ -60,13 +60,15 @@ def _values(cfg, inp, filled, exact, pg, sl, A_of=None, kn_of=None):
     return rows.size, worst
 
 
-def _run(cfg, inp, flags=0, ws_layers=None, copy=None, layers=None):
+def _run(cfg, inp, flags=0, ws_layers=None, copy=None, layers=None, ws_byte=None):
     dev = inp["xS"].device
     filled = B.ridgefill_partition(cfg.N, cfg.T, inp["exact_mask"])
     shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta, d_in=cfg.d_in)
     idx = torch.from_numpy(filled).to(dev)
     ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, filled.size, ws_layers or cfg.n_upper,
                                                       flags), dtype=torch.uint8, device=dev)
+    if ws_byte is not None:             # poison: reads of bytes the call never wrote show up
+        ws.fill_(ws_byte)
     B.ridgefill_fill(shape, inp["xS"], cfg.N, cfg.T, idx, filled.size, layers or inp["layers"],
                      inp["table"], cfg.page_size, inp["num_pages"], ws, copy_stream=copy)
     assert B.ridgefill_read_status(ws) == B.RF_OK
@@ -212,7 +214,7 @@ def test_8b_folded_full_size():
     print(f"8B folded: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
 
 
-def _folded_full(cfg, knorm=False):
+def _folded_full(cfg, knorm=False, streamed=False):
     dev = torch.device("cuda")
     print(f"\n{cfg.name} folded: inputs", flush=True)
     inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
@@ -229,11 +231,23 @@ def _folded_full(cfg, knorm=False):
     B.ridgefill_fold_maps(shape, inp["layers"], bufs, fws)
     assert B.ridgefill_read_status(fws) == B.RF_OK
     del fws
+    if streamed:                       # folded buffers to page-locked host memory
+        host = []
+        for b in bufs:
+            h = torch.empty(b.shape, dtype=b.dtype, pin_memory=True)
+            h.copy_(b.cpu())
+            host.append(h)
+        bufs = host
+        torch.cuda.empty_cache()
     folded = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"],
                    **({"k_norm_w": lay["k_norm_w"]} if knorm else {}))
               for l, lay in enumerate(inp["layers"])]
-    print(f"{cfg.name} folded: fill", flush=True)
-    filled = _run(cfg, inp, B.RF_MAPS_FOLDED, layers=folded)
+    print(f"{cfg.name} folded: fill{' streamed from host memory' if streamed else ''}", flush=True)
+    if streamed:
+        filled = _run(cfg, inp, B.RF_MAPS_FOLDED | B.RF_MAPS_STREAMED, ws_layers=4,
+                      copy=torch.cuda.Stream(), layers=folded, ws_byte=0xFF)
+    else:
+        filled = _run(cfg, inp, B.RF_MAPS_FOLDED, layers=folded)
     _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
     pg, sl = _routing(cfg, inp, filled)
     n, worst = _values(cfg, inp, filled, exact, pg, sl,
@@ -248,3 +262,10 @@ def test_27b_folded_full_size():
 
 def test_qwen3_8b_key_norm_folded_full_size():
     _folded_full(configs.QWEN3_8B, knorm=True)
+
+
+def test_27b_folded_streamed_full_size():
+    # the 48 folded buffers in page-locked host memory, through a workspace of 4 layers
+    # (groups of 1, 2, 3, then 4), as the benchmark runs it; only the upper block triangle
+    # of each R is copied, and the workspace starts as 0xFF bytes
+    _folded_full(configs.QWEN27B, streamed=True)
