@@ -342,7 +342,28 @@ def run_variants(dev):
     res["27b_value_scale"] = {"c": c, "upper_layers": cfg.n_upper, "ms": vms,
                               "tflop": vflop / 1e12,
                               "pct_bf16_mfma_peak": 100.0 * vflop / (vms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
-    del inp, xl, vws
+    # the same factors from folded layers (predicted side folded, exact side through W_V)
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, cfg.n_upper), dtype=torch.uint8,
+                      device=dev)
+    bufs = [torch.empty(B.ridgefill_fold_bytes(shape), dtype=torch.uint8, device=dev)
+            for _ in inp["layers"]]
+    B.ridgefill_fold_maps(shape, inp["layers"], bufs, fws)
+    if B.ridgefill_read_status(fws) != B.RF_OK:
+        raise SystemExit("fold reported a device status for the value-scale layers")
+    del fws
+    flay = [dict(folded=bufs[l], norm_w=lay["norm_w"], W_V=lay["W_V"])
+            for l, lay in enumerate(inp["layers"])]
+    fvws = torch.empty(B.ridgefill_value_scale_workspace_bytes(shape, c, cfg.n_upper,
+                                                               B.RF_MAPS_FOLDED),
+                       dtype=torch.uint8, device=dev)
+    fout = torch.empty_like(out)
+    fvms = _time_ms(lambda: B.ridgefill_value_scale(shape, xt, xl, flay, fout, fvws), 3)
+    fflop = c * cfg.n_upper * (cfg.d * (cfg.d + 1) + 2 * cfg.kv * cfg.d + 2 * cfg.kv * cfg.d)
+    res["27b_value_scale_folded"] = {
+        "c": c, "upper_layers": cfg.n_upper, "ms": fvms, "tflop_executed": fflop / 1e12,
+        "max_rel_diff_vs_plain": float(((fout - out).abs() / out.abs()).max()),
+        "note": "predicted values from P, c, R, r, kappa; the exact rows through W_V"}
+    del inp, xl, vws, fvws, bufs, flay
     torch.cuda.empty_cache()
     res["27b_int8_resident"] = fill_variant(configs.QWEN27B, dev, int8=True)
     res["27b_int8_streamed_4_layer_groups"] = fill_variant(configs.QWEN27B, dev, int8=True,

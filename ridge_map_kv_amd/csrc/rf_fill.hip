@@ -429,8 +429,8 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
     my_off = a.row_slot[t0 + tid];
     if (a.has_knorm && tid < a.hd) my_kn = bf16_to_f32(Lp.kn[tid]);
     if (Lp.vs && tid < a.n_kv) my_vs = Lp.vs[tid];
-    if (a.folded) my_c = Lp.fc[f0 + tid];
   }
+  if (a.folded) my_c = Lp.fc[f0 + tid];
 
   f32x16 acc[4][4];
   gemm_pipeline(acc, Fo, To, a.kdim, smem);
@@ -455,6 +455,16 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
       const int tl = wt * 128 + n * 32 + (lane & 31);
       const int tok = t0 + tl;
       const float r = rstd[tl];
+      if (a.folded) {           // P x + c: the value before the 1/rms scale
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 cv = *reinterpret_cast<const f32x4*>(sfc + wf * 128 + m * 32 + q * 8 + h * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m][n][q * 4 + e] += cv[e];
+          }
+      }
       float s0, s1;
       head_sumsq(acc, n, a.hd, s0, s1);
       if (h == 0 && tok < a.n_filled) {
@@ -1005,8 +1015,8 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
 // RMSNorm and W_V, and the exact tail inputs through RMSNorm and W_V; per (row, head) the
 // two value norms; per head the mean of their ratio.
 hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
-                              const uint16_t* const* x_exact, int n_layers, float* out,
-                              const VsLayout& V, hipStream_t stream) {
+                              const uint16_t* const* x_exact, const uint16_t* const* exact_wv,
+                              int n_layers, float* out, const VsLayout& V, hipStream_t stream) {
   hipError_t e = launch_clear_status(p.status, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(iota_kernel, dim3(p.mpad / 256), dim3(256), 0, stream,
@@ -1021,12 +1031,18 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
       a.L[g] = layers[l0 + g];
       codes[g] = layers[l0 + g].Aq;
     }
-    if (p.flags & kWsInt8) expand_group(p, a, G, codes, stream);
-    a.nft = p.d / kTile;
     a.f_base = 0;
-    hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
-                       a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
+    if (a.folded) {              // |x_hat|^2 from the triangular factor, then 1/rms
+      a.nft = (p.d_in / kTile + 1) / 2;
+      launch_tiles(fill_norm_kernel, a, G * a.ntt * a.nft, stream);
+      hipLaunchKernelGGL(rstd_folded_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a);
+    } else {
+      if (p.flags & kWsInt8) expand_group(p, a, G, codes, stream);
+      a.nft = p.d / kTile;
+      hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
+                         a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
+    }
     ExactArgs x = {};
     for (int g = 0; g < G; ++g) {
       x.x[g] = x_exact[l0 + g];
@@ -1045,9 +1061,15 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
     a.nft = 2 * p.kv / kTile - a.f_base;
     a.vnorm = V.vn_pred;
     hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
-    a.layer_ws = V.exact;
-    a.vnorm = V.vn_exact;
-    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    // the exact rows (bf16(x_l * w), d wide) through the layer's own W_V
+    FillKArgs b = a;
+    b.folded = 0;
+    b.kdim = p.d;
+    b.nchunk = p.d / 128;
+    b.layer_ws = V.exact;
+    b.vnorm = V.vn_exact;
+    for (int g = 0; g < G; ++g) b.L[g].WV = exact_wv[l0 + g];
+    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * b.ntt * b.nft), dim3(kThreads), 0, stream, b);
     hipLaunchKernelGGL(vscale_kernel, dim3(G * p.n_kv), dim3(256), 0, stream, V.vn_pred,
                        V.vn_exact, p.n_filled, p.mpad, p.n_kv, out + (size_t)l0 * p.n_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;

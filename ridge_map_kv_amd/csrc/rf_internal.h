@@ -124,9 +124,11 @@ struct VsLayout {
   float* vn_pred;
   float* vn_exact;
 };
+// The predicted rows use `layers` (plain or folded, as plan.flags says); the exact rows
+// always go through the layers' own W_V, exact_wv[l].
 hipError_t launch_value_scale(const FillPlan& plan, const FillLayerPtrs* layers,
-                              const uint16_t* const* x_exact, int n_layers, float* out,
-                              const VsLayout& V, hipStream_t stream);
+                              const uint16_t* const* x_exact, const uint16_t* const* exact_wv,
+                              int n_layers, float* out, const VsLayout& V, hipStream_t stream);
 
 // Calibration -------------------------------------------------------------------
 struct CalibLayout {

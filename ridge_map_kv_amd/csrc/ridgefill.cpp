@@ -332,11 +332,16 @@ static rf::VsLayout vs_layout(const rf::FillWsLayout& L, int64_t c, int n_kv, in
 
 size_t ridgefill_value_scale_workspace_bytes(const rf_shape* shape, int64_t c, int32_t n_layers,
                                              int32_t map_flags) {
-  if (check_shape(shape) != RF_OK || c < 1 || n_layers < 1 || (map_flags & ~RF_MAPS_INT8))
+  if (check_shape(shape) != RF_OK || c < 1 || n_layers < 1 ||
+      (map_flags & ~(RF_MAPS_INT8 | RF_MAPS_FOLDED)) ||
+      ((map_flags & RF_MAPS_INT8) && (map_flags & RF_MAPS_FOLDED)))
     return 0;
+  if ((map_flags & RF_MAPS_FOLDED) && check_foldable(shape) != RF_OK) return 0;
+  // folded layers use the plain layout: their partials fit where the plain ones go, and the
+  // exact rows need the staged-input blocks either way
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim,
                                                 shape->n_kv_heads * shape->head_dim, c,
-                                                map_flags_of(map_flags));
+                                                map_flags_of(map_flags & RF_MAPS_INT8));
   const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
   const rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, g);
   return V.total_fixed + (size_t)2 * g * L.per_layer;
@@ -359,9 +364,26 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
     return fail(RF_E_SHAPE, "the tail rows of x_S span more than 4 GiB");
   if (!aligned(ws, 256) || !aligned(v_scale_out, 4))
     return fail(RF_E_WORKSPACE, "workspace must be 256-byte aligned, v_scale_out 4-byte aligned");
-  const bool int8 = layers[0].A_q != nullptr;
+  const bool folded = layers[0].folded != nullptr;
+  const bool int8 = !folded && layers[0].A_q != nullptr;
+  if (folded) {
+    s = check_foldable(shape);
+    if (s != RF_OK) return s;
+  }
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
+    if ((l.folded != nullptr) != folded)
+      return fail(RF_E_INVALID, "layer %d: all layers of a call must be folded or none", i);
+    if (folded) {                 // the folded buffer, and for the exact rows W_V and norm_w
+      if (!l.norm_w || !l.W_V || !x_l_tail[i])
+        return fail(RF_E_INVALID, "layer %d: a folded layer needs norm_w, W_V and its exact "
+                    "tail rows", i);
+      if (!aligned(l.folded, 256) || !aligned(l.norm_w, 16) || !aligned(l.W_V, 16) ||
+          !aligned(x_l_tail[i], 16))
+        return fail(RF_E_SHAPE, "layer %d: the folded buffer needs 256-byte, norm_w, W_V and "
+                    "the exact rows 16-byte alignment", i);
+      continue;
+    }
     if (!l.b || !l.norm_w || !l.W_K || !l.W_V || !x_l_tail[i])
       return fail(RF_E_INVALID, "layer %d: b, norm_w, W_K, W_V and its exact tail rows are "
                   "required", i);
@@ -375,9 +397,10 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
       return fail(RF_E_SHAPE, "layer %d: A, A_q, b, norm_w, W_V and the exact rows need 16-byte "
                   "alignment", i);
   }
-  const unsigned flags = int8 ? rf::kWsInt8 : 0u;
+  const unsigned flags = int8 ? rf::kWsInt8 : folded ? rf::kWsFolded : 0u;
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim,
-                                                shape->n_kv_heads * shape->head_dim, c, flags);
+                                                shape->n_kv_heads * shape->head_dim, c,
+                                                int8 ? rf::kWsInt8 : 0u);
   const int gmax = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
   // the largest group the workspace holds: fixed part for that group + 2 blocks per layer
   int group = 0;
@@ -414,12 +437,25 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
   p.group = group;
   p.L = L;
   std::vector<rf::FillLayerPtrs> lp((size_t)n_layers);
+  std::vector<const uint16_t*> wv((size_t)n_layers);
+  const rf::FoldLayout F = rf::fold_layout(d_in, p.kv);
   for (int i = 0; i < n_layers; ++i) {
     const rf_layer& l = layers[i];
-    lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, nullptr, nullptr, nullptr, nullptr, l.A_q, l.A_scale};
+    wv[i] = l.W_V;
+    if (folded) {
+      const unsigned char* f = static_cast<const unsigned char*>(l.folded);
+      const uint16_t* P = reinterpret_cast<const uint16_t*>(f + F.P);
+      lp[i] = {reinterpret_cast<const uint16_t*>(f + F.R), reinterpret_cast<const float*>(f + F.r),
+               l.norm_w, P, P + (size_t)p.kv * d_in, nullptr, nullptr, nullptr, nullptr, nullptr,
+               nullptr, reinterpret_cast<const float*>(f + F.c),
+               reinterpret_cast<const float*>(f + F.kappa)};
+    } else {
+      lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, nullptr, nullptr, nullptr, nullptr, l.A_q,
+               l.A_scale, nullptr, nullptr};
+    }
   }
-  hipError_t e = rf::launch_value_scale(p, lp.data(), x_l_tail, n_layers, v_scale_out, V,
-                                        static_cast<hipStream_t>(stream));
+  hipError_t e = rf::launch_value_scale(p, lp.data(), x_l_tail, wv.data(), n_layers,
+                                        v_scale_out, V, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "value-scale launch");
   return ok();
 }

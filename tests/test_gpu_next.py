@@ -15,8 +15,8 @@ import oracle
 from ridge_map_kv_amd import binding as B
 from ridge_map_kv_amd import synth
 
-from fillcase import (Case, bf16_np, build_inputs, check_routing, check_values, host_maps,
-                      make_shape, run_fill, to_bf16)
+from fillcase import (Case, bf16_np, build_inputs, check_routing, check_values, fold_layers,
+                      host_maps, make_shape, run_fill, to_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,8 +152,11 @@ def _vs_inputs(case, c, dev="cuda"):
     inp = build_inputs(case)
     xS_tail = to_bf16(synth.x_split((c, case.width), seed=case.seed + 1000), dev)
     xt = bf16_np(xS_tail).astype(np.float32)
-    exact = [to_bf16(synth.exact_tail_inputs(xt[:, :case.d] if case.width >= case.d else xt,
-                                             case.d, case.seed, l), dev)
+    if case.width >= case.d:
+        xin = xt[:, :case.d]
+    else:                        # a tall map: the exact inputs are d wide, x_S narrower
+        xin = np.concatenate([xt, np.zeros((c, case.d - case.width), np.float32)], axis=1)
+    exact = [to_bf16(synth.exact_tail_inputs(xin, case.d, case.seed, l), dev)
              for l in range(case.n_layers)]
     return inp, xS_tail, exact
 
@@ -198,6 +201,59 @@ def test_value_scale_factors_parity(d, nl, nkv, hd, c, seed, opts):
     want = _oracle_factors(case, inp, xS_tail, exact)
     print(f"\nfactors {got.ravel()[:4]} ... max rel {np.max(np.abs(got / want - 1)):.2e}", flush=True)
     np.testing.assert_allclose(got, want, rtol=2e-3)
+
+
+VS_FOLDED = [
+    # d, layers, n_kv, hd, c, seed, options
+    (512, 3, 2, 128, 300, 58, {}),
+    (768, 2, 4, 64, 512, 59, dict(d_in=512)),        # tall map
+    (256, 2, 2, 128, 77, 60, {}),                    # c short of one tile
+]
+
+
+@pytest.mark.parametrize("d,nl,nkv,hd,c,seed,opts", VS_FOLDED)
+def test_value_scale_factors_folded_layers(d, nl, nkv, hd, c, seed, opts):
+    # folded layers: the predicted values from P, c, R, r, kappa, the exact ones from the
+    # layer's own W_V and norm weight; against the oracle (plain fields) and the plain GPU path
+    case = _case(d, nl, nkv, hd, 600, 64, 0, 16, seed, **opts)
+    inp, xS_tail, exact = _vs_inputs(case, c)
+    plain = _gpu_factors(case, inp, xS_tail, exact).cpu().numpy().astype(np.float64)
+    bufs, st = fold_layers(case, inp)
+    assert st == B.RF_OK
+    layers = [dict(folded=bufs[l], norm_w=lay["norm_w"], W_V=lay["W_V"])
+              for l, lay in enumerate(inp["layers"])]
+    shape = make_shape(case)
+    ws = torch.empty(B.ridgefill_value_scale_workspace_bytes(shape, c, nl, B.RF_MAPS_FOLDED),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    out = torch.full((nl, nkv), float("nan"), device="cuda")
+    B.ridgefill_value_scale(shape, xS_tail, exact, layers, out, ws)
+    assert B.ridgefill_read_status(ws) == B.RF_OK
+    got = out.cpu().numpy().astype(np.float64)
+    want = _oracle_factors(case, inp, xS_tail, exact)
+    print(f"\nfolded factors max rel {np.max(np.abs(got / want - 1)):.2e} "
+          f"(plain path {np.max(np.abs(plain / want - 1)):.2e})", flush=True)
+    np.testing.assert_allclose(got, want, rtol=2e-3)
+    np.testing.assert_allclose(got, plain, rtol=3e-3)
+
+
+def test_value_scale_folded_argument_errors():
+    case = _case(256, 2, 2, 128, 600, 64, 0, 16, 61)
+    inp, xS_tail, exact = _vs_inputs(case, 100)
+    bufs, _ = fold_layers(case, inp)
+    shape = make_shape(case)
+    ws = torch.empty(B.ridgefill_value_scale_workspace_bytes(shape, 100, 2, B.RF_MAPS_FOLDED),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((2, case.n_kv), device="cuda")
+    no_wv = [dict(folded=bufs[l], norm_w=lay["norm_w"]) for l, lay in enumerate(inp["layers"])]
+    with pytest.raises(RuntimeError, match="W_V"):
+        B.ridgefill_value_scale(shape, xS_tail, exact, no_wv, out, ws)
+    mixed = [dict(folded=bufs[0], norm_w=inp["layers"][0]["norm_w"], W_V=inp["layers"][0]["W_V"]),
+             inp["layers"][1]]
+    with pytest.raises(RuntimeError, match="folded"):
+        B.ridgefill_value_scale(shape, xS_tail, exact, mixed, out, ws)
+    assert B.ridgefill_value_scale_workspace_bytes(shape, 100, 2,
+                                                   B.RF_MAPS_FOLDED | B.RF_MAPS_INT8) == 0
 
 
 def test_value_scale_is_one_when_exact_rows_equal_prediction():
