@@ -178,16 +178,24 @@ def _random_cases(n, seed):
     return out
 
 
-@pytest.mark.parametrize("k", range(12))
+@pytest.mark.parametrize("k", range(32))
 def test_seeded_random_workloads(k):
-    spec = _random_cases(12, 2024)[k]
+    # cases from 12 on also start from a workspace of 0xFF bytes, and every third of them,
+    # every folded one and every one with 3 layers streams its maps (or folded buffers) from
+    # page-locked host memory through a one-layer workspace (landing slots are reused from
+    # the third layer on)
+    spec = _random_cases(32, 2024)[k]
     case, folded = spec["case"], spec["folded"]
+    streamed = k >= 12 and (k % 3 == 0 or folded or case.n_layers == 3)
     print(f"\ncase {k}: d={case.d} d_in={case.width} layers={case.n_layers} kv={case.n_kv}x"
           f"{case.hd} N={case.N} T={case.T} exact={len(case.exact)} page={case.page_size} "
-          f"knorm={case.knorm} vscale={case.vscale} int8={case.int8} folded={folded}", flush=True)
+          f"knorm={case.knorm} vscale={case.vscale} int8={case.int8} folded={folded} "
+          f"streamed={streamed}", flush=True)
     inp = build_inputs(case)
     f = _filled(case)
-    assert run_fill(case, inp, f, folded=folded) == B.RF_OK
+    assert run_fill(case, inp, f, folded=folded, streamed=streamed,
+                    ws_layers=1 if streamed else None,
+                    ws_byte=0xFF if k >= 12 else None) == B.RF_OK
     check_routing(case, inp, f)
     if len(f):
         check_values(case, inp, f)

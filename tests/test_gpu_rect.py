@@ -149,9 +149,9 @@ def _random_fits(n, seed):
     return out
 
 
-@pytest.mark.parametrize("k", range(6))
+@pytest.mark.parametrize("k", range(12))
 def test_seeded_random_fits_match_oracle(k):
-    d_in, d_out, L, rows, cuts, lam, seed = _random_fits(6, 77)[k]
+    d_in, d_out, L, rows, cuts, lam, seed = _random_fits(12, 77)[k]
     print(f"\nfit {k}: d_in={d_in} d_out={d_out} layers={L} rows={rows} cuts={cuts} "
           f"lambda={lam}", flush=True)
     xS, xl = _data(d_in, d_out, L, rows, seed)
