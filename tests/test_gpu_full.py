@@ -190,3 +190,58 @@ def test_full_size_solve_hadamard_closed_form():
             np.testing.assert_allclose(b[l].cpu().numpy(), cs[l] + lam / (1 + lam) * (Ws[l] @ m),
                                        atol=2e-4)
         print(f"full solve: lambda {lam} closed form ok", flush=True)
+
+
+def test_largest_prefix_accepted_one_more_refused():
+    # The fill addresses gathered rows of x_S with 32-bit byte offsets; the host admits a
+    # prefix whose last row ends within 4 GiB.  At d_in = x_stride = 256 that is
+    # P = 8,388,607 rows (a 4.29 GB x_S): rows at both ends of the largest prefix are filled
+    # correctly, and one more prefix row is refused before anything is enqueued.
+    dev = torch.device("cuda")
+    d, n_kv, hd, T, page = 256, 1, 128, 64, 256
+    P = (0xFFFFFFFF - 2 * d) // (2 * d) + 1
+    assert (P - 1) * 2 * d + 2 * d <= 0xFFFFFFFF < P * 2 * d + 2 * d
+    N = P + T
+    print(f"\nlargest prefix: P = {P:,} rows, x_S of {(N + 1) * d * 2 / 1e9:.2f} GB", flush=True)
+    g = torch.Generator(device=dev).manual_seed(11)
+    x_S = torch.empty((N + 1, d), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, N + 1, 1 << 20):
+        r1 = min(r0 + (1 << 20), N + 1)
+        x_S[r0:r1] = torch.randn((r1 - r0, d), generator=g, device=dev).to(torch.bfloat16)
+    A = torch.eye(d, device=dev) + 0.05 * torch.randn(d, d, generator=g, device=dev)
+    A = A.to(torch.bfloat16)
+    b = 0.1 * torch.randn(d, generator=g, device=dev)
+    w = (1 + 0.1 * torch.randn(d, generator=g, device=dev)).to(torch.bfloat16)
+    WK = (torch.randn(n_kv * hd, d, generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
+    WV = (torch.randn(n_kv * hd, d, generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
+    num_pages = (N + 1 + page - 1) // page
+    table_np = np.random.default_rng(12).permutation(num_pages).astype(np.int32)
+    table = torch.from_numpy(table_np).to(dev)
+    pool = lambda: torch.full((num_pages, page, n_kv, hd), -1, dtype=torch.int16,
+                              device=dev).view(torch.bfloat16)
+    kp, vp = pool(), pool()
+    rows = np.concatenate([np.arange(0, 50), np.arange(P - 250, P)]).astype(np.int32)
+    idx = torch.from_numpy(rows).to(dev)
+    shape = B.make_shape(d, n_kv, hd, 1e-5, 5e5)
+    layer = [dict(A=A, b=b, norm_w=w, W_K=WK, W_V=WV, k_pages=kp, v_pages=vp)]
+    ws = torch.empty(B.ridgefill_fill_workspace_bytes(shape, rows.size, 1), dtype=torch.uint8,
+                     device=dev)
+    B.ridgefill_fill(shape, x_S, N, T, idx, rows.size, layer, table, page, num_pages, ws)
+    assert B.ridgefill_read_status(ws) == B.RF_OK
+    pg, sl = oracle.paged_location(rows, table_np, page)
+    written = kp.view(torch.int16) != -1
+    expect = torch.zeros((num_pages, page), dtype=torch.bool, device=dev)
+    expect[torch.from_numpy(pg).to(dev), torch.from_numpy(sl).to(dev)] = True
+    assert torch.equal(written.flatten(2).all(-1), expect)
+    assert torch.equal(written.flatten(2).any(-1), expect)
+    Ko, Vo = oracle.fill_rows(_np64(x_S[idx.long()]), rows, _np64(A),
+                              b.cpu().numpy().astype(np.float64), _np64(w), _np64(WK), _np64(WV),
+                              eps=1e-5, theta=5e5, n_kv=n_kv, hd=hd)
+    tpg, tsl = torch.from_numpy(pg).to(dev), torch.from_numpy(sl).to(dev)
+    ek, ev = _rel(_np64(kp[tpg, tsl]), Ko), _rel(_np64(vp[tpg, tsl]), Vo)
+    print(f"  rows 0..49 and {P - 250:,}..{P - 1:,}: K {ek:.2e} V {ev:.2e}", flush=True)
+    assert ek <= 5e-3 and ev <= 5e-3
+    # one more prefix row: the same call with T one smaller is refused on the host
+    with pytest.raises(RuntimeError, match="4 GiB"):
+        B.ridgefill_fill(shape, x_S, N + 1, T, idx, rows.size, layer, table, page,
+                         num_pages, ws)
