@@ -16,7 +16,10 @@
  *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round-to-nearest-
  *    even where the library produces them).  All matrices are row-major.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is enqueued
- *    on it and the call returns without waiting, except where stated.
+ *    on it and the call returns without waiting, except where stated.  ridgefill_fill
+ *    with resident maps (plain or folded) enqueues kernels only (the status word is
+ *    cleared by a kernel, not a memset), so it can be captured into a HIP graph and
+ *    replayed; the workspace, index list and pools must then stay at their addresses.
  *  - Errors found on the host (null pointers, shapes, sizes, workspace too small,
  *    invalid parameters) return a non-zero rf_status before anything is enqueued;
  *    ridgefill_last_error() then gives a description.  A failed launch returns
