@@ -628,7 +628,11 @@ __global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double
   if (row >= n_layers * d_out) return;
   const float* y = YX + (size_t)row * d_in;
   double s = 0.0;
-  for (int k = lane; k < d_in; k += 64) s += (double)y[k] * v[k];
+  for (int k = lane * 4; k < d_in; k += 256) {          // 16-byte loads: d_in % 64 == 0
+    const f32x4 q = *reinterpret_cast<const f32x4*>(y + k);
+    s += (double)q[0] * v[k] + (double)q[1] * v[k + 1] + (double)q[2] * v[k + 2] +
+         (double)q[3] * v[k + 3];
+  }
   for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
   if (lane == 0) {
     const double n = *reinterpret_cast<const double*>(scalars + kNOff);
@@ -640,34 +644,31 @@ __global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double
 
 // ---------------------------------------------------------------- split bf16 map GEMM
 // Cx[g][o] = [C_hi | C_hi | C_lo] of row o of C_l = YX_l - n mu_l mu_S^T (l = l0 + g;
-// o < d_out, columns k < d_in), the centring in fp64.  Four consecutive k per thread.
+// o < d_out, columns k < d_in), the centring in fp64.  One row per blockIdx.y (g d_out + o),
+// four consecutive k per thread.
 __global__ void split_c_kernel(const float* YX, const double* mu, const unsigned char* scalars,
-                               int d_in, int d_out, int l0, int G, uint16_t* Cx) {
+                               int d_in, int d_out, int l0, int rows, uint16_t* Cx) {
   const double n = *reinterpret_cast<const double*>(scalars + kNOff);
-  const size_t per = (size_t)d_out * d_in;
-  const size_t quads = (size_t)G * per / 4;
-  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads;
-       q += (size_t)gridDim.x * blockDim.x) {
-    const size_t e = q * 4;
-    const int g = (int)(e / per);
-    const size_t r = e - (size_t)g * per;
-    const int o = (int)(r / d_in), k = (int)(r - (size_t)o * d_in);
-    const int l = l0 + g;
-    const f32x4 y = *reinterpret_cast<const f32x4*>(YX + ((size_t)l * d_out + o) * d_in + k);
+  const size_t d = (size_t)d_in;
+  for (int row = blockIdx.y; row < rows; row += gridDim.y)
+  for (int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4; k < d_in;
+       k += gridDim.x * blockDim.x * 4) {
+    const int g = row / d_out, o = row - g * d_out, l = l0 + g;
+    const float* src = YX + ((size_t)l * d_out + o) * d_in;
     const double nm = n * mu[(size_t)d_in + (size_t)l * d_out + o];
+    uint16_t* dst = Cx + (size_t)row * (3 * d);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(src + k);
     uint16_t hi[4], lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) split_bf16((double)y[j] - nm * mu[k + j], hi[j], lo[j]);
-    const size_t d = (size_t)d_in;
-    uint16_t* row = Cx + ((size_t)g * d_out + o) * (3 * d);
     u32x2 h2, l2;
     h2.x = hi[0] | (uint32_t)hi[1] << 16;
     h2.y = hi[2] | (uint32_t)hi[3] << 16;
     l2.x = lo[0] | (uint32_t)lo[1] << 16;
     l2.y = lo[2] | (uint32_t)lo[3] << 16;
-    *reinterpret_cast<u32x2*>(row + k) = h2;
-    *reinterpret_cast<u32x2*>(row + d + k) = h2;
-    *reinterpret_cast<u32x2*>(row + 2 * d + k) = l2;
+    *reinterpret_cast<u32x2*>(dst + k) = h2;
+    *reinterpret_cast<u32x2*>(dst + d + k) = h2;
+    *reinterpret_cast<u32x2*>(dst + 2 * d + k) = l2;
   }
 }
 
@@ -807,8 +808,9 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
 
   for (int l0 = 0; l0 < n_layers; l0 += L.group) {
     const int G = (n_layers - l0) < L.group ? (n_layers - l0) : L.group;
-    hipLaunchKernelGGL(split_c_kernel, dim3(2048), dim3(256), 0, stream, YX, mu, w, d_in, d_out,
-                       l0, G, Cx);
+    const int rows = G * d_out;
+    hipLaunchKernelGGL(split_c_kernel, dim3((d_in + 1023) / 1024, rows < 65535 ? rows : 65535),
+                       dim3(256), 0, stream, YX, mu, w, d_in, d_out, l0, rows, Cx);
     SolveGemmArgs a = {Cx, Mx, A_out, A_bf16, d_in, d_out, l0, d_in / kTile, d_out / kTile};
     ProfileScope ps(RF_KERNEL_SOLVE_MAP, stream);
     hipLaunchKernelGGL(solve_gemm_kernel, dim3(G * a.nt_out * a.nt_in), dim3(kThreads), 0, stream,
