@@ -75,14 +75,17 @@ __global__ void means_kernel(const unsigned char* state, int count, size_t sum_o
 }
 
 // C[r][c] = G[max][min] - n mu_r mu_c (full symmetric, fp64).
+// C = G - n mu mu^T on and below the diagonal, one row per workgroup row (coalesced).  The
+// Cholesky reads nothing above the diagonal (the diagonal blocks' upper entries only under
+// masks, and it writes them as zeros), so the upper triangle is left as it is.
 __global__ void centre_kernel(const float* G, const double* mu, const unsigned char* scalars,
                               int d, double* C) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)d * d) return;
-  const int r = (int)(idx / d), c = (int)(idx - (size_t)r * d);
   const double n = *reinterpret_cast<const double*>(scalars + kNOff);
-  const float g = r >= c ? G[(size_t)r * d + c] : G[(size_t)c * d + r];
-  C[idx] = (double)g - n * mu[r] * mu[c];
+  for (int r = blockIdx.y; r < d; r += gridDim.y) {
+    const double nr = n * mu[r];
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c <= r; c += gridDim.x * blockDim.x)
+      C[(size_t)r * d + c] = (double)G[(size_t)r * d + c] - nr * mu[c];
+  }
 }
 
 // alpha = lambda tr(C) / d in a fixed order; then C += alpha I.
@@ -788,8 +791,6 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
   uint16_t* Cx = reinterpret_cast<uint16_t*>(w + L.Cx);
   const float* G = reinterpret_cast<const float*>(st + CL.G);
   const float* YX = reinterpret_cast<const float*>(st + CL.YX);
-  const size_t dd = (size_t)d * d;
-  const unsigned gdd = (unsigned)((dd + 255) / 256);
   const int nbk = d / NB;
 
   hipError_t e = launch_clear_status(status, stream);
@@ -797,7 +798,8 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
   const int nmu = d_in + n_layers * d_out;
   hipLaunchKernelGGL(means_kernel, dim3((nmu + 255) / 256), dim3(256), 0, stream, st, nmu,
                      CL.sum_S, mu, w);
-  hipLaunchKernelGGL(centre_kernel, dim3(gdd), dim3(256), 0, stream, G, mu, w, d, C);
+  hipLaunchKernelGGL(centre_kernel, dim3((d + 255) / 256, d < 65535 ? d : 65535), dim3(256), 0,
+                     stream, G, mu, w, d, C);
   hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
   // L and U = L^-T together, then M = U U^T
   if ((e = launch_cholesky(C, d, linv, status, stream, 1, 0, 0, W)) != hipSuccess) return e;
