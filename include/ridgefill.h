@@ -199,8 +199,8 @@ size_t ridgefill_fill_workspace_bytes_ex(const rf_shape* shape, int64_t n_filled
  * sized by the workspace (ridgefill_fill_workspace_bytes_ex with RF_MAPS_STREAMED, plus
  * RF_MAPS_INT8 for int8 maps or RF_MAPS_FOLDED for folded layers); group g's maps (or
  * folded buffers) are copied on `copy_stream` into landing slot g % 2 while group g - 1
- * computes on `stream`.  Of a folded buffer only what the fill reads is copied: P, c, r,
- * kappa, and R from each 256-row block's diagonal block rightwards (the zeros below the
+ * computes on `stream`.  Of a folded buffer only what the fill reads is copied: P, c, r1,
+ * g, kappa, and R1 from each 256-row block's diagonal block rightwards (the zeros below the
  * diagonal blocks, about half of R, are not).  copy_stream must be a different stream; both must stay
  * valid until the work completes.  The first copy of a call waits for the work already
  * enqueued on `stream`, so back-to-back calls on one workspace are ordered.  The results
@@ -223,9 +223,20 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
  * RoPE, value rescale and paged store as the plain fill.  Same result up to rounding;
  * R x_S needs half the multiply-adds of A x_S, and x_hat is never stored.
  *
+ * A^T A is accumulated in fp32 from the exact bf16 products; its diagonal is lifted by a
+ * relative 2^-16 before the fp64 Cholesky (so that the accumulation's rounding cannot make
+ * the factorization meet a non-positive pivot for maps of large condition number), which
+ * adds 2^-16 sum_i |A_i|^2 x_i^2 to |x_hat|^2 (about 1.5e-5 of it where the columns A_i x_i
+ * do not cancel).  A zero column of A still gives a zero pivot.
+ * R is stored with a unit diagonal: R = diag(g) R1 with g = diag(R) in fp32 and R1 in
+ * bf16 whose diagonal entries are exactly 1, and r as r1 = r / g, so that
+ * |R x_S + r|^2 = sum_f g_f^2 (R1_f x_S + r1_f)^2 and the diagonal term (through which
+ * alone feature 0 reaches the sum) is not rounded to bf16.
+ *
  * Folded buffer of one layer (offsets from its start, each 256-byte aligned):
- *     P bf16 [2 kv][d_in] (K rows, then V rows), R bf16 [d_in][d_in] (zeros below the
- *     diagonal), c fp32 [2 kv], r fp32 [d_in], kappa fp32;  kv = n_kv_heads * head_dim.
+ *     P bf16 [2 kv][d_in] (K rows, then V rows), R1 bf16 [d_in][d_in] (unit diagonal,
+ *     zeros below it), c fp32 [2 kv], r1 fp32 [d_in], g fp32 [d_in], kappa fp32;
+ *     kv = n_kv_heads * head_dim.
  * ridgefill_fold_bytes returns its size, 0 when the shape cannot be folded: A^T A must be
  * positive definite, so d_in <= d, and d_in must be a multiple of 256.
  *
@@ -304,16 +315,30 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
 /* ------------------------------------------------------------------------------
  * Calibration.  Same section, paragraph on alpha and the one-pass statistics: one pass
  * accumulates X^T X, Y_l^T X and the two means; a new lambda needs only a new solve.
- * The state belongs to one split (one x_S source) and is caller-owned device memory:
- *   [0, 256)   header: int64 row count n, int32 d, int32 n_layers, magic
- *   then       fp64 sum_t x_S          [d]
+ * The state belongs to one split (one x_S source) and is caller-owned device memory.
+ * x_S is accumulated about a per-feature shift s (fp32 holding bf16 values), fixed by the
+ * first call that adds rows: where that call has at least 64 rows, s_i is the bf16
+ * rounding of the mean of feature i over them if that mean exceeds twice their standard
+ * deviation, else 0; a first call of fewer rows fixes s = 0.  Each call accumulates
+ * x'_S = bf16(x_S - s) (exact wherever x_S lies within [s/2, 2s]), so that a feature whose
+ * mean dwarfs its spread keeps its centred moments in fp32 (raw moments would lose them
+ * to cancellation).  Layout:
+ *   [0, 256)   header: int64 row count n, int32 d, int32 n_layers, magic, int32 d,
+ *              int32 shift fixed, int32 state marked bad, int32 (internal)
+ *   then       fp64 sum_t x'_S         [d]
  *              fp64 sum_t x_l          [n_layers][d]
- *              fp32 sum_t x_S x_S^T    [d][d]   (lower triangle valid; i >= j)
- *              fp32 sum_t x_l x_S^T    [n_layers][d][d]  (row = output feature of x_l)
- * Saving the state is a device-to-host copy of ridgefill_calib_state_bytes() bytes.
+ *              fp32 sum_t x'_S x'_S^T  [d][d]   (lower triangle valid; i >= j)
+ *              fp32 sum_t x_l x'_S^T   [n_layers][d][d]  (row = output feature of x_l)
+ *              fp32 s                  [d]
+ *              scratch: 16384 rows of bf16 [d] where each call stages x'_S (a call of
+ *              more rows is processed in pieces of 16384)
+ * Each region starts on a 256-byte boundary.  Saving the state is a device-to-host copy
+ * of everything before the scratch area.
  *
  * ridgefill_calib_reset clears the state for (d, n_layers); later calls on the state
- * must pass the same d and n_layers (they size every access to it).
+ * must pass the same d and n_layers.  A calibrate call whose sizes differ from the
+ * header's changes nothing and marks the state bad; a later solve on it then reports
+ * RF_E_WORKSPACE through ridgefill_read_status.
  * ridgefill_calibrate adds n_rows rows: x_S device bf16 [n_rows][d]; x_l host array
  * [n_layers] of device bf16 [n_rows][d] pointers.  Sums in fp32 per call and fp64
  * across calls for the means; moments accumulated in fp32.  d: multiple of 256;
@@ -329,10 +354,11 @@ rf_status ridgefill_calibrate(void* state, size_t state_bytes, int32_t d, int32_
 /* The same for maps whose input width differs from their output width (section "Ridge
  * map ...", map-size paragraph): x_S rows are d_in wide, x_l rows d_out wide (both
  * multiples of 256).  The state then holds
- *   [0, 256)   header: int64 n, int32 d_out, int32 n_layers, magic, int32 d_in
- *   then       fp64 sum_t x_S [d_in], fp64 sum_t x_l [n_layers][d_out],
- *              fp32 sum_t x_S x_S^T [d_in][d_in] (lower triangle valid),
- *              fp32 sum_t x_l x_S^T [n_layers][d_out][d_in].
+ *   [0, 256)   header: int64 n, int32 d_out, int32 n_layers, magic, int32 d_in, ...
+ *   then       fp64 sum_t x'_S [d_in], fp64 sum_t x_l [n_layers][d_out],
+ *              fp32 sum_t x'_S x'_S^T [d_in][d_in] (lower triangle valid),
+ *              fp32 sum_t x_l x'_S^T [n_layers][d_out][d_in], fp32 s [d_in],
+ *              scratch bf16 [16384][d_in].
  * The plain calls are these with d_in = d_out = d. */
 size_t ridgefill_calib_state_bytes_ex(int32_t d_in, int32_t d_out, int32_t n_layers);
 rf_status ridgefill_calib_reset_ex(void* state, size_t state_bytes, int32_t d_in, int32_t d_out,
@@ -343,13 +369,16 @@ rf_status ridgefill_calibrate_ex(void* state, size_t state_bytes, int32_t d_in, 
 
 /* ------------------------------------------------------------------------------
  * Solve.  Same section, closed-form equation and the scale-free penalty: with
- * mu = sums / n,  C = sum x_S x_S^T - n mu_S mu_S^T,  C_l = sum x_l x_S^T - n mu_l mu_S^T,
- * alpha = lambda * tr(C) / d,
- *     A_l = C_l (C + alpha I)^-1,     b_l = mu_l - A_l mu_S.
+ * mu = sums / n (mu_S of the shifted rows x'_S),  C = sum x'_S x'_S^T - n mu_S mu_S^T,
+ * C_l = sum x_l x'_S^T - n mu_l mu_S^T,  alpha = lambda * tr(C) / d,
+ *     A_l = C_l (C + alpha I)^-1,     b_l = mu_l - A_l (mu_S + s).
  * (C + alpha I) is factored by a device Cholesky in fp64 and inverted in fp64.  The
  * product C_l M (M = (C + alpha I)^-1) is a bf16 matrix-core GEMM on operands split into
- * bf16 high and low parts (three products, fp32 accumulation), about 2^-17 relative per
- * operand; b_l is accumulated in fp64.
+ * bf16 parts, fp32 accumulation: two parts per operand (hi + mid, three products, about
+ * 2^-17 relative per operand) while kappa_F = |C + alpha I|_F |M|_F <= 16 d, else three
+ * parts (hi + mid + lo, six products, about 2^-25 per operand; the product then takes
+ * twice as long).  The relative error of A grows about as 5e-6 kappa_F / d with two parts
+ * and 1e-7 kappa_F / d with three.  b_l is accumulated in fp64.
  *
  *   A_out       device fp32 [n_layers][d][d] (may be NULL if A_bf16_out is given)
  *   b_out       device fp32 [n_layers][d]
@@ -372,10 +401,19 @@ rf_status ridgefill_solve_ex(const void* state, size_t state_bytes, int32_t d_in
                              uint16_t* A_bf16_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Waits for `stream`, then returns the device status word of a fill, solve or selection
- * workspace: RF_OK, RF_E_ROWS, RF_E_NOT_SPD, or RF_E_INVALID for a NaN score.  Each call
+ * workspace: RF_OK, RF_E_ROWS, RF_E_NOT_SPD, RF_E_WORKSPACE for a solve on a calibration
+ * state whose header disagrees with the solve's sizes or that a calibrate call marked bad,
+ * or RF_E_INVALID for a NaN score.  Each call
  * clears that word on the stream before its own kernels run, so the word reflects the
  * last call only. */
 rf_status ridgefill_read_status(void* ws, void* stream);
+
+/* Waits for `stream`, then reports the conditioning of the last solve on this solve
+ * workspace: *kappa_f = |C + alpha I|_F |(C + alpha I)^-1|_F (an upper bound on the
+ * 2-norm condition number) and *parts = the bf16 parts per operand the map product used
+ * (3: hi, mid, hi pairs, three products; 6: six products).  Both outputs are host pointers;
+ * either may be NULL. */
+rf_status ridgefill_solve_info(void* ws, double* kappa_f, int32_t* parts, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Kernel timing for measurement.  While enabled, every compute-kernel launch of the

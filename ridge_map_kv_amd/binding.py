@@ -44,6 +44,7 @@ EXPORTED = [
     "ridgefill_solve_workspace_bytes_ex",
     "ridgefill_solve_ex",
     "ridgefill_read_status",
+    "ridgefill_solve_info",
     "ridgefill_profile_enable",
     "ridgefill_profile_read",
     "ridgefill_profile_reset",
@@ -126,6 +127,7 @@ def lib() -> C.CDLL:
         "ridgefill_solve_workspace_bytes_ex": (sz, [i32, i32, i32]),
         "ridgefill_solve_ex": (st, [vp, sz, i32, i32, i32, C.c_double, vp, vp, vp, vp, sz, vp]),
         "ridgefill_read_status": (st, [vp, vp]),
+        "ridgefill_solve_info": (st, [vp, C.POINTER(C.c_double), C.POINTER(i32), vp]),
         "ridgefill_profile_enable": (st, [i32]),
         "ridgefill_profile_read": (st, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
         "ridgefill_profile_reset": (st, []),
@@ -321,13 +323,22 @@ def ridgefill_solve(state, d: int, n_layers: int, lam: float, A_out, b_out, A_bf
 
 def ridgefill_read_status(ws, stream=None) -> int:
     """Device status of the last fill/solve/selection on this workspace (waits for the
-    stream): RF_OK, RF_E_ROWS, RF_E_NOT_SPD or RF_E_INVALID (a NaN selection score)."""
+    stream): RF_OK, RF_E_ROWS, RF_E_NOT_SPD, RF_E_INVALID (a NaN selection score) or
+    RF_E_WORKSPACE (a solve on a calibration state that does not match its sizes)."""
     if ws is None:
         raise ValueError("ws is None")
     s = lib().ridgefill_read_status(_ptr(ws), _stream(stream))
-    if s not in (RF_OK, RF_E_ROWS, RF_E_NOT_SPD, RF_E_INVALID):
+    if s not in (RF_OK, RF_E_ROWS, RF_E_NOT_SPD, RF_E_INVALID, RF_E_WORKSPACE):
         _check(s)
     return int(s)
+
+
+def ridgefill_solve_info(ws, stream=None) -> tuple[float, int]:
+    """(kappa_F, parts) of the last solve on this workspace (waits for the stream)."""
+    kap = C.c_double(0.0)
+    parts = C.c_int32(0)
+    _check(lib().ridgefill_solve_info(_ptr(ws), C.byref(kap), C.byref(parts), _stream(stream)))
+    return float(kap.value), int(parts.value)
 
 
 RF_KERNEL_FILL_MAP, RF_KERNEL_FILL_KV, RF_KERNEL_CALIB_MOMENTS, RF_KERNEL_CALIB_SUMS, \

@@ -6,9 +6,18 @@
 // lambda is then just another solve.  Raw sums and raw second moments are kept; the solve centres them.
 //
 // Per call (n rows of x_S, bf16 [n][d_in], and of every x_l, bf16 [n][d_out]):
-//   sums   fp64 s_S += sum_t x_S[t], s_l += sum_t x_l[t]; header n += rows
-//   moments one launch over the lower-triangle tiles of G += x_S^T x_S and all tiles of
-//           every YX_l += x_l^T x_S (row = output feature of x_l, column = feature of x_S).
+//   shift  x_S is accumulated about a per-feature shift s, fixed by the first call that
+//          adds rows: s_i = bf16(mean of x_S[:, i] over that call) where the mean exceeds
+//          twice the standard deviation of those rows, else 0.  Each call stages
+//          x'_S = bf16(x_S - s) in the state's scratch area.  Where a feature's values lie
+//          within [s/2, 2s] the difference is exact (Sterbenz), so a feature whose mean
+//          dwarfs its spread is accumulated without the cancellation that raw fp32
+//          moments suffer when centred: sum x x^T ~ n mu mu^T would swamp the centred part.
+//   sums   fp64 s_S += sum_t x'_S[t], s_l += sum_t x_l[t]; header n += rows
+//   moments one launch over the lower-triangle tiles of G += x'_S^T x'_S and all tiles of
+//           every YX_l += x_l^T x'_S (row = output feature of x_l, column = feature of x_S).
+//           Centring is invariant to the shift (x'_S - mean(x'_S) = x_S - mean(x_S)), and
+//           the solve adds s back to mean(x'_S) where the offset b needs the true mean.
 // The moments kernel reduces over rows: each thread loads an 8-row x 8-feature block
 // (eight 16-byte loads), transposes it in registers and writes eight feature-major
 // 16-byte chunks, so the LDS tiles have the same [feature][row] layout the fill's
@@ -28,7 +37,9 @@ CalibLayout calib_layout(int d_in, int d_out, int n_layers) {
   L.sum_l = L.sum_S + align256((size_t)d_in * 8);
   L.G = L.sum_l + align256((size_t)n_layers * d_out * 8);
   L.YX = L.G + align256((size_t)d_in * d_in * 4);
-  L.total = L.YX + (size_t)n_layers * d_out * d_in * 4;
+  L.shift = L.YX + align256((size_t)n_layers * d_out * d_in * 4);
+  L.stage = L.shift + align256((size_t)d_in * 4);
+  L.total = L.stage + (size_t)kCalibStageRows * d_in * 2;
   return L;
 }
 
@@ -37,6 +48,7 @@ namespace {
 constexpr int kMaxCalibLayers = 64;
 
 struct CalibArgs {
+  const unsigned char* hdr;      // the state's header: no work once it is marked bad
   const uint16_t* xS;
   const uint16_t* xl[kMaxCalibLayers];
   int row0;                      // first row this launch covers
@@ -47,6 +59,8 @@ struct CalibArgs {
   float* YX;
 };
 
+// Clears the sums, moments and shift (the scratch area after them is left alone) and
+// writes the header.
 __global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d_in, int d_out,
                                    int n_layers) {
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -56,11 +70,93 @@ __global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d_in,
   const u32x4 z = {0u, 0u, 0u, 0u};
   for (size_t i = tid; i < n16; i += stride) p[i] = z;
   if (tid == 0) {
+    int32_t* h = reinterpret_cast<int32_t*>(state);
     *reinterpret_cast<int64_t*>(state) = 0;
-    reinterpret_cast<int32_t*>(state)[2] = d_out;
-    reinterpret_cast<int32_t*>(state)[3] = n_layers;
-    reinterpret_cast<uint32_t*>(state)[4] = kCalibMagic;
-    reinterpret_cast<int32_t*>(state)[5] = d_in;
+    h[kHdrDOut] = d_out;
+    h[kHdrLayers] = n_layers;
+    reinterpret_cast<uint32_t*>(state)[kHdrMagic] = kCalibMagic;
+    h[kHdrDIn] = d_in;
+    h[kHdrShiftSet] = 0;
+    h[kHdrBad] = 0;
+    h[kHdrDeciding] = 0;
+  }
+}
+
+__device__ __forceinline__ float lo16f(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
+__device__ __forceinline__ float hi16f(uint32_t x) { return bf16_to_f32(x >> 16); }
+
+__device__ __forceinline__ bool state_bad(const unsigned char* state) {
+  return reinterpret_cast<const volatile int32_t*>(state)[kHdrBad] != 0;
+}
+
+// First step of every call (one thread): a header that disagrees with the call's sizes
+// marks the state bad (every later step of this and later calls then does nothing, and a
+// solve reports it).  On a state whose shift is not yet fixed, this call fixes it: from its
+// own rows when it has at least 64 (kHdrDeciding tells the next two kernels to compute
+// it), as zero otherwise.
+__global__ void calib_check_kernel(unsigned char* state, int d_in, int d_out, int n_layers,
+                                   int n_rows) {
+  int32_t* h = reinterpret_cast<int32_t*>(state);
+  if (reinterpret_cast<uint32_t*>(state)[kHdrMagic] != kCalibMagic || h[kHdrDIn] != d_in ||
+      h[kHdrDOut] != d_out || h[kHdrLayers] != n_layers)
+    h[kHdrBad] = 1;
+  h[kHdrDeciding] = 0;
+  if (h[kHdrBad] || h[kHdrShiftSet]) return;
+  h[kHdrDeciding] = n_rows >= 64 ? 1 : 0;
+  h[kHdrShiftSet] = 1;
+}
+
+// Shift statistics, part 1: block (column block cb, row part p of kShiftParts) sums x_S
+// and x_S^2 over rows p, p + kShiftParts, ... in fp64; partials [2][kShiftParts][d_in].
+constexpr int kShiftParts = 64;
+__global__ __launch_bounds__(256) void shift_partials_kernel(const unsigned char* state,
+                                                             const uint16_t* xS, int n_rows,
+                                                             int d_in, double* part) {
+  if (reinterpret_cast<const int32_t*>(state)[kHdrDeciding] == 0) return;
+  const int col = blockIdx.x * 256 + threadIdx.x, p = blockIdx.y;
+  double s1 = 0.0, s2 = 0.0;
+  for (int t = p; t < n_rows; t += kShiftParts) {
+    const double v = (double)bf16_to_f32(xS[(size_t)t * d_in + col]);
+    s1 += v;
+    s2 += v * v;
+  }
+  part[(size_t)p * d_in + col] = s1;
+  part[((size_t)kShiftParts + p) * d_in + col] = s2;
+}
+
+// Part 2: per column, the partials in a fixed order; s = bf16(mean) where |mean| > 2 sd.
+__global__ __launch_bounds__(256) void shift_decide_kernel(unsigned char* state, int n_rows,
+                                                           int d_in, const double* part,
+                                                           float* shift) {
+  if (reinterpret_cast<const int32_t*>(state)[kHdrDeciding] == 0) return;
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  double s1 = 0.0, s2 = 0.0;
+  for (int p = 0; p < kShiftParts; ++p) {
+    s1 += part[(size_t)p * d_in + col];
+    s2 += part[((size_t)kShiftParts + p) * d_in + col];
+  }
+  const double mean = s1 / n_rows;
+  const double var = s2 / n_rows - mean * mean;
+  const double sd = var > 0.0 ? sqrt(var) : 0.0;
+  shift[col] = fabs(mean) > 2.0 * sd ? bf16_to_f32(f32_to_bf16((float)mean)) : 0.0f;
+}
+
+// x'_S = bf16(x_S - s) for rows [0, n_rows) of x_S into the stage; 8 features per thread.
+__global__ __launch_bounds__(256) void shift_stage_kernel(const unsigned char* state,
+                                                          const uint16_t* xS, int n_rows, int d_in,
+                                                          const float* shift, uint16_t* stage) {
+  if (state_bad(state)) return;
+  for (int row = blockIdx.x; row < n_rows; row += gridDim.x)
+  for (int c8 = threadIdx.x * 8; c8 < d_in; c8 += 256 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xS + (size_t)row * d_in + c8);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(shift + c8);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(shift + c8 + 4);
+    u32x4 o;
+    o[0] = pack_bf16x2(lo16f(v[0]) - s0[0], hi16f(v[0]) - s0[1]);
+    o[1] = pack_bf16x2(lo16f(v[1]) - s0[2], hi16f(v[1]) - s0[3]);
+    o[2] = pack_bf16x2(lo16f(v[2]) - s1[0], hi16f(v[2]) - s1[1]);
+    o[3] = pack_bf16x2(lo16f(v[3]) - s1[2], hi16f(v[3]) - s1[3]);
+    *reinterpret_cast<u32x4*>(stage + (size_t)row * d_in + c8) = o;
   }
 }
 
@@ -68,6 +164,7 @@ __global__ void calib_reset_kernel(unsigned char* state, size_t bytes, int d_in,
 // (slice s = tid / 32, group q = tid % 32) sums rows s, s + 8, ... of columns 8q..8q+7 in
 // fp32; the 8 slices are then added in order in fp64 and folded into the state.
 struct SumArgs {
+  const unsigned char* hdr;
   const uint16_t* x[kMaxCalibLayers + 1];
   int n_rows, d_in, d_out;
   int ncb;               // column blocks of the wider of d_in and d_out
@@ -104,6 +201,7 @@ __device__ __forceinline__ void sums_block(const SumArgs& a, int cb, int m, floa
 
 __global__ __launch_bounds__(256) void calib_sums_kernel(SumArgs a) {
   __shared__ float part[8][256];
+  if (state_bad(a.hdr)) return;
   sums_block(a, blockIdx.x, blockIdx.y, part);
 }
 
@@ -213,6 +311,7 @@ __device__ __forceinline__ void calib_store(const f32x16 (&acc)[4][4], const Cal
 // staged with the transpose done in registers.  Used for the ragged row tail.
 __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  if (state_bad(a.hdr)) return;
   const CalibTile t = calib_tile(a, xcd_remap(blockIdx.x, gridDim.x));
   const uint16_t* X = t.X + (size_t)a.row0 * a.d_in;
   const uint16_t* Y = t.Y + (size_t)a.row0 * t.dy;
@@ -326,6 +425,7 @@ __device__ __forceinline__ void calib_operand(DmaOperand& o, const uint16_t* x, 
 // sums read the same rows again, from HBM, while the last tiles multiply.
 __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArgs a, SumArgs s) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
+  if (state_bad(a.hdr)) return;
   const int ntiles = a.ngram + a.n_layers * a.nt_out * a.nt_in;
   if ((int)blockIdx.x >= ntiles) {
     const int b = blockIdx.x - ntiles;
@@ -426,55 +526,78 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
 hipError_t launch_calib_reset(void* state, int d_in, int d_out, int n_layers, hipStream_t stream) {
   const CalibLayout L = calib_layout(d_in, d_out, n_layers);
   hipLaunchKernelGGL(calib_reset_kernel, dim3(2048), dim3(256), 0, stream,
-                     static_cast<unsigned char*>(state), L.total, d_in, d_out, n_layers);
+                     static_cast<unsigned char*>(state), L.stage, d_in, d_out, n_layers);
   return hipGetLastError();
 }
 
+// One call: the header check and (first call) the shift, then per piece of at most
+// kCalibStageRows rows the staging of x'_S and the moments and sums of that piece.
 hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, const uint16_t* xS,
                             const uint16_t* const* xl, int64_t n_rows, hipStream_t stream) {
   if (n_layers > kMaxCalibLayers) return hipErrorInvalidValue;
   const CalibLayout L = calib_layout(d_in, d_out, n_layers);
   unsigned char* st = static_cast<unsigned char*>(state);
+  float* shift = reinterpret_cast<float*>(st + L.shift);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(st + L.stage);
 
-  SumArgs s = {};
-  s.x[0] = xS;
-  for (int l = 0; l < n_layers; ++l) s.x[1 + l] = xl[l];
-  s.n_rows = (int)n_rows;
-  s.d_in = d_in;
-  s.d_out = d_out;
-  s.sums = reinterpret_cast<double*>(st + L.sum_S);
-  s.count = reinterpret_cast<int64_t*>(st);
-  s.ncb = (d_in > d_out ? d_in : d_out) / 256;
-  const int nsums = s.ncb * (1 + n_layers);
-  // sum_l follows sum_S contiguously: d_in * 8 is a multiple of 256 (d_in % 256 == 0).
+  hipLaunchKernelGGL(calib_check_kernel, dim3(1), dim3(1), 0, stream, st, d_in, d_out, n_layers,
+                     (int)n_rows);
+  // the shift statistics use the stage as scratch (2 x 64 x d_in doubles) before any staging
+  static_assert(2 * kShiftParts * 8 <= kCalibStageRows * 2, "partials fit in the stage");
+  double* part = reinterpret_cast<double*>(stage);
+  hipLaunchKernelGGL(shift_partials_kernel, dim3(d_in / 256, kShiftParts), dim3(256), 0, stream,
+                     st, xS, (int)n_rows, d_in, part);
+  hipLaunchKernelGGL(shift_decide_kernel, dim3(d_in / 256), dim3(256), 0, stream, st,
+                     (int)n_rows, d_in, part, shift);
 
-  CalibArgs a = {};
-  a.xS = xS;
-  for (int l = 0; l < n_layers; ++l) a.xl[l] = xl[l];
-  a.d_in = d_in;
-  a.d_out = d_out;
-  a.n_layers = n_layers;
-  a.nt_in = d_in / kTile;
-  a.nt_out = d_out / kTile;
-  a.ngram = a.nt_in * (a.nt_in + 1) / 2;
-  a.G = reinterpret_cast<float*>(st + L.G);
-  a.YX = reinterpret_cast<float*>(st + L.YX);
-  const int tiles = a.ngram + n_layers * a.nt_out * a.nt_in;
-  const int bulk = (int)(n_rows / kPipeBK) * kPipeBK;
-  if (bulk > 0) {                 // the moments of whole 64-row slices, and the sums
-    a.row0 = 0;
-    a.n_rows = bulk;
-    ProfileScope ps(RF_KERNEL_CALIB_MOMENTS, stream);
-    hipLaunchKernelGGL(calib_moments_dma_kernel, dim3(tiles + nsums), dim3(kThreads), 0, stream,
-                       a, s);
-  } else {                        // fewer than 64 rows: the sums alone
-    ProfileScope ps(RF_KERNEL_CALIB_SUMS, stream);
-    hipLaunchKernelGGL(calib_sums_kernel, dim3(s.ncb, 1 + n_layers), dim3(256), 0, stream, s);
-  }
-  if (n_rows > bulk) {
-    a.row0 = bulk;
-    a.n_rows = (int)(n_rows - bulk);
-    hipLaunchKernelGGL(calib_moments_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+  for (int64_t r0 = 0; r0 < n_rows; r0 += kCalibStageRows) {
+    const int rows = (int)(n_rows - r0 < kCalibStageRows ? n_rows - r0 : kCalibStageRows);
+    const uint16_t* xs_piece = xS + r0 * d_in;
+    hipLaunchKernelGGL(shift_stage_kernel, dim3(2048), dim3(256), 0, stream, st, xs_piece, rows,
+                       d_in, shift, stage);
+
+    SumArgs s = {};
+    s.hdr = st;
+    s.x[0] = stage;
+    for (int l = 0; l < n_layers; ++l) s.x[1 + l] = xl[l] + r0 * d_out;
+    s.n_rows = rows;
+    s.d_in = d_in;
+    s.d_out = d_out;
+    s.sums = reinterpret_cast<double*>(st + L.sum_S);
+    s.count = reinterpret_cast<int64_t*>(st);
+    s.ncb = (d_in > d_out ? d_in : d_out) / 256;
+    const int nsums = s.ncb * (1 + n_layers);
+    // sum_l follows sum_S contiguously: d_in * 8 is a multiple of 256 (d_in % 256 == 0).
+
+    CalibArgs a = {};
+    a.hdr = st;
+    a.xS = stage;
+    for (int l = 0; l < n_layers; ++l) a.xl[l] = xl[l] + r0 * d_out;
+    a.d_in = d_in;
+    a.d_out = d_out;
+    a.n_layers = n_layers;
+    a.nt_in = d_in / kTile;
+    a.nt_out = d_out / kTile;
+    a.ngram = a.nt_in * (a.nt_in + 1) / 2;
+    a.G = reinterpret_cast<float*>(st + L.G);
+    a.YX = reinterpret_cast<float*>(st + L.YX);
+    const int tiles = a.ngram + n_layers * a.nt_out * a.nt_in;
+    const int bulk = rows / kPipeBK * kPipeBK;
+    if (bulk > 0) {                 // the moments of whole 64-row slices, and the sums
+      a.row0 = 0;
+      a.n_rows = bulk;
+      ProfileScope ps(RF_KERNEL_CALIB_MOMENTS, stream);
+      hipLaunchKernelGGL(calib_moments_dma_kernel, dim3(tiles + nsums), dim3(kThreads), 0, stream,
+                         a, s);
+    } else {                        // fewer than 64 rows: the sums alone
+      ProfileScope ps(RF_KERNEL_CALIB_SUMS, stream);
+      hipLaunchKernelGGL(calib_sums_kernel, dim3(s.ncb, 1 + n_layers), dim3(256), 0, stream, s);
+    }
+    if (rows > bulk) {
+      a.row0 = bulk;
+      a.n_rows = rows - bulk;
+      hipLaunchKernelGGL(calib_moments_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -188,7 +188,9 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 }
 
 // Folded layers: per row, the sum of squares of (R x_S + r) over 256-feature tiles of the
-// upper-triangular factor R (A^T A = R^T R), written as 128-feature partials.  Row f of R
+// upper-triangular factor R (A^T A = R^T R), written as 128-feature partials.  R is held
+// as R1 = diag(g)^-1 R with unit diagonal (bf16) and r as r1 = r / g: feature f of the
+// output is g_f (R1_f x_S + r1_f).  Row f of R
 // is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only.  A
 // workgroup takes the pair of tiles ft and nft - 1 - ft (the longer first): every pair
 // then reduces over d_in + 256 columns, so the workgroups are of equal length and the
@@ -262,6 +264,7 @@ __device__ __forceinline__ void norm_prologue(const DmaOperand& Fo, const DmaOpe
 __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   __shared__ __attribute__((aligned(16))) float sr[kTile];
+  __shared__ __attribute__((aligned(16))) float sg[kTile];
   const int nft = a.d_in / kTile;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -276,6 +279,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   for (;;) {
     const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
     const float my_r = a.L[cur.g].b[f0 + tid];
+    const float my_g = a.L[cur.g].fg[f0 + tid];
     f32x16 acc[4][4];
     if (half == 0)                                          // each ends with a barrier:
       gemm_mainloop<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
@@ -299,6 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
 
     float* ssq = reinterpret_cast<float*>(a.layer_ws + cur.g * a.per_layer + a.per_layer_h);
     sr[tid] = my_r;
+    sg[tid] = my_g;
     __syncthreads();
     float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -306,12 +311,13 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + wf * 128 + m * 32 + q * 8 + h * 4);
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + wf * 128 + m * 32 + q * 8 + h * 4);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const float v0 = acc[m][n][q * 4 + 0] + rv.x;
-          const float v1 = acc[m][n][q * 4 + 1] + rv.y;
-          const float v2 = acc[m][n][q * 4 + 2] + rv.z;
-          const float v3 = acc[m][n][q * 4 + 3] + rv.w;
+          const float v0 = (acc[m][n][q * 4 + 0] + rv.x) * gv.x;
+          const float v1 = (acc[m][n][q * 4 + 1] + rv.y) * gv.y;
+          const float v2 = (acc[m][n][q * 4 + 2] + rv.z) * gv.z;
+          const float v3 = (acc[m][n][q * 4 + 3] + rv.w) * gv.w;
           ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
         }
       }
@@ -998,6 +1004,7 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
         a.L[g].WV = P + (size_t)p.kv * p.d_in;
         a.L[g].fc = reinterpret_cast<const float*>(land + F.c);
         a.L[g].kap = reinterpret_cast<const float*>(land + F.kappa);
+        a.L[g].fg = reinterpret_cast<const float*>(land + F.g);
       } else {
         a.L[g].A = reinterpret_cast<const uint16_t*>(land);
       }

@@ -6,16 +6,21 @@
 // the projections are linear, so they multiply into the map; the only non-linear
 // quantity is the scalar |x_hat|^2, and with R the upper-triangular factor of A^T A
 //     |A x + b|^2 = |R x + r|^2 + kappa,  r = R^-T A^T b,  kappa = |b|^2 - |r|^2
-// (expand |R x + r|^2).  R x costs half of A x.  Per layer:
+// (expand |R x + r|^2).  R x costs half of A x.  R is stored with unit diagonal,
+// R = diag(g) R1 (g = diag(R) in fp32, R1 in bf16 with its diagonal exactly 1), and r as
+// r1 = r / g, so |R x + r|^2 = sum_i g_i^2 (R1_i x + r1_i)^2: the diagonal term, which
+// carries a feature whose magnitude dwarfs the others' alone through row 0 when it is
+// feature 0, takes no bf16 rounding.  Per layer:
 //   At  = [A^T | A^T]              bf16 [d_in][2d], a transpose (exact)
 //   Wx  = [W_hi | W_lo]            W = [W_K; W_V] diag(w), each product exact in fp32,
 //                                  split hi = bf16(W), lo = bf16(W - hi) (~2^-17 of W)
 //   P   = Wx At^T = W_hi A + W_lo A   bf16 MFMA, fp32 accumulation, one bf16 rounding
 //   H   = A^T A (lower tiles)      bf16 MFMA: exact products, fp32 accumulation, kept fp64
-//   L   = Cholesky(H)              fp64, the solve's blocked kernels;  R = L^T in bf16
+//   L   = Cholesky(H)              fp64, the solve's blocked kernels;  R1 = bf16 of the rows
+//                                  of L^T over their diagonal entries, g = diag(L)
 //   g   = A^T b,  c = W b,  |b|^2  fp64 accumulation in a fixed order
 //   r   = L^-1 g                   blocked forward substitution (right-looking), fp64
-//   kappa = |b|^2 - |r|^2          fp64
+//   kappa = |b|^2 - |r|^2          fp64;  r1 = r / g
 // Layers go in groups as large as the workspace holds: the GEMMs layer by layer, then the
 // group's Cholesky factorizations and substitutions side by side.  Every launch is on the
 // caller's stream.
@@ -32,7 +37,8 @@ FoldLayout fold_layout(int d_in, int kv) {
   F.R = align256((size_t)2 * kv * d_in * 2);
   F.c = F.R + align256((size_t)d_in * d_in * 2);
   F.r = F.c + align256((size_t)2 * kv * 4);
-  F.kappa = F.r + align256((size_t)d_in * 4);
+  F.g = F.r + align256((size_t)d_in * 4);
+  F.kappa = F.g + align256((size_t)d_in * 4);
   F.total = F.kappa + 256;
   return F;
 }
@@ -97,6 +103,18 @@ __global__ void fold_wsplit_kernel(const uint16_t* WK, const uint16_t* WV, const
 // out_l[m][n] = sum_k F_l[m][k] T_l[n][k] for 256 x 256 tiles of the layers l of one launch
 // (F_l, T_l bf16 rows at a fixed element stride from layer to layer, K a multiple of 64);
 // bf16 (mode 0) or fp64 (mode 1) output.  With `lower`, only tiles n <= m.
+//
+// The fp64 output is A^T A, accumulated in fp32 (the products are exact).  Its rounding
+// error E is about 1e-6 of the diagonal in the Jacobi-scaled sense (|E_ij| ~ 1e-6
+// sqrt(H_ii H_jj) at d_in = 4096), which is larger than the smallest eigenvalue of
+// diag(H)^-1/2 H diag(H)^-1/2 once A's condition number passes a few thousand: the
+// Cholesky would then meet a non-positive pivot at random.  The diagonal is therefore
+// lifted by a relative 2^-16, H + 2^-16 diag(H), which keeps the factorization positive
+// for any A without a zero column, at the price of an exactly known bias in the folded
+// norm: |R x + r|^2 + kappa = |A x + b|^2 + 2^-16 sum_i |A_i|^2 x_i^2, about 1.5e-5 of
+// |x_hat|^2 for rows where the columns do not cancel.  A zero column still gives a zero
+// pivot (RF_E_NOT_SPD).
+constexpr double kGramDiagLift = 1.0 + 1.0 / 65536.0;
 struct NtGemmArgs {
   const uint16_t* F;
   const uint16_t* T;
@@ -147,7 +165,8 @@ __global__ __launch_bounds__(kThreads, 1) void fold_gemm_kernel(NtGemmArgs a) {
           if (a.mode == 0)
             reinterpret_cast<uint16_t*>(out)[row * a.ldo + col] = (uint16_t)f32_to_bf16(v);
           else
-            reinterpret_cast<double*>(out)[row * a.ldo + col] = (double)v;
+            reinterpret_cast<double*>(out)[row * a.ldo + col] =
+                row == col ? (double)v * kGramDiagLift : (double)v;
         }
     }
 }
@@ -230,16 +249,19 @@ __global__ __launch_bounds__(256) void fold_fsub_kernel(const double* L, int d, 
   if (q == 0) g[(size_t)(i + m) * FB + row] -= s;
 }
 
-// r to fp32, kappa = |b|^2 - |r|^2 (fixed-order tree).
+// r1 = r / g and g = diag(L) to fp32, kappa = |b|^2 - |r|^2 (fixed-order tree).
 __global__ __launch_bounds__(1024) void fold_finish_kernel(const double* r, const double* scal,
-                                                           int d_in, float* r_out,
+                                                           const double* L, int d_in,
+                                                           float* r_out, float* g_out,
                                                            float* kappa_out) {
   __shared__ double part[1024];
   const int t = threadIdx.x;
   double s = 0.0;
   for (int i = t; i < d_in; i += 1024) {
+    const double gi = L[(size_t)i * d_in + i];
     s += r[i] * r[i];
-    r_out[i] = (float)r[i];
+    r_out[i] = (float)(r[i] / gi);
+    g_out[i] = (float)gi;
   }
   part[t] = s;
   __syncthreads();
@@ -250,9 +272,11 @@ __global__ __launch_bounds__(1024) void fold_finish_kernel(const double* r, cons
   if (t == 0) *kappa_out = (float)(scal[0] - part[0]);
 }
 
-// R[f][k] = bf16(L[k][f]) for k >= f, 0 below the diagonal, through a 64 x 64 LDS tile.
+// R1[f][k] = bf16(L[k][f] / L[f][f]) for k > f, exactly 1 for k = f, 0 below the diagonal,
+// through a 64 x 64 LDS tile.
 __global__ __launch_bounds__(256) void fold_rt_kernel(const double* L, int d_in, uint16_t* R) {
   __shared__ double t[64][65];
+  __shared__ double gd[64];
   const int f0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
   const bool zero = k0 < f0;                      // the whole tile is below the diagonal
   if (!zero) {
@@ -260,12 +284,16 @@ __global__ __launch_bounds__(256) void fold_rt_kernel(const double* L, int d_in,
       const int r = e >> 6, c = e & 63;           // r: k, c: f
       t[r][c] = L[(size_t)(k0 + r) * d_in + f0 + c];
     }
+    if (threadIdx.x < 64) gd[threadIdx.x] = L[(size_t)(f0 + threadIdx.x) * (d_in + 1)];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int r = e >> 6, c = e & 63;             // r: f, c: k
     const int f = f0 + r, k = k0 + c;
-    R[(size_t)f * d_in + k] = (!zero && k >= f) ? (uint16_t)f32_to_bf16((float)t[c][r]) : 0;
+    uint16_t v = 0;
+    if (!zero && k == f) v = 0x3f80u;             // bf16 1.0
+    else if (!zero && k > f) v = (uint16_t)f32_to_bf16((float)(t[c][r] / gd[r]));
+    R[(size_t)f * d_in + k] = v;
   }
 }
 
@@ -325,8 +353,9 @@ hipError_t launch_fold(int d, int d_in, int kv, const FoldLayerIn* layers, int G
     const double* H = reinterpret_cast<const double*>(blk(l) + W.H64);
     hipLaunchKernelGGL(fold_finish_kernel, dim3(1), dim3(1024), 0, stream,
                        reinterpret_cast<const double*>(blk(l) + W.r),
-                       reinterpret_cast<const double*>(blk(l) + W.scal), d_in,
-                       reinterpret_cast<float*>(o + F.r), reinterpret_cast<float*>(o + F.kappa));
+                       reinterpret_cast<const double*>(blk(l) + W.scal), H, d_in,
+                       reinterpret_cast<float*>(o + F.r), reinterpret_cast<float*>(o + F.g),
+                       reinterpret_cast<float*>(o + F.kappa));
     hipLaunchKernelGGL(fold_rt_kernel, dim3(d_in / 64, d_in / 64), dim3(256), 0, stream, H, d_in,
                        reinterpret_cast<uint16_t*>(o + F.R));
   }

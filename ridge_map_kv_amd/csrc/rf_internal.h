@@ -15,12 +15,14 @@ constexpr size_t kStatusBytes = 256;
 constexpr unsigned kStatusRowsBit = 1u;
 constexpr unsigned kStatusNotSpdBit = 2u;
 constexpr unsigned kStatusScoreBit = 4u;     // a selection score was NaN
+constexpr unsigned kStatusStateBit = 8u;     // the calibration state did not match the sizes
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // One layer of a fill launch.  Plain maps use A, b, w, WK, WV.  A folded layer (kWsFolded)
-// puts its triangular factor R [d_in][d_in] in A, r [d_in] in b, the K and V halves of
-// P in WK and WV (rows of d_in), c [2 kv] in fc and kappa in kap; w is unused.
+// puts its unit-diagonal triangular factor R1 [d_in][d_in] in A, r1 [d_in] in b, diag(R)
+// [d_in] in fg, the K and V halves of P in WK and WV (rows of d_in), c [2 kv] in fc and
+// kappa in kap; w is unused.
 struct FillLayerPtrs {
   const uint16_t* A;            // bf16 map (for an int8 map: its expansion in the workspace)
   const float* b;
@@ -35,6 +37,7 @@ struct FillLayerPtrs {
   const float* As;              // int8 map row scales
   const float* fc;              // folded: c
   const float* kap;             // folded: kappa
+  const float* fg;              // folded: diag(R)
 };
 
 // Workspace variants of a fill call.
@@ -43,10 +46,10 @@ constexpr unsigned kWsStreamed = 2u;   // host maps: two landing slots per layer
 constexpr unsigned kWsFolded = 4u;     // folded layers: no predicted-input buffer
 
 // Folded form of one layer in its caller-owned buffer (byte offsets): P bf16 [2 kv][d_in],
-// R bf16 [d_in][d_in] (upper triangle, zeros below), c fp32 [2 kv], r fp32 [d_in],
-// kappa fp32.
+// R1 bf16 [d_in][d_in] (unit upper triangle, zeros below), c fp32 [2 kv], r1 fp32 [d_in],
+// g = diag(R) fp32 [d_in], kappa fp32.
 struct FoldLayout {
-  size_t P, R, c, r, kappa, total;
+  size_t P, R, c, r, g, kappa, total;
 };
 FoldLayout fold_layout(int d_in, int kv);
 
@@ -131,11 +134,19 @@ hipError_t launch_value_scale(const FillPlan& plan, const FillLayerPtrs* layers,
                               int n_layers, float* out, const VsLayout& V, hipStream_t stream);
 
 // Calibration -------------------------------------------------------------------
+// State: header, fp64 sums, fp32 moments of the shifted x_S, the shift, and a scratch area
+// where each call stages its shifted x_S rows (bf16, up to kCalibStageRows rows at a time).
 struct CalibLayout {
-  size_t header, sum_S, sum_l, G, YX, total;
+  size_t header, sum_S, sum_l, G, YX, shift, stage, total;
 };
 CalibLayout calib_layout(int d_in, int d_out, int n_layers);
-constexpr uint32_t kCalibMagic = 0x52464331u;   // "RFC1"
+constexpr uint32_t kCalibMagic = 0x52464332u;   // "RFC2"
+constexpr int kCalibStageRows = 16384;
+// Header words (int32 index into the 256-byte header).
+constexpr int kHdrDOut = 2, kHdrLayers = 3, kHdrMagic = 4, kHdrDIn = 5;
+constexpr int kHdrShiftSet = 6;   // 1 once the shift is fixed (by the first call with rows)
+constexpr int kHdrBad = 7;        // 1 once a call's sizes disagreed with the reset's
+constexpr int kHdrDeciding = 8;   // 1 while the current call computes the shift
 
 hipError_t launch_calib_reset(void* state, int d_in, int d_out, int n_layers, hipStream_t stream);
 hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, const uint16_t* xS,
@@ -143,8 +154,10 @@ hipError_t launch_calibrate(void* state, int d_in, int d_out, int n_layers, cons
 
 // Solve ---------------------------------------------------------------------------
 constexpr int kSolveGroup = 4;   // layers per split-map GEMM launch of the solve
+// In a solve workspace: fp64 kappa_F at kSolveInfoOff, then int32 parts.
+constexpr int kSolveInfoOff = 32, kSolveInfoBytes = 12;
 struct SolveLayout {
-  size_t scalars, mu, C, W, M64, Mx, Cx, linv, v, total;
+  size_t scalars, mu, mut, C, W, M64, Mx, Cx, norms, linv, v, total;
   int group;
 };
 SolveLayout solve_layout(int d_in, int d_out, int n_layers);

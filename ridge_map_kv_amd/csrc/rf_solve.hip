@@ -6,6 +6,8 @@
 //
 // Per call (one lambda):
 //   means    mu = sums / n                                              fp64
+//            (the state holds the moments of x'_S = x_S - s, s the calibration's shift;
+//            mu_S below is the mean of x'_S, the centring being invariant to the shift)
 //   centre   C = G - n mu_S mu_S^T (G mirrored from its lower triangle);
 //            alpha = lambda tr(C) / d; C += alpha I                      fp64
 //   Cholesky blocked, 64-wide blocks: diagonal block factor + its inverse, block
@@ -22,7 +24,8 @@
 //            [C_hi | C_hi | C_lo] (d x 3d) times [M_hi | M_lo | M_hi]^T (M symmetric),
 //            fp32 accumulation, on the fill's 256 x 256 tile pipeline.  Layers go in
 //            groups sized by the workspace.
-//   offsets  b_l = mu_l - A_l mu_S = mu_l - YX_l v + n mu_l (v . mu_S)      fp64 accumulate
+//   offsets  b_l = mu_l - A_l (mu_S + s) = mu_l - YX_l v + n mu_l (v . mu_S), with
+//            v = M (mu_S + s)                                           fp64 accumulate
 // Every launch is on the caller's stream; nothing is synchronised.
 #include "rf_common.h"
 #include "rf_gemm_tile.h"
@@ -36,6 +39,8 @@ namespace {
 constexpr int NB = 64;        // Cholesky / substitution block
 constexpr int kCholPanel = 4; // 64-blocks per Cholesky panel: one trailing update per panel
 constexpr int LDT = NB + 1;   // padded LDS row (fp64)
+constexpr int kSplitMax = 6;  // bf16 parts per operand row of the map GEMM (3 or 6 used)
+constexpr int kNormParts = 1024;   // partial sums of |C + alpha I|_F^2
 }  // namespace
 
 SolveLayout solve_layout(int d_in, int d_out, int n_layers) {
@@ -43,35 +48,54 @@ SolveLayout solve_layout(int d_in, int d_out, int n_layers) {
   const size_t dd = (size_t)d_in * d_in;
   L.scalars = 0;
   L.mu = 256;
-  L.v = L.mu + align256(((size_t)d_in + (size_t)n_layers * d_out) * 8);
+  L.mut = L.mu + align256(((size_t)d_in + (size_t)n_layers * d_out) * 8);
+  L.v = L.mut + align256((size_t)d_in * 8);
   L.linv = L.v + align256((size_t)d_in * 8);
   L.C = L.linv + align256((size_t)(d_in / NB) * NB * NB * 8);
   L.W = L.C + align256(dd * 8);
   L.M64 = L.W + align256(dd * 8);
   L.Mx = L.M64 + align256(dd * 8);
   L.group = n_layers < kSolveGroup ? n_layers : kSolveGroup;
-  L.Cx = L.Mx + align256(dd * 6);
-  L.total = L.Cx + align256((size_t)L.group * d_out * d_in * 6);
+  L.Cx = L.Mx + align256(dd * 2 * kSplitMax);
+  L.norms = L.Cx + align256((size_t)L.group * d_out * d_in * 2 * kSplitMax);
+  const int nbk = d_in / NB;
+  L.total = L.norms + align256(((size_t)kNormParts + (size_t)nbk * (nbk + 1) / 2) * 8);
   return L;
 }
 
 namespace {
 
-// scalars block: [0] status word (unsigned), then doubles at byte offsets below
-constexpr int kAlphaOff = 8, kNOff = 16, kVMuOff = 24;
+// scalars block: [0] status word (unsigned), then doubles at byte offsets below, and the
+// int32 number of bf16 parts the map GEMM uses
+constexpr int kAlphaOff = 8, kNOff = 16, kVMuOff = 24, kKappaOff = kSolveInfoOff,
+              kPartsOff = kSolveInfoOff + 8;
 
 __device__ __forceinline__ double* scal(unsigned char* s, int off) {
   return reinterpret_cast<double*>(s + off);
 }
 
 // mu = sums / n for mu_S [d_in] and every mu_l [d_out] (count = d_in + n_layers d_out).
-__global__ void means_kernel(const unsigned char* state, int count, size_t sum_off, double* mu,
-                             unsigned char* scalars) {
+// The sums of x_S are those of the shifted rows x_S - s: mu[0 .. d_in) is the shifted mean
+// (all the centring needs), mut = mu + s the true mean of x_S (the offsets need it).  A
+// state whose header disagrees with the call's sizes, or that a calibrate call marked,
+// sets the state bit of the status.
+__global__ void means_kernel(const unsigned char* state, int count, size_t sum_off,
+                             size_t shift_off, int d_in, int d_out, int n_layers, double* mu,
+                             double* mut, unsigned char* scalars) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const double n = (double)*reinterpret_cast<const int64_t*>(state);
   const double* sums = reinterpret_cast<const double*>(state + sum_off);
-  if (i < count) mu[i] = n > 0 ? sums[i] / n : 0.0;
-  if (i == 0) *scal(scalars, kNOff) = n;
+  const float* shift = reinterpret_cast<const float*>(state + shift_off);
+  const double m = i < count && n > 0 ? sums[i] / n : 0.0;
+  if (i < count) mu[i] = m;
+  if (i < d_in) mut[i] = m + (double)shift[i];
+  if (i == 0) {
+    *scal(scalars, kNOff) = n;
+    const int32_t* h = reinterpret_cast<const int32_t*>(state);
+    if (reinterpret_cast<const uint32_t*>(state)[kHdrMagic] != kCalibMagic || h[kHdrDIn] != d_in ||
+        h[kHdrDOut] != d_out || h[kHdrLayers] != n_layers || h[kHdrBad] != 0)
+      atomicOr(reinterpret_cast<unsigned*>(scalars), kStatusStateBit);
+  }
 }
 
 // C[r][c] = G[max][min] - n mu_r mu_c (full symmetric, fp64).
@@ -104,6 +128,66 @@ __global__ __launch_bounds__(1024) void alpha_kernel(double* C, int d, double la
   const double alpha = lambda * part[0] / d;
   for (int i = t; i < d; i += 1024) C[(size_t)i * d + i] += alpha;
   if (t == 0) *scal(scalars, kAlphaOff) = alpha;
+}
+
+// Fixed-order sum of 256 per-thread values of a block (tree in LDS); valid in thread 0.
+__device__ __forceinline__ double block_sum256(double v, double* red) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  return red[0];
+}
+
+// |C + alpha I|_F^2 from its lower triangle (entries below the diagonal twice), as
+// kNormParts partial sums: block b takes rows b, b + kNormParts, ...
+__global__ __launch_bounds__(256) void cnorm_kernel(const double* C, int d, double* part) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int r = blockIdx.x; r < d; r += gridDim.x)
+    for (int c = threadIdx.x; c <= r; c += 256) {
+      const double v = C[(size_t)r * d + c];
+      s += (c == r ? 1.0 : 2.0) * v * v;
+    }
+  const double tot = block_sum256(s, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+// kappa_F = |C + alpha I|_F |M|_F from the partial sums (fixed order), and the number of
+// bf16 parts per operand of the map product: with two parts (hi + lo, three products) the
+// relative error of A grows about as 5e-6 kappa_F / d, with three parts (hi + mid + lo,
+// six products) about as 1e-7 kappa_F / d (measured on rotated spectra spread over up to
+// six decades).  Three parts are taken once two would pass about 1e-4.
+constexpr double kSplit6Kappa = 16.0;
+__global__ __launch_bounds__(1024) void kappa_kernel(const double* cpart, const double* mpart,
+                                                     int nm, int d, unsigned char* scalars) {
+  __shared__ double red[1024];
+  const int t = threadIdx.x;
+  double s = t < kNormParts ? cpart[t] : 0.0;
+  red[t] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  const double cn = red[0];
+  __syncthreads();
+  double m = 0.0;
+  for (int i = t; i < nm; i += 1024) m += mpart[i];
+  red[t] = m;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) {
+    const double kap = sqrt(cn) * sqrt(red[0]);
+    *scal(scalars, kKappaOff) = kap;
+    *reinterpret_cast<int*>(scalars + kPartsOff) = kap > kSplit6Kappa * d ? 6 : 3;
+  }
 }
 
 // ---------------------------------------------------------------- 64x64 fp64 tiles
@@ -503,16 +587,24 @@ __global__ void zero_kernel(double* W, size_t n) {
 }
 
 // M = U U^T for lower tiles (ab >= bb), mirrored: M[a][b] = sum_k U[a][k] U[b][k], k >= ab.
-// bf16 parts of an fp64 value: hi = bf16(x), lo = bf16(x - hi); |x - hi - lo| <= ~2^-17 |x|.
-__device__ __forceinline__ void split_bf16(double x, uint16_t& hi, uint16_t& lo) {
+// bf16 parts of an fp64 value: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid);
+// |x - hi - mid| <= ~2^-17 |x| and |x - hi - mid - lo| <= ~2^-25 |x|.
+__device__ __forceinline__ void split_bf16(double x, uint16_t& hi, uint16_t& mid) {
   hi = f32_to_bf16((float)x);
-  lo = f32_to_bf16((float)(x - (double)bf16_to_f32(hi)));
+  mid = f32_to_bf16((float)(x - (double)bf16_to_f32(hi)));
+}
+__device__ __forceinline__ void split3_bf16(double x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  split_bf16(x, hi, mid);
+  lo = f32_to_bf16((float)(x - (double)bf16_to_f32(hi) - (double)bf16_to_f32(mid)));
 }
 
 // M = U U^T (= W^T W with W = L^-1) for one lower tile pair, written to both triangles in
-// fp64 and as the GEMM operand Mx [d][3d] = [M_hi | M_lo | M_hi] (bf16).
+// fp64 and as the first three parts of the GEMM operand Mx [d][6d] = [M_hi | M_mid | M_hi |
+// M_lo | M_hi | M_mid] (bf16; the last three only when the product takes six parts,
+// mx_more_kernel).  mpart[e]: the tile's share of |M|_F^2.
 constexpr int kWk = 32, kWld = kWk + 2;     // reduction slice; padded LDS rows (16-byte aligned)
-__global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double* M64, uint16_t* Mx) {
+__global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double* M64, uint16_t* Mx,
+                                                  double* mpart) {
   __shared__ __attribute__((aligned(16))) double wa[2][NB * kWld];
   __shared__ __attribute__((aligned(16))) double wb[2][NB * kWld];
   const int e = blockIdx.x;
@@ -577,7 +669,8 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double
 #pragma unroll
       for (int j = 0; j < 4; ++j) t[acc_row(bi, j) * kT + acc_col(bj)] = acc.v[bi][bj][j];
   __syncthreads();
-  const size_t d3 = (size_t)3 * d;
+  const size_t d6 = (size_t)kSplitMax * d;
+  double sq = 0.0;
   for (int e = tid; e < NB * NB; e += blockDim.x) {
     const int r = e >> 6, c = e & 63;
     for (int side = 0; side < (ab == bb ? 1 : 2); ++side) {
@@ -586,15 +679,35 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double
       if (side == 1) v = t[c * kT + r];                       // the mirror image
       else if (ab == bb && r < c) v = t[c * kT + r];          // a diagonal tile's lower triangle
       else v = t[r * kT + c];
+      sq += v * v;
       const size_t a = (size_t)rt * NB + r, b = (size_t)ct * NB + c;
       M64[a * d + b] = v;
-      uint16_t hi, lo;
-      split_bf16(v, hi, lo);
-      Mx[a * d3 + b] = hi;
-      Mx[a * d3 + d + b] = lo;
-      Mx[a * d3 + 2 * d + b] = hi;
+      uint16_t hi, mid;
+      split_bf16(v, hi, mid);
+      Mx[a * d6 + b] = hi;
+      Mx[a * d6 + d + b] = mid;
+      Mx[a * d6 + 2 * d + b] = hi;
     }
   }
+  __shared__ double red[256];
+  const double tot = block_sum256(sq, red);
+  if (tid == 0) mpart[e] = tot;
+}
+
+// The last three parts of Mx, [M_lo | M_hi | M_mid], when the product takes six.
+__global__ __launch_bounds__(256) void mx_more_kernel(const double* M64, int d,
+                                                      const unsigned char* scalars, uint16_t* Mx) {
+  if (*reinterpret_cast<const int*>(scalars + kPartsOff) != 6) return;
+  const size_t d6 = (size_t)kSplitMax * d;
+  for (int a = blockIdx.x; a < d; a += gridDim.x)
+    for (int b = threadIdx.x; b < d; b += 256) {
+      uint16_t hi, mid, lo;
+      split3_bf16(M64[(size_t)a * d + b], hi, mid, lo);
+      uint16_t* row = Mx + (size_t)a * d6;
+      row[3 * d + b] = lo;
+      row[4 * d + b] = hi;
+      row[5 * d + b] = mid;
+    }
 }
 
 // v = M mu_S (one wave per row, fixed-order reduction); then v . mu_S.
@@ -646,12 +759,15 @@ __global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double
 }
 
 // ---------------------------------------------------------------- split bf16 map GEMM
-// Cx[g][o] = [C_hi | C_hi | C_lo] of row o of C_l = YX_l - n mu_l mu_S^T (l = l0 + g;
-// o < d_out, columns k < d_in), the centring in fp64.  One row per blockIdx.y (g d_out + o),
-// four consecutive k per thread.
+// Cx[g][o] = [C_hi | C_hi | C_mid] of row o of C_l = YX_l - n mu_l mu_S^T (l = l0 + g;
+// o < d_out, columns k < d_in), the centring in fp64, followed by [C_hi | C_lo | C_mid]
+// when the product takes six parts: the six products C_hi M_hi, C_hi M_mid, C_mid M_hi,
+// C_hi M_lo, C_lo M_hi and C_mid M_mid.  One row per blockIdx.y (g d_out + o), four
+// consecutive k per thread.
 __global__ void split_c_kernel(const float* YX, const double* mu, const unsigned char* scalars,
                                int d_in, int d_out, int l0, int rows, uint16_t* Cx) {
   const double n = *reinterpret_cast<const double*>(scalars + kNOff);
+  const int parts = *reinterpret_cast<const int*>(scalars + kPartsOff);
   const size_t d = (size_t)d_in;
   for (int row = blockIdx.y; row < rows; row += gridDim.y)
   for (int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4; k < d_in;
@@ -659,31 +775,40 @@ __global__ void split_c_kernel(const float* YX, const double* mu, const unsigned
     const int g = row / d_out, o = row - g * d_out, l = l0 + g;
     const float* src = YX + ((size_t)l * d_out + o) * d_in;
     const double nm = n * mu[(size_t)d_in + (size_t)l * d_out + o];
-    uint16_t* dst = Cx + (size_t)row * (3 * d);
+    uint16_t* dst = Cx + (size_t)row * (kSplitMax * d);
     const f32x4 y = *reinterpret_cast<const f32x4*>(src + k);
-    uint16_t hi[4], lo[4];
+    uint16_t hi[4], mid[4], lo[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split_bf16((double)y[j] - nm * mu[k + j], hi[j], lo[j]);
-    u32x2 h2, l2;
+    for (int j = 0; j < 4; ++j) split3_bf16((double)y[j] - nm * mu[k + j], hi[j], mid[j], lo[j]);
+    u32x2 h2, m2, l2;
     h2.x = hi[0] | (uint32_t)hi[1] << 16;
     h2.y = hi[2] | (uint32_t)hi[3] << 16;
+    m2.x = mid[0] | (uint32_t)mid[1] << 16;
+    m2.y = mid[2] | (uint32_t)mid[3] << 16;
     l2.x = lo[0] | (uint32_t)lo[1] << 16;
     l2.y = lo[2] | (uint32_t)lo[3] << 16;
     *reinterpret_cast<u32x2*>(dst + k) = h2;
     *reinterpret_cast<u32x2*>(dst + d + k) = h2;
-    *reinterpret_cast<u32x2*>(dst + 2 * d + k) = l2;
+    *reinterpret_cast<u32x2*>(dst + 2 * d + k) = m2;
+    if (parts == 6) {
+      *reinterpret_cast<u32x2*>(dst + 3 * d + k) = h2;
+      *reinterpret_cast<u32x2*>(dst + 4 * d + k) = l2;
+      *reinterpret_cast<u32x2*>(dst + 5 * d + k) = m2;
+    }
   }
 }
 
 struct SolveGemmArgs {
-  const uint16_t* Cx;       // [G][d_out][3 d_in]
-  const uint16_t* Mx;       // [d_in][3 d_in]
+  const uint16_t* Cx;       // [G][d_out][6 d_in]
+  const uint16_t* Mx;       // [d_in][6 d_in]
+  const unsigned char* scalars;   // the number of parts in use (3 or 6)
   float* A_out;             // [n_layers][d_out][d_in] or null
   uint16_t* A_bf16;         // [n_layers][d_out][d_in] or null
   int d_in, d_out, l0, nt_in, nt_out;
 };
 
-// A_l[o][i] for one 256 x 256 tile: F = rows o of Cx, T = rows i of Mx, K = 3 d_in.  In the
+// A_l[o][i] for one 256 x 256 tile: F = rows o of Cx, T = rows i of Mx, K = 3 d_in or
+// 6 d_in (the parts in use; rows are 6 d_in apart either way).  In the
 // MFMA result each lane holds one i and runs of four o, so for each o a half-wave writes
 // 32 consecutive i.
 __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a) {
@@ -697,7 +822,8 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
   const int left = a.nt_out - fg * 4, gsz = left < 4 ? left : 4;
   const int it = within / gsz, ot = fg * 4 + (within - it * gsz);
   const int o0 = ot * kTile, i0 = it * kTile;
-  const size_t d3 = (size_t)3 * a.d_in;
+  const size_t d3 = (size_t)kSplitMax * a.d_in;
+  const int parts = *reinterpret_cast<const int*>(a.scalars + kPartsOff);
   const int tid = threadIdx.x;
   DmaOperand Fo, To;
   {
@@ -713,7 +839,7 @@ __global__ __launch_bounds__(kThreads, 1) void solve_gemm_kernel(SolveGemmArgs a
     }
   }
   f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, 3 * a.d_in, smem);
+  gemm_pipeline(acc, Fo, To, parts * a.d_in, smem);
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
   const int l = a.l0 + g;
@@ -782,6 +908,7 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
   unsigned char* w = static_cast<unsigned char*>(ws);
   unsigned* status = reinterpret_cast<unsigned*>(w);
   double* mu = reinterpret_cast<double*>(w + L.mu);
+  double* mut = reinterpret_cast<double*>(w + L.mut);
   double* v = reinterpret_cast<double*>(w + L.v);
   double* linv = reinterpret_cast<double*>(w + L.linv);
   double* C = reinterpret_cast<double*>(w + L.C);
@@ -797,14 +924,22 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
   if (e != hipSuccess) return e;
   const int nmu = d_in + n_layers * d_out;
   hipLaunchKernelGGL(means_kernel, dim3((nmu + 255) / 256), dim3(256), 0, stream, st, nmu,
-                     CL.sum_S, mu, w);
+                     CL.sum_S, CL.shift, d_in, d_out, n_layers, mu, mut, w);
   hipLaunchKernelGGL(centre_kernel, dim3((d + 255) / 256, d < 65535 ? d : 65535), dim3(256), 0,
                      stream, G, mu, w, d, C);
   hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1024), 0, stream, C, d, lambda, w);
+  double* cpart = reinterpret_cast<double*>(w + L.norms);
+  double* mpart = cpart + kNormParts;
+  hipLaunchKernelGGL(cnorm_kernel, dim3(kNormParts), dim3(256), 0, stream, C, d, cpart);
   // L and U = L^-T together, then M = U U^T
   if ((e = launch_cholesky(C, d, linv, status, stream, 1, 0, 0, W)) != hipSuccess) return e;
-  hipLaunchKernelGGL(wtw_kernel, dim3(nbk * (nbk + 1) / 2), dim3(256), 0, stream, W, d, M64, Mx);
-  hipLaunchKernelGGL(mv_kernel, dim3((d + 3) / 4), dim3(256), 0, stream, M64, mu, d, v);
+  const int ntri = nbk * (nbk + 1) / 2;
+  hipLaunchKernelGGL(wtw_kernel, dim3(ntri), dim3(256), 0, stream, W, d, M64, Mx, mpart);
+  hipLaunchKernelGGL(kappa_kernel, dim3(1), dim3(1024), 0, stream, cpart, mpart, ntri, d, w);
+  hipLaunchKernelGGL(mx_more_kernel, dim3(d < 4096 ? d : 4096), dim3(256), 0, stream, M64, d, w,
+                     Mx);
+  // v = M (mu' + s) with the true mean; v . mu' with the shifted one (the centring's)
+  hipLaunchKernelGGL(mv_kernel, dim3((d + 3) / 4), dim3(256), 0, stream, M64, mut, d, v);
   hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, stream, v, mu, d, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -813,7 +948,7 @@ hipError_t launch_solve(const void* state, int d_in, int d_out, int n_layers, do
     const int rows = G * d_out;
     hipLaunchKernelGGL(split_c_kernel, dim3((d_in + 1023) / 1024, rows < 65535 ? rows : 65535),
                        dim3(256), 0, stream, YX, mu, w, d_in, d_out, l0, rows, Cx);
-    SolveGemmArgs a = {Cx, Mx, A_out, A_bf16, d_in, d_out, l0, d_in / kTile, d_out / kTile};
+    SolveGemmArgs a = {Cx, Mx, w, A_out, A_bf16, d_in, d_out, l0, d_in / kTile, d_out / kTile};
     ProfileScope ps(RF_KERNEL_SOLVE_MAP, stream);
     hipLaunchKernelGGL(solve_gemm_kernel, dim3(G * a.nt_out * a.nt_in), dim3(kThreads), 0, stream,
                        a);

@@ -188,10 +188,10 @@ rf_status prepare_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, in
       lp[i] = {reinterpret_cast<const uint16_t*>(f + F.R), reinterpret_cast<const float*>(f + F.r),
                nullptr, P, P + (size_t)p.kv * d_in, l.k_pages, l.v_pages, l.k_norm_w, l.v_scale,
                nullptr, nullptr, reinterpret_cast<const float*>(f + F.c),
-               reinterpret_cast<const float*>(f + F.kappa)};
+               reinterpret_cast<const float*>(f + F.kappa), reinterpret_cast<const float*>(f + F.g)};
     } else {
       lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.k_pages, l.v_pages,
-               l.k_norm_w, l.v_scale, l.A_q, l.A_scale, nullptr, nullptr};
+               l.k_norm_w, l.v_scale, l.A_q, l.A_scale, nullptr, nullptr, nullptr};
     }
   }
   return RF_OK;
@@ -448,10 +448,10 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
       lp[i] = {reinterpret_cast<const uint16_t*>(f + F.R), reinterpret_cast<const float*>(f + F.r),
                l.norm_w, P, P + (size_t)p.kv * d_in, nullptr, nullptr, nullptr, nullptr, nullptr,
                nullptr, reinterpret_cast<const float*>(f + F.c),
-               reinterpret_cast<const float*>(f + F.kappa)};
+               reinterpret_cast<const float*>(f + F.kappa), reinterpret_cast<const float*>(f + F.g)};
     } else {
       lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, nullptr, nullptr, nullptr, nullptr, l.A_q,
-               l.A_scale, nullptr, nullptr};
+               l.A_scale, nullptr, nullptr, nullptr};
     }
   }
   hipError_t e = rf::launch_value_scale(p, lp.data(), x_l_tail, wv.data(), n_layers,
@@ -571,9 +571,28 @@ rf_status ridgefill_read_status(void* ws, void* stream) {
   unsigned word = 0;
   e = hipMemcpy(&word, ws, sizeof word, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "status read");
+  if (word & rf::kStatusStateBit)     // first: a mismatched state explains any pivot failure
+    return fail(RF_E_WORKSPACE, "calibration state does not match the sizes it was reset with");
   if (word & rf::kStatusRowsBit) return fail(RF_E_ROWS, "device flagged filled-row indices");
   if (word & rf::kStatusNotSpdBit) return fail(RF_E_NOT_SPD, "device flagged a non-positive pivot");
   if (word & rf::kStatusScoreBit) return fail(RF_E_INVALID, "device flagged a NaN selection score");
+  return ok();
+}
+
+rf_status ridgefill_solve_info(void* ws, double* kappa_f, int32_t* parts, void* stream) {
+  if (!ws) return fail(RF_E_INVALID, "workspace is NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  unsigned char buf[rf::kSolveInfoBytes];
+  e = hipMemcpy(buf, static_cast<unsigned char*>(ws) + rf::kSolveInfoOff, sizeof buf,
+                hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "solve info read");
+  double k;
+  int32_t p;
+  std::memcpy(&k, buf, sizeof k);
+  std::memcpy(&p, buf + 8, sizeof p);
+  if (kappa_f) *kappa_f = k;
+  if (parts) *parts = p;
   return ok();
 }
 

@@ -45,6 +45,7 @@ def rng(seed: int, *tags: int) -> np.random.Generator:
 # Stream tags, so every tensor has its own stream.
 TAG_XS, TAG_EXACT, TAG_TABLE, TAG_NORM, TAG_WK, TAG_WV, TAG_MAPU, TAG_MAPV, TAG_MAPB, \
     TAG_CAL_X, TAG_CAL_NOISE, TAG_CAL_C, TAG_KNORM, TAG_VSCALE, TAG_SCORES = range(1, 16)
+TAG_SPREAD, TAG_HARD = 16, 17
 
 
 def exact_rows(cfg) -> np.ndarray:
@@ -295,3 +296,49 @@ def row_scores(P: int, seed: int) -> np.ndarray:
     s = rng(seed, TAG_SCORES).exponential(1.0, P)
     return (np.round(s * 64.0) / 64.0).astype(np.float32)
 
+
+
+# --------------------------------------------------------------------- harder inputs
+# Inputs that stress the numerics rather than stand in for the timing workloads: feature
+# magnitudes far apart, feature means far larger than the spread, spectra spread over
+# several decades.
+
+def spread_map(d: int, seed: int, layer: int, spread: float) -> np.ndarray:
+    """A = (D1 H) diag(s) (H D2) / d (float32 [d, d]): H the Sylvester Hadamard matrix of
+    order d (a power of two), D1, D2 seeded random signs, so the singular values are
+    exactly s, log-spaced from 1 down to 1/spread and scaled to a root-mean-square of 1."""
+    H = sylvester_hadamard(d).astype(np.float32)
+    g = rng(seed, TAG_SPREAD, layer)
+    s = np.logspace(0.0, -np.log10(spread), d).astype(np.float32)
+    s /= np.sqrt(np.mean(s.astype(np.float64) ** 2)).astype(np.float32)
+    d1 = g.choice(np.array([-1.0, 1.0], dtype=np.float32), size=d)
+    d2 = g.choice(np.array([-1.0, 1.0], dtype=np.float32), size=d)
+    left = (d1[:, None] * H) * s[None, :]
+    return ((left @ (H * d2[None, :])) / np.float32(d)).astype(np.float32)
+
+
+def calib_data_hard(d: int, n_layers: int, rows: int, seed: int, *, mean_lo: float = 10.0,
+                    mean_hi: float = 50.0, spread: float = 1.0, noise_scale: float = 0.1):
+    """Calibration rows whose statistics are hard to keep in fp32 or to invert:
+    x_S = z diag(sd) Q^T + m, z ~ N(0,1), Q a seeded orthogonal matrix (when spread > 1),
+    sd log-spaced so that the covariance's eigenvalues span `spread`, and on a seeded half
+    of the features a mean m of magnitude U[mean_lo, mean_hi] times the unit spread with a
+    random sign; x_l = W_true,l x_S + c_l + noise_scale e with c_l of the same magnitudes
+    on a seeded half of the outputs.  float32 x_S [rows, d], x_l [n_layers, rows, d]."""
+    g = rng(seed, TAG_HARD)
+    z = g.standard_normal((rows, d))
+    if spread > 1.0:
+        sd = np.logspace(0.0, 0.5 * np.log10(spread), d)
+        Q, _ = np.linalg.qr(g.standard_normal((d, d)))
+        z = (z * sd[None, :]) @ Q.T
+    m = np.where(g.random(d) < 0.5, g.uniform(mean_lo, mean_hi, d) * g.choice([-1.0, 1.0], d), 0.0)
+    xS = (z + m[None, :]).astype(np.float32)
+    xl = np.empty((n_layers, rows, d), dtype=np.float32)
+    for l in range(n_layers):
+        U, V = true_map_factors(d, seed, l)
+        gl = rng(seed, TAG_HARD, 1 + l)
+        c = np.where(gl.random(d) < 0.5, gl.uniform(mean_lo, mean_hi, d) * gl.choice([-1.0, 1.0], d),
+                     gl.standard_normal(d))
+        e = gl.standard_normal((rows, d))
+        xl[l] = xS + TRUE_MAP_GAIN * ((xS @ V) @ U.T) + c[None, :].astype(np.float32) + noise_scale * e
+    return xS, xl

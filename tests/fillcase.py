@@ -121,14 +121,15 @@ def host_maps(layers: list[dict]) -> list[dict]:
 
 
 def fold_offsets(case: Case):
-    """Byte offsets of P, R, c, r and kappa in one layer's folded buffer: the sections in
-    that order, each starting on a 256-byte boundary."""
+    """Byte offsets of P, R1, c, r1, g and kappa in one layer's folded buffer: the sections
+    in that order, each starting on a 256-byte boundary."""
     a = lambda x: (x + 255) // 256 * 256
     kv2, din = 2 * case.kv, case.width
     R = a(kv2 * din * 2)
     c = R + a(din * din * 2)
     r = c + a(kv2 * 4)
-    return 0, R, c, r, r + a(din * 4)
+    g = r + a(din * 4)
+    return 0, R, c, r, g, g + a(din * 4)
 
 
 def fold_layers(case: Case, inp, stream=None, layers_at_once=None):
@@ -147,18 +148,27 @@ def fold_layers(case: Case, inp, stream=None, layers_at_once=None):
     return bufs, status
 
 
-def fold_views(case: Case, buf: torch.Tensor):
-    """(P, R, c, r, kappa) of a folded buffer, as float64 numpy values."""
-    oP, oR, oc, orr, ok = fold_offsets(case)
+def fold_raw(case: Case, buf: torch.Tensor):
+    """(P, R1, c, r1, g, kappa) of a folded buffer as stored, float64 numpy values."""
+    oP, oR, oc, orr, og, ok = fold_offsets(case)
     kv2, din = 2 * case.kv, case.width
     b = buf.cpu()
     P = b[oP:oP + kv2 * din * 2].view(torch.bfloat16).float().numpy().reshape(kv2, din)
-    R = b[oR:oR + din * din * 2].view(torch.bfloat16).float().numpy().reshape(din, din)
+    R1 = b[oR:oR + din * din * 2].view(torch.bfloat16).float().numpy().reshape(din, din)
     c = b[oc:oc + kv2 * 4].view(torch.float32).numpy()
-    r = b[orr:orr + din * 4].view(torch.float32).numpy()
+    r1 = b[orr:orr + din * 4].view(torch.float32).numpy()
+    g = b[og:og + din * 4].view(torch.float32).numpy()
     kappa = float(b[ok:ok + 4].view(torch.float32).item())
-    return (P.astype(np.float64), R.astype(np.float64), c.astype(np.float64),
-            r.astype(np.float64), kappa)
+    return (P.astype(np.float64), R1.astype(np.float64), c.astype(np.float64),
+            r1.astype(np.float64), g.astype(np.float64), kappa)
+
+
+def fold_views(case: Case, buf: torch.Tensor):
+    """(P, R, c, r, kappa) of a folded buffer, as float64 numpy values, with R = diag(g) R1
+    and r = g r1 (the buffer holds R's rows over their diagonal entries, and the diagonal
+    apart)."""
+    P, R1, c, r1, g, kappa = fold_raw(case, buf)
+    return P, R1 * g[:, None], c, r1 * g, kappa
 
 
 def folded_layer_dicts(inp):

@@ -33,6 +33,10 @@ class GpuStats:
         self.s_l = raw[off:off + 8 * d * L].view(np.float64).reshape(L, d).copy(); off += 8 * d * L
         self.G = raw[off:off + 4 * d * d].view(np.float32).reshape(d, d).astype(np.float64); off += 4 * d * d
         self.YX = raw[off:off + 4 * d * d * L].view(np.float32).reshape(L, d, d).astype(np.float64)
+        off += 4 * d * d * L
+        self.shift = raw[off:off + 4 * d].view(np.float32).astype(np.float64)
+        self.shift_fixed = int(raw[24:28].view(np.int32)[0])
+        self.bad = int(raw[28:32].view(np.int32)[0])
 
 
 def run_calib(xS_chunks, xl_chunks, d, L):
@@ -124,6 +128,7 @@ def test_reset_clears_state():
     B.ridgefill_calib_reset(state, d, L)
     g = GpuStats(state, d, L)
     assert g.n == 0 and not g.G.any() and not g.YX.any() and not g.s_S.any()
+    assert not g.shift.any() and g.shift_fixed == 0 and g.bad == 0
 
 
 def test_calib_argument_errors():

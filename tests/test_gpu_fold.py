@@ -1,9 +1,12 @@
 """GPU parity of folded layers, through the C ABI.
 
 ridgefill_fold_maps against the oracle's fold_map on the same bf16/fp32 values:
-  P (one bf16 rounding of a product held to ~2^-17) and R (bf16 of an fp64 Cholesky
-  factor of an fp32-accumulated A^T A): relative Frobenius error <= 2e-3 (a bf16
-  rounding's own error is about 1.1e-3 rms); R's strict lower triangle exactly zero;
+  P (one bf16 rounding of a product held to ~2^-17) and R = diag(g) R1 (R1: bf16 of the
+  rows of an fp64 Cholesky factor of an fp32-accumulated A^T A over their diagonal
+  entries, g that diagonal in fp32): relative Frobenius error <= 2e-3 (a bf16 rounding's
+  own error is about 1.1e-3 rms; the fold factors A^T A with its diagonal lifted by a
+  relative 2^-16, far below that); R's strict lower triangle exactly zero, R1's diagonal
+  exactly one;
   c (fp64 accumulation, fp32 result): 1e-6; r (fp64 substitution on the fp32-accumulated
   Gram): 1e-4; kappa within 1e-4 |b|^2.
 The fill of folded layers against the oracle's plain fill_rows (the method's own flow),
@@ -18,7 +21,7 @@ import oracle
 from ridge_map_kv_amd import binding as B
 
 from fillcase import (Case, bf16_np, build_inputs, check_routing, check_values, fold_layers,
-                      fold_views, folded_layer_dicts, make_shape, rel_fro, run_fill, to_bf16)
+                      fold_raw, fold_views, folded_layer_dicts, make_shape, rel_fro, run_fill, to_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,9 +68,13 @@ def test_fold_outputs_vs_oracle(d, nl, nkv, hd, seed, opts):
               f"(oracle {ko:.3e})", flush=True)
         assert eP <= 2e-3 and eR <= 2e-3 and ec <= 1e-6 and er <= 1e-4
         assert np.all(np.tril(R, -1) == 0.0)
+        assert np.all(np.diag(fold_raw(case, bufs[l])[1]) == 1.0)   # unit diagonal, exact
         assert abs(kappa - ko) <= 1e-4 * (b @ b)
         if opts.get("map_kind") == "identity":
-            assert np.array_equal(R, np.eye(case.width))          # Cholesky of I is exact
+            # the Cholesky of I (its diagonal lifted by the relative 2^-16) is exact
+            _, R1, _, _, g, _ = fold_raw(case, bufs[l])
+            assert np.array_equal(R1, np.eye(case.width))
+            assert np.all(g == np.float32(np.sqrt(1.0 + 2.0 ** -16)))
             assert kappa == 0.0
 
 
@@ -138,10 +145,10 @@ def test_fold_group_size_does_not_change_the_buffers():
     three, st3 = fold_layers(case, inp, layers_at_once=3)   # groups of 3 and 1
     assert st3 == B.RF_OK
     for l in range(case.n_layers):
-        ref = fold_views(case, one[l])         # the fields; padding between them is unset
+        ref = fold_raw(case, one[l])           # the fields; padding between them is unset
         for other, tag in ((four[l], "4"), (three[l], "3")):
-            got = fold_views(case, other)
-            for name, x, y in zip(("P", "R", "c", "r", "kappa"), ref, got):
+            got = fold_raw(case, other)
+            for name, x, y in zip(("P", "R1", "c", "r1", "g", "kappa"), ref, got):
                 assert np.array_equal(np.asarray(x), np.asarray(y)), \
                     f"layer {l} {name}: 1 vs {tag} at once"
 

@@ -4,12 +4,14 @@
 Fill (8B, Qwen3-8B and 27B shapes): routing is checked bit-exactly on every byte of every
 layer's K and V pools (sentinel-filled before the call); K and V are checked against the
 oracle on 512 seeded filled rows of every layer (first and last filled row, rows next to
-exact rows, rows on page edges, the rest uniform).
+exact rows, rows on page edges, the rest uniform), and on every filled row of the first
+and the last upper layer.
 
-Calibration (8B shape, 131,072 rows in 16,384-row chunks): 32 seeded columns of the
-Gram matrix, 32 seeded rows of every Y_l^T X and the matching sums against the oracle's
-float64 accumulation of the same bf16 rows.  Solve at full size: a Hadamard design whose
-answer is known in closed form."""
+Calibration (8B shape, 131,072 rows in 16,384-row chunks): 256 seeded columns of the
+Gram matrix, 256 seeded rows of every Y_l^T X and the matching sums against the oracle's
+float64 accumulation of the same bf16 rows.  Solve at full size: the oracle's float64
+solve of the statistics the GPU accumulated, for every layer at all six lambdas, with the
+normal-equation residual; and a Hadamard design whose answer is known in closed form."""
 
 import numpy as np
 import pytest
@@ -29,6 +31,32 @@ def _np64(t):
 
 def _rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _all_rows_layer(cfg, inp, filled, pg, sl, l, A_of=None, kn_of=None, block=4096):
+    """Relative Frobenius errors of K and V over every filled row of layer l against the
+    oracle's plain fill, accumulated over blocks of rows (the oracle is row-wise)."""
+    dev = inp["xS"].device
+    lay = inp["layers"][l]
+    A = A_of(l) if A_of else _np64(lay["A"])
+    b = lay["b"].cpu().numpy().astype(np.float64)
+    w, WK, WV = _np64(lay["norm_w"]), _np64(lay["W_K"]), _np64(lay["W_V"])
+    kn = kn_of(l) if kn_of else None
+    num = np.zeros(2)
+    den = np.zeros(2)
+    for r0 in range(0, filled.size, block):
+        rows = filled[r0:r0 + block]
+        xs = _np64(inp["xS"][torch.from_numpy(rows).to(dev)])
+        Ko, Vo = oracle.fill_rows(xs, rows, A, b, w, WK, WV, eps=cfg.rms_eps,
+                                  theta=cfg.rope_theta, n_kv=cfg.n_kv, hd=cfg.head_dim,
+                                  k_norm_w=kn)
+        tpg = torch.from_numpy(pg[r0:r0 + block]).to(dev)
+        tsl = torch.from_numpy(sl[r0:r0 + block]).to(dev)
+        for j, (key, want) in enumerate((("k_pages", Ko), ("v_pages", Vo))):
+            got = _np64(lay[key][tpg, tsl])
+            num[j] += np.sum((got - want) ** 2)
+            den[j] += np.sum(want ** 2)
+    return float(np.sqrt(num[0] / den[0])), float(np.sqrt(num[1] / den[1]))
 
 
 def _sample_rows(filled, exact, page_size, n=512, seed=7):
@@ -96,6 +124,11 @@ def test_full_size_fill(name):
         assert ek <= TOL and ev <= TOL, f"layer {l}: K {ek:.3e} V {ev:.3e}"
     print(f"full fill {name}: {rows.size} rows x {cfg.n_upper} layers, worst rel {worst:.2e}",
           flush=True)
+    for l in (0, cfg.n_upper - 1):
+        ek, ev = _all_rows_layer(cfg, inp, filled, pg, sl, l)
+        print(f"full fill {name}: layer {l}, all {filled.size} rows: K {ek:.2e} V {ev:.2e}",
+              flush=True)
+        assert ek <= TOL and ev <= TOL, f"layer {l} all rows: K {ek:.3e} V {ev:.3e}"
 
 
 def _state_arrays(state, d, L):
@@ -105,8 +138,9 @@ def _state_arrays(state, d, L):
     sS = raw[off:off + 8 * d].view(np.float64); off += 8 * d
     sl = raw[off:off + 8 * d * L].view(np.float64).reshape(L, d); off += 8 * d * L
     G = raw[off:off + 4 * d * d].view(np.float32).reshape(d, d); off += 4 * d * d
-    YX = raw[off:off + 4 * d * d * L].view(np.float32).reshape(L, d, d)
-    return n, sS, sl, G, YX
+    YX = raw[off:off + 4 * d * d * L].view(np.float32).reshape(L, d, d); off += 4 * d * d * L
+    shift = raw[off:off + 4 * d].view(np.float32).astype(np.float64)
+    return n, sS, sl, G, YX, shift
 
 
 def test_full_size_calibration_sampled():
@@ -120,13 +154,14 @@ def test_full_size_calibration_sampled():
     for xs, xl in chunks:
         B.ridgefill_calibrate(state, d, L, xs, xl)
     torch.cuda.synchronize()
-    n, sS, sl, G, YX = _state_arrays(state, d, L)
+    n, sS, sl, G, YX, shift = _state_arrays(state, d, L)
     assert n == ccfg.rows
+    assert not shift.any()              # zero-mean rows: the moments are the raw ones
 
     print("full calibration: oracle on sampled entries", flush=True)
     g = np.random.default_rng(11)
-    cols = np.sort(g.choice(d, size=32, replace=False))
-    outs = np.sort(g.choice(d, size=32, replace=False))
+    cols = np.sort(g.choice(d, size=256, replace=False))
+    outs = np.sort(g.choice(d, size=256, replace=False))
     Gc = np.zeros((d, cols.size))
     Yr = np.zeros((L, outs.size, d))
     sS_o = np.zeros(d)
@@ -146,6 +181,63 @@ def test_full_size_calibration_sampled():
     assert _rel(YX[:, outs, :].astype(np.float64), Yr) < 1e-5
     np.testing.assert_allclose(sS, sS_o, rtol=1e-6, atol=1e-2)
     np.testing.assert_allclose(sl[:, outs], sl_o, rtol=1e-6, atol=1e-2)
+
+
+@pytest.fixture(scope="module")
+def calib8b():
+    """The 8B-shaped calibration (131,072 rows in 16,384-row calls) on the GPU, and the
+    statistics it accumulated read back as the oracle's CalibStats in float64."""
+    ccfg = configs.CALIB8B
+    d, L = ccfg.d, ccfg.n_layers
+    dev = torch.device("cuda")
+    print("\nfull solve: calibrating 131,072 rows", flush=True)
+    chunks = synth.device_calib_chunks(ccfg, dev)
+    state = torch.empty(B.ridgefill_calib_state_bytes(d, L), dtype=torch.uint8, device=dev)
+    B.ridgefill_calib_reset(state, d, L)
+    for xs, xl in chunks:
+        B.ridgefill_calibrate(state, d, L, xs, xl)
+    torch.cuda.synchronize()
+    del chunks
+    torch.cuda.empty_cache()
+    n, sS, sl, G, YX, shift = _state_arrays(state, d, L)
+    st = oracle.calib_new(d, L)
+    st.n = n
+    st.s_S = sS.astype(np.float64)
+    st.s_l = sl.astype(np.float64)
+    low = np.tril(G.astype(np.float64))
+    st.G = low + np.tril(low, -1).T
+    st.YX = YX.astype(np.float64)
+    return state, st, shift
+
+
+@pytest.mark.parametrize("lam", [1e-4, 1e-3, 0.01, 0.03, 0.1, 1.0])
+def test_full_size_solve_vs_oracle(calib8b, lam):
+    # the oracle's float64 Cholesky solve of the very statistics the GPU accumulated, for
+    # all 20 layers; the GPU's shift (zero here) enters only b = mu_l - A (mu' + s)
+    state, st, shift = calib8b
+    d, L = st.d, st.n_layers
+    dev = torch.device("cuda")
+    A = torch.empty((L, d, d), dtype=torch.float32, device=dev)
+    b = torch.empty((L, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.ridgefill_solve_workspace_bytes(d, L), dtype=torch.uint8, device=dev)
+    B.ridgefill_solve(state, d, L, lam, A, b, None, ws)
+    assert B.ridgefill_read_status(ws) == B.RF_OK
+    print(f"\nfull solve lambda {lam}: oracle", flush=True)
+    Ao, bo = oracle.solve(st, lam)
+    bo = bo - Ao @ shift
+    _, _, XtX, YtX = oracle.centred_moments(st)
+    Cp = torch.from_numpy(XtX + oracle.ridge_alpha(XtX, lam) * np.eye(d)).to(dev)
+    worst_a = worst_b = worst_r = 0.0
+    for l in range(L):
+        Al = A[l].cpu().numpy().astype(np.float64)
+        ea, eb = _rel(Al, Ao[l]), _rel(b[l].cpu().numpy().astype(np.float64), bo[l])
+        Yt = torch.from_numpy(YtX[l]).to(dev)
+        res = float(torch.linalg.norm(Cp @ A[l].double().T - Yt.T) / torch.linalg.norm(Yt))
+        worst_a, worst_b, worst_r = max(worst_a, ea), max(worst_b, eb), max(worst_r, res)
+        assert ea < TOL and eb < TOL, f"layer {l}: A {ea:.2e} b {eb:.2e}"
+        assert res < 1e-4, f"layer {l}: residual {res:.2e}"
+    print(f"full solve lambda {lam}: {L} layers, worst A {worst_a:.2e} b {worst_b:.2e} "
+          f"residual {worst_r:.2e}", flush=True)
 
 
 def test_full_size_solve_hadamard_closed_form():

@@ -7,7 +7,8 @@ groups of up to 4 layers) and Qwen3-8B (key norm) fills against the plain oracle
 
 Fills: routing bit-exact on every byte of every layer's pools (sentinel-filled), K and V
 against the oracle on 512 sampled rows of every layer (first and last filled row, rows
-next to exact rows, page edges, the rest seeded), relative Frobenius error <= 5e-3.
+next to exact rows, page edges, the rest seeded) and on every filled row of the first
+and last upper layer, relative Frobenius error <= 5e-3.
 Value-rescale factors: relative error <= 2e-3 on four layers.  The int8 codes come from the
 oracle's float32 quantizer; the oracle uses q * scale exactly."""
 
@@ -19,7 +20,7 @@ import oracle
 from ridge_map_kv_amd import binding as B
 from ridge_map_kv_amd import configs, synth
 
-from test_gpu_full import _np64, _rel, _sample_rows
+from test_gpu_full import _all_rows_layer, _np64, _rel, _sample_rows
 
 pytestmark = pytest.mark.gpu
 TOL = 5e-3
@@ -40,6 +41,17 @@ def _routing(cfg, inp, filled):
 
 
 def _values(cfg, inp, filled, exact, pg, sl, A_of=None, kn_of=None):
+    """Sampled rows of every layer, then every filled row of the first and last layer."""
+    n, worst = _values_sampled(cfg, inp, filled, exact, pg, sl, A_of, kn_of)
+    for l in (0, len(inp["layers"]) - 1):
+        ek, ev = _all_rows_layer(cfg, inp, filled, pg, sl, l, A_of, kn_of)
+        print(f"  layer {l}, all {filled.size} filled rows: K {ek:.2e} V {ev:.2e}", flush=True)
+        worst = max(worst, ek, ev)
+        assert ek <= TOL and ev <= TOL, f"layer {l} all rows: K {ek:.3e} V {ev:.3e}"
+    return n, worst
+
+
+def _values_sampled(cfg, inp, filled, exact, pg, sl, A_of=None, kn_of=None):
     dev = inp["xS"].device
     rows = _sample_rows(filled, exact, cfg.page_size)
     xs = _np64(inp["xS"][torch.from_numpy(rows).to(dev)])
@@ -198,12 +210,16 @@ def test_8b_folded_full_size():
         Po, co, Ro, ro, ko = oracle.fold_map(_np64(lay["A"]), lay["b"].cpu().numpy().astype(np.float64),
                                              _np64(lay["norm_w"]), _np64(lay["W_K"]), _np64(lay["W_V"]))
         buf = bufs[l].cpu()
+        og = oc + a(2 * kv * 4) + a(cfg.d * 4)
         P = buf[:2 * kv * cfg.d * 2].view(torch.bfloat16).double().numpy().reshape(2 * kv, cfg.d)
-        R = buf[oR:oR + cfg.d * cfg.d * 2].view(torch.bfloat16).double().numpy().reshape(cfg.d, cfg.d)
+        R1 = buf[oR:oR + cfg.d * cfg.d * 2].view(torch.bfloat16).double().numpy().reshape(cfg.d, cfg.d)
         c = buf[oc:oc + 2 * kv * 4].view(torch.float32).double().numpy()
+        g = buf[og:og + cfg.d * 4].view(torch.float32).double().numpy()
+        R = R1 * g[:, None]                  # R = diag(g) R1, R1 with a unit diagonal
         eP, eR, ec = _rel(P, Po), _rel(R, Ro), _rel(c, co)
         print(f"  P {eP:.2e} R {eR:.2e} c {ec:.2e}", flush=True)
         assert eP <= 2e-3 and eR <= 2e-3 and ec <= 1e-6 and np.all(np.tril(R, -1) == 0.0)
+        assert np.all(np.diag(R1) == 1.0)
     folded = [dict(folded=bufs[l], k_pages=lay["k_pages"], v_pages=lay["v_pages"])
               for l, lay in enumerate(inp["layers"])]
     print("8B folded: fill", flush=True)
