@@ -355,17 +355,28 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a)
 // ---------------------------------------------------------------- full 64-row slices
 // The fill's pipeline (two 64 KB stages, loads straight into LDS one slice ahead, loads
 // and fragment reads between MFMAs), with LDS holding each operand's 64 rows x 256
-// features untransposed: 512 bytes per row, 16-byte chunk c of row r at chunk
-// c ^ ((r & 3) << 1).  The fragments come out transposed through ds_read_b64_tr_b16:
-// within each 16-lane group, lane i receives element i % 4 of the 8-byte pieces named by
-// lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  With lane p of the group naming reduction row
-// (p >> 2) and feature 4 (p & 3), lane i receives feature i at four consecutive rows; two
-// such reads give the eight consecutive reduction indices of a v_mfma_f32_32x32x16_bf16
-// operand.
+// features untransposed: 512 bytes per row.  The fragments come out transposed through
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the
+// 8-byte pieces named by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  With lane p of the group
+// naming reduction row (p >> 2) and feature 4 (p & 3), lane i receives feature i at four
+// consecutive rows; two such reads give the eight consecutive reduction indices of a
+// v_mfma_f32_32x32x16_bf16 operand.
+//
+// Placement of 16-byte chunk c of row r: position t(c) ^ ((r & 3) << 1), where t flips bit 3
+// of c when bit 1 is set.  One read's four 16-lane groups take rows r0 .. r0 + 3 (groups 0,
+// 1) and r0 + 8 .. r0 + 11 (groups 2, 3), groups 0 and 2 chunks c0, c0 + 1, groups 1 and 3
+// chunks c0 + 2, c0 + 3 (c0 a multiple of 4).  The row term spreads a group's four rows
+// over eight chunk positions (32 banks); t moves groups 1 and 3 to the other eight
+// positions of the 256-byte bank window, so each half-wave (groups 0, 1 or 2, 3) reads all
+// 64 banks once.  Without t the four groups met in the same 32 banks: two extra cycles per
+// read.  t is an involution, so position p holds chunk t(p ^ ((r & 3) << 1)).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ int tr_flip(int c) { return c ^ (((c >> 1) & 1) << 3); }
+__device__ __forceinline__ int tr_pos(int c, int r) { return tr_flip(c) ^ ((r & 3) << 1); }
+
 __device__ __forceinline__ int tr_off(int r, int col) {
-  return r * 512 + ((((col >> 3) ^ ((r & 3) << 1)) << 4) | ((col & 7) << 1));
+  return r * 512 + ((tr_pos(col >> 3, r) << 4) | ((col & 7) << 1));
 }
 
 __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* op, int s, int col0, int lane) {
@@ -407,13 +418,13 @@ __device__ __forceinline__ void mfma16_read_tr(f32x16 (&acc)[4][4], const bf16x8
 
 // DMA block j = 4 p + wave (p = 0..7) of an operand stage: rows 2 j, 2 j + 1 (1 KB).  Lane
 // l lands on row 2 j + (l >> 5), chunk position l & 31, which holds logical chunk
-// (l & 31) ^ ((row & 3) << 1).
+// tr_flip((l & 31) ^ ((row & 3) << 1)).
 __device__ __forceinline__ void calib_operand(DmaOperand& o, const uint16_t* x, int d, int col0,
                                               int wave, int lane) {
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r0 = 2 * (4 * p + wave), r = r0 + (lane >> 5);
-    const int c = (lane & 31) ^ ((r & 3) << 1);
+    const int c = tr_flip((lane & 31) ^ ((r & 3) << 1));
     o.base[p] = reinterpret_cast<const unsigned char*>(x + (size_t)r0 * d + col0);
     o.off[p] = (uint32_t)((((lane >> 5) * d) + c * 8) * 2);
   }
