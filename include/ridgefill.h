@@ -212,6 +212,28 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
                                   void* ws, size_t ws_bytes, void* stream, void* copy_stream);
 
 /* ------------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that must not call hipMalloc): the same computation and arguments as
+ * ridgefill_fill with resident maps (plain bf16, int8 or folded layers), without a
+ * workspace argument.  The library's own scratch array serves as the workspace:
+ * RIDGEFILL_NOALLOC_SCRATCH_BYTES of device memory per device, part of the library's code
+ * object (allocated when it is loaded on that device, held until the process ends).  The
+ * call allocates nothing; layers are processed in groups as large as the scratch holds.
+ *   status   device pointer to one uint32 (4-byte aligned) that receives the device status
+ *            word of the call (cleared first); read it with ridgefill_read_status(status).
+ * Returns RF_E_WORKSPACE, before anything is enqueued, when one layer's share of the
+ * workspace (ridgefill_fill_workspace_bytes_ex(shape, n_filled, 1, flags)) exceeds the
+ * scratch.  All calls on one device share its scratch, which keeps the last call's
+ * contents: calls that overlap on one device (two streams, two threads) race and must be
+ * ordered by the caller.  Nothing in the scratch needs to start at zero.
+ * ------------------------------------------------------------------------------ */
+#define RIDGEFILL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rf_status ridgefill_fill_noalloc(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                                 int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                                 const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
+                                 uint32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Folded layers.  Section "Ridge map: predict the input, and the original projection runs
  * unchanged": after x_hat = A x_S + b the layer's RMSNorm weight w and its projections
  * W_K, W_V are linear, so they can be multiplied into the map once per layer; the only

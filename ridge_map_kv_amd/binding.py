@@ -24,6 +24,7 @@ EXPORTED = [
     "ridgefill_fill_workspace_bytes_ex",
     "ridgefill_fill",
     "ridgefill_fill_streamed",
+    "ridgefill_fill_noalloc",
     "ridgefill_value_scale_workspace_bytes",
     "ridgefill_value_scale",
     "ridgefill_quantize_map",
@@ -105,6 +106,8 @@ def lib() -> C.CDLL:
         "ridgefill_fill_streamed": (st, [C.POINTER(rf_shape), vp, i64, i64, i64, vp, i64,
                                          C.POINTER(rf_layer), i32, C.POINTER(rf_paged_kv), vp,
                                          sz, vp, vp]),
+        "ridgefill_fill_noalloc": (st, [C.POINTER(rf_shape), vp, i64, i64, i64, vp, i64,
+                                        C.POINTER(rf_layer), i32, C.POINTER(rf_paged_kv), vp, vp]),
         "ridgefill_value_scale_workspace_bytes": (sz, [C.POINTER(rf_shape), i64, i32, i32]),
         "ridgefill_value_scale": (st, [C.POINTER(rf_shape), vp, i64, C.POINTER(vp), i64,
                                        C.POINTER(rf_layer), i32, vp, vp, sz, vp]),
@@ -264,6 +267,22 @@ def ridgefill_fill(shape: rf_shape, x_S, N: int, T: int, filled_idx, n_filled: i
         _check(lib().ridgefill_fill(*args))
     else:
         _check(lib().ridgefill_fill_streamed(*args, _stream(copy_stream)))
+
+
+def ridgefill_fill_noalloc(shape: rf_shape, x_S, N: int, T: int, filled_idx, n_filled: int,
+                           layers: list[dict], block_table, page_size: int, num_pages: int,
+                           status, x_stride: int | None = None, stream=None) -> None:
+    """The fill with the library's fixed device scratch as its workspace (no allocation);
+    the device status goes to `status` (a device int32/uint32 tensor of >= 1 element)."""
+    arr = _layers(layers)
+    kv = rf_paged_kv(_ptr(block_table), int(block_table.numel()), int(page_size), int(num_pages))
+    stride = int(x_stride if x_stride is not None else x_S.stride(0))
+    _check(lib().ridgefill_fill_noalloc(C.byref(shape), _ptr(x_S), int(N), int(T), stride,
+                                        _ptr(filled_idx), int(n_filled), arr, len(layers),
+                                        C.byref(kv), _ptr(status), _stream(stream)))
+
+
+RIDGEFILL_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def ridgefill_value_scale_workspace_bytes(shape: rf_shape, c: int, n_layers: int,

@@ -921,6 +921,34 @@ struct StreamEvents {
 
 }  // namespace
 
+// ------------------------------------------------------------- fixed scratch
+// The workspace of ridgefill_fill_noalloc: a file-scope device array, one copy per device
+// (each device that loads the library holds it until the process ends).  Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): the per-device device address comes from hipGetSymbolAddress, looked up once per
+// device on the first call made with that device current, and kernels receive it as a
+// plain pointer.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_layers,
                        hipStream_t stream) {
   hipError_t e = launch_fill_prep(p, stream);

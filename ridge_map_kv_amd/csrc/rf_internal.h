@@ -115,6 +115,11 @@ struct FillPlan {
 
 hipError_t launch_fill(const FillPlan& plan, const FillLayerPtrs* layers, int n_layers,
                        hipStream_t stream);
+
+// The fixed scratch array of ridgefill_fill_noalloc (in rf_fill.hip): its device address on
+// the current device, looked up there on the first call.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_fill_streamed(const FillPlan& plan, const FillLayerPtrs* layers, int n_layers,
                                 hipStream_t stream, hipStream_t copy_stream);
 

@@ -294,6 +294,38 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
   return ok();
 }
 
+rf_status ridgefill_fill_noalloc(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
+                                 int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
+                                 const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
+                                 uint32_t* status, void* stream) {
+  if (!status || !aligned(status, 4)) return fail(RF_E_INVALID, "status must be a 4-byte aligned device pointer");
+  bool done;
+  rf_status s = fill_front(shape, N, T, n_filled, n_layers, nullptr, 0, stream, &done);
+  if (s != RF_OK) return s;
+  hipError_t e;
+  if (done) {
+    e = rf::launch_clear_status(status, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "status clear");
+    return ok();
+  }
+  void* scratch = nullptr;
+  e = rf::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+  rf::FillPlan p;
+  std::vector<rf::FillLayerPtrs> lp;
+  s = prepare_fill(shape, x_S, N, T, x_stride, filled_idx, n_filled, layers, n_layers, kv, scratch,
+                   rf::kNoAllocScratchBytes, false, p, lp);
+  if (s == RF_E_WORKSPACE)
+    return fail(RF_E_WORKSPACE, "one layer of this call needs more than the %zu-byte scratch of "
+                "ridgefill_fill_noalloc (%s); use ridgefill_fill with a workspace",
+                rf::kNoAllocScratchBytes, g_last_error.c_str());
+  if (s != RF_OK) return s;
+  p.status = status;                     // the caller's status word, not the scratch's
+  e = rf::launch_fill(p, lp.data(), n_layers, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  return ok();
+}
+
 rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, int64_t N, int64_t T,
                                   int64_t x_stride, const int32_t* filled_idx, int64_t n_filled,
                                   const rf_layer* layers, int32_t n_layers, const rf_paged_kv* kv,
