@@ -92,6 +92,9 @@ __device__ __forceinline__ void stage_put4(unsigned char* smem, int r, int f, fl
 __device__ __forceinline__ float lo16(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
 __device__ __forceinline__ float hi16(uint32_t x) { return bf16_to_f32(x >> 16); }
 
+// FQ = 1: int8 map codes, read by the GEMM as they are (the F operand's LDS layout of
+// i8_off) and scaled per output row in the epilogue.
+template <int FQ>
 __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   int g, tt, ft;
@@ -103,12 +106,22 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   DmaOperand Fo, To;
   {
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (FQ) {                    // 1 KB block j = 4 p + wave: rows 16 j .. 16 j + 15 of 64 bytes
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r0 = 16 * (4 * p + wave);
+        Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.Aq + (size_t)(f0 + r0) * a.d_in);
+        Fo.off[p] = (uint32_t)((lane >> 2) * a.d_in + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+      }
+    }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
       const int ce = dma_chunk_elems(r, lane);
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in);
-      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
+      if (!FQ) {
+        Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in);
+        Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
+      }
       const int tok = t0 + r;
       int row = 0;
       if (tok < a.n_filled) {
@@ -130,7 +143,7 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   const float my_s = a.has_scale ? Lp.As[f0 + tid] : 1.0f;
 
   f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, a.d_in, smem);
+  gemm_pipeline<false, FQ>(acc, Fo, To, a.d_in, smem);
 
   sbias[tid] = my_b;
   swt[tid] = bf16_to_f32(my_w);
@@ -183,8 +196,9 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   }
 }
 
+template <int FQ>
 __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
-  fill_map_tile(a, xcd_remap(blockIdx.x, gridDim.x));
+  fill_map_tile<FQ>(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // Folded layers: per row, the sum of squares of (R x_S + r) over 256-feature tiles of the
@@ -647,26 +661,6 @@ __global__ void rstd_folded_kernel(FillKArgs a) {
       1.0f / sqrtf(s / (float)a.d + a.eps);
 }
 
-// int8 map codes as bf16 numbers: |q| <= 127 has at most 8 significant bits, so the bf16
-// value equals the integer exactly (the row scale is applied to the fp32 product).
-__global__ void expand_int8_kernel(const int8_t* q, uint16_t* out, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x * 16;
-  for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; i < n; i += stride) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q + i);   // n and i are multiples of 16
-    u32x4 o[2];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x = v[w];
-      const float f0 = (float)(int8_t)(x & 0xff), f1 = (float)(int8_t)((x >> 8) & 0xff);
-      const float f2 = (float)(int8_t)((x >> 16) & 0xff), f3 = (float)(int8_t)(x >> 24);
-      o[w >> 1][(w & 1) * 2 + 0] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-      o[w >> 1][(w & 1) * 2 + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
-    }
-    *reinterpret_cast<u32x4*>(out + i) = o[0];
-    *reinterpret_cast<u32x4*>(out + i + 8) = o[1];
-  }
-}
-
 __global__ void iota_kernel(int32_t* idx, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) idx[i] = i;
@@ -762,8 +756,7 @@ FillWsLayout fill_ws_layout(int d, int d_in, int hd, int kv, int64_t n_filled, u
   L.per_layer_ssq = align256((size_t)mpad * ((folded ? d_in : d) / 128) * sizeof(float));
   L.per_layer_rstd = align256((size_t)mpad * sizeof(float));
   const size_t map_elems = (size_t)d * d_in;
-  L.expand = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
-  L.land = L.expand + ((flags & kWsInt8) ? align256(map_elems * 2) : 0);
+  L.land = L.per_layer_h + L.per_layer_ssq + L.per_layer_rstd;
   // a landing slot holds one layer's streamed map, or its whole folded buffer
   if (flags & kWsStreamed)
     L.land_slot = folded ? fold_layout(d_in, kv).total
@@ -846,17 +839,6 @@ hipError_t launch_fill_prep(const FillPlan& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// int8 codes of the group's maps -> exact bf16 in each layer block's expansion area.
-void expand_group(const FillPlan& p, FillKArgs& a, int G, const int8_t* const* codes,
-                  hipStream_t stream) {
-  const size_t n = (size_t)p.d * p.d_in;
-  for (int g = 0; g < G; ++g) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.layer_ws + g * a.per_layer + p.L.expand);
-    hipLaunchKernelGGL(expand_int8_kernel, dim3(1024), dim3(256), 0, stream, codes[g], dst, n);
-    a.L[g].A = dst;
-  }
-}
-
 // Map GEMM, 1/RMS, K/V GEMM for the G layers in a.L (their maps already on the device).
 hipError_t launch_fill_group(const FillPlan& p, FillKArgs& a, int G, hipStream_t stream) {
   a.f_base = 0;
@@ -877,7 +859,10 @@ hipError_t launch_fill_group(const FillPlan& p, FillKArgs& a, int G, hipStream_t
   a.nft = p.d / kTile;
   {
     ProfileScope ps(RF_KERNEL_FILL_MAP, stream);
-    hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    if (a.has_scale)
+      hipLaunchKernelGGL(fill_map_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(fill_map_kernel<0>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
   }
   hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
                      a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
@@ -958,12 +943,7 @@ hipError_t launch_fill(const FillPlan& p, const FillLayerPtrs* layers, int n_lay
   for (int l0 = 0; l0 < n_layers; l0 += gsize) {
     const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
     FillKArgs a = fill_args(p, lws);
-    const int8_t* codes[kMaxGroup];
-    for (int g = 0; g < G; ++g) {
-      a.L[g] = layers[l0 + g];
-      codes[g] = layers[l0 + g].Aq;
-    }
-    if (p.flags & kWsInt8) expand_group(p, a, G, codes, stream);
+    for (int g = 0; g < G; ++g) a.L[g] = layers[l0 + g];
     if ((e = launch_fill_group(p, a, G, stream)) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1008,7 +988,6 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
     const int slot = gi & 1;
     if (gi >= 2 && (e = hipStreamWaitEvent(copy_stream, ev.done[slot], 0)) != hipSuccess) return e;
     FillKArgs a = fill_args(p, lws);
-    const int8_t* codes[kMaxGroup];
     for (int g = 0; g < G; ++g) {
       a.L[g] = layers[l0 + g];
       unsigned char* land = lws + g * p.L.per_layer + p.L.land + slot * p.L.land_slot;
@@ -1023,7 +1002,7 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
           return e;
       }
       if (int8) {
-        codes[g] = reinterpret_cast<const int8_t*>(land);
+        a.L[g].Aq = reinterpret_cast<const int8_t*>(land);
       } else if (folded) {
         const uint16_t* P = reinterpret_cast<const uint16_t*>(land + F.P);
         a.L[g].A = reinterpret_cast<const uint16_t*>(land + F.R);
@@ -1039,7 +1018,6 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
     }
     if ((e = hipEventRecord(ev.ready[slot], copy_stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(stream, ev.ready[slot], 0)) != hipSuccess) return e;
-    if (int8) expand_group(p, a, G, codes, stream);
     if ((e = launch_fill_group(p, a, G, stream)) != hipSuccess) return e;
     if ((e = hipEventRecord(ev.done[slot], stream)) != hipSuccess) return e;
   }
@@ -1061,20 +1039,18 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
   for (int l0 = 0; l0 < n_layers; l0 += gsize) {
     const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
     FillKArgs a = fill_args(p, pred);
-    const int8_t* codes[kMaxGroup];
-    for (int g = 0; g < G; ++g) {
-      a.L[g] = layers[l0 + g];
-      codes[g] = layers[l0 + g].Aq;
-    }
+    for (int g = 0; g < G; ++g) a.L[g] = layers[l0 + g];
     a.f_base = 0;
     if (a.folded) {              // |x_hat|^2 from the triangular factor, then 1/rms
       a.nft = (p.d_in / kTile + 1) / 2;
       launch_tiles(fill_norm_kernel, a, G * a.ntt * a.nft, stream);
       hipLaunchKernelGGL(rstd_folded_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a);
     } else {
-      if (p.flags & kWsInt8) expand_group(p, a, G, codes, stream);
       a.nft = p.d / kTile;
-      hipLaunchKernelGGL(fill_map_kernel, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+      if (a.has_scale)
+        hipLaunchKernelGGL(fill_map_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL(fill_map_kernel<0>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
       hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
                          a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
     }

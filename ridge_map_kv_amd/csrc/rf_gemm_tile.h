@@ -96,15 +96,43 @@ __device__ __forceinline__ void dma_block(const DmaOperand& o, int p, int kbytes
   dma16(o.base[p] + kbytes, o.off[p], lds_op + (4 * p + wave) * 1024);
 }
 
+// ---- int8 F operand (FQ = 1): maps stored as int8 codes are read as they are and turned
+// into bf16 numbers between LDS and the MFMA (|q| <= 127 is exact in bf16).  A stage's F
+// operand is then 256 rows of 64 bytes (16 KB); 1 KB DMA block j holds rows 16 j .. 16 j + 15,
+// lane l of the block landing on row 16 j + (l >> 2) at 16-byte position l & 3, which holds
+// logical chunk (l & 3) ^ ((l >> 4) & 3), i.e. chunk q of row r sits at q ^ ((r >> 2) & 3).
+// One 16-wide step reads chunk s of each row, 8 bytes per lane: the 32 rows of a half-wave
+// then spread over all 16 (row & 3, position) bank groups twice, the least a 64-byte row
+// pitch allows.
+__device__ __forceinline__ int i8_off(int r, int q) {
+  return (r >> 4) * 1024 + ((r & 15) * 4 + (q ^ ((r >> 2) & 3))) * 16;
+}
+
+// Eight int8 codes -> eight bf16 numbers (exact).
+__device__ __forceinline__ bf16x8 i8_to_bf16x8(u32x2 q) {
+  u32x4 o;
+  o.x = pack_bf16x2((float)(int8_t)(q.x & 0xff), (float)(int8_t)((q.x >> 8) & 0xff));
+  o.y = pack_bf16x2((float)(int8_t)((q.x >> 16) & 0xff), (float)(int8_t)(q.x >> 24));
+  o.z = pack_bf16x2((float)(int8_t)(q.y & 0xff), (float)(int8_t)((q.y >> 8) & 0xff));
+  o.w = pack_bf16x2((float)(int8_t)((q.y >> 16) & 0xff), (float)(int8_t)(q.y >> 24));
+  return __builtin_bit_cast(bf16x8, o);
+}
+
 // Fragment i (0..3: F rows, 4..7: T rows) of 16-wide step s of a stage.
+template <int FQ = 0>
 __device__ __forceinline__ void read_frag(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
                                           int i, int s, int wf, int wt, int lane) {
   const int c = s * 2 + (lane >> 5);
-  if (i < 4)
-    a[i] = *reinterpret_cast<const bf16x8*>(st + lds_off128(wf * 128 + i * 32 + (lane & 31), c));
-  else
+  if (i < 4) {
+    const int r = wf * 128 + i * 32 + (lane & 31);
+    if (FQ)
+      a[i] = i8_to_bf16x8(*reinterpret_cast<const u32x2*>(st + i8_off(r, s) + (lane >> 5) * 8));
+    else
+      a[i] = *reinterpret_cast<const bf16x8*>(st + lds_off128(r, c));
+  } else {
     b[i - 4] = *reinterpret_cast<const bf16x8*>(st + kPipeOp +
                                                 lds_off128(wt * 128 + (i - 4) * 32 + (lane & 31), c));
+  }
 }
 
 __device__ __forceinline__ void mfma_i(f32x16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4],
@@ -112,18 +140,29 @@ __device__ __forceinline__ void mfma_i(f32x16 (&acc)[4][4], const bf16x8 (&a)[4]
   acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i >> 2], b[i & 3], acc[i >> 2][i & 3], 0, 0, 0);
 }
 
-// Load issue j (0..15) of a slice: even j -> F block j / 2, odd j -> T block j / 2.
+// Load issue j of a slice.  bf16 F (16 issues): even j -> F block j / 2, odd j -> T block
+// j / 2.  int8 F (12 issues, F blocks hold 16 rows and advance half as many bytes per slice):
+// j % 3 == 2 -> F block j / 3, else T block 2 (j / 3) + j % 3.
+template <int FQ = 0>
 __device__ __forceinline__ void dma_issue(const DmaOperand& F, const DmaOperand& T, int j, int kb,
                                           uint32_t dst, int wave) {
-  if (j & 1)
+  if (FQ) {
+    if (j % 3 == 2)
+      dma_block(F, j / 3, kb >> 1, dst, wave);
+    else
+      dma_block(T, 2 * (j / 3) + j % 3, kb, dst + kPipeOp, wave);
+  } else if (j & 1) {
     dma_block(T, j >> 1, kb, dst + kPipeOp, wave);
-  else
+  } else {
     dma_block(F, j >> 1, kb, dst, wave);
+  }
 }
+template <int FQ> constexpr int kIssues = FQ ? 12 : 16;   // load issues per wave and slice
 
 // 16 MFMAs on (a, b); after each of the first 8, one fragment of step s of stage st is
-// read into (na, nb).  With `dma`, load issues j0 .. j0 + 7 of the slice at byte offset kb
-// go out after the even-numbered MFMAs, into the stage at LDS address dst.
+// read into (na, nb).  With `dma`, the second half of the slice's load issues (j0 onwards)
+// at byte offset kb go out after the even-numbered MFMAs, into the stage at LDS address dst.
+template <int FQ = 0>
 __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
                                             const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
                                             const unsigned char* st, int s, int wf, int wt, int lane,
@@ -132,8 +171,8 @@ __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     mfma_i(acc, a, b, i);
-    if (dma && !(i & 1)) dma_issue(F, T, j0 + (i >> 1), kb, dst, wave);
-    if (i < 8) read_frag(na, nb, st, i, s, wf, wt, lane);
+    if (dma && !(i & 1) && (i >> 1) < kIssues<FQ> / 2) dma_issue<FQ>(F, T, j0 + (i >> 1), kb, dst, wave);
+    if (i < 8) read_frag<FQ>(na, nb, st, i, s, wf, wt, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -151,7 +190,7 @@ __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&
 //
 // gemm_prologue: the loads of slices 0 and 1 (32 per wave), into the two stages.  The LDS
 // must be free of readers (after a barrier).
-template <bool REV = false>
+template <bool REV = false, int FQ = 0>
 __device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOperand& T, int K,
                                               unsigned char* smem) {
   constexpr int kStep = REV ? -kPipeBK * 2 : kPipeBK * 2;
@@ -160,10 +199,7 @@ __device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOper
   const uint32_t base = lds_addr(smem);
   for (int s = 0; s < 2 && s < nk; ++s) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      dma_block(F, p, s * kStep, base + s * kPipeStage, wave);
-      dma_block(T, p, s * kStep, base + s * kPipeStage + kPipeOp, wave);
-    }
+    for (int j = 0; j < kIssues<FQ>; ++j) dma_issue<FQ>(F, T, j, s * kStep, base + s * kPipeStage, wave);
   }
 }
 
@@ -173,7 +209,7 @@ __device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOper
 // kt + 2 exists and the first half of its loads goes out in step 0.  With both flags fixed at
 // compile time the steady-state body carries no load conditions, which measurably shortens
 // the issue of the 64 MFMAs of a slice.
-template <bool REV, bool PEND, bool MORE>
+template <bool REV, bool PEND, bool MORE, int FQ = 0>
 __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4], bf16x8 (&b0)[4],
                                            bf16x8 (&a1)[4], bf16x8 (&b1)[4], const DmaOperand& F,
                                            const DmaOperand& T, unsigned char* smem, uint32_t base,
@@ -182,9 +218,10 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4],
   const unsigned char* cur = smem + (kt & 1) * kPipeStage;
   const int kbp = (kt + 1) * kStep;
   const uint32_t dstp = base + ((kt + 1) & 1) * kPipeStage;
-  mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, PEND, F, T, kbp, dstp, 8, wave);
-  mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
-  mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+  mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, PEND, F, T, kbp, dstp,
+                  kIssues<FQ> / 2, wave);
+  mfma16_read<FQ>(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+  mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slice kt + 1, the only one in flight
   __syncthreads();                                       // ... landed for every wave; slice kt read
   const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
@@ -193,8 +230,8 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4],
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     mfma_i(acc, a1, b1, i);
-    if (MORE && !(i & 1)) dma_issue(F, T, i >> 1, kb, dst, wave);
-    if (i >= 8) read_frag(a0, b0, nxt, i - 8, 0, wf, wt, lane);
+    if (MORE && !(i & 1) && (i >> 1) < kIssues<FQ> / 2) dma_issue<FQ>(F, T, i >> 1, kb, dst, wave);
+    if (i >= 8) read_frag<FQ>(a0, b0, nxt, i - 8, 0, wf, wt, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -203,7 +240,7 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4],
 // counts on loads completing in order: while any load of slice 0 is pending, all 16 of
 // slice 1 are too, so at most 16 outstanding operations (stores issued after the
 // prologue included) means slice 0 has landed.
-template <bool REV = false>
+template <bool REV = false, int FQ = 0>
 __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOperand& F,
                                               const DmaOperand& T, int K, unsigned char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -218,29 +255,34 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOper
 
   const int nk = K / kPipeBK;
   const uint32_t base = lds_addr(smem);
-  if (nk > 1)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // slice 0 landed (slice 1: 16 loads)
-  else
+  if (nk > 1) {                                          // slice 0 landed: at most slice 1's
+    if (FQ)                                              // loads are outstanding
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
   bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_frag(a0, b0, smem, i, 0, wf, wt, lane);
+  for (int i = 0; i < 8; ++i) read_frag<FQ>(a0, b0, smem, i, 0, wf, wt, lane);
   // slices 0 .. nk - 2: the first has nothing pending, the last starts no further slice
   if (nk == 2) {
-    gemm_slice<REV, false, false>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, wave);
+    gemm_slice<REV, false, false, FQ>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, wave);
   } else if (nk > 2) {
-    gemm_slice<REV, false, true>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, wave);
+    gemm_slice<REV, false, true, FQ>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, wave);
     for (int kt = 1; kt < nk - 2; ++kt)
-      gemm_slice<REV, true, true>(acc, a0, b0, a1, b1, F, T, smem, base, kt, wf, wt, lane, wave);
-    gemm_slice<REV, true, false>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 2, wf, wt, lane, wave);
+      gemm_slice<REV, true, true, FQ>(acc, a0, b0, a1, b1, F, T, smem, base, kt, wf, wt, lane, wave);
+    gemm_slice<REV, true, false, FQ>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 2, wf, wt, lane,
+                                     wave);
   }
   {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
-    mfma16_read(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, false, F, T, 0, 0, 0, wave);
-    mfma16_read(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
-    mfma16_read(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+    mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+    mfma16_read<FQ>(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, 0, 0, wave);
+    mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, 0, 0, wave);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }
@@ -248,11 +290,11 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOper
 }
 
 // acc = F[256 x K] * T[256 x K]^T: gemm_prologue then gemm_mainloop.
-template <bool REV = false>
+template <bool REV = false, int FQ = 0>
 __device__ __forceinline__ void gemm_pipeline(f32x16 (&acc)[4][4], const DmaOperand& F,
                                               const DmaOperand& T, int K, unsigned char* smem) {
-  gemm_prologue<REV>(F, T, K, smem);
-  gemm_mainloop<REV>(acc, F, T, K, smem);
+  gemm_prologue<REV, FQ>(F, T, K, smem);
+  gemm_mainloop<REV, FQ>(acc, F, T, K, smem);
 }
 
 }  // namespace

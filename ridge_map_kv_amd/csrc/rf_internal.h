@@ -24,7 +24,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // [d_in] in fg, the K and V halves of P in WK and WV (rows of d_in), c [2 kv] in fc and
 // kappa in kap; w is unused.
 struct FillLayerPtrs {
-  const uint16_t* A;            // bf16 map (for an int8 map: its expansion in the workspace)
+  const uint16_t* A;            // bf16 map (null for an int8 map, which the GEMM reads as codes)
   const float* b;
   const uint16_t* w;
   const uint16_t* WK;
@@ -41,7 +41,7 @@ struct FillLayerPtrs {
 };
 
 // Workspace variants of a fill call.
-constexpr unsigned kWsInt8 = 1u;       // int8 maps: a bf16 expansion area per layer
+constexpr unsigned kWsInt8 = 1u;       // int8 maps (codes read by the map GEMM itself)
 constexpr unsigned kWsStreamed = 2u;   // host maps: two landing slots per layer
 constexpr unsigned kWsFolded = 4u;     // folded layers: no predicted-input buffer
 
@@ -84,7 +84,7 @@ hipError_t launch_fold(int d, int d_in, int kv, const FoldLayerIn* layers, int G
 // start of that layer's block).
 struct FillWsLayout {
   size_t rope_cos, rope_sin, row_slot, hbuf, fixed;
-  size_t per_layer_h, per_layer_ssq, per_layer_rstd, expand, land, land_slot, per_layer;
+  size_t per_layer_h, per_layer_ssq, per_layer_rstd, land, land_slot, per_layer;
 };
 FillWsLayout fill_ws_layout(int d, int d_in, int hd, int kv, int64_t n_filled, unsigned flags);
 

@@ -290,9 +290,12 @@ def test_variant_argument_errors():
     f = _filled(case)
     shape = make_shape(case)
     idx = torch.from_numpy(f.astype(np.int32)).cuda()
-    # a bf16-map workspace for one layer lacks the int8 expansion area
-    ws_small = torch.empty(B.ridgefill_fill_workspace_bytes(shape, f.size, 1), dtype=torch.uint8,
-                           device="cuda")
+    # int8 maps are read as codes by the map GEMM: they need no more workspace than bf16 maps
+    assert B.ridgefill_fill_workspace_bytes(shape, f.size, 2, B.RF_MAPS_INT8) == \
+        B.ridgefill_fill_workspace_bytes(shape, f.size, 2)
+    # a workspace short of one layer's block is refused before anything is enqueued
+    ws_small = torch.empty(B.ridgefill_fill_workspace_bytes(shape, f.size, 1) - 256,
+                           dtype=torch.uint8, device="cuda")
     with pytest.raises(B.RidgeFillError) as e:
         B.ridgefill_fill(shape, inp["xS"], case.N, case.T, idx, f.size, inp["layers"],
                          inp["table"], 16, inp["num_pages"], ws_small)
