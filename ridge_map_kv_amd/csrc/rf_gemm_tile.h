@@ -122,6 +122,10 @@ __device__ __forceinline__ bf16x8 i8_to_bf16x8(u32x2 q) {
 template <int FQ = 0>
 __device__ __forceinline__ void read_frag(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
                                           int i, int s, int wf, int wt, int lane) {
+  // Read order a0 b0 b1 b2 b3 a1 a2 a3: the next step's MFMAs (m-major: a0 with b0..b3,
+  // then a1 ...) need the reads in this order, so each MFMA waits on a read issued at least
+  // five slots before it, instead of the first four MFMAs waiting on the last four reads.
+  i = i == 0 ? 0 : i <= 4 ? i + 3 : i - 4;
   const int c = s * 2 + (lane >> 5);
   if (i < 4) {
     const int r = wf * 128 + i * 32 + (lane & 31);
