@@ -313,15 +313,16 @@ rf_status ridgefill_quantize_map(const float* A, int64_t rows, int64_t cols, int
  *   x_S_tail     device bf16 [c][x_stride]: split-layer states of the first c tail rows
  *   x_l_tail     host array [n_layers] of device bf16 [c][d] (contiguous): each layer's
  *                exact input for the same rows
- *   layers       A or A_q/A_scale, b, norm_w, W_K, W_V of each layer (W_K is read only
- *                to share the fill's tiling; K and the pages are not written); or, for
+ *   layers       A or A_q/A_scale, b, norm_w, W_V of each layer (W_K is not read and
+ *                may be null; K and the pages are not written); or, for
  *                folded layers (all or none), folded with norm_w and W_V: the predicted
  *                values then come from the folded form, v_p = (P_V x_S + c_V) / rms with
  *                |x_hat|^2 = |R x_S + r|^2 + kappa, and the exact ones from W_V and norm_w
  *   v_scale_out  device fp32 [n_layers][n_kv_heads]
  *   ws           >= ridgefill_value_scale_workspace_bytes(shape, c, 1, map_flags) with
  *                map_flags 0, RF_MAPS_INT8 or RF_MAPS_FOLDED (the last two exclusive); a
- *                larger one lets more layers share a launch
+ *                larger one lets more layers share a launch (up to 64: the size query for
+ *                n_layers covers min(n_layers, 64) layers)
  * Norms are taken in fp32 on the fp32 projections (before any bf16 rounding of v); the
  * inputs to W_V are rounded to bf16 once, as in the fill (for folded layers P_V is the
  * rounded operand).  The mean is added in row order in fp64.  A predicted norm of 0

@@ -33,6 +33,7 @@ namespace {
 
 struct FillKArgs {
   FillLayerPtrs L[kMaxGroup];
+  const FillLayerPtrs* Ltab;    // or null; else layer g's pointers are Ltab[g] (device memory)
   const uint16_t* xS;
   int64_t x_stride;
   const int32_t* idx;
@@ -55,6 +56,38 @@ struct FillKArgs {
   int n_items;                  // tiles (or tile pairs) of the launch
 };
 static_assert(sizeof(FillKArgs) <= 4096, "kernel arguments must fit in 4 KB");
+
+// Layer g's pointers: from the kernel arguments (up to kMaxGroup layers), or from a table in
+// the workspace when a launch covers more layers than the arguments hold.
+// (A table entry comes in through a vector load; each pointer is made wave-uniform again,
+// since the direct-to-LDS loads take their base addresses in scalar registers.)
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>((uint64_t)hi << 32 | lo);
+}
+
+__device__ __forceinline__ FillLayerPtrs layer_ptrs(const FillKArgs& a, int g) {
+  if (!a.Ltab) return a.L[g];
+  FillLayerPtrs t = a.Ltab[g];
+  t.A = uniform_ptr(t.A);
+  t.b = uniform_ptr(t.b);
+  t.w = uniform_ptr(t.w);
+  t.WK = uniform_ptr(t.WK);
+  t.WV = uniform_ptr(t.WV);
+  t.kp = uniform_ptr(t.kp);
+  t.vp = uniform_ptr(t.vp);
+  t.kn = uniform_ptr(t.kn);
+  t.vs = uniform_ptr(t.vs);
+  t.Aq = uniform_ptr(t.Aq);
+  t.As = uniform_ptr(t.As);
+  t.fc = uniform_ptr(t.fc);
+  t.kap = uniform_ptr(t.kap);
+  t.fg = uniform_ptr(t.fg);
+  return t;
+}
 
 // Tile order: layer, then groups of kFeatGroup feature tiles (weight rows) swept against
 // every token tile.  Combined with xcd_remap, an XCD's 32 concurrent tiles are a block of
@@ -99,7 +132,7 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   int g, tt, ft;
   decode_tile(tile, a.ntt, a.nft, g, tt, ft);
-  const FillLayerPtrs Lp = a.L[g];
+  const FillLayerPtrs Lp = layer_ptrs(a, g);
   const int t0 = tt * kTile, f0 = ft * kTile;
   const int tid = threadIdx.x;
 
@@ -241,7 +274,7 @@ __device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int f0 = t.ft * kTile, t0 = t.tt * kTile;
   const int col = half == 0 ? a.d_in - kPipeBK : f0;
-  const uint16_t* R = a.L[t.g].A;
+  const uint16_t* R = layer_ptrs(a, t.g).A;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
@@ -292,8 +325,9 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   norm_prologue(Fo, To, a.d_in - cur.ft * kTile, 0, smem);
   for (;;) {
     const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
-    const float my_r = a.L[cur.g].b[f0 + tid];
-    const float my_g = a.L[cur.g].fg[f0 + tid];
+    const FillLayerPtrs Lc = layer_ptrs(a, cur.g);
+    const float my_r = Lc.b[f0 + tid];
+    const float my_g = Lc.fg[f0 + tid];
     f32x16 acc[4][4];
     if (half == 0)                                          // each ends with a barrier:
       gemm_mainloop<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
@@ -400,7 +434,11 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
   int g, tt, ft;
   decode_tile(tile, a.ntt, a.nft, g, tt, ft);
   ft += a.f_base;
-  const FillLayerPtrs Lp = a.L[g];
+  const FillLayerPtrs Lp = layer_ptrs(a, g);
+  // Value norms take each layer's form from its pointers (a folded layer has c), so the
+  // exact rows of the value rescale, plain layers, can share a launch with folded ones.
+  const bool folded = MODE == 1 ? Lp.fc != nullptr : a.folded != 0;
+  const int kdim = MODE == 1 ? (folded ? a.d_in : a.d) : a.kdim;
   const int t0 = tt * kTile, f0 = ft * kTile;
   const int tid = threadIdx.x;
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.layer_ws + g * a.per_layer);
@@ -415,10 +453,13 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
       const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
       const int ce = dma_chunk_elems(r, lane);
       const int f = f0 + r0;                 // 8-row blocks never straddle K and V (kv % 128 == 0)
-      Fo.base[p] = reinterpret_cast<const unsigned char*>(
-          f < a.kv ? Lp.WK + (size_t)f * a.kdim : Lp.WV + (size_t)(f - a.kv) * a.kdim);
-      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.kdim + ce) * 2);
-      if (a.folded) {                        // rows of x_S gathered through the index list
+      // value norms discard the K rows of a tile that straddles K and V: they read W_V's
+      // first rows instead, so W_K is never needed there
+      const uint16_t* wrow = f >= a.kv ? Lp.WV + (size_t)(f - a.kv) * kdim
+                             : MODE == 1 ? Lp.WV : Lp.WK + (size_t)f * kdim;
+      Fo.base[p] = reinterpret_cast<const unsigned char*>(wrow);
+      Fo.off[p] = (uint32_t)((dma_lane_row(lane) * kdim + ce) * 2);
+      if (folded) {                        // rows of x_S gathered through the index list
         const int tok = t0 + r;
         int row = 0;
         if (tok < a.n_filled) {
@@ -450,10 +491,10 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
     if (a.has_knorm && tid < a.hd) my_kn = bf16_to_f32(Lp.kn[tid]);
     if (Lp.vs && tid < a.n_kv) my_vs = Lp.vs[tid];
   }
-  if (a.folded) my_c = Lp.fc[f0 + tid];
+  if (folded) my_c = Lp.fc[f0 + tid];
 
   f32x16 acc[4][4];
-  gemm_pipeline(acc, Fo, To, a.kdim, smem);
+  gemm_pipeline(acc, Fo, To, kdim, smem);
 
   rstd[tid] = my_r;
   rowoff[tid] = my_off;
@@ -475,7 +516,7 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
       const int tl = wt * 128 + n * 32 + (lane & 31);
       const int tok = t0 + tl;
       const float r = rstd[tl];
-      if (a.folded) {           // P x + c: the value before the 1/rms scale
+      if (folded) {           // P x + c: the value before the 1/rms scale
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -500,7 +541,7 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
     const int tl = wt * 128 + n * 32 + (lane & 31);
     const int tok = t0 + tl;
     const float r = rstd[tl];   // rows past n_filled: finite padding, never stored
-    if (a.folded) {             // (P x + c) / rms
+    if (folded) {             // (P x + c) / rms
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -656,7 +697,7 @@ __global__ void rstd_folded_kernel(FillKArgs a) {
   const float* p = reinterpret_cast<const float*>(lw + a.per_layer_h) + row;
   float s = 0.f;
   for (int c = 0; c < a.nchunk; ++c) s += p[(size_t)c * a.mpad];
-  s = fmaxf(s + *a.L[g].kap, 0.f);
+  s = fmaxf(s + *layer_ptrs(a, g).kap, 0.f);
   reinterpret_cast<float*>(lw + a.per_layer_h + a.per_layer_ssq)[row] =
       1.0f / sqrtf(s / (float)a.d + a.eps);
 }
@@ -709,6 +750,21 @@ __global__ void exact_rows_kernel(ExactArgs a) {
     float* rs = reinterpret_cast<float*>(lw + a.per_layer_h + a.per_layer_ssq);
     rs[row] = row < a.c ? 1.0f / sqrtf(red[0] / (float)a.d + a.eps) : 0.f;
   }
+}
+
+// Layer-pointer table entries [first, first + n) from the arguments into device memory, one
+// thread per entry.
+constexpr int kTableChunk = 32;
+struct LayerTableChunk {
+  FillLayerPtrs e[kTableChunk];
+  FillLayerPtrs* dst;
+  int n;
+};
+static_assert(sizeof(LayerTableChunk) <= 4096, "kernel arguments must fit in 4 KB");
+
+__global__ void layer_table_kernel(LayerTableChunk c) {
+  const int i = threadIdx.x;
+  if (i < c.n) c.dst[i] = c.e[i];
 }
 
 // v_scale[l][h] = mean over the c rows of |v_exact| / |v_pred|: one block per (l, h); thread
@@ -1026,7 +1082,12 @@ hipError_t launch_fill_streamed(const FillPlan& p, const FillLayerPtrs* layers, 
 
 // Value-rescale factors: the c tail rows (indices 0 .. c-1 of x_S_tail) through the map,
 // RMSNorm and W_V, and the exact tail inputs through RMSNorm and W_V; per (row, head) the
-// two value norms; per head the mean of their ratio.
+// two value norms; per head the mean of their ratio.  A group of G layers runs as: the map
+// (or the folded norm) and 1/rms of the predicted rows for all G layers in one launch; the
+// exact rows' bf16(x_l * w) and 1/rms; then the value norms of both sides in one launch over
+// 2 G table entries (the G layers, then G plain entries with the layers' own W_V whose
+// staged rows are the exact ones); then the factors.  Layer pointers come from a table in
+// the workspace, so a group may hold more layers than the kernel arguments could.
 hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
                               const uint16_t* const* x_exact, const uint16_t* const* exact_wv,
                               int n_layers, float* out, const VsLayout& V, hipStream_t stream) {
@@ -1038,8 +1099,24 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
   const int gsize = group_size(n_layers, p.group);
   for (int l0 = 0; l0 < n_layers; l0 += gsize) {
     const int G = (n_layers - l0) < gsize ? (n_layers - l0) : gsize;
+    // the table: entries 0 .. G-1 the layers, G .. 2G-1 the exact side (W_V, norm weight)
+    for (int c0 = 0; c0 < 2 * G; c0 += kTableChunk) {
+      LayerTableChunk t = {};
+      t.n = (2 * G - c0) < kTableChunk ? (2 * G - c0) : kTableChunk;
+      t.dst = V.table + c0;
+      for (int i = 0; i < t.n; ++i) {
+        const int k = c0 + i;
+        if (k < G) {
+          t.e[i] = layers[l0 + k];
+        } else {
+          t.e[i].w = layers[l0 + k - G].w;
+          t.e[i].WV = exact_wv[l0 + k - G];
+        }
+      }
+      hipLaunchKernelGGL(layer_table_kernel, dim3(1), dim3(kTableChunk), 0, stream, t);
+    }
     FillKArgs a = fill_args(p, pred);
-    for (int g = 0; g < G; ++g) a.L[g] = layers[l0 + g];
+    a.Ltab = V.table;
     a.f_base = 0;
     if (a.folded) {              // |x_hat|^2 from the triangular factor, then 1/rms
       a.nft = (p.d_in / kTile + 1) / 2;
@@ -1054,35 +1131,31 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
       hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
                          a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
     }
-    ExactArgs x = {};
-    for (int g = 0; g < G; ++g) {
-      x.x[g] = x_exact[l0 + g];
-      x.w[g] = layers[l0 + g].w;
+    // the exact rows into the G blocks after the predicted ones
+    for (int c0 = 0; c0 < G; c0 += kMaxGroup) {
+      const int n = (G - c0) < kMaxGroup ? (G - c0) : kMaxGroup;
+      ExactArgs x = {};
+      for (int g = 0; g < n; ++g) {
+        x.x[g] = x_exact[l0 + c0 + g];
+        x.w[g] = layers[l0 + c0 + g].w;
+      }
+      x.c = p.n_filled;
+      x.d = p.d;
+      x.eps = p.eps;
+      x.layer_ws = pred + (size_t)(G + c0) * p.L.per_layer;
+      x.per_layer = p.L.per_layer;
+      x.per_layer_h = p.L.per_layer_h;
+      x.per_layer_ssq = p.L.per_layer_ssq;
+      hipLaunchKernelGGL(exact_rows_kernel, dim3(p.mpad, n), dim3(256), 0, stream, x);
     }
-    x.c = p.n_filled;
-    x.d = p.d;
-    x.eps = p.eps;
-    x.layer_ws = V.exact;
-    x.per_layer = p.L.per_layer;
-    x.per_layer_h = p.L.per_layer_h;
-    x.per_layer_ssq = p.L.per_layer_ssq;
-    hipLaunchKernelGGL(exact_rows_kernel, dim3(p.mpad, G), dim3(256), 0, stream, x);
-    // value norms of the predicted and of the exact rows: the tiles that hold V features
+    // value norms of both sides: the tiles that hold V features of 2 G entries
     a.f_base = p.kv / kTile;
     a.nft = 2 * p.kv / kTile - a.f_base;
-    a.vnorm = V.vn_pred;
-    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
-    // the exact rows (bf16(x_l * w), d wide) through the layer's own W_V
-    FillKArgs b = a;
-    b.folded = 0;
-    b.kdim = p.d;
-    b.nchunk = p.d / 128;
-    b.layer_ws = V.exact;
-    b.vnorm = V.vn_exact;
-    for (int g = 0; g < G; ++g) b.L[g].WV = exact_wv[l0 + g];
-    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(G * b.ntt * b.nft), dim3(kThreads), 0, stream, b);
-    hipLaunchKernelGGL(vscale_kernel, dim3(G * p.n_kv), dim3(256), 0, stream, V.vn_pred,
-                       V.vn_exact, p.n_filled, p.mpad, p.n_kv, out + (size_t)l0 * p.n_kv);
+    a.vnorm = V.vn;
+    hipLaunchKernelGGL(fill_kv_kernel<1>, dim3(2 * G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(vscale_kernel, dim3(G * p.n_kv), dim3(256), 0, stream, V.vn,
+                       V.vn + (size_t)G * p.mpad * p.n_kv, p.n_filled, p.mpad, p.n_kv,
+                       out + (size_t)l0 * p.n_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

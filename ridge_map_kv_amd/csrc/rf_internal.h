@@ -126,11 +126,14 @@ hipError_t launch_fill_streamed(const FillPlan& plan, const FillLayerPtrs* layer
 // Value-rescale pass: the plan describes c tail rows as its "filled" rows (idx points at
 // an int32 [mpad] scratch list the pass fills with 0 .. mpad-1); predicted rows use the
 // plan's per-layer blocks, exact rows the blocks at `exact`.
+// Value-rescale workspace: status, row indices, value norms [2][group][cpad][n_kv]
+// (predicted, then exact rows), a layer-pointer table of 2 group entries, then 2 group
+// per-layer blocks (the predicted rows' staged inputs and norms, then the exact rows').
+constexpr int kVsMaxGroup = 64;  // layers sharing the value-scale launches
 struct VsLayout {
-  size_t idx, vn_pred_off, vn_exact_off, pred, total_fixed;
-  unsigned char* exact;
-  float* vn_pred;
-  float* vn_exact;
+  size_t idx, vn_off, table_off, blocks, total_fixed;
+  float* vn;
+  FillLayerPtrs* table;
 };
 // The predicted rows use `layers` (plain or folded, as plan.flags says); the exact rows
 // always go through the layers' own W_V, exact_wv[l].

@@ -348,17 +348,14 @@ rf_status ridgefill_fill_streamed(const rf_shape* shape, const uint16_t* x_S, in
 
 // Value-rescale workspace: status, row list, two norm arrays, then per layer of a group a
 // predicted block and an exact block (each laid out like a fill layer block).
-static rf::VsLayout vs_layout(const rf::FillWsLayout& L, int64_t c, int n_kv, int group) {
+static rf::VsLayout vs_layout(int64_t c, int n_kv, int group) {
   rf::VsLayout V = {};
   const int64_t cpad = (c + rf::kTile - 1) / rf::kTile * rf::kTile;
   V.idx = rf::kStatusBytes;
-  V.vn_pred_off = V.idx + rf::align256((size_t)cpad * 4);
-  const size_t vn = rf::align256((size_t)group * cpad * n_kv * 4);
-  V.vn_exact_off = V.vn_pred_off + vn;
-  V.pred = V.vn_exact_off + vn;
-  V.exact = nullptr;
-  V.total_fixed = V.pred;
-  (void)L;
+  V.vn_off = V.idx + rf::align256((size_t)cpad * 4);
+  V.table_off = V.vn_off + rf::align256((size_t)2 * group * cpad * n_kv * 4);
+  V.blocks = V.table_off + rf::align256((size_t)2 * group * sizeof(rf::FillLayerPtrs));
+  V.total_fixed = V.blocks;
   return V;
 }
 
@@ -374,8 +371,8 @@ size_t ridgefill_value_scale_workspace_bytes(const rf_shape* shape, int64_t c, i
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in_of(shape), shape->head_dim,
                                                 shape->n_kv_heads * shape->head_dim, c,
                                                 map_flags_of(map_flags & RF_MAPS_INT8));
-  const int g = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
-  const rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, g);
+  const int g = n_layers < rf::kVsMaxGroup ? n_layers : rf::kVsMaxGroup;
+  const rf::VsLayout V = vs_layout(c, shape->n_kv_heads, g);
   return V.total_fixed + (size_t)2 * g * L.per_layer;
 }
 
@@ -416,16 +413,15 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
                     "the exact rows 16-byte alignment", i);
       continue;
     }
-    if (!l.b || !l.norm_w || !l.W_K || !l.W_V || !x_l_tail[i])
-      return fail(RF_E_INVALID, "layer %d: b, norm_w, W_K, W_V and its exact tail rows are "
-                  "required", i);
+    if (!l.b || !l.norm_w || !l.W_V || !x_l_tail[i])
+      return fail(RF_E_INVALID, "layer %d: b, norm_w, W_V and its exact tail rows are required",
+                  i);
     if ((l.A != nullptr) == (l.A_q != nullptr) || (l.A_q != nullptr) != int8 ||
         (int8 && !l.A_scale))
       return fail(RF_E_INVALID, "layer %d: exactly one of A and A_q (with A_scale), the same kind "
                   "for all layers", i);
     if ((l.A && !aligned(l.A, 16)) || (l.A_q && !aligned(l.A_q, 16)) || !aligned(l.b, 16) ||
-        !aligned(l.norm_w, 16) || !aligned(l.W_K, 16) || !aligned(l.W_V, 16) ||
-        !aligned(x_l_tail[i], 16))
+        !aligned(l.norm_w, 16) || !aligned(l.W_V, 16) || !aligned(x_l_tail[i], 16))
       return fail(RF_E_SHAPE, "layer %d: A, A_q, b, norm_w, W_V and the exact rows need 16-byte "
                   "alignment", i);
   }
@@ -433,20 +429,19 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
   const rf::FillWsLayout L = rf::fill_ws_layout(shape->d, d_in, shape->head_dim,
                                                 shape->n_kv_heads * shape->head_dim, c,
                                                 int8 ? rf::kWsInt8 : 0u);
-  const int gmax = n_layers < rf::kMaxGroup ? n_layers : rf::kMaxGroup;
+  const int gmax = n_layers < rf::kVsMaxGroup ? n_layers : rf::kVsMaxGroup;
   // the largest group the workspace holds: fixed part for that group + 2 blocks per layer
   int group = 0;
   for (int g = gmax; g >= 1; --g) {
-    const rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, g);
+    const rf::VsLayout V = vs_layout(c, shape->n_kv_heads, g);
     if (ws_bytes >= V.total_fixed + (size_t)2 * g * L.per_layer) { group = g; break; }
   }
   if (group == 0)
     return fail(RF_E_WORKSPACE, "workspace %zu bytes too small for one layer", ws_bytes);
-  rf::VsLayout V = vs_layout(L, c, shape->n_kv_heads, group);
+  rf::VsLayout V = vs_layout(c, shape->n_kv_heads, group);
   unsigned char* w = static_cast<unsigned char*>(ws);
-  V.exact = w + V.pred + (size_t)group * L.per_layer;
-  V.vn_pred = reinterpret_cast<float*>(w + V.vn_pred_off);
-  V.vn_exact = reinterpret_cast<float*>(w + V.vn_exact_off);
+  V.vn = reinterpret_cast<float*>(w + V.vn_off);
+  V.table = reinterpret_cast<rf::FillLayerPtrs*>(w + V.table_off);
 
   rf::FillPlan p = {};
   p.d = shape->d;
@@ -465,7 +460,7 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
   p.n_filled = (int)c;
   p.mpad = (int)((c + rf::kTile - 1) / rf::kTile * rf::kTile);
   p.status = reinterpret_cast<unsigned*>(w);
-  p.hbuf = reinterpret_cast<uint16_t*>(w + V.pred);
+  p.hbuf = reinterpret_cast<uint16_t*>(w + V.blocks);
   p.group = group;
   p.L = L;
   std::vector<rf::FillLayerPtrs> lp((size_t)n_layers);
@@ -478,11 +473,11 @@ rf_status ridgefill_value_scale(const rf_shape* shape, const uint16_t* x_S_tail,
       const unsigned char* f = static_cast<const unsigned char*>(l.folded);
       const uint16_t* P = reinterpret_cast<const uint16_t*>(f + F.P);
       lp[i] = {reinterpret_cast<const uint16_t*>(f + F.R), reinterpret_cast<const float*>(f + F.r),
-               l.norm_w, P, P + (size_t)p.kv * d_in, nullptr, nullptr, nullptr, nullptr, nullptr,
-               nullptr, reinterpret_cast<const float*>(f + F.c),
+               l.norm_w, nullptr, P + (size_t)p.kv * d_in, nullptr, nullptr, nullptr, nullptr,
+               nullptr, nullptr, reinterpret_cast<const float*>(f + F.c),
                reinterpret_cast<const float*>(f + F.kappa), reinterpret_cast<const float*>(f + F.g)};
-    } else {
-      lp[i] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, nullptr, nullptr, nullptr, nullptr, l.A_q,
+    } else {              // the value norms read W_V only (W_K is not needed)
+      lp[i] = {l.A, l.b, l.norm_w, nullptr, l.W_V, nullptr, nullptr, nullptr, nullptr, l.A_q,
                l.A_scale, nullptr, nullptr, nullptr};
     }
   }

@@ -237,6 +237,41 @@ def test_value_scale_factors_folded_layers(d, nl, nkv, hd, c, seed, opts):
     np.testing.assert_allclose(got, plain, rtol=3e-3)
 
 
+@pytest.mark.parametrize("folded", [False, True])
+def test_value_scale_many_layers_and_uneven_groups(folded):
+    # 40 layers in one group, more than the kernel arguments hold (the layer pointers then
+    # come from a table in the workspace), against the oracle; then through a workspace that
+    # holds 3 layers (groups of 3, the last of 1, whose exact-row blocks and norms sit at
+    # other offsets), which must give the same bits; W_K is not passed (it is not read)
+    nl, c = 40, 300
+    case = _case(256, nl, 2, 128, 600, 64, 0, 16, 62)
+    inp, xS_tail, exact = _vs_inputs(case, c)
+    shape = make_shape(case)
+    flags = 0
+    layers = [{k: v for k, v in lay.items() if k != "W_K"} for lay in inp["layers"]]
+    if folded:
+        bufs, st = fold_layers(case, inp)
+        assert st == B.RF_OK
+        layers = [dict(folded=bufs[l], norm_w=lay["norm_w"], W_V=lay["W_V"])
+                  for l, lay in enumerate(inp["layers"])]
+        flags = B.RF_MAPS_FOLDED
+    outs = []
+    for ws_layers in (nl, 3):
+        ws = torch.empty(B.ridgefill_value_scale_workspace_bytes(shape, c, ws_layers, flags),
+                         dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)
+        out = torch.full((nl, case.n_kv), float("nan"), device="cuda")
+        B.ridgefill_value_scale(shape, xS_tail, exact, layers, out, ws)
+        assert B.ridgefill_read_status(ws) == B.RF_OK
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+    got = outs[0].numpy().astype(np.float64)
+    want = _oracle_factors(case, inp, xS_tail, exact)
+    print(f"\n{nl} layers {'folded' if folded else 'plain'}: max rel "
+          f"{np.max(np.abs(got / want - 1)):.2e}", flush=True)
+    np.testing.assert_allclose(got, want, rtol=2e-3)
+
+
 def test_value_scale_folded_argument_errors():
     case = _case(256, 2, 2, 128, 600, 64, 0, 16, 61)
     inp, xS_tail, exact = _vs_inputs(case, 100)
