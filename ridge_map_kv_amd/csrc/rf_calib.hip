@@ -379,39 +379,59 @@ __device__ __forceinline__ int tr_off(int r, int col) {
   return r * 512 + ((tr_pos(col >> 3, r) << 4) | ((col & 7) << 1));
 }
 
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* op, int s, int col0, int lane) {
+// A transposed fragment of step s at columns col0 .. col0 + 31 (col0 = 128 W + 32 i) of an
+// operand: lane (g = (lane >> 4) & 3, p = lane & 15) reads rows r = 16 s + 8 (g >> 1) + (p >> 2)
+// and r + 4 at column col0 + 16 (g & 1) + 4 (p & 3).  tr_off of those splits into s * 8192, W *
+// 256 (the bits tr_pos leaves alone), + 2048 for the second row, and a per-lane term of i
+// alone: the eight per-lane terms (F with wf, T with wt and the operand's stage offset) are
+// computed once per tile, and the rest are immediates.
+struct TrOff {
+  uint32_t f[4], t[4];
+};
+__device__ __forceinline__ TrOff tr_offsets(int lane, int wf, int wt) {
   const int g = (lane >> 4) & 3, p = lane & 15;
-  const int col = col0 + (g & 1) * 16 + 4 * (p & 3);
-  const int r = 16 * s + 8 * (g >> 1) + (p >> 2);
+  TrOff o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * i + 2 * (g & 1) + ((p & 3) >> 1);
+    const uint32_t v = (8 * (g >> 1) + (p >> 2)) * 512 +
+                       ((tr_pos(c, p >> 2) << 4) | (((4 * (p & 3)) & 7) << 1));
+    o.f[i] = v + wf * 256;
+    o.t[i] = v + wt * 256 + kPipeOp;
+  }
+  return o;
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* at) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)(op + tr_off(r, col)));
+      (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)(at));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)(op + tr_off(r + 4, col)));
+      (lds_s16x4*)(const __attribute__((address_space(3))) unsigned char*)(at + 2048));
   struct Pair { s16x4 a, b; } pr = {lo, hi};
   return __builtin_bit_cast(bf16x8, pr);
 }
 
 __device__ __forceinline__ void read_frag_tr(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
-                                             int i, int s, int wf, int wt, int lane) {
+                                             int i, int s, const TrOff& to) {
   if (i < 4)
-    a[i] = tr_frag(st, s, wf * 128 + i * 32, lane);
+    a[i] = tr_frag(st + to.f[i] + s * 8192);
   else
-    b[i - 4] = tr_frag(st + kPipeOp, s, wt * 128 + (i - 4) * 32, lane);
+    b[i - 4] = tr_frag(st + to.t[i - 4] + s * 8192);
 }
 
 // As mfma16_read, with transposed fragment reads; with `dma`, load issues 8 .. 15 of the
 // slice the operand pointers hold go out after the even-numbered MFMAs, into stage dst.
 __device__ __forceinline__ void mfma16_read_tr(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
                                                const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
-                                               const unsigned char* st, int s, int wf, int wt, int lane,
+                                               const unsigned char* st, int s, const TrOff& to,
                                                bool dma, const DmaOperand& F, const DmaOperand& T,
                                                uint32_t dst, int wave) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     mfma_i(acc, a, b, i);
     if (dma && !(i & 1)) dma_issue(F, T, 8 + (i >> 1), 0, dst, wave);
-    if (i < 8) read_frag_tr(na, nb, st, i, s, wf, wt, lane);
+    if (i < 8) read_frag_tr(na, nb, st, i, s, to);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -481,16 +501,17 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  const TrOff to = tr_offsets(lane, wf, wt);
   bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_frag_tr(a0, b0, smem, i, 0, wf, wt, lane);
+  for (int i = 0; i < 8; ++i) read_frag_tr(a0, b0, smem, i, 0, to);
   // Loads split as in the fill pipeline: blocks 0..3 of each operand right after the
   // barrier that frees a stage, blocks 4..7 during the next slice's first step.  Each block
   // pointer moves on by one slice once its load has gone out.
   for (int kt = 0; kt < nk - 1; ++kt) {
     const unsigned char* cur = smem + (kt & 1) * kPipeStage;
     const bool pend = kt >= 1;                           // second half of slice kt + 1
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, pend, F, T,
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, to, pend, F, T,
                    base + ((kt + 1) & 1) * kPipeStage, wave);
     if (pend) {
 #pragma unroll
@@ -499,8 +520,8 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
         T.base[p] += tslice;
       }
     }
-    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, wave);
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, to, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, to, false, F, T, 0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const bool more = kt + 2 < nk;
@@ -510,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
     for (int i = 0; i < 16; ++i) {
       mfma_i(acc, a1, b1, i);
       if (more && !(i & 1)) dma_issue(F, T, i >> 1, 0, dst, wave);
-      if (i >= 8) read_frag_tr(a0, b0, nxt, i - 8, 0, wf, wt, lane);
+      if (i >= 8) read_frag_tr(a0, b0, nxt, i - 8, 0, to);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
@@ -523,9 +544,9 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
   }
   {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, false, F, T, 0, wave);
-    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, false, F, T, 0, wave);
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, to, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, to, false, F, T, 0, wave);
+    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, to, false, F, T, 0, wave);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }
