@@ -238,7 +238,10 @@ __global__ __launch_bounds__(kThreads, 1) void fill_map_kernel(FillKArgs a) {
 // upper-triangular factor R (A^T A = R^T R), written as 128-feature partials.  R is held
 // as R1 = diag(g)^-1 R with unit diagonal (bf16) and r as r1 = r / g: feature f of the
 // output is g_f (R1_f x_S + r1_f).  Row f of R
-// is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only.  A
+// is zero before column f, so tile ft reduces over columns 256 ft .. d_in - 1 only, and in
+// its first 256 columns skips the MFMAs of the 32-row blocks that are zero there
+// (gemm_mainloop_tri; the wave halves own interleaved blocks, so each 128-feature chunk's
+// sum of squares is the sum of both halves' shares).  A
 // workgroup takes the pair of tiles ft and nft - 1 - ft (the longer first): every pair
 // then reduces over d_in + 256 columns, so the workgroups are of equal length and the
 // short tiles share the fixed cost of a tile with long ones.  With nft odd the middle
@@ -312,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   __shared__ __attribute__((aligned(16))) float sr[kTile];
   __shared__ __attribute__((aligned(16))) float sg[kTile];
+  __shared__ float2 xch[2][4][32];      // the wf = 1 halves' chunk sums, per token
   const int nft = a.d_in / kTile;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,10 +333,10 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     const float my_r = Lc.b[f0 + tid];
     const float my_g = Lc.fg[f0 + tid];
     f32x16 acc[4][4];
-    if (half == 0)                                          // each ends with a barrier:
-      gemm_mainloop<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
+    if (half == 0)                                              // each ends with a barrier:
+      gemm_mainloop_tri<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
     else
-      gemm_mainloop<false>(acc, Fo, To, a.d_in - f0, smem);
+      gemm_mainloop_tri<false>(acc, Fo, To, a.d_in - f0, smem);
 
     // the next tile: the other half of this item (unless it is the middle tile of an odd
     // nft), else the first half of the next item
@@ -353,31 +357,45 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     sr[tid] = my_r;
     sg[tid] = my_g;
     __syncthreads();
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    // wave half wf holds F blocks 2 m + wf: blocks m = 0, 1 lie in the tile's first 128-feature
+    // chunk, m = 2, 3 in its second; the wf = 1 halves hand their sums to the wf = 0 ones
+    float ss0[4] = {0.f, 0.f, 0.f, 0.f}, ss1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + wf * 128 + m * 32 + q * 8 + h * 4);
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + wf * 128 + m * 32 + q * 8 + h * 4);
+        const int fr = (2 * m + wf) * 32 + q * 8 + h * 4;
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + fr);
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + fr);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           const float v0 = (acc[m][n][q * 4 + 0] + rv.x) * gv.x;
           const float v1 = (acc[m][n][q * 4 + 1] + rv.y) * gv.y;
           const float v2 = (acc[m][n][q * 4 + 2] + rv.z) * gv.z;
           const float v3 = (acc[m][n][q * 4 + 3] + rv.w) * gv.w;
-          ss[n] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+          const float t = v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+          if (m < 2) ss0[n] += t; else ss1[n] += t;
         }
       }
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) ss[n] += __shfl_xor(ss[n], 32);
-    if (h == 0) {
-      const int chunk = (f0 + wf * 128) >> 7;
+    for (int n = 0; n < 4; ++n) {
+      ss0[n] += __shfl_xor(ss0[n], 32);
+      ss1[n] += __shfl_xor(ss1[n], 32);
+    }
+    if (wf == 1 && h == 0) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) xch[wt][n][lane & 31] = make_float2(ss0[n], ss1[n]);
+    }
+    __syncthreads();
+    if (wf == 0 && h == 0) {
+      const int chunk = f0 >> 7;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
-        ssq[(size_t)chunk * a.mpad + tok] = ss[n];        // chunk-major: coalesced
+        const float2 o = xch[wt][n][lane & 31];
+        ssq[(size_t)chunk * a.mpad + tok] = ss0[n] + o.x;          // chunk-major: coalesced
+        ssq[(size_t)(chunk + 1) * a.mpad + tok] = ss1[n] + o.y;
       }
     }
     if (!more) break;

@@ -127,6 +127,7 @@ __device__ __forceinline__ bf16x8 i8_to_bf16x8(u32x2 q) {
 // offsets computed per read, and 20 fewer registers.)
 struct FragOff {
   uint32_t o[4][2];
+  uint32_t a[4];        // TRI: this wave half's F-read offsets, o[s][wf] + 4096 wf
 };
 __device__ __forceinline__ FragOff frag_off(int lane) {
   FragOff f;
@@ -139,15 +140,25 @@ __device__ __forceinline__ FragOff frag_off(int lane) {
   return f;
 }
 
-// Fragment i (0..3: F rows, 4..7: T rows) of 16-wide step s of a stage.
-template <int FQ = 0>
+// TRI: the F blocks of wave half wf are 2 m + wf, of parity wf: o[s][wf] = o[s][0] ^ 64 wf (the
+// chunk term's bit 2), plus the block's odd 4096 bytes.
+__device__ __forceinline__ void frag_off_tri(FragOff& f, int wf) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f.a[s] = (f.o[s][0] ^ (64u * wf)) + 4096u * wf;
+}
+
+// Fragment i (0..3: F rows, 4..7: T rows) of 16-wide step s of a stage.  TRI: wave half wf
+// owns the F blocks 2 m + wf (m = 0..3) instead of 4 wf + m, rows interleaved by 32.
+template <int FQ = 0, bool TRI = false>
 __device__ __forceinline__ void read_frag(bf16x8 (&a)[4], bf16x8 (&b)[4], const unsigned char* st,
                                           int i, int s, int wf, int wt, int lane, const FragOff& fo) {
   // Read order a0 b0 b1 b2 b3 a1 a2 a3: the next step's MFMAs (m-major: a0 with b0..b3,
   // then a1 ...) need the reads in this order, so each MFMA waits on a read issued at least
   // five slots before it, instead of the first four MFMAs waiting on the last four reads.
   i = i == 0 ? 0 : i <= 4 ? i + 3 : i - 4;
-  if (i < 4) {
+  if (TRI && i < 4) {
+    a[i] = *reinterpret_cast<const bf16x8*>(st + fo.a[s] + 2 * i * 4096);
+  } else if (i < 4) {
     const int blk = wf * 4 + i;
     if (FQ)
       a[i] = i8_to_bf16x8(*reinterpret_cast<const u32x2*>(st + i8_off(blk * 32 + (lane & 31), s) +
@@ -187,7 +198,8 @@ template <int FQ> constexpr int kIssues = FQ ? 12 : 16;   // load issues per wav
 // 16 MFMAs on (a, b); after each of the first 8, one fragment of step s of stage st is
 // read into (na, nb).  With `dma`, the second half of the slice's load issues (j0 onwards)
 // at byte offset kb go out after the even-numbered MFMAs, into the stage at LDS address dst.
-template <int FQ = 0>
+// MACT < 4: only the MFMAs of F blocks m < MACT are issued (the others would multiply zeros).
+template <int FQ = 0, bool TRI = false, int MACT = 4>
 __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
                                             const bf16x8 (&b)[4], bf16x8 (&na)[4], bf16x8 (&nb)[4],
                                             const unsigned char* st, int s, int wf, int wt, int lane,
@@ -196,9 +208,9 @@ __device__ __forceinline__ void mfma16_read(f32x16 (&acc)[4][4], const bf16x8 (&
                                             int wave) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    mfma_i(acc, a, b, i);
+    if ((i >> 2) < MACT) mfma_i(acc, a, b, i);
     if (dma && !(i & 1) && (i >> 1) < kIssues<FQ> / 2) dma_issue<FQ>(F, T, j0 + (i >> 1), kb, dst, wave);
-    if (i < 8) read_frag<FQ>(na, nb, st, i, s, wf, wt, lane, fo);
+    if (i < 8) read_frag<FQ, TRI>(na, nb, st, i, s, wf, wt, lane, fo);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -235,7 +247,7 @@ __device__ __forceinline__ void gemm_prologue(const DmaOperand& F, const DmaOper
 // kt + 2 exists and the first half of its loads goes out in step 0.  With both flags fixed at
 // compile time the steady-state body carries no load conditions, which measurably shortens
 // the issue of the 64 MFMAs of a slice.
-template <bool REV, bool PEND, bool MORE, int FQ = 0>
+template <bool REV, bool PEND, bool MORE, int FQ = 0, bool TRI = false, int MACT = 4>
 __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4], bf16x8 (&b0)[4],
                                            bf16x8 (&a1)[4], bf16x8 (&b1)[4], const DmaOperand& F,
                                            const DmaOperand& T, unsigned char* smem, uint32_t base,
@@ -245,10 +257,10 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4],
   const unsigned char* cur = smem + (kt & 1) * kPipeStage;
   const int kbp = (kt + 1) * kStep;
   const uint32_t dstp = base + ((kt + 1) & 1) * kPipeStage;
-  mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, fo, PEND, F, T, kbp, dstp,
-                  kIssues<FQ> / 2, wave);
-  mfma16_read<FQ>(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
-  mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
+  mfma16_read<FQ, TRI, MACT>(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, fo, PEND, F, T, kbp, dstp,
+                             kIssues<FQ> / 2, wave);
+  mfma16_read<FQ, TRI, MACT>(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
+  mfma16_read<FQ, TRI, MACT>(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slice kt + 1, the only one in flight
   __syncthreads();                                       // ... landed for every wave; slice kt read
   const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
@@ -256,9 +268,9 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4],
   const int kb = (kt + 2) * kStep;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    mfma_i(acc, a1, b1, i);
+    if ((i >> 2) < MACT) mfma_i(acc, a1, b1, i);
     if (MORE && !(i & 1) && (i >> 1) < kIssues<FQ> / 2) dma_issue<FQ>(F, T, i >> 1, kb, dst, wave);
-    if (i >= 8) read_frag<FQ>(a0, b0, nxt, i - 8, 0, wf, wt, lane, fo);
+    if (i >= 8) read_frag<FQ, TRI>(a0, b0, nxt, i - 8, 0, wf, wt, lane, fo);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -316,6 +328,69 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], const DmaOper
     mfma16_read<FQ>(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
+  }
+  __syncthreads();
+}
+
+// The main loop of an upper-triangular F operand (the folded layers' norm GEMM): F rows
+// f0 .. f0 + 255 are zero left of their diagonal, and the tile's reduction starts (or, with
+// REV, ends) at column f0.  The first four slices from column f0 then hold the triangle's
+// diagonal block: in its slice s (columns f0 + 64 s ..), 32-row block b is zero for
+// b > 2 s + 1.  With the F blocks of the two wave halves interleaved (TRI: blocks 2 m + wf),
+// both halves need exactly the blocks m <= s there, so each diagonal slice issues only the
+// MFMAs of m < s + 1 and the halves stay balanced: 96 of a tile's MFMAs are skipped, 6 of
+// every 16 in the diagonal block (whose zeros would otherwise be multiplied).  The result
+// is that of the full loop (the skipped products are of zero blocks).  K >= 256.
+template <bool REV>
+__device__ __forceinline__ void gemm_mainloop_tri(f32x16 (&acc)[4][4], const DmaOperand& F,
+                                                  const DmaOperand& T, int K, unsigned char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wave >> 1, wt = wave & 1;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+
+  const int nk = K / kPipeBK;
+  const uint32_t base = lds_addr(smem);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");     // slice 0 landed: slice 1 may be pending
+  __syncthreads();
+
+  FragOff fo = frag_off(lane);
+  frag_off_tri(fo, wf);
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_frag<0, true>(a0, b0, smem, i, 0, wf, wt, lane, fo);
+  if (!REV) {            // diagonal slices first: MACT 1, 2, 3, then 4
+    gemm_slice<REV, false, true, 0, true, 1>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, fo, wave);
+    gemm_slice<REV, true, true, 0, true, 2>(acc, a0, b0, a1, b1, F, T, smem, base, 1, wf, wt, lane, fo, wave);
+    if (nk == 4) {
+      gemm_slice<REV, true, false, 0, true, 3>(acc, a0, b0, a1, b1, F, T, smem, base, 2, wf, wt, lane, fo, wave);
+    } else {
+      gemm_slice<REV, true, true, 0, true, 3>(acc, a0, b0, a1, b1, F, T, smem, base, 2, wf, wt, lane, fo, wave);
+      for (int kt = 3; kt < nk - 2; ++kt)
+        gemm_slice<REV, true, true, 0, true, 4>(acc, a0, b0, a1, b1, F, T, smem, base, kt, wf, wt, lane, fo, wave);
+      gemm_slice<REV, true, false, 0, true, 4>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 2, wf, wt, lane, fo, wave);
+    }
+  } else {               // diagonal slices last: MACT 4, ..., then 3, 2 and (the last slice) 1
+    gemm_slice<REV, false, true, 0, true, 4>(acc, a0, b0, a1, b1, F, T, smem, base, 0, wf, wt, lane, fo, wave);
+    for (int kt = 1; kt < nk - 3; ++kt)
+      gemm_slice<REV, true, true, 0, true, 4>(acc, a0, b0, a1, b1, F, T, smem, base, kt, wf, wt, lane, fo, wave);
+    gemm_slice<REV, true, true, 0, true, 3>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 3, wf, wt, lane, fo, wave);
+    gemm_slice<REV, true, false, 0, true, 2>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 2, wf, wt, lane, fo, wave);
+  }
+  {
+    constexpr int kLast = REV ? 1 : 4;
+    const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
+    mfma16_read<0, true, kLast>(acc, a0, b0, a1, b1, cur, 1, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
+    mfma16_read<0, true, kLast>(acc, a1, b1, a0, b0, cur, 2, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
+    mfma16_read<0, true, kLast>(acc, a0, b0, a1, b1, cur, 3, wf, wt, lane, fo, false, F, T, 0, 0, 0, wave);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i >> 2) < kLast) mfma_i(acc, a1, b1, i);
   }
   __syncthreads();
 }
