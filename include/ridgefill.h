@@ -10,7 +10,10 @@
  *  - Pointers marked "device" point to GPU memory the caller allocated; pointers
  *    marked "host" point to CPU memory.  The library allocates no device memory,
  *    keeps no device state between calls and creates no streams (the streamed fill
- *    creates five HIP events per host thread and device on first use and reuses them).
+ *    creates five HIP events per host thread and device on first use and reuses them;
+ *    ridgefill_fill_noalloc works in a fixed array of RIDGEFILL_NOALLOC_SCRATCH_BYTES
+ *    that is part of the library's device code, one per device, whose contents the
+ *    next such call on that device overwrites).
  *    Every buffer it needs beyond inputs and outputs is a caller-owned workspace whose
  *    size a *_workspace_bytes / *_state_bytes query returns.
  *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round-to-nearest-
@@ -165,9 +168,10 @@ rf_status ridgefill_select_rows(const float* scores, int64_t P, int64_t k, uint8
  *               n_filled, 1); a larger workspace (up to the value for n_layers) lets
  *               more layers share one launch.  Its first 256 bytes hold the status.
  * Computation: bf16 inputs, fp32 accumulation, x_hat and the RMS in fp32, one bf16
- * rounding of x_hat * norm_w, one bf16 rounding of the stored k and v.  An int8 map is
- * expanded exactly (integer codes as bf16) into a staging area of the workspace and its
- * row scale is applied to the fp32 product, so it adds no rounding of its own.  All
+ * rounding of x_hat * norm_w, one bf16 rounding of the stored k and v.  An int8 map's
+ * codes are read by the map GEMM as they are and turned into bf16 numbers between LDS and
+ * the matrix cores (exactly: |q| <= 127), and its row scale is applied to the fp32
+ * product, so it adds no rounding of its own.  All
  * layers of one call must agree on which optional parts they use (int8 or bf16 map,
  * key norm); v_scale may be set per layer.
  * ------------------------------------------------------------------------------ */
@@ -179,7 +183,7 @@ rf_status ridgefill_fill(const rf_shape* shape, const uint16_t* x_S, int64_t N, 
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Map variants for the workspace query: RF_MAPS_INT8 when the layers carry A_q/A_scale
- * (the workspace then holds a bf16 expansion of each layer's codes), RF_MAPS_STREAMED for
+ * (the same workspace as for bf16 maps), RF_MAPS_STREAMED for
  * ridgefill_fill_streamed (two landing slots per layer), RF_MAPS_FOLDED when the layers
  * carry folded forms (no predicted-input buffer: a few MB per layer).  Returns 0 on
  * invalid input.
