@@ -106,10 +106,10 @@ __device__ __forceinline__ void decode_tile(int tile, int ntt, int nft, int& g, 
   ft = fg * kFeatGroup + (within - tt * gsz);
 }
 
-// Output staging: after the main loop the 128 KB of LDS hold one 256 (rows) x 256
-// (features) bf16 tile, 512 bytes per row, 16-byte chunk c of row r stored at chunk
-// c ^ (r & 31).  Lanes write their runs of four features (8 bytes); the tile then leaves as
-// 16-byte vectors, 32 lanes per 512-byte row segment.
+// Map kernel output staging: after the main loop the 128 KB of LDS hold one 256 (rows) x
+// 256 (features) bf16 tile, 512 bytes per row, 16-byte chunk c of row r stored at chunk
+// c ^ (r & 31).  Lanes write their runs of four features (8 bytes); the tile then leaves
+// as 16-byte vectors, 32 lanes per 512-byte row segment.
 __device__ __forceinline__ int stage_off(int r, int f) {
   return r * 512 + ((((f >> 3) ^ (r & 31)) << 4) | ((f & 7) << 1));
 }
@@ -120,6 +120,23 @@ __device__ __forceinline__ void stage_put4(unsigned char* smem, int r, int f, fl
   o.x = pack_bf16x2(v0, v1);
   o.y = pack_bf16x2(v2, v3);
   *reinterpret_cast<u32x2*>(smem + stage_off(r, f)) = o;
+}
+
+// The kv kernel's outputs go from the accumulators straight to their page slots (through
+// the LDS, as in the map kernel, was 1% slower).  In an MFMA result block, half-wave h
+// holds features 8 q + 4 h .. 8 q + 4 h + 3 of its row (lane & 31), q = 0..3.  For a pair
+// q = 2 p, 2 p + 1, swapping half 0's q = 2 p + 1 run with half 1's q = 2 p run
+// (v_permlane32_swap, which exchanges lanes 32..63 of its first operand with lanes 0..31 of
+// its second) leaves half 0 with features 16 p .. 16 p + 7 and half 1 with 16 p + 8 ..
+// 16 p + 15 of the same row: one 16-byte store per lane, 32 contiguous bytes per row.
+// x0, x1: the q = 2 p run as bf16 pairs, y0, y1: the q = 2 p + 1 run; row: the row's feature
+// 16 p (bf16 elements).
+__device__ __forceinline__ void store_run_pair(uint16_t* row, int h, uint32_t x0, uint32_t x1,
+                                               uint32_t y0, uint32_t y1, bool valid) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+  const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+  if (valid) *reinterpret_cast<u32x4*>(row + 8 * h) = v;
 }
 
 __device__ __forceinline__ float lo16(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
@@ -308,9 +325,10 @@ __device__ __forceinline__ void norm_prologue(const DmaOperand& Fo, const DmaOpe
 // items blockIdx.x, blockIdx.x + gridDim.x, ..., each one or two tiles.  The loads of a
 // tile's first two slices are issued as soon as the previous tile's main loop has left
 // the LDS, before that tile's epilogue, so the epilogue arithmetic and stores overlap
-// them.  (The map and kv kernels, whose epilogues stage their outputs through that LDS,
-// stay one tile per workgroup.)  gridDim.x is a multiple of 8 or equal to n_items, so
-// item i runs on XCD i % 8 and xcd_remap's tile ranges hold.
+// them.  (The map kernel, whose epilogue stages its outputs through that LDS, and the kv
+// kernel, whose epilogue spills registers in such a loop, stay one tile per workgroup.)
+// gridDim.x is a multiple of 8 or equal to n_items, so item i runs on XCD i % 8 and
+// xcd_remap's tile ranges hold.
 __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
   __shared__ __attribute__((aligned(16))) float sr[kTile];
@@ -613,28 +631,19 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
         for (int e = 0; e < 16; ++e) acc[m][n][e] *= vm;
       }
     }
+    // straight to the token's page slot (off < 0: the row is not stored)
+    const long long off = rowoff[tl];
+    uint16_t* row = (isK ? Lp.kp : Lp.vp) + off + (isK ? fw : fw - a.kv);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        stage_put4(smem, tl, wf * 128 + m * 32 + q * 8 + h * 4, acc[m][n][q * 4 + 0],
-                   acc[m][n][q * 4 + 1], acc[m][n][q * 4 + 2], acc[m][n][q * 4 + 3]);
-  }
-  __syncthreads();
-  // 16-byte chunk c of every valid row goes to its page slot; chunks 0..15 and 16..31 are
-  // the tile's two 128-feature halves, each all K or all V.
-  const int c = tid & 31;
-  const int fh = f0 + (c >> 4) * 128;
-  uint16_t* base = fh < a.kv ? Lp.kp : Lp.vp;
-  const int fo = (fh < a.kv ? fh : fh - a.kv) + (c & 15) * 8;
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) {
-    const int r = (tid >> 5) + 8 * i;
-    const long long off = rowoff[r];
-    if (off >= 0) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
-      *reinterpret_cast<u32x4*>(base + off + fo) = v;
-    }
+      for (int p = 0; p < 2; ++p) {
+        const int e = 8 * p;                   // runs q = 2 p and 2 p + 1
+        store_run_pair(row + m * 32 + 16 * p, h, pack_bf16x2(acc[m][n][e], acc[m][n][e + 1]),
+                       pack_bf16x2(acc[m][n][e + 2], acc[m][n][e + 3]),
+                       pack_bf16x2(acc[m][n][e + 4], acc[m][n][e + 5]),
+                       pack_bf16x2(acc[m][n][e + 6], acc[m][n][e + 7]), off >= 0);
+      }
   }
 }
 
