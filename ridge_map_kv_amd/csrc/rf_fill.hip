@@ -130,13 +130,16 @@ __device__ __forceinline__ void stage_put4(unsigned char* smem, int r, int f, fl
 // its second) leaves half 0 with features 16 p .. 16 p + 7 and half 1 with 16 p + 8 ..
 // 16 p + 15 of the same row: one 16-byte store per lane, 32 contiguous bytes per row.
 // x0, x1: the q = 2 p run as bf16 pairs, y0, y1: the q = 2 p + 1 run; row: the row's feature
-// 16 p (bf16 elements).
+// 16 p (bf16 elements).  The page pools are global memory and the store is issued as such
+// (through the generic layer-table pointer it would be a flat store, which also counts
+// against the LDS reads' wait counter; measured the same).
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 __device__ __forceinline__ void store_run_pair(uint16_t* row, int h, uint32_t x0, uint32_t x1,
                                                uint32_t y0, uint32_t y1, bool valid) {
   const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
   const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
   const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-  if (valid) *reinterpret_cast<u32x4*>(row + 8 * h) = v;
+  if (valid) *(global_u32x4*)(row + 8 * h) = v;
 }
 
 __device__ __forceinline__ float lo16(uint32_t x) { return bf16_to_f32(x & 0xffffu); }
