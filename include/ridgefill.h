@@ -267,29 +267,41 @@ rf_status ridgefill_fill_noalloc(const rf_shape* shape, const uint16_t* x_S, int
  * positive definite, so d_in <= d, and d_in must be a multiple of 256.
  *
  * ridgefill_fold_maps computes every given layer's folded buffer from its plain fields
- * (A bf16, b, norm_w, W_K, W_V; int8 maps are not accepted):
+ * (A bf16, or A_q int8 with A_scale; b, norm_w, W_K, W_V).  All layers of a call carry
+ * bf16 maps or all carry int8 maps:
  *   folded     host array [n_layers] of device pointers, each >= ridgefill_fold_bytes
  *              bytes and 256-byte aligned
- *   ws         device workspace >= ridgefill_fold_workspace_bytes(shape); its first 256
- *              bytes hold the status: RF_E_NOT_SPD when some layer's A^T A had a
+ *   ws         device workspace >= ridgefill_fold_workspace_bytes(shape) for bf16 maps,
+ *              >= ridgefill_fold_workspace_bytes_maps(shape, 1, RF_MAPS_INT8) for int8
+ *              maps (RF_E_WORKSPACE otherwise, before anything is enqueued); its first
+ *              256 bytes hold the status: RF_E_NOT_SPD when some layer's A^T A had a
  *              non-positive pivot (A not of full column rank; that layer's buffer is
  *              then not usable).  A workspace of ridgefill_fold_workspace_bytes_ex(shape, G)
- *              bytes folds G layers side by side (their Cholesky factorizations share
- *              one sequence of launches); a smaller one folds as many as it holds, at
- *              least one (at most 64) at a time.  The results do not depend on G.
+ *              bytes (ridgefill_fold_workspace_bytes_maps(shape, G, RF_MAPS_INT8) for int8
+ *              maps) folds G layers side by side (their Cholesky factorizations share one
+ *              sequence of launches); a smaller one folds as many as it holds, at least
+ *              one (at most 64) at a time.  The results do not depend on G.
  * Arithmetic: P = bf16-split(W diag(w)) times A on the matrix cores (products exact,
  * fp32 accumulation, one bf16 rounding of P); A^T A with exact products and fp32
  * accumulation; Cholesky, r and kappa in fp64; R rounded to bf16 once; c in fp64
- * rounded to fp32.
+ * rounded to fp32.  An int8 map A = diag(A_scale) A_q folds through its codes, which
+ * bf16 holds exactly: P = bf16-split(W diag(w A_scale)) times A_q, and
+ * A^T A = A_q^T diag(A_scale^2) A_q with the scaled side split into two bf16 parts
+ * (about 2^-17 of each entry), as above otherwise; the buffer is the same as from the
+ * bf16 map A_q * A_scale up to those roundings.
  * Folded layers work with ridgefill_fill and, from host memory, ridgefill_fill_streamed;
- * all layers of a fill call must be folded or none.  ridgefill_value_scale always uses
- * the plain fields.
+ * all layers of a fill call must be folded or none.  ridgefill_value_scale takes folded
+ * layers too (see there).
  * ------------------------------------------------------------------------------ */
 size_t ridgefill_fold_bytes(const rf_shape* shape);
 size_t ridgefill_fold_workspace_bytes(const rf_shape* shape);
 /* Workspace that folds layers_at_once (>= 1) layers side by side; 0 for a shape that
  * cannot be folded or layers_at_once < 1. */
 size_t ridgefill_fold_workspace_bytes_ex(const rf_shape* shape, int32_t layers_at_once);
+/* The same for the map kind of the layers: map_flags 0 (bf16 maps, as the _ex query) or
+ * RF_MAPS_INT8 (int8 maps, which take a second operand slot per layer); 0 for other flags. */
+size_t ridgefill_fold_workspace_bytes_maps(const rf_shape* shape, int32_t layers_at_once,
+                                           uint32_t map_flags);
 rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int32_t n_layers,
                               void* const* folded, void* ws, size_t ws_bytes, void* stream);
 

@@ -31,6 +31,7 @@ EXPORTED = [
     "ridgefill_fold_bytes",
     "ridgefill_fold_workspace_bytes",
     "ridgefill_fold_workspace_bytes_ex",
+    "ridgefill_fold_workspace_bytes_maps",
     "ridgefill_fold_maps",
     "ridgefill_select_workspace_bytes",
     "ridgefill_select_rows",
@@ -115,6 +116,7 @@ def lib() -> C.CDLL:
         "ridgefill_fold_bytes": (sz, [C.POINTER(rf_shape)]),
         "ridgefill_fold_workspace_bytes": (sz, [C.POINTER(rf_shape)]),
         "ridgefill_fold_workspace_bytes_ex": (sz, [C.POINTER(rf_shape), i32]),
+        "ridgefill_fold_workspace_bytes_maps": (sz, [C.POINTER(rf_shape), i32, C.c_uint32]),
         "ridgefill_fold_maps": (st, [C.POINTER(rf_shape), C.POINTER(rf_layer), i32,
                                      C.POINTER(vp), vp, sz, vp]),
         "ridgefill_select_workspace_bytes": (sz, [i64]),
@@ -243,6 +245,12 @@ def ridgefill_fold_workspace_bytes(shape: rf_shape) -> int:
 def ridgefill_fold_workspace_bytes_ex(shape: rf_shape, layers_at_once: int) -> int:
     """Fold workspace for layers_at_once layers folded side by side."""
     return int(lib().ridgefill_fold_workspace_bytes_ex(C.byref(shape), layers_at_once))
+
+
+def ridgefill_fold_workspace_bytes_maps(shape: rf_shape, layers_at_once: int, map_flags: int) -> int:
+    """Fold workspace for layers_at_once layers side by side, for bf16 maps (map_flags 0)
+    or int8 maps (RF_MAPS_INT8)."""
+    return int(lib().ridgefill_fold_workspace_bytes_maps(C.byref(shape), layers_at_once, map_flags))
 
 
 def ridgefill_fold_maps(shape: rf_shape, layers: list[dict], folded: list, ws, stream=None) -> None:

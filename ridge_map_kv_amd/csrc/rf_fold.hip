@@ -21,6 +21,11 @@
 //   g   = A^T b,  c = W b,  |b|^2  fp64 accumulation in a fixed order
 //   r   = L^-1 g                   blocked forward substitution (right-looking), fp64
 //   kappa = |b|^2 - |r|^2          fp64;  r1 = r / g
+// An int8 map A = diag(s) Aq (section "Ridge map ...", map-size paragraph) folds with its
+// codes, which bf16 holds exactly: W diag(w) A = W diag(w s) Aq, so Wx splits W diag(w s)
+// (each product formed in fp64) and At holds [Aq^T | Aq^T]; A^T A = Aq^T diag(s^2) Aq is
+// At times [C_hi | C_lo]^T, C[j][k] = s_k^2 Aq[k][j] split into two bf16 parts (~2^-17),
+// over 2 d; A^T b = Aq^T (s b).
 // Layers go in groups as large as the workspace holds: the GEMMs layer by layer, then the
 // group's Cholesky factorizations and substitutions side by side.  Every launch is on the
 // caller's stream.
@@ -43,12 +48,14 @@ FoldLayout fold_layout(int d_in, int kv) {
   return F;
 }
 
-FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par) {
+FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par, bool int8) {
   FoldWsLayout W;
-  W.slots = n_par < kFoldGemmSlots ? n_par : kFoldGemmSlots;
+  const int most = int8 ? kFoldGemmSlots / 2 : kFoldGemmSlots;
+  W.slots = n_par < most ? n_par : most;
+  W.int8 = int8 ? 1 : 0;
   W.At = kStatusBytes;
   W.at_bytes = align256((size_t)d_in * 2 * d * 2);
-  W.Wx = W.At + (size_t)W.slots * W.at_bytes;
+  W.Wx = W.At + (size_t)W.slots * (int8 ? 2 : 1) * W.at_bytes;
   W.wx_bytes = align256((size_t)2 * kv * 2 * d * 2);
   W.blocks = W.Wx + (size_t)W.slots * W.wx_bytes;
   W.H64 = 0;
@@ -84,17 +91,56 @@ __global__ __launch_bounds__(256) void fold_transpose_kernel(const uint16_t* A, 
   }
 }
 
-// Wx[i] = [hi | lo] of row i of [W_K; W_V] diag(w).
+// int8 map: At[i][k] = At[i][d + k] = Aq[k][i] (exact in bf16) and Ct[i] = [hi | lo] of
+// s_k^2 Aq[k][i], through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(256) void fold_transpose_q_kernel(const int8_t* Aq, const float* As,
+                                                               int d, int d_in, uint16_t* At,
+                                                               uint16_t* Ct) {
+  __shared__ int8_t t[64][68];
+  __shared__ double s2[64];
+  const int i0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    t[r][c] = Aq[(size_t)(k0 + r) * d_in + i0 + c];
+  }
+  if (threadIdx.x < 64) {
+    const double sk = (double)As[k0 + threadIdx.x];
+    s2[threadIdx.x] = sk * sk;
+  }
+  __syncthreads();
+  const size_t ld = (size_t)2 * d;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;   // r: i within the tile, c: k within the tile
+    const int q = t[c][r];
+    const uint16_t v = (uint16_t)f32_to_bf16((float)q);
+    const size_t o = (size_t)(i0 + r) * ld + k0 + c;
+    At[o] = v;
+    At[o + d] = v;
+    const double cv = s2[c] * (double)q;
+    const uint32_t hi = f32_to_bf16((float)cv);
+    Ct[o] = (uint16_t)hi;
+    Ct[o + d] = (uint16_t)f32_to_bf16((float)(cv - (double)bf16_to_f32(hi)));
+  }
+}
+
+// Wx[i] = [hi | lo] of row i of [W_K; W_V] diag(w) (int8 map: diag(w As)).
 __global__ void fold_wsplit_kernel(const uint16_t* WK, const uint16_t* WV, const uint16_t* w,
-                                   int kv, int d, uint16_t* Wx) {
+                                   const float* As, int kv, int d, uint16_t* Wx) {
   const size_t n = (size_t)2 * kv * d;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (size_t)gridDim.x * blockDim.x) {
     const int i = (int)(e / d), k = (int)(e - (size_t)i * d);
     const uint16_t wb = i < kv ? WK[(size_t)i * d + k] : WV[(size_t)(i - kv) * d + k];
     const float v = bf16_to_f32(wb) * bf16_to_f32(w[k]);          // exact: 8 x 8 bits
-    const uint32_t hi = f32_to_bf16(v);
-    const uint32_t lo = f32_to_bf16(v - bf16_to_f32(hi));         // v - hi exact in fp32
+    uint32_t hi, lo;
+    if (As) {
+      const double vs = (double)v * (double)As[k];
+      hi = f32_to_bf16((float)vs);
+      lo = f32_to_bf16((float)(vs - (double)bf16_to_f32(hi)));
+    } else {
+      hi = f32_to_bf16(v);
+      lo = f32_to_bf16(v - bf16_to_f32(hi));                     // v - hi exact in fp32
+    }
     Wx[(size_t)i * 2 * d + k] = (uint16_t)hi;
     Wx[(size_t)i * 2 * d + d + k] = (uint16_t)lo;
   }
@@ -171,19 +217,23 @@ __global__ __launch_bounds__(kThreads, 1) void fold_gemm_kernel(NtGemmArgs a) {
     }
 }
 
-// One wave per output: rows 0 .. d_in-1 give g[i] = sum_k A[k][i] b[k] (from At), rows
-// d_in .. d_in + 2kv - 1 give c[j] = sum_k W[j][k] w[k] b[k]; lane-strided fp64 partial
-// sums, then a fixed xor tree.
-__global__ __launch_bounds__(256) void fold_gemv_kernel(const uint16_t* At, const uint16_t* WK,
-                                                        const uint16_t* WV, const uint16_t* w,
-                                                        const float* b, int d, int d_in, int kv,
-                                                        double* g, float* c) {
+// One wave per output: rows 0 .. d_in-1 give g[i] = sum_k A[k][i] b[k] (from At; an int8
+// map's At holds the codes, and the scale multiplies b), rows d_in .. d_in + 2kv - 1 give
+// c[j] = sum_k W[j][k] w[k] b[k]; lane-strided fp64 partial sums, then a fixed xor tree.
+__global__ __launch_bounds__(256) void fold_gemv_kernel(const uint16_t* At, const float* As,
+                                                        const uint16_t* WK, const uint16_t* WV,
+                                                        const uint16_t* w, const float* b, int d,
+                                                        int d_in, int kv, double* g, float* c) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= d_in + 2 * kv) return;
   double s = 0.0;
   if (row < d_in) {
     const uint16_t* a = At + (size_t)row * 2 * d;
-    for (int k = lane; k < d; k += 64) s += (double)bf16_to_f32(a[k]) * (double)b[k];
+    if (As)
+      for (int k = lane; k < d; k += 64)
+        s += (double)bf16_to_f32(a[k]) * ((double)As[k] * (double)b[k]);
+    else
+      for (int k = lane; k < d; k += 64) s += (double)bf16_to_f32(a[k]) * (double)b[k];
   } else {
     const int j = row - d_in;
     const uint16_t* wr = j < kv ? WK + (size_t)j * d : WV + (size_t)(j - kv) * d;
@@ -309,25 +359,34 @@ hipError_t launch_fold(int d, int d_in, int kv, const FoldLayerIn* layers, int G
   auto blk = [&](int l) { return s + W.blocks + (size_t)l * W.per_layer; };
   hipError_t e;
   // the GEMMs of up to W.slots layers per launch, each layer with its own operand slot
+  // int8: layer j's codes in At slot 2 j, its [C_hi | C_lo] in slot 2 j + 1; A^T A over 2 d
+  const int aslots = W.int8 ? 2 : 1;
+  const int64_t sA = (int64_t)(aslots * W.at_bytes / 2);       // elements per layer
+  const uint16_t* Ct0 = W.int8 ? At0 + W.at_bytes / 2 : At0;
   for (int l0 = 0; l0 < G; l0 += W.slots) {
     const int ns = G - l0 < W.slots ? G - l0 : W.slots;
-    NtGemmArgs pa = {Wx0, At0, (int64_t)(W.wx_bytes / 2), (int64_t)(W.at_bytes / 2), {},
+    NtGemmArgs pa = {Wx0, At0, (int64_t)(W.wx_bytes / 2), sA, {},
                      2 * (int64_t)d, 2 * (int64_t)d, d_in, 2 * d, 2 * kv / kTile, d_in / kTile,
                      0, 0};
-    NtGemmArgs ha = {At0, At0, (int64_t)(W.at_bytes / 2), (int64_t)(W.at_bytes / 2), {},
-                     2 * (int64_t)d, 2 * (int64_t)d, d_in, d, d_in / kTile, d_in / kTile, 1, 1};
+    NtGemmArgs ha = {At0, Ct0, sA, sA, {}, 2 * (int64_t)d, 2 * (int64_t)d, d_in,
+                     W.int8 ? 2 * d : d, d_in / kTile, d_in / kTile, 1, 1};
     for (int j = 0; j < ns; ++j) {
       const int l = l0 + j;
       const FoldLayerIn& in = layers[l];
       unsigned char* o = static_cast<unsigned char*>(out[l]);
-      uint16_t* At = reinterpret_cast<uint16_t*>(s + W.At + (size_t)j * W.at_bytes);
+      uint16_t* At = reinterpret_cast<uint16_t*>(s + W.At + (size_t)j * aslots * W.at_bytes);
       uint16_t* Wx = reinterpret_cast<uint16_t*>(s + W.Wx + (size_t)j * W.wx_bytes);
-      hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream,
-                         in.A, d, d_in, At);
+      if (W.int8)
+        hipLaunchKernelGGL(fold_transpose_q_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream,
+                           in.Aq, in.As, d, d_in, At, At + W.at_bytes / 2);
+      else
+        hipLaunchKernelGGL(fold_transpose_kernel, dim3(d_in / 64, d / 64), dim3(256), 0, stream,
+                           in.A, d, d_in, At);
+      const float* As = W.int8 ? in.As : nullptr;
       hipLaunchKernelGGL(fold_wsplit_kernel, dim3(2048), dim3(256), 0, stream, in.WK, in.WV, in.w,
-                         kv, d, Wx);
+                         As, kv, d, Wx);
       hipLaunchKernelGGL(fold_gemv_kernel, dim3((d_in + 2 * kv + 3) / 4), dim3(256), 0, stream,
-                         At, in.WK, in.WV, in.w, in.b, d, d_in, kv,
+                         At, As, in.WK, in.WV, in.w, in.b, d, d_in, kv,
                          reinterpret_cast<double*>(blk(l) + W.g), reinterpret_cast<float*>(o + F.c));
       hipLaunchKernelGGL(fold_bb_kernel, dim3(1), dim3(1024), 0, stream, in.b, d,
                          reinterpret_cast<double*>(blk(l) + W.scal));

@@ -57,22 +57,29 @@ FoldLayout fold_layout(int d_in, int kv);
 // for each layer ([A^T | A^T] and [W_hi | W_lo] in bf16), then one block per layer of a
 // group folded side by side: A^T A in fp64 (the Cholesky works in place), the
 // diagonal-block inverses, A^T b and r in fp64, |b|^2.  Block offsets are from the block's
-// start; `total` covers n_par blocks.
+// start; `total` covers n_par blocks.  An int8 map takes two [A^T | A^T]-sized slots: its
+// codes [Aq^T | Aq^T] and [C_hi | C_lo] with C[j][k] = s_k^2 Aq[k][j], so that
+// A^T A = Aq^T diag(s^2) Aq is one product over 2 d; its layers then share a launch two at
+// a time.
 constexpr int kFoldGemmSlots = 4;   // layers whose fold GEMMs share one launch
 struct FoldWsLayout {
-  int slots;                          // operand slots: [A^T | A^T] and [W_hi | W_lo] each
+  int slots;                          // layers per GEMM launch ([W_hi | W_lo] slots)
+  int int8;                           // 1: two [A^T | A^T]-sized slots per layer
   size_t At, at_bytes, Wx, wx_bytes, blocks;
   size_t H64, linv, g, r, scal, per_layer;
   size_t total;
 };
-FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par);
-// One layer's plain fields: A bf16 [d][d_in], b fp32 [d], w bf16 [d], W_K / W_V bf16 [kv][d].
+FoldWsLayout fold_ws_layout(int d, int d_in, int kv, int n_par, bool int8 = false);
+// One layer's plain fields: A bf16 [d][d_in] or Aq int8 [d][d_in] with As fp32 [d] (the map
+// Aq[o][i] As[o]), b fp32 [d], w bf16 [d], W_K / W_V bf16 [kv][d].
 struct FoldLayerIn {
   const uint16_t* A;
   const float* b;
   const uint16_t* w;
   const uint16_t* WK;
   const uint16_t* WV;
+  const int8_t* Aq;
+  const float* As;
 };
 // Folds G layers (G <= the n_par of W) into their buffers out[0 .. G-1]: the GEMMs layer by
 // layer, then one batched Cholesky and substitution for the G layers.  A non-positive pivot

@@ -628,10 +628,17 @@ size_t ridgefill_fold_bytes(const rf_shape* shape) {
   return rf::fold_layout(d_in_of(shape), shape->n_kv_heads * shape->head_dim).total;
 }
 
-size_t ridgefill_fold_workspace_bytes_ex(const rf_shape* shape, int32_t layers_at_once) {
-  if (check_shape(shape) != RF_OK || check_foldable(shape) != RF_OK || layers_at_once < 1) return 0;
+size_t ridgefill_fold_workspace_bytes_maps(const rf_shape* shape, int32_t layers_at_once,
+                                           uint32_t map_flags) {
+  if (check_shape(shape) != RF_OK || check_foldable(shape) != RF_OK || layers_at_once < 1 ||
+      (map_flags & ~(uint32_t)RF_MAPS_INT8))
+    return 0;
   return rf::fold_ws_layout(shape->d, d_in_of(shape), shape->n_kv_heads * shape->head_dim,
-                            layers_at_once).total;
+                            layers_at_once, (map_flags & RF_MAPS_INT8) != 0).total;
+}
+
+size_t ridgefill_fold_workspace_bytes_ex(const rf_shape* shape, int32_t layers_at_once) {
+  return ridgefill_fold_workspace_bytes_maps(shape, layers_at_once, 0);
 }
 
 size_t ridgefill_fold_workspace_bytes(const rf_shape* shape) {
@@ -647,25 +654,32 @@ rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int
   if (n_layers > 0 && (!layers || !folded)) return fail(RF_E_INVALID, "layers or folded is NULL");
   if (!ws) return fail(RF_E_INVALID, "ws is NULL");
   const int d = shape->d, d_in = d_in_of(shape), kv = shape->n_kv_heads * shape->head_dim;
-  const rf::FoldWsLayout W1 = rf::fold_ws_layout(d, d_in, kv, 1);
+  // int8 maps (A_q, A_scale) or bf16 maps (A): one kind per call
+  const bool int8 = n_layers > 0 && layers[0].A_q != nullptr;
+  for (int i = 0; i < n_layers; ++i) {
+    const rf_layer& l = layers[i];
+    if ((l.A_q != nullptr) != int8)
+      return fail(RF_E_INVALID, "layer %d: all layers of a call need int8 maps or none", i);
+    if (int8 ? (!l.A_q || !l.A_scale || l.A) : !l.A)
+      return fail(RF_E_INVALID, "layer %d: exactly one map, A or A_q with A_scale, is needed", i);
+    if (!l.b || !l.norm_w || !l.W_K || !l.W_V || !folded[i])
+      return fail(RF_E_INVALID, "layer %d: b, norm_w, W_K, W_V and its folded buffer are needed", i);
+    if ((l.A && !aligned(l.A, 16)) || (l.A_scale && !aligned(l.A_scale, 4)) ||
+        !aligned(l.W_K, 16) || !aligned(l.W_V, 16) || !aligned(l.b, 4) ||
+        !aligned(l.norm_w, 2) || !aligned(folded[i], 256))
+      return fail(RF_E_SHAPE, "layer %d: A, W_K, W_V need 16-byte, A_scale and b 4-byte, the "
+                  "folded buffer 256-byte alignment", i);
+  }
+  const rf::FoldWsLayout W1 = rf::fold_ws_layout(d, d_in, kv, 1, int8);
   if (!aligned(ws, 256) || ws_bytes < W1.total)
-    return fail(RF_E_WORKSPACE, "fold workspace must be 256-byte aligned and >= %zu bytes", W1.total);
+    return fail(RF_E_WORKSPACE, "fold workspace must be 256-byte aligned and >= %zu bytes%s",
+                W1.total, int8 ? " (int8 maps)" : "");
   // as many layers side by side as the workspace holds
   int cap = n_layers > 0 ? n_layers : 1;
   if (cap > rf::kMaxFoldGroup) cap = rf::kMaxFoldGroup;
   int n_par = 1;
-  while (n_par < cap && rf::fold_ws_layout(d, d_in, kv, n_par + 1).total <= ws_bytes) ++n_par;
-  const rf::FoldWsLayout W = rf::fold_ws_layout(d, d_in, kv, n_par);
-  for (int i = 0; i < n_layers; ++i) {
-    const rf_layer& l = layers[i];
-    if (l.A_q) return fail(RF_E_UNSUPPORTED, "layer %d: int8 maps cannot be folded", i);
-    if (!l.A || !l.b || !l.norm_w || !l.W_K || !l.W_V || !folded[i])
-      return fail(RF_E_INVALID, "layer %d: A, b, norm_w, W_K, W_V and its folded buffer are needed", i);
-    if (!aligned(l.A, 16) || !aligned(l.W_K, 16) || !aligned(l.W_V, 16) || !aligned(l.b, 4) ||
-        !aligned(l.norm_w, 2) || !aligned(folded[i], 256))
-      return fail(RF_E_SHAPE, "layer %d: A, W_K, W_V need 16-byte, the folded buffer 256-byte "
-                  "alignment", i);
-  }
+  while (n_par < cap && rf::fold_ws_layout(d, d_in, kv, n_par + 1, int8).total <= ws_bytes) ++n_par;
+  const rf::FoldWsLayout W = rf::fold_ws_layout(d, d_in, kv, n_par, int8);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = rf::launch_clear_status(static_cast<unsigned*>(ws), st);
   if (e != hipSuccess) return hip_fail(e, "status clear");
@@ -674,7 +688,7 @@ rf_status ridgefill_fold_maps(const rf_shape* shape, const rf_layer* layers, int
     const int G = n_layers - l0 < n_par ? n_layers - l0 : n_par;
     for (int g = 0; g < G; ++g) {
       const rf_layer& l = layers[l0 + g];
-      in[g] = {l.A, l.b, l.norm_w, l.W_K, l.W_V};
+      in[g] = {l.A, l.b, l.norm_w, l.W_K, l.W_V, l.A_q, l.A_scale};
     }
     e = rf::launch_fold(d, d_in, kv, in, G, folded + l0, ws, W, st);
     if (e != hipSuccess) return hip_fail(e, "fold launch");

@@ -140,7 +140,8 @@ def fold_layers(case: Case, inp, stream=None, layers_at_once=None):
     nb = B.ridgefill_fold_bytes(shape)
     assert nb > 0
     g = layers_at_once or len(inp["layers"])
-    ws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, g), dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.ridgefill_fold_workspace_bytes_maps(shape, g, case.map_flags),
+                     dtype=torch.uint8, device=dev)
     bufs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in inp["layers"]]
     B.ridgefill_fold_maps(shape, inp["layers"], bufs, ws, stream)
     status = B.ridgefill_read_status(ws, stream)

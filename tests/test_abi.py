@@ -127,6 +127,11 @@ def test_fold_size_queries_and_errors():
     w4 = B.ridgefill_fold_workspace_bytes_ex(s, 4)
     assert (w4 - w1) % 3 == 0 and (w4 - w1) // 3 >= 4096 * 4096 * 8
     assert B.ridgefill_fold_workspace_bytes_ex(s, 0) == 0
+    # int8 maps: a second operand slot per layer; unknown map flags give 0
+    assert B.ridgefill_fold_workspace_bytes_maps(s, 1, 0) == w1
+    assert B.ridgefill_fold_workspace_bytes_maps(s, 4, 0) == w4
+    assert B.ridgefill_fold_workspace_bytes_maps(s, 1, B.RF_MAPS_INT8) > w1
+    assert B.ridgefill_fold_workspace_bytes_maps(s, 1, B.RF_MAPS_FOLDED) == 0
     # no predicted-input buffer: a folded fill's per-layer workspace is small
     f1 = B.ridgefill_fill_workspace_bytes(s, 25805, 1, B.RF_MAPS_FOLDED)
     f20 = B.ridgefill_fill_workspace_bytes(s, 25805, 20, B.RF_MAPS_FOLDED)

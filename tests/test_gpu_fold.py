@@ -40,7 +40,9 @@ def _filled(case):
 
 def _oracle_fold(case, inp, l):
     lay = inp["layers"][l]
-    return oracle.fold_map(bf16_np(lay["A"]), lay["b"].cpu().numpy().astype(np.float64),
+    # an int8 map stands for q * scale exactly (float64)
+    A = lay["A_ref"] if "A_ref" in lay else bf16_np(lay["A"])
+    return oracle.fold_map(A, lay["b"].cpu().numpy().astype(np.float64),
                            bf16_np(lay["norm_w"]), bf16_np(lay["W_K"]), bf16_np(lay["W_V"]))
 
 
@@ -49,6 +51,8 @@ FOLDS = [
     (512, 2, 2, 128, 51, {}),
     (768, 1, 4, 64, 52, dict(d_in=512)),        # tall map: kappa > 0
     (256, 1, 2, 64, 53, dict(map_kind="identity")),
+    (512, 3, 2, 128, 54, dict(int8=True)),      # int8 maps: codes and row scales
+    (768, 2, 4, 64, 55, dict(d_in=512, int8=True)),
 ]
 
 
@@ -81,6 +85,7 @@ def test_fold_outputs_vs_oracle(d, nl, nkv, hd, seed, opts):
 FILLS = [
     # d, layers, n_kv, hd, N, T, n_exact, page, seed, options
     (512, 3, 2, 128, 700, 100, 60, 16, 61, {}),
+    (512, 3, 2, 128, 700, 100, 60, 16, 68, dict(int8=True, knorm=True)),   # folded int8 maps
     (512, 2, 2, 128, 700, 100, 60, 16, 62, dict(knorm=True, vscale=True)),
     (768, 2, 4, 64, 333, 33, 17, 8, 63, dict(knorm=True)),
     (768, 2, 4, 64, 600, 40, 25, 16, 64, dict(d_in=512, vscale=True)),     # tall map
@@ -133,10 +138,12 @@ def test_folded_empty_filled_list_leaves_cache_untouched():
         assert torch.equal(l["v_pages"].view(torch.int16), v.view(torch.int16))
 
 
-def test_fold_group_size_does_not_change_the_buffers():
-    # layers folded one at a time and four side by side (one batched Cholesky): the
-    # per-layer arithmetic is the same, so the folded buffers agree bit for bit
-    case = _case(768, 4, 4, 64, 300, 20, 0, 16, 71, d_in=512)
+@pytest.mark.parametrize("int8", [False, True])
+def test_fold_group_size_does_not_change_the_buffers(int8):
+    # layers folded one at a time and four side by side (one batched Cholesky; int8 maps:
+    # GEMM launches of two layers): the per-layer arithmetic is the same, so the folded
+    # buffers agree bit for bit
+    case = _case(768, 4, 4, 64, 300, 20, 0, 16, 71, d_in=512, int8=int8)
     inp = build_inputs(case)
     one, st1 = fold_layers(case, inp, layers_at_once=1)
     one = [t.clone() for t in one]
@@ -202,9 +209,19 @@ def test_folded_argument_errors():
     int8.pop("A")
     int8["A_q"] = torch.zeros((case.d, case.d), dtype=torch.int8, device=dev)
     int8["A_scale"] = torch.ones(case.d, dtype=torch.float32, device=dev)
+    # int8 maps take a second operand slot: the bf16 maps' one-layer workspace is short
     fws = torch.empty(B.ridgefill_fold_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-    with pytest.raises(RuntimeError, match="int8"):
+    assert B.ridgefill_fold_workspace_bytes_maps(shape, 1, B.RF_MAPS_INT8) > fws.numel()
+    with pytest.raises(RuntimeError, match="workspace"):
         B.ridgefill_fold_maps(shape, [int8], [inp["folded"][0]], fws)
+    # one map kind per call
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes_maps(shape, 2, B.RF_MAPS_INT8),
+                      dtype=torch.uint8, device=dev)
+    with pytest.raises(RuntimeError, match="int8 maps or none"):
+        B.ridgefill_fold_maps(shape, [int8, inp["layers"][1]], inp["folded"], fws)
+    both = dict(int8, A=inp["layers"][0]["A"])
+    with pytest.raises(RuntimeError, match="exactly one map"):
+        B.ridgefill_fold_maps(shape, [both], [inp["folded"][0]], fws)
 
 
 def test_folded_group_split_is_bit_identical():
