@@ -230,7 +230,7 @@ def test_8b_folded_full_size():
     print(f"8B folded: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
 
 
-def _folded_full(cfg, knorm=False, streamed=False):
+def _folded_full(cfg, knorm=False, streamed=False, int8=False):
     dev = torch.device("cuda")
     print(f"\n{cfg.name} folded: inputs", flush=True)
     inp = synth.device_fill_inputs(cfg, dev, sentinel=True)
@@ -238,8 +238,19 @@ def _folded_full(cfg, knorm=False, streamed=False):
         for l, lay in enumerate(inp["layers"]):
             lay["k_norm_w"] = torch.from_numpy(synth.key_norm_weight(cfg.head_dim, cfg.seed, l)).to(
                 dev).to(torch.bfloat16)
+    codes = []
+    if int8:                           # int8 maps from the oracle's quantizer, folded as codes
+        for l, lay in enumerate(inp["layers"]):
+            q, sc = oracle.quantize_map_int8(lay["A"].float().cpu().numpy(), np.float32)
+            codes.append((q, sc))
+            del lay["A"]
+            lay["A_q"] = torch.from_numpy(q).to(dev)
+            lay["A_scale"] = torch.from_numpy(sc.astype(np.float32)).to(dev)
+            if l % 12 == 11:
+                print(f"  quantized {l + 1} maps", flush=True)
     shape = B.make_shape(cfg.d, cfg.n_kv, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
-    fws = torch.empty(B.ridgefill_fold_workspace_bytes_ex(shape, len(inp["layers"])),
+    fws = torch.empty(B.ridgefill_fold_workspace_bytes_maps(shape, len(inp["layers"]),
+                                                            B.RF_MAPS_INT8 if int8 else 0),
                       dtype=torch.uint8, device=dev)
     bufs = [torch.empty(B.ridgefill_fold_bytes(shape), dtype=torch.uint8, device=dev)
             for _ in inp["layers"]]
@@ -267,7 +278,8 @@ def _folded_full(cfg, knorm=False, streamed=False):
     _, exact, _ = oracle.partition(cfg.N, cfg.T, synth.exact_rows(cfg))
     pg, sl = _routing(cfg, inp, filled)
     n, worst = _values(cfg, inp, filled, exact, pg, sl,
-                       kn_of=(lambda l: _np64(inp["layers"][l]["k_norm_w"])) if knorm else None)
+                       kn_of=(lambda l: _np64(inp["layers"][l]["k_norm_w"])) if knorm else None,
+                       A_of=(lambda l: oracle.dequantize_map_int8(*codes[l])) if int8 else None)
     print(f"{cfg.name} folded: {n} rows x {cfg.n_upper} layers, worst rel {worst:.2e}", flush=True)
 
 
@@ -278,6 +290,12 @@ def test_27b_folded_full_size():
 
 def test_qwen3_8b_key_norm_folded_full_size():
     _folded_full(configs.QWEN3_8B, knorm=True)
+
+
+def test_27b_folded_from_int8_maps_full_size():
+    # the 48 maps quantized to int8, folded through their codes, against the oracle's fill
+    # with the dequantized maps
+    _folded_full(configs.QWEN27B, int8=True)
 
 
 def test_27b_folded_streamed_full_size():
