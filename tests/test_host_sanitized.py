@@ -110,6 +110,19 @@ int main(void) {
   CHECK(ridgefill_solve_info(NULL, NULL, NULL, NULL) == RF_E_INVALID, 59);
   CHECK(ridgefill_profile_read(RF_KERNEL_COUNT, NULL, NULL) != RF_OK, 60);
   CHECK(strlen(ridgefill_last_error()) > 0, 61);
+  CHECK(ridgefill_fold_workspace_bytes_maps(&s, 1, RF_MAPS_INT8) > ridgefill_fold_workspace_bytes(&s), 62);
+  CHECK(ridgefill_fold_workspace_bytes_maps(&s, 1, RF_MAPS_FOLDED) == 0, 63);
+  CHECK(ridgefill_fold_workspace_bytes_maps(NULL, 1, 0) == 0, 64);
+  {                              /* int8 fold: checked on the host, nothing enqueued */
+    rf_layer q;
+    void* fold_out[1] = {(void*)256};
+    memset(&q, 0, sizeof q);
+    q.A_q = (const int8_t*)256; q.A_scale = (const float*)256; q.b = (const float*)256;
+    q.norm_w = (const uint16_t*)256; q.W_K = (const uint16_t*)256; q.W_V = (const uint16_t*)256;
+    CHECK(ridgefill_fold_maps(&s, &q, 1, fold_out, (void*)256, 4096, NULL) == RF_E_WORKSPACE, 65);
+    q.A = (const uint16_t*)256;  /* both maps given */
+    CHECK(ridgefill_fold_maps(&s, &q, 1, fold_out, (void*)256, 4096, NULL) == RF_E_INVALID, 66);
+  }
   printf("ok\n");
   return 0;
 }
