@@ -147,6 +147,28 @@ __device__ __forceinline__ float hi16(uint32_t x) { return bf16_to_f32(x >> 16);
 
 // FQ = 1: int8 map codes, read by the GEMM as they are (the F operand's LDS layout of
 // i8_off) and scaled per output row in the epilogue.
+// x_S rows behind the 8 DMA blocks of a tile's gathered operand (token tile t0): lane
+// (lane >> 3) of block p is filled-list entry t0 + 8 (4 p + wave) + (lane >> 3).  The eight
+// index loads go out together and are waited for once: each reads an entry of the list (a
+// position past its end reads the last one), and positions past the end or invalid entries
+// then take row 0 (padding rows, never stored).  Loaded one at a time under a condition, they
+// were eight dependent round trips at the start of every tile.
+__device__ __forceinline__ void gathered_rows(const FillKArgs& a, int t0, int wave, int lane,
+                                              int (&row)[8]) {
+  const int last = a.n_filled > 0 ? a.n_filled - 1 : 0;
+  int x[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int tok = t0 + dma_block_row(p, wave) + dma_lane_row(lane);
+    x[p] = a.n_filled > 0 ? a.idx[tok < last ? tok : last] : 0;
+  }
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int tok = t0 + dma_block_row(p, wave) + dma_lane_row(lane);
+    row[p] = (tok < a.n_filled && x[p] >= 0 && x[p] < a.P) ? x[p] : 0;
+  }
+}
+
 template <int FQ>
 __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPipeLds];
@@ -167,6 +189,8 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
         Fo.off[p] = (uint32_t)((lane >> 2) * a.d_in + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
       }
     }
+    int row[8];
+    gathered_rows(a, t0, wave, lane, row);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
@@ -175,14 +199,8 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
         Fo.base[p] = reinterpret_cast<const unsigned char*>(Lp.A + (size_t)(f0 + r0) * a.d_in);
         Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
       }
-      const int tok = t0 + r;
-      int row = 0;
-      if (tok < a.n_filled) {
-        const int t = a.idx[tok];
-        if (t >= 0 && t < a.P) row = t;
-      }
       To.base[p] = reinterpret_cast<const unsigned char*>(a.xS);
-      To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
+      To.off[p] = (uint32_t)(((size_t)row[p] * a.x_stride + ce) * 2);
     }
   }
 
@@ -298,20 +316,16 @@ __device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile
   const int f0 = t.ft * kTile, t0 = t.tt * kTile;
   const int col = half == 0 ? a.d_in - kPipeBK : f0;
   const uint16_t* R = layer_ptrs(a, t.g).A;
+  int row[8];
+  gathered_rows(a, t0, wave, lane, row);
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
     const int ce = dma_chunk_elems(r, lane);
     Fo.base[p] = reinterpret_cast<const unsigned char*>(R + (size_t)(f0 + r0) * a.d_in + col);
     Fo.off[p] = (uint32_t)((dma_lane_row(lane) * a.d_in + ce) * 2);
-    const int tok = t0 + r;
-    int row = 0;
-    if (tok < a.n_filled) {
-      const int x = a.idx[tok];
-      if (x >= 0 && x < a.P) row = x;
-    }
     To.base[p] = reinterpret_cast<const unsigned char*>(a.xS + col);
-    To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
+    To.off[p] = (uint32_t)(((size_t)row[p] * a.x_stride + ce) * 2);
   }
 }
 
@@ -487,6 +501,8 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
   DmaOperand Fo, To;
   {
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int row[8];
+    if (folded) gathered_rows(a, t0, wave, lane, row);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r0 = dma_block_row(p, wave), r = r0 + dma_lane_row(lane);
@@ -499,14 +515,8 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
       Fo.base[p] = reinterpret_cast<const unsigned char*>(wrow);
       Fo.off[p] = (uint32_t)((dma_lane_row(lane) * kdim + ce) * 2);
       if (folded) {                        // rows of x_S gathered through the index list
-        const int tok = t0 + r;
-        int row = 0;
-        if (tok < a.n_filled) {
-          const int t = a.idx[tok];
-          if (t >= 0 && t < a.P) row = t;
-        }
         To.base[p] = reinterpret_cast<const unsigned char*>(a.xS);
-        To.off[p] = (uint32_t)(((size_t)row * a.x_stride + ce) * 2);
+        To.off[p] = (uint32_t)(((size_t)row[p] * a.x_stride + ce) * 2);
       } else {
         To.base[p] = reinterpret_cast<const unsigned char*>(hb + (size_t)(t0 + r0) * a.d);
         To.off[p] = Fo.off[p];
