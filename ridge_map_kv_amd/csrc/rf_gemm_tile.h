@@ -359,7 +359,12 @@ __device__ __forceinline__ void gemm_mainloop_tri(f32x16 (&acc)[4][4], const Dma
   asm volatile("s_waitcnt vmcnt(16)" ::: "memory");     // slice 0 landed: slice 1 may be pending
   __syncthreads();
 
-  FragOff fo = frag_off(lane);
+  // the offsets are formed anew for every tile: in a persistent caller, hoisted out of its
+  // loop they would live across the epilogue, where they were spilled and then reloaded
+  // inside the first slices (a reload waits for every load in flight, the slices' too)
+  int olane = lane;
+  asm volatile("" : "+v"(olane));
+  FragOff fo = frag_off(olane);
   frag_off_tri(fo, wf);
   bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
