@@ -147,6 +147,14 @@ __device__ __forceinline__ float hi16(uint32_t x) { return bf16_to_f32(x >> 16);
 
 // FQ = 1: int8 map codes, read by the GEMM as they are (the F operand's LDS layout of
 // i8_off) and scaled per output row in the epilogue.
+// A load through a layer-table pointer, issued as a global-memory load.  The table's pointers
+// are generic, and a generic (flat) load also counts against the LDS wait counter: pending
+// across a main loop, it turned every fragment-read wait there into a wait for all of them.
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
 // x_S rows behind the 8 DMA blocks of a tile's gathered operand (token tile t0): lane
 // (lane >> 3) of block p is filled-list entry t0 + 8 (4 p + wave) + (lane >> 3).  The eight
 // index loads go out together and are waited for once: each reads an entry of the list (a
@@ -209,9 +217,9 @@ __device__ __forceinline__ void fill_map_tile(const FillKArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) float sbias[kTile];
   __shared__ __attribute__((aligned(16))) float swt[kTile];
   __shared__ __attribute__((aligned(16))) float ssc[kTile];
-  const float my_b = Lp.b[f0 + tid];
-  const uint16_t my_w = Lp.w[f0 + tid];
-  const float my_s = a.has_scale ? Lp.As[f0 + tid] : 1.0f;
+  const float my_b = gload(Lp.b + f0 + tid);
+  const uint16_t my_w = gload(Lp.w + f0 + tid);
+  const float my_s = a.has_scale ? gload(Lp.As + f0 + tid) : 1.0f;
 
   f32x16 acc[4][4];
   gemm_pipeline<false, FQ>(acc, Fo, To, a.d_in, smem);
@@ -365,8 +373,8 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   for (;;) {
     const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
     const FillLayerPtrs Lc = layer_ptrs(a, cur.g);
-    const float my_r = Lc.b[f0 + tid];
-    const float my_g = Lc.fg[f0 + tid];
+    const float my_r = gload(Lc.b + f0 + tid);
+    const float my_g = gload(Lc.fg + f0 + tid);
     f32x16 acc[4][4];
     if (half == 0)                                              // each ends with a barrier:
       gemm_mainloop_tri<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
@@ -537,10 +545,10 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
   float my_kn = 1.f, my_vs = 1.f, my_c = 0.f;
   if (MODE == 0) {
     my_off = a.row_slot[t0 + tid];
-    if (a.has_knorm && tid < a.hd) my_kn = bf16_to_f32(Lp.kn[tid]);
-    if (Lp.vs && tid < a.n_kv) my_vs = Lp.vs[tid];
+    if (a.has_knorm && tid < a.hd) my_kn = bf16_to_f32(gload(Lp.kn + tid));
+    if (Lp.vs && tid < a.n_kv) my_vs = gload(Lp.vs + tid);
   }
-  if (folded) my_c = Lp.fc[f0 + tid];
+  if (folded) my_c = gload(Lp.fc + f0 + tid);
 
   f32x16 acc[4][4];
   gemm_pipeline(acc, Fo, To, kdim, smem);
@@ -737,7 +745,7 @@ __global__ void rstd_folded_kernel(FillKArgs a) {
   const float* p = reinterpret_cast<const float*>(lw + a.per_layer_h) + row;
   float s = 0.f;
   for (int c = 0; c < a.nchunk; ++c) s += p[(size_t)c * a.mpad];
-  s = fmaxf(s + *layer_ptrs(a, g).kap, 0.f);
+  s = fmaxf(s + gload(layer_ptrs(a, g).kap), 0.f);
   reinterpret_cast<float*>(lw + a.per_layer_h + a.per_layer_ssq)[row] =
       1.0f / sqrtf(s / (float)a.d + a.eps);
 }
