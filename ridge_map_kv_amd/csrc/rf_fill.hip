@@ -319,8 +319,8 @@ __device__ __forceinline__ NormTile norm_tile(const FillKArgs& a, int item, int 
 // the tile's gathered x_S rows (the same rows for both tiles of an item).  Half 0 runs from
 // the last column down (the bases point at column d_in - 64), half 1 from column f0 up.
 __device__ __forceinline__ void norm_operands(const FillKArgs& a, const NormTile& t, int half,
-                                              DmaOperand& Fo, DmaOperand& To) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                              int lane, DmaOperand& Fo, DmaOperand& To) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int f0 = t.ft * kTile, t0 = t.tt * kTile;
   const int col = half == 0 ? a.d_in - kPipeBK : f0;
   const uint16_t* R = layer_ptrs(a, t.g).A;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   if (item >= a.n_items) return;
   NormTile cur = norm_tile(a, item, 0);
   DmaOperand Fo, To;
-  norm_operands(a, cur, 0, Fo, To);
+  norm_operands(a, cur, 0, lane, Fo, To);
   norm_prologue(Fo, To, a.d_in - cur.ft * kTile, 0, smem);
   for (;;) {
     const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
@@ -381,6 +381,12 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     else
       gemm_mainloop_tri<false>(acc, Fo, To, a.d_in - f0, smem);
 
+    // Per-lane values of the rest of the iteration are formed from a thread index made
+    // opaque here: hoisted out of the loop, they lived across it and were spilled, and their
+    // reloads in the epilogue waited for the next tile's slice loads issued just before.
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    const int llane = ltid & 63, lh = llane >> 5;
     // the next tile: the other half of this item (unless it is the middle tile of an odd
     // nft), else the first half of the next item
     int nitem = item, nhalf = half + 1;
@@ -392,13 +398,13 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     NormTile nxt = cur;
     if (more) {
       nxt = norm_tile(a, nitem, nhalf);
-      norm_operands(a, nxt, nhalf, Fo, To);
+      norm_operands(a, nxt, nhalf, llane, Fo, To);
       norm_prologue(Fo, To, a.d_in - nxt.ft * kTile, nhalf, smem);
     }
 
     float* ssq = reinterpret_cast<float*>(a.layer_ws + cur.g * a.per_layer + a.per_layer_h);
-    sr[tid] = my_r;
-    sg[tid] = my_g;
+    sr[ltid] = my_r;
+    sg[ltid] = my_g;
     __syncthreads();
     // wave half wf holds F blocks 2 m + wf: blocks m = 0, 1 lie in the tile's first 128-feature
     // chunk, m = 2, 3 in its second; the wf = 1 halves hand their sums to the wf = 0 ones
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int fr = (2 * m + wf) * 32 + q * 8 + h * 4;
+        const int fr = (2 * m + wf) * 32 + q * 8 + lh * 4;
         const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + fr);
         const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + fr);
 #pragma unroll
@@ -426,17 +432,17 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
       ss0[n] += __shfl_xor(ss0[n], 32);
       ss1[n] += __shfl_xor(ss1[n], 32);
     }
-    if (wf == 1 && h == 0) {
+    if (wf == 1 && lh == 0) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) xch[wt][n][lane & 31] = make_float2(ss0[n], ss1[n]);
+      for (int n = 0; n < 4; ++n) xch[wt][n][llane & 31] = make_float2(ss0[n], ss1[n]);
     }
     __syncthreads();
-    if (wf == 0 && h == 0) {
+    if (wf == 0 && lh == 0) {
       const int chunk = f0 >> 7;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int tok = t0 + wt * 128 + n * 32 + (lane & 31);
-        const float2 o = xch[wt][n][lane & 31];
+        const int tok = t0 + wt * 128 + n * 32 + (llane & 31);
+        const float2 o = xch[wt][n][llane & 31];
         ssq[(size_t)chunk * a.mpad + tok] = ss0[n] + o.x;          // chunk-major: coalesced
         ssq[(size_t)(chunk + 1) * a.mpad + tok] = ss1[n] + o.y;
       }
