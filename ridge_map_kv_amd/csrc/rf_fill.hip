@@ -372,9 +372,6 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
   norm_prologue(Fo, To, a.d_in - cur.ft * kTile, 0, smem);
   for (;;) {
     const int f0 = cur.ft * kTile, t0 = cur.tt * kTile;
-    const FillLayerPtrs Lc = layer_ptrs(a, cur.g);
-    const float my_r = gload(Lc.b + f0 + tid);
-    const float my_g = gload(Lc.fg + f0 + tid);
     f32x16 acc[4][4];
     if (half == 0)                                              // each ends with a barrier:
       gemm_mainloop_tri<true>(acc, Fo, To, a.d_in - f0, smem);  // the LDS is free
@@ -387,6 +384,11 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     int ltid = tid;
     asm volatile("" : "+v"(ltid));
     const int llane = ltid & 63, lh = llane >> 5;
+    // this tile's r1 and g, loaded now with the next tile's index loads (loaded before the
+    // main loop, they were spilled across it)
+    const FillLayerPtrs Lc = layer_ptrs(a, cur.g);
+    const float my_r = gload(Lc.b + f0 + ltid);
+    const float my_g = gload(Lc.fg + f0 + ltid);
     // the next tile: the other half of this item (unless it is the middle tile of an odd
     // nft), else the first half of the next item
     int nitem = item, nhalf = half + 1;
@@ -403,6 +405,9 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     }
 
     float* ssq = reinterpret_cast<float*>(a.layer_ws + cur.g * a.per_layer + a.per_layer_h);
+    ltid = tid;                         // again, now that the loads are out
+    asm volatile("" : "+v"(ltid));
+    const int elane = ltid & 63, eh = elane >> 5;
     sr[ltid] = my_r;
     sg[ltid] = my_g;
     __syncthreads();
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int fr = (2 * m + wf) * 32 + q * 8 + lh * 4;
+        const int fr = (2 * m + wf) * 32 + q * 8 + eh * 4;
         const f32x4 rv = *reinterpret_cast<const f32x4*>(sr + fr);
         const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + fr);
 #pragma unroll
@@ -427,22 +432,29 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
         }
       }
     }
+    // the two half-waves' shares: v_permlane32_swap of a value with itself returns its
+    // lower-half lanes' values in the first result and its upper half's in the second, in every
+    // lane, so their sum is the half-waves' sum everywhere (no lane index, no LDS permute)
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      ss0[n] += __shfl_xor(ss0[n], 32);
-      ss1[n] += __shfl_xor(ss1[n], 32);
+      const auto p0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss0[n]), __float_as_uint(ss0[n]),
+                                                       false, false);
+      const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss1[n]), __float_as_uint(ss1[n]),
+                                                       false, false);
+      ss0[n] = __uint_as_float(p0[0]) + __uint_as_float(p0[1]);
+      ss1[n] = __uint_as_float(p1[0]) + __uint_as_float(p1[1]);
     }
-    if (wf == 1 && lh == 0) {
+    if (wf == 1 && eh == 0) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) xch[wt][n][llane & 31] = make_float2(ss0[n], ss1[n]);
+      for (int n = 0; n < 4; ++n) xch[wt][n][elane & 31] = make_float2(ss0[n], ss1[n]);
     }
     __syncthreads();
-    if (wf == 0 && lh == 0) {
+    if (wf == 0 && eh == 0) {
       const int chunk = f0 >> 7;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int tok = t0 + wt * 128 + n * 32 + (llane & 31);
-        const float2 o = xch[wt][n][llane & 31];
+        const int tok = t0 + wt * 128 + n * 32 + (elane & 31);
+        const float2 o = xch[wt][n][elane & 31];
         ssq[(size_t)chunk * a.mpad + tok] = ss0[n] + o.x;          // chunk-major: coalesced
         ssq[(size_t)(chunk + 1) * a.mpad + tok] = ss1[n] + o.y;
       }
