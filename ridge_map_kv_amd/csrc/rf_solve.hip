@@ -619,30 +619,33 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double
   const double* gb = U + (size_t)(bb * NB + lrow) * d + lcol;
   const int k0 = ab * NB, nks = (d - k0) / kWk;
   constexpr int kV = kWk / 8;                 // double2 per thread and operand
-  double2 ra[kV], rb[kV];
-  auto fetch = [&](int k) {
-#pragma unroll
-    for (int q = 0; q < kV; ++q) {
-      ra[q] = *reinterpret_cast<const double2*>(ga + k + 2 * q);
-      rb[q] = *reinterpret_cast<const double2*>(gb + k + 2 * q);
-    }
-  };
-  auto park = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < kV; ++q) {
-      *reinterpret_cast<double2*>(&wa[buf][lrow * kWld + lcol + 2 * q]) = ra[q];
-      *reinterpret_cast<double2*>(&wb[buf][lrow * kWld + lcol + 2 * q]) = rb[q];
-    }
-  };
+  // the next slice in registers: written out as plain code (through lambdas capturing these
+  // arrays, the compiler kept them in scratch memory and waited for every load right away)
+  static_assert(kV == 4, "four 16-byte pieces per thread and operand");
+  double2 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define WTW_FETCH(k)                                                        \
+  {                                                                         \
+    const double2* pa = reinterpret_cast<const double2*>(ga + (k));         \
+    const double2* pb = reinterpret_cast<const double2*>(gb + (k));         \
+    ra0 = pa[0]; ra1 = pa[1]; ra2 = pa[2]; ra3 = pa[3];                     \
+    rb0 = pb[0]; rb1 = pb[1]; rb2 = pb[2]; rb3 = pb[3];                     \
+  }
+#define WTW_PARK(buf)                                                       \
+  {                                                                         \
+    double2* qa = reinterpret_cast<double2*>(&wa[buf][lrow * kWld + lcol]); \
+    double2* qb = reinterpret_cast<double2*>(&wb[buf][lrow * kWld + lcol]); \
+    qa[0] = ra0; qa[1] = ra1; qa[2] = ra2; qa[3] = ra3;                     \
+    qb[0] = rb0; qb[1] = rb1; qb[2] = rb2; qb[3] = rb3;                     \
+  }
   const int lane = tid & 63, w = tid >> 6;
   const int r0 = (w >> 1) * 32 + (lane & 15), c0 = (w & 1) * 32 + (lane & 15), kq = lane >> 4;
   Acc64 acc;
   zero44(acc);
-  fetch(k0);
-  park(0);
+  WTW_FETCH(k0)
+  WTW_PARK(0)
   __syncthreads();
   for (int s = 0; s < nks; ++s) {
-    if (s + 1 < nks) fetch(k0 + (s + 1) * kWk);
+    if (s + 1 < nks) { WTW_FETCH(k0 + (s + 1) * kWk) }
     const double* A = wa[s & 1];
     const double* B = wb[s & 1];
 #pragma unroll
@@ -654,9 +657,11 @@ __global__ __launch_bounds__(256) void wtw_kernel(const double* U, int d, double
       acc.v[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc.v[1][0], 0, 0, 0);
       acc.v[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc.v[1][1], 0, 0, 0);
     }
-    if (s + 1 < nks) park((s + 1) & 1);   // the other stage: last read before the previous barrier
+    if (s + 1 < nks) { WTW_PARK((s + 1) & 1) }   // the other stage: last read before the previous barrier
     __syncthreads();
   }
+#undef WTW_FETCH
+#undef WTW_PARK
   // the tile through LDS, so that it and its mirror image leave as row segments; a
   // diagonal tile takes its lower triangle for both halves (exactly symmetric)
   constexpr int kT = NB + 1;
