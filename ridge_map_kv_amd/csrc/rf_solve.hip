@@ -749,10 +749,15 @@ __global__ __launch_bounds__(256) void bias_kernel(const float* YX, const double
   if (row >= n_layers * d_out) return;
   const float* y = YX + (size_t)row * d_in;
   double s = 0.0;
-  for (int k = lane * 4; k < d_in; k += 256) {          // 16-byte loads: d_in % 64 == 0
+  // 16-byte loads (d_in % 64 == 0), unrolled so that several steps' loads are in flight
+  // together instead of each step waiting for its own
+#pragma unroll 4
+  for (int k = lane * 4; k < d_in; k += 256) {
     const f32x4 q = *reinterpret_cast<const f32x4*>(y + k);
-    s += (double)q[0] * v[k] + (double)q[1] * v[k + 1] + (double)q[2] * v[k + 2] +
-         (double)q[3] * v[k + 3];
+    const double2 v01 = *reinterpret_cast<const double2*>(v + k);
+    const double2 v23 = *reinterpret_cast<const double2*>(v + k + 2);
+    s += (double)q[0] * v01.x + (double)q[1] * v01.y + (double)q[2] * v23.x +
+         (double)q[3] * v23.y;
   }
   for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
   if (lane == 0) {
@@ -782,9 +787,14 @@ __global__ void split_c_kernel(const float* YX, const double* mu, const unsigned
     const double nm = n * mu[(size_t)d_in + (size_t)l * d_out + o];
     uint16_t* dst = Cx + (size_t)row * (kSplitMax * d);
     const f32x4 y = *reinterpret_cast<const f32x4*>(src + k);
+    // mu_S[k .. k + 3] as two 16-byte loads issued with y's (one at a time, each waited for
+    // inside the split, they were four dependent round trips)
+    const double2 m01 = *reinterpret_cast<const double2*>(mu + k);
+    const double2 m23 = *reinterpret_cast<const double2*>(mu + k + 2);
+    const double ms[4] = {m01.x, m01.y, m23.x, m23.y};
     uint16_t hi[4], mid[4], lo[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split3_bf16((double)y[j] - nm * mu[k + j], hi[j], mid[j], lo[j]);
+    for (int j = 0; j < 4; ++j) split3_bf16((double)y[j] - nm * ms[j], hi[j], mid[j], lo[j]);
     u32x2 h2, m2, l2;
     h2.x = hi[0] | (uint32_t)hi[1] << 16;
     h2.y = hi[2] | (uint32_t)hi[3] << 16;
