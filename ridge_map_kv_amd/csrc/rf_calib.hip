@@ -436,6 +436,49 @@ __device__ __forceinline__ void mfma16_read_tr(f32x16 (&acc)[4][4], const bf16x8
   }
 }
 
+// Slice kt of the moments loop (kt + 1 < nk): steps 1 to 3 of slice kt, the barrier that
+// frees its stage, step 0 of slice kt + 1.  PEND: the second half of slice kt + 1's loads
+// goes out in step 1 (kt >= 1; slices 0 and 1 came whole before the loop).  MORE: slice
+// kt + 2 exists and the first half of its loads goes out in step 0.  Each block pointer moves
+// on by one slice once its load has gone out.
+template <bool PEND, bool MORE>
+__device__ __forceinline__ void calib_slice(f32x16 (&acc)[4][4], bf16x8 (&a0)[4], bf16x8 (&b0)[4],
+                                            bf16x8 (&a1)[4], bf16x8 (&b1)[4], DmaOperand& F,
+                                            DmaOperand& T, unsigned char* smem, uint32_t base,
+                                            int kt, const TrOff& to, int64_t fslice,
+                                            int64_t tslice, int wave) {
+  const unsigned char* cur = smem + (kt & 1) * kPipeStage;
+  mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, to, PEND, F, T,
+                 base + ((kt + 1) & 1) * kPipeStage, wave);
+  if (PEND) {
+#pragma unroll
+    for (int p = 4; p < 8; ++p) {
+      F.base[p] += fslice;
+      T.base[p] += tslice;
+    }
+  }
+  mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, to, false, F, T, 0, wave);
+  mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, to, false, F, T, 0, wave);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
+  const uint32_t dst = base + (kt & 1) * kPipeStage;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    mfma_i(acc, a1, b1, i);
+    if (MORE && !(i & 1)) dma_issue(F, T, i >> 1, 0, dst, wave);
+    if (i >= 8) read_frag_tr(a0, b0, nxt, i - 8, 0, to);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (MORE) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      F.base[p] += fslice;
+      T.base[p] += tslice;
+    }
+  }
+}
+
 // DMA block j = 4 p + wave (p = 0..7) of an operand stage: rows 2 j, 2 j + 1 (1 KB).  Lane
 // l lands on row 2 j + (l >> 5), chunk position l & 31, which holds logical chunk
 // tr_flip((l & 31) ^ ((row & 3) << 1)).
@@ -506,41 +549,17 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
 #pragma unroll
   for (int i = 0; i < 8; ++i) read_frag_tr(a0, b0, smem, i, 0, to);
   // Loads split as in the fill pipeline: blocks 0..3 of each operand right after the
-  // barrier that frees a stage, blocks 4..7 during the next slice's first step.  Each block
-  // pointer moves on by one slice once its load has gone out.
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    const unsigned char* cur = smem + (kt & 1) * kPipeStage;
-    const bool pend = kt >= 1;                           // second half of slice kt + 1
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 1, to, pend, F, T,
-                   base + ((kt + 1) & 1) * kPipeStage, wave);
-    if (pend) {
-#pragma unroll
-      for (int p = 4; p < 8; ++p) {
-        F.base[p] += fslice;
-        T.base[p] += tslice;
-      }
-    }
-    mfma16_read_tr(acc, a1, b1, a0, b0, cur, 2, to, false, F, T, 0, wave);
-    mfma16_read_tr(acc, a0, b0, a1, b1, cur, 3, to, false, F, T, 0, wave);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const bool more = kt + 2 < nk;
-    const unsigned char* nxt = smem + ((kt + 1) & 1) * kPipeStage;
-    const uint32_t dst = base + (kt & 1) * kPipeStage;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mfma_i(acc, a1, b1, i);
-      if (more && !(i & 1)) dma_issue(F, T, i >> 1, 0, dst, wave);
-      if (i >= 8) read_frag_tr(a0, b0, nxt, i - 8, 0, to);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        F.base[p] += fslice;
-        T.base[p] += tslice;
-      }
-    }
+  // barrier that frees a stage, blocks 4..7 during the next slice's first step.  The first
+  // slice has no pending half, the last starts no further slice; the steady slices between
+  // carry no load conditions.
+  if (nk == 2) {
+    calib_slice<false, false>(acc, a0, b0, a1, b1, F, T, smem, base, 0, to, fslice, tslice, wave);
+  } else if (nk > 2) {
+    calib_slice<false, true>(acc, a0, b0, a1, b1, F, T, smem, base, 0, to, fslice, tslice, wave);
+    for (int kt = 1; kt < nk - 2; ++kt)
+      calib_slice<true, true>(acc, a0, b0, a1, b1, F, T, smem, base, kt, to, fslice, tslice, wave);
+    calib_slice<true, false>(acc, a0, b0, a1, b1, F, T, smem, base, nk - 2, to, fslice, tslice,
+                             wave);
   }
   {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kPipeStage;
