@@ -576,12 +576,30 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
   if (tid < 128) skn[tid] = my_kn;
   svs[tid] = my_vs;
   sfc[tid] = my_c;
+  // A tile with K features: the RoPE tables of its 256 rows (in the blocked layout, cos and
+  // sin each one contiguous run of half KB) go by direct loads into the LDS the main loop has
+  // left, cos at 0 and sin at 64 KB, and are waited for once here.  (Loaded from memory where
+  // each 32-row block is rotated, they cost several round trips per block.)
+  const int half = a.hd >> 1;
+  const bool tabs = MODE == 0 && f0 < a.kv;
+  if (tabs) {
+    const int dwave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const size_t tbase = (size_t)(t0 >> 5) * (half >> 2) * 128;   // floats
+    const uint32_t lbase = lds_addr(smem);
+    const uint32_t voff = (uint32_t)(tid & 63) * 16;
+    for (int c = dwave; c < 2 * half; c += 4) {    // 1 KB chunks: cos 0 .. half - 1, then sin
+      const bool sinc = c >= half;
+      const int cc = sinc ? c - half : c;
+      dma16((sinc ? a.rsin : a.rcos) + tbase + (size_t)cc * 256, voff,
+            lbase + (sinc ? 65536u : 0u) + (uint32_t)cc * 1024);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6, wf = wave >> 1, wt = wave & 1, h = lane >> 5;
   const int fw = f0 + wf * 128;                  // the wave's first feature
   const bool isK = fw < a.kv;                    // kv % 128 == 0: a wave is all K or all V
-  const int half = a.hd >> 1;
   if (MODE == 1) {
     if (isK) return;                             // a tile may straddle K and V (kv % 256 != 0)
     // heads (fw - kv) / hd and, for hd = 64, the next one
@@ -614,7 +632,6 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int tl = wt * 128 + n * 32 + (lane & 31);
-    const int tok = t0 + tl;
     const float r = rstd[tl];   // rows past n_filled: finite padding, never stored
     if (folded) {             // (P x + c) / rms
 #pragma unroll
@@ -648,9 +665,9 @@ __device__ __forceinline__ void fill_kv_tile(const FillKArgs& a, int tile) {
           }
         }
       }
-      const size_t e0 = ((size_t)(tok >> 5) * (half >> 2) + h) * 128 + (tok & 31) * 4;
-      const float* cs = a.rcos + e0;
-      const float* sn = a.rsin + e0;
+      const int e0 = ((tl >> 5) * (half >> 2) + h) * 128 + (tl & 31) * 4;   // tile-relative
+      const float* cs = reinterpret_cast<const float*>(smem) + e0;
+      const float* sn = reinterpret_cast<const float*>(smem + 65536) + e0;
       if (a.hd == 128) {
         rope_pair<0, 2, 0>(acc, n, cs, sn);
         rope_pair<1, 3, 32>(acc, n, cs, sn);
