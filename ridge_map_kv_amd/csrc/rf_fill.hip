@@ -382,11 +382,11 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     else
       gemm_mainloop_tri<false>(acc, Fo, To, a.d_in - f0, smem);
 
-    // Per-lane values of the rest of the iteration are formed from a thread index made
-    // opaque here: hoisted out of the loop, they lived across it and were spilled, and their
-    // reloads in the epilogue waited for the next tile's slice loads issued just before.
-    int ltid = tid;
-    asm volatile("" : "+v"(ltid));
+    // Per-lane values of the rest of the iteration are formed from a thread index the
+    // compiler cannot trace back to the work-item id: hoisted out of the loop, they lived
+    // across it and were spilled, and their reloads in the epilogue waited for the next tile's
+    // slice loads issued just before.
+    int ltid = (wave << 6) | lane_id_opaque();
     const int llane = ltid & 63, lh = llane >> 5;
     // this tile's r1 and g, loaded now with the next tile's index loads (loaded before the
     // main loop, they were spilled across it)
@@ -409,8 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
     }
 
     float* ssq = reinterpret_cast<float*>(a.layer_ws + cur.g * a.per_layer + a.per_layer_h);
-    ltid = tid;                         // again, now that the loads are out
-    asm volatile("" : "+v"(ltid));
+    ltid = (wave << 6) | lane_id_opaque();          // again, now that the loads are out
     const int elane = ltid & 63, eh = elane >> 5;
     sr[ltid] = my_r;
     sg[ltid] = my_g;

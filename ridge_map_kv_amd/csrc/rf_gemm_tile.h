@@ -78,6 +78,17 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory");
 }
 
+// This lane's index in its wave, read from the hardware's lane counters in a way the
+// compiler cannot trace back to the work-item id: a value derived from that id, used in every
+// iteration of a persistent loop, keeps the id itself live across the loop's main loops,
+// where it is spilled, and its reload at a tile's first slice waits for every slice load in
+// flight.
+__device__ __forceinline__ int lane_id_opaque() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Block j = 4 p + wave (p = 0..7) of an operand stage: LDS rows 8 j .. 8 j + 7.  Lane l
 // lands on row 8 j + (l >> 3) at chunk position l & 7, which holds logical chunk
 // (l & 7) ^ swz(row).  base[p]: wave-uniform byte pointer, off[p]: this lane's byte offset
@@ -362,9 +373,7 @@ __device__ __forceinline__ void gemm_mainloop_tri(f32x16 (&acc)[4][4], const Dma
   // the offsets are formed anew for every tile: in a persistent caller, hoisted out of its
   // loop they would live across the epilogue, where they were spilled and then reloaded
   // inside the first slices (a reload waits for every load in flight, the slices' too)
-  int olane = lane;
-  asm volatile("" : "+v"(olane));
-  FragOff fo = frag_off(olane);
+  FragOff fo = frag_off(lane_id_opaque());
   frag_off_tri(fo, wf);
   bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
