@@ -354,8 +354,10 @@ __device__ __forceinline__ void norm_prologue(const DmaOperand& Fo, const DmaOpe
 // items blockIdx.x, blockIdx.x + gridDim.x, ..., each one or two tiles.  The loads of a
 // tile's first two slices are issued as soon as the previous tile's main loop has left
 // the LDS, before that tile's epilogue, so the epilogue arithmetic and stores overlap
-// them.  (The map kernel, whose epilogue stages its outputs through that LDS, and the kv
-// kernel, whose epilogue spills registers in such a loop, stay one tile per workgroup.)
+// them.  (The map kernel stages its outputs through that LDS and the kv kernel its RoPE
+// tables, so both stay one tile per workgroup; a kv kernel in such a loop, without the
+// tables in LDS, measured no faster: its epilogue's own loads then wait behind the next
+// tile's slice loads, which complete first.)
 // gridDim.x is a multiple of 8 or equal to n_items, so item i runs on XCD i % 8 and
 // xcd_remap's tile ranges hold.
 __global__ __launch_bounds__(kThreads, 1) void fill_norm_kernel(FillKArgs a) {
