@@ -122,6 +122,32 @@ def test_calib_empty_and_one_row_chunks_bit_exact():
     assert np.array_equal(g.s_S, st.s_S) and np.array_equal(g.s_l, st.s_l)
 
 
+def test_calib_short_chunks_every_slice_count_bit_exact():
+    # chunks of 64, 128, 192 and 256 rows run the moments loop with 1, 2, 3 and 4 row
+    # slices (no loop, the first-and-last slice alone, first then last, and one steady slice
+    # between), 65 and 130 rows add a ragged tail to the shortest; on exactly representable
+    # data every sum equals the oracle's bit for bit.  The first call (64 rows) fixes the
+    # shift: the columns whose 64 values are all equal (the Sylvester columns c with
+    # c % 64 == 0, +1 in rows 0..63) are accumulated about that value, the balanced ones
+    # (mean 0) about zero; the shifted values, 0 and -2, stay exact.
+    n, d, L = 2048, 256, 2
+    X, Y, _, _ = _hadamard(n, d, L, 42)
+    xs_g, yl_g = bf16(X), [bf16(y) for y in Y]
+    cuts = [0, 64, 192, 384, 640, 705, 835, n]
+    g = GpuStats(run_calib([xs_g[a:b] for a, b in zip(cuts, cuts[1:])],
+                           [[y[a:b] for y in yl_g] for a, b in zip(cuts, cuts[1:])], d, L), d, L)
+    want = np.where(np.all(X[:64] == X[0], axis=0), X[0], 0.0)
+    assert np.count_nonzero(want) == 4 and g.shift_fixed
+    assert np.array_equal(g.shift, want)
+    st = oracle.calib_new(d, L)
+    oracle.calib_accumulate(st, X - want, list(Y))
+    low = np.tril(np.ones((d, d), dtype=bool))
+    assert g.n == n
+    assert np.array_equal(g.G[low], st.G[low])
+    assert np.array_equal(g.YX, st.YX)
+    assert np.array_equal(g.s_S, st.s_S) and np.array_equal(g.s_l, st.s_l)
+
+
 def test_reset_clears_state():
     d, L = 256, 1
     state = torch.full((B.ridgefill_calib_state_bytes(d, L),), 7, dtype=torch.uint8, device="cuda")
