@@ -307,6 +307,58 @@ __device__ __forceinline__ void calib_store(const f32x16 (&acc)[4][4], const Cal
   }
 }
 
+// The moments of a tile added to the state row by row (the DMA kernel's epilogue): each
+// half of the tile (128 rows of 256 fp32 columns, 128 KB) is parked in the LDS the main
+// loop has left, then every wave adds whole 1 KB row segments to the state, one 16-byte
+// piece per lane, and writes them back as full cache lines, non-temporally: the next call
+// reads them only after every tile of this one.  The same fp32 addition as calib_store, so
+// the same results.  16-byte piece k of LDS row r sits at position k ^ (r & 63).
+__device__ __forceinline__ void calib_store_rows(const f32x16 (&acc)[4][4], const CalibTile& t,
+                                                 int d, unsigned char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wave >> 1, wt = wave & 1, h = lane >> 5;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    __syncthreads();                      // the LDS is free (the main loop's, or the last half's)
+    if (wt == hh) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int r = n * 32 + (lane & 31);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = wf * 32 + m * 8 + q * 2 + h;        // 16-byte piece of the row
+            const f32x4 v = {acc[m][n][q * 4 + 0], acc[m][n][q * 4 + 1], acc[m][n][q * 4 + 2],
+                             acc[m][n][q * 4 + 3]};
+            *reinterpret_cast<f32x4*>(smem + r * 1024 + ((k ^ (r & 63)) << 4)) = v;
+          }
+      }
+    }
+    __syncthreads();
+    // rows wave, wave + 4, ..., wave + 124 of this half: all 32 reads in flight at once
+    f32x4 old[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int r = wave + 4 * i;
+      old[i] = *reinterpret_cast<const f32x4*>(t.out + (size_t)(t.o0 + hh * 128 + r) * d + t.f0 +
+                                              lane * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int r = wave + 4 * i;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(smem + r * 1024 + ((lane ^ (r & 63)) << 4));
+      f32x4 o = old[i];
+      o[0] += v[0];
+      o[1] += v[1];
+      o[2] += v[2];
+      o[3] += v[3];
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(t.out + (size_t)(t.o0 + hh * 128 + r) * d +
+                                                          t.f0 + lane * 4));
+    }
+  }
+}
+
 // Rows row0 .. row0 + n_rows - 1 (any count; rows past the end read as zero), register-
 // staged with the transpose done in registers.  Used for the ragged row tail.
 __global__ __launch_bounds__(kThreads, 1) void calib_moments_kernel(CalibArgs a) {
@@ -569,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 1) void calib_moments_dma_kernel(CalibArg
 #pragma unroll
     for (int i = 0; i < 16; ++i) mfma_i(acc, a1, b1, i);
   }
-  calib_store(acc, t, a.d_in);
+  calib_store_rows(acc, t, a.d_in, smem);
 }
 
 }  // namespace
