@@ -322,21 +322,23 @@ __global__ __launch_bounds__(kDiagThreads) void chol_diag_kernel(double* C, int 
   __syncthreads();
   for (int j = 0; j < NB; j += 2) {
     const int b = (j >> 1) & 1;
-    double p0 = colA[b][j];
-    const bool bad0 = !(p0 > 0.0) || !isfinite(p0);
-    if (bad0) p0 = 1.0;
-    const double r0 = recip(p0);
-    const double a10 = colA[b][j + 1];
-    const double g = a10 * r0;
-    double p1 = colB[b][j + 1] - a10 * g;
-    const bool bad1 = !(p1 > 0.0) || !isfinite(p1);
-    if (bad1) p1 = 1.0;
-    if (t == 0) {
-      piv[j] = p0;
-      piv[j + 1] = p1;
-      if (bad0 || bad1) atomicOr(status, kStatusNotSpdBit);
-    }
+    // rows up to j have nothing left to eliminate: their waves skip the step, the pivot
+    // arithmetic included (every row below works it out for itself; row j + 1 records it)
     if (row > j) {
+      double p0 = colA[b][j];
+      const bool bad0 = !(p0 > 0.0) || !isfinite(p0);
+      if (bad0) p0 = 1.0;
+      const double r0 = recip(p0);
+      const double a10 = colA[b][j + 1];
+      const double g = a10 * r0;
+      double p1 = colB[b][j + 1] - a10 * g;
+      const bool bad1 = !(p1 > 0.0) || !isfinite(p1);
+      if (bad1) p1 = 1.0;
+      if (row == j + 1 && c0 == 0) {
+        piv[j] = p0;
+        piv[j + 1] = p1;
+        if (bad0 || bad1) atomicOr(status, kStatusNotSpdBit);
+      }
       const double xa = colA[b][row];
       const double m0 = xa * r0;
       // column j+1 of this row, after column j's elimination, and its multiplier
