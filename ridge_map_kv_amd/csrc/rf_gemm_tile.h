@@ -67,15 +67,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // One 16-byte load per lane from sbase + voff (sbase wave-uniform); lane l lands at
 // lds + 16 l.  The LDS destination goes through M0.  A scalar write of M0 followed by an
 // LDS DMA needs one wait state on this architecture family, which the compiler cannot
-// insert inside an asm string: the s_nop provides it.  M0 is a reserved register that the
-// compiler sets only for the few instructions that read it; none of them occurs in the
-// kernels built on this helper (their gfx950 assembly writes M0 only here), so no value
-// of the compiler's own lives in M0 across the load.
+// insert inside an asm string: the s_nop provides it.  M0 is declared clobbered, so the
+// compiler keeps none of its own values there across the load (none of the kernels built
+// on this helper uses M0 otherwise: their gfx950 assembly is the same with and without the
+// clobber).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
+               : "memory", "m0");
 }
 
 // This lane's index in its wave, read from the hardware's lane counters in a way the
