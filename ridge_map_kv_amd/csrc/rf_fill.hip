@@ -790,53 +790,64 @@ __global__ void rstd_folded_kernel(FillKArgs a) {
       1.0f / sqrtf(s / (float)a.d + a.eps);
 }
 
-__global__ void iota_kernel(int32_t* idx, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) idx[i] = i;
-}
-
-// Exact tail inputs of the value rescale, one block per (row, layer): bf16(x * w) and
+// Exact tail inputs of the value rescale, one wave per (row, exact entry): bf16(x * w) and
 // 1/sqrt(mean(x^2) + eps), written where the map kernel and rstd_kernel put the predicted
-// ones, so the value-norm pass reads both the same way.  Padding rows get zeros.
+// ones, so the value-norm pass reads both the same way.  Padding rows get zeros.  Entry l of
+// the exact side is table entry G + l: its w is the layer's norm weight and its A field holds
+// the layer's exact rows x (bf16 [c][d]), which no other kernel reads from those entries.
+// The waves of entry 0 also write the identity index list (row i -> i) that the predicted
+// side gathers its rows through.
 struct ExactArgs {
-  const uint16_t* x[kMaxGroup];
-  const uint16_t* w[kMaxGroup];
+  const FillLayerPtrs* tab;     // the exact entries
+  int32_t* idx;
   int c, d;
   float eps;
-  unsigned char* layer_ws;
+  unsigned char* layer_ws;      // the first exact entry's area
   size_t per_layer, per_layer_h, per_layer_ssq;
 };
 
-__global__ void exact_rows_kernel(ExactArgs a) {
-  const int row = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+__global__ __launch_bounds__(256) void exact_rows_kernel(ExactArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = blockIdx.y, lane = threadIdx.x & 63;
+  const uint16_t* xr = a.tab[l].A;    // read once, before any store
+  const uint16_t* w = a.tab[l].w;
+  const uint16_t* x = xr + (size_t)row * a.d;
   unsigned char* lw = a.layer_ws + (size_t)l * a.per_layer;
   uint16_t* hb = reinterpret_cast<uint16_t*>(lw) + (size_t)row * a.d;
-  __shared__ float red[256];
+  const bool live = row < a.c;
+  const int nch = a.d >> 3;                     // 16-byte chunks of a row
   float s = 0.f;
-  for (int c8 = tid; c8 < a.d / 8; c8 += 256) {
-    u32x4 o = {0u, 0u, 0u, 0u};
-    if (row < a.c) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x[l] + (size_t)row * a.d + c8 * 8);
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(a.w[l] + c8 * 8);
+  for (int c0 = 0; c0 < nch; c0 += 4 * 64) {    // four chunks per lane in flight
+    u32x4 xv[4], wv[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = bf16_to_f32(xv[k] & 0xffffu), x1 = bf16_to_f32(xv[k] >> 16);
-        s += x0 * x0;
-        s += x1 * x1;
-        o[k] = pack_bf16x2(x0 * bf16_to_f32(wv[k] & 0xffffu), x1 * bf16_to_f32(wv[k] >> 16));
+    for (int j = 0; j < 4; ++j) {
+      const int c8 = c0 + j * 64 + lane;
+      xv[j] = u32x4{0u, 0u, 0u, 0u};
+      wv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (live && c8 < nch) {
+        xv[j] = *reinterpret_cast<const u32x4*>(x + c8 * 8);
+        wv[j] = *reinterpret_cast<const u32x4*>(w + c8 * 8);
       }
     }
-    *reinterpret_cast<u32x4*>(hb + c8 * 8) = o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c8 = c0 + j * 64 + lane;
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = bf16_to_f32(xv[j][k] & 0xffffu), x1 = bf16_to_f32(xv[j][k] >> 16);
+        s += x0 * x0;
+        s += x1 * x1;
+        o[k] = pack_bf16x2(x0 * bf16_to_f32(wv[j][k] & 0xffffu), x1 * bf16_to_f32(wv[j][k] >> 16));
+      }
+      if (c8 < nch) *reinterpret_cast<u32x4*>(hb + c8 * 8) = o;
+    }
   }
-  red[tid] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {          // fixed-order tree: deterministic
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) s += __shfl_xor(s, m);   // fixed butterfly: deterministic
+  if (lane == 0) {
     float* rs = reinterpret_cast<float*>(lw + a.per_layer_h + a.per_layer_ssq);
-    rs[row] = row < a.c ? 1.0f / sqrtf(red[0] / (float)a.d + a.eps) : 0.f;
+    rs[row] = live ? 1.0f / sqrtf(s / (float)a.d + a.eps) : 0.f;
+    if (l == 0) a.idx[row] = row;
   }
 }
 
@@ -1181,8 +1192,6 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
                               int n_layers, float* out, const VsLayout& V, hipStream_t stream) {
   hipError_t e = launch_clear_status(p.status, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(iota_kernel, dim3(p.mpad / 256), dim3(256), 0, stream,
-                     const_cast<int32_t*>(p.idx), p.mpad);
   unsigned char* pred = reinterpret_cast<unsigned char*>(p.hbuf);
   const int gsize = group_size(n_layers, p.group);
   for (int l0 = 0; l0 < n_layers; l0 += gsize) {
@@ -1199,10 +1208,23 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
         } else {
           t.e[i].w = layers[l0 + k - G].w;
           t.e[i].WV = exact_wv[l0 + k - G];
+          t.e[i].A = x_exact[l0 + k - G];
         }
       }
       hipLaunchKernelGGL(layer_table_kernel, dim3(1), dim3(kTableChunk), 0, stream, t);
     }
+    // the exact rows into the G blocks after the predicted ones (and the index list 0 .. mpad-1)
+    ExactArgs x = {};
+    x.tab = V.table + G;
+    x.idx = const_cast<int32_t*>(p.idx);
+    x.c = p.n_filled;
+    x.d = p.d;
+    x.eps = p.eps;
+    x.layer_ws = pred + (size_t)G * p.L.per_layer;
+    x.per_layer = p.L.per_layer;
+    x.per_layer_h = p.L.per_layer_h;
+    x.per_layer_ssq = p.L.per_layer_ssq;
+    hipLaunchKernelGGL(exact_rows_kernel, dim3(p.mpad / 4, G), dim3(256), 0, stream, x);
     FillKArgs a = fill_args(p, pred);
     a.Ltab = V.table;
     a.f_base = 0;
@@ -1218,23 +1240,6 @@ hipError_t launch_value_scale(const FillPlan& p, const FillLayerPtrs* layers,
         hipLaunchKernelGGL(fill_map_kernel<0>, dim3(G * a.ntt * a.nft), dim3(kThreads), 0, stream, a);
       hipLaunchKernelGGL(rstd_kernel, dim3(p.mpad / 256, G), dim3(256), 0, stream, a.layer_ws,
                          a.per_layer, a.per_layer_h, a.per_layer_ssq, p.mpad, a.nchunk, p.d, p.eps);
-    }
-    // the exact rows into the G blocks after the predicted ones
-    for (int c0 = 0; c0 < G; c0 += kMaxGroup) {
-      const int n = (G - c0) < kMaxGroup ? (G - c0) : kMaxGroup;
-      ExactArgs x = {};
-      for (int g = 0; g < n; ++g) {
-        x.x[g] = x_exact[l0 + c0 + g];
-        x.w[g] = layers[l0 + c0 + g].w;
-      }
-      x.c = p.n_filled;
-      x.d = p.d;
-      x.eps = p.eps;
-      x.layer_ws = pred + (size_t)(G + c0) * p.L.per_layer;
-      x.per_layer = p.L.per_layer;
-      x.per_layer_h = p.L.per_layer_h;
-      x.per_layer_ssq = p.L.per_layer_ssq;
-      hipLaunchKernelGGL(exact_rows_kernel, dim3(p.mpad, n), dim3(256), 0, stream, x);
     }
     // value norms of both sides: the tiles that hold V features of 2 G entries
     a.f_base = p.kv / kTile;
